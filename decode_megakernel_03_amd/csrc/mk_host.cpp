@@ -1,0 +1,801 @@
+// Host side of libmk: model validation, workspace, the static task scheduler, a schedule validator,
+// a CPU simulation of the persistent loop, and the C ABI declared in include/mk.h.
+//
+// Scheduling follows "mostly static" scheduling (P3 "Scheduling and Performance Benchmarks"): the
+// host expands one decode step into tasks, groups them into topological levels (one parallel layer
+// = three levels: QKV/router -> attention/expert slices -> output rows) and deals each level's
+// tasks to the resident workers by a longest-first list schedule over an HBM-bytes cost model.
+// Tile counts are derived from the worker count rather than a fixed tile, so a level never ends
+// with a partly filled wave of tiles (P1 "One persistent kernel for the whole decode step": wave
+// quantization). Attention is split per KV group so an output row waits only for the attention it
+// reads; weight loads are issued before dependency waits inside the kernel.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <numeric>
+#include <random>
+#include <string>
+#include <vector>
+
+#include "../../include/mk.h"
+#include "mk_internal.h"
+#include "mk_launch.h"
+
+using namespace mk;
+
+namespace {
+
+struct Task {
+  int32_t w[DESC_WORDS];
+};
+
+std::string fmt(const char* f, ...) {
+  char buf[1024];
+  va_list ap;
+  va_start(ap, f);
+  vsnprintf(buf, sizeof buf, f, ap);
+  va_end(ap);
+  return buf;
+}
+
+void put(char* buf, size_t n, const std::string& s) {
+  if (!buf || n == 0) return;
+  size_t k = std::min(n - 1, s.size());
+  memcpy(buf, s.data(), k);
+  buf[k] = 0;
+}
+
+struct Dims {
+  int L, H, HQ, HKV, D, E, K, F, V, HPG, QKVR, AD, PART;
+  bool lm;
+};
+
+Dims dims_of(const mk_model_desc& d) {
+  Dims m;
+  m.L = d.n_layers; m.H = d.hidden; m.HQ = d.n_q_heads; m.HKV = d.n_kv_heads; m.D = d.head_dim;
+  m.E = d.n_experts; m.K = d.top_k; m.F = d.expert_ffn; m.V = d.vocab;
+  m.HPG = m.HQ / m.HKV; m.QKVR = (m.HQ + 2 * m.HKV) * m.D; m.AD = m.HQ * m.D;
+  m.PART = m.HPG * (m.D + 2);
+  m.lm = d.has_lm_head != 0;
+  return m;
+}
+
+mk_status check_desc(const mk_model_desc* d, std::string* why) {
+  if (!d) { *why = "desc is NULL"; return MK_ERR_INVALID_ARG; }
+  if (d->abi_version != MK_ABI_VERSION) { *why = fmt("abi_version %d != %d", d->abi_version, MK_ABI_VERSION); return MK_ERR_INVALID_ARG; }
+  if (d->n_layers < 1 || d->vocab < 1 || d->num_pages < 1 || d->max_pages_per_seq < 1) {
+    *why = "n_layers, vocab, num_pages and max_pages_per_seq must be >= 1"; return MK_ERR_INVALID_ARG;
+  }
+  if (d->max_batch < 1 || d->max_batch > MK_MAX_BATCH) { *why = fmt("max_batch %d outside 1..%d", d->max_batch, MK_MAX_BATCH); return MK_ERR_INVALID_ARG; }
+  if (d->page_size != PAGE) { *why = fmt("page_size %d unsupported (16)", d->page_size); return MK_ERR_UNSUPPORTED; }
+  if (shape_id(d->hidden, d->head_dim, d->n_q_heads, d->n_kv_heads, d->n_experts, d->top_k, d->expert_ffn) < 0) {
+    *why = "no compiled kernel for this (hidden, head_dim, heads, experts, top_k, expert_ffn)"; return MK_ERR_UNSUPPORTED;
+  }
+  if (!(d->rms_eps > 0.f) || !(d->rope_theta > 0.f)) { *why = "rms_eps and rope_theta must be > 0"; return MK_ERR_INVALID_ARG; }
+  return MK_OK;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// counter indices of one schedule
+struct Ctrs {
+  int n = 0;
+  int alloc(int k = 1) { int c = n; n += k; return c; }
+};
+
+}  // namespace
+
+// ============================================================================== the plan
+
+struct mk_plan {
+  mk_model_desc desc;
+  Dims m;
+  int B = 0, n_workers = 0, split_keys = 0;
+  std::vector<int> seq_lens;
+  std::vector<Task> tasks;        // queue order: worker 0's tasks, worker 1's, ...
+  std::vector<int32_t> qoff;      // n_workers + 1
+  std::vector<int64_t> bytes;     // cost model, per task (queue order)
+  int n_ctr = 0, done_ctr = 0, parts_per_layer = 0, n_attn = 0;
+  std::vector<int> capacity;      // per sequence: largest seq_len the schedule can serve
+};
+
+namespace {
+
+struct Proto {            // task before placement
+  Task t;
+  int64_t bytes;
+  int prio;               // order inside a worker's level segment (lower first)
+};
+
+void set(Task& t, int op, int layer, int level) {
+  for (int i = 0; i < DESC_WORDS; ++i) t.w[i] = 0;
+  t.w[D_OP] = op; t.w[D_LAYER] = layer; t.w[D_LEVEL] = level;
+  t.w[D_W0] = t.w[D_W1] = t.w[D_SIG] = t.w[D_SIG2] = -1;
+}
+
+// Split [0, len) into n near-equal ranges.
+std::vector<std::pair<int, int>> even(int len, int n) {
+  std::vector<std::pair<int, int>> r;
+  n = std::max(1, std::min(n, len));
+  for (int i = 0; i < n; ++i) r.push_back({(int)((int64_t)len * i / n), (int)((int64_t)len * (i + 1) / n)});
+  return r;
+}
+
+mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, int W, int split_req,
+                     mk_plan* P, std::string* why) {
+  const Dims m = dims_of(desc);
+  P->desc = desc; P->m = m; P->B = B; P->n_workers = W;
+  P->seq_lens.assign(seq_lens, seq_lens + B);
+  const int SPLITMAX = split_max(), OUTR = out_max_rows();
+  for (int b = 0; b < B; ++b) {
+    if (seq_lens[b] < 1 || seq_lens[b] > desc.max_pages_per_seq * PAGE) {
+      *why = fmt("seq_lens[%d] = %d outside 1..%d", b, seq_lens[b], desc.max_pages_per_seq * PAGE);
+      return MK_ERR_INVALID_ARG;
+    }
+  }
+  // attention split length: keep per-(b, g) split counts moderate and tasks ~128 KB of K+V
+  int maxlen = *std::max_element(seq_lens, seq_lens + B);
+  int split = split_req > 0 ? split_req : std::max(256, (int)ceil_div(ceil_div(maxlen, 64), 16) * 16);
+  split = std::max(16, std::min(split, SPLITMAX / 2));
+  split = (split + 15) / 16 * 16;
+  P->split_keys = split;
+
+  Ctrs C;
+  const int L = m.L;
+  std::vector<int> c_x(L + 1, -1), c_rarr(L), c_route(L), c_h(L), c_att(L);
+  std::vector<std::vector<int>> c_qkv(L, std::vector<int>(m.HKV));
+  std::vector<std::vector<int>> c_aarr(L, std::vector<int>(B * m.HKV));
+  for (int l = 0; l < L; ++l) {
+    for (int g = 0; g < m.HKV; ++g) c_qkv[l][g] = C.alloc();
+    c_rarr[l] = C.alloc(); c_route[l] = C.alloc(); c_h[l] = C.alloc(); c_att[l] = C.alloc();
+    for (int i = 0; i < B * m.HKV; ++i) c_aarr[l][i] = C.alloc();
+    c_x[l + 1] = C.alloc();
+  }
+  P->done_ctr = C.alloc();
+  P->n_ctr = C.n;
+
+  // tile sizes from the worker count
+  const int qkv_tile = std::max(4, std::min(64, (int)ceil_div(m.QKVR, W)));
+  const int router_tiles = std::max(1, std::min(8, m.E / 16));
+  const int slots = std::min(m.E, m.K * B);
+  int nf = (int)ceil_div(m.F, std::max<int64_t>(1, ceil_div(W, slots)));
+  nf = std::max(4, std::min(64, nf));
+  const int slices = (int)ceil_div(m.F, nf);
+
+  // attention splits per sequence: [k0, k0 + split) ... last split open-ended from k0_last
+  std::vector<int> nsplit(B), pbase_b(B);
+  int parts = 0;
+  P->capacity.resize(B);
+  for (int b = 0; b < B; ++b) {
+    const int pos = seq_lens[b] - 1;
+    const int k0_last = pos / split * split;
+    nsplit[b] = k0_last / split + 1;
+    pbase_b[b] = parts;
+    parts += nsplit[b] * m.HKV;
+    P->capacity[b] = std::min(k0_last + SPLITMAX, desc.max_pages_per_seq * PAGE);
+  }
+  P->parts_per_layer = parts;
+
+  std::vector<std::vector<Proto>> levels(3 * L + 1);
+  int n_attn = 0;
+  for (int l = 0; l < L; ++l) {
+    const int lv0 = 3 * l, lv1 = 3 * l + 1, lv2 = 3 * l + 2;
+    // level 0: QKV rows (per KV group: q heads, k, v) and router tiles
+    std::vector<int> qkv_count(m.HKV, 0);
+    for (int g = 0; g < m.HKV; ++g) {
+      const int regions[3][2] = {{g * m.HPG * m.D, m.HPG * m.D}, {m.HQ * m.D + g * m.D, m.D}, {(m.HQ + m.HKV) * m.D + g * m.D, m.D}};
+      for (auto& rg : regions)
+        for (auto [a, e] : even(rg[1], (int)ceil_div(rg[1], qkv_tile))) {
+          Proto pr;
+          set(pr.t, OP_QKV, l, lv0);
+          pr.t.w[D_A0] = rg[0] + a; pr.t.w[D_A1] = e - a;
+          pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;   // target filled below
+          pr.t.w[D_SIG] = c_qkv[l][g];
+          pr.bytes = (int64_t)(e - a) * m.H * 2;
+          pr.prio = 1;
+          levels[lv0].push_back(pr);
+          qkv_count[g]++;
+        }
+    }
+    for (auto [a, e] : even(m.E, router_tiles)) {
+      Proto pr;
+      set(pr.t, OP_ROUTER, l, lv0);
+      pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a; pr.t.w[D_A2] = router_tiles;
+      pr.t.w[D_W0] = c_x[l];
+      pr.t.w[D_SIG] = c_rarr[l]; pr.t.w[D_SIG2] = c_route[l];
+      pr.bytes = (int64_t)(e - a) * m.H * 2;
+      pr.prio = 0;
+      levels[lv0].push_back(pr);
+    }
+    // level 1: attention splits, expert slices
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < m.HKV; ++g)
+        for (int s = 0; s < nsplit[b]; ++s) {
+          Proto pr;
+          set(pr.t, OP_ATTN, l, lv1);
+          const int k0 = s * split;
+          const bool last = s == nsplit[b] - 1;
+          pr.t.w[D_A0] = b; pr.t.w[D_A1] = g; pr.t.w[D_A2] = k0; pr.t.w[D_A3] = last ? -1 : k0 + split;
+          pr.t.w[D_A4] = pbase_b[b] + g * nsplit[b];
+          pr.t.w[D_A5] = s | (nsplit[b] << 16);
+          pr.t.w[D_W0] = c_qkv[l][g]; pr.t.w[D_T0] = qkv_count[g];
+          pr.t.w[D_SIG] = c_aarr[l][b * m.HKV + g]; pr.t.w[D_SIG2] = c_att[l];
+          const int keys = last ? seq_lens[b] - k0 : split;
+          pr.bytes = (int64_t)keys * m.D * 2 * 2;
+          pr.prio = 0;
+          levels[lv1].push_back(pr);
+          n_attn++;
+        }
+    int n_gu = 0;
+    for (int u = 0; u < slots; ++u)
+      for (int j = 0; j < slices; ++j) {
+        Proto pr;
+        set(pr.t, OP_GATEUP, l, lv1);
+        const int f0 = j * nf, f1 = std::min(m.F, f0 + nf);
+        pr.t.w[D_A0] = u; pr.t.w[D_A1] = f0; pr.t.w[D_A2] = f1 - f0;
+        pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
+        pr.t.w[D_SIG] = c_h[l];
+        pr.bytes = (int64_t)2 * (f1 - f0) * m.H * 2;
+        pr.prio = 1;
+        levels[lv1].push_back(pr);
+        n_gu++;
+      }
+    // level 2: output rows (O-proj + expert down-proj + residual)
+    int n_out = 0;
+    for (auto [a, e] : even(m.H, (int)ceil_div(m.H, OUTR))) {
+      Proto pr;
+      set(pr.t, OP_OUT, l, lv2);
+      pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
+      pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV;
+      pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
+      pr.t.w[D_W1] = c_h[l]; pr.t.w[D_T1] = n_gu;
+      pr.t.w[D_SIG] = c_x[l + 1];
+      pr.bytes = (int64_t)(e - a) * (m.AD + (int64_t)slots * m.F) * 2;
+      pr.prio = 0;
+      levels[lv2].push_back(pr);
+      n_out++;
+    }
+    // targets of the waits on x_l+1 (next layer's level 0, or lm_head)
+    for (int lv = 0; lv < (int)levels.size(); ++lv) (void)lv;
+    P->n_attn = n_attn;
+    // fill T0 of the next layer's x waits once its producers are known
+    if (l + 1 < L) {
+      // placeholder: set after the loop (producer counts are identical per layer)
+    }
+    (void)n_out;
+  }
+  const int n_out_per_layer = (int)ceil_div(m.H, OUTR);
+  for (auto& lvl : levels)
+    for (auto& pr : lvl)
+      if ((pr.t.w[D_OP] == OP_QKV || pr.t.w[D_OP] == OP_ROUTER) && pr.t.w[D_W0] >= 0) pr.t.w[D_T0] = n_out_per_layer;
+  if (m.lm) {
+    for (auto [a, e] : even(m.V, W)) {
+      Proto pr;
+      set(pr.t, OP_LMHEAD, L, 3 * L);
+      pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
+      pr.t.w[D_W0] = c_x[L]; pr.t.w[D_T0] = n_out_per_layer;
+      pr.bytes = (int64_t)(e - a) * m.H * 2;
+      pr.prio = 0;
+      levels[3 * L].push_back(pr);
+    }
+  }
+
+  // placement: per level, longest task first onto the worker with the least load in that level
+  // (ties: least total load, then lowest index); each worker's queue is level-ordered, and inside
+  // a level its tasks run in priority order (router before QKV, attention before expert slices).
+  std::vector<std::vector<std::pair<int, Proto>>> queues(W);   // (level, proto)
+  std::vector<int64_t> total(W, 0);
+  for (int lv = 0; lv < (int)levels.size(); ++lv) {
+    auto& lvl = levels[lv];
+    std::vector<int> order(lvl.size());
+    std::iota(order.begin(), order.end(), 0);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return lvl[a].bytes > lvl[b].bytes; });
+    std::vector<int64_t> lload(W, 0);
+    for (int idx : order) {
+      int best = 0;
+      for (int w = 1; w < W; ++w)
+        if (lload[w] < lload[best] || (lload[w] == lload[best] && total[w] < total[best])) best = w;
+      lload[best] += lvl[idx].bytes;
+      total[best] += lvl[idx].bytes;
+      queues[best].push_back({lv, lvl[idx]});
+    }
+  }
+  P->tasks.clear(); P->bytes.clear(); P->qoff.assign(W + 1, 0);
+  for (int w = 0; w < W; ++w) {
+    auto& q = queues[w];
+    std::stable_sort(q.begin(), q.end(), [](const auto& a, const auto& b) {
+      return a.first != b.first ? a.first < b.first : a.second.prio < b.second.prio;
+    });
+    P->qoff[w] = (int32_t)P->tasks.size();
+    for (auto& [lv, pr] : q) {
+      Task t = pr.t;
+      t.w[D_ID] = (int32_t)P->tasks.size();
+      P->tasks.push_back(t);
+      P->bytes.push_back(pr.bytes);
+    }
+  }
+  P->qoff[W] = (int32_t)P->tasks.size();
+  return MK_OK;
+}
+
+// ---- validation --------------------------------------------------------------------------
+
+mk_status validate_plan(const mk_plan& P, std::string* why) {
+  const Dims& m = P.m;
+  const int nt = (int)P.tasks.size();
+  std::vector<int> sig(P.n_ctr, 0);
+  std::map<int, std::vector<int>> sig2_groups;      // SIG2 counter -> SIG counters feeding it
+  std::vector<int> prod_level(P.n_ctr, -1);
+  for (auto& t : P.tasks) {
+    const int s = t.w[D_SIG], s2 = t.w[D_SIG2], lv = t.w[D_LEVEL];
+    if (s >= P.n_ctr || s2 >= P.n_ctr || t.w[D_W0] >= P.n_ctr || t.w[D_W1] >= P.n_ctr) { *why = fmt("task %d: counter index out of range", t.w[D_ID]); return MK_ERR_INVALID_ARG; }
+    if (s >= 0) { sig[s]++; prod_level[s] = std::max(prod_level[s], lv); }
+    if (s2 >= 0) {
+      auto& v = sig2_groups[s2];
+      if (std::find(v.begin(), v.end(), s) == v.end()) v.push_back(s);
+      prod_level[s2] = std::max(prod_level[s2], lv);
+    }
+    if (s == P.done_ctr || s2 == P.done_ctr) { *why = "a task signals the end-of-step counter"; return MK_ERR_INVALID_ARG; }
+  }
+  for (auto& [c, v] : sig2_groups) sig[c] += (int)v.size();
+  for (auto& t : P.tasks) {
+    const int waits[3][2] = {{t.w[D_W0], t.w[D_T0]}, {t.w[D_W1], t.w[D_T1]},
+                             {t.w[D_OP] == OP_OUT ? t.w[D_A2] : -1, t.w[D_OP] == OP_OUT ? t.w[D_A3] : 0}};
+    for (auto& wt : waits) {
+      if (wt[0] < 0) continue;
+      if (wt[1] != sig[wt[0]]) { *why = fmt("task %d (op %d) waits for counter %d >= %d but %d signals exist", t.w[D_ID], t.w[D_OP], wt[0], wt[1], sig[wt[0]]); return MK_ERR_INVALID_ARG; }
+      if (prod_level[wt[0]] >= t.w[D_LEVEL]) { *why = fmt("task %d (level %d) depends on counter %d produced at level %d", t.w[D_ID], t.w[D_LEVEL], wt[0], prod_level[wt[0]]); return MK_ERR_INVALID_ARG; }
+    }
+    if (t.w[D_OP] == OP_ROUTER && t.w[D_A2] != sig[t.w[D_SIG]]) { *why = fmt("router task %d expects %d tiles, %d exist", t.w[D_ID], t.w[D_A2], sig[t.w[D_SIG]]); return MK_ERR_INVALID_ARG; }
+    if (t.w[D_OP] == OP_ATTN && (t.w[D_A5] >> 16) != sig[t.w[D_SIG]]) { *why = fmt("attention task %d expects %d splits, %d exist", t.w[D_ID], t.w[D_A5] >> 16, sig[t.w[D_SIG]]); return MK_ERR_INVALID_ARG; }
+  }
+  for (int w = 0; w < P.n_workers; ++w)
+    for (int i = P.qoff[w] + 1; i < P.qoff[w + 1]; ++i)
+      if (P.tasks[i].w[D_LEVEL] < P.tasks[i - 1].w[D_LEVEL]) { *why = fmt("worker %d queue is not level-ordered at task %d", w, i); return MK_ERR_INVALID_ARG; }
+  // coverage: each output written exactly once
+  for (int l = 0; l < m.L; ++l) {
+    std::vector<int> qkv(m.QKVR, 0), out(m.H, 0), rt(m.E, 0);
+    std::map<int, std::vector<int>> gu;
+    std::map<int, std::vector<std::pair<int, int>>> att;
+    for (auto& t : P.tasks) {
+      if (t.w[D_LAYER] != l) continue;
+      switch (t.w[D_OP]) {
+        case OP_QKV: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) qkv[r]++; break;
+        case OP_ROUTER: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) rt[r]++; break;
+        case OP_OUT: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) out[r]++; break;
+        case OP_GATEUP: {
+          auto& v = gu[t.w[D_A0]];
+          v.resize(m.F, 0);
+          for (int f = t.w[D_A1]; f < t.w[D_A1] + t.w[D_A2]; ++f) v[f]++;
+          break;
+        }
+        case OP_ATTN: att[t.w[D_A0] * m.HKV + t.w[D_A1]].push_back({t.w[D_A2], t.w[D_A3]}); break;
+      }
+    }
+    for (int r = 0; r < m.QKVR; ++r) if (qkv[r] != 1) { *why = fmt("layer %d qkv row %d written %d times", l, r, qkv[r]); return MK_ERR_INVALID_ARG; }
+    for (int r = 0; r < m.E; ++r) if (rt[r] != 1) { *why = fmt("layer %d router row %d written %d times", l, r, rt[r]); return MK_ERR_INVALID_ARG; }
+    for (int r = 0; r < m.H; ++r) if (out[r] != 1) { *why = fmt("layer %d output row %d written %d times", l, r, out[r]); return MK_ERR_INVALID_ARG; }
+    if ((int)gu.size() != std::min(m.E, m.K * P.B)) { *why = fmt("layer %d: %zu expert slots", l, gu.size()); return MK_ERR_INVALID_ARG; }
+    for (auto& [u, v] : gu) for (int f = 0; f < m.F; ++f) if (v[f] != 1) { *why = fmt("layer %d slot %d ffn row %d written %d times", l, u, f, v[f]); return MK_ERR_INVALID_ARG; }
+    for (int b = 0; b < P.B; ++b)
+      for (int g = 0; g < m.HKV; ++g) {
+        auto v = att[b * m.HKV + g];
+        std::sort(v.begin(), v.end());
+        int k = 0;
+        for (size_t i = 0; i < v.size(); ++i) {
+          if (v[i].first != k) { *why = fmt("layer %d seq %d group %d: key ranges leave a gap at %d", l, b, g, k); return MK_ERR_INVALID_ARG; }
+          const bool last = i + 1 == v.size();
+          if (last != (v[i].second < 0)) { *why = fmt("layer %d seq %d group %d: only the last split may be open", l, b, g); return MK_ERR_INVALID_ARG; }
+          k = v[i].second;
+        }
+        if (v.empty()) { *why = fmt("layer %d seq %d group %d: no attention", l, b, g); return MK_ERR_INVALID_ARG; }
+      }
+  }
+  if (m.lm) {
+    std::vector<int> rows(m.V, 0);
+    for (auto& t : P.tasks) if (t.w[D_OP] == OP_LMHEAD) for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) rows[r]++;
+    for (int r = 0; r < m.V; ++r) if (rows[r] != 1) { *why = fmt("lm_head row %d written %d times", r, rows[r]); return MK_ERR_INVALID_ARG; }
+  }
+  (void)nt;
+  return MK_OK;
+}
+
+// ---- CPU simulation of the persistent loop -------------------------------------------------
+// Workers advance through their queues in order; at each event a random worker whose next task's
+// waits are satisfied completes it (random interleavings stand in for random latencies). A worker
+// told to stall stops before queue position stall_at. If no worker can move while tasks remain,
+// the simulated watchdog reports the first blocked wait, as the kernel would.
+mk_status simulate_plan(const mk_plan& P, uint64_t seed, int stall_worker, int stall_at, std::string* why) {
+  std::mt19937_64 rng(seed);
+  std::vector<uint32_t> ctr(P.n_ctr, 0);
+  std::vector<int> pos(P.n_workers);
+  for (int w = 0; w < P.n_workers; ++w) pos[w] = P.qoff[w];
+  int remaining = (int)P.tasks.size();
+  auto ready = [&](const Task& t, int* c, uint32_t* tg) {
+    const int waits[3][2] = {{t.w[D_W0], t.w[D_T0]}, {t.w[D_W1], t.w[D_T1]},
+                             {t.w[D_OP] == OP_OUT ? t.w[D_A2] : -1, t.w[D_OP] == OP_OUT ? t.w[D_A3] : 0}};
+    for (auto& wt : waits)
+      if (wt[0] >= 0 && ctr[wt[0]] < (uint32_t)wt[1]) { *c = wt[0]; *tg = (uint32_t)wt[1]; return false; }
+    return true;
+  };
+  std::vector<int> cand;
+  while (remaining > 0) {
+    cand.clear();
+    for (int w = 0; w < P.n_workers; ++w) {
+      if (pos[w] >= P.qoff[w + 1]) continue;
+      if (w == stall_worker && pos[w] - P.qoff[w] >= stall_at) continue;
+      int c; uint32_t tg;
+      if (ready(P.tasks[pos[w]], &c, &tg)) cand.push_back(w);
+    }
+    if (cand.empty()) {
+      for (int w = 0; w < P.n_workers; ++w) {
+        if (pos[w] >= P.qoff[w + 1]) continue;
+        const Task& t = P.tasks[pos[w]];
+        int c = -1; uint32_t tg = 0;
+        if (w == stall_worker && pos[w] - P.qoff[w] >= stall_at) {
+          if (ready(t, &c, &tg)) continue;   // the stalled worker itself is not blocked by a wait
+        }
+        if (!ready(t, &c, &tg)) {
+          *why = fmt("watchdog: worker %d task %d (op %d, layer %d) waits for counter %d >= %u, observed %u",
+                     w, t.w[D_ID], t.w[D_OP], t.w[D_LAYER], c, tg, ctr[c]);
+          return MK_ERR_DEVICE;
+        }
+      }
+      *why = fmt("stalled worker %d holds the remaining %d tasks", stall_worker, remaining);
+      return MK_ERR_DEVICE;
+    }
+    const int w = cand[rng() % cand.size()];
+    const Task& t = P.tasks[pos[w]];
+    if (t.w[D_SIG] >= 0) {
+      const uint32_t old = ctr[t.w[D_SIG]]++;
+      if (t.w[D_SIG2] >= 0) {
+        uint32_t need = 0;
+        if (t.w[D_OP] == OP_ROUTER) need = (uint32_t)t.w[D_A2];
+        if (t.w[D_OP] == OP_ATTN) need = (uint32_t)(t.w[D_A5] >> 16);
+        if (old + 1 == need) ctr[t.w[D_SIG2]]++;
+      }
+    }
+    pos[w]++;
+    remaining--;
+  }
+  return MK_OK;
+}
+
+}  // namespace
+
+// ============================================================================== the engine
+
+struct mk_engine {
+  mk_model_desc desc;
+  Dims m;
+  int shape = -1, n_cu = 0, device = 0;
+  mk_options opt{};
+  LayerPtrs* d_layers = nullptr;
+  double* d_inv_freq = nullptr;
+  float *d_x = nullptr, *d_qkv = nullptr, *d_rlog = nullptr, *d_h = nullptr, *d_attn = nullptr, *d_apart = nullptr;
+  RouteTable* d_route = nullptr;
+  unsigned long long* d_amax = nullptr;
+  uint32_t* d_ctr = nullptr;
+  DevError* d_err = nullptr;
+  int32_t *d_tasks = nullptr, *d_qoff = nullptr;
+  size_t apart_floats = 0, ctr_cap = 0, task_cap = 0, qoff_cap = 0;
+  mk_weight_ptrs w{};
+  mk_plan* plan = nullptr;
+  int steps_since_build = 0;
+  int32_t *argmax_out = nullptr, *topk_out = nullptr;
+  float* hidden_out = nullptr;
+  uint64_t* trace_out = nullptr;
+  hipStream_t last_stream = nullptr;
+  mk_status sticky = MK_OK;
+  std::string msg;
+};
+
+namespace {
+
+mk_status hip_fail(mk_engine* e, hipError_t err, const char* what) {
+  if (e) e->msg = fmt("%s: %s", what, hipGetErrorString(err));
+  return MK_ERR_HIP;
+}
+
+#define HIPCHK(e, call)                                              \
+  do {                                                               \
+    hipError_t err_ = (call);                                        \
+    if (err_ != hipSuccess) return hip_fail((e), err_, #call);       \
+  } while (0)
+
+template <class T>
+hipError_t dalloc(T** p, size_t n) {
+  return hipMalloc(reinterpret_cast<void**>(p), std::max<size_t>(n, 1) * sizeof(T));
+}
+
+void free_all(mk_engine* e) {
+  void* ps[] = {e->d_layers, e->d_inv_freq, e->d_x, e->d_qkv, e->d_rlog, e->d_h, e->d_attn, e->d_apart,
+                e->d_route, e->d_amax, e->d_ctr, e->d_err, e->d_tasks, e->d_qoff};
+  for (void* p : ps) if (p) (void)hipFree(p);
+}
+
+}  // namespace
+
+extern "C" {
+
+mk_status mk_create(const mk_model_desc* desc, const mk_weight_ptrs* w, mk_engine** out) {
+  std::string why;
+  if (!out) return MK_ERR_INVALID_ARG;
+  *out = nullptr;
+  mk_status st = check_desc(desc, &why);
+  if (st != MK_OK) { fprintf(stderr, "mk_create: %s\n", why.c_str()); return st; }
+  if (!w || !w->embed || !w->final_norm || !w->attn_norm || !w->w_qkv || !w->w_o || !w->w_router || !w->w_gate ||
+      !w->w_up || !w->w_down || !w->k_cache || !w->v_cache || (desc->has_lm_head && !w->lm_head) ||
+      (desc->has_router_bias && !w->router_bias)) {
+    fprintf(stderr, "mk_create: a required weight pointer is NULL\n");
+    return MK_ERR_INVALID_ARG;
+  }
+  const int L = desc->n_layers;
+  for (int l = 0; l < L; ++l)
+    if (!w->attn_norm[l] || !w->w_qkv[l] || !w->w_o[l] || !w->w_router[l] || !w->w_gate[l] || !w->w_up[l] ||
+        !w->w_down[l] || !w->k_cache[l] || !w->v_cache[l] || (desc->has_router_bias && !w->router_bias[l])) {
+      fprintf(stderr, "mk_create: layer %d has a NULL weight pointer\n", l);
+      return MK_ERR_INVALID_ARG;
+    }
+  mk_engine* e = new mk_engine();
+  e->desc = *desc;
+  e->m = dims_of(*desc);
+  e->w = *w;
+  e->shape = shape_id(desc->hidden, desc->head_dim, desc->n_q_heads, desc->n_kv_heads, desc->n_experts, desc->top_k, desc->expert_ffn);
+  e->opt.workers_per_cu = 2;
+  e->opt.watchdog_ms = 2000;
+  auto fail = [&](mk_status s) { free_all(e); delete e; return s; };
+  hipDeviceProp_t prop;
+  if (hipGetDevice(&e->device) != hipSuccess || hipGetDeviceProperties(&prop, e->device) != hipSuccess) {
+    fprintf(stderr, "mk_create: no HIP device\n");
+    return fail(MK_ERR_HIP);
+  }
+  e->n_cu = prop.multiProcessorCount;
+  const Dims& m = e->m;
+  std::vector<LayerPtrs> lp(L);
+  for (int l = 0; l < L; ++l) {
+    lp[l].attn_norm = (const uint16_t*)w->attn_norm[l];
+    lp[l].w_qkv = (const uint16_t*)w->w_qkv[l];
+    lp[l].w_o = (const uint16_t*)w->w_o[l];
+    lp[l].w_router = (const uint16_t*)w->w_router[l];
+    lp[l].router_bias = desc->has_router_bias ? w->router_bias[l] : nullptr;
+    lp[l].w_gate = (const uint16_t*)w->w_gate[l];
+    lp[l].w_up = (const uint16_t*)w->w_up[l];
+    lp[l].w_down = (const uint16_t*)w->w_down[l];
+    lp[l].k_cache = (uint16_t*)w->k_cache[l];
+    lp[l].v_cache = (uint16_t*)w->v_cache[l];
+  }
+  std::vector<double> inv(m.D / 2);
+  for (int i = 0; i < m.D / 2; ++i) inv[i] = std::pow((double)desc->rope_theta, -2.0 * i / m.D);
+  bool ok = dalloc(&e->d_layers, L) == hipSuccess && dalloc(&e->d_inv_freq, m.D / 2) == hipSuccess &&
+            dalloc(&e->d_x, (size_t)(L + 1) * MAXB * m.H) == hipSuccess &&
+            dalloc(&e->d_qkv, (size_t)L * MAXB * m.QKVR) == hipSuccess &&
+            dalloc(&e->d_rlog, (size_t)L * MAXB * m.E) == hipSuccess &&
+            dalloc(&e->d_h, (size_t)L * MAXB * m.K * m.F) == hipSuccess &&
+            dalloc(&e->d_attn, (size_t)L * MAXB * m.AD) == hipSuccess &&
+            dalloc(&e->d_route, (size_t)L) == hipSuccess && dalloc(&e->d_amax, MAXB) == hipSuccess &&
+            dalloc(&e->d_err, 1) == hipSuccess;
+  if (!ok) { fprintf(stderr, "mk_create: out of device memory\n"); return fail(MK_ERR_OOM); }
+  if (hipMemcpy(e->d_layers, lp.data(), sizeof(LayerPtrs) * L, hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(e->d_inv_freq, inv.data(), sizeof(double) * inv.size(), hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemset(e->d_amax, 0, sizeof(unsigned long long) * MAXB) != hipSuccess ||
+      hipMemset(e->d_err, 0, sizeof(DevError)) != hipSuccess ||
+      hipMemset(e->d_x, 0, sizeof(float) * (size_t)(L + 1) * MAXB * m.H) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess) {
+    fprintf(stderr, "mk_create: HIP copy failed\n");
+    return fail(MK_ERR_HIP);
+  }
+  *out = e;
+  return MK_OK;
+}
+
+mk_status mk_set_options(mk_engine* e, const mk_options* o) {
+  if (!e || !o) return MK_ERR_INVALID_ARG;
+  if (o->workers_per_cu < 0 || o->workers_per_cu > 4 || o->split_keys < 0 || o->watchdog_ms < 0) {
+    e->msg = "options out of range";
+    return MK_ERR_INVALID_ARG;
+  }
+  if (o->workers_per_cu) e->opt.workers_per_cu = o->workers_per_cu;
+  e->opt.split_keys = o->split_keys;
+  if (o->watchdog_ms) e->opt.watchdog_ms = o->watchdog_ms;
+  e->opt.flags = o->flags;
+  return MK_OK;
+}
+
+mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens_host) {
+  if (!e || !seq_lens_host || batch < 1 || batch > e->desc.max_batch) {
+    if (e) e->msg = "mk_build_schedule: bad batch or seq_lens";
+    return MK_ERR_INVALID_ARG;
+  }
+  int per_cu = 0;
+  HIPCHK(e, step_occupancy(e->shape, batch, &per_cu));
+  const int wpc = std::min(e->opt.workers_per_cu, per_cu);
+  if (wpc < 1) { e->msg = "kernel does not fit on a CU"; return MK_ERR_UNSUPPORTED; }
+  mk_plan* P = new mk_plan();
+  std::string why;
+  mk_status st = build_plan(e->desc, batch, seq_lens_host, e->n_cu * wpc, e->opt.split_keys, P, &why);
+  if (st == MK_OK) st = validate_plan(*P, &why);
+  if (st != MK_OK) { e->msg = "mk_build_schedule: " + why; delete P; return st; }
+  // (re)size device buffers that depend on the schedule
+  HIPCHK(e, hipDeviceSynchronize());
+  const size_t ntask = P->tasks.size(), nq = P->qoff.size(), nctr = P->n_ctr;
+  const size_t napart = (size_t)e->m.L * P->parts_per_layer * e->m.PART;
+  if (ntask > e->task_cap) { if (e->d_tasks) (void)hipFree(e->d_tasks); e->d_tasks = nullptr; HIPCHK(e, dalloc(&e->d_tasks, ntask * DESC_WORDS)); e->task_cap = ntask; }
+  if (nq > e->qoff_cap) { if (e->d_qoff) (void)hipFree(e->d_qoff); e->d_qoff = nullptr; HIPCHK(e, dalloc(&e->d_qoff, nq)); e->qoff_cap = nq; }
+  if (nctr > e->ctr_cap) { if (e->d_ctr) (void)hipFree(e->d_ctr); e->d_ctr = nullptr; HIPCHK(e, dalloc(&e->d_ctr, nctr)); e->ctr_cap = nctr; }
+  if (napart > e->apart_floats) { if (e->d_apart) (void)hipFree(e->d_apart); e->d_apart = nullptr; HIPCHK(e, dalloc(&e->d_apart, napart)); e->apart_floats = napart; }
+  HIPCHK(e, hipMemcpy(e->d_tasks, P->tasks.data(), ntask * sizeof(Task), hipMemcpyHostToDevice));
+  HIPCHK(e, hipMemcpy(e->d_qoff, P->qoff.data(), nq * sizeof(int32_t), hipMemcpyHostToDevice));
+  HIPCHK(e, hipMemset(e->d_ctr, 0, e->ctr_cap * sizeof(uint32_t)));
+  HIPCHK(e, hipDeviceSynchronize());
+  delete e->plan;
+  e->plan = P;
+  e->steps_since_build = 0;
+  return MK_OK;
+}
+
+mk_status mk_set_step_outputs(mk_engine* e, int32_t* argmax_out, int32_t* topk_out, float* hidden_out, uint64_t* trace_out) {
+  if (!e) return MK_ERR_INVALID_ARG;
+  e->argmax_out = argmax_out; e->topk_out = topk_out; e->hidden_out = hidden_out; e->trace_out = trace_out;
+  return MK_OK;
+}
+
+mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* positions, const int32_t* block_tables,
+                         const int32_t* seq_lens, float* logits_out, void* stream) {
+  if (!e) return MK_ERR_INVALID_ARG;
+  if (e->sticky != MK_OK) return e->sticky;
+  if (!tokens || !positions || !block_tables || !seq_lens || (e->desc.has_lm_head && !logits_out)) {
+    e->msg = "mk_decode_step: NULL input";
+    return MK_ERR_INVALID_ARG;
+  }
+  if (!e->plan) { e->msg = "mk_decode_step: no schedule"; return MK_ERR_NO_SCHEDULE; }
+  const mk_plan& P = *e->plan;
+  for (int b = 0; b < P.B; ++b)
+    if (P.seq_lens[b] + e->steps_since_build > P.capacity[b]) {
+      e->msg = fmt("sequence %d would reach length %d, beyond the schedule's capacity %d", b,
+                   P.seq_lens[b] + e->steps_since_build, P.capacity[b]);
+      return MK_ERR_SCHEDULE_STALE;
+    }
+  Params p{};
+  p.layers = e->d_layers; p.embed = (const uint16_t*)e->w.embed; p.lm_head = (const uint16_t*)e->w.lm_head;
+  p.final_norm = (const uint16_t*)e->w.final_norm; p.inv_freq = e->d_inv_freq;
+  p.x = e->d_x; p.qkv = e->d_qkv; p.rlog = e->d_rlog; p.route = e->d_route; p.h = e->d_h; p.apart = e->d_apart;
+  p.attn = e->d_attn; p.amax = e->d_amax; p.ctr = e->d_ctr; p.err = e->d_err;
+  p.tasks = e->d_tasks; p.qoff = e->d_qoff;
+  p.tokens = tokens; p.positions = positions; p.block_tables = block_tables; p.seq_lens = seq_lens;
+  p.logits = e->desc.has_lm_head ? logits_out : nullptr;
+  p.argmax_out = e->desc.has_lm_head ? e->argmax_out : nullptr;
+  p.topk_out = e->topk_out; p.hidden_out = e->hidden_out;
+  p.trace = (unsigned long long*)e->trace_out;
+  p.L = e->m.L; p.V = e->m.V; p.B = P.B; p.max_pages = e->desc.max_pages_per_seq; p.num_pages = e->desc.num_pages;
+  p.parts_per_layer = P.parts_per_layer; p.n_workers = P.n_workers; p.n_ctr = P.n_ctr; p.done_ctr = P.done_ctr;
+  p.flags = e->opt.flags; p.has_lm_head = e->desc.has_lm_head; p.has_bias = e->desc.has_router_bias;
+  p.eps = e->desc.rms_eps;
+  p.watchdog_ticks = (uint64_t)e->opt.watchdog_ms * 100000ull;
+  hipStream_t st = (hipStream_t)stream;
+  size_t lds = 0;
+  hipError_t err = launch_step(e->shape, P.B, p, P.n_workers, st, &lds);
+  if (err != hipSuccess) return hip_fail(e, err, "cooperative launch");
+  e->last_stream = st;
+  e->steps_since_build++;
+  return MK_OK;
+}
+
+static mk_status read_device_error(mk_engine* e) {
+  DevError de{};
+  HIPCHK(e, hipStreamSynchronize(e->last_stream));
+  HIPCHK(e, hipMemcpy(&de, e->d_err, sizeof de, hipMemcpyDeviceToHost));
+  if (de.code != DEV_OK) {
+    static const char* names[] = {"ok", "dependency wait timed out (watchdog)", "position != seq_len - 1",
+                                  "page id out of range", "sequence outgrew its attention split",
+                                  "token id out of range", "bad opcode"};
+    const char* nm = de.code < 7 ? names[de.code] : "unknown";
+    e->msg = fmt("device fault: %s (task %u, worker %u, counter %d, target %u, observed %u, detail %u)", nm, de.task,
+                 de.worker, (int)de.counter, de.target, de.observed, de.detail);
+    e->sticky = MK_ERR_DEVICE;
+    return MK_ERR_DEVICE;
+  }
+  return MK_OK;
+}
+
+mk_status mk_sync(mk_engine* e) {
+  if (!e) return MK_ERR_INVALID_ARG;
+  if (e->sticky != MK_OK) return e->sticky;
+  return read_device_error(e);
+}
+
+mk_status mk_get_error(mk_engine* e, char* buf, size_t n) {
+  if (!e) { put(buf, n, "NULL engine"); return MK_ERR_INVALID_ARG; }
+  mk_status s = e->sticky != MK_OK ? e->sticky : read_device_error(e);
+  put(buf, n, e->msg);
+  return s;
+}
+
+mk_status mk_reset(mk_engine* e) {
+  if (!e) return MK_ERR_INVALID_ARG;
+  HIPCHK(e, hipDeviceSynchronize());
+  HIPCHK(e, hipMemset(e->d_err, 0, sizeof(DevError)));
+  if (e->d_ctr) HIPCHK(e, hipMemset(e->d_ctr, 0, e->ctr_cap * sizeof(uint32_t)));
+  HIPCHK(e, hipMemset(e->d_amax, 0, sizeof(unsigned long long) * MAXB));
+  HIPCHK(e, hipDeviceSynchronize());
+  e->sticky = MK_OK;
+  e->msg.clear();
+  return MK_OK;
+}
+
+void mk_destroy(mk_engine* e) {
+  if (!e) return;
+  (void)hipDeviceSynchronize();
+  free_all(e);
+  delete e->plan;
+  delete e;
+}
+
+// ---- host-only schedule API ---------------------------------------------------------------
+
+mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* seq_lens_host, int32_t n_workers,
+                        int32_t split_keys, mk_plan** out) {
+  std::string why;
+  if (!out) return MK_ERR_INVALID_ARG;
+  *out = nullptr;
+  mk_status st = check_desc(desc, &why);
+  if (st != MK_OK) { fprintf(stderr, "mk_plan_build: %s\n", why.c_str()); return st; }
+  if (!seq_lens_host || batch < 1 || batch > desc->max_batch || n_workers < 1 || split_keys < 0) return MK_ERR_INVALID_ARG;
+  mk_plan* P = new mk_plan();
+  st = build_plan(*desc, batch, seq_lens_host, n_workers, split_keys, P, &why);
+  if (st != MK_OK) { fprintf(stderr, "mk_plan_build: %s\n", why.c_str()); delete P; return st; }
+  *out = P;
+  return MK_OK;
+}
+
+mk_status mk_plan_info_get(const mk_plan* P, mk_plan_info* info) {
+  if (!P || !info) return MK_ERR_INVALID_ARG;
+  info->n_tasks = (int32_t)P->tasks.size();
+  info->n_workers = P->n_workers;
+  info->n_counters = P->n_ctr;
+  info->max_queue = 0;
+  std::vector<int64_t> per(P->n_workers, 0);
+  for (int w = 0; w < P->n_workers; ++w) {
+    info->max_queue = std::max(info->max_queue, P->qoff[w + 1] - P->qoff[w]);
+    for (int i = P->qoff[w]; i < P->qoff[w + 1]; ++i) per[w] += P->bytes[i];
+  }
+  info->bytes_total = std::accumulate(per.begin(), per.end(), (int64_t)0);
+  info->bytes_max_worker = *std::max_element(per.begin(), per.end());
+  info->n_attn_splits = P->n_attn;
+  info->key_capacity_min = *std::min_element(P->capacity.begin(), P->capacity.end());
+  return MK_OK;
+}
+
+mk_status mk_plan_export(const mk_plan* P, int32_t* tasks, int32_t* qoff) {
+  if (!P) return MK_ERR_INVALID_ARG;
+  if (tasks) memcpy(tasks, P->tasks.data(), P->tasks.size() * sizeof(Task));
+  if (qoff) memcpy(qoff, P->qoff.data(), P->qoff.size() * sizeof(int32_t));
+  return MK_OK;
+}
+
+mk_status mk_plan_validate(const mk_plan* P, char* buf, size_t n) {
+  if (!P) return MK_ERR_INVALID_ARG;
+  std::string why;
+  mk_status st = validate_plan(*P, &why);
+  put(buf, n, st == MK_OK ? "ok" : why);
+  return st;
+}
+
+mk_status mk_plan_simulate(const mk_plan* P, uint64_t seed, int32_t stall_worker, int32_t stall_at, char* buf, size_t n) {
+  if (!P) return MK_ERR_INVALID_ARG;
+  std::string why;
+  mk_status st = simulate_plan(*P, seed, stall_worker, stall_at, &why);
+  put(buf, n, st == MK_OK ? "ok" : why);
+  return st;
+}
+
+const mk_plan* mk_engine_plan(const mk_engine* e) { return e ? e->plan : nullptr; }
+
+void mk_plan_destroy(mk_plan* P) { delete P; }
+
+}  // extern "C"

@@ -1,0 +1,1079 @@
+// The persistent decode megakernel for gfx950 (MI355X).
+//
+// One launch runs a whole decode step (P1 "One persistent kernel for the whole decode step"):
+// every resident workgroup ("worker", 256 threads = 4 wave64s; two per CU) walks its own queue of
+// 64-byte task descriptors built by the host (P3 "Key Technologies and Architecture": a task list
+// in global memory), waits on per-producer counters in HBM instead of kernel boundaries, runs the
+// task and bumps the counter of what it produced.
+//
+// Hand-off protocol (measured on MI355X: an agent-scope release fence writes back the whole L2 and
+// costs ~12 us inside a streaming loop, so it is never used):
+//   producer: outputs written with sc1 (agent-coherent, write-through) buffer stores;
+//             s_waitcnt vmcnt(0) in every wave; workgroup barrier; one relaxed atomic add.
+//   consumer: thread 0 polls the counter with relaxed agent-scope loads (s_sleep backoff, bounded
+//             by a watchdog); workgroup barrier; hand-off data read with sc1 buffer loads.
+// Weights are activation-independent, so each task issues its first block of weight loads BEFORE
+// waiting on its dependencies (P1: weights stream while the producers finish).
+//
+// Numerics: activations stay float32 everywhere; dot products use explicit fmaf in a fixed order;
+// no float atomics, so a step is bitwise deterministic whatever the timing. The file is compiled
+// with -ffp-contract=off so that the non-dot arithmetic rounds exactly as written.
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "mk_internal.h"
+#include "mk_launch.h"
+
+namespace mk {
+
+typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+typedef float f4 __attribute__((ext_vector_type(4)));
+
+template <int H_, int D_, int HQ_, int HKV_, int E_, int K_, int F_>
+struct Shape {
+  static constexpr int H = H_, D = D_, HQ = HQ_, HKV = HKV_, E = E_, K = K_, F = F_;
+  static constexpr int HPG = HQ / HKV;           // query heads per KV head (GQA group)
+  static constexpr int QKVR = (HQ + 2 * HKV) * D;
+  static constexpr int AD = HQ * D;              // attention output width
+  static constexpr int PART = HPG * (D + 2);     // one attention partial: m[HPG] l[HPG] o[HPG][D]
+};
+using ShapeSmall = Shape<256, 32, 8, 2, 8, 2, 128>;
+using ShapeFull = Shape<2048, 128, 32, 4, 128, 8, 768>;
+
+constexpr int SPLIT_MAX = 1024;   // keys one attention task may cover (LDS score buffer)
+constexpr int OUT_MAXR = 4;       // rows of one OUT task
+constexpr int SC1 = 16;           // buffer cache-policy bit for agent-coherent access
+
+// ------------------------------------------------------------------------------ primitives
+
+// Every op is a separate (non-inlined) function so that registers are allocated per op. They reach
+// the kernel parameters through the kernarg segment pointer (scalar loads) and use file-scope LDS.
+extern __shared__ __align__(16) float smem[];
+typedef const __attribute__((address_space(4))) Params CParams;
+
+__device__ __forceinline__ CParams& P() {
+#if defined(__HIP_DEVICE_COMPILE__)
+  // laundered so that each op re-reads its parameters instead of keeping them live across ops
+  uint64_t a = reinterpret_cast<uint64_t>(__builtin_amdgcn_kernarg_segment_ptr());
+  asm volatile("" : "+s"(a));
+  return *reinterpret_cast<CParams*>(a);
+#else
+  return *reinterpret_cast<CParams*>(0);
+#endif
+}
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7FFFFFFF, 0x00020000);
+}
+__device__ __forceinline__ float ldc(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, SC1));
+}
+__device__ __forceinline__ int32_t ldci(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(int32_t, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, SC1));
+}
+__device__ __forceinline__ f4 ldc4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, SC1));
+}
+__device__ __forceinline__ void stc(__amdgpu_buffer_rsrc_t r, uint32_t off, float v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, SC1);
+}
+__device__ __forceinline__ void stci(__amdgpu_buffer_rsrc_t r, uint32_t off, int32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v), r, off, 0, SC1);
+}
+__device__ __forceinline__ void stc4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, SC1);
+}
+typedef const __attribute__((address_space(1))) u4 gu4;
+__device__ __forceinline__ u4 ldw(const void* p) {   // streamed weight / KV load (global memory)
+  return __builtin_nontemporal_load((gu4*)p);
+}
+__device__ __forceinline__ uint32_t ctr_load(const uint32_t* c) {
+  return __hip_atomic_load(c, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ctr_add(uint32_t* c, uint32_t v) {
+  return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
+
+__device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf1(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ uint32_t f2bf(float f) {   // round to nearest even
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
+  return ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16) & 0xffffu;
+}
+
+// acc += sum_m w[m] * a[m] over the 8 bf16 of w, in element order
+__device__ __forceinline__ float dot8(u4 w, f4 a0, f4 a1, float acc) {
+  acc = __builtin_fmaf(bf_lo(w.x), a0.x, acc);
+  acc = __builtin_fmaf(bf_hi(w.x), a0.y, acc);
+  acc = __builtin_fmaf(bf_lo(w.y), a0.z, acc);
+  acc = __builtin_fmaf(bf_hi(w.y), a0.w, acc);
+  acc = __builtin_fmaf(bf_lo(w.z), a1.x, acc);
+  acc = __builtin_fmaf(bf_hi(w.z), a1.y, acc);
+  acc = __builtin_fmaf(bf_lo(w.w), a1.z, acc);
+  acc = __builtin_fmaf(bf_hi(w.w), a1.w, acc);
+  return acc;
+}
+
+template <int N>
+__device__ __forceinline__ float wsum(float v) {   // sum over aligned groups of N lanes
+#pragma unroll
+  for (int m = 1; m < N; m <<= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+template <int N>
+__device__ __forceinline__ float wmax(float v) {
+#pragma unroll
+  for (int m = 1; m < N; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+// ------------------------------------------------------------------------------ control
+
+struct Ctl {            // small per-worker control block in static LDS
+  int ok;
+  int flag;
+  int toks[MAXB];       // batch rows of the tokens a task works on
+  int bis[MAXB];        // (b << 8) | i of those tokens (expert slices)
+};
+__shared__ Ctl ctl_s;
+
+__device__ void raise_error(CParams& p, uint32_t code, int task, int ctr, uint32_t target,
+                            uint32_t observed, uint32_t detail) {
+  uint32_t prev = atomicCAS(&p.err->code, 0u, code);
+  if (prev == 0) {
+    __hip_atomic_store(&p.err->task, (uint32_t)task, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.err->worker, (uint32_t)blockIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.err->counter, (uint32_t)ctr, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.err->target, target, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.err->observed, observed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&p.err->detail, detail, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __hip_atomic_store(&p.err->abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Block until counter c >= target (thread 0 polls, the workgroup waits at a barrier). Returns false
+// if the step was aborted or this wait exceeded the watchdog (which then aborts the step).
+__device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) {
+  if (c < 0) return true;
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    uint32_t v = ctr_load(p.ctr + c);
+    if (v < target) {
+      const uint64_t t0 = now();
+      uint32_t it = 0;
+      for (;;) {
+        __builtin_amdgcn_s_sleep(1);
+        v = ctr_load(p.ctr + c);
+        if (v >= target) break;
+        if ((++it & 15u) == 0) {
+          if (ctr_load(&p.err->abort_flag)) { ok = 0; break; }
+          if (now() - t0 > p.watchdog_ticks) {
+            raise_error(p, DEV_TIMEOUT, task, c, target, v, 0);
+            ok = 0;
+            break;
+          }
+        }
+      }
+    }
+    ctl.ok = ok;
+  }
+  __syncthreads();
+  const bool ok = ctl.ok != 0;
+  __syncthreads();
+  return ok;
+}
+
+// Make this worker's sc1 stores visible, then bump counter c. Returns the counter's old value
+// (meaningful on thread 0 only; broadcast through ctl.flag when `want_old`).
+__device__ uint32_t signal(CParams& p, Ctl& ctl, int c, bool want_old) {
+  drain();
+  __syncthreads();
+  uint32_t old = 0;
+  if (threadIdx.x == 0 && c >= 0) {
+    old = ctr_add(p.ctr + c, 1u);
+    if (want_old) ctl.flag = (int)old;
+  }
+  if (want_old) {
+    __syncthreads();
+    old = (uint32_t)ctl.flag;
+    __syncthreads();
+  }
+  return old;
+}
+
+__device__ __forceinline__ bool aborted(CParams& p) { return ctr_load(&p.err->abort_flag) != 0; }
+
+// ------------------------------------------------------------------------------ GEMV engine
+//
+// A wave multiplies rows of a bf16 matrix (row length KD) with float32 activations held in LDS.
+// LPR lanes cover one row; each lane owns CPL 16-byte chunks of the row (chunk lir + j*LPR), so
+// every load instruction of a wave reads whole contiguous row segments. A "pass" is RPP rows;
+// passes are dealt round-robin to the 4 waves; a "block" is NP passes per wave, double-buffered in
+// registers so the next block's loads are in flight while the current one is multiplied.
+
+template <int KD>
+struct Geo {
+  static constexpr int CPR = KD / 8;
+  static constexpr int LPR = (CPR % 64 == 0) ? 64 : (CPR % 32 == 0) ? 32 : (CPR % 16 == 0) ? 16 : 8;
+  static constexpr int RPP = 64 / LPR;
+  static constexpr int CPL = CPR / LPR;
+  static_assert(CPR % LPR == 0, "row length must be a multiple of 8*LPR");
+};
+
+template <int KD, int NP>
+struct WBuf {
+  u4 w[NP][Geo<KD>::CPL];
+};
+
+template <int KD, int NP>
+__device__ __forceinline__ int block_rows() { return NP * NWAVE * Geo<KD>::RPP; }
+
+// RowPtr(r) -> const uint16_t* start of row r (only called for r < nrows)
+template <int KD, int NP, class RowPtr>
+__device__ __forceinline__ void load_block(WBuf<KD, NP>& b, int blk, int nrows, RowPtr rowptr) {
+  using G = Geo<KD>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rip = lane / G::LPR, lir = lane % G::LPR;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
+    if (r < nrows) {
+      const uint16_t* src = rowptr(r) + 8 * lir;
+#pragma unroll
+      for (int j = 0; j < G::CPL; ++j) b.w[i][j] = ldw(src + 8 * G::LPR * j);
+    } else {
+#pragma unroll
+      for (int j = 0; j < G::CPL; ++j) b.w[i][j] = u4{0u, 0u, 0u, 0u};
+    }
+  }
+}
+
+// ActOf(r, t) -> const float* LDS activations (KD floats) for row r, token t
+// Emit(r, t, value) is called on the lane with lir == 0 of each row (value = full dot product)
+template <int KD, int NP, int TB, class ActOf, class Emit>
+__device__ __forceinline__ void compute_block(const WBuf<KD, NP>& b, int blk, int nrows, int ntok,
+                                              ActOf act_of, Emit emit) {
+  using G = Geo<KD>;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rip = lane / G::LPR, lir = lane % G::LPR;
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
+    const int rr = r < nrows ? r : 0;
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      if (t < ntok) {
+        const float* a = act_of(rr, t) + 8 * lir;
+        float acc = 0.f;
+#pragma unroll
+        for (int j = 0; j < G::CPL; ++j) {
+          const f4* ap = reinterpret_cast<const f4*>(a + 8 * G::LPR * j);
+          acc = dot8(b.w[i][j], ap[0], ap[1], acc);
+        }
+        acc = wsum<G::LPR>(acc);
+        if (lir == 0 && r < nrows) emit(r, t, acc);
+      }
+    }
+  }
+}
+
+// Stream `nrows` rows; block 0 may already be loaded into A (prefetched before a dependency wait).
+template <int KD, int NP, int TB, class RowPtr, class ActOf, class Emit>
+__device__ __forceinline__ void gemv_stream(WBuf<KD, NP>& A, bool a_loaded, int nrows, int ntok,
+                                            RowPtr rowptr, ActOf act_of, Emit emit) {
+  const int nblk = (nrows + block_rows<KD, NP>() - 1) / block_rows<KD, NP>();
+  WBuf<KD, NP> B;
+  if (!a_loaded) load_block<KD, NP>(A, 0, nrows, rowptr);
+  for (int blk = 0; blk < nblk; blk += 2) {
+    if (blk + 1 < nblk) load_block<KD, NP>(B, blk + 1, nrows, rowptr);
+    compute_block<KD, NP, TB>(A, blk, nrows, ntok, act_of, emit);
+    if (blk + 1 < nblk) {
+      if (blk + 2 < nblk) load_block<KD, NP>(A, blk + 2, nrows, rowptr);
+      compute_block<KD, NP, TB>(B, blk + 1, nrows, ntok, act_of, emit);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------ norm staging
+
+// act[t][H] = RMSNorm(x_l[b_t]) * gain for the listed tokens (P1: one shared normed input per
+// layer). x_0 is the token's embedding row; x_l (l >= 1) comes from the previous layer's OUT
+// tasks. One wave per token: each lane sums H/64 squares, then a wave tree.
+template <class S>
+__device__ void stage_norm(CParams& p, int l, const int* toks, int ntok, const uint16_t* gain,
+                           float* act, int task) {
+  constexpr int H = S::H;
+  constexpr int G4 = H / 256;            // groups of 4 consecutive floats per lane
+  static_assert(H % 256 == 0, "");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int t = wave; t < ntok; t += NWAVE) {
+    const int b = toks[t];
+    float v[4 * G4];
+    if (l == 0) {
+      int tok = p.tokens[b];
+      if (tok < 0 || tok >= p.V) {
+        if (lane == 0) raise_error(p, DEV_BAD_TOKEN, task, -1, 0, (uint32_t)tok, (uint32_t)b);
+        tok = 0;
+      }
+      const uint16_t* row = p.embed + (size_t)tok * H;
+#pragma unroll
+      for (int k = 0; k < G4; ++k) {
+        const uint2 w = *reinterpret_cast<const uint2*>(row + 4 * lane + 256 * k);
+        v[4 * k + 0] = bf_lo(w.x); v[4 * k + 1] = bf_hi(w.x);
+        v[4 * k + 2] = bf_lo(w.y); v[4 * k + 3] = bf_hi(w.y);
+      }
+    } else {
+      const __amdgpu_buffer_rsrc_t X = rsrc(p.x + ((size_t)l * MAXB + b) * H);
+#pragma unroll
+      for (int k = 0; k < G4; ++k) {
+        const f4 a = ldc4(X, 4u * (4 * lane + 256 * k));
+        v[4 * k + 0] = a.x; v[4 * k + 1] = a.y; v[4 * k + 2] = a.z; v[4 * k + 3] = a.w;
+      }
+    }
+    float ss = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4 * G4; ++k) ss = __builtin_fmaf(v[k], v[k], ss);
+    ss = wsum<64>(ss);
+    const float denom = sqrtf(ss / (float)H + p.eps);
+#pragma unroll
+    for (int k = 0; k < G4; ++k) {
+      const uint2 g = *reinterpret_cast<const uint2*>(gain + 4 * lane + 256 * k);
+      const float gg[4] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y)};
+      f4 o;
+      o.x = (v[4 * k + 0] / denom) * gg[0];
+      o.y = (v[4 * k + 1] / denom) * gg[1];
+      o.z = (v[4 * k + 2] / denom) * gg[2];
+      o.w = (v[4 * k + 3] / denom) * gg[3];
+      *reinterpret_cast<f4*>(act + (size_t)t * H + 4 * lane + 256 * k) = o;
+    }
+  }
+  __syncthreads();
+}
+
+// ------------------------------------------------------------------------------ ops
+
+struct TaskHdr {
+  int id, op, layer, a0, a1, a2, a3, a4, a5, w0, t0, w1, t1, sig, sig2;
+};
+
+// Fields of task `ti` (uniform: the descriptor is read with scalar loads).
+__device__ __forceinline__ TaskHdr read_task(CParams& p, int ti) {
+  ti = __builtin_amdgcn_readfirstlane(ti);
+  const int32_t* d = p.tasks + (size_t)ti * DESC_WORDS;
+  TaskHdr T;
+  T.id = ti;
+  T.op = d[D_OP]; T.layer = d[D_LAYER];
+  T.a0 = d[D_A0]; T.a1 = d[D_A1]; T.a2 = d[D_A2]; T.a3 = d[D_A3]; T.a4 = d[D_A4]; T.a5 = d[D_A5];
+  T.w0 = d[D_W0]; T.t0 = d[D_T0]; T.w1 = d[D_W1]; T.t1 = d[D_T1];
+  T.sig = d[D_SIG]; T.sig2 = d[D_SIG2];
+  return T;
+}
+
+// QKV rows (any contiguous range inside one KV group's q, k or v rows).
+template <class S, int TB>
+__device__ __forceinline__ bool op_qkv(int task) {
+  CParams& p = P();
+  Ctl& ctl = ctl_s;
+  float* sm = smem;
+  const TaskHdr T = read_task(p, task);
+  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
+  const LayerPtrs& Lp = p.layers[T.layer];
+  const int row0 = T.a0, nrows = T.a1;
+  auto rowptr = [&](int r) { return Lp.w_qkv + (size_t)(row0 + r) * H; };
+  WBuf<H, NP> A;
+  const bool pre = !(p.flags & 2);
+  if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+  if (threadIdx.x < MAXB) ctl.toks[threadIdx.x] = threadIdx.x;
+  __syncthreads();
+  stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
+  const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + (size_t)T.layer * MAXB * S::QKVR);
+  gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
+      [&](int r, int t) { return sm + (size_t)t * H; },
+      [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); });
+  signal(p, ctl, T.sig, false);
+  return true;
+}
+
+// Routing decision of layer l for the whole batch, computed by the last router tile (R7 of the
+// oracle's readings): top-k of the raw logits with ties to the lower index, softmax over the k
+// selected, the union of experts over the batch and each union slot's token list.
+template <class S>
+__device__ __forceinline__ void compute_route(CParams& p, int l, float* sm) {
+  constexpr int E = S::E, K = S::K;
+  const int B = p.B;
+  float* rl = sm;                                          // [B][E] logits
+  int* selflag = reinterpret_cast<int*>(sm + MAXB * E);    // [B][E] 1 if selected
+  int* posi = selflag + MAXB * E;                          // [B][E] rank among the selected (ascending e)
+  int* used = posi + MAXB * E;                             // [E] selected by any token
+  const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)l * MAXB * E);
+  for (int i = threadIdx.x; i < B * E; i += NT) rl[i] = ldc(R, 4u * i);
+  __syncthreads();
+  for (int i = threadIdx.x; i < B * E; i += NT) {
+    const int b = i / E, e = i % E;
+    const float re = rl[i];
+    int rank = 0;
+    for (int f = 0; f < E; ++f) {
+      const float rf = rl[b * E + f];
+      rank += (rf > re || (rf == re && f < e)) ? 1 : 0;
+    }
+    selflag[i] = rank < K ? 1 : 0;
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < B * E; i += NT) {
+    const int b = i / E, e = i % E;
+    int c = 0;
+    for (int f = 0; f < e; ++f) c += selflag[b * E + f];
+    posi[i] = c;
+  }
+  for (int e = threadIdx.x; e < E; e += NT) {
+    int u = 0;
+    for (int b = 0; b < B; ++b) u |= selflag[b * E + e];
+    used[e] = u;
+  }
+  __syncthreads();
+  RouteTable* rt = p.route + l;
+  const __amdgpu_buffer_rsrc_t RT = rsrc(rt);
+  // selected experts of each token in ascending order, with their softmax weights
+  if (threadIdx.x < B) {
+    const int b = threadIdx.x;
+    int sel[8];
+    int n = 0;
+    for (int e = 0; e < E && n < K; ++e)
+      if (selflag[b * E + e]) sel[n++] = e;
+    float m = -INFINITY;
+    for (int i = 0; i < K; ++i) m = fmaxf(m, rl[b * E + sel[i]]);
+    float ex[8], sum = 0.f;
+    for (int i = 0; i < K; ++i) { ex[i] = expf(rl[b * E + sel[i]] - m); sum += ex[i]; }
+    for (int i = 0; i < K; ++i) {
+      stci(RT, (uint32_t)offsetof(RouteTable, sel) + 4u * (b * 8 + i), sel[i]);
+      stc(RT, (uint32_t)offsetof(RouteTable, w) + 4u * (b * 8 + i), ex[i] / sum);
+      if (p.topk_out) p.topk_out[((size_t)l * B + b) * K + i] = sel[i];
+    }
+  }
+  // union slots (ascending expert id) and their token lists (ascending b)
+  for (int e = threadIdx.x; e < E; e += NT) {
+    int u = 0;
+    for (int f = 0; f < e; ++f) u += used[f];
+    if (e == E - 1) stci(RT, (uint32_t)offsetof(RouteTable, n_union), u + used[e]);
+    if (!used[e]) continue;
+    stci(RT, (uint32_t)offsetof(RouteTable, union_e) + 4u * u, e);
+    int nt = 0;
+    for (int b = 0; b < B; ++b) {
+      if (!selflag[b * E + e]) continue;
+      stci(RT, (uint32_t)offsetof(RouteTable, tok_bi) + 4u * (u * MAXB + nt), (b << 8) | posi[b * E + e]);
+      ++nt;
+    }
+    stci(RT, (uint32_t)offsetof(RouteTable, n_tok) + 4u * u, nt);
+  }
+}
+
+template <class S, int TB>
+__device__ __forceinline__ bool op_router(int task) {
+  CParams& p = P();
+  Ctl& ctl = ctl_s;
+  float* sm = smem;
+  const TaskHdr T = read_task(p, task);
+  constexpr int H = S::H, E = S::E, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
+  const LayerPtrs& Lp = p.layers[T.layer];
+  const int row0 = T.a0, nrows = T.a1;
+  auto rowptr = [&](int r) { return Lp.w_router + (size_t)(row0 + r) * H; };
+  WBuf<H, NP> A;
+  const bool pre = !(p.flags & 2);
+  if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+  if (threadIdx.x < MAXB) ctl.toks[threadIdx.x] = threadIdx.x;
+  __syncthreads();
+  stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
+  const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)T.layer * MAXB * E);
+  const float* bias = p.has_bias ? Lp.router_bias : nullptr;
+  gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
+      [&](int r, int t) { return sm + (size_t)t * H; },
+      [&](int r, int t, float v) {
+        const int e = row0 + r;
+        stc(R, 4u * (t * E + e), bias ? v + bias[e] : v);
+      });
+  const uint32_t old = signal(p, ctl, T.sig, true);
+  if (old + 1 == (uint32_t)T.a2) {      // last router tile of the layer: route the batch
+    __syncthreads();
+    compute_route<S>(p, T.layer, sm);
+    signal(p, ctl, T.sig2, false);
+  }
+  return true;
+}
+
+// Expert slice: rows f0..f0+nf of W_gate[e] and W_up[e] for the tokens routed to union slot u;
+// h = SiLU(g) * u (P3 "Key Technologies and Architecture": fused SiLU-multiply).
+template <class S, int TB>
+__device__ __forceinline__ bool op_gateup(int task) {
+  CParams& p = P();
+  Ctl& ctl = ctl_s;
+  float* sm = smem;
+  const TaskHdr T = read_task(p, task);
+  constexpr int H = S::H, F = S::F, K = S::K, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
+  const int l = T.layer, u = T.a0, f0 = T.a1, nf = T.a2;
+  const LayerPtrs& Lp = p.layers[l];
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+  const __amdgpu_buffer_rsrc_t RT = rsrc(p.route + l);
+  const int nu = ldci(RT, (uint32_t)offsetof(RouteTable, n_union));
+  if (u < nu) {
+    const int e = ldci(RT, (uint32_t)offsetof(RouteTable, union_e) + 4u * u);
+    const int ntok = ldci(RT, (uint32_t)offsetof(RouteTable, n_tok) + 4u * u);
+    const uint16_t* wg = Lp.w_gate + (size_t)e * F * H;
+    const uint16_t* wu = Lp.w_up + (size_t)e * F * H;
+    auto rowptr = [&](int r) { return r < nf ? wg + (size_t)(f0 + r) * H : wu + (size_t)(f0 + r - nf) * H; };
+    WBuf<H, NP> A;
+    load_block<H, NP>(A, 0, 2 * nf, rowptr);
+    if (threadIdx.x < MAXB) {
+      const int t = threadIdx.x;
+      const int bi = t < ntok ? ldci(RT, (uint32_t)offsetof(RouteTable, tok_bi) + 4u * (u * MAXB + t)) : 0;
+      ctl.bis[t] = bi;
+      ctl.toks[t] = bi >> 8;
+    }
+    __syncthreads();
+    stage_norm<S>(p, l, ctl.toks, ntok, Lp.attn_norm, sm, T.id);
+    float* gu = sm + (size_t)TB * H;                 // [TB][2 nf]
+    gemv_stream<H, NP, TB>(A, true, 2 * nf, ntok, rowptr,
+        [&](int r, int t) { return sm + (size_t)t * H; },
+        [&](int r, int t, float v) { gu[t * 2 * nf + r] = v; });
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
+    for (int i = threadIdx.x; i < ntok * nf; i += NT) {
+      const int t = i / nf, f = i % nf;
+      const int bi = ctl.bis[t];
+      const float g = gu[t * 2 * nf + f], up = gu[t * 2 * nf + nf + f];
+      const float hv = (g / (1.f + expf(-g))) * up;
+      stc(Hb, 4u * (((bi >> 8) * K + (bi & 255)) * F + f0 + f), hv);
+    }
+  }
+  signal(p, ctl, T.sig, false);
+  return true;
+}
+
+// Split-KV paged GQA decode attention for one (sequence b, KV group g, key range) with fused RoPE
+// (P3 "Key Technologies and Architecture": restructured paged attention, fused RoPE; P1 "From
+// demo to a full serving system": paged KV, ragged lengths). The split holding the new position
+// writes the new K/V into the cache first and scores it. The last split of (b, g) to finish merges
+// all partials in split order (log-sum-exp) and publishes the group's attention output.
+template <class S>
+__device__ __forceinline__ bool op_attn(int task) {
+  CParams& p = P();
+  Ctl& ctl = ctl_s;
+  float* sm = smem;
+  const TaskHdr T = read_task(p, task);
+  constexpr int D = S::D, HPG = S::HPG, LPK = D / 8, KPW = 64 / LPK, KPI = NWAVE * KPW;
+  constexpr int NB = 4;   // keys per lane per register block
+  static_assert(LPK >= HPG / 2 && LPK <= 64, "");
+  const int l = T.layer, b = T.a0, g = T.a1, k0 = T.a2, k1 = T.a3;
+  const int pbase = T.a4, s_idx = T.a5 & 0xffff, nsplit = T.a5 >> 16;
+  const LayerPtrs& Lp = p.layers[l];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int li = lane % LPK, slot = wave * KPW + lane / LPK;
+  const int n_ctx = p.seq_lens[b], pos = p.positions[b];
+  const bool last = k1 < 0;
+  if (pos != n_ctx - 1 || pos < 0 || n_ctx > p.max_pages * PAGE) {
+    if (threadIdx.x == 0) raise_error(p, DEV_BAD_POS, T.id, -1, (uint32_t)n_ctx, (uint32_t)pos, (uint32_t)b);
+    return false;
+  }
+  int kend = last ? pos : (k1 < pos ? k1 : pos);
+  if (kend < k0) kend = k0;
+  const int nk = kend - k0;                       // cached keys scored by this task
+  const int ntot = nk + (last ? 1 : 0);
+  if ((last && pos < k0) || ntot > SPLIT_MAX) {
+    if (threadIdx.x == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)k0, (uint32_t)pos, (uint32_t)b);
+    return false;
+  }
+  const int32_t* bt = p.block_tables + (size_t)b * p.max_pages;
+  // key j of this task -> address of its chunk li in the K (or V) cache
+  auto kv_off = [&](int j) -> size_t {
+    int page = bt[j / PAGE];
+    if (page < 0 || page >= p.num_pages) {
+      raise_error(p, DEV_BAD_PAGE, T.id, -1, (uint32_t)p.num_pages, (uint32_t)page, (uint32_t)j);
+      page = 0;
+    }
+    return (((size_t)page * S::HKV + g) * PAGE + (j % PAGE)) * D + 8 * li;
+  };
+  const int nit = (nk + KPI - 1) / KPI;           // key iterations
+  const int nblk = (nit + NB - 1) / NB;
+  auto load_kv = [&](u4 (&buf)[NB], const uint16_t* cache, int blk) {
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+      const int j = k0 + (blk * NB + q) * KPI + slot;
+      buf[q] = (j < kend) ? ldw(cache + kv_off(j)) : u4{0u, 0u, 0u, 0u};
+    }
+  };
+  // RoPE table for this position (angles in float64, as the oracle's reading R3)
+  float* cs = sm;                                  // [D/2] cos, [D/2] sin
+  float* sbuf = sm + D;                            // [SPLIT_MAX + 1][HPG] scores -> probabilities
+  float* vnew = sbuf + (SPLIT_MAX + 1) * HPG;      // [D]
+  float* ml = vnew + D;                            // [2][HPG]
+  float* obuf = ml + 2 * HPG;                      // [NWAVE][LPK][HPG * 8]
+  if (threadIdx.x < D / 2) {
+    const double ang = (double)pos * p.inv_freq[threadIdx.x];
+    cs[threadIdx.x] = (float)cos(ang);
+    cs[D / 2 + threadIdx.x] = (float)sin(ang);
+  }
+  // prefetch the first K and V blocks (old keys do not depend on this step's activations)
+  u4 kb[NB], vb[NB];
+  if (nblk > 0) { load_kv(kb, Lp.k_cache, 0); load_kv(vb, Lp.v_cache, 0); }
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+  // rotated query chunk of this lane for the HPG heads of group g
+  const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + ((size_t)l * MAXB + b) * S::QKVR);
+  const float sd = sqrtf((float)D);
+  float q[HPG][8];
+  auto rope_chunk = [&](uint32_t base, float (&out)[8]) {   // base: float index of a head vector
+    const int d0 = 8 * li, pd0 = d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
+    const f4 x0 = ldc4(Q, 4u * (base + d0)), x1 = ldc4(Q, 4u * (base + d0 + 4));
+    const f4 y0 = ldc4(Q, 4u * (base + pd0)), y1 = ldc4(Q, 4u * (base + pd0 + 4));
+    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const float ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int i = (d0 + m) % (D / 2);
+      const float c = cs[i], s = cs[D / 2 + i];
+      out[m] = d0 < D / 2 ? xs[m] * c - ys[m] * s : xs[m] * c + ys[m] * s;
+    }
+  };
+#pragma unroll
+  for (int hh = 0; hh < HPG; ++hh) rope_chunk((uint32_t)((g * HPG + hh) * D), q[hh]);
+
+  // ---- pass A: scores s[j][hh] = (k_j . q_hh) / sqrt(D)
+  auto score_chunk = [&](const float (&kv)[8], int jj) {
+    float part[HPG];
+#pragma unroll
+    for (int hh = 0; hh < HPG; ++hh) {
+      float a = 0.f;
+#pragma unroll
+      for (int m = 0; m < 8; ++m) a = __builtin_fmaf(q[hh][m], kv[m], a);
+      part[hh] = a;
+    }
+    // reduce-scatter over the LPK lanes of this key: after log2(HPG) halvings each lane keeps one
+    // head; the remaining steps finish the sum. Lane li ends with head li >> (log2 LPK - log2 HPG).
+    constexpr int LH = __builtin_ctz(HPG), LL = __builtin_ctz(LPK);
+    float cur[HPG];
+#pragma unroll
+    for (int hh = 0; hh < HPG; ++hh) cur[hh] = part[hh];
+    int n = HPG;
+#pragma unroll
+    for (int st = 0; st < LH; ++st) {
+      const int mask = LPK >> (st + 1);
+      const bool hi = (li & mask) != 0;
+      n >>= 1;
+#pragma unroll
+      for (int m = 0; m < HPG / 2; ++m) {
+        if (m < n) {
+          const float keep = hi ? cur[n + m] : cur[m];
+          const float send = hi ? cur[m] : cur[n + m];
+          cur[m] = keep + __shfl_xor(send, mask, 64);
+        }
+      }
+    }
+    float sc = cur[0];
+#pragma unroll
+    for (int st = LH; st < LL; ++st) sc += __shfl_xor(sc, LPK >> (st + 1), 64);
+    const int hh = li >> (LL - LH);
+    if ((li & ((1 << (LL - LH)) - 1)) == 0 && jj >= 0) sbuf[jj * HPG + hh] = sc / sd;
+  };
+  for (int blk = 0; blk < nblk; ++blk) {
+    u4 kn[NB];
+    if (blk + 1 < nblk) load_kv(kn, Lp.k_cache, blk + 1);
+#pragma unroll
+    for (int qq = 0; qq < NB; ++qq) {
+      const int jj = (blk * NB + qq) * KPI + slot;
+      const float kv[8] = {bf_lo(kb[qq].x), bf_hi(kb[qq].x), bf_lo(kb[qq].y), bf_hi(kb[qq].y),
+                           bf_lo(kb[qq].z), bf_hi(kb[qq].z), bf_lo(kb[qq].w), bf_hi(kb[qq].w)};
+      score_chunk(kv, jj < nk ? jj : -1);
+    }
+#pragma unroll
+    for (int qq = 0; qq < NB; ++qq) kb[qq] = kn[qq];
+  }
+  if (last) {
+    // new key/value: RoPE(k) and v from this step's QKV rows, rounded to bf16 (the cache format),
+    // written at slot pos, and scored in rounded form by key slot 0 (wave 0, lanes < LPK).
+    if (wave == 0 && lane < LPK) {
+      float kr[8];
+      rope_chunk((uint32_t)(S::HQ * D + g * D), kr);
+      const uint32_t vbase = (uint32_t)((S::HQ + S::HKV) * D + g * D + 8 * li);
+      const f4 v0 = ldc4(Q, 4u * vbase), v1 = ldc4(Q, 4u * (vbase + 4));
+      const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+      uint32_t kw[4], vw[4];
+      float kq[8];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t ka = f2bf(kr[2 * m]), kb2 = f2bf(kr[2 * m + 1]);
+        const uint32_t va = f2bf(vv[2 * m]), vb2 = f2bf(vv[2 * m + 1]);
+        kw[m] = ka | (kb2 << 16);
+        vw[m] = va | (vb2 << 16);
+        kq[2 * m] = bf1((uint16_t)ka); kq[2 * m + 1] = bf1((uint16_t)kb2);
+        vnew[8 * li + 2 * m] = bf1((uint16_t)va); vnew[8 * li + 2 * m + 1] = bf1((uint16_t)vb2);
+      }
+      const size_t off = kv_off(pos);
+      *reinterpret_cast<u4*>(Lp.k_cache + off) = u4{kw[0], kw[1], kw[2], kw[3]};
+      *reinterpret_cast<u4*>(Lp.v_cache + off) = u4{vw[0], vw[1], vw[2], vw[3]};
+      score_chunk(kq, nk);
+    } else if (wave == 0) {
+      // the other lanes of wave 0 take part in the shuffles of score_chunk with dummy data
+      float dummy[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+      score_chunk(dummy, -1);
+    }
+  }
+  __syncthreads();
+  // ---- softmax statistics per head (wave w handles heads w, w + 4, ...)
+  for (int hh = wave; hh < HPG; hh += NWAVE) {
+    float m = -INFINITY;
+    for (int j = lane; j < ntot; j += 64) m = fmaxf(m, sbuf[j * HPG + hh]);
+    m = wmax<64>(m);
+    float lsum = 0.f;
+    for (int j = lane; j < ntot; j += 64) {
+      const float e = expf(sbuf[j * HPG + hh] - m);
+      sbuf[j * HPG + hh] = e;
+      lsum += e;
+    }
+    lsum = wsum<64>(lsum);
+    if (lane == 0) { ml[hh] = m; ml[HPG + hh] = lsum; }
+  }
+  __syncthreads();
+  // ---- pass B: o[hh][d] = sum_j p[j][hh] v_j[d]
+  float o[HPG][8];
+#pragma unroll
+  for (int hh = 0; hh < HPG; ++hh)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) o[hh][m] = 0.f;
+  auto accum = [&](const float (&vv)[8], int jj) {
+    const float* pr = sbuf + jj * HPG;
+#pragma unroll
+    for (int hh = 0; hh < HPG; ++hh) {
+      const float pj = pr[hh];
+#pragma unroll
+      for (int m = 0; m < 8; ++m) o[hh][m] = __builtin_fmaf(pj, vv[m], o[hh][m]);
+    }
+  };
+  for (int blk = 0; blk < nblk; ++blk) {
+    u4 vn[NB];
+    if (blk + 1 < nblk) load_kv(vn, Lp.v_cache, blk + 1);
+#pragma unroll
+    for (int qq = 0; qq < NB; ++qq) {
+      const int jj = (blk * NB + qq) * KPI + slot;
+      if (jj < nk) {
+        const float vv[8] = {bf_lo(vb[qq].x), bf_hi(vb[qq].x), bf_lo(vb[qq].y), bf_hi(vb[qq].y),
+                             bf_lo(vb[qq].z), bf_hi(vb[qq].z), bf_lo(vb[qq].w), bf_hi(vb[qq].w)};
+        accum(vv, jj);
+      }
+    }
+#pragma unroll
+    for (int qq = 0; qq < NB; ++qq) vb[qq] = vn[qq];
+  }
+  if (last && slot == 0) {
+    float vv[8];
+#pragma unroll
+    for (int m = 0; m < 8; ++m) vv[m] = vnew[8 * li + m];
+    accum(vv, nk);
+  }
+  // reduce o over the key slots of the wave (lanes sharing li), then over the waves via LDS
+#pragma unroll
+  for (int hh = 0; hh < HPG; ++hh)
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      float v = o[hh][m];
+#pragma unroll
+      for (int s = LPK; s < 64; s <<= 1) v += __shfl_xor(v, s, 64);
+      o[hh][m] = v;
+    }
+  if (lane < LPK) {
+#pragma unroll
+    for (int hh = 0; hh < HPG; ++hh)
+#pragma unroll
+      for (int m = 0; m < 8; ++m) obuf[(wave * LPK + li) * HPG * 8 + hh * 8 + m] = o[hh][m];
+  }
+  __syncthreads();
+  // partial: m[HPG], l[HPG], o[HPG][D] (unnormalised)
+  const size_t part = ((size_t)l * p.parts_per_layer + pbase + s_idx) * S::PART;
+  const __amdgpu_buffer_rsrc_t P = rsrc(p.apart + part);
+  for (int i = threadIdx.x; i < HPG * D; i += NT) {
+    const int hh = i / D, d = i % D, c = d / 8, m = d % 8;
+    float v = 0.f;
+    for (int w = 0; w < NWAVE; ++w) v += obuf[(w * LPK + c) * HPG * 8 + hh * 8 + m];
+    stc(P, 4u * (2 * HPG + i), v);
+  }
+  if (threadIdx.x < 2 * HPG) stc(P, 4u * threadIdx.x, ml[threadIdx.x]);
+  const uint32_t old = signal(p, ctl, T.sig, true);
+  if (old + 1 == (uint32_t)nsplit) {
+    // last arriver: merge the nsplit partials of (b, g) in split order
+    const __amdgpu_buffer_rsrc_t P0 = rsrc(p.apart + ((size_t)l * p.parts_per_layer + pbase) * S::PART);
+    const __amdgpu_buffer_rsrc_t A = rsrc(p.attn + ((size_t)l * MAXB + b) * S::AD + g * HPG * D);
+    for (int i = threadIdx.x; i < HPG * D; i += NT) {
+      const int hh = i / D;
+      float M = -INFINITY;
+      for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ldc(P0, 4u * (s * S::PART + hh)));
+      float L = 0.f, O = 0.f;
+      for (int s = 0; s < nsplit; ++s) {
+        const float ms = ldc(P0, 4u * (s * S::PART + hh));
+        const float sc = ms == -INFINITY ? 0.f : expf(ms - M);
+        L = __builtin_fmaf(ldc(P0, 4u * (s * S::PART + HPG + hh)), sc, L);
+        O = __builtin_fmaf(ldc(P0, 4u * (s * S::PART + 2 * HPG + i)), sc, O);
+      }
+      stc(A, 4u * i, O / L);
+    }
+    signal(p, ctl, T.sig2, false);
+  }
+  return true;
+}
+
+// Output rows row0..row0+nrows of the layer for every token: the fused residual add that rejoins
+// both branches (P1 "One persistent kernel for the whole decode step"):
+//   x_{l+1} = (x_l + W_o attn) + sum_i w_i W_down[e_i] h_i   (experts in ascending index).
+// Waits for the routing table (to prefetch the right W_down rows), the MoE slices and the
+// attention of every KV group.
+template <class S, int TB>
+__device__ __forceinline__ bool op_out(int task) {
+  CParams& p = P();
+  Ctl& ctl = ctl_s;
+  float* sm = smem;
+  const TaskHdr T = read_task(p, task);
+  constexpr int H = S::H, AD = S::AD, F = S::F, K = S::K;
+  constexpr int NPO = (OUT_MAXR + NWAVE * Geo<AD>::RPP - 1) / (NWAVE * Geo<AD>::RPP);
+  constexpr int NPD = (OUT_MAXR * K + NWAVE * Geo<F>::RPP - 1) / (NWAVE * Geo<F>::RPP);
+  const int l = T.layer, row0 = T.a0, nrows = T.a1;
+  const LayerPtrs& Lp = p.layers[l];
+  auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * AD; };
+  WBuf<AD, NPO> WO;
+  const bool pre = !(p.flags & 2);
+  if (pre) load_block<AD, NPO>(WO, 0, nrows, orow);
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;      // routing known
+  const __amdgpu_buffer_rsrc_t RT = rsrc(p.route + l);
+  float* a_s = sm;                                                     // [AD]
+  float* h_s = sm + AD;                                                // [K][F]
+  float* o_s = h_s + K * F;                                            // [OUT_MAXR]
+  float* y_s = o_s + OUT_MAXR;                                         // [K][OUT_MAXR]
+  if (!pre) load_block<AD, NPO>(WO, 0, nrows, orow);
+  const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
+  const __amdgpu_buffer_rsrc_t At = rsrc(p.attn + (size_t)l * MAXB * AD);
+  const __amdgpu_buffer_rsrc_t Xn = rsrc(p.x + (size_t)(l + 1) * MAXB * H);
+  for (int b = 0; b < p.B; ++b) {
+    int sel[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) sel[i] = ldci(RT, (uint32_t)offsetof(RouteTable, sel) + 4u * (b * 8 + i));
+    auto drow = [&](int q) {   // q = i * nrows + r
+      const int i = q / nrows, r = q % nrows;
+      int e = 0;
+#pragma unroll
+      for (int ii = 0; ii < K; ++ii) if (ii == i) e = sel[ii];
+      return Lp.w_down + ((size_t)e * H + row0 + r) * F;
+    };
+    WBuf<F, NPD> WD;
+    load_block<F, NPD>(WD, 0, K * nrows, drow);
+    if (b == 0) {
+      if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;  // all MoE slices
+      if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;  // attention of all groups
+    }
+    for (int i = threadIdx.x * 4; i < AD; i += NT * 4) *reinterpret_cast<f4*>(a_s + i) = ldc4(At, 4u * (b * AD + i));
+    for (int i = threadIdx.x * 4; i < K * F; i += NT * 4) *reinterpret_cast<f4*>(h_s + i) = ldc4(Hb, 4u * (b * K * F + i));
+    __syncthreads();
+    compute_block<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
+                              [&](int r, int t, float v) { o_s[r] = v; });
+    compute_block<F, NPD, 1>(WD, 0, K * nrows, 1, [&](int q, int t) { return h_s + (q / nrows) * F; },
+                             [&](int q, int t, float v) { y_s[(q / nrows) * OUT_MAXR + q % nrows] = v; });
+    __syncthreads();
+    if (threadIdx.x < nrows) {
+      const int r = threadIdx.x, row = row0 + r;
+      float xv;
+      if (l == 0) {
+        int tok = p.tokens[b];
+        tok = (tok < 0 || tok >= p.V) ? 0 : tok;
+        xv = bf1(p.embed[(size_t)tok * H + row]);
+      } else {
+        xv = ldc(rsrc(p.x + ((size_t)l * MAXB + b) * H), 4u * row);
+      }
+      float moe = 0.f;
+      for (int i = 0; i < K; ++i)
+        moe = moe + ldc(RT, (uint32_t)offsetof(RouteTable, w) + 4u * (b * 8 + i)) * y_s[i * OUT_MAXR + r];
+      const float xn = (xv + o_s[r]) + moe;
+      stc(Xn, 4u * (b * H + row), xn);
+      if (p.hidden_out && l == p.L - 1) p.hidden_out[(size_t)b * H + row] = xn;
+    }
+    __syncthreads();
+  }
+  signal(p, ctl, T.sig, false);
+  return true;
+}
+
+// lm_head rows row0..row0+nrows: logits = W_lm . RMSNorm_final(x_L), plus the running greedy
+// argmax (first index of the maximum) through a 64-bit atomic max on (ordered logit, ~index).
+template <class S, int TB>
+__device__ __forceinline__ bool op_lmhead(int task) {
+  CParams& p = P();
+  Ctl& ctl = ctl_s;
+  float* sm = smem;
+  const TaskHdr T = read_task(p, task);
+  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 4 : 8, RPP = Geo<H>::RPP;
+  const int row0 = T.a0, nrows = T.a1;
+  auto rowptr = [&](int r) { return p.lm_head + (size_t)(row0 + r) * H; };
+  WBuf<H, NP> A;
+  const bool pre = !(p.flags & 2);
+  if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+  if (threadIdx.x < MAXB) ctl.toks[threadIdx.x] = threadIdx.x;
+  __syncthreads();
+  stage_norm<S>(p, p.L, ctl.toks, p.B, p.final_norm, sm, T.id);
+  float bv[TB];
+  int bi[TB];
+#pragma unroll
+  for (int t = 0; t < TB; ++t) { bv[t] = -INFINITY; bi[t] = 0x7fffffff; }
+  float* logits = p.logits;
+  const int V = p.V;
+  gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
+      [&](int r, int t) { return sm + (size_t)t * H; },
+      [&](int r, int t, float v) {
+        const int row = row0 + r;
+        if (logits) __builtin_nontemporal_store(v, logits + (size_t)t * V + row);
+#pragma unroll
+        for (int tt = 0; tt < TB; ++tt)
+          if (tt == t && (v > bv[tt] || (v == bv[tt] && row < bi[tt]))) { bv[tt] = v; bi[tt] = row; }
+      });
+  // combine the emitting lanes (lir == 0) of every wave, then one atomic per token
+  float* cv = sm + (size_t)TB * H;                                 // [NWAVE * RPP][TB]
+  int* ci = reinterpret_cast<int*>(cv + NWAVE * RPP * TB);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane % Geo<H>::LPR == 0) {
+    const int slot = wave * RPP + lane / Geo<H>::LPR;
+#pragma unroll
+    for (int t = 0; t < TB; ++t) { cv[slot * TB + t] = bv[t]; ci[slot * TB + t] = bi[t]; }
+  }
+  __syncthreads();
+  if (threadIdx.x < p.B) {
+    const int t = threadIdx.x;
+    float best = -INFINITY;
+    int besti = 0x7fffffff;
+    for (int s = 0; s < NWAVE * RPP; ++s) {
+      const float v = cv[s * TB + t];
+      const int i = ci[s * TB + t];
+      if (v > best || (v == best && i < besti)) { best = v; besti = i; }
+    }
+    if (besti != 0x7fffffff) {
+      uint32_t u = __float_as_uint(best);
+      u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+      const unsigned long long key = ((unsigned long long)u << 32) | (0xffffffffu - (uint32_t)besti);
+      __hip_atomic_fetch_max(p.amax + t, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  signal(p, ctl, T.sig, false);
+  return true;
+}
+
+// End of the worker's queue: the last worker to finish publishes the argmax and clears every
+// counter and the argmax keys for the next step (single assignment per step: nothing else needs
+// clearing).
+__device__ void finish(CParams& p, Ctl& ctl) {
+  drain();
+  __syncthreads();
+  if (threadIdx.x == 0) ctl.flag = (int)(ctr_add(p.ctr + p.done_ctr, 1u) == (uint32_t)(p.n_workers - 1));
+  __syncthreads();
+  if (!ctl.flag) return;
+  if (threadIdx.x < MAXB) {
+    const unsigned long long key = __hip_atomic_load(p.amax + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (p.argmax_out && threadIdx.x < p.B) p.argmax_out[threadIdx.x] = (int32_t)(0xffffffffu - (uint32_t)key);
+    __hip_atomic_store(p.amax + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  for (int c = threadIdx.x; c < p.n_ctr; c += NT)
+    if (c != p.done_ctr) __hip_atomic_store(p.ctr + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  drain();
+  __syncthreads();
+  if (threadIdx.x == 0) __hip_atomic_store(p.ctr + p.done_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <class S, int TB>
+__global__ void __launch_bounds__(NT, 2) mk_step(Params) {
+  CParams& p = P();
+  const int qs = p.qoff[blockIdx.x], qe = p.qoff[blockIdx.x + 1];
+  const bool trace = (p.flags & 1) && p.trace;
+  for (int ti = qs; ti < qe; ++ti) {
+    const int op = p.tasks[(size_t)ti * DESC_WORDS + D_OP];
+    const uint64_t t_start = trace ? now() : 0;
+    bool ok;
+    switch (op) {
+      case OP_QKV: ok = op_qkv<S, TB>(ti); break;
+      case OP_ROUTER: ok = op_router<S, TB>(ti); break;
+      case OP_GATEUP: ok = op_gateup<S, TB>(ti); break;
+      case OP_ATTN: ok = op_attn<S>(ti); break;
+      case OP_OUT: ok = op_out<S, TB>(ti); break;
+      case OP_LMHEAD: ok = op_lmhead<S, TB>(ti); break;
+      default:
+        if (threadIdx.x == 0) raise_error(p, DEV_BAD_OP, ti, -1, 0, (uint32_t)op, 0);
+        ok = false;
+    }
+    if (trace && threadIdx.x == 0) {
+      unsigned long long* tr = p.trace + (size_t)ti * 4;
+      tr[0] = (unsigned long long)ti | ((unsigned long long)blockIdx.x << 32);
+      tr[1] = t_start;
+      tr[2] = 0;
+      tr[3] = now();
+    }
+    if (!ok) break;
+    __syncthreads();
+  }
+  finish(p, ctl_s);
+}
+
+// ------------------------------------------------------------------------------ host side
+
+template <class S>
+static size_t lds_bytes(int tb) {
+  // norm-staged activations + GEMV scratch, attention buffers, OUT staging: the largest wins
+  const size_t act = (size_t)tb * S::H * 4 + (size_t)tb * 2 * 64 * 4 + 4096;
+  const size_t att = ((size_t)S::D + (SPLIT_MAX + 1) * S::HPG + S::D + 2 * S::HPG +
+                      (size_t)NWAVE * (S::D / 8) * S::HPG * 8) * 4;
+  const size_t out = ((size_t)S::AD + S::K * S::F + OUT_MAXR + S::K * OUT_MAXR) * 4;
+  const size_t rte = ((size_t)MAXB * S::E * 3 + S::E) * 4 + 256;
+  size_t m = act;
+  if (att > m) m = att;
+  if (out > m) m = out;
+  if (rte > m) m = rte;
+  return (m + 255) & ~(size_t)255;
+}
+
+template <class S, int TB>
+static hipError_t launch_one(const Params& p, int grid, hipStream_t st, size_t* lds_out) {
+  const size_t lds = lds_bytes<S>(TB);
+  if (lds_out) *lds_out = lds;
+  hipError_t e = hipFuncSetAttribute((const void*)mk_step<S, TB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  Params pp = p;
+  void* args[] = {&pp};
+  return hipLaunchCooperativeKernel((const void*)mk_step<S, TB>, dim3(grid), dim3(NT), args, (unsigned)lds, st);
+}
+
+template <class S, int TB>
+static hipError_t occupancy_one(int* blocks_per_cu) {
+  const size_t lds = lds_bytes<S>(TB);
+  hipError_t e = hipFuncSetAttribute((const void*)mk_step<S, TB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)mk_step<S, TB>, NT, lds);
+}
+
+int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F) {
+  if (H == ShapeSmall::H && D == ShapeSmall::D && HQ == ShapeSmall::HQ && HKV == ShapeSmall::HKV &&
+      E == ShapeSmall::E && K == ShapeSmall::K && F == ShapeSmall::F) return 0;
+  if (H == ShapeFull::H && D == ShapeFull::D && HQ == ShapeFull::HQ && HKV == ShapeFull::HKV &&
+      E == ShapeFull::E && K == ShapeFull::K && F == ShapeFull::F) return 1;
+  return -1;
+}
+
+hipError_t launch_step(int shape, int batch, const Params& p, int grid, hipStream_t st, size_t* lds) {
+  if (shape == 0) return batch == 1 ? launch_one<ShapeSmall, 1>(p, grid, st, lds) : launch_one<ShapeSmall, MAXB>(p, grid, st, lds);
+  return batch == 1 ? launch_one<ShapeFull, 1>(p, grid, st, lds) : launch_one<ShapeFull, MAXB>(p, grid, st, lds);
+}
+
+hipError_t step_occupancy(int shape, int batch, int* blocks_per_cu) {
+  if (shape == 0) return batch == 1 ? occupancy_one<ShapeSmall, 1>(blocks_per_cu) : occupancy_one<ShapeSmall, MAXB>(blocks_per_cu);
+  return batch == 1 ? occupancy_one<ShapeFull, 1>(blocks_per_cu) : occupancy_one<ShapeFull, MAXB>(blocks_per_cu);
+}
+
+int split_max() { return SPLIT_MAX; }
+int out_max_rows() { return OUT_MAXR; }
+
+}  // namespace mk

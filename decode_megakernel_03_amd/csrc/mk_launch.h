@@ -1,0 +1,16 @@
+// Host-visible entry points of the kernel translation unit (mk_kernel.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+
+#include "mk_internal.h"
+
+namespace mk {
+// 0 = hidden 256 small model, 1 = hidden 2048 30B MoE, -1 = no compiled instance
+int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F);
+// cooperative launch of one step on `grid` workers (batch 1 or up to 8 instance)
+hipError_t launch_step(int shape, int batch, const Params& p, int grid, hipStream_t st, size_t* lds_bytes);
+hipError_t step_occupancy(int shape, int batch, int* blocks_per_cu);
+int split_max();      // keys one attention task may cover
+int out_max_rows();   // rows of one OUT task
+}  // namespace mk

@@ -1,0 +1,282 @@
+"""Thin ctypes binding over libmk.so (the C ABI declared in include/mk.h).
+
+Functions carry the ABI's names and only marshal arguments: every step of the decode path runs
+in the library's HIP kernel. Importing this module loads libmk.so and raises if it is missing -
+there is no fallback path. ``Engine`` is a convenience owner of an engine handle that keeps the
+torch tensors it points at alive.
+"""
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libmk.so")
+
+MK_OK, MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_OOM = 0, -1, -2, -3, -4
+MK_ERR_NO_SCHEDULE, MK_ERR_SCHEDULE_STALE, MK_ERR_DEVICE = -5, -6, -7
+MK_ABI_VERSION = 1
+MK_MAX_BATCH = 8
+MK_FLAG_TRACE = 1
+MK_FLAG_NO_PREFETCH = 2
+DESC_WORDS = 16
+
+EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_decode_step", "mk_set_step_outputs",
+            "mk_sync", "mk_get_error", "mk_reset", "mk_destroy", "mk_plan_build", "mk_plan_info_get",
+            "mk_plan_export", "mk_plan_validate", "mk_plan_simulate", "mk_engine_plan", "mk_plan_destroy"]
+
+
+class MkError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__(f"libmk status {status}: {msg}")
+        self.status = status
+
+
+class ModelDesc(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in (
+        "abi_version", "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
+        "expert_ffn", "vocab", "page_size", "num_pages", "max_batch", "max_pages_per_seq", "has_router_bias",
+        "has_lm_head")] + [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+
+
+_PP = ctypes.POINTER(ctypes.c_void_p)
+
+
+class WeightPtrs(ctypes.Structure):
+    _fields_ = [("embed", ctypes.c_void_p), ("lm_head", ctypes.c_void_p), ("final_norm", ctypes.c_void_p),
+                ("attn_norm", _PP), ("w_qkv", _PP), ("w_o", _PP), ("w_router", _PP), ("router_bias", _PP),
+                ("w_gate", _PP), ("w_up", _PP), ("w_down", _PP), ("k_cache", _PP), ("v_cache", _PP)]
+
+
+class Options(ctypes.Structure):
+    _fields_ = [("workers_per_cu", ctypes.c_int32), ("split_keys", ctypes.c_int32),
+                ("watchdog_ms", ctypes.c_int32), ("flags", ctypes.c_int32)]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("n_tasks", ctypes.c_int32), ("n_workers", ctypes.c_int32), ("n_counters", ctypes.c_int32),
+                ("max_queue", ctypes.c_int32), ("bytes_total", ctypes.c_int64), ("bytes_max_worker", ctypes.c_int64),
+                ("n_attn_splits", ctypes.c_int32), ("key_capacity_min", ctypes.c_int32)]
+
+
+def load(path=LIB_PATH):
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python -m decode_megakernel_03_amd.build`")
+    lib = ctypes.CDLL(path)
+    vp, i32, u64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint64, ctypes.c_size_t
+    P32 = ctypes.POINTER(ctypes.c_int32)
+    sig = {
+        "mk_create": [ctypes.POINTER(ModelDesc), ctypes.POINTER(WeightPtrs), ctypes.POINTER(vp)],
+        "mk_set_options": [vp, ctypes.POINTER(Options)],
+        "mk_build_schedule": [vp, i32, P32],
+        "mk_decode_step": [vp, vp, vp, vp, vp, vp, vp],
+        "mk_set_step_outputs": [vp, vp, vp, vp, vp],
+        "mk_sync": [vp],
+        "mk_get_error": [vp, ctypes.c_char_p, sz],
+        "mk_reset": [vp],
+        "mk_destroy": [vp],
+        "mk_plan_build": [ctypes.POINTER(ModelDesc), i32, P32, i32, i32, ctypes.POINTER(vp)],
+        "mk_plan_info_get": [vp, ctypes.POINTER(PlanInfo)],
+        "mk_plan_export": [vp, P32, P32],
+        "mk_plan_validate": [vp, ctypes.c_char_p, sz],
+        "mk_plan_simulate": [vp, u64, i32, i32, ctypes.c_char_p, sz],
+        "mk_engine_plan": [vp],
+        "mk_plan_destroy": [vp],
+    }
+    for name, args in sig.items():
+        f = getattr(lib, name)
+        f.argtypes = args
+        f.restype = None if name in ("mk_destroy", "mk_plan_destroy") else (vp if name == "mk_engine_plan" else ctypes.c_int)
+    return lib
+
+
+LIB = load()
+
+
+def _i32_array(values):
+    arr = (ctypes.c_int32 * len(values))(*[int(v) for v in values])
+    return arr
+
+
+def _ptr(t):
+    return ctypes.c_void_p(0 if t is None else t.data_ptr())
+
+
+def model_desc(wl, num_pages, max_pages_per_seq, max_batch=None, has_router_bias=False):
+    """mk_model_desc for a workload description (decode_megakernel_03_amd.synth.Workload)."""
+    return ModelDesc(MK_ABI_VERSION, wl.n_layers, wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
+                     wl.n_experts, wl.top_k, wl.expert_ffn, wl.vocab, wl.page_size, int(num_pages),
+                     int(max_batch or wl.batch), int(max_pages_per_seq), int(bool(has_router_bias)),
+                     int(bool(wl.lm_head)), float(wl.rope_theta), float(wl.rms_eps))
+
+
+# ---------------------------------------------------------------- same-name wrappers
+
+def _check(status, handle=None, what=""):
+    if status != MK_OK:
+        msg = what
+        if handle:
+            buf = ctypes.create_string_buffer(1024)
+            LIB.mk_get_error(handle, buf, 1024)
+            msg = f"{what}: {buf.value.decode()}"
+        raise MkError(status, msg)
+
+
+def mk_create(desc, ptrs):
+    h = ctypes.c_void_p()
+    _check(LIB.mk_create(ctypes.byref(desc), ctypes.byref(ptrs), ctypes.byref(h)), None, "mk_create")
+    return h
+
+
+def mk_set_options(h, workers_per_cu=0, split_keys=0, watchdog_ms=0, flags=0):
+    _check(LIB.mk_set_options(h, ctypes.byref(Options(workers_per_cu, split_keys, watchdog_ms, flags))), h, "mk_set_options")
+
+
+def mk_build_schedule(h, seq_lens):
+    arr = _i32_array(seq_lens)
+    _check(LIB.mk_build_schedule(h, len(seq_lens), arr), h, "mk_build_schedule")
+
+
+def mk_decode_step(h, tokens, positions, block_tables, seq_lens, logits_out, stream=None):
+    st = LIB.mk_decode_step(h, _ptr(tokens), _ptr(positions), _ptr(block_tables), _ptr(seq_lens), _ptr(logits_out),
+                            ctypes.c_void_p(stream or 0))
+    return st
+
+
+def mk_set_step_outputs(h, argmax_out=None, topk_out=None, hidden_out=None, trace_out=None):
+    _check(LIB.mk_set_step_outputs(h, _ptr(argmax_out), _ptr(topk_out), _ptr(hidden_out), _ptr(trace_out)), h,
+           "mk_set_step_outputs")
+
+
+def mk_sync(h):
+    return LIB.mk_sync(h)
+
+
+def mk_get_error(h):
+    buf = ctypes.create_string_buffer(2048)
+    st = LIB.mk_get_error(h, buf, 2048)
+    return st, buf.value.decode()
+
+
+def mk_reset(h):
+    _check(LIB.mk_reset(h), h, "mk_reset")
+
+
+def mk_destroy(h):
+    LIB.mk_destroy(h)
+
+
+def mk_plan_build(desc, seq_lens, n_workers, split_keys=0):
+    h = ctypes.c_void_p()
+    _check(LIB.mk_plan_build(ctypes.byref(desc), len(seq_lens), _i32_array(seq_lens), int(n_workers),
+                             int(split_keys), ctypes.byref(h)), None, "mk_plan_build")
+    return h
+
+
+def mk_plan_info_get(plan):
+    info = PlanInfo()
+    _check(LIB.mk_plan_info_get(plan, ctypes.byref(info)), None, "mk_plan_info_get")
+    return info
+
+
+def mk_plan_export(plan):
+    import numpy as np
+    info = mk_plan_info_get(plan)
+    tasks = np.zeros((info.n_tasks, DESC_WORDS), np.int32)
+    qoff = np.zeros(info.n_workers + 1, np.int32)
+    P32 = ctypes.POINTER(ctypes.c_int32)
+    _check(LIB.mk_plan_export(plan, tasks.ctypes.data_as(P32), qoff.ctypes.data_as(P32)), None, "mk_plan_export")
+    return tasks, qoff
+
+
+def mk_plan_validate(plan):
+    buf = ctypes.create_string_buffer(1024)
+    return LIB.mk_plan_validate(plan, buf, 1024), buf.value.decode()
+
+
+def mk_plan_simulate(plan, seed, stall_worker=-1, stall_at=0):
+    buf = ctypes.create_string_buffer(1024)
+    return LIB.mk_plan_simulate(plan, int(seed), int(stall_worker), int(stall_at), buf, 1024), buf.value.decode()
+
+
+def mk_engine_plan(h):
+    return ctypes.c_void_p(LIB.mk_engine_plan(h))
+
+
+def mk_plan_destroy(plan):
+    LIB.mk_plan_destroy(plan)
+
+
+# ---------------------------------------------------------------- convenience owner
+
+class Engine:
+    """Owns an engine over torch-resident weights (dict from synth.make_weights) and KV caches."""
+
+    def __init__(self, wl, weights, k_cache, v_cache, num_pages, max_pages_per_seq, max_batch=None):
+        self.wl = wl
+        self._keep = (weights, k_cache, v_cache)
+        L = wl.n_layers
+        has_bias = weights["layers"][0]["router_bias"] is not None
+        self.desc = model_desc(wl, num_pages, max_pages_per_seq, max_batch, has_bias)
+
+        def arr(key):
+            a = (ctypes.c_void_p * L)(*[weights["layers"][l][key].data_ptr() for l in range(L)])
+            return ctypes.cast(a, _PP), a
+
+        keep = []
+        fields = {}
+        for key in ("attn_norm", "w_qkv", "w_o", "w_router", "w_gate", "w_up", "w_down"):
+            p, a = arr(key)
+            fields[key] = p
+            keep.append(a)
+        rb = None
+        if has_bias:
+            a = (ctypes.c_void_p * L)(*[weights["layers"][l]["router_bias"].data_ptr() for l in range(L)])
+            rb = ctypes.cast(a, _PP)
+            keep.append(a)
+        ka = (ctypes.c_void_p * L)(*[t.data_ptr() for t in k_cache])
+        va = (ctypes.c_void_p * L)(*[t.data_ptr() for t in v_cache])
+        keep += [ka, va]
+        ptrs = WeightPtrs(weights["embed"].data_ptr(),
+                          0 if weights["lm_head"] is None else weights["lm_head"].data_ptr(),
+                          weights["final_norm"].data_ptr(), fields["attn_norm"], fields["w_qkv"], fields["w_o"],
+                          fields["w_router"], rb, fields["w_gate"], fields["w_up"], fields["w_down"],
+                          ctypes.cast(ka, _PP), ctypes.cast(va, _PP))
+        self.h = mk_create(self.desc, ptrs)
+        self._ptr_arrays = keep
+
+    def set_options(self, **kw):
+        mk_set_options(self.h, **kw)
+
+    def build_schedule(self, seq_lens):
+        mk_build_schedule(self.h, list(seq_lens))
+
+    def set_step_outputs(self, **kw):
+        self._outs = kw
+        mk_set_step_outputs(self.h, **kw)
+
+    def step(self, tokens, positions, block_tables, seq_lens, logits_out, stream=None):
+        st = mk_decode_step(self.h, tokens, positions, block_tables, seq_lens, logits_out, stream)
+        if st != MK_OK:
+            _check(st, self.h, "mk_decode_step")
+
+    def sync(self):
+        st = mk_sync(self.h)
+        if st != MK_OK:
+            _check(st, self.h, "mk_sync")
+
+    def error(self):
+        return mk_get_error(self.h)
+
+    def plan_info(self):
+        return mk_plan_info_get(mk_engine_plan(self.h))
+
+    def close(self):
+        if getattr(self, "h", None):
+            mk_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

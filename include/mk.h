@@ -1,0 +1,206 @@
+/*
+ * mk.h - C ABI of libmk, a persistent decode megakernel for AMD MI355X (gfx950).
+ *
+ * One call to mk_decode_step runs one whole decode step of a parallel-layer MoE transformer for a
+ * batch of 1..8 sequences as ONE persistent HIP kernel: resident workgroups pull fixed-size task
+ * descriptors from a host-built list in device memory and wait on per-producer counters in HBM
+ * instead of kernel boundaries.
+ *
+ * Sources (cited by page title and section):
+ *   P1  aimodeling.com, "cohere-megakernel-north-mini-code-h100": sections "Decode is a bandwidth
+ *       game", "One persistent kernel for the whole decode step", "From demo to a full serving
+ *       system", "Caveats and takeaways".
+ *   P2  "Cohere Megakernel Beats vLLM by 1.58x on H100 GPUs" (latestnews.news), body.
+ *   P3  "Cohere Releases Megakernel Engine for North Mini Code, Achieving Up to 1.41x Speedup Over
+ *       vLLM" (aibriefing.imbch.dev): "Key Technologies and Architecture", "Scheduling and
+ *       Performance Benchmarks", "Limitations and Future Plans".
+ *
+ * Conventions for every entry point:
+ *   - All functions return an mk_status; none throws, aborts or exits. Errors leave the engine
+ *     usable unless the status is MK_ERR_DEVICE, which is sticky until mk_reset.
+ *   - "device pointer" = memory on the engine's GPU (hipMalloc / torch CUDA tensor storage);
+ *     "host pointer" = ordinary process memory. The library never takes ownership of caller memory.
+ *   - An engine is not thread-safe: one decode owner thread drives it (P3 "Scheduling and
+ *     Performance Benchmarks": a C++ thread owns decode).
+ *   - bf16 means IEEE binary32 truncated to its upper 16 bits (stored as uint16).
+ */
+#ifndef MK_H
+#define MK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MK_ABI_VERSION 1
+#define MK_MAX_BATCH 8 /* batch sizes up to 8 (P2 body; P3 "Limitations and Future Plans") */
+
+typedef struct mk_engine mk_engine;
+typedef struct mk_plan mk_plan;
+
+typedef enum {
+  MK_OK = 0,
+  MK_ERR_INVALID_ARG = -1,    /* NULL where a pointer is required, sizes out of range        */
+  MK_ERR_UNSUPPORTED = -2,    /* a shape with no compiled kernel instance                     */
+  MK_ERR_HIP = -3,            /* a HIP runtime call failed (message via mk_get_error)         */
+  MK_ERR_OOM = -4,            /* workspace allocation failed                                  */
+  MK_ERR_NO_SCHEDULE = -5,    /* mk_decode_step before mk_build_schedule                      */
+  MK_ERR_SCHEDULE_STALE = -6, /* sequences outgrew the schedule's key capacity: rebuild it      */
+  MK_ERR_DEVICE = -7          /* the kernel reported a fault (watchdog, bad page, bad position) */
+} mk_status;
+
+/* Model description. Shapes the library is compiled for:
+ *   hidden 256,  heads 8/2 of 32,  8 experts top-2, expert_ffn 128   (small test model)
+ *   hidden 2048, heads 32/4 of 128, 128 experts top-8, expert_ffn 768 (30B-total MoE)
+ * n_layers, vocab, num_pages, max_pages_per_seq are free; page_size must be 16. */
+typedef struct {
+  int32_t abi_version;       /* = MK_ABI_VERSION */
+  int32_t n_layers;
+  int32_t hidden;            /* H */
+  int32_t n_q_heads;         /* Hq */
+  int32_t n_kv_heads;        /* Hkv (query head h reads KV head h / (Hq/Hkv)) */
+  int32_t head_dim;          /* D */
+  int32_t n_experts;         /* E */
+  int32_t top_k;             /* k experts per token */
+  int32_t expert_ffn;        /* F */
+  int32_t vocab;             /* V: rows of the embedding table (and of lm_head when present) */
+  int32_t page_size;         /* KV tokens per page (16) */
+  int32_t num_pages;         /* pages in each layer's K (and V) cache */
+  int32_t max_batch;         /* 1..MK_MAX_BATCH */
+  int32_t max_pages_per_seq; /* row length of block_tables */
+  int32_t has_router_bias;   /* 1: per-layer float32 [E] bias added to router logits */
+  int32_t has_lm_head;       /* 0: the step ends at the residual stream (no logits) */
+  float rope_theta;          /* RoPE base (rotate-half, full head_dim) */
+  float rms_eps;             /* RMSNorm epsilon */
+} mk_model_desc;
+
+/* Weight and KV-cache pointers (all device pointers; host arrays of per-layer pointers of length
+ * n_layers). Layouts, row-major:
+ *   embed [V, H] bf16; lm_head [V, H] bf16 (ignored when has_lm_head = 0); final_norm [H] bf16
+ *   attn_norm[l] [H] bf16     the one input norm shared by attention and MoE (parallel layer, P1
+ *                             "One persistent kernel for the whole decode step")
+ *   w_qkv[l] [(Hq+2Hkv)*D, H] bf16, rows: all q heads, then k heads, then v heads
+ *   w_o[l] [H, Hq*D] bf16; w_router[l] [E, H] bf16; router_bias[l] [E] float32 or NULL
+ *   w_gate[l], w_up[l] [E, F, H] bf16; w_down[l] [E, H, F] bf16
+ *   k_cache[l], v_cache[l] [num_pages, Hkv, page_size, D] bf16 (paged KV, P1 "From demo to a
+ *                             full serving system"); written in place by mk_decode_step.
+ * The engine keeps the pointers; the caller keeps the memory alive until mk_destroy. */
+typedef struct {
+  const void* embed;
+  const void* lm_head;
+  const void* final_norm;
+  const void* const* attn_norm;
+  const void* const* w_qkv;
+  const void* const* w_o;
+  const void* const* w_router;
+  const float* const* router_bias;
+  const void* const* w_gate;
+  const void* const* w_up;
+  const void* const* w_down;
+  void* const* k_cache;
+  void* const* v_cache;
+} mk_weight_ptrs;
+
+/* Engine tuning knobs (mk_set_options). Zero fields keep their defaults. */
+typedef struct {
+  int32_t workers_per_cu;    /* resident workgroups per CU (default 2) */
+  int32_t split_keys;        /* target keys per attention split (default: chosen from the load) */
+  int32_t watchdog_ms;       /* bound on any single dependency wait (default 2000) */
+  int32_t flags;             /* MK_FLAG_* */
+} mk_options;
+
+#define MK_FLAG_TRACE 1u       /* record per-task timestamps into the trace buffer */
+#define MK_FLAG_NO_PREFETCH 2u /* ablation: issue weight loads only after dependencies are met */
+
+/* Create an engine for `desc` over caller-owned weights (P1 "One persistent kernel for the whole
+ * decode step"). Validates the description, copies the pointer tables to the device and
+ * allocates the workspace (activations, partials, counters, task list). Nothing is copied from the
+ * weights. Uses the current HIP device. *out is set only on MK_OK. */
+mk_status mk_create(const mk_model_desc* desc, const mk_weight_ptrs* weights, mk_engine** out);
+
+/* Set tuning options; takes effect at the next mk_build_schedule. */
+mk_status mk_set_options(mk_engine* e, const mk_options* opt);
+
+/* Build the static task schedule for `batch` sequences whose current lengths (host int32 [batch],
+ * counting the token about to be decoded) are seq_lens_host (P3 "Scheduling and Performance
+ * Benchmarks": mostly static scheduling). Attention key ranges are split for balance and given
+ * room to grow; mk_decode_step returns MK_ERR_SCHEDULE_STALE once any sequence outgrows it.
+ * Synchronous; call again when the batch composition changes. */
+mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens_host);
+
+/* Enqueue one decode step on `stream` (a hipStream_t; NULL = default stream). Device pointers:
+ *   tokens int32 [B]                 token being decoded per sequence
+ *   positions int32 [B]              its position; must equal seq_lens[b] - 1
+ *   block_tables int32 [B, max_pages_per_seq]  page ids; entries past ceil(seq_len/16) unread
+ *   seq_lens int32 [B]               context length including the new token
+ *   logits_out float32 [B, V]        written (may be NULL when has_lm_head = 0)
+ * The new K/V of every sequence is written into the caches at its position before attention.
+ * Asynchronous: returns after the launch. Device-side faults surface as MK_ERR_DEVICE from the
+ * next mk_decode_step / mk_sync / mk_get_error. Host-side checks: MK_ERR_NO_SCHEDULE,
+ * MK_ERR_SCHEDULE_STALE (lengths tracked on the host from the schedule, +1 per step). */
+mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* positions,
+                         const int32_t* block_tables, const int32_t* seq_lens, float* logits_out,
+                         void* stream);
+
+/* Optional per-step outputs (device pointers, NULL = off), written by every later step:
+ *   argmax_out int32 [B]       greedy token (first index of the maximum logit)
+ *   topk_out int32 [L, B, k]   routed experts per layer and token, ascending expert index
+ *   hidden_out float32 [B, H]  residual stream after the last layer
+ *   trace_out uint64 [tasks, 4] when MK_FLAG_TRACE: {task id | worker << 32, t_start, t_ready,
+ *                              t_end} in 100 MHz ticks (size via mk_plan_info). */
+mk_status mk_set_step_outputs(mk_engine* e, int32_t* argmax_out, int32_t* topk_out,
+                              float* hidden_out, uint64_t* trace_out);
+
+/* Wait for the engine's last step and report a device fault, if any, as MK_ERR_DEVICE. */
+mk_status mk_sync(mk_engine* e);
+
+/* Describe the last error in `buf` (NUL-terminated, truncated to n). Synchronizes the engine's
+ * last stream to read the device error word. Returns the sticky status (MK_OK if none). */
+mk_status mk_get_error(mk_engine* e, char* buf, size_t n);
+
+/* Clear a sticky device error and reset every counter (after MK_ERR_DEVICE). Synchronous. */
+mk_status mk_reset(mk_engine* e);
+
+void mk_destroy(mk_engine* e);
+
+/* ---- schedule inspection (host only: no GPU needed) -------------------------------------- */
+
+typedef struct {
+  int32_t n_tasks;           /* descriptors in the step */
+  int32_t n_workers;         /* resident workgroups the schedule targets */
+  int32_t n_counters;        /* dependency counters */
+  int32_t max_queue;         /* longest per-worker queue */
+  int64_t bytes_total;       /* weight + KV bytes the tasks stream (cost model) */
+  int64_t bytes_max_worker;  /* largest per-worker byte load (cost model) */
+  int32_t n_attn_splits;     /* attention split tasks */
+  int32_t key_capacity_min;  /* smallest per-sequence key capacity before MK_ERR_SCHEDULE_STALE */
+} mk_plan_info;
+
+/* Build a schedule without any GPU (for validation and tests): same algorithm as
+ * mk_build_schedule for `n_workers` workers. *out is owned by the caller (mk_plan_destroy). */
+mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* seq_lens_host,
+                        int32_t n_workers, int32_t split_keys, mk_plan** out);
+mk_status mk_plan_info_get(const mk_plan* p, mk_plan_info* info);
+/* Copy descriptors (n_tasks x 16 int32) and per-worker queue bounds (n_workers + 1 int32). */
+mk_status mk_plan_export(const mk_plan* p, int32_t* tasks, int32_t* queue_offsets);
+/* Check the schedule: every task's dependencies are produced by tasks earlier in topological
+ * level, counters' targets equal their producer counts, queues are level-ordered (no deadlock
+ * with co-resident workers), every output region is written exactly once. Returns MK_OK or
+ * MK_ERR_INVALID_ARG with a description in buf. */
+mk_status mk_plan_validate(const mk_plan* p, char* buf, size_t n);
+/* Discrete-event simulation of the persistent loop on the CPU with random per-task latencies
+ * (seeded). Fails (MK_ERR_DEVICE + description) if a dependency wait would never end.
+ * stall_worker >= 0 makes that worker stop before its queue position stall_at (a forced stall
+ * the simulated watchdog must report). */
+mk_status mk_plan_simulate(const mk_plan* p, uint64_t seed, int32_t stall_worker, int32_t stall_at,
+                           char* buf, size_t n);
+/* Plan of the engine's current schedule (owned by the engine, valid until the next build). */
+const mk_plan* mk_engine_plan(const mk_engine* e);
+void mk_plan_destroy(mk_plan* p);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MK_H */

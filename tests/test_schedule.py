@@ -1,0 +1,137 @@
+"""Host-side checks of libmk without a GPU: the library loads and exports every symbol the header
+declares, and the static scheduler's plans are valid, deadlock-free under random interleavings
+(CPU simulation of the persistent loop), and report forced stalls the way the watchdog would."""
+
+import os
+import re
+
+import numpy as np
+import pytest
+
+from decode_megakernel_03_amd import mk, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "mk.h")).read()
+    declared = set(re.findall(r"\b(mk_\w+)\s*\(", header))
+    assert declared == set(mk.EXPORTED)
+    for name in declared:
+        assert hasattr(mk.LIB, name), name
+
+
+def _desc(wl, batch, ctx_max):
+    max_pages = (ctx_max + 1024 + 15) // 16
+    return mk.model_desc(wl, num_pages=batch * max_pages, max_pages_per_seq=max_pages, max_batch=batch)
+
+
+CASES = [
+    ("tiny", [65], 512),
+    ("tiny", [65, 17, 200], 512),
+    ("full", [8193], 512),
+    ("full", [8193] * 8, 512),
+    ("full", [1025, 30000, 4096, 77, 16, 17, 32768, 9000], 512),
+    ("full", [262145], 512),
+    ("full", [8193], 64),
+    ("layer", [8193], 512),
+]
+
+
+@pytest.mark.parametrize("name,lens,workers", CASES)
+def test_plan_valid_and_deadlock_free(name, lens, workers):
+    wl = synth.workload(name)
+    desc = _desc(wl, len(lens), max(lens))
+    plan = mk.mk_plan_build(desc, lens, workers)
+    try:
+        st, msg = mk.mk_plan_validate(plan)
+        assert st == mk.MK_OK, msg
+        for seed in range(3 if wl.n_layers > 2 else 6):
+            st, msg = mk.mk_plan_simulate(plan, seed)
+            assert st == mk.MK_OK, msg
+        info = mk.mk_plan_info_get(plan)
+        assert info.n_workers == workers
+        # balance: no worker carries much more than its share of the streamed bytes
+        assert info.bytes_max_worker <= 1.6 * info.bytes_total / workers + 600_000
+        assert info.key_capacity_min >= min(lens) + 256
+    finally:
+        mk.mk_plan_destroy(plan)
+
+
+def test_plan_structure_full_bs1():
+    """Counts per layer and the structural properties the method relies on."""
+    wl = synth.workload("full")
+    desc = _desc(wl, 1, 8193)
+    plan = mk.mk_plan_build(desc, [8193], 512)
+    tasks, qoff = mk.mk_plan_export(plan)
+    mk.mk_plan_destroy(plan)
+    op = tasks[:, 0]
+    L = 48
+    assert (op == 6).sum() == 512                                     # lm_head spread over every worker
+    per_layer_out = (op == 5).sum() // L
+    assert per_layer_out * 4 >= 2048
+    # output rows of layer l wait on the attention merges of all KV groups of layer l only
+    att = tasks[op == 4]
+    out = tasks[op == 5]
+    for l in (0, 17, 47):
+        att_sig2 = set(att[att[:, 1] == l][:, 13])
+        assert att_sig2 == set(out[out[:, 1] == l][:, 4])
+    # attention of group g waits only on the QKV tiles of group g (no false dependency on other groups)
+    qkv = tasks[op == 1]
+    for g in range(4):
+        a = att[(att[:, 1] == 3) & (att[:, 3] == g)]
+        producers = qkv[(qkv[:, 1] == 3) & (qkv[:, 12] == a[0, 8])]
+        rows = np.concatenate([np.arange(r0, r0 + n) for r0, n in producers[:, 2:4]])
+        heads = set(rows[rows < 4096] // 128)
+        assert heads == set(range(8 * g, 8 * g + 8))
+        assert set(rows[(rows >= 4096) & (rows < 4608)] // 128) == {32 + g}
+    # router and QKV tiles never wait on anything produced in their own layer
+    first = tasks[(op <= 2)]
+    assert np.all(first[first[:, 1] == 0][:, 8] == -1)
+    # every queue is level-ordered
+    lv = tasks[:, 14]
+    for w in range(512):
+        q = lv[qoff[w]:qoff[w + 1]]
+        assert np.all(np.diff(q) >= 0)
+
+
+def test_simulated_watchdog_names_the_blocked_wait():
+    wl = synth.workload("tiny")
+    desc = _desc(wl, 1, 65)
+    plan = mk.mk_plan_build(desc, [65], 16)
+    tasks, qoff = mk.mk_plan_export(plan)
+    # stall the worker that owns a router tile of layer 0 right before that tile
+    rows = np.nonzero((tasks[:, 0] == 2) & (tasks[:, 1] == 0))[0]
+    t = int(rows[0])
+    w = int(np.searchsorted(qoff, t, side="right") - 1)
+    st, msg = mk.mk_plan_simulate(plan, 1, stall_worker=w, stall_at=t - int(qoff[w]))
+    mk.mk_plan_destroy(plan)
+    assert st == mk.MK_ERR_DEVICE
+    assert "watchdog" in msg and "waits for counter" in msg
+
+
+def test_plan_rejects_bad_inputs():
+    wl = synth.workload("tiny")
+    desc = _desc(wl, 2, 65)
+    with pytest.raises(mk.MkError):
+        mk.mk_plan_build(desc, [0], 8)                 # empty sequence
+    with pytest.raises(mk.MkError):
+        mk.mk_plan_build(desc, [65, 65, 65], 8)        # batch above max_batch
+    bad = mk.model_desc(wl, 64, 64)
+    bad.page_size = 32
+    with pytest.raises(mk.MkError):
+        mk.mk_plan_build(bad, [65], 8)
+    bad = mk.model_desc(wl, 64, 64)
+    bad.hidden = 512
+    with pytest.raises(mk.MkError):
+        mk.mk_plan_build(bad, [65], 8)
+
+
+def test_schedule_capacity_grows_with_split():
+    wl = synth.workload("full")
+    desc = _desc(wl, 1, 8193)
+    plan = mk.mk_plan_build(desc, [8193], 512, split_keys=256)
+    info = mk.mk_plan_info_get(plan)
+    mk.mk_plan_destroy(plan)
+    assert info.n_attn_splits == 48 * 4 * 33
+    assert info.key_capacity_min == 8192 + 1024
