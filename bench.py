@@ -1,0 +1,260 @@
+#!/usr/bin/env python3
+"""Decode throughput of the persistent megakernel on one MI355X.
+
+A step is one decode step of the synthetic 48-layer parallel-MoE model (hidden 2048, 32/4 heads of
+128, 128 experts top-8, FFN 768, vocab 151936, random bf16 weights) for the batch, with the KV cache
+resident in HBM. Greedy decoding runs on the device (each step's argmax is the next step's token).
+
+Prints ONE JSON line: tok/s, % of HBM speed of light (algorithmic bytes / step time / 8 TB/s, with
+the expert union measured from the step's routing), the roofline of the step kernel, and the CPU
+oracle timed on the host cores over one full decode step (which also checks the first GPU step).
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
+METRIC = "decode tok/s on 1 GPU at bs1 & bs8, 8K ctx; % of HBM speed-of-light"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in ("mk_kernel.hip", "mk_host.cpp", "mk_internal.h"):
+        h.update(open(os.path.join(ROOT, "decode_megakernel_03_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=128)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--workload", default="full")
+    ap.add_argument("--batch", type=int, default=0)
+    ap.add_argument("--context", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--workers-per-cu", type=int, default=0)
+    ap.add_argument("--split-keys", type=int, default=0)
+    ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--trace", default="", help="after timing, trace one step and write a summary + Chrome JSON here")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (for scaling HBM counters)")
+    return ap.parse_args()
+
+
+def copy_calibration():
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "dispatches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if args.copy_calibration:
+        return copy_calibration()
+    from decode_megakernel_03_amd import metrics, mk, synth
+
+    over = {}
+    if args.batch:
+        over["batch"] = args.batch
+    if args.context:
+        over["context"] = args.context
+    wl = synth.workload(args.workload, **over)
+    B = wl.batch
+    total_steps = args.warmup + args.steps
+    dev = "cuda"
+    t0 = time.time()
+    log(f"[bench] generating {wl.name}: {wl.n_layers} layers, batch {B}, context {wl.context} on the GPU")
+    bias = synth.zipf_router_bias(wl) if wl.zipf_s else None
+    w = synth.make_weights(wl, seed=0, device=dev, router_bias=bias)
+    ctx = synth.context_lengths(wl)
+    bt_np, num_pages = synth.make_block_tables(ctx, total_steps + 1, wl.page_size)
+    k, v = synth.make_kv(wl, num_pages, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; KV pages {num_pages}")
+
+    want_cpu = not args.no_cpu_baseline
+    kv_host0 = None
+    if want_cpu:
+        from tests import harness
+        kv_host0 = harness.host_kv(k, v)            # KV state before the first step (oracle input)
+
+    eng = mk.Engine(wl, w, k, v, num_pages, bt_np.shape[1], max_batch=B)
+    eng.set_options(workers_per_cu=args.workers_per_cu, split_keys=args.split_keys, flags=args.flags)
+    eng.build_schedule((ctx + 1).tolist())
+    info = eng.plan_info()
+    log(f"[bench] schedule: {info.n_tasks} tasks on {info.n_workers} workers, {info.n_attn_splits} attention splits")
+
+    # per-step inputs precomputed on the device: positions / lengths advance by one each step and the
+    # token buffer doubles as the argmax output, so the timed loop is nothing but kernel launches
+    pos_all = torch.from_numpy((ctx[None, :] + np.arange(total_steps)[:, None]).astype(np.int32)).to(dev)
+    len_all = pos_all + 1
+    bt = torch.from_numpy(bt_np).to(dev)
+    tokens = torch.from_numpy(synth.first_tokens(wl)).to(dev)
+    tok0 = tokens.clone()
+    topk = torch.zeros(total_steps, wl.n_layers, B, wl.top_k, dtype=torch.int32, device=dev)
+    logits = torch.empty(B, wl.vocab, dtype=torch.float32, device=dev)
+    logits0 = None
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
+    for s in range(total_steps):
+        mk.mk_set_step_outputs(eng.h, argmax_out=tokens, topk_out=topk[s])
+        if s == args.warmup:
+            torch.cuda.synchronize()
+            log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
+            t_wall = time.perf_counter()
+        starts[s].record(stream)
+        st = mk.mk_decode_step(eng.h, tokens, pos_all[s], bt, len_all[s], logits, h)
+        ends[s].record(stream)
+        if st != mk.MK_OK:
+            raise mk.MkError(st, mk.mk_get_error(eng.h)[1])
+        if s == 0:
+            torch.cuda.synchronize()
+            eng.sync()
+            logits0 = logits.cpu().numpy().copy()
+            log("[bench] step 0 ok")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    eng.sync()
+    step_ms = np.array([starts[s].elapsed_time(ends[s]) for s in range(args.warmup, total_steps)])
+    # timed region: first start event to last end event (includes launch gaps)
+    span_ms = starts[args.warmup].elapsed_time(ends[total_steps - 1])
+    topk_h = topk.cpu().numpy()
+    union = np.array([[len(np.unique(topk_h[s, l])) for l in range(wl.n_layers)] for s in range(total_steps)])
+    step_bytes = np.array([metrics.step_bytes(wl, union[s], ctx + 1 + s) for s in range(total_steps)])
+    timed_bytes = step_bytes[args.warmup:]
+    tok_s = B * args.steps / (span_ms / 1e3)
+    achieved = float(np.mean(timed_bytes / (step_ms / 1e3)))      # per launch: bytes / kernel duration
+    sol_frac = float(np.sum(timed_bytes) / (span_ms / 1e3) / PEAK_HBM)
+    log(f"[bench] {args.steps} steps: mean {step_ms.mean():.3f} ms, median {np.median(step_ms):.3f} ms, span {span_ms:.1f} ms, "
+        f"wall {wall * 1e3:.1f} ms -> {tok_s:.1f} tok/s; {timed_bytes.mean() / 1e9:.3f} GB/step; "
+        f"{achieved / 1e9:.0f} GB/s per launch ({achieved / PEAK_HBM:.1%} of 8 TB/s)")
+
+    if args.trace:
+        run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps)
+
+    traffic = None
+    prof = os.path.join(ROOT, "profiles", f"traffic_{wl.name}_b{B}.json")
+    if os.path.exists(prof):
+        rec = json.load(open(prof))
+        if rec.get("kernel_hash") == kernel_source_hash():
+            traffic = rec.get("bytes_per_launch")
+
+    cpu = None
+    parity = None
+    if want_cpu:
+        cpu, parity = cpu_baseline(wl, w, kv_host0, tok0.cpu().numpy(), ctx, bt_np, logits0, topk_h[0])
+    out = {
+        "metric": METRIC,
+        "value": round(tok_s, 2),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(span_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{wl.name}: {wl.n_layers}-layer parallel-MoE decoder, batch {B}, context {int(ctx.max())}"
+                               f"{' (ragged)' if wl.ragged else ''}, bf16 weights and KV, fp32 arithmetic",
+                   "batch": B, "context": int(ctx.max()), "layers": wl.n_layers, "hidden": wl.hidden,
+                   "experts": f"{wl.n_experts} top-{wl.top_k}", "vocab": wl.vocab,
+                   "workers": info.n_workers, "tasks_per_step": info.n_tasks},
+        "sol_fraction": round(sol_frac, 4),
+        "bytes_per_step": int(timed_bytes.mean()),
+        "experts_union_mean": round(float(union[args.warmup:].mean()), 2),
+        "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM, 4), "traffic": traffic},
+        "cpu_baseline": cpu,
+        "parity_first_step": parity,
+    }
+    print(json.dumps(out), flush=True)
+    eng.close()
+
+
+def run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps):
+    """One more step with per-task timestamps; summary to stderr, records + Chrome JSON to files."""
+    import torch
+    from decode_megakernel_03_amd import mk, trace
+    info = eng.plan_info()
+    buf = torch.zeros(info.n_tasks, 8, dtype=torch.int64, device="cuda")
+    mk.mk_set_options(eng.h, flags=args.flags | mk.MK_FLAG_TRACE)
+    mk.mk_set_step_outputs(eng.h, argmax_out=tokens, trace_out=buf)
+    s = total_steps - 1
+    for _ in range(2):          # the second traced step is the one reported
+        st = mk.mk_decode_step(eng.h, tokens, pos_all[s], bt, len_all[s], logits, h)
+        if st != mk.MK_OK:
+            raise mk.MkError(st, mk.mk_get_error(eng.h)[1])
+        torch.cuda.synchronize()
+    eng.sync()
+    tr = buf.cpu().numpy().view(np.uint64)
+    tasks, qoff = mk.mk_plan_export(mk.mk_engine_plan(eng.h))
+    rec = trace.decode(tr, tasks)
+    log(trace.summary(rec, info.n_workers))
+    os.makedirs(os.path.dirname(os.path.abspath(args.trace)), exist_ok=True)
+    np.save(args.trace + ".npy", rec)
+    trace.chrome_json(rec, args.trace + ".json")
+    mk.mk_set_options(eng.h, flags=args.flags)
+
+
+def cpu_baseline(wl, w, kv0, tokens, ctx, bt, logits_gpu, topk_gpu):
+    """The oracle (numpy, fp32) on one full decode step of the same workload, on the host cores.
+    Weights touched by the step are copied to the host first (an untimed pass fills the cache)."""
+    import oracle
+    from tests import harness
+    import copy as cp
+    cores = len(os.sched_getaffinity(0))
+    dims = harness.dims_of(wl)
+    lw = harness.LazyWeights(w)
+    log(f"[bench] cpu baseline: untimed oracle pass (fetching touched weights to the host), {cores} cores")
+    t = time.perf_counter()
+    r = oracle.decode_step(dims, lw, cp.deepcopy(kv0), tokens, ctx, bt, ctx + 1)
+    log(f"[bench] cpu baseline: fetch pass {time.perf_counter() - t:.1f}s; timed pass")
+    t = time.perf_counter()
+    r = oracle.decode_step(dims, lw, cp.deepcopy(kv0), tokens, ctx, bt, ctx + 1)
+    dt = time.perf_counter() - t
+    log(f"[bench] cpu baseline: {dt:.2f}s per step")
+    d = np.abs(logits_gpu.astype(np.float64) - r.logits)
+    rel = float(np.linalg.norm(logits_gpu - r.logits) / np.linalg.norm(r.logits))
+    same_topk = int(sum(set(topk_gpu[l, b]) == set(r.topk[l, b]) for l in range(wl.n_layers) for b in range(wl.batch)))
+    parity = {"max_abs_logit_diff": float(d.max()), "rel_l2": rel,
+              "argmax_equal": bool(np.array_equal(np.argmax(logits_gpu, 1), np.argmax(r.logits, 1))),
+              "topk_sets_equal": f"{same_topk}/{wl.n_layers * wl.batch}",
+              "min_router_margin": float(r.margin.min())}
+    cpu = {"value": round(wl.batch / dt, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+           "sample": f"one full decode step (batch {wl.batch}, {wl.n_layers} layers, context {int(ctx.max())}) "
+                     f"after an untimed pass that copies the touched weights to the host"}
+    return cpu, parity
+
+
+if __name__ == "__main__":
+    main()

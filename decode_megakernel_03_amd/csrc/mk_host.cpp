@@ -139,9 +139,13 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     }
   }
   // attention split length: keep per-(b, g) split counts moderate and tasks ~128 KB of K+V
+  // ~256 keys (128 KB of K+V) per task; long contexts use longer splits so that a (sequence, KV
+  // group) never has more splits than one merge can combine (merge_max()), and the last split keeps
+  // at least a quarter of SPLIT_MAX of room to grow before the schedule must be rebuilt
   int maxlen = *std::max_element(seq_lens, seq_lens + B);
-  int split = split_req > 0 ? split_req : std::max(256, (int)ceil_div(ceil_div(maxlen, 64), 16) * 16);
-  split = std::max(16, std::min(split, SPLITMAX / 2));
+  int split = split_req > 0 ? split_req : 256;
+  split = std::max(split, (int)ceil_div(ceil_div(maxlen, merge_max() - 8), 16) * 16);
+  split = std::max(16, std::min(split, 3 * SPLITMAX / 4));
   split = (split + 15) / 16 * 16;
   P->split_keys = split;
 
@@ -160,13 +164,9 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   P->n_ctr = C.n;
 
   // tile sizes from the worker count
-  const int qkv_tile = std::max(4, std::min(64, (int)ceil_div(m.QKVR, W)));
+  // level 0 holds QKV tiles and router tiles: size QKV tiles so that no worker needs two
   const int router_tiles = std::max(1, std::min(8, m.E / 16));
-  const int slots = std::min(m.E, m.K * B);
-  int nf = (int)ceil_div(m.F, std::max<int64_t>(1, ceil_div(W, slots)));
-  nf = std::max(4, std::min(64, nf));
-  const int slices = (int)ceil_div(m.F, nf);
-
+  const int qkv_tile = std::max(4, std::min(64, (int)ceil_div(m.QKVR, std::max(1, W - router_tiles - 2 * 3 * m.HKV))));
   // attention splits per sequence: [k0, k0 + split) ... last split open-ended from k0_last
   std::vector<int> nsplit(B), pbase_b(B);
   int parts = 0;
@@ -180,6 +180,13 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     P->capacity[b] = std::min(k0_last + SPLITMAX, desc.max_pages_per_seq * PAGE);
   }
   P->parts_per_layer = parts;
+  // level 1 holds the attention splits and the expert slices: size the slices so that the level
+  // has about one task per worker (tasks are latency-bound; a second task per worker doubles it)
+  const int slots = std::min(m.E, m.K * B);
+  const int64_t gu_target = std::max<int64_t>(slots, W - parts);
+  int nf = (int)ceil_div(m.F, std::max<int64_t>(1, gu_target / slots));
+  nf = std::max(4, std::min(64, nf));
+  const int slices = (int)ceil_div(m.F, nf);
 
   std::vector<std::vector<Proto>> levels(3 * L + 1);
   int n_attn = 0;
@@ -285,6 +292,12 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     }
   }
 
+  // Every task pays a fixed latency (dependency poll, activation round trip, drain) worth about
+  // TASK_FIXED bytes of streaming at a worker's share of HBM bandwidth; attention also pays for
+  // its arithmetic (8 query heads per key on the vector units).
+  const int64_t TASK_FIXED = 96 * 1024;
+  for (auto& lvl : levels)
+    for (auto& pr : lvl) pr.bytes = pr.bytes * (pr.t.w[D_OP] == OP_ATTN ? 2 : 1) + TASK_FIXED;
   // placement: per level, longest task first onto the worker with the least load in that level
   // (ties: least total load, then lowest index); each worker's queue is level-ordered, and inside
   // a level its tasks run in priority order (router before QKV, attention before expert slices).

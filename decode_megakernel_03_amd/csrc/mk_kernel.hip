@@ -42,6 +42,7 @@ using ShapeSmall = Shape<256, 32, 8, 2, 8, 2, 128>;
 using ShapeFull = Shape<2048, 128, 32, 4, 128, 8, 768>;
 
 constexpr int SPLIT_MAX = 1024;   // keys one attention task may cover (LDS score buffer)
+constexpr int MERGE_MAX = (SPLIT_MAX + 1) / 2;   // splits one (sequence, KV group) may have
 constexpr int OUT_MAXR = 4;       // rows of one OUT task
 constexpr int SC1 = 16;           // buffer cache-policy bit for agent-coherent access
 
@@ -85,6 +86,13 @@ __device__ __forceinline__ void stc4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, SC1);
 }
 typedef const __attribute__((address_space(1))) u4 gu4;
+
+// Step-constant tables (descriptors, queue bounds, layer pointers, per-step inputs) are read
+// through the constant address space so that uniform reads become scalar loads.
+template <class T>
+__device__ __forceinline__ const __attribute__((address_space(4))) T* cst(const T* p) {
+  return (const __attribute__((address_space(4))) T*)p;
+}
 __device__ __forceinline__ u4 ldw(const void* p) {   // streamed weight / KV load (global memory)
   return __builtin_nontemporal_load((gu4*)p);
 }
@@ -119,10 +127,30 @@ __device__ __forceinline__ float dot8(u4 w, f4 a0, f4 a1, float acc) {
   return acc;
 }
 
+// Value of `v` in a partner lane within the same 16-lane row, by DPP (no LDS traffic). For a bit b
+// of the lane index (b = 1, 2, 4, 8) the partner differs from the lane exactly in that bit's half:
+// quad permutes for 1 and 2, the half-row mirror (i <-> 7 - i) for 4, the row mirror (i <-> 15 - i)
+// for 8. Either partner pattern serves sums and half-exchanging reductions alike.
+template <int BIT>
+__device__ __forceinline__ float dpp_partner(float v) {
+  constexpr int ctrl = BIT == 1 ? 0xB1 : BIT == 2 ? 0x4E : BIT == 4 ? 0x141 : 0x140;
+  static_assert(BIT == 1 || BIT == 2 || BIT == 4 || BIT == 8, "");
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float partner(float v, int bit) {   // any bit of the lane index
+  switch (bit) {
+    case 1: return dpp_partner<1>(v);
+    case 2: return dpp_partner<2>(v);
+    case 4: return dpp_partner<4>(v);
+    case 8: return dpp_partner<8>(v);
+    default: return __shfl_xor(v, bit, 64);
+  }
+}
+
 template <int N>
 __device__ __forceinline__ float wsum(float v) {   // sum over aligned groups of N lanes
 #pragma unroll
-  for (int m = 1; m < N; m <<= 1) v += __shfl_xor(v, m, 64);
+  for (int m = 1; m < N; m <<= 1) v += partner(v, m);
   return v;
 }
 template <int N>
@@ -137,10 +165,25 @@ __device__ __forceinline__ float wmax(float v) {
 struct Ctl {            // small per-worker control block in static LDS
   int ok;
   int flag;
+  unsigned long long t_ready;   // when the task's last dependency wait ended (trace)
+  unsigned long long mark[4];   // op-specific phase ends (trace)
   int toks[MAXB];       // batch rows of the tokens a task works on
   int bis[MAXB];        // (b << 8) | i of those tokens (expert slices)
+  alignas(16) RouteTable rt;   // the layer's routing decision, copied in one round trip
 };
 __shared__ Ctl ctl_s;
+static_assert(sizeof(RouteTable) % 16 == 0, "");
+
+// Trace: time the end of an op's phase i (0..3); no-op unless tracing.
+#define MARK(i) do { if ((p.flags & 1) && threadIdx.x == 0) ctl_s.mark[i] = now(); } while (0)
+
+// Copy layer l's routing table into LDS: every thread loads 16 bytes, one round trip.
+__device__ __forceinline__ void load_route(CParams& p, int l) {
+  const __amdgpu_buffer_rsrc_t R = rsrc(p.route + l);
+  f4* dst = reinterpret_cast<f4*>(&ctl_s.rt);
+  for (int i = threadIdx.x; i < (int)(sizeof(RouteTable) / 16); i += NT) dst[i] = ldc4(R, 16u * i);
+  __syncthreads();
+}
 
 __device__ void raise_error(CParams& p, uint32_t code, int task, int ctr, uint32_t target,
                             uint32_t observed, uint32_t detail) {
@@ -181,6 +224,40 @@ __device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) 
       }
     }
     ctl.ok = ok;
+    ctl.t_ready = now();
+  }
+  __syncthreads();
+  const bool ok = ctl.ok != 0;
+  __syncthreads();
+  return ok;
+}
+
+// Block until counter c0 >= t0 and counter c1 >= t1, polling both in the same round trip.
+__device__ bool wait_ge2(CParams& p, Ctl& ctl, int c0, uint32_t t0, int c1, uint32_t t1, int task) {
+  if (threadIdx.x == 0) {
+    int ok = 1;
+    uint32_t v0 = c0 >= 0 ? ctr_load(p.ctr + c0) : t0, v1 = c1 >= 0 ? ctr_load(p.ctr + c1) : t1;
+    if (v0 < t0 || v1 < t1) {
+      const uint64_t ts = now();
+      uint32_t it = 0;
+      for (;;) {
+        __builtin_amdgcn_s_sleep(1);
+        if (c0 >= 0) v0 = ctr_load(p.ctr + c0);
+        if (c1 >= 0) v1 = ctr_load(p.ctr + c1);
+        if (v0 >= t0 && v1 >= t1) break;
+        if ((++it & 15u) == 0) {
+          if (ctr_load(&p.err->abort_flag)) { ok = 0; break; }
+          if (now() - ts > p.watchdog_ticks) {
+            const bool first = v0 < t0;
+            raise_error(p, DEV_TIMEOUT, task, first ? c0 : c1, first ? t0 : t1, first ? v0 : v1, 0);
+            ok = 0;
+            break;
+          }
+        }
+      }
+    }
+    ctl.ok = ok;
+    ctl.t_ready = now();
   }
   __syncthreads();
   const bool ok = ctl.ok != 0;
@@ -315,7 +392,7 @@ __device__ void stage_norm(CParams& p, int l, const int* toks, int ntok, const u
     const int b = toks[t];
     float v[4 * G4];
     if (l == 0) {
-      int tok = p.tokens[b];
+      int tok = cst(p.tokens)[b];
       if (tok < 0 || tok >= p.V) {
         if (lane == 0) raise_error(p, DEV_BAD_TOKEN, task, -1, 0, (uint32_t)tok, (uint32_t)b);
         tok = 0;
@@ -364,7 +441,7 @@ struct TaskHdr {
 // Fields of task `ti` (uniform: the descriptor is read with scalar loads).
 __device__ __forceinline__ TaskHdr read_task(CParams& p, int ti) {
   ti = __builtin_amdgcn_readfirstlane(ti);
-  const int32_t* d = p.tasks + (size_t)ti * DESC_WORDS;
+  const __attribute__((address_space(4))) int32_t* d = cst(p.tasks) + (size_t)ti * DESC_WORDS;
   TaskHdr T;
   T.id = ti;
   T.op = d[D_OP]; T.layer = d[D_LAYER];
@@ -381,8 +458,8 @@ __device__ __forceinline__ bool op_qkv(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
-  const LayerPtrs& Lp = p.layers[T.layer];
+  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 2 : 4;
+  const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_qkv + (size_t)(row0 + r) * H; };
   WBuf<H, NP> A;
@@ -392,10 +469,14 @@ __device__ __forceinline__ bool op_qkv(int task) {
   if (threadIdx.x < MAXB) ctl.toks[threadIdx.x] = threadIdx.x;
   __syncthreads();
   stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
+  MARK(0);
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + (size_t)T.layer * MAXB * S::QKVR);
   gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); });
+  MARK(1);
+  drain();
+  MARK(2);
   signal(p, ctl, T.sig, false);
   return true;
 }
@@ -405,71 +486,96 @@ __device__ __forceinline__ bool op_qkv(int task) {
 // selected, the union of experts over the batch and each union slot's token list.
 template <class S>
 __device__ __forceinline__ void compute_route(CParams& p, int l, float* sm) {
-  constexpr int E = S::E, K = S::K;
+  constexpr int E = S::E, K = S::K, EPL = (E + 63) / 64;   // experts held per lane
+  static_assert(E <= 128 && K <= 8, "");
   const int B = p.B;
-  float* rl = sm;                                          // [B][E] logits
-  int* selflag = reinterpret_cast<int*>(sm + MAXB * E);    // [B][E] 1 if selected
-  int* posi = selflag + MAXB * E;                          // [B][E] rank among the selected (ascending e)
-  int* used = posi + MAXB * E;                             // [E] selected by any token
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  unsigned long long* mask = reinterpret_cast<unsigned long long*>(sm);   // [MAXB][2] selected experts
   const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)l * MAXB * E);
-  for (int i = threadIdx.x; i < B * E; i += NT) rl[i] = ldc(R, 4u * i);
-  __syncthreads();
-  for (int i = threadIdx.x; i < B * E; i += NT) {
-    const int b = i / E, e = i % E;
-    const float re = rl[i];
-    int rank = 0;
-    for (int f = 0; f < E; ++f) {
-      const float rf = rl[b * E + f];
-      rank += (rf > re || (rf == re && f < e)) ? 1 : 0;
-    }
-    selflag[i] = rank < K ? 1 : 0;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < B * E; i += NT) {
-    const int b = i / E, e = i % E;
-    int c = 0;
-    for (int f = 0; f < e; ++f) c += selflag[b * E + f];
-    posi[i] = c;
-  }
-  for (int e = threadIdx.x; e < E; e += NT) {
-    int u = 0;
-    for (int b = 0; b < B; ++b) u |= selflag[b * E + e];
-    used[e] = u;
-  }
-  __syncthreads();
-  RouteTable* rt = p.route + l;
-  const __amdgpu_buffer_rsrc_t RT = rsrc(rt);
-  // selected experts of each token in ascending order, with their softmax weights
-  if (threadIdx.x < B) {
-    const int b = threadIdx.x;
-    int sel[8];
-    int n = 0;
-    for (int e = 0; e < E && n < K; ++e)
-      if (selflag[b * E + e]) sel[n++] = e;
-    float m = -INFINITY;
-    for (int i = 0; i < K; ++i) m = fmaxf(m, rl[b * E + sel[i]]);
-    float ex[8], sum = 0.f;
-    for (int i = 0; i < K; ++i) { ex[i] = expf(rl[b * E + sel[i]] - m); sum += ex[i]; }
+  const __amdgpu_buffer_rsrc_t RT = rsrc(p.route + l);
+  // one wave per token: K rounds of wave-wide (largest logit, lowest index), winners removed
+  for (int b = wave; b < B; b += NWAVE) {
+    float v[EPL];
+#pragma unroll
+    for (int k = 0; k < EPL; ++k) v[k] = (lane + 64 * k < E) ? ldc(R, 4u * (b * E + lane + 64 * k)) : -INFINITY;
+    int widx[K];
+    float wval[K];
+#pragma unroll
     for (int i = 0; i < K; ++i) {
-      stci(RT, (uint32_t)offsetof(RouteTable, sel) + 4u * (b * 8 + i), sel[i]);
-      stc(RT, (uint32_t)offsetof(RouteTable, w) + 4u * (b * 8 + i), ex[i] / sum);
-      if (p.topk_out) p.topk_out[((size_t)l * B + b) * K + i] = sel[i];
+      float bv = v[0];
+      int bi = lane;
+#pragma unroll
+      for (int k = 1; k < EPL; ++k)
+        if (v[k] > bv) { bv = v[k]; bi = lane + 64 * k; }
+#pragma unroll
+      for (int m = 1; m < 64; m <<= 1) {
+        const float ov = __shfl_xor(bv, m, 64);
+        const int oi = __shfl_xor(bi, m, 64);
+        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
+      }
+      widx[i] = bi;
+      wval[i] = bv;
+#pragma unroll
+      for (int k = 0; k < EPL; ++k)
+        if (lane + 64 * k == bi) v[k] = -INFINITY;
     }
+    const float top = wval[0];
+    // ascending expert order (the MoE sum order)
+#pragma unroll
+    for (int i = 1; i < K; ++i)
+#pragma unroll
+      for (int j = i; j > 0; --j)
+        if (widx[j - 1] > widx[j]) {
+          const int ti = widx[j]; widx[j] = widx[j - 1]; widx[j - 1] = ti;
+          const float tv = wval[j]; wval[j] = wval[j - 1]; wval[j - 1] = tv;
+        }
+    float ex[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) ex[i] = expf(wval[i] - top);
+    float tot;
+    if constexpr (K == 8) {
+      tot = ((ex[0] + ex[1]) + (ex[2] + ex[3])) + ((ex[4] + ex[5]) + (ex[6] + ex[7]));
+    } else {
+      tot = 0.f;
+#pragma unroll
+      for (int i = 0; i < K; ++i) tot += ex[i];
+    }
+    unsigned long long m0 = 0, m1 = 0;
+#pragma unroll
+    for (int i = 0; i < K; ++i) {
+      if (widx[i] < 64) m0 |= 1ull << widx[i]; else m1 |= 1ull << (widx[i] - 64);
+      if (lane == i) {
+        stci(RT, (uint32_t)offsetof(RouteTable, sel) + 4u * (b * 8 + i), widx[i]);
+        stc(RT, (uint32_t)offsetof(RouteTable, w) + 4u * (b * 8 + i), ex[i] / tot);
+        if (p.topk_out) p.topk_out[((size_t)l * B + b) * K + i] = widx[i];
+      }
+    }
+    if (lane == 0) { mask[2 * b] = m0; mask[2 * b + 1] = m1; }
   }
-  // union slots (ascending expert id) and their token lists (ascending b)
-  for (int e = threadIdx.x; e < E; e += NT) {
-    int u = 0;
-    for (int f = 0; f < e; ++f) u += used[f];
-    if (e == E - 1) stci(RT, (uint32_t)offsetof(RouteTable, n_union), u + used[e]);
-    if (!used[e]) continue;
-    stci(RT, (uint32_t)offsetof(RouteTable, union_e) + 4u * u, e);
-    int nt = 0;
-    for (int b = 0; b < B; ++b) {
-      if (!selflag[b * E + e]) continue;
-      stci(RT, (uint32_t)offsetof(RouteTable, tok_bi) + 4u * (u * MAXB + nt), (b << 8) | posi[b * E + e]);
-      ++nt;
+  __syncthreads();
+  // union over the batch (ascending expert ids) and each union slot's tokens (ascending b)
+  if (threadIdx.x < E) {
+    const int e = threadIdx.x;
+    unsigned long long u0 = 0, u1 = 0;
+    for (int b = 0; b < B; ++b) { u0 |= mask[2 * b]; u1 |= mask[2 * b + 1]; }
+    const bool used = e < 64 ? (u0 >> e) & 1 : (u1 >> (e - 64)) & 1;
+    const int slot = e < 64 ? __builtin_popcountll(u0 & ((1ull << e) - 1))
+                            : __builtin_popcountll(u0) + __builtin_popcountll(u1 & ((1ull << (e - 64)) - 1));
+    if (e == E - 1) stci(RT, (uint32_t)offsetof(RouteTable, n_union), __builtin_popcountll(u0) + __builtin_popcountll(u1));
+    if (used) {
+      stci(RT, (uint32_t)offsetof(RouteTable, union_e) + 4u * slot, e);
+      int nt = 0;
+      for (int b = 0; b < B; ++b) {
+        const unsigned long long b0 = mask[2 * b], b1 = mask[2 * b + 1];
+        const bool has = e < 64 ? (b0 >> e) & 1 : (b1 >> (e - 64)) & 1;
+        if (!has) continue;
+        const int i = e < 64 ? __builtin_popcountll(b0 & ((1ull << e) - 1))
+                             : __builtin_popcountll(b0) + __builtin_popcountll(b1 & ((1ull << (e - 64)) - 1));
+        stci(RT, (uint32_t)offsetof(RouteTable, tok_bi) + 4u * (slot * MAXB + nt), (b << 8) | i);
+        ++nt;
+      }
+      stci(RT, (uint32_t)offsetof(RouteTable, n_tok) + 4u * slot, nt);
     }
-    stci(RT, (uint32_t)offsetof(RouteTable, n_tok) + 4u * u, nt);
   }
 }
 
@@ -479,8 +585,8 @@ __device__ __forceinline__ bool op_router(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, E = S::E, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
-  const LayerPtrs& Lp = p.layers[T.layer];
+  constexpr int H = S::H, E = S::E, NP = (Geo<H>::CPL >= 4) ? 2 : 4;
+  const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_router + (size_t)(row0 + r) * H; };
   WBuf<H, NP> A;
@@ -515,15 +621,17 @@ __device__ __forceinline__ bool op_gateup(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, F = S::F, K = S::K, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
+  constexpr int H = S::H, F = S::F, K = S::K, NP = (Geo<H>::CPL >= 4) ? 2 : 4;
   const int l = T.layer, u = T.a0, f0 = T.a1, nf = T.a2;
-  const LayerPtrs& Lp = p.layers[l];
+  const auto& Lp = cst(p.layers)[l];
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  const __amdgpu_buffer_rsrc_t RT = rsrc(p.route + l);
-  const int nu = ldci(RT, (uint32_t)offsetof(RouteTable, n_union));
+  load_route(p, l);
+  MARK(0);
+  const RouteTable& rt = ctl.rt;
+  const int nu = rt.n_union;
   if (u < nu) {
-    const int e = ldci(RT, (uint32_t)offsetof(RouteTable, union_e) + 4u * u);
-    const int ntok = ldci(RT, (uint32_t)offsetof(RouteTable, n_tok) + 4u * u);
+    const int e = rt.union_e[u];
+    const int ntok = rt.n_tok[u];
     const uint16_t* wg = Lp.w_gate + (size_t)e * F * H;
     const uint16_t* wu = Lp.w_up + (size_t)e * F * H;
     auto rowptr = [&](int r) { return r < nf ? wg + (size_t)(f0 + r) * H : wu + (size_t)(f0 + r - nf) * H; };
@@ -531,17 +639,19 @@ __device__ __forceinline__ bool op_gateup(int task) {
     load_block<H, NP>(A, 0, 2 * nf, rowptr);
     if (threadIdx.x < MAXB) {
       const int t = threadIdx.x;
-      const int bi = t < ntok ? ldci(RT, (uint32_t)offsetof(RouteTable, tok_bi) + 4u * (u * MAXB + t)) : 0;
+      const int bi = t < ntok ? rt.tok_bi[u][t] : 0;
       ctl.bis[t] = bi;
       ctl.toks[t] = bi >> 8;
     }
     __syncthreads();
     stage_norm<S>(p, l, ctl.toks, ntok, Lp.attn_norm, sm, T.id);
+    MARK(1);
     float* gu = sm + (size_t)TB * H;                 // [TB][2 nf]
     gemv_stream<H, NP, TB>(A, true, 2 * nf, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)t * H; },
         [&](int r, int t, float v) { gu[t * 2 * nf + r] = v; });
     __syncthreads();
+    MARK(2);
     const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
     for (int i = threadIdx.x; i < ntok * nf; i += NT) {
       const int t = i / nf, f = i % nf;
@@ -551,6 +661,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
       stc(Hb, 4u * (((bi >> 8) * K + (bi & 255)) * F + f0 + f), hv);
     }
   }
+  drain();
+  MARK(3);
   signal(p, ctl, T.sig, false);
   return true;
 }
@@ -558,23 +670,34 @@ __device__ __forceinline__ bool op_gateup(int task) {
 // Split-KV paged GQA decode attention for one (sequence b, KV group g, key range) with fused RoPE
 // (P3 "Key Technologies and Architecture": restructured paged attention, fused RoPE; P1 "From
 // demo to a full serving system": paged KV, ragged lengths). The split holding the new position
-// writes the new K/V into the cache first and scores it. The last split of (b, g) to finish merges
-// all partials in split order (log-sum-exp) and publishes the group's attention output.
+// writes the new K/V into the cache and scores it in rounded form. The last split of (b, g) to
+// finish merges all partials in split order (log-sum-exp) and publishes the group's output.
+//
+// Scores run on the matrix cores: S = Q K^T per block of 16 keys (one KV page, 4 KB contiguous) is
+// a 16x16x32 bf16 MFMA chain whose A rows are the group's HPG query heads split into bf16 high and
+// low parts (q = hi + lo to 2^-16), so fp32 accuracy is kept while the operand takes 16 registers.
+// Every K of a 256-key chunk is requested before the dependency wait; V of the chunk is requested
+// as soon as the scores are done (the K registers are free then). P V runs on the vector units.
 template <class S>
 __device__ __forceinline__ bool op_attn(int task) {
   CParams& p = P();
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
+  typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
   constexpr int D = S::D, HPG = S::HPG, LPK = D / 8, KPW = 64 / LPK, KPI = NWAVE * KPW;
-  constexpr int NB = 4;   // keys per lane per register block
-  static_assert(LPK >= HPG / 2 && LPK <= 64, "");
+  constexpr int KB = D / 32;             // MFMA k-blocks per head vector
+  constexpr int KC = 256;                // keys per chunk
+  constexpr int GPW = KC / 16 / NWAVE;   // 16-key column blocks per wave per chunk
+  constexpr int VPL = KC / KPI;          // V loads per lane per chunk (P V layout)
+  static_assert(2 * HPG <= 16 && HPG % 4 == 0 && D % 32 == 0 && KC % KPI == 0, "");
   const int l = T.layer, b = T.a0, g = T.a1, k0 = T.a2, k1 = T.a3;
   const int pbase = T.a4, s_idx = T.a5 & 0xffff, nsplit = T.a5 >> 16;
-  const LayerPtrs& Lp = p.layers[l];
+  const auto& Lp = cst(p.layers)[l];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int li = lane % LPK, slot = wave * KPW + lane / LPK;
-  const int n_ctx = p.seq_lens[b], pos = p.positions[b];
+  const int li = lane % LPK, slot = wave * KPW + lane / LPK;   // P V layout: key slot, 8-dim chunk
+  const int col = lane & 15, grp = lane >> 4;                   // MFMA layout
+  const int n_ctx = cst(p.seq_lens)[b], pos = cst(p.positions)[b];
   const bool last = k1 < 0;
   if (pos != n_ctx - 1 || pos < 0 || n_ctx > p.max_pages * PAGE) {
     if (threadIdx.x == 0) raise_error(p, DEV_BAD_POS, T.id, -1, (uint32_t)n_ctx, (uint32_t)pos, (uint32_t)b);
@@ -588,46 +711,62 @@ __device__ __forceinline__ bool op_attn(int task) {
     if (threadIdx.x == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)k0, (uint32_t)pos, (uint32_t)b);
     return false;
   }
-  const int32_t* bt = p.block_tables + (size_t)b * p.max_pages;
-  // key j of this task -> address of its chunk li in the K (or V) cache
-  auto kv_off = [&](int j) -> size_t {
-    int page = bt[j / PAGE];
-    if (page < 0 || page >= p.num_pages) {
-      raise_error(p, DEV_BAD_PAGE, T.id, -1, (uint32_t)p.num_pages, (uint32_t)page, (uint32_t)j);
-      page = 0;
-    }
-    return (((size_t)page * S::HKV + g) * PAGE + (j % PAGE)) * D + 8 * li;
-  };
-  const int nit = (nk + KPI - 1) / KPI;           // key iterations
-  const int nblk = (nit + NB - 1) / NB;
-  auto load_kv = [&](u4 (&buf)[NB], const uint16_t* cache, int blk) {
-#pragma unroll
-    for (int q = 0; q < NB; ++q) {
-      const int j = k0 + (blk * NB + q) * KPI + slot;
-      buf[q] = (j < kend) ? ldw(cache + kv_off(j)) : u4{0u, 0u, 0u, 0u};
-    }
-  };
-  // RoPE table for this position (angles in float64, as the oracle's reading R3)
+  // LDS layout
   float* cs = sm;                                  // [D/2] cos, [D/2] sin
   float* sbuf = sm + D;                            // [SPLIT_MAX + 1][HPG] scores -> probabilities
   float* vnew = sbuf + (SPLIT_MAX + 1) * HPG;      // [D]
   float* ml = vnew + D;                            // [2][HPG]
   float* obuf = ml + 2 * HPG;                      // [NWAVE][LPK][HPG * 8]
+  int* pg = reinterpret_cast<int*>(obuf + NWAVE * LPK * HPG * 8);   // [SPLIT_MAX / PAGE + 1] page ids
+  uint32_t* knew = reinterpret_cast<uint32_t*>(pg + SPLIT_MAX / PAGE + 4);   // [D / 2] new key, bf16 pairs
+  {
+    const __attribute__((address_space(4))) int32_t* bt = cst(p.block_tables) + (size_t)b * p.max_pages + k0 / PAGE;
+    const int npg = (ntot + PAGE - 1) / PAGE;
+    for (int i = threadIdx.x; i < npg; i += NT) {
+      int page = bt[i];
+      if (page < 0 || page >= p.num_pages) {
+        raise_error(p, DEV_BAD_PAGE, T.id, -1, (uint32_t)p.num_pages, (uint32_t)page, (uint32_t)(k0 / PAGE + i));
+        page = 0;
+      }
+      pg[i] = page;
+    }
+  }
   if (threadIdx.x < D / 2) {
-    const double ang = (double)pos * p.inv_freq[threadIdx.x];
+    const double ang = (double)pos * cst(p.inv_freq)[threadIdx.x];
     cs[threadIdx.x] = (float)cos(ang);
     cs[D / 2 + threadIdx.x] = (float)sin(ang);
   }
-  // prefetch the first K and V blocks (old keys do not depend on this step's activations)
-  u4 kb[NB], vb[NB];
-  if (nblk > 0) { load_kv(kb, Lp.k_cache, 0); load_kv(vb, Lp.v_cache, 0); }
+  __syncthreads();
+  // key j, dims d0..d0+7 -> element offset in the K (or V) cache
+  auto kaddr = [&](int j, int d0) -> size_t {
+    return (((size_t)pg[(j - k0) / PAGE] * S::HKV + g) * PAGE + (j % PAGE)) * D + d0;
+  };
+  const int nchunk = (ntot + KC - 1) / KC;
+  u4 kr[GPW][KB];       // MFMA B operands: key k0 + c*KC + (wave + NWAVE*i)*16 + col, dims 32kb + 8grp
+  auto load_k = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int j = k0 + c * KC + (wave + NWAVE * i) * 16 + col;
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+        kr[i][kb] = (j < kend) ? ldw(Lp.k_cache + kaddr(j, 32 * kb + 8 * grp)) : u4{0u, 0u, 0u, 0u};
+    }
+  };
+  u4 vr[VPL];           // P V layout: key k0 + c*KC + q*KPI + slot, dims 8li
+  auto load_v = [&](int c) {
+#pragma unroll
+    for (int q = 0; q < VPL; ++q) {
+      const int j = k0 + c * KC + q * KPI + slot;
+      vr[q] = (j < kend) ? ldw(Lp.v_cache + kaddr(j, 8 * li)) : u4{0u, 0u, 0u, 0u};
+    }
+  };
+  load_k(0);            // old keys do not depend on this step's activations
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  // rotated query chunk of this lane for the HPG heads of group g
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + ((size_t)l * MAXB + b) * S::QKVR);
   const float sd = sqrtf((float)D);
-  float q[HPG][8];
-  auto rope_chunk = [&](uint32_t base, float (&out)[8]) {   // base: float index of a head vector
-    const int d0 = 8 * li, pd0 = d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
+  // RoPE of dims d0..d0+7 of the head vector at float index `base` (rotate-half pairs d, d +- D/2)
+  auto rope8 = [&](uint32_t base, int d0, float (&out)[8]) {
+    const int pd0 = d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
     const f4 x0 = ldc4(Q, 4u * (base + d0)), x1 = ldc4(Q, 4u * (base + d0 + 4));
     const f4 y0 = ldc4(Q, 4u * (base + pd0)), y1 = ldc4(Q, 4u * (base + pd0 + 4));
     const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -639,90 +778,78 @@ __device__ __forceinline__ bool op_attn(int task) {
       out[m] = d0 < D / 2 ? xs[m] * c - ys[m] * s : xs[m] * c + ys[m] * s;
     }
   };
+  // MFMA A operand: row r = col; r < HPG: head r, high part; HPG <= r < 2 HPG: head r - HPG, low part
+  bf8 qa[KB];
+  {
+    const int h = col % HPG;
+    const bool valid = col < 2 * HPG, lo = col >= HPG;
 #pragma unroll
-  for (int hh = 0; hh < HPG; ++hh) rope_chunk((uint32_t)((g * HPG + hh) * D), q[hh]);
-
-  // ---- pass A: scores s[j][hh] = (k_j . q_hh) / sqrt(D)
-  auto score_chunk = [&](const float (&kv)[8], int jj) {
-    float part[HPG];
+    for (int kb = 0; kb < KB; ++kb) {
+      float x[8];
+      rope8((uint32_t)((g * HPG + h) * D), 32 * kb + 8 * grp, x);
+      uint32_t w[4];
 #pragma unroll
-    for (int hh = 0; hh < HPG; ++hh) {
-      float a = 0.f;
-#pragma unroll
-      for (int m = 0; m < 8; ++m) a = __builtin_fmaf(q[hh][m], kv[m], a);
-      part[hh] = a;
-    }
-    // reduce-scatter over the LPK lanes of this key: after log2(HPG) halvings each lane keeps one
-    // head; the remaining steps finish the sum. Lane li ends with head li >> (log2 LPK - log2 HPG).
-    constexpr int LH = __builtin_ctz(HPG), LL = __builtin_ctz(LPK);
-    float cur[HPG];
-#pragma unroll
-    for (int hh = 0; hh < HPG; ++hh) cur[hh] = part[hh];
-    int n = HPG;
-#pragma unroll
-    for (int st = 0; st < LH; ++st) {
-      const int mask = LPK >> (st + 1);
-      const bool hi = (li & mask) != 0;
-      n >>= 1;
-#pragma unroll
-      for (int m = 0; m < HPG / 2; ++m) {
-        if (m < n) {
-          const float keep = hi ? cur[n + m] : cur[m];
-          const float send = hi ? cur[m] : cur[n + m];
-          cur[m] = keep + __shfl_xor(send, mask, 64);
-        }
+      for (int m = 0; m < 4; ++m) {
+        uint32_t a = f2bf(x[2 * m]), c = f2bf(x[2 * m + 1]);
+        if (lo) { a = f2bf(x[2 * m] - bf1((uint16_t)a)); c = f2bf(x[2 * m + 1] - bf1((uint16_t)c)); }
+        w[m] = valid ? (a | (c << 16)) : 0u;
       }
+      qa[kb] = __builtin_bit_cast(bf8, u4{w[0], w[1], w[2], w[3]});
     }
-    float sc = cur[0];
-#pragma unroll
-    for (int st = LH; st < LL; ++st) sc += __shfl_xor(sc, LPK >> (st + 1), 64);
-    const int hh = li >> (LL - LH);
-    if ((li & ((1 << (LL - LH)) - 1)) == 0 && jj >= 0) sbuf[jj * HPG + hh] = sc / sd;
-  };
-  for (int blk = 0; blk < nblk; ++blk) {
-    u4 kn[NB];
-    if (blk + 1 < nblk) load_kv(kn, Lp.k_cache, blk + 1);
-#pragma unroll
-    for (int qq = 0; qq < NB; ++qq) {
-      const int jj = (blk * NB + qq) * KPI + slot;
-      const float kv[8] = {bf_lo(kb[qq].x), bf_hi(kb[qq].x), bf_lo(kb[qq].y), bf_hi(kb[qq].y),
-                           bf_lo(kb[qq].z), bf_hi(kb[qq].z), bf_lo(kb[qq].w), bf_hi(kb[qq].w)};
-      score_chunk(kv, jj < nk ? jj : -1);
-    }
-#pragma unroll
-    for (int qq = 0; qq < NB; ++qq) kb[qq] = kn[qq];
   }
+  MARK(0);
   if (last) {
     // new key/value: RoPE(k) and v from this step's QKV rows, rounded to bf16 (the cache format),
-    // written at slot pos, and scored in rounded form by key slot 0 (wave 0, lanes < LPK).
+    // written at slot pos, and kept in LDS for scoring and for P V
     if (wave == 0 && lane < LPK) {
-      float kr[8];
-      rope_chunk((uint32_t)(S::HQ * D + g * D), kr);
+      float kr8[8];
+      rope8((uint32_t)(S::HQ * D + g * D), 8 * li, kr8);
       const uint32_t vbase = (uint32_t)((S::HQ + S::HKV) * D + g * D + 8 * li);
       const f4 v0 = ldc4(Q, 4u * vbase), v1 = ldc4(Q, 4u * (vbase + 4));
       const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
       uint32_t kw[4], vw[4];
-      float kq[8];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
-        const uint32_t ka = f2bf(kr[2 * m]), kb2 = f2bf(kr[2 * m + 1]);
+        const uint32_t ka = f2bf(kr8[2 * m]), kb2 = f2bf(kr8[2 * m + 1]);
         const uint32_t va = f2bf(vv[2 * m]), vb2 = f2bf(vv[2 * m + 1]);
         kw[m] = ka | (kb2 << 16);
         vw[m] = va | (vb2 << 16);
-        kq[2 * m] = bf1((uint16_t)ka); kq[2 * m + 1] = bf1((uint16_t)kb2);
+        knew[4 * li + m] = kw[m];
         vnew[8 * li + 2 * m] = bf1((uint16_t)va); vnew[8 * li + 2 * m + 1] = bf1((uint16_t)vb2);
       }
-      const size_t off = kv_off(pos);
+      const size_t off = kaddr(pos, 8 * li);
       *reinterpret_cast<u4*>(Lp.k_cache + off) = u4{kw[0], kw[1], kw[2], kw[3]};
       *reinterpret_cast<u4*>(Lp.v_cache + off) = u4{vw[0], vw[1], vw[2], vw[3]};
-      score_chunk(kq, nk);
-    } else if (wave == 0) {
-      // the other lanes of wave 0 take part in the shuffles of score_chunk with dummy data
-      float dummy[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      score_chunk(dummy, -1);
+    }
+    __syncthreads();
+  }
+  // ---- pass A: s[j][hh] = (k_j . q_hh) / sqrt(D) on the matrix cores
+  for (int c = 0; c < nchunk; ++c) {
+    if (c > 0) load_k(c);
+#pragma unroll
+    for (int i = 0; i < GPW; ++i) {
+      const int jb = c * KC + (wave + NWAVE * i) * 16;   // first key of the block, relative to k0
+      if (jb >= ntot) continue;                           // uniform in the wave
+      const bool is_new = last && jb + col == nk;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        u4 kv = kr[i][kb];
+        if (is_new) kv = *reinterpret_cast<const u4*>(knew + 16 * kb + 4 * grp);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], __builtin_bit_cast(bf8, kv), acc, 0, 0, 0);
+      }
+      // rows r and r + HPG hold the high and low parts of the same head: add them
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], 4 * HPG, 64);
+      if (grp < HPG / 4 && jb + col < ntot) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) sbuf[(jb + col) * HPG + 4 * grp + j] = acc[j] / sd;
+      }
     }
   }
+  load_v(0);            // V streams while the softmax statistics are computed
   __syncthreads();
+  MARK(1);
   // ---- softmax statistics per head (wave w handles heads w, w + 4, ...)
   for (int hh = wave; hh < HPG; hh += NWAVE) {
     float m = -INFINITY;
@@ -753,20 +880,17 @@ __device__ __forceinline__ bool op_attn(int task) {
       for (int m = 0; m < 8; ++m) o[hh][m] = __builtin_fmaf(pj, vv[m], o[hh][m]);
     }
   };
-  for (int blk = 0; blk < nblk; ++blk) {
-    u4 vn[NB];
-    if (blk + 1 < nblk) load_kv(vn, Lp.v_cache, blk + 1);
+  for (int c = 0; c < nchunk; ++c) {
+    if (c > 0) load_v(c);
 #pragma unroll
-    for (int qq = 0; qq < NB; ++qq) {
-      const int jj = (blk * NB + qq) * KPI + slot;
+    for (int q = 0; q < VPL; ++q) {
+      const int jj = c * KC + q * KPI + slot;
       if (jj < nk) {
-        const float vv[8] = {bf_lo(vb[qq].x), bf_hi(vb[qq].x), bf_lo(vb[qq].y), bf_hi(vb[qq].y),
-                             bf_lo(vb[qq].z), bf_hi(vb[qq].z), bf_lo(vb[qq].w), bf_hi(vb[qq].w)};
+        const float vv[8] = {bf_lo(vr[q].x), bf_hi(vr[q].x), bf_lo(vr[q].y), bf_hi(vr[q].y),
+                             bf_lo(vr[q].z), bf_hi(vr[q].z), bf_lo(vr[q].w), bf_hi(vr[q].w)};
         accum(vv, jj);
       }
     }
-#pragma unroll
-    for (int qq = 0; qq < NB; ++qq) vb[qq] = vn[qq];
   }
   if (last && slot == 0) {
     float vv[8];
@@ -774,6 +898,7 @@ __device__ __forceinline__ bool op_attn(int task) {
     for (int m = 0; m < 8; ++m) vv[m] = vnew[8 * li + m];
     accum(vv, nk);
   }
+  MARK(2);
   // reduce o over the key slots of the wave (lanes sharing li), then over the waves via LDS
 #pragma unroll
   for (int hh = 0; hh < HPG; ++hh)
@@ -781,7 +906,7 @@ __device__ __forceinline__ bool op_attn(int task) {
     for (int m = 0; m < 8; ++m) {
       float v = o[hh][m];
 #pragma unroll
-      for (int s = LPK; s < 64; s <<= 1) v += __shfl_xor(v, s, 64);
+      for (int s2 = LPK; s2 < 64; s2 <<= 1) v += __shfl_xor(v, s2, 64);
       o[hh][m] = v;
     }
   if (lane < LPK) {
@@ -793,31 +918,67 @@ __device__ __forceinline__ bool op_attn(int task) {
   __syncthreads();
   // partial: m[HPG], l[HPG], o[HPG][D] (unnormalised)
   const size_t part = ((size_t)l * p.parts_per_layer + pbase + s_idx) * S::PART;
-  const __amdgpu_buffer_rsrc_t P = rsrc(p.apart + part);
+  const __amdgpu_buffer_rsrc_t Pw = rsrc(p.apart + part);
   for (int i = threadIdx.x; i < HPG * D; i += NT) {
     const int hh = i / D, d = i % D, c = d / 8, m = d % 8;
     float v = 0.f;
     for (int w = 0; w < NWAVE; ++w) v += obuf[(w * LPK + c) * HPG * 8 + hh * 8 + m];
-    stc(P, 4u * (2 * HPG + i), v);
+    stc(Pw, 4u * (2 * HPG + i), v);
   }
-  if (threadIdx.x < 2 * HPG) stc(P, 4u * threadIdx.x, ml[threadIdx.x]);
+  if (threadIdx.x < 2 * HPG) stc(Pw, 4u * threadIdx.x, ml[threadIdx.x]);
   const uint32_t old = signal(p, ctl, T.sig, true);
+  MARK(3);
   if (old + 1 == (uint32_t)nsplit) {
-    // last arriver: merge the nsplit partials of (b, g) in split order
+    // last arriver: merge the nsplit partials of (b, g) in split order (log-sum-exp). The m and l of
+    // every split come in one round trip into LDS; each thread then owns 4 consecutive outputs of
+    // the HPG x D block and reads them from every partial with independent 16-byte loads.
     const __amdgpu_buffer_rsrc_t P0 = rsrc(p.apart + ((size_t)l * p.parts_per_layer + pbase) * S::PART);
-    const __amdgpu_buffer_rsrc_t A = rsrc(p.attn + ((size_t)l * MAXB + b) * S::AD + g * HPG * D);
-    for (int i = threadIdx.x; i < HPG * D; i += NT) {
-      const int hh = i / D;
+    float* msl = sbuf;          // [nsplit][2 * HPG] m then l; m is overwritten by exp(m - M)
+    float* linv = ml;           // [HPG] sum over splits of l * exp(m - M)
+    if (nsplit > MERGE_MAX) {
+      if (threadIdx.x == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)MERGE_MAX, (uint32_t)nsplit, (uint32_t)b);
+      return false;
+    }
+    for (int i = threadIdx.x; i < nsplit * 2 * HPG; i += NT)
+      msl[i] = ldc(P0, 4u * ((i / (2 * HPG)) * S::PART + i % (2 * HPG)));
+    __syncthreads();
+    for (int hh = threadIdx.x; hh < HPG; hh += NT) {
       float M = -INFINITY;
-      for (int s = 0; s < nsplit; ++s) M = fmaxf(M, ldc(P0, 4u * (s * S::PART + hh)));
-      float L = 0.f, O = 0.f;
-      for (int s = 0; s < nsplit; ++s) {
-        const float ms = ldc(P0, 4u * (s * S::PART + hh));
+      for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, msl[s2 * 2 * HPG + hh]);
+      float Lsum = 0.f;
+      for (int s2 = 0; s2 < nsplit; ++s2) {
+        const float ms = msl[s2 * 2 * HPG + hh];
         const float sc = ms == -INFINITY ? 0.f : expf(ms - M);
-        L = __builtin_fmaf(ldc(P0, 4u * (s * S::PART + HPG + hh)), sc, L);
-        O = __builtin_fmaf(ldc(P0, 4u * (s * S::PART + 2 * HPG + i)), sc, O);
+        msl[s2 * 2 * HPG + hh] = sc;
+        Lsum = __builtin_fmaf(msl[s2 * 2 * HPG + HPG + hh], sc, Lsum);
       }
-      stc(A, 4u * i, O / L);
+      linv[hh] = Lsum;
+    }
+    __syncthreads();
+    const __amdgpu_buffer_rsrc_t A = rsrc(p.attn + ((size_t)l * MAXB + b) * S::AD + g * HPG * D);
+    for (int i4 = threadIdx.x * 4; i4 < HPG * D; i4 += NT * 4) {
+      const int hh = i4 / D;
+      f4 acc = {0.f, 0.f, 0.f, 0.f};
+      int s2 = 0;
+      for (; s2 + 8 <= nsplit; s2 += 8) {
+        f4 o[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) o[u] = ldc4(P0, 4u * ((s2 + u) * S::PART + 2 * HPG + i4));
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const float sc = msl[(s2 + u) * 2 * HPG + hh];
+          acc.x = __builtin_fmaf(o[u].x, sc, acc.x); acc.y = __builtin_fmaf(o[u].y, sc, acc.y);
+          acc.z = __builtin_fmaf(o[u].z, sc, acc.z); acc.w = __builtin_fmaf(o[u].w, sc, acc.w);
+        }
+      }
+      for (; s2 < nsplit; ++s2) {
+        const f4 o = ldc4(P0, 4u * (s2 * S::PART + 2 * HPG + i4));
+        const float sc = msl[s2 * 2 * HPG + hh];
+        acc.x = __builtin_fmaf(o.x, sc, acc.x); acc.y = __builtin_fmaf(o.y, sc, acc.y);
+        acc.z = __builtin_fmaf(o.z, sc, acc.z); acc.w = __builtin_fmaf(o.w, sc, acc.w);
+      }
+      const float Lh = linv[hh];
+      stc4(A, 4u * i4, f4{acc.x / Lh, acc.y / Lh, acc.z / Lh, acc.w / Lh});
     }
     signal(p, ctl, T.sig2, false);
   }
@@ -839,13 +1000,14 @@ __device__ __forceinline__ bool op_out(int task) {
   constexpr int NPO = (OUT_MAXR + NWAVE * Geo<AD>::RPP - 1) / (NWAVE * Geo<AD>::RPP);
   constexpr int NPD = (OUT_MAXR * K + NWAVE * Geo<F>::RPP - 1) / (NWAVE * Geo<F>::RPP);
   const int l = T.layer, row0 = T.a0, nrows = T.a1;
-  const LayerPtrs& Lp = p.layers[l];
+  const auto& Lp = cst(p.layers)[l];
   auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * AD; };
   WBuf<AD, NPO> WO;
   const bool pre = !(p.flags & 2);
   if (pre) load_block<AD, NPO>(WO, 0, nrows, orow);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;      // routing known
-  const __amdgpu_buffer_rsrc_t RT = rsrc(p.route + l);
+  load_route(p, l);
+  const RouteTable& rt = ctl.rt;
   float* a_s = sm;                                                     // [AD]
   float* h_s = sm + AD;                                                // [K][F]
   float* o_s = h_s + K * F;                                            // [OUT_MAXR]
@@ -857,7 +1019,7 @@ __device__ __forceinline__ bool op_out(int task) {
   for (int b = 0; b < p.B; ++b) {
     int sel[K];
 #pragma unroll
-    for (int i = 0; i < K; ++i) sel[i] = ldci(RT, (uint32_t)offsetof(RouteTable, sel) + 4u * (b * 8 + i));
+    for (int i = 0; i < K; ++i) sel[i] = rt.sel[b][i];
     auto drow = [&](int q) {   // q = i * nrows + r
       const int i = q / nrows, r = q % nrows;
       int e = 0;
@@ -868,12 +1030,13 @@ __device__ __forceinline__ bool op_out(int task) {
     WBuf<F, NPD> WD;
     load_block<F, NPD>(WD, 0, K * nrows, drow);
     if (b == 0) {
-      if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;  // all MoE slices
-      if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;  // attention of all groups
+      // all MoE slices and the attention of every KV group
+      if (!wait_ge2(p, ctl, T.w1, (uint32_t)T.t1, T.a2, (uint32_t)T.a3, T.id)) return false;
     }
     for (int i = threadIdx.x * 4; i < AD; i += NT * 4) *reinterpret_cast<f4*>(a_s + i) = ldc4(At, 4u * (b * AD + i));
     for (int i = threadIdx.x * 4; i < K * F; i += NT * 4) *reinterpret_cast<f4*>(h_s + i) = ldc4(Hb, 4u * (b * K * F + i));
     __syncthreads();
+    if (b == 0) MARK(0);
     compute_block<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
                               [&](int r, int t, float v) { o_s[r] = v; });
     compute_block<F, NPD, 1>(WD, 0, K * nrows, 1, [&](int q, int t) { return h_s + (q / nrows) * F; },
@@ -883,7 +1046,7 @@ __device__ __forceinline__ bool op_out(int task) {
       const int r = threadIdx.x, row = row0 + r;
       float xv;
       if (l == 0) {
-        int tok = p.tokens[b];
+        int tok = cst(p.tokens)[b];
         tok = (tok < 0 || tok >= p.V) ? 0 : tok;
         xv = bf1(p.embed[(size_t)tok * H + row]);
       } else {
@@ -891,13 +1054,16 @@ __device__ __forceinline__ bool op_out(int task) {
       }
       float moe = 0.f;
       for (int i = 0; i < K; ++i)
-        moe = moe + ldc(RT, (uint32_t)offsetof(RouteTable, w) + 4u * (b * 8 + i)) * y_s[i * OUT_MAXR + r];
+        moe = moe + rt.w[b][i] * y_s[i * OUT_MAXR + r];
       const float xn = (xv + o_s[r]) + moe;
       stc(Xn, 4u * (b * H + row), xn);
       if (p.hidden_out && l == p.L - 1) p.hidden_out[(size_t)b * H + row] = xn;
     }
     __syncthreads();
   }
+  MARK(1);
+  drain();
+  MARK(2);
   signal(p, ctl, T.sig, false);
   return true;
 }
@@ -910,7 +1076,7 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 4 : 8, RPP = Geo<H>::RPP;
+  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 2 : 4, RPP = Geo<H>::RPP;
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return p.lm_head + (size_t)(row0 + r) * H; };
   WBuf<H, NP> A;
@@ -989,11 +1155,15 @@ __device__ void finish(CParams& p, Ctl& ctl) {
 template <class S, int TB>
 __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
   CParams& p = P();
-  const int qs = p.qoff[blockIdx.x], qe = p.qoff[blockIdx.x + 1];
+  const int qs = cst(p.qoff)[blockIdx.x], qe = cst(p.qoff)[blockIdx.x + 1];
   const bool trace = (p.flags & 1) && p.trace;
   for (int ti = qs; ti < qe; ++ti) {
-    const int op = p.tasks[(size_t)ti * DESC_WORDS + D_OP];
+    const int op = cst(p.tasks)[(size_t)ti * DESC_WORDS + D_OP];
     const uint64_t t_start = trace ? now() : 0;
+    if (trace && threadIdx.x == 0) {
+      ctl_s.t_ready = t_start;
+      ctl_s.mark[0] = ctl_s.mark[1] = ctl_s.mark[2] = ctl_s.mark[3] = 0;
+    }
     bool ok;
     switch (op) {
       case OP_QKV: ok = op_qkv<S, TB>(ti); break;
@@ -1007,11 +1177,12 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
         ok = false;
     }
     if (trace && threadIdx.x == 0) {
-      unsigned long long* tr = p.trace + (size_t)ti * 4;
+      unsigned long long* tr = p.trace + (size_t)ti * 8;
       tr[0] = (unsigned long long)ti | ((unsigned long long)blockIdx.x << 32);
       tr[1] = t_start;
-      tr[2] = 0;
+      tr[2] = ctl_s.t_ready;
       tr[3] = now();
+      tr[4] = ctl_s.mark[0]; tr[5] = ctl_s.mark[1]; tr[6] = ctl_s.mark[2]; tr[7] = ctl_s.mark[3];
     }
     if (!ok) break;
     __syncthreads();
@@ -1026,7 +1197,7 @@ static size_t lds_bytes(int tb) {
   // norm-staged activations + GEMV scratch, attention buffers, OUT staging: the largest wins
   const size_t act = (size_t)tb * S::H * 4 + (size_t)tb * 2 * 64 * 4 + 4096;
   const size_t att = ((size_t)S::D + (SPLIT_MAX + 1) * S::HPG + S::D + 2 * S::HPG +
-                      (size_t)NWAVE * (S::D / 8) * S::HPG * 8) * 4;
+                      (size_t)NWAVE * (S::D / 8) * S::HPG * 8 + SPLIT_MAX / PAGE + 4 + S::D / 2) * 4;
   const size_t out = ((size_t)S::AD + S::K * S::F + OUT_MAXR + S::K * OUT_MAXR) * 4;
   const size_t rte = ((size_t)MAXB * S::E * 3 + S::E) * 4 + 256;
   size_t m = act;
@@ -1074,6 +1245,7 @@ hipError_t step_occupancy(int shape, int batch, int* blocks_per_cu) {
 }
 
 int split_max() { return SPLIT_MAX; }
+int merge_max() { return MERGE_MAX; }
 int out_max_rows() { return OUT_MAXR; }
 
 }  // namespace mk

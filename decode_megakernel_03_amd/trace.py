@@ -1,0 +1,92 @@
+"""Decode the per-task trace of a step (MK_FLAG_TRACE) into timings and a Perfetto/Chrome JSON.
+
+Each task record is eight uint64: (task id | worker << 32, t_start, t_ready, t_end, mark0..3) in
+100 MHz ticks of the GPU's constant real-time clock: t_ready is when its last dependency wait
+ended, so t_ready - t_start is time spent waiting (with its first weight block already in flight)
+and t_end - t_ready is time spent executing and signalling; marks are op-specific phase ends
+(attention: query loaded, scores, softmax + PV, partial signalled; expert slice: routing table
+loaded, activations staged, GEMV done), 0 where unset.
+"""
+
+import json
+
+import numpy as np
+
+OPS = {1: "qkv", 2: "router", 3: "gateup", 4: "attn", 5: "out", 6: "lmhead"}
+TICK_US = 0.01
+
+
+def decode(trace, tasks):
+    """trace uint64 [n_tasks, 4]; tasks int32 [n_tasks, 16] (descriptors). Returns a record array."""
+    t0 = trace[:, 1].min()
+    rec = np.zeros(len(trace), dtype=[("id", "i4"), ("worker", "i4"), ("op", "i4"), ("layer", "i4"),
+                                      ("start", "f8"), ("ready", "f8"), ("end", "f8"), ("mark", "f8", (4,))])
+    rec["id"] = (trace[:, 0] & 0xFFFFFFFF).astype(np.int64)
+    rec["worker"] = (trace[:, 0] >> 32).astype(np.int64)
+    rec["op"] = tasks[:, 0]
+    rec["layer"] = tasks[:, 1]
+    rec["start"] = (trace[:, 1] - t0) * TICK_US
+    rec["ready"] = (trace[:, 2] - t0) * TICK_US
+    rec["end"] = (trace[:, 3] - t0) * TICK_US
+    marks = trace[:, 4:8].astype(np.float64)
+    rec["mark"] = np.where(marks > 0, (marks - float(t0)) * TICK_US, np.nan)
+    return rec
+
+
+def summary(rec, n_workers):
+    lines = []
+    span = rec["end"].max()
+    busy = np.zeros(n_workers)
+    wait = np.zeros(n_workers)
+    for r in rec:
+        busy[r["worker"]] += r["end"] - r["ready"]
+        wait[r["worker"]] += r["ready"] - r["start"]
+    lines.append(f"step span {span:.1f} us; per worker: exec {busy.mean():.1f} us ({busy.mean() / span:.0%}), "
+                 f"waiting {wait.mean():.1f} us, idle between tasks {span - busy.mean() - wait.mean():.1f} us")
+    for op, name in OPS.items():
+        m = rec["op"] == op
+        if not m.any():
+            continue
+        r = rec[m]
+        lines.append(f"  {name:7s} n={m.sum():6d}  wait {np.mean(r['ready'] - r['start']):7.2f} us  "
+                     f"exec {np.mean(r['end'] - r['ready']):7.2f} us (p90 {np.percentile(r['end'] - r['ready'], 90):6.2f})")
+        prev = r["ready"]
+        parts = []
+        for i in range(4):
+            mk_i = r["mark"][:, i]
+            ok = ~np.isnan(mk_i)
+            if ok.any():
+                parts.append(f"m{i} +{np.mean(mk_i[ok] - prev[ok]):.2f}")
+                prev = np.where(ok, mk_i, prev)
+        if parts:
+            parts.append(f"end +{np.mean(r['end'] - prev):.2f}")
+            lines.append("          phases (us, cumulative steps): " + ", ".join(parts))
+    layers = sorted(set(rec["layer"].tolist()))
+    lines.append("  layer  qkv_end  route_end  gateup_end  attn_end  out_end   (us from step start)")
+    for l in layers[: min(len(layers), 4)] + layers[-2:]:
+        r = rec[rec["layer"] == l]
+        def last(op):
+            x = r[r["op"] == op]
+            return x["end"].max() if len(x) else float("nan")
+        lines.append(f"  {l:5d} {last(1):8.1f} {last(2):10.1f} {last(3):11.1f} {last(4):9.1f} {last(5):8.1f}")
+    per_layer = []
+    for l in layers:
+        r = rec[(rec["layer"] == l) & (rec["op"] == 5)]
+        if len(r):
+            per_layer.append(r["end"].max())
+    if len(per_layer) > 2:
+        lines.append(f"  mean layer time {np.mean(np.diff(per_layer)):.1f} us")
+    return "\n".join(lines)
+
+
+def chrome_json(rec, path):
+    ev = []
+    for r in rec:
+        name = OPS.get(int(r["op"]), str(r["op"]))
+        if r["ready"] > r["start"]:
+            ev.append({"name": f"wait {name}", "ph": "X", "pid": 0, "tid": int(r["worker"]), "ts": float(r["start"]),
+                       "dur": float(r["ready"] - r["start"]), "args": {"layer": int(r["layer"])}})
+        ev.append({"name": name, "ph": "X", "pid": 0, "tid": int(r["worker"]), "ts": float(r["ready"]),
+                   "dur": float(r["end"] - r["ready"]), "args": {"layer": int(r["layer"]), "task": int(r["id"])}})
+    with open(path, "w") as f:
+        json.dump({"traceEvents": ev}, f)

@@ -148,8 +148,9 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
  *   argmax_out int32 [B]       greedy token (first index of the maximum logit)
  *   topk_out int32 [L, B, k]   routed experts per layer and token, ascending expert index
  *   hidden_out float32 [B, H]  residual stream after the last layer
- *   trace_out uint64 [tasks, 4] when MK_FLAG_TRACE: {task id | worker << 32, t_start, t_ready,
- *                              t_end} in 100 MHz ticks (size via mk_plan_info). */
+ *   trace_out uint64 [tasks, 8] when MK_FLAG_TRACE: {task id | worker << 32, t_start, t_ready,
+ *                              t_end, mark0..mark3} in 100 MHz ticks (size via mk_plan_info);
+ *                              marks are op-specific phase ends, 0 where an op sets none. */
 mk_status mk_set_step_outputs(mk_engine* e, int32_t* argmax_out, int32_t* topk_out,
                               float* hidden_out, uint64_t* trace_out);
 

@@ -53,7 +53,7 @@ class LazyWeights:
                                                           synth.to_u16(lw["w_down"][int(e)])))
 
     def lm_head_rows(self, start, stop):
-        return synth.to_u16(self.w["lm_head"][start:stop])
+        return self._get(("lm", start, stop), lambda: synth.to_u16(self.w["lm_head"][start:stop]))
 
     def drop_layers(self):
         """Forget cached per-layer tensors (bounded host memory for long models)."""
