@@ -164,9 +164,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   P->n_ctr = C.n;
 
   // tile sizes from the worker count
-  // level 0 holds QKV tiles and router tiles: size QKV tiles so that no worker needs two
   const int router_tiles = std::max(1, std::min(8, m.E / 16));
-  const int qkv_tile = std::max(4, std::min(64, (int)ceil_div(m.QKVR, std::max(1, W - router_tiles - 2 * 3 * m.HKV))));
   // attention splits per sequence: [k0, k0 + split) ... last split open-ended from k0_last
   std::vector<int> nsplit(B), pbase_b(B);
   int parts = 0;
@@ -180,6 +178,11 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     P->capacity[b] = std::min(k0_last + SPLITMAX, desc.max_pages_per_seq * PAGE);
   }
   P->parts_per_layer = parts;
+  // level 0 holds QKV tiles and router tiles. Size the QKV tiles so that level 0 leaves a worker
+  // free for every attention split: those workers reach their split at the start of the layer and
+  // its keys stream in while level 0 runs (old keys do not depend on the step's activations).
+  const int lvl0_budget = std::max(W / 4, W - parts - router_tiles - 3 * m.HKV);
+  const int qkv_tile = std::max(4, std::min(64, (int)ceil_div(m.QKVR, lvl0_budget)));
   // level 1 holds the attention splits and the expert slices: size the slices so that the level
   // has about one task per worker (tasks are latency-bound; a second task per worker doubles it)
   const int slots = std::min(m.E, m.K * B);
@@ -298,11 +301,13 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   const int64_t TASK_FIXED = 96 * 1024;
   for (auto& lvl : levels)
     for (auto& pr : lvl) pr.bytes = pr.bytes * (pr.t.w[D_OP] == OP_ATTN ? 2 : 1) + TASK_FIXED;
-  // placement: per level, longest task first onto the worker with the least load in that level
-  // (ties: least total load, then lowest index); each worker's queue is level-ordered, and inside
-  // a level its tasks run in priority order (router before QKV, attention before expert slices).
+  // placement: per level, longest task first onto the worker with the least load in that level;
+  // ties go to the worker with the least load in the previous level (so attention splits land on
+  // workers idle in level 0 and prefetch their keys early), then least total load, then index.
+  // Each worker's queue is level-ordered, and inside a level its tasks run in priority order
+  // (router before QKV, attention before expert slices).
   std::vector<std::vector<std::pair<int, Proto>>> queues(W);   // (level, proto)
-  std::vector<int64_t> total(W, 0);
+  std::vector<int64_t> total(W, 0), prev(W, 0);
   for (int lv = 0; lv < (int)levels.size(); ++lv) {
     auto& lvl = levels[lv];
     std::vector<int> order(lvl.size());
@@ -311,12 +316,17 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     std::vector<int64_t> lload(W, 0);
     for (int idx : order) {
       int best = 0;
-      for (int w = 1; w < W; ++w)
-        if (lload[w] < lload[best] || (lload[w] == lload[best] && total[w] < total[best])) best = w;
+      for (int w = 1; w < W; ++w) {
+        const bool better = lload[w] != lload[best] ? lload[w] < lload[best]
+                          : prev[w] != prev[best] ? prev[w] < prev[best]
+                          : total[w] < total[best];
+        if (better) best = w;
+      }
       lload[best] += lvl[idx].bytes;
       total[best] += lvl[idx].bytes;
       queues[best].push_back({lv, lvl[idx]});
     }
+    prev = lload;
   }
   P->tasks.clear(); P->bytes.clear(); P->qoff.assign(W + 1, 0);
   for (int w = 0; w < W; ++w) {
