@@ -513,6 +513,7 @@ struct mk_engine {
   int32_t *argmax_out = nullptr, *topk_out = nullptr;
   float* hidden_out = nullptr;
   uint64_t* trace_out = nullptr;
+  float* rlog_out = nullptr;
   hipStream_t last_stream = nullptr;
   mk_status sticky = MK_OK;
   std::string msg;
@@ -662,9 +663,11 @@ mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens
   return MK_OK;
 }
 
-mk_status mk_set_step_outputs(mk_engine* e, int32_t* argmax_out, int32_t* topk_out, float* hidden_out, uint64_t* trace_out) {
+mk_status mk_set_step_outputs(mk_engine* e, int32_t* argmax_out, int32_t* topk_out, float* hidden_out, uint64_t* trace_out,
+                              float* router_logits_out) {
   if (!e) return MK_ERR_INVALID_ARG;
   e->argmax_out = argmax_out; e->topk_out = topk_out; e->hidden_out = hidden_out; e->trace_out = trace_out;
+  e->rlog_out = router_logits_out;
   return MK_OK;
 }
 
@@ -693,7 +696,7 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
   p.tokens = tokens; p.positions = positions; p.block_tables = block_tables; p.seq_lens = seq_lens;
   p.logits = e->desc.has_lm_head ? logits_out : nullptr;
   p.argmax_out = e->desc.has_lm_head ? e->argmax_out : nullptr;
-  p.topk_out = e->topk_out; p.hidden_out = e->hidden_out;
+  p.topk_out = e->topk_out; p.hidden_out = e->hidden_out; p.rlog_out = e->rlog_out;
   p.trace = (unsigned long long*)e->trace_out;
   p.L = e->m.L; p.V = e->m.V; p.B = P.B; p.max_pages = e->desc.max_pages_per_seq; p.num_pages = e->desc.num_pages;
   p.parts_per_layer = P.parts_per_layer; p.n_workers = P.n_workers; p.n_ctr = P.n_ctr; p.done_ctr = P.done_ctr;

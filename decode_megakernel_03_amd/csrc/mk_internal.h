@@ -101,6 +101,7 @@ struct Params {
   int32_t* argmax_out;       // [B] or null
   int32_t* topk_out;         // [L][B][K] or null
   float* hidden_out;         // [B][H] or null
+  float* rlog_out;           // [L][B][E] or null
   unsigned long long* trace; // [n_tasks][4] or null
 
   int32_t L, V, B, max_pages, num_pages, parts_per_layer, n_workers, n_ctr;

@@ -103,15 +103,23 @@ __device__ __forceinline__ uint32_t ctr_add(uint32_t* c, uint32_t v) {
   return __hip_atomic_fetch_add(c, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 __device__ __forceinline__ void drain() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// threadIdx.x made opaque per call, so that per-lane values derived from it are recomputed inside
+// each task instead of being hoisted out of the task loop into long-lived (spilled) registers
+__device__ __forceinline__ int tid() {
+  int x = (int)threadIdx.x;
+  asm volatile("" : "+v"(x));
+  return x;
+}
 __device__ __forceinline__ uint64_t now() { return __builtin_amdgcn_s_memrealtime(); }
 
 __device__ __forceinline__ float bf_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 __device__ __forceinline__ float bf1(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
-__device__ __forceinline__ uint32_t f2bf(float f) {   // round to nearest even
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return ((u >> 16) | 0x40u) & 0xffffu;
-  return ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16) & 0xffffu;
+__device__ __forceinline__ uint32_t f2bf(float f) {   // round to nearest even (NaN stays quiet NaN)
+  const uint32_t u = __float_as_uint(f);
+  const uint32_t r = ((u + 0x7fffu + ((u >> 16) & 1u)) >> 16) & 0xffffu;
+  const uint32_t q = ((u >> 16) | 0x40u) & 0xffffu;
+  return (u & 0x7fffffffu) > 0x7f800000u ? q : r;
 }
 
 // acc += sum_m w[m] * a[m] over the 8 bf16 of w, in element order
@@ -175,13 +183,14 @@ __shared__ Ctl ctl_s;
 static_assert(sizeof(RouteTable) % 16 == 0, "");
 
 // Trace: time the end of an op's phase i (0..3); no-op unless tracing.
-#define MARK(i) do { if ((p.flags & 1) && threadIdx.x == 0) ctl_s.mark[i] = now(); } while (0)
+// The latest of the four waves counts: each wave's first lane folds its clock into an LDS max.
+#define MARK(i) do { if ((p.flags & 1) && (tid() & 63) == 0) atomicMax(&ctl_s.mark[i], (unsigned long long)now()); } while (0)
 
 // Copy layer l's routing table into LDS: every thread loads 16 bytes, one round trip.
 __device__ __forceinline__ void load_route(CParams& p, int l) {
   const __amdgpu_buffer_rsrc_t R = rsrc(p.route + l);
   f4* dst = reinterpret_cast<f4*>(&ctl_s.rt);
-  for (int i = threadIdx.x; i < (int)(sizeof(RouteTable) / 16); i += NT) dst[i] = ldc4(R, 16u * i);
+  for (int i = tid(); i < (int)(sizeof(RouteTable) / 16); i += NT) dst[i] = ldc4(R, 16u * i);
   __syncthreads();
 }
 
@@ -203,7 +212,7 @@ __device__ void raise_error(CParams& p, uint32_t code, int task, int ctr, uint32
 // if the step was aborted or this wait exceeded the watchdog (which then aborts the step).
 __device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) {
   if (c < 0) return true;
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     int ok = 1;
     uint32_t v = ctr_load(p.ctr + c);
     if (v < target) {
@@ -234,7 +243,7 @@ __device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) 
 
 // Block until counter c0 >= t0 and counter c1 >= t1, polling both in the same round trip.
 __device__ bool wait_ge2(CParams& p, Ctl& ctl, int c0, uint32_t t0, int c1, uint32_t t1, int task) {
-  if (threadIdx.x == 0) {
+  if (tid() == 0) {
     int ok = 1;
     uint32_t v0 = c0 >= 0 ? ctr_load(p.ctr + c0) : t0, v1 = c1 >= 0 ? ctr_load(p.ctr + c1) : t1;
     if (v0 < t0 || v1 < t1) {
@@ -271,7 +280,7 @@ __device__ uint32_t signal(CParams& p, Ctl& ctl, int c, bool want_old) {
   drain();
   __syncthreads();
   uint32_t old = 0;
-  if (threadIdx.x == 0 && c >= 0) {
+  if (tid() == 0 && c >= 0) {
     old = ctr_add(p.ctr + c, 1u);
     if (want_old) ctl.flag = (int)old;
   }
@@ -314,7 +323,7 @@ __device__ __forceinline__ int block_rows() { return NP * NWAVE * Geo<KD>::RPP; 
 template <int KD, int NP, class RowPtr>
 __device__ __forceinline__ void load_block(WBuf<KD, NP>& b, int blk, int nrows, RowPtr rowptr) {
   using G = Geo<KD>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
@@ -336,7 +345,7 @@ template <int KD, int NP, int TB, class ActOf, class Emit>
 __device__ __forceinline__ void compute_block(const WBuf<KD, NP>& b, int blk, int nrows, int ntok,
                                               ActOf act_of, Emit emit) {
   using G = Geo<KD>;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
@@ -387,7 +396,12 @@ __device__ void stage_norm(CParams& p, int l, const int* toks, int ntok, const u
   constexpr int H = S::H;
   constexpr int G4 = H / 256;            // groups of 4 consecutive floats per lane
   static_assert(H % 256 == 0, "");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  uint2 gw[G4];                          // the gain, requested together with the activations
+  if (wave < ntok) {
+#pragma unroll
+    for (int k = 0; k < G4; ++k) gw[k] = *reinterpret_cast<const uint2*>(gain + 4 * lane + 256 * k);
+  }
   for (int t = wave; t < ntok; t += NWAVE) {
     const int b = toks[t];
     float v[4 * G4];
@@ -416,16 +430,15 @@ __device__ void stage_norm(CParams& p, int l, const int* toks, int ntok, const u
 #pragma unroll
     for (int k = 0; k < 4 * G4; ++k) ss = __builtin_fmaf(v[k], v[k], ss);
     ss = wsum<64>(ss);
-    const float denom = sqrtf(ss / (float)H + p.eps);
+    const float inv = 1.0f / sqrtf(ss / (float)H + p.eps);
 #pragma unroll
     for (int k = 0; k < G4; ++k) {
-      const uint2 g = *reinterpret_cast<const uint2*>(gain + 4 * lane + 256 * k);
-      const float gg[4] = {bf_lo(g.x), bf_hi(g.x), bf_lo(g.y), bf_hi(g.y)};
+      const float gg[4] = {bf_lo(gw[k].x), bf_hi(gw[k].x), bf_lo(gw[k].y), bf_hi(gw[k].y)};
       f4 o;
-      o.x = (v[4 * k + 0] / denom) * gg[0];
-      o.y = (v[4 * k + 1] / denom) * gg[1];
-      o.z = (v[4 * k + 2] / denom) * gg[2];
-      o.w = (v[4 * k + 3] / denom) * gg[3];
+      o.x = (v[4 * k + 0] * inv) * gg[0];
+      o.y = (v[4 * k + 1] * inv) * gg[1];
+      o.z = (v[4 * k + 2] * inv) * gg[2];
+      o.w = (v[4 * k + 3] * inv) * gg[3];
       *reinterpret_cast<f4*>(act + (size_t)t * H + 4 * lane + 256 * k) = o;
     }
   }
@@ -458,7 +471,7 @@ __device__ __forceinline__ bool op_qkv(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 2 : 4;
+  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 4 : 8;   // a whole 16-row tile in flight before the wait
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_qkv + (size_t)(row0 + r) * H; };
@@ -466,7 +479,7 @@ __device__ __forceinline__ bool op_qkv(int task) {
   const bool pre = !(p.flags & 2);
   if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  if (threadIdx.x < MAXB) ctl.toks[threadIdx.x] = threadIdx.x;
+  if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
   stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
   MARK(0);
@@ -489,7 +502,7 @@ __device__ __forceinline__ void compute_route(CParams& p, int l, float* sm) {
   constexpr int E = S::E, K = S::K, EPL = (E + 63) / 64;   // experts held per lane
   static_assert(E <= 128 && K <= 8, "");
   const int B = p.B;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   unsigned long long* mask = reinterpret_cast<unsigned long long*>(sm);   // [MAXB][2] selected experts
   const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)l * MAXB * E);
   const __amdgpu_buffer_rsrc_t RT = rsrc(p.route + l);
@@ -498,6 +511,11 @@ __device__ __forceinline__ void compute_route(CParams& p, int l, float* sm) {
     float v[EPL];
 #pragma unroll
     for (int k = 0; k < EPL; ++k) v[k] = (lane + 64 * k < E) ? ldc(R, 4u * (b * E + lane + 64 * k)) : -INFINITY;
+    if (p.rlog_out) {
+#pragma unroll
+      for (int k = 0; k < EPL; ++k)
+        if (lane + 64 * k < E) p.rlog_out[((size_t)l * B + b) * E + lane + 64 * k] = v[k];
+    }
     int widx[K];
     float wval[K];
 #pragma unroll
@@ -554,8 +572,8 @@ __device__ __forceinline__ void compute_route(CParams& p, int l, float* sm) {
   }
   __syncthreads();
   // union over the batch (ascending expert ids) and each union slot's tokens (ascending b)
-  if (threadIdx.x < E) {
-    const int e = threadIdx.x;
+  if (tid() < E) {
+    const int e = tid();
     unsigned long long u0 = 0, u1 = 0;
     for (int b = 0; b < B; ++b) { u0 |= mask[2 * b]; u1 |= mask[2 * b + 1]; }
     const bool used = e < 64 ? (u0 >> e) & 1 : (u1 >> (e - 64)) & 1;
@@ -585,7 +603,7 @@ __device__ __forceinline__ bool op_router(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, E = S::E, NP = (Geo<H>::CPL >= 4) ? 2 : 4;
+  constexpr int H = S::H, E = S::E, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_router + (size_t)(row0 + r) * H; };
@@ -593,7 +611,7 @@ __device__ __forceinline__ bool op_router(int task) {
   const bool pre = !(p.flags & 2);
   if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  if (threadIdx.x < MAXB) ctl.toks[threadIdx.x] = threadIdx.x;
+  if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
   stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
   const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)T.layer * MAXB * E);
@@ -637,8 +655,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
     auto rowptr = [&](int r) { return r < nf ? wg + (size_t)(f0 + r) * H : wu + (size_t)(f0 + r - nf) * H; };
     WBuf<H, NP> A;
     load_block<H, NP>(A, 0, 2 * nf, rowptr);
-    if (threadIdx.x < MAXB) {
-      const int t = threadIdx.x;
+    if (tid() < MAXB) {
+      const int t = tid();
       const int bi = t < ntok ? rt.tok_bi[u][t] : 0;
       ctl.bis[t] = bi;
       ctl.toks[t] = bi >> 8;
@@ -653,7 +671,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
     __syncthreads();
     MARK(2);
     const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
-    for (int i = threadIdx.x; i < ntok * nf; i += NT) {
+    for (int i = tid(); i < ntok * nf; i += NT) {
       const int t = i / nf, f = i % nf;
       const int bi = ctl.bis[t];
       const float g = gu[t * 2 * nf + f], up = gu[t * 2 * nf + nf + f];
@@ -678,6 +696,22 @@ __device__ __forceinline__ bool op_gateup(int task) {
 // low parts (q = hi + lo to 2^-16), so fp32 accuracy is kept while the operand takes 16 registers.
 // Every K of a 256-key chunk is requested before the dependency wait; V of the chunk is requested
 // as soon as the scores are done (the K registers are free then). P V runs on the vector units.
+// LDS layout of an attention task, in floats (every region 16-byte aligned)
+template <class S>
+struct AttnLds {
+  static constexpr int al(int x) { return (x + 3) & ~3; }
+  static constexpr int D = S::D, HPG = S::HPG;
+  static constexpr int CS = 0;
+  static constexpr int SB = al(CS + D);
+  static constexpr int VN = al(SB + (SPLIT_MAX + 1) * HPG);
+  static constexpr int ML = al(VN + D);
+  static constexpr int OB = al(ML + 2 * HPG);
+  static constexpr int PG = al(OB + NWAVE * (D / 8) * HPG * 8);
+  static constexpr int KN = al(PG + SPLIT_MAX / PAGE + 1);
+  static constexpr int QF = al(KN + D / 2);
+  static constexpr int END = al(QF + HPG * D);
+};
+
 template <class S>
 __device__ __forceinline__ bool op_attn(int task) {
   CParams& p = P();
@@ -690,17 +724,17 @@ __device__ __forceinline__ bool op_attn(int task) {
   constexpr int KC = 256;                // keys per chunk
   constexpr int GPW = KC / 16 / NWAVE;   // 16-key column blocks per wave per chunk
   constexpr int VPL = KC / KPI;          // V loads per lane per chunk (P V layout)
-  static_assert(2 * HPG <= 16 && HPG % 4 == 0 && D % 32 == 0 && KC % KPI == 0, "");
+  static_assert(2 * HPG <= 16 && HPG % 2 == 0 && D % 32 == 0 && KC % KPI == 0, "");
   const int l = T.layer, b = T.a0, g = T.a1, k0 = T.a2, k1 = T.a3;
   const int pbase = T.a4, s_idx = T.a5 & 0xffff, nsplit = T.a5 >> 16;
   const auto& Lp = cst(p.layers)[l];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int li = lane % LPK, slot = wave * KPW + lane / LPK;   // P V layout: key slot, 8-dim chunk
   const int col = lane & 15, grp = lane >> 4;                   // MFMA layout
   const int n_ctx = cst(p.seq_lens)[b], pos = cst(p.positions)[b];
   const bool last = k1 < 0;
   if (pos != n_ctx - 1 || pos < 0 || n_ctx > p.max_pages * PAGE) {
-    if (threadIdx.x == 0) raise_error(p, DEV_BAD_POS, T.id, -1, (uint32_t)n_ctx, (uint32_t)pos, (uint32_t)b);
+    if (tx == 0) raise_error(p, DEV_BAD_POS, T.id, -1, (uint32_t)n_ctx, (uint32_t)pos, (uint32_t)b);
     return false;
   }
   int kend = last ? pos : (k1 < pos ? k1 : pos);
@@ -708,21 +742,23 @@ __device__ __forceinline__ bool op_attn(int task) {
   const int nk = kend - k0;                       // cached keys scored by this task
   const int ntot = nk + (last ? 1 : 0);
   if ((last && pos < k0) || ntot > SPLIT_MAX) {
-    if (threadIdx.x == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)k0, (uint32_t)pos, (uint32_t)b);
+    if (tx == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)k0, (uint32_t)pos, (uint32_t)b);
     return false;
   }
-  // LDS layout
-  float* cs = sm;                                  // [D/2] cos, [D/2] sin
-  float* sbuf = sm + D;                            // [SPLIT_MAX + 1][HPG] scores -> probabilities
-  float* vnew = sbuf + (SPLIT_MAX + 1) * HPG;      // [D]
-  float* ml = vnew + D;                            // [2][HPG]
-  float* obuf = ml + 2 * HPG;                      // [NWAVE][LPK][HPG * 8]
-  int* pg = reinterpret_cast<int*>(obuf + NWAVE * LPK * HPG * 8);   // [SPLIT_MAX / PAGE + 1] page ids
-  uint32_t* knew = reinterpret_cast<uint32_t*>(pg + SPLIT_MAX / PAGE + 4);   // [D / 2] new key, bf16 pairs
+  // LDS layout (float offsets in AttnLds<S>)
+  using L = AttnLds<S>;
+  float* cs = sm + L::CS;                          // [D/2] cos, [D/2] sin
+  float* sbuf = sm + L::SB;                        // [SPLIT_MAX + 1][HPG] scores -> probabilities
+  float* vnew = sm + L::VN;                        // [D]
+  float* ml = sm + L::ML;                          // [2][HPG]
+  float* obuf = sm + L::OB;                        // [NWAVE][LPK][HPG * 8]
+  int* pg = reinterpret_cast<int*>(sm + L::PG);    // [SPLIT_MAX / PAGE + 1] page ids
+  uint32_t* knew = reinterpret_cast<uint32_t*>(sm + L::KN);   // [D / 2] new key, bf16 pairs
+  float* qf = sm + L::QF;                          // [HPG][D] RoPE'd queries
   {
     const __attribute__((address_space(4))) int32_t* bt = cst(p.block_tables) + (size_t)b * p.max_pages + k0 / PAGE;
     const int npg = (ntot + PAGE - 1) / PAGE;
-    for (int i = threadIdx.x; i < npg; i += NT) {
+    for (int i = tx; i < npg; i += NT) {
       int page = bt[i];
       if (page < 0 || page >= p.num_pages) {
         raise_error(p, DEV_BAD_PAGE, T.id, -1, (uint32_t)p.num_pages, (uint32_t)page, (uint32_t)(k0 / PAGE + i));
@@ -731,10 +767,10 @@ __device__ __forceinline__ bool op_attn(int task) {
       pg[i] = page;
     }
   }
-  if (threadIdx.x < D / 2) {
-    const double ang = (double)pos * cst(p.inv_freq)[threadIdx.x];
-    cs[threadIdx.x] = (float)cos(ang);
-    cs[D / 2 + threadIdx.x] = (float)sin(ang);
+  if (tx < D / 2) {
+    const double ang = (double)pos * cst(p.inv_freq)[tx];
+    cs[tx] = (float)cos(ang);
+    cs[D / 2 + tx] = (float)sin(ang);
   }
   __syncthreads();
   // key j, dims d0..d0+7 -> element offset in the K (or V) cache
@@ -760,33 +796,69 @@ __device__ __forceinline__ bool op_attn(int task) {
       vr[q] = (j < kend) ? ldw(Lp.v_cache + kaddr(j, 8 * li)) : u4{0u, 0u, 0u, 0u};
     }
   };
-  load_k(0);            // old keys do not depend on this step's activations
+  // the cached keys and values do not depend on this step's activations: the first chunk of both
+  // is in flight while the task waits for the QKV rows
+  load_k(0);
+  load_v(0);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + ((size_t)l * MAXB + b) * S::QKVR);
-  const float sd = sqrtf((float)D);
-  // RoPE of dims d0..d0+7 of the head vector at float index `base` (rotate-half pairs d, d +- D/2)
-  auto rope8 = [&](uint32_t base, int d0, float (&out)[8]) {
-    const int pd0 = d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
-    const f4 x0 = ldc4(Q, 4u * (base + d0)), x1 = ldc4(Q, 4u * (base + d0 + 4));
-    const f4 y0 = ldc4(Q, 4u * (base + pd0)), y1 = ldc4(Q, 4u * (base + pd0 + 4));
-    const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    const float ys[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+  const float rsd = 1.0f / sqrtf((float)D);
+  // rotate-half RoPE of 4 dims d0..d0+3 (all on one side of D/2) given x and its partner dims y
+  auto rope4 = [&](f4 x, f4 y, int d0) -> f4 {
+    f4 r;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
+    for (int m = 0; m < 4; ++m) {
       const int i = (d0 + m) % (D / 2);
       const float c = cs[i], s = cs[D / 2 + i];
-      out[m] = d0 < D / 2 ? xs[m] * c - ys[m] * s : xs[m] * c + ys[m] * s;
+      r[m] = d0 < D / 2 ? x[m] * c - y[m] * s : x[m] * c + y[m] * s;
     }
+    return r;
   };
-  // MFMA A operand: row r = col; r < HPG: head r, high part; HPG <= r < 2 HPG: head r - HPG, low part
+  // the group's query rows, RoPE'd, into LDS (one round trip); the last split also forms the new
+  // key and value: RoPE(k) and v rounded to bf16 (the cache format), written at slot pos and kept in
+  // LDS for scoring and for P V
+  for (int i4 = 4 * tx; i4 < HPG * D; i4 += 4 * NT) {
+    const int hh = i4 / D, d0 = i4 % D, pd0 = d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
+    const uint32_t base = (uint32_t)((g * HPG + hh) * D);
+    const f4 x = ldc4(Q, 4u * (base + d0)), y = ldc4(Q, 4u * (base + pd0));
+    *reinterpret_cast<f4*>(qf + i4) = rope4(x, y, d0);
+  }
+  if (last && wave == 0 && lane < LPK) {
+    const int d0 = 8 * li, pd0 = d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
+    const uint32_t kbase = (uint32_t)(S::HQ * D + g * D), vbase = (uint32_t)((S::HQ + S::HKV) * D + g * D);
+    const f4 x0 = ldc4(Q, 4u * (kbase + d0)), x1 = ldc4(Q, 4u * (kbase + d0 + 4));
+    const f4 y0 = ldc4(Q, 4u * (kbase + pd0)), y1 = ldc4(Q, 4u * (kbase + pd0 + 4));
+    const f4 v0 = ldc4(Q, 4u * (vbase + d0)), v1 = ldc4(Q, 4u * (vbase + d0 + 4));
+    const f4 k0r = rope4(x0, y0, d0), k1r = rope4(x1, y1, d0 + 4);
+    const float kk[8] = {k0r.x, k0r.y, k0r.z, k0r.w, k1r.x, k1r.y, k1r.z, k1r.w};
+    const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+    uint32_t kw[4], vw[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t ka = f2bf(kk[2 * m]), kb2 = f2bf(kk[2 * m + 1]);
+      const uint32_t va = f2bf(vv[2 * m]), vb2 = f2bf(vv[2 * m + 1]);
+      kw[m] = ka | (kb2 << 16);
+      vw[m] = va | (vb2 << 16);
+      knew[4 * li + m] = kw[m];
+      vnew[8 * li + 2 * m] = bf1((uint16_t)va); vnew[8 * li + 2 * m + 1] = bf1((uint16_t)vb2);
+    }
+    const size_t off = kaddr(pos, 8 * li);
+    *reinterpret_cast<u4*>(Lp.k_cache + off) = u4{kw[0], kw[1], kw[2], kw[3]};
+    *reinterpret_cast<u4*>(Lp.v_cache + off) = u4{vw[0], vw[1], vw[2], vw[3]};
+  }
+  __syncthreads();
+  // MFMA A operand, row r = col: with a = r / 4, rows 4a, 4a+1 hold the bf16 high parts of heads
+  // 2a, 2a+1 and rows 4a+2, 4a+3 their low parts (q - bf16(q)), so that the output rows a lane holds
+  // (4 grp .. 4 grp + 3) are the two parts of heads 2 grp and 2 grp + 1
   bf8 qa[KB];
   {
-    const int h = col % HPG;
-    const bool valid = col < 2 * HPG, lo = col >= HPG;
+    const int h = 2 * (col >> 2) + (col & 1);
+    const bool valid = h < HPG, lo = (col & 2) != 0;
+    const float* qrow = qf + (valid ? h : 0) * D + 8 * grp;
 #pragma unroll
     for (int kb = 0; kb < KB; ++kb) {
-      float x[8];
-      rope8((uint32_t)((g * HPG + h) * D), 32 * kb + 8 * grp, x);
+      const f4 x0 = *reinterpret_cast<const f4*>(qrow + 32 * kb), x1 = *reinterpret_cast<const f4*>(qrow + 32 * kb + 4);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
       uint32_t w[4];
 #pragma unroll
       for (int m = 0; m < 4; ++m) {
@@ -798,71 +870,55 @@ __device__ __forceinline__ bool op_attn(int task) {
     }
   }
   MARK(0);
-  if (last) {
-    // new key/value: RoPE(k) and v from this step's QKV rows, rounded to bf16 (the cache format),
-    // written at slot pos, and kept in LDS for scoring and for P V
-    if (wave == 0 && lane < LPK) {
-      float kr8[8];
-      rope8((uint32_t)(S::HQ * D + g * D), 8 * li, kr8);
-      const uint32_t vbase = (uint32_t)((S::HQ + S::HKV) * D + g * D + 8 * li);
-      const f4 v0 = ldc4(Q, 4u * vbase), v1 = ldc4(Q, 4u * (vbase + 4));
-      const float vv[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-      uint32_t kw[4], vw[4];
-#pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const uint32_t ka = f2bf(kr8[2 * m]), kb2 = f2bf(kr8[2 * m + 1]);
-        const uint32_t va = f2bf(vv[2 * m]), vb2 = f2bf(vv[2 * m + 1]);
-        kw[m] = ka | (kb2 << 16);
-        vw[m] = va | (vb2 << 16);
-        knew[4 * li + m] = kw[m];
-        vnew[8 * li + 2 * m] = bf1((uint16_t)va); vnew[8 * li + 2 * m + 1] = bf1((uint16_t)vb2);
-      }
-      const size_t off = kaddr(pos, 8 * li);
-      *reinterpret_cast<u4*>(Lp.k_cache + off) = u4{kw[0], kw[1], kw[2], kw[3]};
-      *reinterpret_cast<u4*>(Lp.v_cache + off) = u4{vw[0], vw[1], vw[2], vw[3]};
-    }
-    __syncthreads();
-  }
-  // ---- pass A: s[j][hh] = (k_j . q_hh) / sqrt(D) on the matrix cores
+  // ---- pass A: s[j][hh] = (k_j . q_hh) / sqrt(D) on the matrix cores, cached keys j < nk
   for (int c = 0; c < nchunk; ++c) {
     if (c > 0) load_k(c);
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int jb = c * KC + (wave + NWAVE * i) * 16;   // first key of the block, relative to k0
-      if (jb >= ntot) continue;                           // uniform in the wave
-      const bool is_new = last && jb + col == nk;
+      if (jb >= nk) continue;                             // uniform in the wave
       f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < KB; ++kb) {
-        u4 kv = kr[i][kb];
-        if (is_new) kv = *reinterpret_cast<const u4*>(knew + 16 * kb + 4 * grp);
-        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], __builtin_bit_cast(bf8, kv), acc, 0, 0, 0);
-      }
-      // rows r and r + HPG hold the high and low parts of the same head: add them
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += __shfl_xor(acc[j], 4 * HPG, 64);
-      if (grp < HPG / 4 && jb + col < ntot) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) sbuf[(jb + col) * HPG + 4 * grp + j] = acc[j] / sd;
+      for (int kb = 0; kb < KB; ++kb)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], __builtin_bit_cast(bf8, kr[i][kb]), acc, 0, 0, 0);
+      if (2 * grp < HPG && jb + col < nk) {
+        typedef float f2 __attribute__((ext_vector_type(2)));
+        *reinterpret_cast<f2*>(sbuf + (jb + col) * HPG + 2 * grp) = f2{(acc[0] + acc[2]) * rsd, (acc[1] + acc[3]) * rsd};
       }
     }
   }
-  load_v(0);            // V streams while the softmax statistics are computed
   __syncthreads();
   MARK(1);
-  // ---- softmax statistics per head (wave w handles heads w, w + 4, ...)
+  // ---- softmax statistics per head (wave w handles heads w, w + 4, ...); the new key's score is a
+  // plain fp32 dot product of the RoPE'd query with the bf16 key
   for (int hh = wave; hh < HPG; hh += NWAVE) {
-    float m = -INFINITY;
-    for (int j = lane; j < ntot; j += 64) m = fmaxf(m, sbuf[j * HPG + hh]);
+    float snew = -INFINITY;
+    if (last) {
+      float t = 0.f;
+      for (int d2 = lane; d2 < D / 2; d2 += 64) {
+        const uint32_t kw = knew[d2];
+        t += qf[hh * D + 2 * d2] * bf_lo(kw) + qf[hh * D + 2 * d2 + 1] * bf_hi(kw);
+      }
+      snew = wsum<64>(t) * rsd;
+    }
+    float m = snew;
+    for (int j = lane; j < nk; j += 64) m = fmaxf(m, sbuf[j * HPG + hh]);
     m = wmax<64>(m);
     float lsum = 0.f;
-    for (int j = lane; j < ntot; j += 64) {
+    for (int j = lane; j < nk; j += 64) {
       const float e = expf(sbuf[j * HPG + hh] - m);
       sbuf[j * HPG + hh] = e;
       lsum += e;
     }
     lsum = wsum<64>(lsum);
-    if (lane == 0) { ml[hh] = m; ml[HPG + hh] = lsum; }
+    if (lane == 0) {
+      if (last) {
+        const float e = expf(snew - m);
+        sbuf[nk * HPG + hh] = e;
+        lsum += e;
+      }
+      ml[hh] = m; ml[HPG + hh] = lsum;
+    }
   }
   __syncthreads();
   // ---- pass B: o[hh][d] = sum_j p[j][hh] v_j[d]
@@ -919,13 +975,13 @@ __device__ __forceinline__ bool op_attn(int task) {
   // partial: m[HPG], l[HPG], o[HPG][D] (unnormalised)
   const size_t part = ((size_t)l * p.parts_per_layer + pbase + s_idx) * S::PART;
   const __amdgpu_buffer_rsrc_t Pw = rsrc(p.apart + part);
-  for (int i = threadIdx.x; i < HPG * D; i += NT) {
+  for (int i = tx; i < HPG * D; i += NT) {
     const int hh = i / D, d = i % D, c = d / 8, m = d % 8;
     float v = 0.f;
     for (int w = 0; w < NWAVE; ++w) v += obuf[(w * LPK + c) * HPG * 8 + hh * 8 + m];
     stc(Pw, 4u * (2 * HPG + i), v);
   }
-  if (threadIdx.x < 2 * HPG) stc(Pw, 4u * threadIdx.x, ml[threadIdx.x]);
+  if (tx < 2 * HPG) stc(Pw, 4u * tx, ml[tx]);
   const uint32_t old = signal(p, ctl, T.sig, true);
   MARK(3);
   if (old + 1 == (uint32_t)nsplit) {
@@ -936,13 +992,13 @@ __device__ __forceinline__ bool op_attn(int task) {
     float* msl = sbuf;          // [nsplit][2 * HPG] m then l; m is overwritten by exp(m - M)
     float* linv = ml;           // [HPG] sum over splits of l * exp(m - M)
     if (nsplit > MERGE_MAX) {
-      if (threadIdx.x == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)MERGE_MAX, (uint32_t)nsplit, (uint32_t)b);
+      if (tx == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)MERGE_MAX, (uint32_t)nsplit, (uint32_t)b);
       return false;
     }
-    for (int i = threadIdx.x; i < nsplit * 2 * HPG; i += NT)
+    for (int i = tx; i < nsplit * 2 * HPG; i += NT)
       msl[i] = ldc(P0, 4u * ((i / (2 * HPG)) * S::PART + i % (2 * HPG)));
     __syncthreads();
-    for (int hh = threadIdx.x; hh < HPG; hh += NT) {
+    for (int hh = tx; hh < HPG; hh += NT) {
       float M = -INFINITY;
       for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, msl[s2 * 2 * HPG + hh]);
       float Lsum = 0.f;
@@ -956,7 +1012,7 @@ __device__ __forceinline__ bool op_attn(int task) {
     }
     __syncthreads();
     const __amdgpu_buffer_rsrc_t A = rsrc(p.attn + ((size_t)l * MAXB + b) * S::AD + g * HPG * D);
-    for (int i4 = threadIdx.x * 4; i4 < HPG * D; i4 += NT * 4) {
+    for (int i4 = tx * 4; i4 < HPG * D; i4 += NT * 4) {
       const int hh = i4 / D;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
       int s2 = 0;
@@ -1033,8 +1089,8 @@ __device__ __forceinline__ bool op_out(int task) {
       // all MoE slices and the attention of every KV group
       if (!wait_ge2(p, ctl, T.w1, (uint32_t)T.t1, T.a2, (uint32_t)T.a3, T.id)) return false;
     }
-    for (int i = threadIdx.x * 4; i < AD; i += NT * 4) *reinterpret_cast<f4*>(a_s + i) = ldc4(At, 4u * (b * AD + i));
-    for (int i = threadIdx.x * 4; i < K * F; i += NT * 4) *reinterpret_cast<f4*>(h_s + i) = ldc4(Hb, 4u * (b * K * F + i));
+    for (int i = tid() * 4; i < AD; i += NT * 4) *reinterpret_cast<f4*>(a_s + i) = ldc4(At, 4u * (b * AD + i));
+    for (int i = tid() * 4; i < K * F; i += NT * 4) *reinterpret_cast<f4*>(h_s + i) = ldc4(Hb, 4u * (b * K * F + i));
     __syncthreads();
     if (b == 0) MARK(0);
     compute_block<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
@@ -1042,8 +1098,8 @@ __device__ __forceinline__ bool op_out(int task) {
     compute_block<F, NPD, 1>(WD, 0, K * nrows, 1, [&](int q, int t) { return h_s + (q / nrows) * F; },
                              [&](int q, int t, float v) { y_s[(q / nrows) * OUT_MAXR + q % nrows] = v; });
     __syncthreads();
-    if (threadIdx.x < nrows) {
-      const int r = threadIdx.x, row = row0 + r;
+    if (tid() < nrows) {
+      const int r = tid(), row = row0 + r;
       float xv;
       if (l == 0) {
         int tok = cst(p.tokens)[b];
@@ -1083,7 +1139,7 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   const bool pre = !(p.flags & 2);
   if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  if (threadIdx.x < MAXB) ctl.toks[threadIdx.x] = threadIdx.x;
+  if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
   stage_norm<S>(p, p.L, ctl.toks, p.B, p.final_norm, sm, T.id);
   float bv[TB];
@@ -1104,15 +1160,15 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   // combine the emitting lanes (lir == 0) of every wave, then one atomic per token
   float* cv = sm + (size_t)TB * H;                                 // [NWAVE * RPP][TB]
   int* ci = reinterpret_cast<int*>(cv + NWAVE * RPP * TB);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   if (lane % Geo<H>::LPR == 0) {
     const int slot = wave * RPP + lane / Geo<H>::LPR;
 #pragma unroll
     for (int t = 0; t < TB; ++t) { cv[slot * TB + t] = bv[t]; ci[slot * TB + t] = bi[t]; }
   }
   __syncthreads();
-  if (threadIdx.x < p.B) {
-    const int t = threadIdx.x;
+  if (tid() < p.B) {
+    const int t = tid();
     float best = -INFINITY;
     int besti = 0x7fffffff;
     for (int s = 0; s < NWAVE * RPP; ++s) {
@@ -1137,19 +1193,19 @@ __device__ __forceinline__ bool op_lmhead(int task) {
 __device__ void finish(CParams& p, Ctl& ctl) {
   drain();
   __syncthreads();
-  if (threadIdx.x == 0) ctl.flag = (int)(ctr_add(p.ctr + p.done_ctr, 1u) == (uint32_t)(p.n_workers - 1));
+  if (tid() == 0) ctl.flag = (int)(ctr_add(p.ctr + p.done_ctr, 1u) == (uint32_t)(p.n_workers - 1));
   __syncthreads();
   if (!ctl.flag) return;
-  if (threadIdx.x < MAXB) {
-    const unsigned long long key = __hip_atomic_load(p.amax + threadIdx.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (p.argmax_out && threadIdx.x < p.B) p.argmax_out[threadIdx.x] = (int32_t)(0xffffffffu - (uint32_t)key);
-    __hip_atomic_store(p.amax + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid() < MAXB) {
+    const unsigned long long key = __hip_atomic_load(p.amax + tid(), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (p.argmax_out && tid() < p.B) p.argmax_out[tid()] = (int32_t)(0xffffffffu - (uint32_t)key);
+    __hip_atomic_store(p.amax + tid(), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  for (int c = threadIdx.x; c < p.n_ctr; c += NT)
+  for (int c = tid(); c < p.n_ctr; c += NT)
     if (c != p.done_ctr) __hip_atomic_store(p.ctr + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   drain();
   __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(p.ctr + p.done_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid() == 0) __hip_atomic_store(p.ctr + p.done_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class S, int TB>
@@ -1160,10 +1216,11 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
   for (int ti = qs; ti < qe; ++ti) {
     const int op = cst(p.tasks)[(size_t)ti * DESC_WORDS + D_OP];
     const uint64_t t_start = trace ? now() : 0;
-    if (trace && threadIdx.x == 0) {
+    if (trace && tid() == 0) {
       ctl_s.t_ready = t_start;
       ctl_s.mark[0] = ctl_s.mark[1] = ctl_s.mark[2] = ctl_s.mark[3] = 0;
     }
+    if (trace) __syncthreads();
     bool ok;
     switch (op) {
       case OP_QKV: ok = op_qkv<S, TB>(ti); break;
@@ -1173,10 +1230,11 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
       case OP_OUT: ok = op_out<S, TB>(ti); break;
       case OP_LMHEAD: ok = op_lmhead<S, TB>(ti); break;
       default:
-        if (threadIdx.x == 0) raise_error(p, DEV_BAD_OP, ti, -1, 0, (uint32_t)op, 0);
+        if (tid() == 0) raise_error(p, DEV_BAD_OP, ti, -1, 0, (uint32_t)op, 0);
         ok = false;
     }
-    if (trace && threadIdx.x == 0) {
+    if (trace) __syncthreads();          // t_end: every wave is done with the task
+    if (trace && tid() == 0) {
       unsigned long long* tr = p.trace + (size_t)ti * 8;
       tr[0] = (unsigned long long)ti | ((unsigned long long)blockIdx.x << 32);
       tr[1] = t_start;
@@ -1196,8 +1254,7 @@ template <class S>
 static size_t lds_bytes(int tb) {
   // norm-staged activations + GEMV scratch, attention buffers, OUT staging: the largest wins
   const size_t act = (size_t)tb * S::H * 4 + (size_t)tb * 2 * 64 * 4 + 4096;
-  const size_t att = ((size_t)S::D + (SPLIT_MAX + 1) * S::HPG + S::D + 2 * S::HPG +
-                      (size_t)NWAVE * (S::D / 8) * S::HPG * 8 + SPLIT_MAX / PAGE + 4 + S::D / 2) * 4;
+  const size_t att = (size_t)AttnLds<S>::END * 4;
   const size_t out = ((size_t)S::AD + S::K * S::F + OUT_MAXR + S::K * OUT_MAXR) * 4;
   const size_t rte = ((size_t)MAXB * S::E * 3 + S::E) * 4 + 256;
   size_t m = act;

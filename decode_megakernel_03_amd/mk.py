@@ -69,7 +69,7 @@ def load(path=LIB_PATH):
         "mk_set_options": [vp, ctypes.POINTER(Options)],
         "mk_build_schedule": [vp, i32, P32],
         "mk_decode_step": [vp, vp, vp, vp, vp, vp, vp],
-        "mk_set_step_outputs": [vp, vp, vp, vp, vp],
+        "mk_set_step_outputs": [vp, vp, vp, vp, vp, vp],
         "mk_sync": [vp],
         "mk_get_error": [vp, ctypes.c_char_p, sz],
         "mk_reset": [vp],
@@ -142,9 +142,9 @@ def mk_decode_step(h, tokens, positions, block_tables, seq_lens, logits_out, str
     return st
 
 
-def mk_set_step_outputs(h, argmax_out=None, topk_out=None, hidden_out=None, trace_out=None):
-    _check(LIB.mk_set_step_outputs(h, _ptr(argmax_out), _ptr(topk_out), _ptr(hidden_out), _ptr(trace_out)), h,
-           "mk_set_step_outputs")
+def mk_set_step_outputs(h, argmax_out=None, topk_out=None, hidden_out=None, trace_out=None, router_logits_out=None):
+    _check(LIB.mk_set_step_outputs(h, _ptr(argmax_out), _ptr(topk_out), _ptr(hidden_out), _ptr(trace_out),
+                                   _ptr(router_logits_out)), h, "mk_set_step_outputs")
 
 
 def mk_sync(h):

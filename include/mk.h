@@ -150,9 +150,11 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
  *   hidden_out float32 [B, H]  residual stream after the last layer
  *   trace_out uint64 [tasks, 8] when MK_FLAG_TRACE: {task id | worker << 32, t_start, t_ready,
  *                              t_end, mark0..mark3} in 100 MHz ticks (size via mk_plan_info);
- *                              marks are op-specific phase ends, 0 where an op sets none. */
+ *                              marks are op-specific phase ends, 0 where an op sets none
+ *   router_logits_out float32 [L, B, E]  the router logits (bias included) exactly as the routing
+ *                              decision of each layer read them */
 mk_status mk_set_step_outputs(mk_engine* e, int32_t* argmax_out, int32_t* topk_out,
-                              float* hidden_out, uint64_t* trace_out);
+                              float* hidden_out, uint64_t* trace_out, float* router_logits_out);
 
 /* Wait for the engine's last step and report a device fault, if any, as MK_ERR_DEVICE. */
 mk_status mk_sync(mk_engine* e);

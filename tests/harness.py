@@ -92,3 +92,42 @@ def tiny_setup(wl=None, seed=0, gains="ones", batch=None, device="cpu"):
     k, v = synth.make_kv(wl, num_pages, device=device)
     tokens = synth.first_tokens(wl)
     return dict(wl=wl, w=w, ctx=ctx, block_tables=bt, num_pages=num_pages, k=k, v=v, tokens=tokens)
+
+
+class RoutingMismatch(AssertionError):
+    """The GPU took a routing decision the oracle does not accept as a near-tie."""
+
+    def __init__(self, msg, ref, forced):
+        super().__init__(msg)
+        self.ref, self.forced = ref, forced
+
+
+def replay_near_ties(run, g_topk, near_tie, max_rounds=32):
+    """Reconcile the GPU's expert sets g_topk [L, B, k] with the oracle, layer by layer.
+
+    ``run(forced)`` runs the oracle step with ``forced_topk=forced`` and returns its result. The
+    first layer where the two disagree must be a near-tie for every disagreeing token (oracle margin
+    <= near_tie, exactly one expert swapped); the oracle is then rerun with the GPU's sets forced
+    there, which changes everything after that layer, and the walk continues. Disagreements after
+    an unreplayed flip are never judged against an oracle that has already diverged.
+    Returns (result, forced); raises RoutingMismatch otherwise.
+    """
+    forced = {}
+    L, B = g_topk.shape[:2]
+    for _ in range(max_rounds):
+        ref = run(forced or None)
+        for l in range(L):
+            diff = [b for b in range(B)
+                    if (l, b) not in forced and set(g_topk[l, b].tolist()) != set(ref.topk[l, b].tolist())]
+            if diff:
+                break
+        else:
+            return ref, forced
+        for b in diff:
+            gs, rs = set(g_topk[l, b].tolist()), set(ref.topk[l, b].tolist())
+            if not (ref.margin[l, b] <= near_tie and len(gs ^ rs) == 2):
+                raise RoutingMismatch(f"layer {l} token {b}: GPU experts {sorted(gs)} != oracle {sorted(rs)} "
+                                      f"(margin {ref.margin[l, b]:.3g}, earlier near-tie replays {sorted(forced)})",
+                                      ref, forced)
+            forced[(l, b)] = sorted(gs)
+    raise RoutingMismatch(f"more than {max_rounds} rounds of near-tie replays", ref, forced)

@@ -35,21 +35,6 @@ def to_dev(w):
     return out
 
 
-def compare_topk(gpu, ref, margins, where):
-    """gpu/ref int [L, B, k]; returns dict of replays {(l, b): gpu_set} for accepted near-ties."""
-    replay = {}
-    L, B, _ = ref.shape
-    for l in range(L):
-        for b in range(B):
-            g, r = set(gpu[l, b].tolist()), set(ref[l, b].tolist())
-            if g == r:
-                continue
-            assert margins[l, b] <= NEAR_TIE and len(g ^ r) == 2, \
-                f"{where}: layer {l} token {b}: GPU experts {sorted(g)} != oracle {sorted(r)} (margin {margins[l, b]:.3g})"
-            replay[(l, b)] = sorted(g)
-    return replay
-
-
 def check_logits(gpu, ref, where):
     for b in range(ref.shape[0]):
         d = np.abs(gpu[b].astype(np.float64) - ref[b])
@@ -93,10 +78,9 @@ def run_steps(wl, steps, gains="ones", seed=0, teacher_force=False, split_keys=0
         g_arg = argmax.cpu().numpy().astype(np.int64)
         g_hidden = hidden.cpu().numpy()
         toks_for_ref = tok_gpu if teacher_force else tok_ref
-        ref = oracle_step(dims, dw, kv_ref, toks_for_ref, pos, s["block_tables"])
-        replay = compare_topk(g_topk, ref.topk, ref.margin, f"step {step}")
-        if replay:
-            ref = oracle_step(dims, dw, kv_ref, toks_for_ref, pos, s["block_tables"], forced=replay, rewind=True)
+        ref, replay = harness.replay_near_ties(
+            lambda forced: oracle_step(dims, dw, kv_ref, toks_for_ref, pos, s["block_tables"], forced=forced),
+            g_topk, NEAR_TIE)
         kv_ref = ref.kv
         where = f"{wl.name} step {step}"
         if wl.lm_head:
@@ -123,7 +107,7 @@ class _Ref:
     pass
 
 
-def oracle_step(dims, dw, kv, tokens, pos, bt, forced=None, rewind=False):
+def oracle_step(dims, dw, kv, tokens, pos, bt, forced=None):
     import oracle
     kv2 = copy.deepcopy(kv)
     r = oracle.decode_step(dims, dw, kv2, tokens, pos, bt, pos + 1, forced_topk=forced)
