@@ -248,7 +248,8 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
         set(pr.t, OP_GATEUP, l, lv1);
         const int f0 = j * nf, f1 = std::min(m.F, f0 + nf);
         pr.t.w[D_A0] = u; pr.t.w[D_A1] = f0; pr.t.w[D_A2] = f1 - f0;
-        pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
+        pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
+        pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
         pr.t.w[D_SIG] = c_h[l];
         pr.bytes = (int64_t)2 * (f1 - f0) * m.H * 2;
         pr.prio = 1;
@@ -282,7 +283,8 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   const int n_out_per_layer = (int)ceil_div(m.H, OUTR);
   for (auto& lvl : levels)
     for (auto& pr : lvl)
-      if ((pr.t.w[D_OP] == OP_QKV || pr.t.w[D_OP] == OP_ROUTER) && pr.t.w[D_W0] >= 0) pr.t.w[D_T0] = n_out_per_layer;
+      if ((pr.t.w[D_OP] == OP_QKV || pr.t.w[D_OP] == OP_ROUTER || pr.t.w[D_OP] == OP_GATEUP) && pr.t.w[D_W0] >= 0)
+        pr.t.w[D_T0] = n_out_per_layer;
   if (m.lm) {
     for (auto [a, e] : even(m.V, W)) {
       Proto pr;
@@ -651,11 +653,11 @@ mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens
   const size_t napart = (size_t)e->m.L * P->parts_per_layer * e->m.PART;
   if (ntask > e->task_cap) { if (e->d_tasks) (void)hipFree(e->d_tasks); e->d_tasks = nullptr; HIPCHK(e, dalloc(&e->d_tasks, ntask * DESC_WORDS)); e->task_cap = ntask; }
   if (nq > e->qoff_cap) { if (e->d_qoff) (void)hipFree(e->d_qoff); e->d_qoff = nullptr; HIPCHK(e, dalloc(&e->d_qoff, nq)); e->qoff_cap = nq; }
-  if (nctr > e->ctr_cap) { if (e->d_ctr) (void)hipFree(e->d_ctr); e->d_ctr = nullptr; HIPCHK(e, dalloc(&e->d_ctr, nctr)); e->ctr_cap = nctr; }
+  if (nctr > e->ctr_cap) { if (e->d_ctr) (void)hipFree(e->d_ctr); e->d_ctr = nullptr; HIPCHK(e, dalloc(&e->d_ctr, nctr * CTR_STRIDE)); e->ctr_cap = nctr; }
   if (napart > e->apart_floats) { if (e->d_apart) (void)hipFree(e->d_apart); e->d_apart = nullptr; HIPCHK(e, dalloc(&e->d_apart, napart)); e->apart_floats = napart; }
   HIPCHK(e, hipMemcpy(e->d_tasks, P->tasks.data(), ntask * sizeof(Task), hipMemcpyHostToDevice));
   HIPCHK(e, hipMemcpy(e->d_qoff, P->qoff.data(), nq * sizeof(int32_t), hipMemcpyHostToDevice));
-  HIPCHK(e, hipMemset(e->d_ctr, 0, e->ctr_cap * sizeof(uint32_t)));
+  HIPCHK(e, hipMemset(e->d_ctr, 0, e->ctr_cap * CTR_STRIDE * sizeof(uint32_t)));
   HIPCHK(e, hipDeviceSynchronize());
   delete e->plan;
   e->plan = P;
@@ -746,7 +748,7 @@ mk_status mk_reset(mk_engine* e) {
   if (!e) return MK_ERR_INVALID_ARG;
   HIPCHK(e, hipDeviceSynchronize());
   HIPCHK(e, hipMemset(e->d_err, 0, sizeof(DevError)));
-  if (e->d_ctr) HIPCHK(e, hipMemset(e->d_ctr, 0, e->ctr_cap * sizeof(uint32_t)));
+  if (e->d_ctr) HIPCHK(e, hipMemset(e->d_ctr, 0, e->ctr_cap * CTR_STRIDE * sizeof(uint32_t)));
   HIPCHK(e, hipMemset(e->d_amax, 0, sizeof(unsigned long long) * MAXB));
   HIPCHK(e, hipDeviceSynchronize());
   e->sticky = MK_OK;

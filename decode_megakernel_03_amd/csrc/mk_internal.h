@@ -10,7 +10,10 @@ constexpr int MAXB = 8;          // batch sizes up to 8 (P2 body)
 constexpr int PAGE = 16;         // KV tokens per page
 constexpr int NT = 256;          // threads per worker (4 wave64s)
 constexpr int NWAVE = NT / 64;
-constexpr int DESC_WORDS = 16;   // a task descriptor is 16 int32 = 64 bytes
+constexpr int DESC_WORDS = 16;
+// Dependency counters sit 256 bytes apart, one per cache line, so that the pollers and atomics of
+// different counters never share a line (and, across lines, spread over memory channels).
+constexpr int CTR_STRIDE = 64;   // a task descriptor is 16 int32 = 64 bytes
 
 // Task descriptor words. Which a* words an op reads is listed with the opcode.
 enum DescWord {

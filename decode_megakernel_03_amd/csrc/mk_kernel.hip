@@ -176,7 +176,8 @@ struct Ctl {            // small per-worker control block in static LDS
   unsigned long long t_ready;   // when the task's last dependency wait ended (trace)
   unsigned long long mark[4];   // op-specific phase ends (trace)
   int toks[MAXB];       // batch rows of the tokens a task works on
-  int bis[MAXB];        // (b << 8) | i of those tokens (expert slices)
+  int trank[MAXB];      // rank of an expert in each listed token's selection (expert slices)
+  unsigned long long mask[MAXB][2];   // per token: experts selected by the router (bit e)
   alignas(16) RouteTable rt;   // the layer's routing decision, copied in one round trip
 };
 __shared__ Ctl ctl_s;
@@ -214,13 +215,13 @@ __device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) 
   if (c < 0) return true;
   if (tid() == 0) {
     int ok = 1;
-    uint32_t v = ctr_load(p.ctr + c);
+    uint32_t v = ctr_load(p.ctr + (size_t)(c) * CTR_STRIDE);
     if (v < target) {
       const uint64_t t0 = now();
       uint32_t it = 0;
       for (;;) {
         __builtin_amdgcn_s_sleep(1);
-        v = ctr_load(p.ctr + c);
+        v = ctr_load(p.ctr + (size_t)(c) * CTR_STRIDE);
         if (v >= target) break;
         if ((++it & 15u) == 0) {
           if (ctr_load(&p.err->abort_flag)) { ok = 0; break; }
@@ -245,14 +246,14 @@ __device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) 
 __device__ bool wait_ge2(CParams& p, Ctl& ctl, int c0, uint32_t t0, int c1, uint32_t t1, int task) {
   if (tid() == 0) {
     int ok = 1;
-    uint32_t v0 = c0 >= 0 ? ctr_load(p.ctr + c0) : t0, v1 = c1 >= 0 ? ctr_load(p.ctr + c1) : t1;
+    uint32_t v0 = c0 >= 0 ? ctr_load(p.ctr + (size_t)(c0) * CTR_STRIDE) : t0, v1 = c1 >= 0 ? ctr_load(p.ctr + (size_t)(c1) * CTR_STRIDE) : t1;
     if (v0 < t0 || v1 < t1) {
       const uint64_t ts = now();
       uint32_t it = 0;
       for (;;) {
         __builtin_amdgcn_s_sleep(1);
-        if (c0 >= 0) v0 = ctr_load(p.ctr + c0);
-        if (c1 >= 0) v1 = ctr_load(p.ctr + c1);
+        if (c0 >= 0) v0 = ctr_load(p.ctr + (size_t)(c0) * CTR_STRIDE);
+        if (c1 >= 0) v1 = ctr_load(p.ctr + (size_t)(c1) * CTR_STRIDE);
         if (v0 >= t0 && v1 >= t1) break;
         if ((++it & 15u) == 0) {
           if (ctr_load(&p.err->abort_flag)) { ok = 0; break; }
@@ -281,7 +282,7 @@ __device__ uint32_t signal(CParams& p, Ctl& ctl, int c, bool want_old) {
   __syncthreads();
   uint32_t old = 0;
   if (tid() == 0 && c >= 0) {
-    old = ctr_add(p.ctr + c, 1u);
+    old = ctr_add(p.ctr + (size_t)(c) * CTR_STRIDE, 1u);
     if (want_old) ctl.flag = (int)old;
   }
   if (want_old) {
@@ -497,56 +498,80 @@ __device__ __forceinline__ bool op_qkv(int task) {
 // Routing decision of layer l for the whole batch, computed by the last router tile (R7 of the
 // oracle's readings): top-k of the raw logits with ties to the lower index, softmax over the k
 // selected, the union of experts over the batch and each union slot's token list.
+// Top-k of token b's router logits on one wave (R7 of the oracle's readings): K rounds of
+// wave-wide (largest logit, lowest index), returned in ascending expert order with the selection
+// as a 128-bit mask. Every consumer of a routing decision runs this same selection on the same
+// logits, so they agree exactly.
 template <class S>
-__device__ __forceinline__ void compute_route(CParams& p, int l, float* sm) {
+__device__ __forceinline__ void topk_select(CParams& p, int l, int b, int lane, bool emit, int (&widx)[S::K],
+                                            float (&wval)[S::K], unsigned long long& m0, unsigned long long& m1) {
   constexpr int E = S::E, K = S::K, EPL = (E + 63) / 64;   // experts held per lane
   static_assert(E <= 128 && K <= 8, "");
+  const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)l * MAXB * E);
+  float v[EPL];
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) v[k] = (lane + 64 * k < E) ? ldc(R, 4u * (b * E + lane + 64 * k)) : -INFINITY;
+  if (emit && p.rlog_out) {
+#pragma unroll
+    for (int k = 0; k < EPL; ++k)
+      if (lane + 64 * k < E) p.rlog_out[((size_t)l * p.B + b) * E + lane + 64 * k] = v[k];
+  }
+  // K rounds of wave-wide (largest logit, lowest index), winners removed
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    float bv = v[0];
+    int bi = lane;
+#pragma unroll
+    for (int k = 1; k < EPL; ++k)
+      if (v[k] > bv) { bv = v[k]; bi = lane + 64 * k; }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+      const float ov = __shfl_xor(bv, m, 64);
+      const int oi = __shfl_xor(bi, m, 64);
+      const bool take = ov > bv || (ov == bv && oi < bi);
+      bv = take ? ov : bv;
+      bi = take ? oi : bi;
+    }
+    widx[i] = bi;
+    wval[i] = bv;
+#pragma unroll
+    for (int k = 0; k < EPL; ++k)
+      if (lane + 64 * k == bi) v[k] = -INFINITY;
+  }
+  // ascending expert order (the MoE sum order)
+#pragma unroll
+  for (int i = 1; i < K; ++i)
+#pragma unroll
+    for (int j = i; j > 0; --j)
+      if (widx[j - 1] > widx[j]) {
+        const int ti = widx[j]; widx[j] = widx[j - 1]; widx[j - 1] = ti;
+        const float tv = wval[j]; wval[j] = wval[j - 1]; wval[j - 1] = tv;
+      }
+  m0 = 0; m1 = 0;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (widx[i] < 64) m0 |= 1ull << widx[i]; else m1 |= 1ull << (widx[i] - 64);
+  }
+}
+
+// Routing decision of layer l for the whole batch, computed by the last router tile (R7 of the
+// oracle's readings): top-k of the raw logits with ties to the lower index, softmax over the k
+// selected, the union of experts over the batch and each union slot's token list.
+template <class S>
+__device__ __forceinline__ void compute_route(CParams& p, int l) {
+  constexpr int E = S::E, K = S::K;
   const int B = p.B;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
-  unsigned long long* mask = reinterpret_cast<unsigned long long*>(sm);   // [MAXB][2] selected experts
-  const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)l * MAXB * E);
+  unsigned long long* mask = &ctl_s.mask[0][0];   // [MAXB][2] selected experts
   const __amdgpu_buffer_rsrc_t RT = rsrc(p.route + l);
-  // one wave per token: K rounds of wave-wide (largest logit, lowest index), winners removed
   for (int b = wave; b < B; b += NWAVE) {
-    float v[EPL];
-#pragma unroll
-    for (int k = 0; k < EPL; ++k) v[k] = (lane + 64 * k < E) ? ldc(R, 4u * (b * E + lane + 64 * k)) : -INFINITY;
-    if (p.rlog_out) {
-#pragma unroll
-      for (int k = 0; k < EPL; ++k)
-        if (lane + 64 * k < E) p.rlog_out[((size_t)l * B + b) * E + lane + 64 * k] = v[k];
-    }
     int widx[K];
     float wval[K];
+    unsigned long long m0, m1;
+    topk_select<S>(p, l, b, lane, true, widx, wval, m0, m1);
+    float top = wval[0];
 #pragma unroll
-    for (int i = 0; i < K; ++i) {
-      float bv = v[0];
-      int bi = lane;
-#pragma unroll
-      for (int k = 1; k < EPL; ++k)
-        if (v[k] > bv) { bv = v[k]; bi = lane + 64 * k; }
-#pragma unroll
-      for (int m = 1; m < 64; m <<= 1) {
-        const float ov = __shfl_xor(bv, m, 64);
-        const int oi = __shfl_xor(bi, m, 64);
-        if (ov > bv || (ov == bv && oi < bi)) { bv = ov; bi = oi; }
-      }
-      widx[i] = bi;
-      wval[i] = bv;
-#pragma unroll
-      for (int k = 0; k < EPL; ++k)
-        if (lane + 64 * k == bi) v[k] = -INFINITY;
-    }
-    const float top = wval[0];
-    // ascending expert order (the MoE sum order)
-#pragma unroll
-    for (int i = 1; i < K; ++i)
-#pragma unroll
-      for (int j = i; j > 0; --j)
-        if (widx[j - 1] > widx[j]) {
-          const int ti = widx[j]; widx[j] = widx[j - 1]; widx[j - 1] = ti;
-          const float tv = wval[j]; wval[j] = wval[j - 1]; wval[j - 1] = tv;
-        }
+    for (int i = 1; i < K; ++i) top = fmaxf(top, wval[i]);
     float ex[K];
 #pragma unroll
     for (int i = 0; i < K; ++i) ex[i] = expf(wval[i] - top);
@@ -558,10 +583,8 @@ __device__ __forceinline__ void compute_route(CParams& p, int l, float* sm) {
 #pragma unroll
       for (int i = 0; i < K; ++i) tot += ex[i];
     }
-    unsigned long long m0 = 0, m1 = 0;
 #pragma unroll
     for (int i = 0; i < K; ++i) {
-      if (widx[i] < 64) m0 |= 1ull << widx[i]; else m1 |= 1ull << (widx[i] - 64);
       if (lane == i) {
         stci(RT, (uint32_t)offsetof(RouteTable, sel) + 4u * (b * 8 + i), widx[i]);
         stc(RT, (uint32_t)offsetof(RouteTable, w) + 4u * (b * 8 + i), ex[i] / tot);
@@ -614,6 +637,7 @@ __device__ __forceinline__ bool op_router(int task) {
   if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
   stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
+  MARK(0);
   const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)T.layer * MAXB * E);
   const float* bias = p.has_bias ? Lp.router_bias : nullptr;
   gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
@@ -622,61 +646,92 @@ __device__ __forceinline__ bool op_router(int task) {
         const int e = row0 + r;
         stc(R, 4u * (t * E + e), bias ? v + bias[e] : v);
       });
+  MARK(1);
   const uint32_t old = signal(p, ctl, T.sig, true);
+  MARK(2);
   if (old + 1 == (uint32_t)T.a2) {      // last router tile of the layer: route the batch
     __syncthreads();
-    compute_route<S>(p, T.layer, sm);
+    compute_route<S>(p, T.layer);
+    MARK(3);
     signal(p, ctl, T.sig2, false);
   }
   return true;
 }
 
 // Expert slice: rows f0..f0+nf of W_gate[e] and W_up[e] for the tokens routed to union slot u;
-// h = SiLU(g) * u (P3 "Key Technologies and Architecture": fused SiLU-multiply).
+// h = SiLU(g) * u (P3 "Key Technologies and Architecture": fused SiLU-multiply). The normed input of
+// every token is staged as soon as x_l is complete, before the routing decision is awaited, so
+// that only the route table and the weights are on the path after the router.
 template <class S, int TB>
 __device__ __forceinline__ bool op_gateup(int task) {
   CParams& p = P();
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, F = S::F, K = S::K, NP = (Geo<H>::CPL >= 4) ? 2 : 4;
+  constexpr int H = S::H, F = S::F, K = S::K, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
   const int l = T.layer, u = T.a0, f0 = T.a1, nf = T.a2;
   const auto& Lp = cst(p.layers)[l];
-  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  load_route(p, l);
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;     // x_l complete
+  if (tid() < MAXB) ctl.toks[tid()] = tid();
+  __syncthreads();
+  stage_norm<S>(p, l, ctl.toks, p.B, Lp.attn_norm, sm, T.id);         // act[b] for every batch row
   MARK(0);
-  const RouteTable& rt = ctl.rt;
-  const int nu = rt.n_union;
+  if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;     // every router tile done
+  // the routing decision, taken here from the logits with the same selection as the route table
+  // (no further hop through the router's last tile): each wave selects for its tokens
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  for (int b = wave; b < p.B; b += NWAVE) {
+    int widx[K];
+    float wval[K];
+    unsigned long long m0, m1;
+    topk_select<S>(p, l, b, lane, false, widx, wval, m0, m1);
+    if (lane == 0) { ctl.mask[b][0] = m0; ctl.mask[b][1] = m1; }
+  }
+  __syncthreads();
+  unsigned long long u0 = 0, u1 = 0;
+  for (int b = 0; b < p.B; ++b) { u0 |= ctl.mask[b][0]; u1 |= ctl.mask[b][1]; }
+  const int n0 = __builtin_popcountll(u0), nu = n0 + __builtin_popcountll(u1);
   if (u < nu) {
-    const int e = rt.union_e[u];
-    const int ntok = rt.n_tok[u];
+    // expert of union slot u (the u-th selected expert in ascending order) and its tokens
+    unsigned long long m = u < n0 ? u0 : u1;
+    for (int j = u < n0 ? u : u - n0; j > 0; --j) m &= m - 1;
+    const int e = (u < n0 ? 0 : 64) + __builtin_ctzll(m);
+    if (tx == 0) {
+      int nt = 0;
+      for (int b = 0; b < p.B; ++b) {
+        const unsigned long long b0 = ctl.mask[b][0], b1 = ctl.mask[b][1];
+        const bool has = e < 64 ? (b0 >> e) & 1 : (b1 >> (e - 64)) & 1;
+        if (!has) continue;
+        ctl.toks[nt] = b;
+        ctl.trank[nt] = e < 64 ? __builtin_popcountll(b0 & ((1ull << e) - 1))
+                               : __builtin_popcountll(b0) + __builtin_popcountll(b1 & ((1ull << (e - 64)) - 1));
+        ++nt;
+      }
+      ctl.flag = nt;
+    }
     const uint16_t* wg = Lp.w_gate + (size_t)e * F * H;
     const uint16_t* wu = Lp.w_up + (size_t)e * F * H;
     auto rowptr = [&](int r) { return r < nf ? wg + (size_t)(f0 + r) * H : wu + (size_t)(f0 + r - nf) * H; };
     WBuf<H, NP> A;
     load_block<H, NP>(A, 0, 2 * nf, rowptr);
-    if (tid() < MAXB) {
-      const int t = tid();
-      const int bi = t < ntok ? rt.tok_bi[u][t] : 0;
-      ctl.bis[t] = bi;
-      ctl.toks[t] = bi >> 8;
-    }
     __syncthreads();
-    stage_norm<S>(p, l, ctl.toks, ntok, Lp.attn_norm, sm, T.id);
     MARK(1);
+    const int ntok = ctl.flag;
+    int brow[TB];       // batch row of the slot's t-th token
+#pragma unroll
+    for (int t = 0; t < TB; ++t) brow[t] = t < ntok ? ctl.toks[t] : 0;
     float* gu = sm + (size_t)TB * H;                 // [TB][2 nf]
     gemv_stream<H, NP, TB>(A, true, 2 * nf, ntok, rowptr,
-        [&](int r, int t) { return sm + (size_t)t * H; },
+        [&](int r, int t) { return sm + (size_t)brow[t] * H; },
         [&](int r, int t, float v) { gu[t * 2 * nf + r] = v; });
     __syncthreads();
     MARK(2);
     const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
     for (int i = tid(); i < ntok * nf; i += NT) {
       const int t = i / nf, f = i % nf;
-      const int bi = ctl.bis[t];
       const float g = gu[t * 2 * nf + f], up = gu[t * 2 * nf + nf + f];
       const float hv = (g / (1.f + expf(-g))) * up;
-      stc(Hb, 4u * (((bi >> 8) * K + (bi & 255)) * F + f0 + f), hv);
+      stc(Hb, 4u * ((ctl.toks[t] * K + ctl.trank[t]) * F + f0 + f), hv);
     }
   }
   drain();
@@ -1193,7 +1248,7 @@ __device__ __forceinline__ bool op_lmhead(int task) {
 __device__ void finish(CParams& p, Ctl& ctl) {
   drain();
   __syncthreads();
-  if (tid() == 0) ctl.flag = (int)(ctr_add(p.ctr + p.done_ctr, 1u) == (uint32_t)(p.n_workers - 1));
+  if (tid() == 0) ctl.flag = (int)(ctr_add(p.ctr + (size_t)(p.done_ctr) * CTR_STRIDE, 1u) == (uint32_t)(p.n_workers - 1));
   __syncthreads();
   if (!ctl.flag) return;
   if (tid() < MAXB) {
@@ -1202,10 +1257,10 @@ __device__ void finish(CParams& p, Ctl& ctl) {
     __hip_atomic_store(p.amax + tid(), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   for (int c = tid(); c < p.n_ctr; c += NT)
-    if (c != p.done_ctr) __hip_atomic_store(p.ctr + c, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (c != p.done_ctr) __hip_atomic_store(p.ctr + (size_t)(c) * CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   drain();
   __syncthreads();
-  if (tid() == 0) __hip_atomic_store(p.ctr + p.done_ctr, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid() == 0) __hip_atomic_store(p.ctr + (size_t)(p.done_ctr) * CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class S, int TB>
