@@ -495,13 +495,9 @@ __device__ __forceinline__ bool op_qkv(int task) {
   return true;
 }
 
-// Routing decision of layer l for the whole batch, computed by the last router tile (R7 of the
-// oracle's readings): top-k of the raw logits with ties to the lower index, softmax over the k
-// selected, the union of experts over the batch and each union slot's token list.
-// Top-k of token b's router logits on one wave (R7 of the oracle's readings): K rounds of
-// wave-wide (largest logit, lowest index), returned in ascending expert order with the selection
-// as a 128-bit mask. Every consumer of a routing decision runs this same selection on the same
-// logits, so they agree exactly.
+// Top-k of token b's router logits on one wave (R7 of the oracle's readings: ties go to the lower
+// expert index), returned in ascending expert order with the selection as a 128-bit mask. Every
+// consumer of a routing decision runs this same selection on the same logits, so they agree exactly.
 template <class S>
 __device__ __forceinline__ void topk_select(CParams& p, int l, int b, int lane, bool emit, int (&widx)[S::K],
                                             float (&wval)[S::K], unsigned long long& m0, unsigned long long& m1) {
@@ -516,41 +512,47 @@ __device__ __forceinline__ void topk_select(CParams& p, int l, int b, int lane, 
     for (int k = 0; k < EPL; ++k)
       if (lane + 64 * k < E) p.rlog_out[((size_t)l * p.B + b) * E + lane + 64 * k] = v[k];
   }
-  // K rounds of wave-wide (largest logit, lowest index), winners removed
+  // radix select of the K-th largest order key T (a ballot per bit: no data leaves the lanes),
+  // then every key above T and the lowest-indexed keys equal to T
+  uint32_t key[EPL];
 #pragma unroll
-  for (int i = 0; i < K; ++i) {
-    float bv = v[0];
-    int bi = lane;
-#pragma unroll
-    for (int k = 1; k < EPL; ++k)
-      if (v[k] > bv) { bv = v[k]; bi = lane + 64 * k; }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-      const float ov = __shfl_xor(bv, m, 64);
-      const int oi = __shfl_xor(bi, m, 64);
-      const bool take = ov > bv || (ov == bv && oi < bi);
-      bv = take ? ov : bv;
-      bi = take ? oi : bi;
-    }
-    widx[i] = bi;
-    wval[i] = bv;
-#pragma unroll
-    for (int k = 0; k < EPL; ++k)
-      if (lane + 64 * k == bi) v[k] = -INFINITY;
+  for (int k = 0; k < EPL; ++k) {
+    const uint32_t u = __float_as_uint(v[k] + 0.0f);          // -0 and +0 tie, as they compare
+    key[k] = (lane + 64 * k < E) ? ((u & 0x80000000u) ? ~u : (u | 0x80000000u)) : 0u;
   }
-  // ascending expert order (the MoE sum order)
+  uint32_t T = 0;
+  for (int bit = 31; bit >= 0; --bit) {
+    const uint32_t c = T | (1u << bit);
+    int cnt = 0;
 #pragma unroll
-  for (int i = 1; i < K; ++i)
+    for (int k = 0; k < EPL; ++k) cnt += __builtin_popcountll(__ballot(key[k] >= c));
+    if (cnt >= K) T = c;
+  }
+  unsigned long long sel[2] = {0ull, 0ull};
+  int need = K;
 #pragma unroll
-    for (int j = i; j > 0; --j)
-      if (widx[j - 1] > widx[j]) {
-        const int ti = widx[j]; widx[j] = widx[j - 1]; widx[j - 1] = ti;
-        const float tv = wval[j]; wval[j] = wval[j - 1]; wval[j - 1] = tv;
-      }
-  m0 = 0; m1 = 0;
+  for (int k = 0; k < EPL; ++k) {
+    sel[k] = __ballot(key[k] > T);
+    need -= __builtin_popcountll(sel[k]);
+  }
+#pragma unroll
+  for (int k = 0; k < EPL; ++k) {
+    unsigned long long eq = __ballot(key[k] == T);
+    while (need > 0 && eq) { sel[k] |= eq & (~eq + 1); eq &= eq - 1; --need; }
+  }
+  m0 = sel[0];
+  m1 = sel[1];
+  // the selected experts in ascending index order (the MoE sum order) and their logits
+  unsigned long long r0 = m0, r1 = m1;
 #pragma unroll
   for (int i = 0; i < K; ++i) {
-    if (widx[i] < 64) m0 |= 1ull << widx[i]; else m1 |= 1ull << (widx[i] - 64);
+    const bool lo = r0 != 0;
+    const unsigned long long r = lo ? r0 : r1;
+    const int bitpos = __builtin_ctzll(r);
+    if (lo) r0 &= r0 - 1; else r1 &= r1 - 1;
+    widx[i] = bitpos + (lo ? 0 : 64);
+    const float src = lo ? v[0] : v[EPL - 1];
+    wval[i] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(src), bitpos));
   }
 }
 

@@ -42,9 +42,11 @@ def check_logits(gpu, ref, where):
         assert d.max() <= MAX_ABS and rel <= MAX_REL_L2, f"{where}: token {b}: max|d| {d.max():.3g}, rel L2 {rel:.3g}"
 
 
-def run_steps(wl, steps, gains="ones", seed=0, teacher_force=False, split_keys=0):
+def run_steps(wl, steps, gains="ones", seed=0, teacher_force=False, split_keys=0, mutate=None, near_tie=NEAR_TIE):
     from decode_megakernel_03_amd import mk
     s = harness.tiny_setup(wl, seed=seed, gains=gains)
+    if mutate is not None:
+        mutate(s["w"])
     dims = harness.dims_of(wl)
     dw = harness.dense_weights(s["w"])
     kv_ref = harness.host_kv(s["k"], s["v"])
@@ -80,7 +82,7 @@ def run_steps(wl, steps, gains="ones", seed=0, teacher_force=False, split_keys=0
         toks_for_ref = tok_gpu if teacher_force else tok_ref
         ref, replay = harness.replay_near_ties(
             lambda forced: oracle_step(dims, dw, kv_ref, toks_for_ref, pos, s["block_tables"], forced=forced),
-            g_topk, NEAR_TIE)
+            g_topk, near_tie)
         kv_ref = ref.kv
         where = f"{wl.name} step {step}"
         if wl.lm_head:
@@ -136,3 +138,17 @@ def test_tiny_batch3_ragged():
 def test_tiny_split_attention():
     say("test_tiny_split_attention: 32-key attention splits (3 splits + log-sum-exp merge per group)")
     run_steps(synth.workload("tiny"), 4, split_keys=32)
+
+
+def _tied_router(w):
+    """Every router row equal to row 0 except the last, its exact negation: each layer's logits tie
+    exactly (experts 0..E-2) and the last expert is either the unique maximum or the unique minimum."""
+    for lw in w["layers"]:
+        r = lw["w_router"]
+        r[:] = r[0]
+        r[-1] = -r[0]
+
+
+def test_tiny_router_exact_ties():
+    say("test_tiny_router_exact_ties: exactly tied router logits resolve to the lowest expert index")
+    run_steps(synth.workload("tiny"), 4, mutate=_tied_router, near_tie=-1.0)
