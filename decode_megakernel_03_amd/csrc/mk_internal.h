@@ -13,7 +13,10 @@ constexpr int NWAVE = NT / 64;
 constexpr int DESC_WORDS = 16;
 // Dependency counters sit 256 bytes apart, one per cache line, so that the pollers and atomics of
 // different counters never share a line (and, across lines, spread over memory channels).
-constexpr int CTR_STRIDE = 64;   // a task descriptor is 16 int32 = 64 bytes
+constexpr int CTR_STRIDE = 64;
+// Trace record per task (MK_FLAG_TRACE): id | worker << 32, t_start, t_ready, t_end, marks.
+constexpr int TRACE_WORDS = 16;
+constexpr int TRACE_MARKS = TRACE_WORDS - 4;   // a task descriptor is 16 int32 = 64 bytes
 
 // Task descriptor words. Which a* words an op reads is listed with the opcode.
 enum DescWord {

@@ -151,20 +151,29 @@ __device__ __forceinline__ float partner(float v, int bit) {   // any bit of the
     case 2: return dpp_partner<2>(v);
     case 4: return dpp_partner<4>(v);
     case 8: return dpp_partner<8>(v);
+    case 16:   // swizzle in bit-mask mode: source lane = lane ^ 16 within each 32-lane half
+      return __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
     default: return __shfl_xor(v, bit, 64);
   }
 }
+__device__ __forceinline__ float lane_val(float v, int l) {     // v of lane l (uniform l)
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), l));
+}
 
+// Reductions over aligned groups of N lanes; for N = 64 the wave must be fully active (the last
+// step reads lanes 0 and 32) and the result is the same in every lane.
 template <int N>
-__device__ __forceinline__ float wsum(float v) {   // sum over aligned groups of N lanes
+__device__ __forceinline__ float wsum(float v) {
 #pragma unroll
-  for (int m = 1; m < N; m <<= 1) v += partner(v, m);
+  for (int m = 1; m < N && m < 32; m <<= 1) v += partner(v, m);
+  if constexpr (N == 64) v = lane_val(v, 0) + lane_val(v, 32);
   return v;
 }
 template <int N>
 __device__ __forceinline__ float wmax(float v) {
 #pragma unroll
-  for (int m = 1; m < N; m <<= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  for (int m = 1; m < N && m < 32; m <<= 1) v = fmaxf(v, partner(v, m));
+  if constexpr (N == 64) v = fmaxf(lane_val(v, 0), lane_val(v, 32));
   return v;
 }
 
@@ -174,7 +183,7 @@ struct Ctl {            // small per-worker control block in static LDS
   int ok;
   int flag;
   unsigned long long t_ready;   // when the task's last dependency wait ended (trace)
-  unsigned long long mark[4];   // op-specific phase ends (trace)
+  unsigned long long mark[TRACE_MARKS];   // op-specific phase ends (trace)
   int toks[MAXB];       // batch rows of the tokens a task works on
   int trank[MAXB];      // rank of an expert in each listed token's selection (expert slices)
   unsigned long long mask[MAXB][2];   // per token: experts selected by the router (bit e)
@@ -670,7 +679,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, F = S::F, K = S::K, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
+  constexpr int H = S::H, F = S::F, K = S::K, NP = (Geo<H>::CPL >= 4) ? 2 : 4;
   const int l = T.layer, u = T.a0, f0 = T.a1, nf = T.a2;
   const auto& Lp = cst(p.layers)[l];
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;     // x_l complete
@@ -978,6 +987,7 @@ __device__ __forceinline__ bool op_attn(int task) {
     }
   }
   __syncthreads();
+  MARK(2);
   // ---- pass B: o[hh][d] = sum_j p[j][hh] v_j[d]
   float o[HPG][8];
 #pragma unroll
@@ -1011,7 +1021,7 @@ __device__ __forceinline__ bool op_attn(int task) {
     for (int m = 0; m < 8; ++m) vv[m] = vnew[8 * li + m];
     accum(vv, nk);
   }
-  MARK(2);
+  MARK(3);
   // reduce o over the key slots of the wave (lanes sharing li), then over the waves via LDS
 #pragma unroll
   for (int hh = 0; hh < HPG; ++hh)
@@ -1039,12 +1049,17 @@ __device__ __forceinline__ bool op_attn(int task) {
     stc(Pw, 4u * (2 * HPG + i), v);
   }
   if (tx < 2 * HPG) stc(Pw, 4u * tx, ml[tx]);
+  MARK(4);
+  drain();
+  MARK(5);
   const uint32_t old = signal(p, ctl, T.sig, true);
-  MARK(3);
+  MARK(6);
   if (old + 1 == (uint32_t)nsplit) {
-    // last arriver: merge the nsplit partials of (b, g) in split order (log-sum-exp). The m and l of
-    // every split come in one round trip into LDS; each thread then owns 4 consecutive outputs of
-    // the HPG x D block and reads them from every partial with independent 16-byte loads.
+    // last arriver: merge the nsplit partials of (b, g) in split order (log-sum-exp). Each thread
+    // owns 4 consecutive outputs of the HPG x D block and reads them from MB partials per round
+    // trip (independent 16-byte loads); the first batch is requested together with the m and l of
+    // every split, which go through LDS.
+    constexpr int MB = 32;
     const __amdgpu_buffer_rsrc_t P0 = rsrc(p.apart + ((size_t)l * p.parts_per_layer + pbase) * S::PART);
     float* msl = sbuf;          // [nsplit][2 * HPG] m then l; m is overwritten by exp(m - M)
     float* linv = ml;           // [HPG] sum over splits of l * exp(m - M)
@@ -1052,47 +1067,64 @@ __device__ __forceinline__ bool op_attn(int task) {
       if (tx == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)MERGE_MAX, (uint32_t)nsplit, (uint32_t)b);
       return false;
     }
+    static_assert(HPG * D % 4 == 0 && HPG * D <= 4 * NT, "one float4 of outputs per thread");
+    const int i4 = tx * 4;
+    const bool mine = i4 < HPG * D;
+    f4 ob[MB];
+#pragma unroll
+    for (int u = 0; u < MB; ++u)
+      ob[u] = (mine && u < nsplit) ? ldc4(P0, 4u * (u * S::PART + 2 * HPG + i4)) : f4{0.f, 0.f, 0.f, 0.f};
     for (int i = tx; i < nsplit * 2 * HPG; i += NT)
       msl[i] = ldc(P0, 4u * ((i / (2 * HPG)) * S::PART + i % (2 * HPG)));
     __syncthreads();
-    for (int hh = tx; hh < HPG; hh += NT) {
+    MARK(7);
+    // per head: M = max over splits of m, scale_s = exp(m_s - M), L = sum_s l_s scale_s; half a
+    // wave per head, lanes over splits
+    static_assert(HPG <= 2 * NWAVE, "");
+    {
+      const int hh = 2 * wave + (lane >> 5), sl = lane & 31;
       float M = -INFINITY;
-      for (int s2 = 0; s2 < nsplit; ++s2) M = fmaxf(M, msl[s2 * 2 * HPG + hh]);
+      if (hh < HPG)
+        for (int s2 = sl; s2 < nsplit; s2 += 32) M = fmaxf(M, msl[s2 * 2 * HPG + hh]);
+      M = wmax<32>(M);
       float Lsum = 0.f;
-      for (int s2 = 0; s2 < nsplit; ++s2) {
-        const float ms = msl[s2 * 2 * HPG + hh];
-        const float sc = ms == -INFINITY ? 0.f : expf(ms - M);
-        msl[s2 * 2 * HPG + hh] = sc;
-        Lsum = __builtin_fmaf(msl[s2 * 2 * HPG + HPG + hh], sc, Lsum);
-      }
-      linv[hh] = Lsum;
+      if (hh < HPG)
+        for (int s2 = sl; s2 < nsplit; s2 += 32) {
+          const float ms = msl[s2 * 2 * HPG + hh];
+          const float sc = ms == -INFINITY ? 0.f : expf(ms - M);
+          msl[s2 * 2 * HPG + hh] = sc;
+          Lsum = __builtin_fmaf(msl[s2 * 2 * HPG + HPG + hh], sc, Lsum);
+        }
+      Lsum = wsum<32>(Lsum);
+      if (hh < HPG && sl == 0) linv[hh] = Lsum;
     }
     __syncthreads();
-    const __amdgpu_buffer_rsrc_t A = rsrc(p.attn + ((size_t)l * MAXB + b) * S::AD + g * HPG * D);
-    for (int i4 = tx * 4; i4 < HPG * D; i4 += NT * 4) {
+    MARK(8);
+    if (mine) {
       const int hh = i4 / D;
       f4 acc = {0.f, 0.f, 0.f, 0.f};
-      int s2 = 0;
-      for (; s2 + 8 <= nsplit; s2 += 8) {
-        f4 o[8];
+      for (int s0 = 0; s0 < nsplit; s0 += MB) {
+        if (s0 > 0) {
 #pragma unroll
-        for (int u = 0; u < 8; ++u) o[u] = ldc4(P0, 4u * ((s2 + u) * S::PART + 2 * HPG + i4));
+          for (int u = 0; u < MB; ++u)
+            ob[u] = (s0 + u < nsplit) ? ldc4(P0, 4u * ((s0 + u) * S::PART + 2 * HPG + i4)) : f4{0.f, 0.f, 0.f, 0.f};
+        }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float sc = msl[(s2 + u) * 2 * HPG + hh];
-          acc.x = __builtin_fmaf(o[u].x, sc, acc.x); acc.y = __builtin_fmaf(o[u].y, sc, acc.y);
-          acc.z = __builtin_fmaf(o[u].z, sc, acc.z); acc.w = __builtin_fmaf(o[u].w, sc, acc.w);
+        for (int u = 0; u < MB; ++u) {
+          if (s0 + u < nsplit) {
+            const float sc = msl[(s0 + u) * 2 * HPG + hh];
+            acc.x = __builtin_fmaf(ob[u].x, sc, acc.x); acc.y = __builtin_fmaf(ob[u].y, sc, acc.y);
+            acc.z = __builtin_fmaf(ob[u].z, sc, acc.z); acc.w = __builtin_fmaf(ob[u].w, sc, acc.w);
+          }
         }
       }
-      for (; s2 < nsplit; ++s2) {
-        const f4 o = ldc4(P0, 4u * (s2 * S::PART + 2 * HPG + i4));
-        const float sc = msl[s2 * 2 * HPG + hh];
-        acc.x = __builtin_fmaf(o.x, sc, acc.x); acc.y = __builtin_fmaf(o.y, sc, acc.y);
-        acc.z = __builtin_fmaf(o.z, sc, acc.z); acc.w = __builtin_fmaf(o.w, sc, acc.w);
-      }
       const float Lh = linv[hh];
+      const __amdgpu_buffer_rsrc_t A = rsrc(p.attn + ((size_t)l * MAXB + b) * S::AD + g * HPG * D);
       stc4(A, 4u * i4, f4{acc.x / Lh, acc.y / Lh, acc.z / Lh, acc.w / Lh});
     }
+    MARK(9);
+    drain();
+    MARK(10);
     signal(p, ctl, T.sig2, false);
   }
   return true;
@@ -1275,7 +1307,8 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
     const uint64_t t_start = trace ? now() : 0;
     if (trace && tid() == 0) {
       ctl_s.t_ready = t_start;
-      ctl_s.mark[0] = ctl_s.mark[1] = ctl_s.mark[2] = ctl_s.mark[3] = 0;
+#pragma unroll
+      for (int i = 0; i < TRACE_MARKS; ++i) ctl_s.mark[i] = 0;
     }
     if (trace) __syncthreads();
     bool ok;
@@ -1292,12 +1325,13 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
     }
     if (trace) __syncthreads();          // t_end: every wave is done with the task
     if (trace && tid() == 0) {
-      unsigned long long* tr = p.trace + (size_t)ti * 8;
+      unsigned long long* tr = p.trace + (size_t)ti * TRACE_WORDS;
       tr[0] = (unsigned long long)ti | ((unsigned long long)blockIdx.x << 32);
       tr[1] = t_start;
       tr[2] = ctl_s.t_ready;
       tr[3] = now();
-      tr[4] = ctl_s.mark[0]; tr[5] = ctl_s.mark[1]; tr[6] = ctl_s.mark[2]; tr[7] = ctl_s.mark[3];
+#pragma unroll
+      for (int i = 0; i < TRACE_MARKS; ++i) tr[4 + i] = ctl_s.mark[i];
     }
     if (!ok) break;
     __syncthreads();

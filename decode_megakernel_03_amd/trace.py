@@ -1,6 +1,6 @@
 """Decode the per-task trace of a step (MK_FLAG_TRACE) into timings and a Perfetto/Chrome JSON.
 
-Each task record is eight uint64: (task id | worker << 32, t_start, t_ready, t_end, mark0..3) in
+Each task record is sixteen uint64: (task id | worker << 32, t_start, t_ready, t_end, mark0..11) in
 100 MHz ticks of the GPU's constant real-time clock: t_ready is when its last dependency wait
 ended, so t_ready - t_start is time spent waiting (with its first weight block already in flight)
 and t_end - t_ready is time spent executing and signalling; marks are op-specific phase ends
@@ -14,13 +14,15 @@ import numpy as np
 
 OPS = {1: "qkv", 2: "router", 3: "gateup", 4: "attn", 5: "out", 6: "lmhead"}
 TICK_US = 0.01
+WORDS = 16
+MARKS = WORDS - 4
 
 
 def decode(trace, tasks):
-    """trace uint64 [n_tasks, 4]; tasks int32 [n_tasks, 16] (descriptors). Returns a record array."""
+    """trace uint64 [n_tasks, WORDS]; tasks int32 [n_tasks, 16] (descriptors). Returns a record array."""
     t0 = trace[:, 1].min()
     rec = np.zeros(len(trace), dtype=[("id", "i4"), ("worker", "i4"), ("op", "i4"), ("layer", "i4"),
-                                      ("start", "f8"), ("ready", "f8"), ("end", "f8"), ("mark", "f8", (4,))])
+                                      ("start", "f8"), ("ready", "f8"), ("end", "f8"), ("mark", "f8", (MARKS,))])
     rec["id"] = (trace[:, 0] & 0xFFFFFFFF).astype(np.int64)
     rec["worker"] = (trace[:, 0] >> 32).astype(np.int64)
     rec["op"] = tasks[:, 0]
@@ -28,7 +30,7 @@ def decode(trace, tasks):
     rec["start"] = (trace[:, 1] - t0) * TICK_US
     rec["ready"] = (trace[:, 2] - t0) * TICK_US
     rec["end"] = (trace[:, 3] - t0) * TICK_US
-    marks = trace[:, 4:8].astype(np.float64)
+    marks = trace[:, 4:WORDS].astype(np.float64)
     rec["mark"] = np.where(marks > 0, (marks - float(t0)) * TICK_US, np.nan)
     return rec
 
@@ -52,7 +54,7 @@ def summary(rec, n_workers):
                      f"exec {np.mean(r['end'] - r['ready']):7.2f} us (p90 {np.percentile(r['end'] - r['ready'], 90):6.2f})")
         prev = r["ready"]
         parts = []
-        for i in range(4):
+        for i in range(MARKS):
             mk_i = r["mark"][:, i]
             ok = ~np.isnan(mk_i)
             if ok.any():
