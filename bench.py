@@ -206,7 +206,7 @@ def run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps):
     import torch
     from decode_megakernel_03_amd import mk, trace
     info = eng.plan_info()
-    buf = torch.zeros(info.n_tasks, 8, dtype=torch.int64, device="cuda")
+    buf = torch.zeros(info.n_tasks, trace.WORDS, dtype=torch.int64, device="cuda")
     mk.mk_set_options(eng.h, flags=args.flags | mk.MK_FLAG_TRACE)
     mk.mk_set_step_outputs(eng.h, argmax_out=tokens, trace_out=buf)
     s = total_steps - 1

@@ -767,18 +767,39 @@ template <class S>
 struct AttnLds {
   static constexpr int al(int x) { return (x + 3) & ~3; }
   static constexpr int D = S::D, HPG = S::HPG;
-  static constexpr int CS = 0;
-  static constexpr int SB = al(CS + D);
-  static constexpr int VN = al(SB + (SPLIT_MAX + 1) * HPG);
+  static constexpr int PS = SPLIT_MAX + 32;        // P row stride (keys, zero tail for the last block)
+  static constexpr int VRS = D / 2 + 4;            // V tile row stride in floats (bf16 pairs + pad)
+  static constexpr int SB = 0;                     // [HPG][PS] scores -> probabilities
+  static constexpr int VT = al(SB + HPG * PS);     // [NWAVE][32][VRS] V tiles (one per wave)
+  static constexpr int OB = VT;                    // [NWAVE][HPG][D] per-wave P V, after the tiles
+  static constexpr int VN = al(VT + (NWAVE * 32 * VRS > NWAVE * HPG * D ? NWAVE * 32 * VRS : NWAVE * HPG * D));
   static constexpr int ML = al(VN + D);
-  static constexpr int OB = al(ML + 2 * HPG);
-  static constexpr int PG = al(OB + NWAVE * (D / 8) * HPG * 8);
+  static constexpr int PG = al(ML + 2 * HPG);
   static constexpr int KN = al(PG + SPLIT_MAX / PAGE + 1);
   static constexpr int QF = al(KN + D / 2);
   static constexpr int END = al(QF + HPG * D);
 };
 
+// Dynamic LDS: the ops' working area (the largest of: norm-staged activations + GEMV scratch,
+// attention buffers, OUT staging, routing scratch), then the step's RoPE table.
 template <class S>
+__host__ __device__ constexpr int rope_off(int tb) {
+  const int act = tb * S::H + tb * 2 * 64 + 1024;
+  const int att = AttnLds<S>::END;
+  const int out = S::AD + S::K * S::F + OUT_MAXR + S::K * OUT_MAXR + 2 * MAXB * OUT_MAXR;
+  const int rte = MAXB * S::E * 3 + S::E + 64;
+  int m = act;
+  if (att > m) m = att;
+  if (out > m) m = out;
+  if (rte > m) m = rte;
+  return (m + 63) & ~63;
+}
+
+// cos and sin of pos_b * inv_freq[i] for every sequence b of the step: [b][0..D/2) cos, [D/2..D) sin
+template <class S, int TB>
+__device__ __forceinline__ float* rope_tab() { return smem + rope_off<S>(TB); }
+
+template <class S, int TB>
 __device__ __forceinline__ bool op_attn(int task) {
   CParams& p = P();
   Ctl& ctl = ctl_s;
@@ -791,11 +812,12 @@ __device__ __forceinline__ bool op_attn(int task) {
   constexpr int GPW = KC / 16 / NWAVE;   // 16-key column blocks per wave per chunk
   constexpr int VPL = KC / KPI;          // V loads per lane per chunk (P V layout)
   static_assert(2 * HPG <= 16 && HPG % 2 == 0 && D % 32 == 0 && KC % KPI == 0, "");
+  static_assert(KC / NWAVE == 64 && KPW * VPL == 64 && HPG <= 2 * NWAVE, "P V: one 64-key quarter per wave");
   const int l = T.layer, b = T.a0, g = T.a1, k0 = T.a2, k1 = T.a3;
   const int pbase = T.a4, s_idx = T.a5 & 0xffff, nsplit = T.a5 >> 16;
   const auto& Lp = cst(p.layers)[l];
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
-  const int li = lane % LPK, slot = wave * KPW + lane / LPK;   // P V layout: key slot, 8-dim chunk
+  const int li = lane % LPK;                                    // 8-dim chunk of a V row
   const int col = lane & 15, grp = lane >> 4;                   // MFMA layout
   const int n_ctx = cst(p.seq_lens)[b], pos = cst(p.positions)[b];
   const bool last = k1 < 0;
@@ -813,11 +835,13 @@ __device__ __forceinline__ bool op_attn(int task) {
   }
   // LDS layout (float offsets in AttnLds<S>)
   using L = AttnLds<S>;
-  float* cs = sm + L::CS;                          // [D/2] cos, [D/2] sin
-  float* sbuf = sm + L::SB;                        // [SPLIT_MAX + 1][HPG] scores -> probabilities
+  const float* cs = rope_tab<S, TB>() + b * D;     // [D/2] cos, [D/2] sin at pos
+  constexpr int PS = L::PS, VRS = L::VRS;
+  float* sbuf = sm + L::SB;                        // [HPG][PS] scores -> probabilities
+  uint32_t* vt = reinterpret_cast<uint32_t*>(sm + L::VT) + wave * 32 * VRS;   // this wave's V tile
   float* vnew = sm + L::VN;                        // [D]
   float* ml = sm + L::ML;                          // [2][HPG]
-  float* obuf = sm + L::OB;                        // [NWAVE][LPK][HPG * 8]
+  float* obuf = sm + L::OB;                        // [NWAVE][HPG][D]
   int* pg = reinterpret_cast<int*>(sm + L::PG);    // [SPLIT_MAX / PAGE + 1] page ids
   uint32_t* knew = reinterpret_cast<uint32_t*>(sm + L::KN);   // [D / 2] new key, bf16 pairs
   float* qf = sm + L::QF;                          // [HPG][D] RoPE'd queries
@@ -833,17 +857,12 @@ __device__ __forceinline__ bool op_attn(int task) {
       pg[i] = page;
     }
   }
-  if (tx < D / 2) {
-    const double ang = (double)pos * cst(p.inv_freq)[tx];
-    cs[tx] = (float)cos(ang);
-    cs[D / 2 + tx] = (float)sin(ang);
-  }
   __syncthreads();
   // key j, dims d0..d0+7 -> element offset in the K (or V) cache
   auto kaddr = [&](int j, int d0) -> size_t {
     return (((size_t)pg[(j - k0) / PAGE] * S::HKV + g) * PAGE + (j % PAGE)) * D + d0;
   };
-  const int nchunk = (ntot + KC - 1) / KC;
+  const int nchunk = (nk + KC - 1) / KC;           // chunks of cached keys (the new key is apart)
   u4 kr[GPW][KB];       // MFMA B operands: key k0 + c*KC + (wave + NWAVE*i)*16 + col, dims 32kb + 8grp
   auto load_k = [&](int c) {
 #pragma unroll
@@ -854,11 +873,11 @@ __device__ __forceinline__ bool op_attn(int task) {
         kr[i][kb] = (j < kend) ? ldw(Lp.k_cache + kaddr(j, 32 * kb + 8 * grp)) : u4{0u, 0u, 0u, 0u};
     }
   };
-  u4 vr[VPL];           // P V layout: key k0 + c*KC + q*KPI + slot, dims 8li
+  u4 vr[VPL];           // key k0 + c*KC + 64*wave + KPW*q + lane/LPK (the wave's quarter), dims 8li
   auto load_v = [&](int c) {
 #pragma unroll
     for (int q = 0; q < VPL; ++q) {
-      const int j = k0 + c * KC + q * KPI + slot;
+      const int j = k0 + c * KC + (KC / NWAVE) * wave + KPW * q + lane / LPK;
       vr[q] = (j < kend) ? ldw(Lp.v_cache + kaddr(j, 8 * li)) : u4{0u, 0u, 0u, 0u};
     }
   };
@@ -948,104 +967,139 @@ __device__ __forceinline__ bool op_attn(int task) {
       for (int kb = 0; kb < KB; ++kb)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], __builtin_bit_cast(bf8, kr[i][kb]), acc, 0, 0, 0);
       if (2 * grp < HPG && jb + col < nk) {
-        typedef float f2 __attribute__((ext_vector_type(2)));
-        *reinterpret_cast<f2*>(sbuf + (jb + col) * HPG + 2 * grp) = f2{(acc[0] + acc[2]) * rsd, (acc[1] + acc[3]) * rsd};
+        sbuf[(2 * grp) * PS + jb + col] = (acc[0] + acc[2]) * rsd;
+        sbuf[(2 * grp + 1) * PS + jb + col] = (acc[1] + acc[3]) * rsd;
       }
     }
   }
   __syncthreads();
   MARK(1);
-  // ---- softmax statistics per head (wave w handles heads w, w + 4, ...); the new key's score is a
-  // plain fp32 dot product of the RoPE'd query with the bf16 key
-  for (int hh = wave; hh < HPG; hh += NWAVE) {
+  // ---- softmax statistics per head (half a wave per head, lanes over keys); the new key's score
+  // is a plain fp32 dot product of the RoPE'd query with the bf16 key
+  {
+    const int hh = 2 * wave + (lane >> 5), sl = lane & 31;
+    const bool hv = hh < HPG;
+    float* prow = sbuf + (hv ? hh : 0) * PS;
     float snew = -INFINITY;
     if (last) {
       float t = 0.f;
-      for (int d2 = lane; d2 < D / 2; d2 += 64) {
-        const uint32_t kw = knew[d2];
-        t += qf[hh * D + 2 * d2] * bf_lo(kw) + qf[hh * D + 2 * d2 + 1] * bf_hi(kw);
-      }
-      snew = wsum<64>(t) * rsd;
+      if (hv)
+        for (int d2 = sl; d2 < D / 2; d2 += 32) {
+          const uint32_t kw = knew[d2];
+          t += qf[hh * D + 2 * d2] * bf_lo(kw) + qf[hh * D + 2 * d2 + 1] * bf_hi(kw);
+        }
+      snew = wsum<32>(t) * rsd;
     }
     float m = snew;
-    for (int j = lane; j < nk; j += 64) m = fmaxf(m, sbuf[j * HPG + hh]);
-    m = wmax<64>(m);
+    if (hv)
+      for (int j = sl; j < nk; j += 32) m = fmaxf(m, prow[j]);
+    m = wmax<32>(m);
     float lsum = 0.f;
-    for (int j = lane; j < nk; j += 64) {
-      const float e = expf(sbuf[j * HPG + hh] - m);
-      sbuf[j * HPG + hh] = e;
-      lsum += e;
-    }
-    lsum = wsum<64>(lsum);
-    if (lane == 0) {
-      if (last) {
-        const float e = expf(snew - m);
-        sbuf[nk * HPG + hh] = e;
+    if (hv)
+      for (int j = sl; j < nk; j += 32) {
+        const float e = expf(prow[j] - m);
+        prow[j] = e;
         lsum += e;
       }
-      ml[hh] = m; ml[HPG + hh] = lsum;
+    lsum = wsum<32>(lsum);
+    if (hv) {
+      // the new key's probability, then zeros up to the end of the last 32-key block (P V reads it)
+      const int zend = ((nk + 31) & ~31) + 32;
+      for (int j = nk + sl; j < zend; j += 32) prow[j] = (last && j == nk) ? expf(snew - m) : 0.f;
+      if (sl == 0) {
+        ml[hh] = m;
+        ml[HPG + hh] = last ? lsum + expf(snew - m) : lsum;
+      }
     }
   }
   __syncthreads();
   MARK(2);
-  // ---- pass B: o[hh][d] = sum_j p[j][hh] v_j[d]
-  float o[HPG][8];
+  // ---- pass B: o[hh][d] = sum_j p[hh][j] v_j[d] on the matrix cores. Each wave owns a 64-key
+  // quarter of every chunk: its V rows go through a private LDS tile so that the B operand (8
+  // consecutive keys of one dimension) is read column-wise; the A operand is P in bf16 high and low
+  // parts, rows arranged as for the scores (heads 2a, 2a+1 high in rows 4a, 4a+1, low in 4a+2, 4a+3).
+  constexpr int NCB = D / 16;            // 16-dim column blocks
+  f4 oacc[NCB];
 #pragma unroll
-  for (int hh = 0; hh < HPG; ++hh)
+  for (int cb = 0; cb < NCB; ++cb) oacc[cb] = f4{0.f, 0.f, 0.f, 0.f};
+  {
+    const int ph = 2 * (col >> 2) + (col & 1);
+    const bool pvalid = ph < HPG, plo = (col & 2) != 0;
+    const float* prow = sbuf + (pvalid ? ph : 0) * PS;
+    for (int c = 0; c < nchunk; ++c) {
+      if (c > 0) load_v(c);
 #pragma unroll
-    for (int m = 0; m < 8; ++m) o[hh][m] = 0.f;
-  auto accum = [&](const float (&vv)[8], int jj) {
-    const float* pr = sbuf + jj * HPG;
+      for (int kh = 0; kh < 2; ++kh) {              // the wave's two 32-key blocks
+        const int kbase = c * KC + (KC / NWAVE) * wave + 32 * kh;   // relative to k0
+        if (kbase >= nk) continue;                   // uniform in the wave
+        // V rows kbase + r (r < 32) into the tile: load QPB * kh + q holds row KPW * q + lane / LPK
+        constexpr int QPB = 32 / KPW;
 #pragma unroll
-    for (int hh = 0; hh < HPG; ++hh) {
-      const float pj = pr[hh];
+        for (int q = 0; q < QPB; ++q) {
+          const int r = KPW * q + lane / LPK;
+          *reinterpret_cast<u4*>(vt + r * VRS + 4 * li) = vr[QPB * kh + q];
+        }
+        // the tile is written as 16-byte vectors and read as 16-bit halves: keep the compiler from
+        // moving either across the other (the wave's own LDS accesses execute in order)
+        asm volatile("" ::: "memory");
+        // A operand: P rows, keys kbase + 8 grp .. + 7
+        bf8 pa;
+        {
+          const f4 x0 = *reinterpret_cast<const f4*>(prow + kbase + 8 * grp);
+          const f4 x1 = *reinterpret_cast<const f4*>(prow + kbase + 8 * grp + 4);
+          const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+          uint32_t w[4];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) o[hh][m] = __builtin_fmaf(pj, vv[m], o[hh][m]);
-    }
-  };
-  for (int c = 0; c < nchunk; ++c) {
-    if (c > 0) load_v(c);
+          for (int m = 0; m < 4; ++m) {
+            uint32_t a = f2bf(x[2 * m]), c2 = f2bf(x[2 * m + 1]);
+            if (plo) { a = f2bf(x[2 * m] - bf1((uint16_t)a)); c2 = f2bf(x[2 * m + 1] - bf1((uint16_t)c2)); }
+            w[m] = pvalid ? (a | (c2 << 16)) : 0u;
+          }
+          pa = __builtin_bit_cast(bf8, u4{w[0], w[1], w[2], w[3]});
+        }
+        // B operands: tile rows 8 grp .. + 7 of dimension 16 cb + col
+        const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
 #pragma unroll
-    for (int q = 0; q < VPL; ++q) {
-      const int jj = c * KC + q * KPI + slot;
-      if (jj < nk) {
-        const float vv[8] = {bf_lo(vr[q].x), bf_hi(vr[q].x), bf_lo(vr[q].y), bf_hi(vr[q].y),
-                             bf_lo(vr[q].z), bf_hi(vr[q].z), bf_lo(vr[q].w), bf_hi(vr[q].w)};
-        accum(vv, jj);
+        for (int cb = 0; cb < NCB; ++cb) {
+          uint32_t w[4];
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            const uint32_t lo16 = vt16[(8 * grp + 2 * m) * (2 * VRS) + 16 * cb + col];
+            const uint32_t hi16 = vt16[(8 * grp + 2 * m + 1) * (2 * VRS) + 16 * cb + col];
+            w[m] = lo16 | (hi16 << 16);
+          }
+          oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf8, u4{w[0], w[1], w[2], w[3]}),
+                                                             oacc[cb], 0, 0, 0);
+        }
+        asm volatile("" ::: "memory");
       }
     }
   }
-  if (last && slot == 0) {
-    float vv[8];
-#pragma unroll
-    for (int m = 0; m < 8; ++m) vv[m] = vnew[8 * li + m];
-    accum(vv, nk);
-  }
   MARK(3);
-  // reduce o over the key slots of the wave (lanes sharing li), then over the waves via LDS
+  // rows 4a..4a+3 of a lane's accumulators: high and low parts of heads 2a, 2a+1 -> add them; the
+  // new key's value row joins in wave 0
+  __syncthreads();                       // every wave is done with its V tile (obuf aliases them)
+  if (2 * grp < HPG) {
+    const float pn0 = last ? sbuf[(2 * grp) * PS + nk] : 0.f, pn1 = last ? sbuf[(2 * grp + 1) * PS + nk] : 0.f;
 #pragma unroll
-  for (int hh = 0; hh < HPG; ++hh)
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      float v = o[hh][m];
-#pragma unroll
-      for (int s2 = LPK; s2 < 64; s2 <<= 1) v += __shfl_xor(v, s2, 64);
-      o[hh][m] = v;
+    for (int cb = 0; cb < NCB; ++cb) {
+      const int d = 16 * cb + col;
+      float o0 = oacc[cb][0] + oacc[cb][2], o1 = oacc[cb][1] + oacc[cb][3];
+      if (last && wave == 0) {
+        o0 = __builtin_fmaf(pn0, vnew[d], o0);
+        o1 = __builtin_fmaf(pn1, vnew[d], o1);
+      }
+      obuf[(wave * HPG + 2 * grp) * D + d] = o0;
+      obuf[(wave * HPG + 2 * grp + 1) * D + d] = o1;
     }
-  if (lane < LPK) {
-#pragma unroll
-    for (int hh = 0; hh < HPG; ++hh)
-#pragma unroll
-      for (int m = 0; m < 8; ++m) obuf[(wave * LPK + li) * HPG * 8 + hh * 8 + m] = o[hh][m];
   }
   __syncthreads();
   // partial: m[HPG], l[HPG], o[HPG][D] (unnormalised)
   const size_t part = ((size_t)l * p.parts_per_layer + pbase + s_idx) * S::PART;
   const __amdgpu_buffer_rsrc_t Pw = rsrc(p.apart + part);
   for (int i = tx; i < HPG * D; i += NT) {
-    const int hh = i / D, d = i % D, c = d / 8, m = d % 8;
     float v = 0.f;
-    for (int w = 0; w < NWAVE; ++w) v += obuf[(w * LPK + c) * HPG * 8 + hh * 8 + m];
+    for (int w = 0; w < NWAVE; ++w) v += obuf[w * HPG * D + i];
     stc(Pw, 4u * (2 * HPG + i), v);
   }
   if (tx < 2 * HPG) stc(Pw, 4u * tx, ml[tx]);
@@ -1133,8 +1187,8 @@ __device__ __forceinline__ bool op_attn(int task) {
 // Output rows row0..row0+nrows of the layer for every token: the fused residual add that rejoins
 // both branches (P1 "One persistent kernel for the whole decode step"):
 //   x_{l+1} = (x_l + W_o attn) + sum_i w_i W_down[e_i] h_i   (experts in ascending index).
-// Waits for the routing table (to prefetch the right W_down rows), the MoE slices and the
-// attention of every KV group.
+// Waits for the routing table (to prefetch the right W_down rows), then for the MoE slices (the
+// MoE term is formed first), then for the attention of every KV group.
 template <class S, int TB>
 __device__ __forceinline__ bool op_out(int task) {
   CParams& p = P();
@@ -1158,9 +1212,13 @@ __device__ __forceinline__ bool op_out(int task) {
   float* o_s = h_s + K * F;                                            // [OUT_MAXR]
   float* y_s = o_s + OUT_MAXR;                                         // [K][OUT_MAXR]
   if (!pre) load_block<AD, NPO>(WO, 0, nrows, orow);
+  float* mo_s = y_s + K * OUT_MAXR;                                    // [MAXB][OUT_MAXR] MoE term
+  float* xv_s = mo_s + MAXB * OUT_MAXR;                                // [MAXB][OUT_MAXR] x_l rows
   const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
   const __amdgpu_buffer_rsrc_t At = rsrc(p.attn + (size_t)l * MAXB * AD);
   const __amdgpu_buffer_rsrc_t Xn = rsrc(p.x + (size_t)(l + 1) * MAXB * H);
+  // MoE branch first: the expert slices finish before the attention merges, so only the O
+  // projection and the residual add remain once attention is in
   for (int b = 0; b < p.B; ++b) {
     int sel[K];
 #pragma unroll
@@ -1174,16 +1232,10 @@ __device__ __forceinline__ bool op_out(int task) {
     };
     WBuf<F, NPD> WD;
     load_block<F, NPD>(WD, 0, K * nrows, drow);
-    if (b == 0) {
-      // all MoE slices and the attention of every KV group
-      if (!wait_ge2(p, ctl, T.w1, (uint32_t)T.t1, T.a2, (uint32_t)T.a3, T.id)) return false;
-    }
-    for (int i = tid() * 4; i < AD; i += NT * 4) *reinterpret_cast<f4*>(a_s + i) = ldc4(At, 4u * (b * AD + i));
+    if (b == 0 && !wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every MoE slice
     for (int i = tid() * 4; i < K * F; i += NT * 4) *reinterpret_cast<f4*>(h_s + i) = ldc4(Hb, 4u * (b * K * F + i));
     __syncthreads();
     if (b == 0) MARK(0);
-    compute_block<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
-                              [&](int r, int t, float v) { o_s[r] = v; });
     compute_block<F, NPD, 1>(WD, 0, K * nrows, 1, [&](int q, int t) { return h_s + (q / nrows) * F; },
                              [&](int q, int t, float v) { y_s[(q / nrows) * OUT_MAXR + q % nrows] = v; });
     __syncthreads();
@@ -1200,15 +1252,30 @@ __device__ __forceinline__ bool op_out(int task) {
       float moe = 0.f;
       for (int i = 0; i < K; ++i)
         moe = moe + rt.w[b][i] * y_s[i * OUT_MAXR + r];
-      const float xn = (xv + o_s[r]) + moe;
+      mo_s[b * OUT_MAXR + r] = moe;
+      xv_s[b * OUT_MAXR + r] = xv;
+    }
+  }
+  MARK(1);
+  if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
+  for (int b = 0; b < p.B; ++b) {
+    for (int i = tid() * 4; i < AD; i += NT * 4) *reinterpret_cast<f4*>(a_s + i) = ldc4(At, 4u * (b * AD + i));
+    __syncthreads();
+    if (b == 0) MARK(2);
+    compute_block<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
+                              [&](int r, int t, float v) { o_s[r] = v; });
+    __syncthreads();
+    if (tid() < nrows) {
+      const int r = tid(), row = row0 + r;
+      const float xn = (xv_s[b * OUT_MAXR + r] + o_s[r]) + mo_s[b * OUT_MAXR + r];
       stc(Xn, 4u * (b * H + row), xn);
       if (p.hidden_out && l == p.L - 1) p.hidden_out[(size_t)b * H + row] = xn;
     }
     __syncthreads();
   }
-  MARK(1);
+  MARK(3);
   drain();
-  MARK(2);
+  MARK(4);
   signal(p, ctl, T.sig, false);
   return true;
 }
@@ -1302,6 +1369,18 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
   CParams& p = P();
   const int qs = cst(p.qoff)[blockIdx.x], qe = cst(p.qoff)[blockIdx.x + 1];
   const bool trace = (p.flags & 1) && p.trace;
+  {
+    // the step's RoPE table: angle in double precision (R3), then rounded to float
+    constexpr int D = S::D;
+    float* tab = rope_tab<S, TB>();
+    for (int i = tid(); i < p.B * (D / 2); i += NT) {
+      const int b = i / (D / 2), j = i % (D / 2);
+      const double ang = (double)cst(p.positions)[b] * cst(p.inv_freq)[j];
+      tab[b * D + j] = (float)cos(ang);
+      tab[b * D + D / 2 + j] = (float)sin(ang);
+    }
+    __syncthreads();
+  }
   for (int ti = qs; ti < qe; ++ti) {
     const int op = cst(p.tasks)[(size_t)ti * DESC_WORDS + D_OP];
     const uint64_t t_start = trace ? now() : 0;
@@ -1316,7 +1395,7 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
       case OP_QKV: ok = op_qkv<S, TB>(ti); break;
       case OP_ROUTER: ok = op_router<S, TB>(ti); break;
       case OP_GATEUP: ok = op_gateup<S, TB>(ti); break;
-      case OP_ATTN: ok = op_attn<S>(ti); break;
+      case OP_ATTN: ok = op_attn<S, TB>(ti); break;
       case OP_OUT: ok = op_out<S, TB>(ti); break;
       case OP_LMHEAD: ok = op_lmhead<S, TB>(ti); break;
       default:
@@ -1343,16 +1422,7 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
 
 template <class S>
 static size_t lds_bytes(int tb) {
-  // norm-staged activations + GEMV scratch, attention buffers, OUT staging: the largest wins
-  const size_t act = (size_t)tb * S::H * 4 + (size_t)tb * 2 * 64 * 4 + 4096;
-  const size_t att = (size_t)AttnLds<S>::END * 4;
-  const size_t out = ((size_t)S::AD + S::K * S::F + OUT_MAXR + S::K * OUT_MAXR) * 4;
-  const size_t rte = ((size_t)MAXB * S::E * 3 + S::E) * 4 + 256;
-  size_t m = act;
-  if (att > m) m = att;
-  if (out > m) m = out;
-  if (rte > m) m = rte;
-  return (m + 255) & ~(size_t)255;
+  return ((size_t)rope_off<S>(tb) + MAXB * S::D) * 4;
 }
 
 template <class S, int TB>

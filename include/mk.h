@@ -148,8 +148,8 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
  *   argmax_out int32 [B]       greedy token (first index of the maximum logit)
  *   topk_out int32 [L, B, k]   routed experts per layer and token, ascending expert index
  *   hidden_out float32 [B, H]  residual stream after the last layer
- *   trace_out uint64 [tasks, 8] when MK_FLAG_TRACE: {task id | worker << 32, t_start, t_ready,
- *                              t_end, mark0..mark3} in 100 MHz ticks (size via mk_plan_info);
+ *   trace_out uint64 [tasks, 16] when MK_FLAG_TRACE: {task id | worker << 32, t_start, t_ready,
+ *                              t_end, mark0..mark11} in 100 MHz ticks (size via mk_plan_info);
  *                              marks are op-specific phase ends, 0 where an op sets none
  *   router_logits_out float32 [L, B, E]  the router logits (bias included) exactly as the routing
  *                              decision of each layer read them */

@@ -95,12 +95,17 @@ def run_steps(wl, steps, gains="ones", seed=0, teacher_force=False, split_keys=0
         stats.append((float(np.abs(g_logits[:, :wl.vocab] - ref.logits).max()) if wl.lm_head else float(d.max()), len(replay)))
         tok_gpu = g_arg
         tok_ref = np.argmax(ref.logits, axis=1) if wl.lm_head else tok_gpu
-    # the KV cache the GPU wrote equals the oracle's (bf16 patterns; rare 1-ulp rounding flips allowed)
+    # the KV cache the GPU wrote equals the oracle's bf16 patterns except for rare rounding flips: the
+    # new rows are fp32 results rounded to bf16, so a flip is one bf16 step (2^-7 relative at most)
+    # of a value, or, for values near zero, the fp32 noise (~1e-6 absolute) that reaches them
+    import oracle
     for l in range(wl.n_layers):
         for name, dev, host in (("K", kd, kv_ref.k), ("V", vd, kv_ref.v)):
-            g = synth.to_u16(dev[l]).astype(np.int32)
-            diff = np.abs(g - host[l].astype(np.int32))
-            assert diff.max() <= 1 and (diff > 0).mean() < 1e-3, f"layer {l} {name} cache differs (max {diff.max()})"
+            g16 = synth.to_u16(dev[l])
+            gd, hd = oracle.bf16_to_f32(g16).astype(np.float64), oracle.bf16_to_f32(host[l]).astype(np.float64)
+            bad = np.abs(gd - hd) > np.abs(hd) * 2.0 ** -7 + 1e-5
+            assert not bad.any(), f"layer {l} {name} cache differs at {np.argwhere(bad)[:4].tolist()}"
+            assert (g16 != host[l]).mean() < 1e-3, f"layer {l} {name} cache: {(g16 != host[l]).sum()} entries differ"
     eng.close()
     return stats
 
