@@ -165,7 +165,8 @@ def main():
     if os.path.exists(prof):
         rec = json.load(open(prof))
         if rec.get("kernel_hash") == kernel_source_hash():
-            traffic = rec.get("bytes_per_launch")
+            # measured HBM bytes per launch over the same per-launch duration as `achieved`
+            traffic = round(rec["bytes_per_launch"] / float(np.mean(step_ms / 1e3)) / 1e9, 1)
 
     cpu = None
     parity = None
