@@ -21,6 +21,7 @@
 #include <random>
 #include <string>
 #include <vector>
+#include <unordered_map>
 
 #include "../../include/mk.h"
 #include "mk_internal.h"
@@ -110,6 +111,7 @@ struct Proto {            // task before placement
   Task t;
   int64_t bytes;
   int prio;               // order inside a worker's level segment (lower first)
+  int pin = -1;           // attention merge: placed on the worker of this split (b, g, s) key
 };
 
 void set(Task& t, int op, int layer, int level) {
@@ -127,7 +129,7 @@ std::vector<std::pair<int, int>> even(int len, int n) {
 }
 
 mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, int W, int split_req,
-                     mk_plan* P, std::string* why) {
+                     mk_plan* P, std::string* why, int flags = 0) {
   const Dims m = dims_of(desc);
   P->desc = desc; P->m = m; P->B = B; P->n_workers = W;
   P->seq_lens.assign(seq_lens, seq_lens + B);
@@ -191,10 +193,14 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   nf = std::max(4, std::min(64, nf));
   const int slices = (int)ceil_div(m.F, nf);
 
-  std::vector<std::vector<Proto>> levels(3 * L + 1);
+  // levels per layer: QKV + router | attention splits + expert slices | attention merges | output rows
+  constexpr int LPL = 4;
+  const int nslice = std::max(1, m.HPG * m.D / 256);       // merge tasks per (sequence, KV group)
+  auto split_key = [&](int l, int b, int g, int s) { return ((l * B + b) * m.HKV + g) * 65536 + s; };
+  std::vector<std::vector<Proto>> levels(LPL * L + 1);
   int n_attn = 0;
   for (int l = 0; l < L; ++l) {
-    const int lv0 = 3 * l, lv1 = 3 * l + 1, lv2 = 3 * l + 2;
+    const int lv0 = LPL * l, lv1 = LPL * l + 1, lvm = LPL * l + 2, lv2 = LPL * l + 3;
     // level 0: QKV rows (per KV group: q heads, k, v) and router tiles
     std::vector<int> qkv_count(m.HKV, 0);
     for (int g = 0; g < m.HKV; ++g) {
@@ -216,13 +222,14 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       Proto pr;
       set(pr.t, OP_ROUTER, l, lv0);
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a; pr.t.w[D_A2] = router_tiles;
-      pr.t.w[D_W0] = c_x[l];
+      pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;   // target filled below
       pr.t.w[D_SIG] = c_rarr[l]; pr.t.w[D_SIG2] = c_route[l];
       pr.bytes = (int64_t)(e - a) * m.H * 2;
       pr.prio = 0;
       levels[lv0].push_back(pr);
     }
-    // level 1: attention splits, expert slices
+    // level 1: attention splits (each writes its partial and signals its group's arrival
+    // counter), expert slices
     for (int b = 0; b < B; ++b)
       for (int g = 0; g < m.HKV; ++g)
         for (int s = 0; s < nsplit[b]; ++s) {
@@ -234,10 +241,11 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.t.w[D_A4] = pbase_b[b] + g * nsplit[b];
           pr.t.w[D_A5] = s | (nsplit[b] << 16);
           pr.t.w[D_W0] = c_qkv[l][g]; pr.t.w[D_T0] = qkv_count[g];
-          pr.t.w[D_SIG] = c_aarr[l][b * m.HKV + g]; pr.t.w[D_SIG2] = c_att[l];
+          pr.t.w[D_SIG] = c_aarr[l][b * m.HKV + g];
           const int keys = last ? seq_lens[b] - k0 : split;
           pr.bytes = (int64_t)keys * m.D * 2 * 2;
           pr.prio = 0;
+          pr.pin = -2 - split_key(l, b, g, s);     // records its worker (see placement)
           levels[lv1].push_back(pr);
           n_attn++;
         }
@@ -256,13 +264,29 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
         levels[lv1].push_back(pr);
         n_gu++;
       }
+    // level 2: attention merges, nslice per (sequence, KV group), each on the worker of one of the
+    // group's splits (that worker is done with the step's heavy streams by then)
+    for (int b = 0; b < B; ++b)
+      for (int g = 0; g < m.HKV; ++g)
+        for (int q = 0; q < nslice; ++q) {
+          Proto pr;
+          set(pr.t, OP_MERGE, l, lvm);
+          pr.t.w[D_A0] = b; pr.t.w[D_A1] = g; pr.t.w[D_A2] = q; pr.t.w[D_A3] = nslice;
+          pr.t.w[D_A4] = pbase_b[b] + g * nsplit[b]; pr.t.w[D_A5] = nsplit[b];
+          pr.t.w[D_W0] = c_aarr[l][b * m.HKV + g]; pr.t.w[D_T0] = nsplit[b];
+          pr.t.w[D_SIG] = c_att[l];
+          pr.bytes = (int64_t)nsplit[b] * m.HPG * (m.D + 2) * 4 / nslice;
+          pr.prio = 0;
+          pr.pin = split_key(l, b, g, (int)((int64_t)q * nsplit[b] / nslice));
+          levels[lvm].push_back(pr);
+        }
     // level 2: output rows (O-proj + expert down-proj + residual)
     int n_out = 0;
     for (auto [a, e] : even(m.H, (int)ceil_div(m.H, OUTR))) {
       Proto pr;
       set(pr.t, OP_OUT, l, lv2);
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
-      pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV;
+      pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV * nslice;
       pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
       pr.t.w[D_W1] = c_h[l]; pr.t.w[D_T1] = n_gu;
       pr.t.w[D_SIG] = c_x[l + 1];
@@ -283,17 +307,18 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   const int n_out_per_layer = (int)ceil_div(m.H, OUTR);
   for (auto& lvl : levels)
     for (auto& pr : lvl)
-      if ((pr.t.w[D_OP] == OP_QKV || pr.t.w[D_OP] == OP_ROUTER || pr.t.w[D_OP] == OP_GATEUP) && pr.t.w[D_W0] >= 0)
+      if ((pr.t.w[D_OP] == OP_QKV || pr.t.w[D_OP] == OP_ROUTER || pr.t.w[D_OP] == OP_GATEUP) && pr.t.w[D_W0] >= 0 &&
+          pr.t.w[D_T0] < 0)
         pr.t.w[D_T0] = n_out_per_layer;
   if (m.lm) {
     for (auto [a, e] : even(m.V, W)) {
       Proto pr;
-      set(pr.t, OP_LMHEAD, L, 3 * L);
+      set(pr.t, OP_LMHEAD, L, LPL * L);
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
       pr.t.w[D_W0] = c_x[L]; pr.t.w[D_T0] = n_out_per_layer;
       pr.bytes = (int64_t)(e - a) * m.H * 2;
       pr.prio = 0;
-      levels[3 * L].push_back(pr);
+      levels[LPL * L].push_back(pr);
     }
   }
 
@@ -309,6 +334,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // Each worker's queue is level-ordered, and inside a level its tasks run in priority order
   // (router before QKV, attention before expert slices).
   std::vector<std::vector<std::pair<int, Proto>>> queues(W);   // (level, proto)
+  std::unordered_map<int, int> split_worker;                    // attention split key -> worker
   std::vector<int64_t> total(W, 0), prev(W, 0);
   for (int lv = 0; lv < (int)levels.size(); ++lv) {
     auto& lvl = levels[lv];
@@ -318,6 +344,13 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     std::vector<int64_t> lload(W, 0);
     for (int idx : order) {
       int best = 0;
+      if (lvl[idx].pin >= 0) {                 // attention merge: on the worker of its split
+        best = split_worker.at(lvl[idx].pin);
+        lload[best] += lvl[idx].bytes;
+        total[best] += lvl[idx].bytes;
+        queues[best].push_back({lv, lvl[idx]});
+        continue;
+      }
       for (int w = 1; w < W; ++w) {
         const bool better = lload[w] != lload[best] ? lload[w] < lload[best]
                           : prev[w] != prev[best] ? prev[w] < prev[best]
@@ -327,6 +360,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       lload[best] += lvl[idx].bytes;
       total[best] += lvl[idx].bytes;
       queues[best].push_back({lv, lvl[idx]});
+      if (lvl[idx].pin <= -2) split_worker[-2 - lvl[idx].pin] = best;
     }
     prev = lload;
   }
@@ -361,8 +395,12 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
     if (s >= P.n_ctr || s2 >= P.n_ctr || t.w[D_W0] >= P.n_ctr || t.w[D_W1] >= P.n_ctr) { *why = fmt("task %d: counter index out of range", t.w[D_ID]); return MK_ERR_INVALID_ARG; }
     if (s >= 0) { sig[s]++; prod_level[s] = std::max(prod_level[s], lv); }
     if (s2 >= 0) {
-      auto& v = sig2_groups[s2];
-      if (std::find(v.begin(), v.end(), s) == v.end()) v.push_back(s);
+      if (s < 0) {
+        sig[s2]++;                          // signalled once by this task
+      } else {                              // signalled once by the last arriver of counter s
+        auto& v = sig2_groups[s2];
+        if (std::find(v.begin(), v.end(), s) == v.end()) v.push_back(s);
+      }
       prod_level[s2] = std::max(prod_level[s2], lv);
     }
     if (s == P.done_ctr || s2 == P.done_ctr) { *why = "a task signals the end-of-step counter"; return MK_ERR_INVALID_ARG; }
@@ -377,7 +415,7 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
       if (prod_level[wt[0]] >= t.w[D_LEVEL]) { *why = fmt("task %d (level %d) depends on counter %d produced at level %d", t.w[D_ID], t.w[D_LEVEL], wt[0], prod_level[wt[0]]); return MK_ERR_INVALID_ARG; }
     }
     if (t.w[D_OP] == OP_ROUTER && t.w[D_A2] != sig[t.w[D_SIG]]) { *why = fmt("router task %d expects %d tiles, %d exist", t.w[D_ID], t.w[D_A2], sig[t.w[D_SIG]]); return MK_ERR_INVALID_ARG; }
-    if (t.w[D_OP] == OP_ATTN && (t.w[D_A5] >> 16) != sig[t.w[D_SIG]]) { *why = fmt("attention task %d expects %d splits, %d exist", t.w[D_ID], t.w[D_A5] >> 16, sig[t.w[D_SIG]]); return MK_ERR_INVALID_ARG; }
+    if (t.w[D_OP] == OP_MERGE && t.w[D_A5] != sig[t.w[D_W0]]) { *why = fmt("merge task %d expects %d splits, %d exist", t.w[D_ID], t.w[D_A5], sig[t.w[D_W0]]); return MK_ERR_INVALID_ARG; }
   }
   for (int w = 0; w < P.n_workers; ++w)
     for (int i = P.qoff[w] + 1; i < P.qoff[w + 1]; ++i)
@@ -386,7 +424,7 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
   for (int l = 0; l < m.L; ++l) {
     std::vector<int> qkv(m.QKVR, 0), out(m.H, 0), rt(m.E, 0);
     std::map<int, std::vector<int>> gu;
-    std::map<int, std::vector<std::pair<int, int>>> att;
+    std::map<int, std::vector<std::pair<int, int>>> att, mrg;
     for (auto& t : P.tasks) {
       if (t.w[D_LAYER] != l) continue;
       switch (t.w[D_OP]) {
@@ -400,6 +438,7 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
           break;
         }
         case OP_ATTN: att[t.w[D_A0] * m.HKV + t.w[D_A1]].push_back({t.w[D_A2], t.w[D_A3]}); break;
+        case OP_MERGE: mrg[t.w[D_A0] * m.HKV + t.w[D_A1]].push_back({t.w[D_A2], t.w[D_A3]}); break;
       }
     }
     for (int r = 0; r < m.QKVR; ++r) if (qkv[r] != 1) { *why = fmt("layer %d qkv row %d written %d times", l, r, qkv[r]); return MK_ERR_INVALID_ARG; }
@@ -419,6 +458,11 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
           k = v[i].second;
         }
         if (v.empty()) { *why = fmt("layer %d seq %d group %d: no attention", l, b, g); return MK_ERR_INVALID_ARG; }
+        auto mv = mrg[b * m.HKV + g];
+        std::sort(mv.begin(), mv.end());
+        bool ok = !mv.empty();
+        for (size_t i = 0; ok && i < mv.size(); ++i) ok = mv[i].first == (int)i && mv[i].second == (int)mv.size();
+        if (!ok) { *why = fmt("layer %d seq %d group %d: merge slices do not cover the output once", l, b, g); return MK_ERR_INVALID_ARG; }
       }
   }
   if (m.lm) {
@@ -478,12 +522,10 @@ mk_status simulate_plan(const mk_plan& P, uint64_t seed, int stall_worker, int s
     const Task& t = P.tasks[pos[w]];
     if (t.w[D_SIG] >= 0) {
       const uint32_t old = ctr[t.w[D_SIG]]++;
-      if (t.w[D_SIG2] >= 0) {
-        uint32_t need = 0;
-        if (t.w[D_OP] == OP_ROUTER) need = (uint32_t)t.w[D_A2];
-        if (t.w[D_OP] == OP_ATTN) need = (uint32_t)(t.w[D_A5] >> 16);
-        if (old + 1 == need) ctr[t.w[D_SIG2]]++;
-      }
+      // last arriver of the router tiles publishes the routing table
+      if (t.w[D_SIG2] >= 0 && t.w[D_OP] == OP_ROUTER && old + 1 == (uint32_t)t.w[D_A2]) ctr[t.w[D_SIG2]]++;
+    } else if (t.w[D_SIG2] >= 0) {
+      ctr[t.w[D_SIG2]]++;
     }
     pos[w]++;
     remaining--;
@@ -644,7 +686,7 @@ mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens
   if (wpc < 1) { e->msg = "kernel does not fit on a CU"; return MK_ERR_UNSUPPORTED; }
   mk_plan* P = new mk_plan();
   std::string why;
-  mk_status st = build_plan(e->desc, batch, seq_lens_host, e->n_cu * wpc, e->opt.split_keys, P, &why);
+  mk_status st = build_plan(e->desc, batch, seq_lens_host, e->n_cu * wpc, e->opt.split_keys, P, &why, e->opt.flags);
   if (st == MK_OK) st = validate_plan(*P, &why);
   if (st != MK_OK) { e->msg = "mk_build_schedule: " + why; delete P; return st; }
   // (re)size device buffers that depend on the schedule

@@ -754,14 +754,16 @@ __device__ __forceinline__ bool op_gateup(int task) {
 // Split-KV paged GQA decode attention for one (sequence b, KV group g, key range) with fused RoPE
 // (P3 "Key Technologies and Architecture": restructured paged attention, fused RoPE; P1 "From
 // demo to a full serving system": paged KV, ragged lengths). The split holding the new position
-// writes the new K/V into the cache and scores it in rounded form. The last split of (b, g) to
-// finish merges all partials in split order (log-sum-exp) and publishes the group's output.
+// writes the new K/V into the cache and scores it in fp32 against the rounded key. Each split
+// publishes an unnormalised partial (m, l, o) and bumps its group's arrival counter; merge tasks
+// combine the partials.
 //
-// Scores run on the matrix cores: S = Q K^T per block of 16 keys (one KV page, 4 KB contiguous) is
-// a 16x16x32 bf16 MFMA chain whose A rows are the group's HPG query heads split into bf16 high and
-// low parts (q = hi + lo to 2^-16), so fp32 accuracy is kept while the operand takes 16 registers.
-// Every K of a 256-key chunk is requested before the dependency wait; V of the chunk is requested
-// as soon as the scores are done (the K registers are free then). P V runs on the vector units.
+// Both contractions run on the matrix cores (16x16x32 bf16 MFMA). Scores S = Q K^T per block of
+// 16 keys (one KV page, 4 KB contiguous), the A rows being the group's HPG query heads split into
+// bf16 high and low parts (q = hi + lo to 2^-16), so fp32 accuracy is kept. P V per 32-key block,
+// with P split the same way and V transposed through a per-wave LDS tile. The first 256-key chunk
+// of K and V is requested before the dependency wait.
+
 // LDS layout of an attention task, in floats (every region 16-byte aligned)
 template <class S>
 struct AttnLds {
@@ -788,10 +790,12 @@ __host__ __device__ constexpr int rope_off(int tb) {
   const int att = AttnLds<S>::END;
   const int out = S::AD + S::K * S::F + OUT_MAXR + S::K * OUT_MAXR + 2 * MAXB * OUT_MAXR;
   const int rte = MAXB * S::E * 3 + S::E + 64;
+  const int mrg = MERGE_MAX * 2 * 2 * NWAVE + 2 * NWAVE;
   int m = act;
   if (att > m) m = att;
   if (out > m) m = out;
   if (rte > m) m = rte;
+  if (mrg > m) m = mrg;
   return (m + 63) & ~63;
 }
 
@@ -990,16 +994,33 @@ __device__ __forceinline__ bool op_attn(int task) {
         }
       snew = wsum<32>(t) * rsd;
     }
+    // 256 keys per pass: 8 independent LDS reads per lane (entries past nk are masked; the
+    // buffer has room for them)
     float m = snew;
     if (hv)
-      for (int j = sl; j < nk; j += 32) m = fmaxf(m, prow[j]);
+      for (int j0 = 0; j0 < nk; j0 += 256) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = prow[j0 + 32 * u + sl];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = j0 + 32 * u + sl < nk ? fmaxf(m, v[u]) : m;
+      }
     m = wmax<32>(m);
     float lsum = 0.f;
     if (hv)
-      for (int j = sl; j < nk; j += 32) {
-        const float e = expf(prow[j] - m);
-        prow[j] = e;
-        lsum += e;
+      for (int j0 = 0; j0 < nk; j0 += 256) {
+        float v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = prow[j0 + 32 * u + sl];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int j = j0 + 32 * u + sl;
+          if (j < nk) {
+            const float e = expf(v[u] - m);
+            prow[j] = e;
+            lsum += e;
+          }
+        }
       }
     lsum = wsum<32>(lsum);
     if (hv) {
@@ -1094,7 +1115,7 @@ __device__ __forceinline__ bool op_attn(int task) {
     }
   }
   __syncthreads();
-  // partial: m[HPG], l[HPG], o[HPG][D] (unnormalised)
+  // partial of this split: m[HPG], l[HPG], o[HPG][D] (unnormalised)
   const size_t part = ((size_t)l * p.parts_per_layer + pbase + s_idx) * S::PART;
   const __amdgpu_buffer_rsrc_t Pw = rsrc(p.apart + part);
   for (int i = tx; i < HPG * D; i += NT) {
@@ -1106,81 +1127,86 @@ __device__ __forceinline__ bool op_attn(int task) {
   MARK(4);
   drain();
   MARK(5);
-  const uint32_t old = signal(p, ctl, T.sig, true);
-  MARK(6);
-  if (old + 1 == (uint32_t)nsplit) {
-    // last arriver: merge the nsplit partials of (b, g) in split order (log-sum-exp). Each thread
-    // owns 4 consecutive outputs of the HPG x D block and reads them from MB partials per round
-    // trip (independent 16-byte loads); the first batch is requested together with the m and l of
-    // every split, which go through LDS.
-    constexpr int MB = 32;
-    const __amdgpu_buffer_rsrc_t P0 = rsrc(p.apart + ((size_t)l * p.parts_per_layer + pbase) * S::PART);
-    float* msl = sbuf;          // [nsplit][2 * HPG] m then l; m is overwritten by exp(m - M)
-    float* linv = ml;           // [HPG] sum over splits of l * exp(m - M)
-    if (nsplit > MERGE_MAX) {
-      if (tx == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)MERGE_MAX, (uint32_t)nsplit, (uint32_t)b);
-      return false;
-    }
-    static_assert(HPG * D % 4 == 0 && HPG * D <= 4 * NT, "one float4 of outputs per thread");
-    const int i4 = tx * 4;
-    const bool mine = i4 < HPG * D;
-    f4 ob[MB];
-#pragma unroll
-    for (int u = 0; u < MB; ++u)
-      ob[u] = (mine && u < nsplit) ? ldc4(P0, 4u * (u * S::PART + 2 * HPG + i4)) : f4{0.f, 0.f, 0.f, 0.f};
-    for (int i = tx; i < nsplit * 2 * HPG; i += NT)
-      msl[i] = ldc(P0, 4u * ((i / (2 * HPG)) * S::PART + i % (2 * HPG)));
-    __syncthreads();
-    MARK(7);
-    // per head: M = max over splits of m, scale_s = exp(m_s - M), L = sum_s l_s scale_s; half a
-    // wave per head, lanes over splits
-    static_assert(HPG <= 2 * NWAVE, "");
-    {
-      const int hh = 2 * wave + (lane >> 5), sl = lane & 31;
-      float M = -INFINITY;
-      if (hh < HPG)
-        for (int s2 = sl; s2 < nsplit; s2 += 32) M = fmaxf(M, msl[s2 * 2 * HPG + hh]);
-      M = wmax<32>(M);
-      float Lsum = 0.f;
-      if (hh < HPG)
-        for (int s2 = sl; s2 < nsplit; s2 += 32) {
-          const float ms = msl[s2 * 2 * HPG + hh];
-          const float sc = ms == -INFINITY ? 0.f : expf(ms - M);
-          msl[s2 * 2 * HPG + hh] = sc;
-          Lsum = __builtin_fmaf(msl[s2 * 2 * HPG + HPG + hh], sc, Lsum);
-        }
-      Lsum = wsum<32>(Lsum);
-      if (hh < HPG && sl == 0) linv[hh] = Lsum;
-    }
-    __syncthreads();
-    MARK(8);
-    if (mine) {
-      const int hh = i4 / D;
-      f4 acc = {0.f, 0.f, 0.f, 0.f};
-      for (int s0 = 0; s0 < nsplit; s0 += MB) {
-        if (s0 > 0) {
-#pragma unroll
-          for (int u = 0; u < MB; ++u)
-            ob[u] = (s0 + u < nsplit) ? ldc4(P0, 4u * ((s0 + u) * S::PART + 2 * HPG + i4)) : f4{0.f, 0.f, 0.f, 0.f};
-        }
-#pragma unroll
-        for (int u = 0; u < MB; ++u) {
-          if (s0 + u < nsplit) {
-            const float sc = msl[(s0 + u) * 2 * HPG + hh];
-            acc.x = __builtin_fmaf(ob[u].x, sc, acc.x); acc.y = __builtin_fmaf(ob[u].y, sc, acc.y);
-            acc.z = __builtin_fmaf(ob[u].z, sc, acc.z); acc.w = __builtin_fmaf(ob[u].w, sc, acc.w);
-          }
-        }
-      }
-      const float Lh = linv[hh];
-      const __amdgpu_buffer_rsrc_t A = rsrc(p.attn + ((size_t)l * MAXB + b) * S::AD + g * HPG * D);
-      stc4(A, 4u * i4, f4{acc.x / Lh, acc.y / Lh, acc.z / Lh, acc.w / Lh});
-    }
-    MARK(9);
-    drain();
-    MARK(10);
-    signal(p, ctl, T.sig2, false);
+  signal(p, ctl, T.sig, false);
+  return true;
+}
+
+// One slice of the attention output of (sequence b, KV group g): combine the nsplit partials in
+// split order (log-sum-exp, P3 "Key Technologies and Architecture": split-KV attention). Each
+// (b, g) has `slices` merge tasks over consecutive output ranges, so that the partials are read
+// by several CUs at once; one output per thread, MB partials per round trip.
+template <class S>
+__device__ __forceinline__ bool op_merge(int task) {
+  CParams& p = P();
+  Ctl& ctl = ctl_s;
+  float* sm = smem;
+  const TaskHdr T = read_task(p, task);
+  constexpr int D = S::D, HPG = S::HPG, MB = 32;
+  const int l = T.layer, b = T.a0, g = T.a1, q = T.a2, slices = T.a3, pbase = T.a4, nsplit = T.a5;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  const int ops = (HPG * D) / slices;             // outputs of this slice
+  const int nh = ops / D;                         // heads of this slice (a slice is whole heads)
+  if (slices < 1 || ops * slices != HPG * D || ops % D != 0 || ops > NT || nh > 2 * NWAVE || nsplit > MERGE_MAX) {
+    if (tx == 0) raise_error(p, DEV_STALE, T.id, -1, (uint32_t)slices, (uint32_t)nsplit, (uint32_t)b);
+    return false;
   }
+  const int o0 = q * ops, h0 = o0 / D;            // first output and first head of the slice
+  const __amdgpu_buffer_rsrc_t P0 = rsrc(p.apart + ((size_t)l * p.parts_per_layer + pbase) * S::PART);
+  float* msl = sm;                                // [nsplit][2 nh]: m (then the scale) and l per head
+  float* linv = sm + MERGE_MAX * 2 * 2 * NWAVE;   // [nh] sum over splits of l * scale
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;   // every split of (b, g)
+  const bool mine = tx < ops;
+  const int o = o0 + tx, hh = tx / D;             // this thread's output and its head in the slice
+  float ob[MB];
+#pragma unroll
+  for (int u = 0; u < MB; ++u) ob[u] = (mine && u < nsplit) ? ldc(P0, 4u * (u * S::PART + 2 * HPG + o)) : 0.f;
+  for (int i = tx; i < nsplit * 2 * nh; i += NT) {
+    const int s2 = i / (2 * nh), j = i % (2 * nh);
+    msl[i] = ldc(P0, 4u * (s2 * S::PART + (j < nh ? h0 + j : HPG + h0 + j - nh)));
+  }
+  __syncthreads();
+  MARK(0);
+  // per head: M = max over splits of m, scale_s = exp(m_s - M), L = sum_s l_s scale_s; half a
+  // wave per head, lanes over splits
+  {
+    const int h = 2 * wave + (lane >> 5), sl = lane & 31;
+    float M = -INFINITY;
+    if (h < nh)
+      for (int s2 = sl; s2 < nsplit; s2 += 32) M = fmaxf(M, msl[s2 * 2 * nh + h]);
+    M = wmax<32>(M);
+    float Lsum = 0.f;
+    if (h < nh)
+      for (int s2 = sl; s2 < nsplit; s2 += 32) {
+        const float ms = msl[s2 * 2 * nh + h];
+        const float sc = ms == -INFINITY ? 0.f : expf(ms - M);
+        msl[s2 * 2 * nh + h] = sc;
+        Lsum = __builtin_fmaf(msl[s2 * 2 * nh + nh + h], sc, Lsum);
+      }
+    Lsum = wsum<32>(Lsum);
+    if (h < nh && sl == 0) linv[h] = Lsum;
+  }
+  __syncthreads();
+  MARK(1);
+  if (mine) {
+    float acc = 0.f;
+    for (int s0 = 0; s0 < nsplit; s0 += MB) {
+      if (s0 > 0) {
+#pragma unroll
+        for (int u = 0; u < MB; ++u) ob[u] = (s0 + u < nsplit) ? ldc(P0, 4u * ((s0 + u) * S::PART + 2 * HPG + o)) : 0.f;
+      }
+      float sc[MB];                      // all scales first (independent LDS reads), then the sum
+#pragma unroll
+      for (int u = 0; u < MB; ++u) sc[u] = s0 + u < nsplit ? msl[(s0 + u) * 2 * nh + hh] : 0.f;
+#pragma unroll
+      for (int u = 0; u < MB; ++u) acc = __builtin_fmaf(ob[u], sc[u], acc);
+    }
+    const __amdgpu_buffer_rsrc_t A = rsrc(p.attn + ((size_t)l * MAXB + b) * S::AD + g * HPG * D);
+    stc(A, 4u * o, acc / linv[hh]);
+  }
+  MARK(2);
+  drain();
+  MARK(3);
+  signal(p, ctl, T.sig, false);
   return true;
 }
 
@@ -1398,6 +1424,7 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
       case OP_ATTN: ok = op_attn<S, TB>(ti); break;
       case OP_OUT: ok = op_out<S, TB>(ti); break;
       case OP_LMHEAD: ok = op_lmhead<S, TB>(ti); break;
+      case OP_MERGE: ok = op_merge<S>(ti); break;
       default:
         if (tid() == 0) raise_error(p, DEV_BAD_OP, ti, -1, 0, (uint32_t)op, 0);
         ok = false;

@@ -12,7 +12,7 @@ import json
 
 import numpy as np
 
-OPS = {1: "qkv", 2: "router", 3: "gateup", 4: "attn", 5: "out", 6: "lmhead"}
+OPS = {1: "qkv", 2: "router", 3: "gateup", 4: "attn", 5: "out", 6: "lmhead", 7: "merge"}
 TICK_US = 0.01
 WORDS = 16
 MARKS = WORDS - 4

@@ -73,9 +73,22 @@ def test_plan_structure_full_bs1():
     # output rows of layer l wait on the attention merges of all KV groups of layer l only
     att = tasks[op == 4]
     out = tasks[op == 5]
+    mrg = tasks[op == 7]
     for l in (0, 17, 47):
-        att_sig2 = set(att[att[:, 1] == l][:, 13])
-        assert att_sig2 == set(out[out[:, 1] == l][:, 4])
+        m_l = mrg[mrg[:, 1] == l]
+        assert len(m_l) == 4 * 4 and set(m_l[:, 12]) == set(out[out[:, 1] == l][:, 4])   # 4 slices per group
+        a_l = att[att[:, 1] == l]
+        assert np.all(a_l[:, 13] == -1) and np.all(a_l[:, 10] == -1)  # splits only signal arrival
+        for mt in m_l:                                                # a merge waits for every split of its group
+            grp = a_l[(a_l[:, 2] == mt[2]) & (a_l[:, 3] == mt[3])]
+            assert mt[8] == grp[0, 12] and mt[9] == len(grp) == mt[7] and set(grp[:, 12]) == {mt[8]}
+        assert np.all(out[out[:, 1] == l][:, 5] == 16)                # output rows wait for all 16 slices
+    # a merge runs on a worker that ran one of its group's splits
+    worker = np.repeat(np.arange(512), np.diff(qoff))
+    for i in np.where(op == 7)[0][:64]:
+        t = tasks[i]
+        same = (op == 4) & (tasks[:, 1] == t[1]) & (tasks[:, 2] == t[2]) & (tasks[:, 3] == t[3])
+        assert worker[i] in set(worker[same])
     # attention of group g waits only on the QKV tiles of group g (no false dependency on other groups)
     qkv = tasks[op == 1]
     for g in range(4):
