@@ -1141,7 +1141,7 @@ __device__ __forceinline__ bool op_merge(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int D = S::D, HPG = S::HPG, MB = 32;
+  constexpr int D = S::D, HPG = S::HPG, MB = 64;
   const int l = T.layer, b = T.a0, g = T.a1, q = T.a2, slices = T.a3, pbase = T.a4, nsplit = T.a5;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int ops = (HPG * D) / slices;             // outputs of this slice
