@@ -128,6 +128,14 @@ std::vector<std::pair<int, int>> even(int len, int n) {
   return r;
 }
 
+// Split [0, len) into consecutive ranges of `size` (the last one shorter).
+std::vector<std::pair<int, int>> chunks(int len, int size) {
+  std::vector<std::pair<int, int>> r;
+  size = std::max(1, size);
+  for (int a = 0; a < len; a += size) r.push_back({a, std::min(len, a + size)});
+  return r;
+}
+
 mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, int W, int split_req,
                      mk_plan* P, std::string* why, int flags = 0) {
   const Dims m = dims_of(desc);
@@ -140,15 +148,38 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       return MK_ERR_INVALID_ARG;
     }
   }
-  // attention split length: keep per-(b, g) split counts moderate and tasks ~128 KB of K+V
-  // ~256 keys (128 KB of K+V) per task; long contexts use longer splits so that a (sequence, KV
-  // group) never has more splits than one merge can combine (merge_max()), and the last split keeps
-  // at least a quarter of SPLIT_MAX of room to grow before the schedule must be rebuilt
+  // Tile sizes. Every tile whose output another worker reads writes whole 64-byte sectors (16
+  // floats) that no other tile writes: sectors written in parts by several workers made those
+  // stores take several microseconds to complete under load, on the path of every consumer.
+  const int slots = std::min(m.E, m.K * B);
+  const int align = (m.F % 16 == 0) ? 16 : 1;
+  auto splits_for = [&](int sp) {
+    int n = 0;
+    for (int b = 0; b < B; ++b) n += ((seq_lens[b] - 1) / sp + 1) * m.HKV;
+    return n;
+  };
+  // attention split length: ~256 keys (128 KB of K+V) per task; long contexts use longer splits so
+  // that a (sequence, KV group) never has more splits than one merge can combine (merge_max()), and
+  // the last split keeps at least a quarter of SPLIT_MAX of room to grow before the schedule must
+  // be rebuilt
   int maxlen = *std::max_element(seq_lens, seq_lens + B);
   int split = split_req > 0 ? split_req : 256;
   split = std::max(split, (int)ceil_div(ceil_div(maxlen, merge_max() - 8), 16) * 16);
   split = std::max(16, std::min(split, 3 * SPLITMAX / 4));
   split = (split + 15) / 16 * 16;
+  // level 1 holds the attention splits and the expert slices: size the slices so that the level
+  // has about one task per worker (tasks are latency-bound; a second task on a worker doubles its
+  // part of the level), in whole sectors
+  const int64_t gu_target = std::max<int64_t>(slots, W - splits_for(split));
+  int nf = (int)ceil_div(m.F, std::max<int64_t>(1, gu_target / slots));
+  nf = std::max(4, std::min(64, nf));
+  if (align > 1) nf = std::max(align, (nf + align / 2) / align * align);
+  const int slices = (int)ceil_div(m.F, nf);
+  // if slices and splits then exceed one task per worker, lengthen the splits (up to twice the
+  // default) until they fit
+  if (split_req <= 0)
+    for (int sp = split; sp <= std::min(2 * split, 3 * SPLITMAX / 4); sp += 16)
+      if (splits_for(sp) + slots * slices <= W) { split = sp; break; }
   P->split_keys = split;
 
   Ctrs C;
@@ -184,18 +215,19 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // free for every attention split: those workers reach their split at the start of the layer and
   // its keys stream in while level 0 runs (old keys do not depend on the step's activations).
   const int lvl0_budget = std::max(W / 4, W - parts - router_tiles - 3 * m.HKV);
-  const int qkv_tile = std::max(4, std::min(64, (int)ceil_div(m.QKVR, lvl0_budget)));
-  // level 1 holds the attention splits and the expert slices: size the slices so that the level
-  // has about one task per worker (tasks are latency-bound; a second task per worker doubles it)
-  const int slots = std::min(m.E, m.K * B);
-  const int64_t gu_target = std::max<int64_t>(slots, W - parts);
-  int nf = (int)ceil_div(m.F, std::max<int64_t>(1, gu_target / slots));
-  nf = std::max(4, std::min(64, nf));
-  const int slices = (int)ceil_div(m.F, nf);
+  int qkv_tile = std::max(4, std::min(64, (int)ceil_div(m.QKVR, lvl0_budget)));
+  if (m.D % 16 == 0) qkv_tile = std::min(m.D, (qkv_tile + 15) / 16 * 16);   // whole sectors
 
   // levels per layer: QKV + router | attention splits + expert slices | attention merges | output rows
   constexpr int LPL = 4;
   const int nslice = std::max(1, m.HPG * m.D / 256);       // merge tasks per (sequence, KV group)
+  // output rows: OUT_ROWS per task, except that the workers of the attention merges, which reach
+  // their OUT task only after the merge, get none when the others can take every row in tasks of
+  // at most OUTR rows
+  constexpr int OUT_ROWS = 4;
+  const int n_merge = B * m.HKV * nslice;
+  int n_out_l = (int)ceil_div(m.H, std::min(OUT_ROWS, OUTR));
+  if (W - n_merge >= (int)ceil_div(m.H, OUTR)) n_out_l = std::min(n_out_l, W - n_merge);
   auto split_key = [&](int l, int b, int g, int s) { return ((l * B + b) * m.HKV + g) * 65536 + s; };
   std::vector<std::vector<Proto>> levels(LPL * L + 1);
   int n_attn = 0;
@@ -206,7 +238,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     for (int g = 0; g < m.HKV; ++g) {
       const int regions[3][2] = {{g * m.HPG * m.D, m.HPG * m.D}, {m.HQ * m.D + g * m.D, m.D}, {(m.HQ + m.HKV) * m.D + g * m.D, m.D}};
       for (auto& rg : regions)
-        for (auto [a, e] : even(rg[1], (int)ceil_div(rg[1], qkv_tile))) {
+        for (auto [a, e] : chunks(rg[1], qkv_tile)) {
           Proto pr;
           set(pr.t, OP_QKV, l, lv0);
           pr.t.w[D_A0] = rg[0] + a; pr.t.w[D_A1] = e - a;
@@ -280,9 +312,9 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.pin = split_key(l, b, g, (int)((int64_t)q * nsplit[b] / nslice));
           levels[lvm].push_back(pr);
         }
-    // level 2: output rows (O-proj + expert down-proj + residual)
+    // level 3: output rows (O-proj + expert down-proj + residual)
     int n_out = 0;
-    for (auto [a, e] : even(m.H, (int)ceil_div(m.H, OUTR))) {
+    for (auto [a, e] : even(m.H, n_out_l)) {
       Proto pr;
       set(pr.t, OP_OUT, l, lv2);
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
@@ -304,7 +336,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     }
     (void)n_out;
   }
-  const int n_out_per_layer = (int)ceil_div(m.H, OUTR);
+  const int n_out_per_layer = n_out_l;
   for (auto& lvl : levels)
     for (auto& pr : lvl)
       if ((pr.t.w[D_OP] == OP_QKV || pr.t.w[D_OP] == OP_ROUTER || pr.t.w[D_OP] == OP_GATEUP) && pr.t.w[D_W0] >= 0 &&
@@ -336,16 +368,22 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   std::vector<std::vector<std::pair<int, Proto>>> queues(W);   // (level, proto)
   std::unordered_map<int, int> split_worker;                    // attention split key -> worker
   std::vector<int64_t> total(W, 0), prev(W, 0);
+  std::vector<char> merge_w(W, 0);                              // workers with a merge this layer
+  constexpr int64_t AVOID = (int64_t)1 << 50;
   for (int lv = 0; lv < (int)levels.size(); ++lv) {
     auto& lvl = levels[lv];
     std::vector<int> order(lvl.size());
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return lvl[a].bytes > lvl[b].bytes; });
     std::vector<int64_t> lload(W, 0);
+    const bool out_level = lv < LPL * L && lv % LPL == LPL - 1;
+    if (out_level)
+      for (int w = 0; w < W; ++w) lload[w] = merge_w[w] ? AVOID : 0;
     for (int idx : order) {
       int best = 0;
       if (lvl[idx].pin >= 0) {                 // attention merge: on the worker of its split
         best = split_worker.at(lvl[idx].pin);
+        merge_w[best] = 1;
         lload[best] += lvl[idx].bytes;
         total[best] += lvl[idx].bytes;
         queues[best].push_back({lv, lvl[idx]});
@@ -361,6 +399,10 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       total[best] += lvl[idx].bytes;
       queues[best].push_back({lv, lvl[idx]});
       if (lvl[idx].pin <= -2) split_worker[-2 - lvl[idx].pin] = best;
+    }
+    if (out_level) {
+      for (int w = 0; w < W; ++w) if (merge_w[w]) lload[w] -= AVOID;
+      std::fill(merge_w.begin(), merge_w.end(), 0);
     }
     prev = lload;
   }
@@ -695,11 +737,11 @@ mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens
   const size_t napart = (size_t)e->m.L * P->parts_per_layer * e->m.PART;
   if (ntask > e->task_cap) { if (e->d_tasks) (void)hipFree(e->d_tasks); e->d_tasks = nullptr; HIPCHK(e, dalloc(&e->d_tasks, ntask * DESC_WORDS)); e->task_cap = ntask; }
   if (nq > e->qoff_cap) { if (e->d_qoff) (void)hipFree(e->d_qoff); e->d_qoff = nullptr; HIPCHK(e, dalloc(&e->d_qoff, nq)); e->qoff_cap = nq; }
-  if (nctr > e->ctr_cap) { if (e->d_ctr) (void)hipFree(e->d_ctr); e->d_ctr = nullptr; HIPCHK(e, dalloc(&e->d_ctr, nctr * CTR_STRIDE)); e->ctr_cap = nctr; }
+  if (nctr > e->ctr_cap) { if (e->d_ctr) (void)hipFree(e->d_ctr); e->d_ctr = nullptr; HIPCHK(e, dalloc(&e->d_ctr, (nctr * CTR_SUB + 1) * CTR_STRIDE)); e->ctr_cap = nctr; }
   if (napart > e->apart_floats) { if (e->d_apart) (void)hipFree(e->d_apart); e->d_apart = nullptr; HIPCHK(e, dalloc(&e->d_apart, napart)); e->apart_floats = napart; }
   HIPCHK(e, hipMemcpy(e->d_tasks, P->tasks.data(), ntask * sizeof(Task), hipMemcpyHostToDevice));
   HIPCHK(e, hipMemcpy(e->d_qoff, P->qoff.data(), nq * sizeof(int32_t), hipMemcpyHostToDevice));
-  HIPCHK(e, hipMemset(e->d_ctr, 0, e->ctr_cap * CTR_STRIDE * sizeof(uint32_t)));
+  HIPCHK(e, hipMemset(e->d_ctr, 0, (e->ctr_cap * CTR_SUB + 1) * CTR_STRIDE * sizeof(uint32_t)));
   HIPCHK(e, hipDeviceSynchronize());
   delete e->plan;
   e->plan = P;
@@ -790,7 +832,7 @@ mk_status mk_reset(mk_engine* e) {
   if (!e) return MK_ERR_INVALID_ARG;
   HIPCHK(e, hipDeviceSynchronize());
   HIPCHK(e, hipMemset(e->d_err, 0, sizeof(DevError)));
-  if (e->d_ctr) HIPCHK(e, hipMemset(e->d_ctr, 0, e->ctr_cap * CTR_STRIDE * sizeof(uint32_t)));
+  if (e->d_ctr) HIPCHK(e, hipMemset(e->d_ctr, 0, (e->ctr_cap * CTR_SUB + 1) * CTR_STRIDE * sizeof(uint32_t)));
   HIPCHK(e, hipMemset(e->d_amax, 0, sizeof(unsigned long long) * MAXB));
   HIPCHK(e, hipDeviceSynchronize());
   e->sticky = MK_OK;

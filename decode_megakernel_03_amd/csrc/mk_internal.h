@@ -13,7 +13,8 @@ constexpr int NWAVE = NT / 64;
 constexpr int DESC_WORDS = 16;
 // Dependency counters sit 256 bytes apart, one per cache line, so that the pollers and atomics of
 // different counters never share a line (and, across lines, spread over memory channels).
-constexpr int CTR_STRIDE = 64;
+constexpr int CTR_STRIDE = 64;      // uint32 between sub-counters (one 256-byte line each)
+constexpr int CTR_SUB = 16;         // sub-counters per dependency counter
 // Trace record per task (MK_FLAG_TRACE): id | worker << 32, t_start, t_ready, t_end, marks.
 constexpr int TRACE_WORDS = 16;
 constexpr int TRACE_MARKS = TRACE_WORDS - 4;   // a task descriptor is 16 int32 = 64 bytes
@@ -94,7 +95,7 @@ struct Params {
   float* apart;              // [L][parts_per_layer][HPG * (D + 2)]
   float* attn;               // [L][MAXB][HQ * D]
   unsigned long long* amax;  // [MAXB] packed (ordered logit << 32 | ~index)
-  uint32_t* ctr;             // [n_ctr] dependency counters (zero between steps)
+  uint32_t* ctr;             // [n_ctr][CTR_SUB] + 1 lines of CTR_STRIDE: dependency counters (zero between steps)
   DevError* err;
 
   const int32_t* tasks;      // [n_tasks][16]

@@ -43,7 +43,7 @@ using ShapeFull = Shape<2048, 128, 32, 4, 128, 8, 768>;
 
 constexpr int SPLIT_MAX = 1024;   // keys one attention task may cover (LDS score buffer)
 constexpr int MERGE_MAX = (SPLIT_MAX + 1) / 2;   // splits one (sequence, KV group) may have
-constexpr int OUT_MAXR = 4;       // rows of one OUT task
+constexpr int OUT_MAXR = 5;       // most rows of one OUT task
 constexpr int SC1 = 16;           // buffer cache-policy bit for agent-coherent access
 
 // ------------------------------------------------------------------------------ primitives
@@ -218,32 +218,62 @@ __device__ void raise_error(CParams& p, uint32_t code, int task, int ctr, uint32
   __hip_atomic_store(&p.err->abort_flag, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Block until counter c >= target (thread 0 polls, the workgroup waits at a barrier). Returns false
+// Each dependency counter is CTR_SUB sub-counters on lines of their own: a signal adds to its
+// worker's sub-counter and a wait sums them. Atomics to one address complete one after another
+// (tens of ns each), so a burst of several hundred signals on one line delays the last of them by
+// microseconds; spread over CTR_SUB lines the burst drains CTR_SUB times faster.
+__device__ __forceinline__ uint32_t* ctr_at(CParams& p, int c, int s) {
+  return p.ctr + ((size_t)c * CTR_SUB + s) * CTR_STRIDE;
+}
+
+// Sum of counter c's sub-counters, one load per lane of the calling wave (wave-uniform result).
+__device__ __forceinline__ uint32_t ctr_sum(CParams& p, int c, int lane) {
+  const uint32_t v = lane < CTR_SUB ? ctr_load(ctr_at(p, c, lane)) : 0u;
+  uint32_t s = 0;
+#pragma unroll
+  for (int i = 0; i < CTR_SUB; ++i) s += __builtin_amdgcn_readlane(v, i);
+  return s;
+}
+
+// Block until counter c >= target (wave 0 polls, the workgroup waits at a barrier). Returns false
 // if the step was aborted or this wait exceeded the watchdog (which then aborts the step).
 __device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) {
   if (c < 0) return true;
-  if (tid() == 0) {
+  const int tx = tid(), lane = tx & 63;
+  if (__builtin_amdgcn_readfirstlane(tx >> 6) == 0) {
     int ok = 1;
-    uint32_t v = ctr_load(p.ctr + (size_t)(c) * CTR_STRIDE);
+    const bool tr = p.flags & 1;
+    uint64_t q0 = tr ? now() : 0;
+    uint32_t v = ctr_sum(p, c, lane);
+    if (tr && lane == 0) {   // trace: round trip of the first and of the last poll, and the number of polls
+      const uint64_t q1 = now();
+      ctl.mark[8] = q1 - q0;
+      ctl.mark[10] = q1 - q0;
+      ctl.mark[11] = 1;
+    }
     if (v < target) {
       const uint64_t t0 = now();
       uint32_t it = 0;
       for (;;) {
         __builtin_amdgcn_s_sleep(1);
-        v = ctr_load(p.ctr + (size_t)(c) * CTR_STRIDE);
+        if (tr) q0 = now();
+        v = ctr_sum(p, c, lane);
+        if (tr && lane == 0) { ctl.mark[10] = now() - q0; ctl.mark[11] += 1; }
         if (v >= target) break;
         if ((++it & 15u) == 0) {
-          if (ctr_load(&p.err->abort_flag)) { ok = 0; break; }
+          if (__builtin_amdgcn_readfirstlane(ctr_load(&p.err->abort_flag))) { ok = 0; break; }
           if (now() - t0 > p.watchdog_ticks) {
-            raise_error(p, DEV_TIMEOUT, task, c, target, v, 0);
+            if (lane == 0) raise_error(p, DEV_TIMEOUT, task, c, target, v, 0);
             ok = 0;
             break;
           }
         }
       }
     }
-    ctl.ok = ok;
-    ctl.t_ready = now();
+    if (lane == 0) {
+      ctl.ok = ok;
+      ctl.t_ready = now();
+    }
   }
   __syncthreads();
   const bool ok = ctl.ok != 0;
@@ -253,30 +283,33 @@ __device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) 
 
 // Block until counter c0 >= t0 and counter c1 >= t1, polling both in the same round trip.
 __device__ bool wait_ge2(CParams& p, Ctl& ctl, int c0, uint32_t t0, int c1, uint32_t t1, int task) {
-  if (tid() == 0) {
+  const int tx = tid(), lane = tx & 63;
+  if (__builtin_amdgcn_readfirstlane(tx >> 6) == 0) {
     int ok = 1;
-    uint32_t v0 = c0 >= 0 ? ctr_load(p.ctr + (size_t)(c0) * CTR_STRIDE) : t0, v1 = c1 >= 0 ? ctr_load(p.ctr + (size_t)(c1) * CTR_STRIDE) : t1;
+    uint32_t v0 = c0 >= 0 ? ctr_sum(p, c0, lane) : t0, v1 = c1 >= 0 ? ctr_sum(p, c1, lane) : t1;
     if (v0 < t0 || v1 < t1) {
       const uint64_t ts = now();
       uint32_t it = 0;
       for (;;) {
         __builtin_amdgcn_s_sleep(1);
-        if (c0 >= 0) v0 = ctr_load(p.ctr + (size_t)(c0) * CTR_STRIDE);
-        if (c1 >= 0) v1 = ctr_load(p.ctr + (size_t)(c1) * CTR_STRIDE);
+        if (c0 >= 0) v0 = ctr_sum(p, c0, lane);
+        if (c1 >= 0) v1 = ctr_sum(p, c1, lane);
         if (v0 >= t0 && v1 >= t1) break;
         if ((++it & 15u) == 0) {
-          if (ctr_load(&p.err->abort_flag)) { ok = 0; break; }
+          if (__builtin_amdgcn_readfirstlane(ctr_load(&p.err->abort_flag))) { ok = 0; break; }
           if (now() - ts > p.watchdog_ticks) {
             const bool first = v0 < t0;
-            raise_error(p, DEV_TIMEOUT, task, first ? c0 : c1, first ? t0 : t1, first ? v0 : v1, 0);
+            if (lane == 0) raise_error(p, DEV_TIMEOUT, task, first ? c0 : c1, first ? t0 : t1, first ? v0 : v1, 0);
             ok = 0;
             break;
           }
         }
       }
     }
-    ctl.ok = ok;
-    ctl.t_ready = now();
+    if (lane == 0) {
+      ctl.ok = ok;
+      ctl.t_ready = now();
+    }
   }
   __syncthreads();
   const bool ok = ctl.ok != 0;
@@ -286,12 +319,24 @@ __device__ bool wait_ge2(CParams& p, Ctl& ctl, int c0, uint32_t t0, int c1, uint
 
 // Make this worker's sc1 stores visible, then bump counter c. Returns the counter's old value
 // (meaningful on thread 0 only; broadcast through ctl.flag when `want_old`).
+// drain() that, when tracing, records how long wave 0 waited
+__device__ __forceinline__ void drain_t(CParams& p) {
+  if ((p.flags & 1) && tid() == 0) {
+    const uint64_t d0 = now();
+    drain();
+    ctl_s.mark[9] = now() - d0;
+  }
+  drain();
+}
+
 __device__ uint32_t signal(CParams& p, Ctl& ctl, int c, bool want_old) {
   drain();
   __syncthreads();
   uint32_t old = 0;
   if (tid() == 0 && c >= 0) {
-    old = ctr_add(p.ctr + (size_t)(c) * CTR_STRIDE, 1u);
+    // a signal whose old value is used counts on sub-counter 0 only (all of that counter's
+    // signals do), so that the old value is the number of earlier signals
+    old = ctr_add(ctr_at(p, c, want_old ? 0 : (int)(blockIdx.x % CTR_SUB)), 1u);
     if (want_old) ctl.flag = (int)old;
   }
   if (want_old) {
@@ -498,7 +543,7 @@ __device__ __forceinline__ bool op_qkv(int task) {
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); });
   MARK(1);
-  drain();
+  drain_t(p);
   MARK(2);
   signal(p, ctl, T.sig, false);
   return true;
@@ -745,7 +790,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
       stc(Hb, 4u * ((ctl.toks[t] * K + ctl.trank[t]) * F + f0 + f), hv);
     }
   }
-  drain();
+  MARK(4);
+  drain_t(p);
   MARK(3);
   signal(p, ctl, T.sig, false);
   return true;
@@ -1125,7 +1171,7 @@ __device__ __forceinline__ bool op_attn(int task) {
   }
   if (tx < 2 * HPG) stc(Pw, 4u * tx, ml[tx]);
   MARK(4);
-  drain();
+  drain_t(p);
   MARK(5);
   signal(p, ctl, T.sig, false);
   return true;
@@ -1204,7 +1250,7 @@ __device__ __forceinline__ bool op_merge(int task) {
     stc(A, 4u * o, acc / linv[hh]);
   }
   MARK(2);
-  drain();
+  drain_t(p);
   MARK(3);
   signal(p, ctl, T.sig, false);
   return true;
@@ -1300,7 +1346,7 @@ __device__ __forceinline__ bool op_out(int task) {
     __syncthreads();
   }
   MARK(3);
-  drain();
+  drain_t(p);
   MARK(4);
   signal(p, ctl, T.sig, false);
   return true;
@@ -1375,7 +1421,17 @@ __device__ __forceinline__ bool op_lmhead(int task) {
 __device__ void finish(CParams& p, Ctl& ctl) {
   drain();
   __syncthreads();
-  if (tid() == 0) ctl.flag = (int)(ctr_add(p.ctr + (size_t)(p.done_ctr) * CTR_STRIDE, 1u) == (uint32_t)(p.n_workers - 1));
+  // end-of-step detection in two levels: the last worker of each sub-counter of done_ctr bumps
+  // the line after the last counter; the last of those resets the counters
+  uint32_t* top = p.ctr + (size_t)p.n_ctr * CTR_SUB * CTR_STRIDE;
+  if (tid() == 0) {
+    const int s = (int)(blockIdx.x % CTR_SUB);
+    const uint32_t n_s = (uint32_t)((p.n_workers - s + CTR_SUB - 1) / CTR_SUB);
+    const uint32_t nsub = (uint32_t)(p.n_workers < CTR_SUB ? p.n_workers : CTR_SUB);
+    int last = 0;
+    if (ctr_add(ctr_at(p, p.done_ctr, s), 1u) == n_s - 1) last = ctr_add(top, 1u) == nsub - 1;
+    ctl.flag = last;
+  }
   __syncthreads();
   if (!ctl.flag) return;
   if (tid() < MAXB) {
@@ -1383,11 +1439,12 @@ __device__ void finish(CParams& p, Ctl& ctl) {
     if (p.argmax_out && tid() < p.B) p.argmax_out[tid()] = (int32_t)(0xffffffffu - (uint32_t)key);
     __hip_atomic_store(p.amax + tid(), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  for (int c = tid(); c < p.n_ctr; c += NT)
-    if (c != p.done_ctr) __hip_atomic_store(p.ctr + (size_t)(c) * CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = tid(); i < p.n_ctr * CTR_SUB; i += NT)
+    if (i / CTR_SUB != p.done_ctr) __hip_atomic_store(p.ctr + (size_t)i * CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   drain();
   __syncthreads();
-  if (tid() == 0) __hip_atomic_store(p.ctr + (size_t)(p.done_ctr) * CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid() < CTR_SUB) __hip_atomic_store(ctr_at(p, p.done_ctr, tid()), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid() == 0) __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <class S, int TB>
