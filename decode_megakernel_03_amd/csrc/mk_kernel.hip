@@ -1471,6 +1471,7 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
       ctl_s.t_ready = t_start;
 #pragma unroll
       for (int i = 0; i < TRACE_MARKS; ++i) ctl_s.mark[i] = 0;
+      ctl_s.mark[7] = __builtin_amdgcn_s_memtime();   // shader clock at the start (cycles over the task)
     }
     if (trace) __syncthreads();
     bool ok;
@@ -1493,6 +1494,7 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
       tr[1] = t_start;
       tr[2] = ctl_s.t_ready;
       tr[3] = now();
+      ctl_s.mark[7] = __builtin_amdgcn_s_memtime() - ctl_s.mark[7];
 #pragma unroll
       for (int i = 0; i < TRACE_MARKS; ++i) tr[4 + i] = ctl_s.mark[i];
     }
@@ -1505,9 +1507,12 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
 // ------------------------------------------------------------------------------ host side
 
 template <class S>
-static size_t lds_bytes(int tb) {
-  return ((size_t)rope_off<S>(tb) + MAXB * S::D) * 4;
+constexpr size_t lds_bytes(int tb) {
+  return ((size_t)rope_off<S>(tb) + (size_t)tb * S::D) * 4;   // RoPE table: tb sequences
 }
+// two workers per CU: both workers' LDS (dynamic + the static control block) within 160 KB
+static_assert(2 * (lds_bytes<ShapeFull>(1) + sizeof(Ctl)) <= 160 * 1024, "batch-1 kernel: LDS for two workers per CU");
+static_assert(2 * (lds_bytes<ShapeFull>(MAXB) + sizeof(Ctl)) <= 160 * 1024, "batch-8 kernel: LDS for two workers per CU");
 
 template <class S, int TB>
 static hipError_t launch_one(const Params& p, int grid, hipStream_t st, size_t* lds_out) {

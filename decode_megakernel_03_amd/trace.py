@@ -3,11 +3,12 @@
 Each task record is sixteen uint64: (task id | worker << 32, t_start, t_ready, t_end, mark0..11) in
 100 MHz ticks of the GPU's constant real-time clock: t_ready is when its last dependency wait
 ended, so t_ready - t_start is time spent waiting (with its first weight block already in flight)
-and t_end - t_ready is time spent executing and signalling; marks 0..7 are op-specific phase ends
+and t_end - t_ready is time spent executing and signalling; marks 0..6 are op-specific phase ends
 (attention: query loaded, scores, softmax + PV, partial signalled; expert slice: routing table
-loaded, activations staged, GEMV done), 0 where unset. Words 12..15 are not times but measurements
-of the task's last dependency wait and its store drain: round trip of the first poll, drain
-duration, round trip of the last poll (ticks) and number of polls.
+loaded, activations staged, GEMV done), 0 where unset. Words 11..15 are not times but
+measurements: shader clock cycles over the task, then of the task's last dependency wait and its
+store drain: round trip of the first poll, drain duration, round trip of the last poll (ticks) and
+number of polls.
 """
 
 import json
@@ -18,14 +19,14 @@ OPS = {1: "qkv", 2: "router", 3: "gateup", 4: "attn", 5: "out", 6: "lmhead", 7: 
 TICK_US = 0.01
 WORDS = 16
 MARKS = WORDS - 4
-TIME_MARKS = 8
+TIME_MARKS = 7
 
 
 def decode(trace, tasks):
     """trace uint64 [n_tasks, WORDS]; tasks int32 [n_tasks, 16] (descriptors). Returns a record array."""
     t0 = trace[:, 1].min()
     rec = np.zeros(len(trace), dtype=[("id", "i4"), ("worker", "i4"), ("op", "i4"), ("layer", "i4"),
-                                      ("start", "f8"), ("ready", "f8"), ("end", "f8"), ("mark", "f8", (TIME_MARKS,)),
+                                      ("start", "f8"), ("ready", "f8"), ("end", "f8"), ("mark", "f8", (TIME_MARKS,)), ("cycles", "f8"),
                                       ("poll_first", "f8"), ("drain", "f8"), ("poll_last", "f8"), ("polls", "i4")])
     rec["id"] = (trace[:, 0] & 0xFFFFFFFF).astype(np.int64)
     rec["worker"] = (trace[:, 0] >> 32).astype(np.int64)
@@ -36,10 +37,11 @@ def decode(trace, tasks):
     rec["end"] = (trace[:, 3] - t0) * TICK_US
     marks = trace[:, 4:4 + TIME_MARKS].astype(np.float64)
     rec["mark"] = np.where(marks > 0, (marks - float(t0)) * TICK_US, np.nan)
-    rec["poll_first"] = trace[:, 4 + TIME_MARKS] * TICK_US
-    rec["drain"] = trace[:, 5 + TIME_MARKS] * TICK_US
-    rec["poll_last"] = trace[:, 6 + TIME_MARKS] * TICK_US
-    rec["polls"] = trace[:, 7 + TIME_MARKS].astype(np.int64)
+    rec["cycles"] = trace[:, 4 + TIME_MARKS].astype(np.float64)
+    rec["poll_first"] = trace[:, 5 + TIME_MARKS] * TICK_US
+    rec["drain"] = trace[:, 6 + TIME_MARKS] * TICK_US
+    rec["poll_last"] = trace[:, 7 + TIME_MARKS] * TICK_US
+    rec["polls"] = trace[:, 8 + TIME_MARKS].astype(np.int64)
     return rec
 
 
