@@ -214,7 +214,10 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // level 0 holds QKV tiles and router tiles. Size the QKV tiles so that level 0 leaves a worker
   // free for every attention split: those workers reach their split at the start of the layer and
   // its keys stream in while level 0 runs (old keys do not depend on the step's activations).
-  const int lvl0_budget = std::max(W / 4, W - parts - router_tiles - 3 * m.HKV);
+  // When the splits alone fill the workers (large batches), no worker can be kept free for them
+  // and level 0 spreads over every worker instead.
+  const int lvl0_budget = parts + router_tiles + 3 * m.HKV + W / 4 <= W ? W - parts - router_tiles - 3 * m.HKV
+                                                                       : W - router_tiles;
   int qkv_tile = std::max(4, std::min(64, (int)ceil_div(m.QKVR, lvl0_budget)));
   if (m.D % 16 == 0) qkv_tile = std::min(m.D, (qkv_tile + 15) / 16 * 16);   // whole sectors
 
