@@ -1256,6 +1256,25 @@ __device__ __forceinline__ bool op_merge(int task) {
   return true;
 }
 
+// dst[0, n) = the n floats at byte offset off of R (n a multiple of 4, at most NMAX): every load of
+// the thread is issued before its first LDS write, so the staging costs one round trip
+template <int NMAX>
+__device__ __forceinline__ void stage_f4(float* dst, __amdgpu_buffer_rsrc_t R, uint32_t off, int n) {
+  constexpr int NI = (NMAX + 4 * NT - 1) / (4 * NT);
+  const int tx = tid();
+  f4 v[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int i = (u * NT + tx) * 4;
+    v[u] = i < n ? ldc4(R, off + 4u * i) : f4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int i = (u * NT + tx) * 4;
+    if (i < n) *reinterpret_cast<f4*>(dst + i) = v[u];
+  }
+}
+
 // Output rows row0..row0+nrows of the layer for every token: the fused residual add that rejoins
 // both branches (P1 "One persistent kernel for the whole decode step"):
 //   x_{l+1} = (x_l + W_o attn) + sum_i w_i W_down[e_i] h_i   (experts in ascending index).
@@ -1305,7 +1324,7 @@ __device__ __forceinline__ bool op_out(int task) {
     WBuf<F, NPD> WD;
     load_block<F, NPD>(WD, 0, K * nrows, drow);
     if (b == 0 && !wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every MoE slice
-    for (int i = tid() * 4; i < K * F; i += NT * 4) *reinterpret_cast<f4*>(h_s + i) = ldc4(Hb, 4u * (b * K * F + i));
+    stage_f4<K * F>(h_s, Hb, 4u * (b * K * F), K * F);
     __syncthreads();
     if (b == 0) MARK(0);
     compute_block<F, NPD, 1>(WD, 0, K * nrows, 1, [&](int q, int t) { return h_s + (q / nrows) * F; },
@@ -1331,7 +1350,7 @@ __device__ __forceinline__ bool op_out(int task) {
   MARK(1);
   if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
   for (int b = 0; b < p.B; ++b) {
-    for (int i = tid() * 4; i < AD; i += NT * 4) *reinterpret_cast<f4*>(a_s + i) = ldc4(At, 4u * (b * AD + i));
+    stage_f4<AD>(a_s, At, 4u * (b * AD), AD);
     __syncthreads();
     if (b == 0) MARK(2);
     compute_block<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
