@@ -172,7 +172,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // part of the level), in whole sectors
   const int64_t gu_target = std::max<int64_t>(slots, W - splits_for(split));
   int nf = (int)ceil_div(m.F, std::max<int64_t>(1, gu_target / slots));
-  nf = std::max(4, std::min(64, nf));
+  nf = std::max(4, std::min(32, nf));   // at most 256 KB of gate + up per task (balance at large batches)
   if (align > 1) nf = std::max(align, (nf + align / 2) / align * align);
   const int slices = (int)ceil_div(m.F, nf);
   // if slices and splits then exceed one task per worker, lengthen the splits (up to twice the

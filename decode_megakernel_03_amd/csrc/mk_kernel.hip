@@ -728,9 +728,12 @@ __device__ __forceinline__ bool op_gateup(int task) {
   const int l = T.layer, u = T.a0, f0 = T.a1, nf = T.a2;
   const auto& Lp = cst(p.layers)[l];
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;     // x_l complete
-  if (tid() < MAXB) ctl.toks[tid()] = tid();
-  __syncthreads();
-  stage_norm<S>(p, l, ctl.toks, p.B, Lp.attn_norm, sm, T.id);         // act[b] for every batch row
+  if constexpr (TB == 1) {
+    // one token: normed while the router runs (x_l is in long before the routing)
+    if (tid() < MAXB) ctl.toks[tid()] = tid();
+    __syncthreads();
+    stage_norm<S>(p, l, ctl.toks, p.B, Lp.attn_norm, sm, T.id);       // act[b] for every batch row
+  }
   MARK(0);
   if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;     // every router tile done
   // the routing decision, taken here from the logits with the same selection as the route table
@@ -771,11 +774,14 @@ __device__ __forceinline__ bool op_gateup(int task) {
     WBuf<H, NP> A;
     load_block<H, NP>(A, 0, 2 * nf, rowptr);
     __syncthreads();
-    MARK(1);
     const int ntok = ctl.flag;
-    int brow[TB];       // batch row of the slot's t-th token
+    // several tokens: only the slot's tokens are normed (act[t] for its t-th token), their x rows
+    // requested behind the weights
+    if constexpr (TB > 1) stage_norm<S>(p, l, ctl.toks, ntok, Lp.attn_norm, sm, T.id);
+    MARK(1);
+    int brow[TB];       // act row of the slot's t-th token
 #pragma unroll
-    for (int t = 0; t < TB; ++t) brow[t] = t < ntok ? ctl.toks[t] : 0;
+    for (int t = 0; t < TB; ++t) brow[t] = t < ntok ? (TB == 1 ? ctl.toks[t] : t) : 0;
     float* gu = sm + (size_t)TB * H;                 // [TB][2 nf]
     gemv_stream<H, NP, TB>(A, true, 2 * nf, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)brow[t] * H; },
