@@ -379,7 +379,8 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return lvl[a].bytes > lvl[b].bytes; });
     std::vector<int64_t> lload(W, 0);
-    const bool out_level = lv < LPL * L && lv % LPL == LPL - 1;
+    // output rows avoid the merge workers only when the others can take one output task each
+    const bool out_level = lv < LPL * L && lv % LPL == LPL - 1 && W - n_merge >= n_out_l;
     if (out_level)
       for (int w = 0; w < W; ++w) lload[w] = merge_w[w] ? AVOID : 0;
     for (int idx : order) {
