@@ -49,6 +49,7 @@ def parse():
     ap.add_argument("--workers-per-cu", type=int, default=0)
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--no-b8", action="store_true", help="with the default workload, skip the batch-8 line in the JSON")
     ap.add_argument("--trace", default="", help="after timing, trace one step and write a summary + Chrome JSON here")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
@@ -86,77 +87,12 @@ def main():
         over["context"] = args.context
     wl = synth.workload(args.workload, **over)
     B = wl.batch
-    total_steps = args.warmup + args.steps
-    dev = "cuda"
-    t0 = time.time()
-    log(f"[bench] generating {wl.name}: {wl.n_layers} layers, batch {B}, context {wl.context} on the GPU")
-    bias = synth.zipf_router_bias(wl) if wl.zipf_s else None
-    w = synth.make_weights(wl, seed=0, device=dev, router_bias=bias)
-    ctx = synth.context_lengths(wl)
-    bt_np, num_pages = synth.make_block_tables(ctx, total_steps + 1, wl.page_size)
-    k, v = synth.make_kv(wl, num_pages, device=dev)
-    torch.cuda.synchronize()
-    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; KV pages {num_pages}")
-
     want_cpu = not args.no_cpu_baseline
-    kv_host0 = None
-    if want_cpu:
-        from tests import harness
-        kv_host0 = harness.host_kv(k, v)            # KV state before the first step (oracle input)
-
-    eng = mk.Engine(wl, w, k, v, num_pages, bt_np.shape[1], max_batch=B)
-    eng.set_options(workers_per_cu=args.workers_per_cu, split_keys=args.split_keys, flags=args.flags)
-    eng.build_schedule((ctx + 1).tolist())
-    info = eng.plan_info()
-    log(f"[bench] schedule: {info.n_tasks} tasks on {info.n_workers} workers, {info.n_attn_splits} attention splits")
-
-    # per-step inputs precomputed on the device: positions / lengths advance by one each step and the
-    # token buffer doubles as the argmax output, so the timed loop is nothing but kernel launches
-    pos_all = torch.from_numpy((ctx[None, :] + np.arange(total_steps)[:, None]).astype(np.int32)).to(dev)
-    len_all = pos_all + 1
-    bt = torch.from_numpy(bt_np).to(dev)
-    tokens = torch.from_numpy(synth.first_tokens(wl)).to(dev)
-    tok0 = tokens.clone()
-    topk = torch.zeros(total_steps, wl.n_layers, B, wl.top_k, dtype=torch.int32, device=dev)
-    logits = torch.empty(B, wl.vocab, dtype=torch.float32, device=dev)
-    logits0 = None
-    stream = torch.cuda.current_stream()
-    h = stream.cuda_stream
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
-    for s in range(total_steps):
-        mk.mk_set_step_outputs(eng.h, argmax_out=tokens, topk_out=topk[s])
-        if s == args.warmup:
-            torch.cuda.synchronize()
-            log(f"[bench] warmup done ({args.warmup} steps); timing {args.steps} steps")
-            t_wall = time.perf_counter()
-        starts[s].record(stream)
-        st = mk.mk_decode_step(eng.h, tokens, pos_all[s], bt, len_all[s], logits, h)
-        ends[s].record(stream)
-        if st != mk.MK_OK:
-            raise mk.MkError(st, mk.mk_get_error(eng.h)[1])
-        if s == 0:
-            torch.cuda.synchronize()
-            eng.sync()
-            logits0 = logits.cpu().numpy().copy()
-            log("[bench] step 0 ok")
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_wall
-    eng.sync()
-    step_ms = np.array([starts[s].elapsed_time(ends[s]) for s in range(args.warmup, total_steps)])
-    # timed region: first start event to last end event (includes launch gaps)
-    span_ms = starts[args.warmup].elapsed_time(ends[total_steps - 1])
-    topk_h = topk.cpu().numpy()
-    union = np.array([[len(np.unique(topk_h[s, l])) for l in range(wl.n_layers)] for s in range(total_steps)])
-    step_bytes = np.array([metrics.step_bytes(wl, union[s], ctx + 1 + s) for s in range(total_steps)])
-    timed_bytes = step_bytes[args.warmup:]
-    tok_s = B * args.steps / (span_ms / 1e3)
-    achieved = float(np.mean(timed_bytes / (step_ms / 1e3)))      # per launch: bytes / kernel duration
-    sol_frac = float(np.sum(timed_bytes) / (span_ms / 1e3) / PEAK_HBM)
-    log(f"[bench] {args.steps} steps: mean {step_ms.mean():.3f} ms, median {np.median(step_ms):.3f} ms, span {span_ms:.1f} ms, "
-        f"wall {wall * 1e3:.1f} ms -> {tok_s:.1f} tok/s; {timed_bytes.mean() / 1e9:.3f} GB/step; "
-        f"{achieved / 1e9:.0f} GB/s per launch ({achieved / PEAK_HBM:.1%} of 8 TB/s)")
-
+    r = measure(wl, args, args.steps, args.warmup, keep_kv_host=want_cpu)
+    eng, info, ctx, bt_np, w = r["eng"], r["info"], r["ctx"], r["bt_np"], r["w"]
+    step_ms, span_ms, tok_s, achieved, sol_frac = r["step_ms"], r["span_ms"], r["tok_s"], r["achieved"], r["sol_frac"]
+    timed_bytes, union, topk_h, logits0, tok0, kv_host0 = r["timed_bytes"], r["union"], r["topk_h"], r["logits0"], r["tok0"], r["kv_host0"]
+    tokens, pos_all, bt, len_all, logits, h, total_steps = r["loop"]
     if args.trace:
         run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps)
 
@@ -198,8 +134,102 @@ def main():
         "cpu_baseline": cpu,
         "parity_first_step": parity,
     }
-    print(json.dumps(out), flush=True)
     eng.close()
+    # the metric is quoted at batch 1 and batch 8: the batch-8 figure of the same model and context
+    # joins the line (its own engine, inputs and timing; value above stays the batch-1 workload)
+    if args.workload == "full" and args.batch in (0, 1) and not args.no_b8:
+        del r, w
+        torch.cuda.empty_cache()
+        wl8 = synth.workload("full_b8")
+        r8 = measure(wl8, args, 16, 4)
+        r8["eng"].close()
+        out["bs8"] = {"workload": f"{wl8.name}: batch 8, context {int(r8['ctx'].max())} each",
+                      "value": round(r8["tok_s"], 2), "unit": "tok/s", "steps": 16, "warmup": 4,
+                      "ms_per_step": round(r8["span_ms"] / 16, 4), "sol_fraction": round(r8["sol_frac"], 4),
+                      "bytes_per_step": int(r8["timed_bytes"].mean()),
+                      "experts_union_mean": round(float(r8["union"][4:].mean()), 2),
+                      "roofline_frac": round(r8["achieved"] / PEAK_HBM, 4)}
+    print(json.dumps(out), flush=True)
+
+
+def measure(wl, args, steps, warmup, keep_kv_host=False):
+    """Synthetic inputs of workload wl on the GPU, an engine and its schedule, then `warmup` untimed
+    and `steps` timed decode steps (HIP events on the launch stream around every step)."""
+    import torch
+    from decode_megakernel_03_amd import metrics, mk, synth
+    B = wl.batch
+    total_steps = warmup + steps
+    dev = "cuda"
+    t0 = time.time()
+    log(f"[bench] generating {wl.name}: {wl.n_layers} layers, batch {B}, context {wl.context} on the GPU")
+    bias = synth.zipf_router_bias(wl) if wl.zipf_s else None
+    w = synth.make_weights(wl, seed=0, device=dev, router_bias=bias)
+    ctx = synth.context_lengths(wl)
+    bt_np, num_pages = synth.make_block_tables(ctx, total_steps + 1, wl.page_size)
+    k, v = synth.make_kv(wl, num_pages, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs ready in {time.time() - t0:.1f}s; KV pages {num_pages}")
+    kv_host0 = None
+    if keep_kv_host:
+        from tests import harness
+        kv_host0 = harness.host_kv(k, v)            # KV state before the first step (oracle input)
+
+    eng = mk.Engine(wl, w, k, v, num_pages, bt_np.shape[1], max_batch=B)
+    eng.set_options(workers_per_cu=args.workers_per_cu, split_keys=args.split_keys, flags=args.flags)
+    eng.build_schedule((ctx + 1).tolist())
+    info = eng.plan_info()
+    log(f"[bench] schedule: {info.n_tasks} tasks on {info.n_workers} workers, {info.n_attn_splits} attention splits")
+
+    # per-step inputs precomputed on the device: positions / lengths advance by one each step and the
+    # token buffer doubles as the argmax output, so the timed loop is nothing but kernel launches
+    pos_all = torch.from_numpy((ctx[None, :] + np.arange(total_steps)[:, None]).astype(np.int32)).to(dev)
+    len_all = pos_all + 1
+    bt = torch.from_numpy(bt_np).to(dev)
+    tokens = torch.from_numpy(synth.first_tokens(wl)).to(dev)
+    tok0 = tokens.clone()
+    topk = torch.zeros(total_steps, wl.n_layers, B, wl.top_k, dtype=torch.int32, device=dev)
+    logits = torch.empty(B, wl.vocab, dtype=torch.float32, device=dev)
+    logits0 = None
+    stream = torch.cuda.current_stream()
+    h = stream.cuda_stream
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
+    for s in range(total_steps):
+        mk.mk_set_step_outputs(eng.h, argmax_out=tokens, topk_out=topk[s])
+        if s == warmup:
+            torch.cuda.synchronize()
+            log(f"[bench] warmup done ({warmup} steps); timing {steps} steps")
+            t_wall = time.perf_counter()
+        starts[s].record(stream)
+        st = mk.mk_decode_step(eng.h, tokens, pos_all[s], bt, len_all[s], logits, h)
+        ends[s].record(stream)
+        if st != mk.MK_OK:
+            raise mk.MkError(st, mk.mk_get_error(eng.h)[1])
+        if s == 0:
+            torch.cuda.synchronize()
+            eng.sync()
+            logits0 = logits.cpu().numpy().copy()
+            log("[bench] step 0 ok")
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_wall
+    eng.sync()
+    step_ms = np.array([starts[s].elapsed_time(ends[s]) for s in range(warmup, total_steps)])
+    # timed region: first start event to last end event (includes launch gaps)
+    span_ms = starts[warmup].elapsed_time(ends[total_steps - 1])
+    topk_h = topk.cpu().numpy()
+    union = np.array([[len(np.unique(topk_h[s, l])) for l in range(wl.n_layers)] for s in range(total_steps)])
+    step_bytes = np.array([metrics.step_bytes(wl, union[s], ctx + 1 + s) for s in range(total_steps)])
+    timed_bytes = step_bytes[warmup:]
+    tok_s = B * steps / (span_ms / 1e3)
+    achieved = float(np.mean(timed_bytes / (step_ms / 1e3)))      # per launch: bytes / kernel duration
+    sol_frac = float(np.sum(timed_bytes) / (span_ms / 1e3) / PEAK_HBM)
+    log(f"[bench] {wl.name}: {steps} steps: mean {step_ms.mean():.3f} ms, median {np.median(step_ms):.3f} ms, "
+        f"span {span_ms:.1f} ms, wall {wall * 1e3:.1f} ms -> {tok_s:.1f} tok/s; {timed_bytes.mean() / 1e9:.3f} GB/step; "
+        f"{achieved / 1e9:.0f} GB/s per launch ({achieved / PEAK_HBM:.1%} of 8 TB/s)")
+    return {"eng": eng, "info": info, "ctx": ctx, "bt_np": bt_np, "w": w, "step_ms": step_ms, "span_ms": span_ms,
+            "tok_s": tok_s, "achieved": achieved, "sol_frac": sol_frac, "timed_bytes": timed_bytes, "union": union,
+            "topk_h": topk_h, "logits0": logits0, "tok0": tok0, "kv_host0": kv_host0,
+            "loop": (tokens, pos_all, bt, len_all, logits, h, total_steps)}
 
 
 def run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps):
