@@ -187,9 +187,14 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   std::vector<int> c_x(L + 1, -1), c_rarr(L), c_route(L), c_h(L), c_att(L);
   std::vector<std::vector<int>> c_qkv(L, std::vector<int>(m.HKV));
   std::vector<std::vector<int>> c_aarr(L, std::vector<int>(B * m.HKV));
+  // expert slices drawn from a per-layer queue (dynamic work stealing) unless static slices are
+  // asked for; the queue is a counter of its own (zeroed with the others at the end of a step)
+  const bool steal = !(flags & MK_FLAG_STATIC_EXPERTS);
+  std::vector<int> c_queue(L, -1);
   for (int l = 0; l < L; ++l) {
     for (int g = 0; g < m.HKV; ++g) c_qkv[l][g] = C.alloc();
     c_rarr[l] = C.alloc(); c_route[l] = C.alloc(); c_h[l] = C.alloc(); c_att[l] = C.alloc();
+    if (steal) c_queue[l] = C.alloc();
     for (int i = 0; i < B * m.HKV; ++i) c_aarr[l][i] = C.alloc();
     c_x[l + 1] = C.alloc();
   }
@@ -285,20 +290,41 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           n_attn++;
         }
     int n_gu = 0;
-    for (int u = 0; u < slots; ++u)
-      for (int j = 0; j < slices; ++j) {
+    if (steal) {
+      // one task per worker at most: each draws (slot, slice) items until the queue is empty, so
+      // the routing-dependent expert work goes to whichever workers are free first
+      const int n_items = slots * slices;
+      const int tickets = std::min(n_items, W);
+      const int nq = std::min(CTR_SUB, tickets);
+      for (int t = 0; t < tickets; ++t) {
         Proto pr;
         set(pr.t, OP_GATEUP, l, lv1);
-        const int f0 = j * nf, f1 = std::min(m.F, f0 + nf);
-        pr.t.w[D_A0] = u; pr.t.w[D_A1] = f0; pr.t.w[D_A2] = f1 - f0;
+        pr.t.w[D_A0] = t % nq; pr.t.w[D_A1] = nq; pr.t.w[D_A2] = slices; pr.t.w[D_A3] = c_queue[l];
+        pr.t.w[D_A4] = nf;
         pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
         pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
         pr.t.w[D_SIG] = c_h[l];
-        pr.bytes = (int64_t)2 * (f1 - f0) * m.H * 2;
+        pr.bytes = (int64_t)n_items * 2 * nf * m.H * 2 / tickets;
         pr.prio = 1;
         levels[lv1].push_back(pr);
         n_gu++;
       }
+    } else {
+      for (int u = 0; u < slots; ++u)
+        for (int j = 0; j < slices; ++j) {
+          Proto pr;
+          set(pr.t, OP_GATEUP, l, lv1);
+          const int f0 = j * nf, f1 = std::min(m.F, f0 + nf);
+          pr.t.w[D_A0] = u; pr.t.w[D_A1] = f0; pr.t.w[D_A2] = f1 - f0; pr.t.w[D_A3] = -1;
+          pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
+          pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
+          pr.t.w[D_SIG] = c_h[l];
+          pr.bytes = (int64_t)2 * (f1 - f0) * m.H * 2;
+          pr.prio = 1;
+          levels[lv1].push_back(pr);
+          n_gu++;
+        }
+    }
     // level 2: attention merges, nslice per (sequence, KV group), each on the worker of one of the
     // group's splits (that worker is done with the step's heavy streams by then)
     for (int b = 0; b < B; ++b)
@@ -471,6 +497,7 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
     std::vector<int> qkv(m.QKVR, 0), out(m.H, 0), rt(m.E, 0);
     std::map<int, std::vector<int>> gu;
     std::map<int, std::vector<std::pair<int, int>>> att, mrg;
+    std::vector<const Task*> queue_tasks;
     for (auto& t : P.tasks) {
       if (t.w[D_LAYER] != l) continue;
       switch (t.w[D_OP]) {
@@ -478,6 +505,7 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
         case OP_ROUTER: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) rt[r]++; break;
         case OP_OUT: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) out[r]++; break;
         case OP_GATEUP: {
+          if (t.w[D_A3] >= 0) { queue_tasks.push_back(&t); break; }
           auto& v = gu[t.w[D_A0]];
           v.resize(m.F, 0);
           for (int f = t.w[D_A1]; f < t.w[D_A1] + t.w[D_A2]; ++f) v[f]++;
@@ -490,7 +518,31 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
     for (int r = 0; r < m.QKVR; ++r) if (qkv[r] != 1) { *why = fmt("layer %d qkv row %d written %d times", l, r, qkv[r]); return MK_ERR_INVALID_ARG; }
     for (int r = 0; r < m.E; ++r) if (rt[r] != 1) { *why = fmt("layer %d router row %d written %d times", l, r, rt[r]); return MK_ERR_INVALID_ARG; }
     for (int r = 0; r < m.H; ++r) if (out[r] != 1) { *why = fmt("layer %d output row %d written %d times", l, r, out[r]); return MK_ERR_INVALID_ARG; }
-    if ((int)gu.size() != std::min(m.E, m.K * P.B)) { *why = fmt("layer %d: %zu expert slots", l, gu.size()); return MK_ERR_INVALID_ARG; }
+    if (!queue_tasks.empty()) {
+      // queue mode: one queue counter per layer that no task waits on or signals; its items cover
+      // every FFN row of every union slot once; every sub-queue has a task that drains it
+      if (!gu.empty()) { *why = fmt("layer %d mixes static and queued expert slices", l); return MK_ERR_INVALID_ARG; }
+      const Task& t0 = *queue_tasks[0];
+      const int qc = t0.w[D_A3], nq = t0.w[D_A1], slices = t0.w[D_A2], nfs = t0.w[D_A4];
+      if (qc >= P.n_ctr || nq < 1 || nq > CTR_SUB || slices < 1 || nfs < 1 || slices * nfs < m.F || (slices - 1) * nfs >= m.F) {
+        *why = fmt("layer %d: bad expert queue (counter %d, %d sub-queues, %d slices of %d rows)", l, qc, nq, slices, nfs);
+        return MK_ERR_INVALID_ARG;
+      }
+      std::vector<int> drained(nq, 0);
+      for (const Task* t : queue_tasks) {
+        if (t->w[D_A3] != qc || t->w[D_A1] != nq || t->w[D_A2] != slices || t->w[D_A4] != nfs || t->w[D_A0] < 0 || t->w[D_A0] >= nq) {
+          *why = fmt("layer %d: expert task %d disagrees on the queue", l, t->w[D_ID]);
+          return MK_ERR_INVALID_ARG;
+        }
+        drained[t->w[D_A0]]++;
+      }
+      for (int q = 0; q < nq; ++q) if (!drained[q]) { *why = fmt("layer %d: expert sub-queue %d has no task", l, q); return MK_ERR_INVALID_ARG; }
+      for (auto& t : P.tasks) {
+        const bool uses = t.w[D_W0] == qc || t.w[D_W1] == qc || t.w[D_SIG] == qc || t.w[D_SIG2] == qc ||
+                          (t.w[D_OP] == OP_OUT && t.w[D_A2] == qc);
+        if (uses) { *why = fmt("task %d waits on or signals the expert queue counter %d", t.w[D_ID], qc); return MK_ERR_INVALID_ARG; }
+      }
+    } else if ((int)gu.size() != std::min(m.E, m.K * P.B)) { *why = fmt("layer %d: %zu expert slots", l, gu.size()); return MK_ERR_INVALID_ARG; }
     for (auto& [u, v] : gu) for (int f = 0; f < m.F; ++f) if (v[f] != 1) { *why = fmt("layer %d slot %d ffn row %d written %d times", l, u, f, v[f]); return MK_ERR_INVALID_ARG; }
     for (int b = 0; b < P.B; ++b)
       for (int g = 0; g < m.HKV; ++g) {
@@ -855,7 +907,7 @@ void mk_destroy(mk_engine* e) {
 // ---- host-only schedule API ---------------------------------------------------------------
 
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* seq_lens_host, int32_t n_workers,
-                        int32_t split_keys, mk_plan** out) {
+                        int32_t split_keys, uint32_t flags, mk_plan** out) {
   std::string why;
   if (!out) return MK_ERR_INVALID_ARG;
   *out = nullptr;
@@ -863,7 +915,7 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   if (st != MK_OK) { fprintf(stderr, "mk_plan_build: %s\n", why.c_str()); return st; }
   if (!seq_lens_host || batch < 1 || batch > desc->max_batch || n_workers < 1 || split_keys < 0) return MK_ERR_INVALID_ARG;
   mk_plan* P = new mk_plan();
-  st = build_plan(*desc, batch, seq_lens_host, n_workers, split_keys, P, &why);
+  st = build_plan(*desc, batch, seq_lens_host, n_workers, split_keys, P, &why, (int)flags);
   if (st != MK_OK) { fprintf(stderr, "mk_plan_build: %s\n", why.c_str()); delete P; return st; }
   *out = P;
   return MK_OK;

@@ -44,6 +44,7 @@ using ShapeFull = Shape<2048, 128, 32, 4, 128, 8, 768>;
 constexpr int SPLIT_MAX = 1024;   // keys one attention task may cover (LDS score buffer)
 constexpr int MERGE_MAX = (SPLIT_MAX + 1) / 2;   // splits one (sequence, KV group) may have
 constexpr int OUT_MAXR = 5;       // most rows of one OUT task
+constexpr int STEAL_PROBES = 4;   // sub-queues an expert task draws from (its own, then 3 more)
 constexpr int SC1 = 16;           // buffer cache-policy bit for agent-coherent access
 
 // ------------------------------------------------------------------------------ primitives
@@ -182,6 +183,9 @@ __device__ __forceinline__ float wmax(float v) {
 struct Ctl {            // small per-worker control block in static LDS
   int ok;
   int flag;
+  int item;             // expert-queue draw broadcast to the workgroup
+  int steal;            // sub-queue to steal from next (-1: none had items left)
+  int norm_l;           // layer whose normed input the expert-slice staging area holds (-1: none)
   unsigned long long t_ready;   // when the task's last dependency wait ended (trace)
   unsigned long long mark[TRACE_MARKS];   // op-specific phase ends (trace)
   int toks[MAXB];       // batch rows of the tokens a task works on
@@ -423,7 +427,42 @@ __device__ __forceinline__ void compute_block(const WBuf<KD, NP>& b, int blk, in
   }
 }
 
+// compute_block for activations that do not depend on the row (every GEMV whose rows share one
+// input vector per token): each 16-byte activation read from LDS serves all NP passes of the block,
+// so a batch of TB tokens reads LDS NP times less. Per row, the products are summed in the same
+// order as compute_block.
+template <int KD, int NP, int TB, class ActOf, class Emit>
+__device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int blk, int nrows, int ntok,
+                                                     ActOf act_of, Emit emit) {
+  using G = Geo<KD>;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  const int rip = lane / G::LPR, lir = lane % G::LPR;
+#pragma unroll
+  for (int t = 0; t < TB; ++t) {
+    if (t < ntok) {
+      const float* a = act_of(0, t) + 8 * lir;
+      float acc[NP];
+#pragma unroll
+      for (int i = 0; i < NP; ++i) acc[i] = 0.f;
+#pragma unroll
+      for (int j = 0; j < G::CPL; ++j) {
+        const f4* ap = reinterpret_cast<const f4*>(a + 8 * G::LPR * j);
+        const f4 a0 = ap[0], a1 = ap[1];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) acc[i] = dot8(b.w[i][j], a0, a1, acc[i]);
+      }
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
+        const float v = wsum<G::LPR>(acc[i]);
+        if (lir == 0 && r < nrows) emit(r, t, v);
+      }
+    }
+  }
+}
+
 // Stream `nrows` rows; block 0 may already be loaded into A (prefetched before a dependency wait).
+// The activations are shared by all rows (ActOf ignores its row argument).
 template <int KD, int NP, int TB, class RowPtr, class ActOf, class Emit>
 __device__ __forceinline__ void gemv_stream(WBuf<KD, NP>& A, bool a_loaded, int nrows, int ntok,
                                             RowPtr rowptr, ActOf act_of, Emit emit) {
@@ -432,10 +471,10 @@ __device__ __forceinline__ void gemv_stream(WBuf<KD, NP>& A, bool a_loaded, int 
   if (!a_loaded) load_block<KD, NP>(A, 0, nrows, rowptr);
   for (int blk = 0; blk < nblk; blk += 2) {
     if (blk + 1 < nblk) load_block<KD, NP>(B, blk + 1, nrows, rowptr);
-    compute_block<KD, NP, TB>(A, blk, nrows, ntok, act_of, emit);
+    compute_block_shared<KD, NP, TB>(A, blk, nrows, ntok, act_of, emit);
     if (blk + 1 < nblk) {
       if (blk + 2 < nblk) load_block<KD, NP>(A, blk + 2, nrows, rowptr);
-      compute_block<KD, NP, TB>(B, blk + 1, nrows, ntok, act_of, emit);
+      compute_block_shared<KD, NP, TB>(B, blk + 1, nrows, ntok, act_of, emit);
     }
   }
 }
@@ -725,20 +764,40 @@ __device__ __forceinline__ bool op_gateup(int task) {
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
   constexpr int H = S::H, F = S::F, K = S::K, NP = (Geo<H>::CPL >= 4) ? 2 : 4;
-  const int l = T.layer, u = T.a0, f0 = T.a1, nf = T.a2;
+  const int l = T.layer;
   const auto& Lp = cst(p.layers)[l];
-  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;     // x_l complete
-  if constexpr (TB == 1) {
-    // one token: normed while the router runs (x_l is in long before the routing)
+  // Queue mode (a3 >= 0, P3 "Scheduling and Performance Benchmarks": dynamic work stealing): the
+  // items (union slot u, FFN slice j) of the layer are drawn from counter a3, whose sub-counter q
+  // hands out the items q, q + nq, q + 2 nq, ... (a0 = own sub-queue, a1 = nq, a2 = slices per
+  // slot, a4 = rows per slice). The task draws from its own sub-queue until it is exhausted, then
+  // steals from the next ones. The first draw is issued before the dependency waits.
+  const bool dyn = T.a3 >= 0;
+  const int nq = dyn ? T.a1 : 1;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  int sq = dyn ? T.a0 : 0;
+  // a draw: lane 0 of wave 0 takes the next item of sub-queue q; lanes < nq read every sub-queue's
+  // head at the same time (a snapshot: heads only grow, so a sub-queue it shows exhausted stays so)
+  uint32_t kreq = 0, head = 0xffffffffu;
+  auto draw = [&](int q) {
+    if (wave == 0) {
+      if (lane == 0) kreq = ctr_add(ctr_at(p, T.a3, q), 1u);
+      head = lane < nq ? ctr_load(ctr_at(p, T.a3, lane)) : 0xffffffffu;
+    }
+  };
+  if (dyn) draw(sq);
+  // the normed input of every token: staged once per worker and layer (consecutive expert tasks
+  // of one layer on a worker reuse it), before the routing decision is awaited
+  if (ctl.norm_l != l) {
+    if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;     // x_l complete
     if (tid() < MAXB) ctl.toks[tid()] = tid();
     __syncthreads();
     stage_norm<S>(p, l, ctl.toks, p.B, Lp.attn_norm, sm, T.id);       // act[b] for every batch row
+    if (tid() == 0) ctl.norm_l = l;
   }
   MARK(0);
   if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;     // every router tile done
   // the routing decision, taken here from the logits with the same selection as the route table
   // (no further hop through the router's last tile): each wave selects for its tokens
-  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   for (int b = wave; b < p.B; b += NWAVE) {
     int widx[K];
     float wval[K];
@@ -750,8 +809,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
   unsigned long long u0 = 0, u1 = 0;
   for (int b = 0; b < p.B; ++b) { u0 |= ctl.mask[b][0]; u1 |= ctl.mask[b][1]; }
   const int n0 = __builtin_popcountll(u0), nu = n0 + __builtin_popcountll(u1);
-  if (u < nu) {
-    // expert of union slot u (the u-th selected expert in ascending order) and its tokens
+  // rows f0..f0+nf of union slot u (the u-th selected expert in ascending order) for its tokens
+  auto run_item = [&](int u, int f0, int nf) {
     unsigned long long m = u < n0 ? u0 : u1;
     for (int j = u < n0 ? u : u - n0; j > 0; --j) m &= m - 1;
     const int e = (u < n0 ? 0 : 64) + __builtin_ctzll(m);
@@ -775,13 +834,10 @@ __device__ __forceinline__ bool op_gateup(int task) {
     load_block<H, NP>(A, 0, 2 * nf, rowptr);
     __syncthreads();
     const int ntok = ctl.flag;
-    // several tokens: only the slot's tokens are normed (act[t] for its t-th token), their x rows
-    // requested behind the weights
-    if constexpr (TB > 1) stage_norm<S>(p, l, ctl.toks, ntok, Lp.attn_norm, sm, T.id);
     MARK(1);
-    int brow[TB];       // act row of the slot's t-th token
+    int brow[TB];       // act row (batch row) of the slot's t-th token
 #pragma unroll
-    for (int t = 0; t < TB; ++t) brow[t] = t < ntok ? (TB == 1 ? ctl.toks[t] : t) : 0;
+    for (int t = 0; t < TB; ++t) brow[t] = t < ntok ? ctl.toks[t] : 0;
     float* gu = sm + (size_t)TB * H;                 // [TB][2 nf]
     gemv_stream<H, NP, TB>(A, true, 2 * nf, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)brow[t] * H; },
@@ -794,6 +850,46 @@ __device__ __forceinline__ bool op_gateup(int task) {
       const float g = gu[t * 2 * nf + f], up = gu[t * 2 * nf + nf + f];
       const float hv = (g / (1.f + expf(-g))) * up;
       stc(Hb, 4u * ((ctl.toks[t] * K + ctl.trank[t]) * F + f0 + f), hv);
+    }
+    __syncthreads();      // toks / trank / gu are rewritten by the next item
+  };
+  if (!dyn) {
+    if (T.a0 < nu) run_item(T.a0, T.a1, T.a2);
+  } else {
+    const int slices = T.a2, nfs = T.a4, n_items = nu * slices;
+    // hand the draw to the workgroup, with the sub-queue that had the most items left in the
+    // snapshot (-1: none had any)
+    auto publish = [&]() {
+      if (wave == 0) {
+        const int64_t first = (int64_t)head * nq + lane;
+        const int rem = lane < nq && first < n_items ? (int)((n_items - first + nq - 1) / nq) : 0;
+        const int best = (int)wmax<64>((float)rem);
+        const unsigned long long who = __ballot(rem == best && rem > 0);
+        if (lane == 0) {
+          ctl.item = (int)kreq;
+          ctl.steal = who ? __builtin_ctzll(who) : -1;
+        }
+      }
+      __syncthreads();
+    };
+    publish();
+    int probes = 1;
+    for (;;) {
+      const int k = ctl.item, steal_q = ctl.steal;
+      __syncthreads();    // every thread has read the draw
+      const int i = sq + nq * k;
+      if (i >= n_items) {               // this sub-queue is exhausted: steal from another one
+        if (steal_q < 0 || probes >= STEAL_PROBES) break;
+        ++probes;
+        sq = steal_q;
+        draw(sq);
+        publish();
+        continue;
+      }
+      draw(sq);                         // the next draw, in flight during the item
+      const int u = i / slices, j = i - u * slices, f0 = j * nfs;
+      run_item(u, f0, F - f0 < nfs ? F - f0 : nfs);
+      publish();
     }
   }
   MARK(4);
@@ -1487,10 +1583,13 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
       tab[b * D + j] = (float)cos(ang);
       tab[b * D + D / 2 + j] = (float)sin(ang);
     }
+    if (tid() == 0) ctl_s.norm_l = -1;
     __syncthreads();
   }
   for (int ti = qs; ti < qe; ++ti) {
     const int op = cst(p.tasks)[(size_t)ti * DESC_WORDS + D_OP];
+    // every other op overwrites the LDS area where expert slices keep the staged normed input
+    if (op != OP_GATEUP && tid() == 0) ctl_s.norm_l = -1;
     const uint64_t t_start = trace ? now() : 0;
     if (trace && tid() == 0) {
       ctl_s.t_ready = t_start;

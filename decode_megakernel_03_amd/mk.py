@@ -18,6 +18,7 @@ MK_ABI_VERSION = 1
 MK_MAX_BATCH = 8
 MK_FLAG_TRACE = 1
 MK_FLAG_NO_PREFETCH = 2
+MK_FLAG_STATIC_EXPERTS = 4
 DESC_WORDS = 16
 
 EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_decode_step", "mk_set_step_outputs",
@@ -74,7 +75,7 @@ def load(path=LIB_PATH):
         "mk_get_error": [vp, ctypes.c_char_p, sz],
         "mk_reset": [vp],
         "mk_destroy": [vp],
-        "mk_plan_build": [ctypes.POINTER(ModelDesc), i32, P32, i32, i32, ctypes.POINTER(vp)],
+        "mk_plan_build": [ctypes.POINTER(ModelDesc), i32, P32, i32, i32, ctypes.c_uint32, ctypes.POINTER(vp)],
         "mk_plan_info_get": [vp, ctypes.POINTER(PlanInfo)],
         "mk_plan_export": [vp, P32, P32],
         "mk_plan_validate": [vp, ctypes.c_char_p, sz],
@@ -165,10 +166,10 @@ def mk_destroy(h):
     LIB.mk_destroy(h)
 
 
-def mk_plan_build(desc, seq_lens, n_workers, split_keys=0):
+def mk_plan_build(desc, seq_lens, n_workers, split_keys=0, flags=0):
     h = ctypes.c_void_p()
     _check(LIB.mk_plan_build(ctypes.byref(desc), len(seq_lens), _i32_array(seq_lens), int(n_workers),
-                             int(split_keys), ctypes.byref(h)), None, "mk_plan_build")
+                             int(split_keys), int(flags), ctypes.byref(h)), None, "mk_plan_build")
     return h
 
 

@@ -113,6 +113,10 @@ typedef struct {
 
 #define MK_FLAG_TRACE 1u       /* record per-task timestamps into the trace buffer */
 #define MK_FLAG_NO_PREFETCH 2u /* ablation: issue weight loads only after dependencies are met */
+/* Ablation: deal the expert slices statically, one (union slot, FFN slice) per task, instead of
+ * from the per-layer work queue that tasks drain and steal from (P3 "Scheduling and Performance
+ * Benchmarks": dynamic work stealing). Read by mk_build_schedule / mk_plan_build. */
+#define MK_FLAG_STATIC_EXPERTS 4u
 
 /* Create an engine for `desc` over caller-owned weights (P1 "One persistent kernel for the whole
  * decode step"). Validates the description, copies the pointer tables to the device and
@@ -182,9 +186,10 @@ typedef struct {
 } mk_plan_info;
 
 /* Build a schedule without any GPU (for validation and tests): same algorithm as
- * mk_build_schedule for `n_workers` workers. *out is owned by the caller (mk_plan_destroy). */
+ * mk_build_schedule for `n_workers` workers; `flags` as in the options struct (MK_FLAG_STATIC_EXPERTS is
+ * the one the schedule reads). *out is owned by the caller (mk_plan_destroy). */
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* seq_lens_host,
-                        int32_t n_workers, int32_t split_keys, mk_plan** out);
+                        int32_t n_workers, int32_t split_keys, uint32_t flags, mk_plan** out);
 mk_status mk_plan_info_get(const mk_plan* p, mk_plan_info* info);
 /* Copy descriptors (n_tasks x 16 int32) and per-worker queue bounds (n_workers + 1 int32). */
 mk_status mk_plan_export(const mk_plan* p, int32_t* tasks, int32_t* queue_offsets);

@@ -42,7 +42,8 @@ def check_logits(gpu, ref, where):
         assert d.max() <= MAX_ABS and rel <= MAX_REL_L2, f"{where}: token {b}: max|d| {d.max():.3g}, rel L2 {rel:.3g}"
 
 
-def run_steps(wl, steps, gains="ones", seed=0, teacher_force=False, split_keys=0, mutate=None, near_tie=NEAR_TIE):
+def run_steps(wl, steps, gains="ones", seed=0, teacher_force=False, split_keys=0, mutate=None, near_tie=NEAR_TIE,
+              flags=0):
     from decode_megakernel_03_amd import mk
     s = harness.tiny_setup(wl, seed=seed, gains=gains)
     if mutate is not None:
@@ -57,8 +58,8 @@ def run_steps(wl, steps, gains="ones", seed=0, teacher_force=False, split_keys=0
     bt = torch.from_numpy(s["block_tables"]).cuda()
     eng = mk.Engine(wl, wd, kd, vd, s["num_pages"], s["block_tables"].shape[1], max_batch=B)
     ctx = s["ctx"].astype(np.int64)
-    if split_keys:
-        eng.set_options(split_keys=split_keys)
+    if split_keys or flags:
+        eng.set_options(split_keys=split_keys, flags=flags)
     eng.build_schedule((ctx + 1).tolist())
     argmax = torch.zeros(B, dtype=torch.int32, device="cuda")
     topk = torch.zeros(wl.n_layers, B, wl.top_k, dtype=torch.int32, device="cuda")
@@ -138,6 +139,13 @@ def test_tiny_batch3_ragged():
     say("test_tiny_batch3_ragged: batch 3, contexts 64 / 17 / 200 (spans several attention splits)")
     wl = synth.workload("tiny", batch=3, ragged=(17, 200))
     run_steps(wl, 4, teacher_force=True)
+
+
+def test_tiny_batch3_static_expert_slices():
+    say("test_tiny_batch3_static_expert_slices: batch 3 with static expert slices instead of the work queue")
+    from decode_megakernel_03_amd import mk
+    wl = synth.workload("tiny", batch=3, ragged=(17, 200))
+    run_steps(wl, 3, teacher_force=True, flags=mk.MK_FLAG_STATIC_EXPERTS)
 
 
 def test_tiny_split_attention():

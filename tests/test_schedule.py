@@ -38,11 +38,12 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("flags", [0, mk.MK_FLAG_STATIC_EXPERTS], ids=["queue", "static"])
 @pytest.mark.parametrize("name,lens,workers", CASES)
-def test_plan_valid_and_deadlock_free(name, lens, workers):
+def test_plan_valid_and_deadlock_free(name, lens, workers, flags):
     wl = synth.workload(name)
     desc = _desc(wl, len(lens), max(lens))
-    plan = mk.mk_plan_build(desc, lens, workers)
+    plan = mk.mk_plan_build(desc, lens, workers, flags=flags)
     try:
         st, msg = mk.mk_plan_validate(plan)
         assert st == mk.MK_OK, msg
@@ -148,3 +149,66 @@ def test_schedule_capacity_grows_with_split():
     mk.mk_plan_destroy(plan)
     assert info.n_attn_splits == 48 * 4 * 33
     assert info.key_capacity_min == 8192 + 1024
+
+
+STEAL_PROBES = 4     # sub-queues one expert task draws from (the kernel's constant)
+
+
+def _drain_queue(tickets, nq, n_items, rng):
+    """The expert-queue protocol of the kernel, with random interleavings of the tasks' draws: a
+    draw takes the next item of one sub-queue (an atomic add on its head) and snapshots every head;
+    a task draws from its own sub-queue until a draw lands past the last item, then steals from the
+    sub-queue with the most items left in its last snapshot (STEAL_PROBES draws at most), and stops
+    when the snapshot shows none. Returns how often each item was run."""
+    heads = [0] * nq
+    runs = np.zeros(n_items, dtype=int)
+
+    def rem(snap):
+        r = [max(0, -(-(n_items - (h * nq + q)) // nq)) for q, h in enumerate(snap)]
+        best = max(r)
+        return r.index(best) if best > 0 else -1
+
+    state = []
+    for q in tickets:
+        k = heads[q]; heads[q] += 1
+        state.append({"sq": q, "probes": 1, "k": k, "steal": rem(list(heads))})
+    live = list(range(len(tickets)))
+    while live:
+        i = live[rng.integers(len(live))]
+        st = state[i]
+        item = st["sq"] + nq * st["k"]
+        if item >= n_items:
+            if st["steal"] < 0 or st["probes"] >= STEAL_PROBES:
+                live.remove(i)
+                continue
+            st["probes"] += 1
+            st["sq"] = st["steal"]
+        else:
+            runs[item] += 1
+        st["k"] = heads[st["sq"]]; heads[st["sq"]] += 1
+        st["steal"] = rem(list(heads))
+    return runs
+
+
+@pytest.mark.parametrize("name,lens,workers", [("full", [8193] * 8, 512), ("full", [8193], 512), ("tiny", [65, 17, 200], 16),
+                                               ("full", [1025, 30000, 4096, 77, 16, 17, 32768, 9000], 512)])
+def test_expert_queue_runs_every_item_once(name, lens, workers):
+    """Queue-mode expert tasks: one queue counter per layer that nothing waits on, every sub-queue
+    owned by some task, and under random interleavings every (slot, slice) item of the step's union
+    is run exactly once whatever the union size."""
+    wl = synth.workload(name)
+    desc = _desc(wl, len(lens), max(lens))
+    plan = mk.mk_plan_build(desc, lens, workers)
+    tasks, qoff = mk.mk_plan_export(plan)
+    mk.mk_plan_destroy(plan)
+    gu = tasks[(tasks[:, 0] == 3) & (tasks[:, 1] == 1)]
+    assert len(gu) <= workers
+    qc, nq, slices, nfs = gu[0, 5], gu[0, 3], gu[0, 4], gu[0, 6]
+    assert np.all(gu[:, 5] == qc) and np.all(gu[:, 3] == nq) and set(gu[:, 2]) == set(range(nq))
+    assert slices * nfs >= wl.expert_ffn > (slices - 1) * nfs
+    assert not np.isin(tasks[:, [8, 10, 12, 13]], [qc]).any()
+    rng = np.random.default_rng(0)
+    slots = min(wl.n_experts, wl.top_k * len(lens))
+    for nu in sorted({wl.top_k, (wl.top_k + slots) // 2, slots}):
+        runs = _drain_queue(list(gu[:, 2]), nq, nu * slices, rng)
+        assert np.all(runs == 1)
