@@ -188,8 +188,10 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   std::vector<std::vector<int>> c_qkv(L, std::vector<int>(m.HKV));
   std::vector<std::vector<int>> c_aarr(L, std::vector<int>(B * m.HKV));
   // expert slices drawn from a per-layer queue (dynamic work stealing) unless static slices are
-  // asked for; the queue is a counter of its own (zeroed with the others at the end of a step)
-  const bool steal = !(flags & MK_FLAG_STATIC_EXPERTS);
+  // asked for; the queue is a counter of its own (zeroed with the others at the end of a step).
+  // At batch 1 the union is always top_k experts, so the work is known before the step and the
+  // static deal is kept (measured: the queue only moves items between equally loaded workers).
+  const bool steal = B > 1 && !(flags & MK_FLAG_STATIC_EXPERTS);
   std::vector<int> c_queue(L, -1);
   for (int l = 0; l < L; ++l) {
     for (int g = 0; g < m.HKV; ++g) c_qkv[l][g] = C.alloc();

@@ -190,10 +190,10 @@ def _drain_queue(tickets, nq, n_items, rng):
     return runs
 
 
-@pytest.mark.parametrize("name,lens,workers", [("full", [8193] * 8, 512), ("full", [8193], 512), ("tiny", [65, 17, 200], 16),
+@pytest.mark.parametrize("name,lens,workers", [("full", [8193] * 8, 512), ("full", [8193, 8193], 512), ("tiny", [65, 17, 200], 16),
                                                ("full", [1025, 30000, 4096, 77, 16, 17, 32768, 9000], 512)])
 def test_expert_queue_runs_every_item_once(name, lens, workers):
-    """Queue-mode expert tasks: one queue counter per layer that nothing waits on, every sub-queue
+    """Queue-mode expert tasks (batches above 1): one queue counter per layer that nothing waits on, every sub-queue
     owned by some task, and under random interleavings every (slot, slice) item of the step's union
     is run exactly once whatever the union size."""
     wl = synth.workload(name)
@@ -212,3 +212,13 @@ def test_expert_queue_runs_every_item_once(name, lens, workers):
     for nu in sorted({wl.top_k, (wl.top_k + slots) // 2, slots}):
         runs = _drain_queue(list(gu[:, 2]), nq, nu * slices, rng)
         assert np.all(runs == 1)
+
+
+def test_batch1_keeps_static_expert_slices():
+    """At batch 1 the union is always top_k experts: the slices are dealt statically."""
+    wl = synth.workload("full")
+    plan = mk.mk_plan_build(_desc(wl, 1, 8193), [8193], 512)
+    tasks, _ = mk.mk_plan_export(plan)
+    mk.mk_plan_destroy(plan)
+    gu = tasks[tasks[:, 0] == 3]
+    assert np.all(gu[:, 5] == -1) and len(gu) == 48 * 8 * len(set(gu[gu[:, 1] == 0][:, 3]))
