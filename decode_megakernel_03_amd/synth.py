@@ -193,6 +193,29 @@ def make_kv(wl, num_pages, seed=1, device="cpu", n_layers=None):
     return k, v
 
 
+def refill_sequence(wl, k, v, bt, b, new_ctx, extra_steps, seed):
+    """Continuous batching: sequence slot b has hit its length and restarts with a fresh prompt of
+    new_ctx positions. Its pages are reshuffled (seeded) and the ones covering the new prompt get
+    fresh N(0,1) K/V in every layer (in place, on whatever device k and v live). Returns the slot's
+    new block-table row (the same pages, in the new order) and the new sequence's first token."""
+    row = np.asarray(bt[b])
+    pages = row[row >= 0]
+    need = int((new_ctx + extra_steps + wl.page_size - 1) // wl.page_size)
+    if need > len(pages):
+        raise ValueError(f"slot {b} owns {len(pages)} pages, the new sequence needs {need}")
+    rng = np.random.default_rng([seed, 13, b])
+    pages = rng.permutation(pages)
+    out = np.full(row.shape, -1, np.int32)
+    out[:len(pages)] = pages
+    shape = (need, wl.n_kv_heads, wl.page_size, wl.head_dim)
+    for l in range(len(k)):
+        idx = torch.as_tensor(pages[:need].astype(np.int64), device=k[l].device)
+        k[l][idx] = normal_bf16(shape, 1.0, seed, 5000 + 2 * l, k[l].device)
+        v[l][idx] = normal_bf16(shape, 1.0, seed, 5001 + 2 * l, v[l].device)
+    token = int(rng.integers(0, max(wl.vocab, 1)))
+    return out, token
+
+
 def first_tokens(wl, seed=2):
     rng = np.random.default_rng([seed, 3])
     return rng.integers(0, max(wl.vocab, 1), size=wl.batch).astype(np.int32)

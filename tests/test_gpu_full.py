@@ -135,6 +135,23 @@ def test_full_shape_single_layer():
         m.close()
 
 
+def test_full_shape_single_layer_262k():
+    """One full-shape layer at 262144 context (16384 pages of 16, 537 MB of K+V): long splits and
+    the merge of many partials per KV group; two steps, so the second attends to the key the first
+    appended."""
+    say("test_full_shape_single_layer_262k")
+    wl = synth.workload("layer", context=262144)
+    m = Model(wl, steps=2)
+    try:
+        info = m.eng.plan_info()
+        say(f"  {info.n_attn_splits} attention splits, key capacity {info.key_capacity_min}")
+        assert info.n_attn_splits >= 4 * 256
+        for s in range(2):
+            m.step_and_check()
+    finally:
+        m.close()
+
+
 def test_full_model_batch1_8k():
     """48-layer model, batch 1, 8192 context: steps 0, 1 and 3 checked (2 runs unchecked)."""
     say("test_full_model_batch1_8k")

@@ -136,7 +136,7 @@ def test_tiny_uniform_gains():
 
 
 def test_tiny_batch3_ragged():
-    say("test_tiny_batch3_ragged: batch 3, contexts 64 / 17 / 200 (spans several attention splits)")
+    say("test_tiny_batch3_ragged: batch 3, contexts 91 / 21 / 44 (spans several attention splits)")
     wl = synth.workload("tiny", batch=3, ragged=(17, 200))
     run_steps(wl, 4, teacher_force=True)
 
@@ -165,3 +165,54 @@ def _tied_router(w):
 def test_tiny_router_exact_ties():
     say("test_tiny_router_exact_ties: exactly tied router logits resolve to the lowest expert index")
     run_steps(synth.workload("tiny"), 4, mutate=_tied_router, near_tie=-1.0)
+
+
+def test_tiny_slot_refill():
+    """Continuous batching with slot refill: batch 3 (contexts 91 / 21 / 44); after step 1 sequence 1
+    hits its length, its pages are reshuffled and refilled with fresh N(0,1) K/V for a new 30-token
+    prompt with a new first token, the schedule is rebuilt for the new lengths, and decoding goes on.
+    Every step is checked against the oracle on the KV state the step began with (teacher-forced)."""
+    from decode_megakernel_03_amd import mk
+    say("test_tiny_slot_refill: batch 3, sequence 1 refilled after step 1, schedule rebuilt")
+    wl = synth.workload("tiny", batch=3, ragged=(17, 200))
+    s = harness.tiny_setup(wl)
+    dims = harness.dims_of(wl)
+    dw = harness.dense_weights(s["w"])
+    wd = to_dev(s["w"])
+    kd = [t.cuda() for t in s["k"]]
+    vd = [t.cuda() for t in s["v"]]
+    B = wl.batch
+    bt_np = s["block_tables"].copy()
+    eng = mk.Engine(wl, wd, kd, vd, s["num_pages"], bt_np.shape[1], max_batch=B)
+    pos = s["ctx"].astype(np.int64).copy()
+    eng.build_schedule((pos + 1).tolist())
+    argmax = torch.zeros(B, dtype=torch.int32, device="cuda")
+    topk = torch.zeros(wl.n_layers, B, wl.top_k, dtype=torch.int32, device="cuda")
+    eng.set_step_outputs(argmax_out=argmax, topk_out=topk)
+    logits = torch.zeros(B, wl.vocab, dtype=torch.float32, device="cuda")
+    tok = s["tokens"].astype(np.int64)
+    for step in range(5):
+        if step == 2:
+            row, first = synth.refill_sequence(wl, kd, vd, bt_np, 1, 30, 8, seed=9)
+            bt_np[1] = row
+            pos[1] = 30
+            tok[1] = first
+            eng.build_schedule((pos + 1).tolist())
+            say(f"  refill: sequence 1 restarts at position 30, token {first}, pages {row[:3].tolist()}...")
+        kv0 = harness.host_kv(kd, vd)
+        bt = torch.from_numpy(bt_np).cuda()
+        say(f"  step {step}: positions {pos.tolist()}")
+        eng.step(torch.from_numpy(tok.astype(np.int32)).cuda(), torch.from_numpy(pos.astype(np.int32)).cuda(), bt,
+                 torch.from_numpy((pos + 1).astype(np.int32)).cuda(), logits)
+        torch.cuda.synchronize()
+        eng.sync()
+        g_logits = logits.cpu().numpy()
+        g_topk = topk.cpu().numpy()
+        g_arg = argmax.cpu().numpy().astype(np.int64)
+        ref, _ = harness.replay_near_ties(
+            lambda forced: oracle_step(dims, dw, kv0, tok, pos, bt_np, forced=forced), g_topk, NEAR_TIE)
+        check_logits(g_logits, ref.logits, f"refill step {step}")
+        assert np.array_equal(g_arg, np.argmax(ref.logits, axis=1)), f"refill step {step}: greedy tokens differ"
+        tok = g_arg
+        pos = pos + 1
+    eng.close()
