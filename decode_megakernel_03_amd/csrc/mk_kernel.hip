@@ -930,13 +930,28 @@ struct AttnLds {
   static constexpr int END = al(QF + HPG * D);
 };
 
+constexpr int OUT_OT = 4;   // tokens whose attention vectors are staged together
+
+template <class S>
+struct OutLds {   // LDS layout of a batched output task, in floats
+  static constexpr int KF = S::K * S::F;
+  static constexpr int A = 0;                           // [OUT_OT][AD] attention (O-projection phase)
+  static constexpr int HA = 0, HB = KF;                 // [K][F] h of two tokens (MoE phase)
+  static constexpr int Y = (OUT_OT * S::AD > 2 * KF ? OUT_OT * S::AD : 2 * KF);   // [K][OUT_MAXR]
+  static constexpr int MO = Y + S::K * OUT_MAXR;        // [MAXB][OUT_MAXR] MoE term
+  static constexpr int XV = MO + MAXB * OUT_MAXR;       // [MAXB][OUT_MAXR] x_l rows
+  static constexpr int O = XV + MAXB * OUT_MAXR;        // [OUT_OT][OUT_MAXR] O-projection rows
+  static constexpr int END = O + OUT_OT * OUT_MAXR;
+};
+
 // Dynamic LDS: the ops' working area (the largest of: norm-staged activations + GEMV scratch,
 // attention buffers, OUT staging, routing scratch), then the step's RoPE table.
 template <class S>
 __host__ __device__ constexpr int rope_off(int tb) {
   const int act = tb * S::H + tb * 2 * 64 + 1024;
   const int att = AttnLds<S>::END;
-  const int out = S::AD + S::K * S::F + OUT_MAXR + S::K * OUT_MAXR + 2 * MAXB * OUT_MAXR;
+  const int out1 = S::AD + S::K * S::F + OUT_MAXR + S::K * OUT_MAXR + 2 * MAXB * OUT_MAXR;
+  const int out = tb > 1 && OutLds<S>::END > out1 ? OutLds<S>::END : out1;
   const int rte = MAXB * S::E * 3 + S::E + 64;
   const int mrg = MERGE_MAX * 2 * 2 * NWAVE + 2 * NWAVE;
   int m = act;
@@ -1473,6 +1488,135 @@ __device__ __forceinline__ bool op_out(int task) {
   return true;
 }
 
+// Output rows for a batch of several tokens: the same sums as op_out, in the same order (so the
+// results are bitwise those of the one-token form), laid out for latency:
+//   * the x_l rows of every token are requested once, up front;
+//   * the MoE term is pipelined over tokens: the W_down rows and the h vectors of token b+1 are in
+//     flight while token b is multiplied (two register buffers, two LDS h buffers);
+//   * the attention vectors of OT tokens are staged together and the O projection multiplies them
+//     in one pass over the W_o rows.
+template <class S, int TB>
+__device__ __forceinline__ bool op_out_batch(int task) {
+  CParams& p = P();
+  Ctl& ctl = ctl_s;
+  float* sm = smem;
+  const TaskHdr T = read_task(p, task);
+  constexpr int H = S::H, AD = S::AD, F = S::F, K = S::K, KF = K * F;
+  using LY = OutLds<S>;
+  constexpr int NPO = (OUT_MAXR + NWAVE * Geo<AD>::RPP - 1) / (NWAVE * Geo<AD>::RPP);
+  constexpr int NPD = (OUT_MAXR * K + NWAVE * Geo<F>::RPP - 1) / (NWAVE * Geo<F>::RPP);
+  constexpr int HI = (KF + 4 * NT - 1) / (4 * NT);
+  const int l = T.layer, row0 = T.a0, nrows = T.a1, B = p.B;
+  const auto& Lp = cst(p.layers)[l];
+  float* y_s = sm + LY::Y;
+  float* mo_s = sm + LY::MO;
+  float* xv_s = sm + LY::XV;
+  float* o_s = sm + LY::O;
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;      // routing known
+  load_route(p, l);
+  const RouteTable& rt = ctl.rt;
+  const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
+  const __amdgpu_buffer_rsrc_t At = rsrc(p.attn + (size_t)l * MAXB * AD);
+  const __amdgpu_buffer_rsrc_t Xn = rsrc(p.x + (size_t)(l + 1) * MAXB * H);
+  // x_l[b][row0 + r] for every (b, r): one value per thread, written to LDS after the MoE term
+  float xv = 0.f;
+  const int tx = tid();
+  if (tx < B * nrows) {
+    const int b = tx / nrows, row = row0 + tx % nrows;
+    if (l == 0) {
+      int tok = cst(p.tokens)[b];
+      tok = (tok < 0 || tok >= p.V) ? 0 : tok;
+      xv = bf1(p.embed[(size_t)tok * H + row]);
+    } else {
+      xv = ldc(rsrc(p.x + ((size_t)l * MAXB + b) * H), 4u * row);
+    }
+  }
+  // W_down rows of token b: q = i * nrows + r is row row0 + r of its i-th expert
+  auto drow_of = [&](int b) {
+    return [&, b](int q) {
+      const int i = q / nrows, r = q - i * nrows;
+      return Lp.w_down + ((size_t)rt.sel[b][i] * H + row0 + r) * F;
+    };
+  };
+  f4 hv[HI];
+  auto h_issue = [&](int b) {
+#pragma unroll
+    for (int u = 0; u < HI; ++u) {
+      const int i = (u * NT + tx) * 4;
+      hv[u] = i < KF ? ldc4(Hb, 4u * (b * KF + i)) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+  };
+  auto h_put = [&](float* dst) {
+#pragma unroll
+    for (int u = 0; u < HI; ++u) {
+      const int i = (u * NT + tx) * 4;
+      if (i < KF) *reinterpret_cast<f4*>(dst + i) = hv[u];
+    }
+  };
+  // token b's MoE term from its W_down rows (in W) and its h (staged at hs)
+  auto moe_token = [&](const WBuf<F, NPD>& W, const float* hs, int b) {
+    compute_block<F, NPD, 1>(W, 0, K * nrows, 1, [&](int q, int t) { return hs + (q / nrows) * F; },
+                             [&](int q, int t, float v) { y_s[(q / nrows) * OUT_MAXR + q % nrows] = v; });
+    __syncthreads();
+    if (tx < nrows) {
+      float moe = 0.f;
+      for (int i = 0; i < K; ++i) moe = moe + rt.w[b][i] * y_s[i * OUT_MAXR + tx];
+      mo_s[b * OUT_MAXR + tx] = moe;
+    }
+  };
+  float* hA = sm + LY::HA;
+  float* hB = sm + LY::HB;
+  WBuf<F, NPD> WA, WB;
+  load_block<F, NPD>(WA, 0, K * nrows, drow_of(0));
+  if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every MoE slice
+  h_issue(0);
+  h_put(hA);
+  MARK(0);
+  for (int b = 0; b < B; b += 2) {
+    const bool has1 = b + 1 < B;
+    if (has1) { load_block<F, NPD>(WB, 0, K * nrows, drow_of(b + 1)); h_issue(b + 1); }
+    __syncthreads();                       // hA staged; the previous token is done with y_s
+    moe_token(WA, hA, b);
+    if (has1) h_put(hB);
+    if (b + 2 < B) { load_block<F, NPD>(WA, 0, K * nrows, drow_of(b + 2)); h_issue(b + 2); }
+    if (has1) {
+      __syncthreads();                     // hB staged; token b is done with y_s and hA
+      moe_token(WB, hB, b + 1);
+      if (b + 2 < B) h_put(hA);
+    }
+  }
+  if (tx < B * nrows) xv_s[(tx / nrows) * OUT_MAXR + tx % nrows] = xv;
+  MARK(1);
+  // O projection of OUT_OT tokens per pass over the W_o rows
+  auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * AD; };
+  WBuf<AD, NPO> WO;
+  load_block<AD, NPO>(WO, 0, nrows, orow);
+  __syncthreads();                         // the MoE phase is done with the LDS it shares with a_s
+  if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
+  float* a_s = sm + LY::A;
+  for (int b0 = 0; b0 < B; b0 += OUT_OT) {
+    const int nt = B - b0 < OUT_OT ? B - b0 : OUT_OT;
+    stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
+    __syncthreads();
+    if (b0 == 0) MARK(2);
+    compute_block_shared<AD, NPO, OUT_OT>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
+                                          [&](int r, int t, float v) { o_s[t * OUT_MAXR + r] = v; });
+    __syncthreads();
+    if (tx < nt * nrows) {
+      const int t = tx / nrows, r = tx % nrows, b = b0 + t, row = row0 + r;
+      const float xn = (xv_s[b * OUT_MAXR + r] + o_s[t * OUT_MAXR + r]) + mo_s[b * OUT_MAXR + r];
+      stc(Xn, 4u * (b * H + row), xn);
+      if (p.hidden_out && l == p.L - 1) p.hidden_out[(size_t)b * H + row] = xn;
+    }
+    __syncthreads();
+  }
+  MARK(3);
+  drain_t(p);
+  MARK(4);
+  signal(p, ctl, T.sig, false);
+  return true;
+}
+
 // lm_head rows row0..row0+nrows: logits = W_lm . RMSNorm_final(x_L), plus the running greedy
 // argmax (first index of the maximum) through a 64-bit atomic max on (ordered logit, ~index).
 template <class S, int TB>
@@ -1604,7 +1748,10 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
       case OP_ROUTER: ok = op_router<S, TB>(ti); break;
       case OP_GATEUP: ok = op_gateup<S, TB>(ti); break;
       case OP_ATTN: ok = op_attn<S, TB>(ti); break;
-      case OP_OUT: ok = op_out<S, TB>(ti); break;
+      case OP_OUT:
+        if constexpr (TB == 1) ok = op_out<S, TB>(ti);
+        else ok = op_out_batch<S, TB>(ti);
+        break;
       case OP_LMHEAD: ok = op_lmhead<S, TB>(ti); break;
       case OP_MERGE: ok = op_merge<S>(ti); break;
       default:
