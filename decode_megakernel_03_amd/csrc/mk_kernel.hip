@@ -940,8 +940,8 @@ struct OutLds {   // LDS layout of a batched output task, in floats
   static constexpr int Y = (OUT_OT * S::AD > 2 * KF ? OUT_OT * S::AD : 2 * KF);   // [K][OUT_MAXR]
   static constexpr int MO = Y + S::K * OUT_MAXR;        // [MAXB][OUT_MAXR] MoE term
   static constexpr int XV = MO + MAXB * OUT_MAXR;       // [MAXB][OUT_MAXR] x_l rows
-  static constexpr int O = XV + MAXB * OUT_MAXR;        // [MAXB][OUT_MAXR] O-projection rows
-  static constexpr int END = O + MAXB * OUT_MAXR;
+  static constexpr int O = XV + MAXB * OUT_MAXR;        // [OUT_OT][OUT_MAXR] O-projection rows
+  static constexpr int END = O + OUT_OT * OUT_MAXR;
 };
 
 // Dynamic LDS: the ops' working area (the largest of: norm-staged activations + GEMV scratch,
@@ -1490,13 +1490,11 @@ __device__ __forceinline__ bool op_out(int task) {
 
 // Output rows for a batch of several tokens: the same sums as op_out, in the same order (so the
 // results are bitwise those of the one-token form), laid out for latency:
-//   * with several tokens the attention is in long before the expert slices are done (the
-//     routing-dependent expert streams are the bulk of the layer), so the O projection comes
-//     first: the attention vectors of OUT_OT tokens are staged together and multiplied in one pass
-//     over the W_o rows (prefetched before the wait), while the expert slices still stream;
 //   * the x_l rows of every token are requested once, up front;
 //   * the MoE term is pipelined over tokens: the W_down rows and the h vectors of token b+1 are in
-//     flight while token b is multiplied (two register buffers, two LDS h buffers).
+//     flight while token b is multiplied (two register buffers, two LDS h buffers);
+//   * the attention vectors of OT tokens are staged together and the O projection multiplies them
+//     in one pass over the W_o rows.
 template <class S, int TB>
 __device__ __forceinline__ bool op_out_batch(int task) {
   CParams& p = P();
@@ -1514,32 +1512,15 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   float* mo_s = sm + LY::MO;
   float* xv_s = sm + LY::XV;
   float* o_s = sm + LY::O;
+  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;      // routing known
+  load_route(p, l);
+  const RouteTable& rt = ctl.rt;
   const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
   const __amdgpu_buffer_rsrc_t At = rsrc(p.attn + (size_t)l * MAXB * AD);
   const __amdgpu_buffer_rsrc_t Xn = rsrc(p.x + (size_t)(l + 1) * MAXB * H);
-  const int tx = tid();
-  // O projection first (W_o rows requested before the wait)
-  auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * AD; };
-  {
-    WBuf<AD, NPO> WO;
-    const bool pre = !(p.flags & 2);
-    if (pre) load_block<AD, NPO>(WO, 0, nrows, orow);
-    if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;    // attention of every KV group
-    if (!pre) load_block<AD, NPO>(WO, 0, nrows, orow);
-    float* a_s = sm + LY::A;
-    for (int b0 = 0; b0 < B; b0 += OUT_OT) {
-      const int nt = B - b0 < OUT_OT ? B - b0 : OUT_OT;
-      stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
-      __syncthreads();
-      if (b0 == 0) MARK(0);
-      compute_block_shared<AD, NPO, OUT_OT>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
-                                            [&](int r, int t, float v) { o_s[(b0 + t) * OUT_MAXR + r] = v; });
-      __syncthreads();
-    }
-  }
-  MARK(1);
   // x_l[b][row0 + r] for every (b, r): one value per thread, written to LDS after the MoE term
   float xv = 0.f;
+  const int tx = tid();
   if (tx < B * nrows) {
     const int b = tx / nrows, row = row0 + tx % nrows;
     if (l == 0) {
@@ -1550,9 +1531,6 @@ __device__ __forceinline__ bool op_out_batch(int task) {
       xv = ldc(rsrc(p.x + ((size_t)l * MAXB + b) * H), 4u * row);
     }
   }
-  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;      // routing known
-  load_route(p, l);
-  const RouteTable& rt = ctl.rt;
   // W_down rows of token b: q = i * nrows + r is row row0 + r of its i-th expert
   auto drow_of = [&](int b) {
     return [&, b](int q) {
@@ -1593,7 +1571,7 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every MoE slice
   h_issue(0);
   h_put(hA);
-  MARK(2);
+  MARK(0);
   for (int b = 0; b < B; b += 2) {
     const bool has1 = b + 1 < B;
     if (has1) { load_block<F, NPD>(WB, 0, K * nrows, drow_of(b + 1)); h_issue(b + 1); }
@@ -1608,13 +1586,29 @@ __device__ __forceinline__ bool op_out_batch(int task) {
     }
   }
   if (tx < B * nrows) xv_s[(tx / nrows) * OUT_MAXR + tx % nrows] = xv;
-  __syncthreads();
-  // the residual add that rejoins both branches, for every token and row
-  if (tx < B * nrows) {
-    const int b = tx / nrows, r = tx % nrows, row = row0 + r;
-    const float xn = (xv_s[b * OUT_MAXR + r] + o_s[b * OUT_MAXR + r]) + mo_s[b * OUT_MAXR + r];
-    stc(Xn, 4u * (b * H + row), xn);
-    if (p.hidden_out && l == p.L - 1) p.hidden_out[(size_t)b * H + row] = xn;
+  MARK(1);
+  // O projection of OUT_OT tokens per pass over the W_o rows
+  auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * AD; };
+  WBuf<AD, NPO> WO;
+  load_block<AD, NPO>(WO, 0, nrows, orow);
+  __syncthreads();                         // the MoE phase is done with the LDS it shares with a_s
+  if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
+  float* a_s = sm + LY::A;
+  for (int b0 = 0; b0 < B; b0 += OUT_OT) {
+    const int nt = B - b0 < OUT_OT ? B - b0 : OUT_OT;
+    stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
+    __syncthreads();
+    if (b0 == 0) MARK(2);
+    compute_block_shared<AD, NPO, OUT_OT>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
+                                          [&](int r, int t, float v) { o_s[t * OUT_MAXR + r] = v; });
+    __syncthreads();
+    if (tx < nt * nrows) {
+      const int t = tx / nrows, r = tx % nrows, b = b0 + t, row = row0 + r;
+      const float xn = (xv_s[b * OUT_MAXR + r] + o_s[t * OUT_MAXR + r]) + mo_s[b * OUT_MAXR + r];
+      stc(Xn, 4u * (b * H + row), xn);
+      if (p.hidden_out && l == p.L - 1) p.hidden_out[(size_t)b * H + row] = xn;
+    }
+    __syncthreads();
   }
   MARK(3);
   drain_t(p);
