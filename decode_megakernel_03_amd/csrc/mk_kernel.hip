@@ -1049,9 +1049,23 @@ __device__ __forceinline__ bool op_attn(int task) {
     }
   };
   // the cached keys and values do not depend on this step's activations: the first chunk of both
-  // is in flight while the task waits for the QKV rows
+  // is in flight while the task waits for the QKV rows. When a second chunk holds at most one page
+  // (splits a little longer than a chunk), that page's values are requested with the first chunk:
+  // they fall in wave 0's first rows, which take them in a few more registers instead of paying a
+  // dependent round trip in the P V pass. (Its keys are loaded at the second score chunk: holding
+  // them through the score pass as well would exceed the register budget.)
   load_k(0);
   load_v(0);
+  const bool tail = nchunk == 2 && nk - KC <= PAGE;    // uniform in the workgroup
+  constexpr int VT_Q = PAGE / KPW;                     // V loads of wave 0 that hold the tail page
+  u4 vtl[VT_Q];
+  if (tail && wave == 0) {
+#pragma unroll
+    for (int q = 0; q < VT_Q; ++q) {
+      const int jv = k0 + KC + KPW * q + lane / LPK;
+      vtl[q] = jv < kend ? ldw(Lp.v_cache + kaddr(jv, 8 * li)) : u4{0u, 0u, 0u, 0u};
+    }
+  }
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + ((size_t)l * MAXB + b) * S::QKVR);
   const float rsd = 1.0f / sqrtf((float)D);
@@ -1124,7 +1138,9 @@ __device__ __forceinline__ bool op_attn(int task) {
   MARK(0);
   // ---- pass A: s[j][hh] = (k_j . q_hh) / sqrt(D) on the matrix cores, cached keys j < nk
   for (int c = 0; c < nchunk; ++c) {
-    if (c > 0) load_k(c);
+    if (c > 0) {
+      load_k(c);
+    }
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int jb = c * KC + (wave + NWAVE * i) * 16;   // first key of the block, relative to k0
@@ -1211,7 +1227,14 @@ __device__ __forceinline__ bool op_attn(int task) {
     const bool pvalid = ph < HPG, plo = (col & 2) != 0;
     const float* prow = sbuf + (pvalid ? ph : 0) * PS;
     for (int c = 0; c < nchunk; ++c) {
-      if (c > 0) load_v(c);
+      if (c > 0) {
+        if (!tail) {
+          load_v(c);
+        } else if (wave == 0) {          // the prefetched tail page, zeros after it
+#pragma unroll
+          for (int q = 0; q < VPL; ++q) vr[q] = q < VT_Q ? vtl[q < VT_Q ? q : 0] : u4{0u, 0u, 0u, 0u};
+        }
+      }
 #pragma unroll
       for (int kh = 0; kh < 2; ++kh) {              // the wave's two 32-key blocks
         const int kbase = c * KC + (KC / NWAVE) * wave + 32 * kh;   // relative to k0
