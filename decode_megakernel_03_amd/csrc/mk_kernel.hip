@@ -1648,7 +1648,8 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 2 : 4, RPP = Geo<H>::RPP;
+  // several tokens: more row passes per block, so that each activation read from LDS serves more rows
+  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? (TB > 1 ? 4 : 2) : 4, RPP = Geo<H>::RPP;
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return p.lm_head + (size_t)(row0 + r) * H; };
   WBuf<H, NP> A;
