@@ -192,12 +192,6 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // At batch 1 the union is always top_k experts, so the work is known before the step and the
   // static deal is kept (measured: the queue only moves items between equally loaded workers).
   const bool steal = B > 1 && !(flags & MK_FLAG_STATIC_EXPERTS);
-  // Order inside level 1 of a worker's queue. At batch 1 the attention splits come first (the
-  // attention chain is the layer's critical path). With several tokens the expert slices are the
-  // bulk of the layer's bytes and the routing is known soon after the QKV tiles, so the expert
-  // tasks come first and the splits (whose outputs the output rows need last) after them.
-  const bool experts_first = B > 1 && !(flags & MK_FLAG_SPLITS_FIRST);
-  const int prio_attn = experts_first ? 1 : 0, prio_gu = experts_first ? 0 : 1;
   std::vector<int> c_queue(L, -1);
   for (int l = 0; l < L; ++l) {
     for (int g = 0; g < m.HKV; ++g) c_qkv[l][g] = C.alloc();
@@ -292,7 +286,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.t.w[D_SIG] = c_aarr[l][b * m.HKV + g];
           const int keys = last ? seq_lens[b] - k0 : split;
           pr.bytes = (int64_t)keys * m.D * 2 * 2;
-          pr.prio = prio_attn;
+          pr.prio = 0;
           pr.pin = -2 - split_key(l, b, g, s);     // records its worker (see placement)
           levels[lv1].push_back(pr);
           n_attn++;
@@ -313,7 +307,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
         pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
         pr.t.w[D_SIG] = c_h[l];
         pr.bytes = (int64_t)n_items * 2 * nf * m.H * 2 / tickets;
-        pr.prio = prio_gu;
+        pr.prio = 1;
         levels[lv1].push_back(pr);
         n_gu++;
       }
@@ -328,7 +322,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
           pr.t.w[D_SIG] = c_h[l];
           pr.bytes = (int64_t)2 * (f1 - f0) * m.H * 2;
-          pr.prio = prio_gu;
+          pr.prio = 1;
           levels[lv1].push_back(pr);
           n_gu++;
         }
@@ -401,7 +395,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // ties go to the worker with the least load in the previous level (so attention splits land on
   // workers idle in level 0 and prefetch their keys early), then least total load, then index.
   // Each worker's queue is level-ordered, and inside a level its tasks run in priority order
-  // (router before QKV; at level 1 as chosen above: attention or expert slices first).
+  // (router before QKV, attention before expert slices).
   std::vector<std::vector<std::pair<int, Proto>>> queues(W);   // (level, proto)
   std::unordered_map<int, int> split_worker;                    // attention split key -> worker
   std::vector<int64_t> total(W, 0), prev(W, 0);

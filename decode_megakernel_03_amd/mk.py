@@ -19,7 +19,6 @@ MK_MAX_BATCH = 8
 MK_FLAG_TRACE = 1
 MK_FLAG_NO_PREFETCH = 2
 MK_FLAG_STATIC_EXPERTS = 4
-MK_FLAG_SPLITS_FIRST = 8
 DESC_WORDS = 16
 
 EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_decode_step", "mk_set_step_outputs",

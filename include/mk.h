@@ -117,9 +117,6 @@ typedef struct {
  * from the per-layer work queue that tasks drain and steal from (P3 "Scheduling and Performance
  * Benchmarks": dynamic work stealing). Read by mk_build_schedule / mk_plan_build. */
 #define MK_FLAG_STATIC_EXPERTS 4u
-/* Ablation: at batch > 1, run a worker's attention splits before its expert task (the default at
- * batch > 1 runs the expert task first: the expert streams are the bulk of the layer). */
-#define MK_FLAG_SPLITS_FIRST 8u
 
 /* Create an engine for `desc` over caller-owned weights (P1 "One persistent kernel for the whole
  * decode step"). Validates the description, copies the pointer tables to the device and
