@@ -375,21 +375,18 @@ struct WBuf {
   u4 w[NP][Geo<KD>::CPL];
 };
 
-// WV0 > 0: waves 0..WV0-1 take no rows (they stay free for dependency polls, whose results would
-// otherwise return only after the wave's own weight loads: a wave's loads complete in order).
-template <int KD, int NP, int WV0 = 0>
-__host__ __device__ constexpr int block_rows() { return NP * (NWAVE - WV0) * Geo<KD>::RPP; }
+template <int KD, int NP>
+__device__ __forceinline__ int block_rows() { return NP * NWAVE * Geo<KD>::RPP; }
 
 // RowPtr(r) -> const uint16_t* start of row r (only called for r < nrows)
-template <int KD, int NP, int WV0 = 0, class RowPtr>
+template <int KD, int NP, class RowPtr>
 __device__ __forceinline__ void load_block(WBuf<KD, NP>& b, int blk, int nrows, RowPtr rowptr) {
   using G = Geo<KD>;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
-  if (wave < WV0) return;
 #pragma unroll
   for (int i = 0; i < NP; ++i) {
-    const int r = ((blk * NP + i) * (NWAVE - WV0) + wave - WV0) * G::RPP + rip;
+    const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
     if (r < nrows) {
       const uint16_t* src = rowptr(r) + 8 * lir;
 #pragma unroll
@@ -434,13 +431,12 @@ __device__ __forceinline__ void compute_block(const WBuf<KD, NP>& b, int blk, in
 // input vector per token): each 16-byte activation read from LDS serves all NP passes of the block,
 // so a batch of TB tokens reads LDS NP times less. Per row, the products are summed in the same
 // order as compute_block.
-template <int KD, int NP, int TB, int WV0 = 0, class ActOf, class Emit>
+template <int KD, int NP, int TB, class ActOf, class Emit>
 __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int blk, int nrows, int ntok,
                                                      ActOf act_of, Emit emit) {
   using G = Geo<KD>;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
-  if (wave < WV0) return;
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     if (t < ntok) {
@@ -457,7 +453,7 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int 
       }
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
-        const int r = ((blk * NP + i) * (NWAVE - WV0) + wave - WV0) * G::RPP + rip;
+        const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
         const float v = wsum<G::LPR>(acc[i]);
         if (lir == 0 && r < nrows) emit(r, t, v);
       }
@@ -467,19 +463,18 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int 
 
 // Stream `nrows` rows; block 0 may already be loaded into A (prefetched before a dependency wait).
 // The activations are shared by all rows (ActOf ignores its row argument).
-template <int KD, int NP, int TB, int WV0 = 0, class RowPtr, class ActOf, class Emit>
+template <int KD, int NP, int TB, class RowPtr, class ActOf, class Emit>
 __device__ __forceinline__ void gemv_stream(WBuf<KD, NP>& A, bool a_loaded, int nrows, int ntok,
                                             RowPtr rowptr, ActOf act_of, Emit emit) {
-  constexpr int BR = block_rows<KD, NP, WV0>();
-  const int nblk = (nrows + BR - 1) / BR;
+  const int nblk = (nrows + block_rows<KD, NP>() - 1) / block_rows<KD, NP>();
   WBuf<KD, NP> B;
-  if (!a_loaded) load_block<KD, NP, WV0>(A, 0, nrows, rowptr);
+  if (!a_loaded) load_block<KD, NP>(A, 0, nrows, rowptr);
   for (int blk = 0; blk < nblk; blk += 2) {
-    if (blk + 1 < nblk) load_block<KD, NP, WV0>(B, blk + 1, nrows, rowptr);
-    compute_block_shared<KD, NP, TB, WV0>(A, blk, nrows, ntok, act_of, emit);
+    if (blk + 1 < nblk) load_block<KD, NP>(B, blk + 1, nrows, rowptr);
+    compute_block_shared<KD, NP, TB>(A, blk, nrows, ntok, act_of, emit);
     if (blk + 1 < nblk) {
-      if (blk + 2 < nblk) load_block<KD, NP, WV0>(A, blk + 2, nrows, rowptr);
-      compute_block_shared<KD, NP, TB, WV0>(B, blk + 1, nrows, ntok, act_of, emit);
+      if (blk + 2 < nblk) load_block<KD, NP>(A, blk + 2, nrows, rowptr);
+      compute_block_shared<KD, NP, TB>(B, blk + 1, nrows, ntok, act_of, emit);
     }
   }
 }
@@ -570,23 +565,20 @@ __device__ __forceinline__ bool op_qkv(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  // a whole 16-row tile in flight before the wait; with one token, wave 0 takes no rows: it polls
-  // the residual-stream counter and stages the normed input while waves 1-3 stream the tile
-  constexpr int WV0 = TB == 1 ? 1 : 0;
-  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? (WV0 ? 6 : 4) : 8;
+  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 4 : 8;   // a whole 16-row tile in flight before the wait
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_qkv + (size_t)(row0 + r) * H; };
   WBuf<H, NP> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<H, NP, WV0>(A, 0, nrows, rowptr);
+  if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
   stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
   MARK(0);
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + (size_t)T.layer * MAXB * S::QKVR);
-  gemv_stream<H, NP, TB, WV0>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); });
   MARK(1);
@@ -729,14 +721,13 @@ __device__ __forceinline__ bool op_router(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int WV0 = TB == 1 ? 1 : 0;     // as for the QKV tiles
-  constexpr int H = S::H, E = S::E, NP = (Geo<H>::CPL >= 4) ? (WV0 ? 6 : 4) : 8;
+  constexpr int H = S::H, E = S::E, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_router + (size_t)(row0 + r) * H; };
   WBuf<H, NP> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<H, NP, WV0>(A, 0, nrows, rowptr);
+  if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
@@ -744,7 +735,7 @@ __device__ __forceinline__ bool op_router(int task) {
   MARK(0);
   const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)T.layer * MAXB * E);
   const float* bias = p.has_bias ? Lp.router_bias : nullptr;
-  gemv_stream<H, NP, TB, WV0>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) {
         const int e = row0 + r;
