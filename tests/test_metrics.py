@@ -44,3 +44,4 @@ def test_step_bytes_by_enumeration():
     assert metrics.step_bytes(wl, np.full(L, 8), [8192]) == total + kv
     # 6.08 GB of weights and 0.81 GB of KV, as the shapes imply
     assert math.isclose(total / 1e9, 6.0835, abs_tol=1e-3) and math.isclose(kv / 1e9, 0.8053, abs_tol=1e-3)
+
