@@ -80,14 +80,15 @@ def host_kv(k, v):
     return oracle.PagedKV(k=[synth.to_u16(t) for t in k], v=[synth.to_u16(t) for t in v])
 
 
-def tiny_setup(wl=None, seed=0, gains="ones", batch=None, device="cpu"):
-    """Generated inputs for a small workload: weights, KV, tables, lengths, first tokens."""
+def tiny_setup(wl=None, seed=0, gains="ones", batch=None, device="cpu", ctx=None):
+    """Generated inputs for a small workload: weights, KV, tables, lengths, first tokens.
+    ``ctx`` overrides the prefilled context per sequence (e.g. 0: the sequence's first token)."""
     wl = wl or synth.workload("tiny")
     if batch is not None:
         wl = synth.workload(wl.name, batch=batch) if wl.name in synth.WORKLOADS else wl
     bias = synth.zipf_router_bias(wl) if wl.zipf_s else None
     w = synth.make_weights(wl, seed=seed, device=device, gains=gains, router_bias=bias)
-    ctx = synth.context_lengths(wl)
+    ctx = synth.context_lengths(wl) if ctx is None else np.asarray(ctx, np.int64)
     bt, num_pages = synth.make_block_tables(ctx, wl.steps, wl.page_size)
     k, v = synth.make_kv(wl, num_pages, device=device)
     tokens = synth.first_tokens(wl)

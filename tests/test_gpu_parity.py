@@ -43,9 +43,9 @@ def check_logits(gpu, ref, where):
 
 
 def run_steps(wl, steps, gains="ones", seed=0, teacher_force=False, split_keys=0, mutate=None, near_tie=NEAR_TIE,
-              flags=0):
+              flags=0, ctx=None):
     from decode_megakernel_03_amd import mk
-    s = harness.tiny_setup(wl, seed=seed, gains=gains)
+    s = harness.tiny_setup(wl, seed=seed, gains=gains, ctx=ctx)
     if mutate is not None:
         mutate(s["w"])
     dims = harness.dims_of(wl)
@@ -146,6 +146,14 @@ def test_tiny_batch3_static_expert_slices():
     from decode_megakernel_03_amd import mk
     wl = synth.workload("tiny", batch=3, ragged=(17, 200))
     run_steps(wl, 3, teacher_force=True, flags=mk.MK_FLAG_STATIC_EXPERTS)
+
+
+def test_tiny_first_token_and_page_boundary():
+    """Degenerate contexts: sequence 0 decodes its first token (position 0: attention over its own
+    key only), sequence 1's new token opens a fresh page (position 16); three steps each."""
+    say("test_tiny_first_token_and_page_boundary: batch 2, contexts 0 and 16")
+    wl = synth.workload("tiny", batch=2)
+    run_steps(wl, 3, teacher_force=True, ctx=[0, 16])
 
 
 def test_tiny_split_attention():
