@@ -3,8 +3,11 @@
 //
 // Scheduling follows "mostly static" scheduling (P3 "Scheduling and Performance Benchmarks"): the
 // host expands one decode step into tasks, groups them into topological levels (one parallel layer
-// = three levels: QKV/router -> attention/expert slices -> output rows) and deals each level's
-// tasks to the resident workers by a longest-first list schedule over an HBM-bytes cost model.
+// = four levels: QKV/router -> attention splits/expert slices -> attention merges -> output rows)
+// and deals each level's tasks to the resident workers by a longest-first list schedule over an
+// HBM-bytes cost model. At batch > 1 the expert slices are not dealt but drawn at run time from a
+// per-layer work queue (dynamic work stealing): which experts a step needs is known only after
+// the router.
 // Tile counts are derived from the worker count rather than a fixed tile, so a level never ends
 // with a partly filled wave of tiles (P1 "One persistent kernel for the whole decode step": wave
 // quantization). Attention is split per KV group so an output row waits only for the attention it

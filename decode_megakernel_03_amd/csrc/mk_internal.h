@@ -37,7 +37,9 @@ enum Op {
   OP_NOP = 0,
   OP_QKV = 1,     // a0 row0, a1 nrows: qkv[l][b][row] = W_qkv[row] . rmsnorm(x_l[b])
   OP_ROUTER = 2,  // a0 row0, a1 nrows, a2 router tiles: logits; the last tile routes (top-k)
-  OP_GATEUP = 3,  // a0 union slot, a1 f0, a2 nf: h = SiLU(W_gate n) * (W_up n) on rows f0..
+  OP_GATEUP = 3,  // static: a0 union slot, a1 f0, a2 nf, a3 -1: h = SiLU(W_gate n) * (W_up n) on rows f0..
+                  // queue: a0 own sub-queue, a1 sub-queues, a2 slices per slot, a3 queue counter,
+                  // a4 rows per slice: (slot, slice) items drawn from the layer's work queue
   OP_ATTN = 4,    // a0 b, a1 g, a2 k0, a3 k1 (-1 = to seq_len, the split holding the new token),
                   // a4 first partial of (b, g) in the layer, a5 split | nsplit << 16
   OP_OUT = 5,     // a0 row0, a1 nrows: x_{l+1} = x_l + W_o attn + sum_i w_i W_down[e_i] h_i

@@ -16,6 +16,7 @@ Workloads (shapes follow the parallel-MoE decoders the method is benchmarked on,
 * ``full_b8`` - the same model at batch 8, 8192 context each.
 * ``ragged``  - the same model at batch 8 with contexts log-uniform in [1024, 32768], shuffled
                 block tables and a Zipf(1.1) router bias.
+* ``ragged_uniform`` - the ragged batch without the router bias (uniform-routing control).
 * ``long``    - the same model at batch 1 with 262144 context.
 
 Distributions: weights N(0, 0.02) rounded to bf16; norm gains 1.0 (or U(0.5, 1.5) when asked,
@@ -69,6 +70,8 @@ WORKLOADS = {
     "full": Workload("full", **_FULL, batch=1, context=8192, steps=1024),
     "full_b8": Workload("full_b8", **_FULL, batch=8, context=8192, steps=1024),
     "ragged": Workload("ragged", **_FULL, batch=8, context=0, steps=1024, ragged=(1024, 32768), zipf_s=1.1),
+    # the uniform-routing control of the ragged batch (same contexts and pages, no router bias)
+    "ragged_uniform": Workload("ragged_uniform", **_FULL, batch=8, context=0, steps=1024, ragged=(1024, 32768)),
     "long": Workload("long", **_FULL, batch=1, context=262144, steps=256),
 }
 
