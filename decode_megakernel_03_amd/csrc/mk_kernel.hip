@@ -1054,27 +1054,19 @@ __device__ __forceinline__ bool op_attn(int task) {
   // they fall in wave 0's first rows, which take them in a few more registers instead of paying a
   // dependent round trip in the P V pass. (Its keys are loaded at the second score chunk: holding
   // them through the score pass as well would exceed the register budget.)
-  // With one token the values are requested only once the QKV rows are in: at the start of a
-  // layer the splits' keys and values would otherwise share HBM with the QKV tiles' weights, which
-  // are on the path to every split, while the values are first used several microseconds into the
-  // split (after the query load, the scores and the softmax).
-  constexpr bool V_EARLY = TB > 1;
+  load_k(0);
+  load_v(0);
   const bool tail = nchunk == 2 && nk - KC <= PAGE;    // uniform in the workgroup
   constexpr int VT_Q = PAGE / KPW;                     // V loads of wave 0 that hold the tail page
   u4 vtl[VT_Q];
-  auto load_v_tail = [&]() {
-    if (tail && wave == 0) {
+  if (tail && wave == 0) {
 #pragma unroll
-      for (int q = 0; q < VT_Q; ++q) {
-        const int jv = k0 + KC + KPW * q + lane / LPK;
-        vtl[q] = jv < kend ? ldw(Lp.v_cache + kaddr(jv, 8 * li)) : u4{0u, 0u, 0u, 0u};
-      }
+    for (int q = 0; q < VT_Q; ++q) {
+      const int jv = k0 + KC + KPW * q + lane / LPK;
+      vtl[q] = jv < kend ? ldw(Lp.v_cache + kaddr(jv, 8 * li)) : u4{0u, 0u, 0u, 0u};
     }
-  };
-  load_k(0);
-  if (V_EARLY) { load_v(0); load_v_tail(); }
+  }
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  if (!V_EARLY) { load_v(0); load_v_tail(); }
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + ((size_t)l * MAXB + b) * S::QKVR);
   const float rsd = 1.0f / sqrtf((float)D);
   // rotate-half RoPE of 4 dims d0..d0+3 (all on one side of D/2) given x and its partner dims y
