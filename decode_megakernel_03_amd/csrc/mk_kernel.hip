@@ -87,6 +87,8 @@ __device__ __forceinline__ void stc4(__amdgpu_buffer_rsrc_t r, uint32_t off, f4 
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u4, v), r, off, 0, SC1);
 }
 typedef const __attribute__((address_space(1))) u4 gu4;
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s lv4s;     // LDS pointer for the transpose reads
 
 // Step-constant tables (descriptors, queue bounds, layer pointers, per-step inputs) are read
 // through the constant address space so that uniform reads become scalar loads.
@@ -1264,19 +1266,24 @@ __device__ __forceinline__ bool op_attn(int task) {
           }
           pa = __builtin_bit_cast(bf8, u4{w[0], w[1], w[2], w[3]});
         }
-        // B operands: tile rows 8 grp .. + 7 of dimension 16 cb + col
+        // B operands: tile rows 8 grp .. + 7 of dimension 16 cb + col, by LDS transpose reads. In
+        // each group of 16 lanes the lanes' 8-byte addresses form a 4 x 16 block of 16-bit values
+        // and lane i receives column i of it: lane j supplies tile row 8 grp + j / 4 (+ 4 for the
+        // second read) at dimensions 16 cb + 4 (j % 4) .. + 3, so lane col receives the four
+        // consecutive keys of dimension 16 cb + col.
         const uint16_t* vt16 = reinterpret_cast<const uint16_t*>(vt);
+        const int trow = 8 * grp + (col >> 2), tdim = 4 * (col & 3);
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          uint32_t w[4];
-#pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            const uint32_t lo16 = vt16[(8 * grp + 2 * m) * (2 * VRS) + 16 * cb + col];
-            const uint32_t hi16 = vt16[(8 * grp + 2 * m + 1) * (2 * VRS) + 16 * cb + col];
-            w[m] = lo16 | (hi16 << 16);
-          }
-          oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf8, u4{w[0], w[1], w[2], w[3]}),
-                                                             oacc[cb], 0, 0, 0);
+          const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lv4s*)(vt16 + trow * (2 * VRS) + 16 * cb + tdim));
+          const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (lv4s*)(vt16 + (trow + 4) * (2 * VRS) + 16 * cb + tdim));
+          const u4 w = {(uint32_t)(uint16_t)r0.x | ((uint32_t)(uint16_t)r0.y << 16),
+                        (uint32_t)(uint16_t)r0.z | ((uint32_t)(uint16_t)r0.w << 16),
+                        (uint32_t)(uint16_t)r1.x | ((uint32_t)(uint16_t)r1.y << 16),
+                        (uint32_t)(uint16_t)r1.z | ((uint32_t)(uint16_t)r1.w << 16)};
+          oacc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf8, w), oacc[cb], 0, 0, 0);
         }
         asm volatile("" ::: "memory");
       }
