@@ -1175,32 +1175,33 @@ __device__ __forceinline__ bool op_attn(int task) {
         }
       snew = wsum<32>(t) * rsd;
     }
-    // 256 keys per pass: 8 independent LDS reads per lane (entries past nk are masked; the
-    // buffer has room for them)
+    // 256 keys per pass: each lane reads 8 consecutive keys as two 16-byte LDS reads (entries
+    // past nk are masked; the buffer has room for them)
     float m = snew;
     if (hv)
       for (int j0 = 0; j0 < nk; j0 += 256) {
-        float v[8];
+        const int jl = j0 + 8 * sl;
+        const f4 va = *reinterpret_cast<const f4*>(prow + jl), vb = *reinterpret_cast<const f4*>(prow + jl + 4);
+        const float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = prow[j0 + 32 * u + sl];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) m = j0 + 32 * u + sl < nk ? fmaxf(m, v[u]) : m;
+        for (int u = 0; u < 8; ++u) m = jl + u < nk ? fmaxf(m, v[u]) : m;
       }
     m = wmax<32>(m);
     float lsum = 0.f;
     if (hv)
       for (int j0 = 0; j0 < nk; j0 += 256) {
-        float v[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = prow[j0 + 32 * u + sl];
+        const int jl = j0 + 8 * sl;
+        const f4 va = *reinterpret_cast<const f4*>(prow + jl), vb = *reinterpret_cast<const f4*>(prow + jl + 4);
+        const float v[8] = {va.x, va.y, va.z, va.w, vb.x, vb.y, vb.z, vb.w};
+        float e[8];
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
-          const int j = j0 + 32 * u + sl;
-          if (j < nk) {
-            const float e = expf(v[u] - m);
-            prow[j] = e;
-            lsum += e;
-          }
+          e[u] = jl + u < nk ? expf(v[u] - m) : 0.f;
+          lsum += e[u];
+        }
+        if (jl < nk) {     // entries past nk are rewritten below (zeros and the new key)
+          *reinterpret_cast<f4*>(prow + jl) = f4{e[0], e[1], e[2], e[3]};
+          *reinterpret_cast<f4*>(prow + jl + 4) = f4{e[4], e[5], e[6], e[7]};
         }
       }
     lsum = wsum<32>(lsum);
