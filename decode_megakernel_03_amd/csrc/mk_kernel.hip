@@ -1346,7 +1346,10 @@ __device__ __forceinline__ bool op_merge(int task) {
   }
   const int o0 = q * ops, h0 = o0 / D;            // first output and first head of the slice
   const __amdgpu_buffer_rsrc_t P0 = rsrc(p.apart + ((size_t)l * p.parts_per_layer + pbase) * S::PART);
-  float* msl = sm;                                // [nsplit][2 nh]: m (then the scale) and l per head
+  // [2 nh][MERGE_MAX]: per head, m (then the scale) of every split, then l of every split (one head's
+  // splits contiguous, so that the combine reads its scales as 16-byte vectors)
+  constexpr int SST = MERGE_MAX;
+  float* msl = sm;
   float* linv = sm + MERGE_MAX * 2 * 2 * NWAVE;   // [nh] sum over splits of l * scale
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;   // every split of (b, g)
   const bool mine = tx < ops;
@@ -1356,7 +1359,7 @@ __device__ __forceinline__ bool op_merge(int task) {
   for (int u = 0; u < MB; ++u) ob[u] = (mine && u < nsplit) ? ldc(P0, 4u * (u * S::PART + 2 * HPG + o)) : 0.f;
   for (int i = tx; i < nsplit * 2 * nh; i += NT) {
     const int s2 = i / (2 * nh), j = i % (2 * nh);
-    msl[i] = ldc(P0, 4u * (s2 * S::PART + (j < nh ? h0 + j : HPG + h0 + j - nh)));
+    msl[j * SST + s2] = ldc(P0, 4u * (s2 * S::PART + (j < nh ? h0 + j : HPG + h0 + j - nh)));
   }
   __syncthreads();
   MARK(0);
@@ -1366,15 +1369,15 @@ __device__ __forceinline__ bool op_merge(int task) {
     const int h = 2 * wave + (lane >> 5), sl = lane & 31;
     float M = -INFINITY;
     if (h < nh)
-      for (int s2 = sl; s2 < nsplit; s2 += 32) M = fmaxf(M, msl[s2 * 2 * nh + h]);
+      for (int s2 = sl; s2 < nsplit; s2 += 32) M = fmaxf(M, msl[h * SST + s2]);
     M = wmax<32>(M);
     float Lsum = 0.f;
     if (h < nh)
       for (int s2 = sl; s2 < nsplit; s2 += 32) {
-        const float ms = msl[s2 * 2 * nh + h];
+        const float ms = msl[h * SST + s2];
         const float sc = ms == -INFINITY ? 0.f : expf(ms - M);
-        msl[s2 * 2 * nh + h] = sc;
-        Lsum = __builtin_fmaf(msl[s2 * 2 * nh + nh + h], sc, Lsum);
+        msl[h * SST + s2] = sc;
+        Lsum = __builtin_fmaf(msl[(nh + h) * SST + s2], sc, Lsum);
       }
     Lsum = wsum<32>(Lsum);
     if (h < nh && sl == 0) linv[h] = Lsum;
@@ -1388,9 +1391,13 @@ __device__ __forceinline__ bool op_merge(int task) {
 #pragma unroll
         for (int u = 0; u < MB; ++u) ob[u] = (s0 + u < nsplit) ? ldc(P0, 4u * ((s0 + u) * S::PART + 2 * HPG + o)) : 0.f;
       }
-      float sc[MB];                      // all scales first (independent LDS reads), then the sum
+      float sc[MB];                      // all scales first (16-byte LDS reads), then the sum
 #pragma unroll
-      for (int u = 0; u < MB; ++u) sc[u] = s0 + u < nsplit ? msl[(s0 + u) * 2 * nh + hh] : 0.f;
+      for (int u4 = 0; u4 < MB / 4; ++u4) {
+        const f4 v = *reinterpret_cast<const f4*>(msl + hh * SST + s0 + 4 * u4);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) sc[4 * u4 + c] = s0 + 4 * u4 + c < nsplit ? v[c] : 0.f;
+      }
 #pragma unroll
       for (int u = 0; u < MB; ++u) acc = __builtin_fmaf(ob[u], sc[u], acc);
     }
