@@ -1054,8 +1054,9 @@ __device__ __forceinline__ bool op_attn(int task) {
   // is in flight while the task waits for the QKV rows. When a second chunk holds at most one page
   // (splits a little longer than a chunk), that page's values are requested with the first chunk:
   // they fall in wave 0's first rows, which take them in a few more registers instead of paying a
-  // dependent round trip in the P V pass. (Its keys are loaded at the second score chunk: holding
-  // them through the score pass as well would exceed the register budget.)
+  // dependent round trip in the P V pass. (Its keys go to wave 0's first key registers once that
+  // block's first-chunk products are done: holding them from the start as well would exceed the
+  // register budget.)
   load_k(0);
   load_v(0);
   const bool tail = nchunk == 2 && nk - KC <= PAGE;    // uniform in the workgroup
@@ -1140,9 +1141,9 @@ __device__ __forceinline__ bool op_attn(int task) {
   MARK(0);
   // ---- pass A: s[j][hh] = (k_j . q_hh) / sqrt(D) on the matrix cores, cached keys j < nk
   for (int c = 0; c < nchunk; ++c) {
-    if (c > 0) {
-      load_k(c);
-    }
+    // a one-page second chunk is wave 0's first block only: its keys were requested into kr[0]
+    // right after that block's first-chunk products (below)
+    if (c > 0 && !tail) load_k(c);
 #pragma unroll
     for (int i = 0; i < GPW; ++i) {
       const int jb = c * KC + (wave + NWAVE * i) * 16;   // first key of the block, relative to k0
@@ -1151,6 +1152,12 @@ __device__ __forceinline__ bool op_attn(int task) {
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kb], __builtin_bit_cast(bf8, kr[i][kb]), acc, 0, 0, 0);
+      if (i == 0 && c == 0 && tail && wave == 0) {
+        const int jk = k0 + KC + col;
+#pragma unroll
+        for (int kb = 0; kb < KB; ++kb)
+          kr[0][kb] = jk < kend ? ldw(Lp.k_cache + kaddr(jk, 32 * kb + 8 * grp)) : u4{0u, 0u, 0u, 0u};
+      }
       if (2 * grp < HPG && jb + col < nk) {
         sbuf[(2 * grp) * PS + jb + col] = (acc[0] + acc[2]) * rsd;
         sbuf[(2 * grp + 1) * PS + jb + col] = (acc[1] + acc[3]) * rsd;
@@ -1312,10 +1319,14 @@ __device__ __forceinline__ bool op_attn(int task) {
   // partial of this split: m[HPG], l[HPG], o[HPG][D] (unnormalised)
   const size_t part = ((size_t)l * p.parts_per_layer + pbase + s_idx) * S::PART;
   const __amdgpu_buffer_rsrc_t Pw = rsrc(p.apart + part);
-  for (int i = tx; i < HPG * D; i += NT) {
-    float v = 0.f;
-    for (int w = 0; w < NWAVE; ++w) v += obuf[w * HPG * D + i];
-    stc(Pw, 4u * (2 * HPG + i), v);
+  static_assert((HPG * D) % 4 == 0, "");
+  for (int i = 4 * tx; i < HPG * D; i += 4 * NT) {      // four outputs per thread, waves summed in order
+    f4 v = {0.f, 0.f, 0.f, 0.f};
+    for (int w = 0; w < NWAVE; ++w) {
+      const f4 o = *reinterpret_cast<const f4*>(obuf + w * HPG * D + i);
+      v.x += o.x; v.y += o.y; v.z += o.z; v.w += o.w;
+    }
+    stc4(Pw, 4u * (2 * HPG + i), v);
   }
   if (tx < 2 * HPG) stc(Pw, 4u * tx, ml[tx]);
   MARK(4);
@@ -1508,8 +1519,8 @@ __device__ __forceinline__ bool op_out(int task) {
     stage_f4<AD>(a_s, At, 4u * (b * AD), AD);
     __syncthreads();
     if (b == 0) MARK(2);
-    compute_block<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
-                              [&](int r, int t, float v) { o_s[r] = v; });
+    compute_block_shared<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
+                                     [&](int r, int t, float v) { o_s[r] = v; });
     __syncthreads();
     if (tid() < nrows) {
       const int r = tid(), row = row0 + r;
