@@ -22,14 +22,16 @@ COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=
 SOURCES = ["mk_kernel.hip", "mk_host.cpp"]
 
 
-def build(verbose=True):
+def build(verbose=True, csrc=CSRC, out=LIB):
+    """Compile the sources in `csrc` (default: this package's csrc/) into the shared library `out`."""
+    common = [c if c != CSRC else csrc for c in COMMON]
     with tempfile.TemporaryDirectory() as tmp:
         objs = []
         procs = []
         for src in SOURCES:
             obj = os.path.join(tmp, src + ".o")
             lang = [] if src.endswith(".hip") else ["-x", "hip"]
-            cmd = [HIPCC] + COMMON + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+            cmd = [HIPCC] + common + lang + ["-c", os.path.join(csrc, src), "-o", obj]
             if verbose:
                 print(" ".join(cmd), flush=True)
             procs.append((subprocess.Popen(cmd), cmd))
@@ -37,13 +39,13 @@ def build(verbose=True):
         for pr, cmd in procs:
             if pr.wait() != 0:
                 raise RuntimeError("compile failed: " + " ".join(cmd))
-        tmp_lib = LIB + ".tmp"
+        tmp_lib = out + ".tmp"
         cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp_lib] + objs
         if verbose:
             print(" ".join(cmd), flush=True)
         subprocess.check_call(cmd)
-        os.replace(tmp_lib, LIB)
-    return LIB
+        os.replace(tmp_lib, out)
+    return out
 
 
 if __name__ == "__main__":

@@ -90,7 +90,8 @@ def load(path=LIB_PATH):
     return lib
 
 
-LIB = load()
+# MK_LIBRARY names another build of the same C ABI (e.g. to compare two builds in one process tree)
+LIB = load(os.environ.get("MK_LIBRARY", LIB_PATH))
 
 
 def _i32_array(values):
