@@ -389,9 +389,11 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   }
 
   // Every task pays a fixed latency (dependency poll, activation round trip, drain) worth about
-  // TASK_FIXED bytes of streaming at a worker's share of HBM bandwidth; attention also pays for
-  // its arithmetic (8 query heads per key on the vector units).
-  const int64_t TASK_FIXED = 96 * 1024;
+  // TASK_FIXED bytes of streaming; attention also pays for its arithmetic (8 query heads per key).
+  // The term is large on purpose: a second task on a worker in one level costs its hops in full,
+  // so the placement balances task counts first and bytes second (measured on MI355X: 48, 96, 192,
+  // 288, 384 KB -> 561, 563, 570, 574, 573 tok/s at batch 1; 288 KB also best at batch 8).
+  const int64_t TASK_FIXED = 288 * 1024;
   for (auto& lvl : levels)
     for (auto& pr : lvl) pr.bytes = pr.bytes * (pr.t.w[D_OP] == OP_ATTN ? 2 : 1) + TASK_FIXED;
   // placement: per level, longest task first onto the worker with the least load in that level;
