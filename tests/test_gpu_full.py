@@ -163,6 +163,19 @@ def test_full_model_batch1_8k():
         m.close()
 
 
+def test_full_model_batch1_256_greedy_steps():
+    """48-layer model, batch 1, 8192 context, 256 greedy steps on the device: steps 0, 127 and 255
+    checked against the oracle (teacher-forced on the GPU's tokens and KV state), the rest run
+    unchecked, so late steps (longer context, KV rows the kernel itself appended) are covered."""
+    say("test_full_model_batch1_256_greedy_steps")
+    m = Model(synth.workload("full"), steps=256)
+    try:
+        for s in range(256):
+            m.step_and_check(check=s in (0, 127, 255))
+    finally:
+        m.close()
+
+
 def test_full_model_batch8_8k():
     """48-layer model, batch 8, every sequence 8192 context: first step checked."""
     say("test_full_model_batch8_8k")
