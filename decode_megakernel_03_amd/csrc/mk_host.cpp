@@ -911,6 +911,38 @@ void mk_destroy(mk_engine* e) {
   delete e;
 }
 
+// ---- measurement helper ------------------------------------------------------------------
+
+mk_status mk_stream_read_bandwidth(const void* buf, size_t bytes, int32_t reps, double* bytes_per_s) {
+  if (!buf || bytes < 16 || reps < 1 || !bytes_per_s || ((uintptr_t)buf & 15u)) return MK_ERR_INVALID_ARG;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return MK_ERR_HIP;
+  uint32_t* sink = nullptr;
+  hipEvent_t a = nullptr, b = nullptr;
+  mk_status st = MK_OK;
+  const size_t n16 = bytes / 16;
+  const int blocks = 8 * ncu;
+  float ms = 0.f;
+  if (hipMalloc(&sink, sizeof(uint32_t)) != hipSuccess) return MK_ERR_OOM;
+  if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess ||
+      launch_stream_read(buf, n16, sink, blocks, nullptr) != hipSuccess ||      // warm-up pass
+      hipEventRecord(a, nullptr) != hipSuccess) {
+    st = MK_ERR_HIP;
+  } else {
+    for (int r = 0; r < reps && st == MK_OK; ++r)
+      if (launch_stream_read(buf, n16, sink, blocks, nullptr) != hipSuccess) st = MK_ERR_HIP;
+    if (st == MK_OK && (hipEventRecord(b, nullptr) != hipSuccess || hipEventSynchronize(b) != hipSuccess ||
+                        hipEventElapsedTime(&ms, a, b) != hipSuccess || ms <= 0.f))
+      st = MK_ERR_HIP;
+  }
+  if (st == MK_OK) *bytes_per_s = (double)(n16 * 16) * reps / (ms * 1e-3);
+  if (a) (void)hipEventDestroy(a);
+  if (b) (void)hipEventDestroy(b);
+  (void)hipFree(sink);
+  return st;
+}
+
 // ---- host-only schedule API ---------------------------------------------------------------
 
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* seq_lens_host, int32_t n_workers,

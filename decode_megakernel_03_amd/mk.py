@@ -23,7 +23,8 @@ DESC_WORDS = 16
 
 EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_decode_step", "mk_set_step_outputs",
             "mk_sync", "mk_get_error", "mk_reset", "mk_destroy", "mk_plan_build", "mk_plan_info_get",
-            "mk_plan_export", "mk_plan_validate", "mk_plan_simulate", "mk_engine_plan", "mk_plan_destroy"]
+            "mk_plan_export", "mk_plan_validate", "mk_plan_simulate", "mk_engine_plan", "mk_plan_destroy",
+            "mk_stream_read_bandwidth"]
 
 
 class MkError(RuntimeError):
@@ -82,6 +83,7 @@ def load(path=LIB_PATH):
         "mk_plan_simulate": [vp, u64, i32, i32, ctypes.c_char_p, sz],
         "mk_engine_plan": [vp],
         "mk_plan_destroy": [vp],
+        "mk_stream_read_bandwidth": [vp, sz, i32, ctypes.POINTER(ctypes.c_double)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -165,6 +167,14 @@ def mk_reset(h):
 
 def mk_destroy(h):
     LIB.mk_destroy(h)
+
+
+def mk_stream_read_bandwidth(buf_ptr, nbytes, reps=5):
+    """Streaming-read bandwidth (bytes/s) of the current device over a caller-owned device buffer."""
+    out = ctypes.c_double(0.0)
+    _check(LIB.mk_stream_read_bandwidth(ctypes.c_void_p(buf_ptr), ctypes.c_size_t(nbytes), int(reps), ctypes.byref(out)),
+           None, "mk_stream_read_bandwidth")
+    return out.value
 
 
 def mk_plan_build(desc, seq_lens, n_workers, split_keys=0, flags=0):

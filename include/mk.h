@@ -172,6 +172,14 @@ mk_status mk_reset(mk_engine* e);
 
 void mk_destroy(mk_engine* e);
 
+/* Measurement helper: the plain streaming-read bandwidth of the current device, a ceiling to set the
+ * step kernel's achieved bandwidth against. Reads `bytes` (rounded down to 16) from the device buffer
+ * `buf` (16-byte aligned, owned by the caller, not modified) `reps` times with 16-byte non-temporal
+ * loads on 8 workgroups per CU, after one untimed pass; *bytes_per_s = bytes read / elapsed time
+ * (HIP events on the default stream). Synchronous. MK_ERR_INVALID_ARG for a NULL or misaligned
+ * buffer, bytes < 16 or reps < 1; MK_ERR_HIP / MK_ERR_OOM on runtime failures. */
+mk_status mk_stream_read_bandwidth(const void* buf, size_t bytes, int32_t reps, double* bytes_per_s);
+
 /* ---- schedule inspection (host only: no GPU needed) -------------------------------------- */
 
 typedef struct {

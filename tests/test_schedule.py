@@ -222,3 +222,11 @@ def test_batch1_keeps_static_expert_slices():
     mk.mk_plan_destroy(plan)
     gu = tasks[tasks[:, 0] == 3]
     assert np.all(gu[:, 5] == -1) and len(gu) == 48 * 8 * len(set(gu[gu[:, 1] == 0][:, 3]))
+
+
+def test_stream_read_bandwidth_rejects_bad_arguments():
+    """The measurement helper validates its arguments before touching the GPU."""
+    for args in ((0, 1 << 20, 1), (16 + 4, 1 << 20, 1), (1 << 20, 8, 1), (1 << 20, 1 << 20, 0)):
+        with pytest.raises(mk.MkError) as e:
+            mk.mk_stream_read_bandwidth(*args)
+        assert e.value.status == mk.MK_ERR_INVALID_ARG
