@@ -166,7 +166,9 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // the last split keeps at least a quarter of SPLIT_MAX of room to grow before the schedule must
   // be rebuilt
   int maxlen = *std::max_element(seq_lens, seq_lens + B);
-  int split = split_req > 0 ? split_req : 256;
+  // (with several sequences the splits alone fill the workers: two 256-key chunks per split halve
+  // their count, measured +4 % at batch 8 over 256 keys; 384 and 768 keys were slower)
+  int split = split_req > 0 ? split_req : (B > 1 ? 512 : 256);
   split = std::max(split, (int)ceil_div(ceil_div(maxlen, merge_max() - 8), 16) * 16);
   split = std::max(16, std::min(split, 3 * SPLITMAX / 4));
   split = (split + 15) / 16 * 16;
@@ -176,6 +178,9 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   const int64_t gu_target = std::max<int64_t>(slots, W - splits_for(split));
   int nf = (int)ceil_div(m.F, std::max<int64_t>(1, gu_target / slots));
   nf = std::max(4, std::min(32, nf));   // at most 256 KB of gate + up per task (balance at large batches)
+  // with several sequences the slices are queue items: 16 rows, which the kernel takes two at a time
+  // when the step's union is large (see the expert queue in the kernel)
+  if (B > 1 && !(flags & MK_FLAG_STATIC_EXPERTS)) nf = 16;
   if (align > 1) nf = std::max(align, (nf + align / 2) / align * align);
   const int slices = (int)ceil_div(m.F, nf);
   // if slices and splits then exceed one task per worker, lengthen the splits (up to twice the

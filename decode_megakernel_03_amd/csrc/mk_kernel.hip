@@ -858,7 +858,13 @@ __device__ __forceinline__ bool op_gateup(int task) {
   if (!dyn) {
     if (T.a0 < nu) run_item(T.a0, T.a1, T.a2);
   } else {
-    const int slices = T.a2, nfs = T.a4, n_items = nu * slices;
+    // item size from the step's union: with at least four slices per worker, a draw takes two
+    // adjacent slices (fewer draws and larger streams); a small union (skewed routing) keeps
+    // single slices so that the work spreads over more workers. Every task derives the same grain.
+    const int slices = T.a2, nfs = T.a4;
+    const int grain = (nu * slices >= 4 * p.n_workers && 2 * nfs <= 32) ? 2 : 1;
+    const int slices_c = (slices + grain - 1) / grain, rows = grain * nfs;
+    const int n_items = nu * slices_c;
     // hand the draw to the workgroup, with the sub-queue that had the most items left in the
     // snapshot (-1: none had any)
     auto publish = [&]() {
@@ -889,8 +895,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
         continue;
       }
       draw(sq);                         // the next draw, in flight during the item
-      const int u = i / slices, j = i - u * slices, f0 = j * nfs;
-      run_item(u, f0, F - f0 < nfs ? F - f0 : nfs);
+      const int u = i / slices_c, j = i - u * slices_c, f0 = j * rows;
+      run_item(u, f0, F - f0 < rows ? F - f0 : rows);
       publish();
     }
   }

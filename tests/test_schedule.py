@@ -210,8 +210,17 @@ def test_expert_queue_runs_every_item_once(name, lens, workers):
     rng = np.random.default_rng(0)
     slots = min(wl.n_experts, wl.top_k * len(lens))
     for nu in sorted({wl.top_k, (wl.top_k + slots) // 2, slots}):
-        runs = _drain_queue(list(gu[:, 2]), nq, nu * slices, rng)
+        # the kernel's item size: two adjacent slices per draw once there are 4 slices per worker
+        grain = 2 if nu * slices >= 4 * workers and 2 * nfs <= 32 else 1
+        slices_c = -(-slices // grain)
+        runs = _drain_queue(list(gu[:, 2]), nq, nu * slices_c, rng)
         assert np.all(runs == 1)
+        # the items of a slot cover its FFN rows exactly once
+        rows = np.zeros(wl.expert_ffn, dtype=int)
+        for j in range(slices_c):
+            f0 = j * grain * nfs
+            rows[f0:min(wl.expert_ffn, f0 + grain * nfs)] += 1
+        assert np.all(rows == 1)
 
 
 def test_batch1_keeps_static_expert_slices():
