@@ -433,12 +433,63 @@ __device__ __forceinline__ void compute_block(const WBuf<KD, NP>& b, int blk, in
 // input vector per token): each 16-byte activation read from LDS serves all NP passes of the block,
 // so a batch of TB tokens reads LDS NP times less. Per row, the products are summed in the same
 // order as compute_block.
-template <int KD, int NP, int TB, class ActOf, class Emit>
+//
+// TG = 2 (every token of the batch multiplies every row: QKV, router): tokens are taken in pairs, so
+// that each weight is unpacked from bf16 once per pair (the GEMV is bound by vector-ALU issue at 8
+// tokens). A pair is computed whole once its first token is in range (act_of must return readable
+// LDS for every t < TB); the second token's result is emitted only if it is in range. Same per-row
+// order of products.
+template <int KD, int NP, int TB, int TG = 1, class ActOf, class Emit>
 __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int blk, int nrows, int ntok,
                                                      ActOf act_of, Emit emit) {
   using G = Geo<KD>;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
+  if constexpr (TG == 2) {
+    static_assert(TB % 2 == 0, "");
+#pragma unroll
+    for (int t0 = 0; t0 < TB; t0 += 2) {
+      if (t0 < ntok) {
+        const float* pa = act_of(0, t0) + 8 * lir;
+        const float* pb = act_of(0, t0 + 1) + 8 * lir;
+        float acc0[NP], acc1[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) { acc0[i] = 0.f; acc1[i] = 0.f; }
+#pragma unroll
+        for (int j = 0; j < G::CPL; ++j) {
+          const f4* qa = reinterpret_cast<const f4*>(pa + 8 * G::LPR * j);
+          const f4* qb = reinterpret_cast<const f4*>(pb + 8 * G::LPR * j);
+          const f4 a0 = qa[0], a1 = qa[1], b0 = qb[0], b1 = qb[1];
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            const u4 w = b.w[i][j];
+            const float wf[8] = {bf_lo(w.x), bf_hi(w.x), bf_lo(w.y), bf_hi(w.y),
+                                 bf_lo(w.z), bf_hi(w.z), bf_lo(w.w), bf_hi(w.w)};
+            float x = acc0[i], y = acc1[i];
+            x = __builtin_fmaf(wf[0], a0.x, x); y = __builtin_fmaf(wf[0], b0.x, y);
+            x = __builtin_fmaf(wf[1], a0.y, x); y = __builtin_fmaf(wf[1], b0.y, y);
+            x = __builtin_fmaf(wf[2], a0.z, x); y = __builtin_fmaf(wf[2], b0.z, y);
+            x = __builtin_fmaf(wf[3], a0.w, x); y = __builtin_fmaf(wf[3], b0.w, y);
+            x = __builtin_fmaf(wf[4], a1.x, x); y = __builtin_fmaf(wf[4], b1.x, y);
+            x = __builtin_fmaf(wf[5], a1.y, x); y = __builtin_fmaf(wf[5], b1.y, y);
+            x = __builtin_fmaf(wf[6], a1.z, x); y = __builtin_fmaf(wf[6], b1.z, y);
+            x = __builtin_fmaf(wf[7], a1.w, x); y = __builtin_fmaf(wf[7], b1.w, y);
+            acc0[i] = x; acc1[i] = y;
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
+          const float v0 = wsum<G::LPR>(acc0[i]), v1 = wsum<G::LPR>(acc1[i]);
+          if (lir == 0 && r < nrows) {
+            emit(r, t0, v0);
+            if (t0 + 1 < ntok) emit(r, t0 + 1, v1);
+          }
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     if (t < ntok) {
@@ -465,7 +516,7 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int 
 
 // Stream `nrows` rows; block 0 may already be loaded into A (prefetched before a dependency wait).
 // The activations are shared by all rows (ActOf ignores its row argument).
-template <int KD, int NP, int TB, class RowPtr, class ActOf, class Emit>
+template <int KD, int NP, int TB, int TG = 1, class RowPtr, class ActOf, class Emit>
 __device__ __forceinline__ void gemv_stream(WBuf<KD, NP>& A, bool a_loaded, int nrows, int ntok,
                                             RowPtr rowptr, ActOf act_of, Emit emit) {
   const int nblk = (nrows + block_rows<KD, NP>() - 1) / block_rows<KD, NP>();
@@ -473,10 +524,10 @@ __device__ __forceinline__ void gemv_stream(WBuf<KD, NP>& A, bool a_loaded, int 
   if (!a_loaded) load_block<KD, NP>(A, 0, nrows, rowptr);
   for (int blk = 0; blk < nblk; blk += 2) {
     if (blk + 1 < nblk) load_block<KD, NP>(B, blk + 1, nrows, rowptr);
-    compute_block_shared<KD, NP, TB>(A, blk, nrows, ntok, act_of, emit);
+    compute_block_shared<KD, NP, TB, TG>(A, blk, nrows, ntok, act_of, emit);
     if (blk + 1 < nblk) {
       if (blk + 2 < nblk) load_block<KD, NP>(A, blk + 2, nrows, rowptr);
-      compute_block_shared<KD, NP, TB>(B, blk + 1, nrows, ntok, act_of, emit);
+      compute_block_shared<KD, NP, TB, TG>(B, blk + 1, nrows, ntok, act_of, emit);
     }
   }
 }
@@ -580,7 +631,7 @@ __device__ __forceinline__ bool op_qkv(int task) {
   stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
   MARK(0);
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + (size_t)T.layer * MAXB * S::QKVR);
-  gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<H, NP, TB, (TB > 1 ? 2 : 1)>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); });
   MARK(1);
@@ -737,7 +788,7 @@ __device__ __forceinline__ bool op_router(int task) {
   MARK(0);
   const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)T.layer * MAXB * E);
   const float* bias = p.has_bias ? Lp.router_bias : nullptr;
-  gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<H, NP, TB, (TB > 1 ? 2 : 1)>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) {
         const int e = row0 + r;
