@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-b8", action="store_true", help="with the default workload, skip the batch-8 line in the JSON")
-    ap.add_argument("--trace", default="", help="after timing, trace one step and write a summary + Chrome JSON here")
+    ap.add_argument("--trace", default="", help="write the traced step's summary (.txt), records (.npy) and Chrome JSON here")
+    ap.add_argument("--no-trace-stats", action="store_true", help="skip the traced step after timing")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (for scaling HBM counters)")
     return ap.parse_args()
@@ -93,8 +94,11 @@ def main():
     step_ms, span_ms, tok_s, achieved, sol_frac = r["step_ms"], r["span_ms"], r["tok_s"], r["achieved"], r["sol_frac"]
     timed_bytes, union, topk_h, logits0, tok0, kv_host0 = r["timed_bytes"], r["union"], r["topk_h"], r["logits0"], r["tok0"], r["kv_host0"]
     tokens, pos_all, bt, len_all, logits, h, total_steps = r["loop"]
-    if args.trace:
-        run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps)
+    # where the workers' time goes (executing / spinning on counters / idle), from one traced step
+    # after the timed ones (tracing adds a little time per task, so it is kept out of the timing)
+    sched = None
+    if not args.no_trace_stats:
+        sched = run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps, args.trace)
 
     traffic = None
     prof = os.path.join(ROOT, "profiles", f"traffic_{wl.name}_b{B}.json")
@@ -133,28 +137,41 @@ def main():
                      "frac": round(achieved / PEAK_HBM, 4), "traffic": traffic},
         "cpu_baseline": cpu,
         "parity_first_step": parity,
+        "schedule": sched,
+        "schedule_rebuilds_in_timed_steps": len([s for s in r["rebuilds"] if s >= args.warmup]),
     }
+    # release the engine and every device buffer of this workload now, while the runtime (and any
+    # profiler attached to it) is up, instead of leaving them to interpreter shutdown
     eng.close()
+    del r, w, eng, tokens, pos_all, bt, len_all, logits, kv_host0
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     # the metric is quoted at batch 1 and batch 8: the batch-8 figure of the same model and context
     # joins the line (its own engine, inputs and timing; value above stays the batch-1 workload)
     if args.workload == "full" and args.batch in (0, 1) and not args.no_b8:
-        del r, w
-        torch.cuda.empty_cache()
         wl8 = synth.workload("full_b8")
         r8 = measure(wl8, args, 16, 4)
+        sched8 = None
+        if not args.no_trace_stats:
+            sched8 = run_trace(args, r8["eng"], *r8["loop"], path=(args.trace + "_b8") if args.trace else "")
         r8["eng"].close()
+        r8["eng"] = r8["w"] = r8["loop"] = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
         out["bs8"] = {"workload": f"{wl8.name}: batch 8, context {int(r8['ctx'].max())} each",
                       "value": round(r8["tok_s"], 2), "unit": "tok/s", "steps": 16, "warmup": 4,
                       "ms_per_step": round(r8["span_ms"] / 16, 4), "sol_fraction": round(r8["sol_frac"], 4),
                       "bytes_per_step": int(r8["timed_bytes"].mean()),
                       "experts_union_mean": round(float(r8["union"][4:].mean()), 2),
-                      "roofline_frac": round(r8["achieved"] / PEAK_HBM, 4)}
+                      "roofline_frac": round(r8["achieved"] / PEAK_HBM, 4), "schedule": sched8}
+        del r8
     # the measured streaming-read ceiling of this machine, next to the 8 TB/s figure
     ceil = read_ceiling()
     out["hbm_read_ceiling"] = {"value": round(ceil / 1e9, 1), "unit": "GB/s",
                                "method": "mk_stream_read_bandwidth: 4 GiB streamed 5 times after one warm-up pass"}
     out["roofline"]["frac_of_read_ceiling"] = round(achieved / ceil, 4)
     print(json.dumps(out), flush=True)
+    torch.cuda.synchronize()
 
 
 def read_ceiling(nbytes=4 << 30, reps=5):
@@ -213,6 +230,7 @@ def measure(wl, args, steps, warmup, keep_kv_host=False):
     logits0 = None
     stream = torch.cuda.current_stream()
     h = stream.cuda_stream
+    rebuilds = []
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
     for s in range(total_steps):
@@ -223,6 +241,13 @@ def measure(wl, args, steps, warmup, keep_kv_host=False):
             t_wall = time.perf_counter()
         starts[s].record(stream)
         st = mk.mk_decode_step(eng.h, tokens, pos_all[s], bt, len_all[s], logits, h)
+        if st == mk.MK_ERR_SCHEDULE_STALE:
+            # a sequence outgrew the attention splits' room: rebuild for the current lengths (host
+            # work inside the timed region, as a serving loop would pay it) and issue the step again
+            mk.mk_build_schedule(eng.h, (ctx + 1 + s).tolist())
+            rebuilds.append(s)
+            log(f"[bench] step {s}: schedule rebuilt for lengths {(ctx + 1 + s).tolist()[:4]}")
+            st = mk.mk_decode_step(eng.h, tokens, pos_all[s], bt, len_all[s], logits, h)
         ends[s].record(stream)
         if st != mk.MK_OK:
             raise mk.MkError(st, mk.mk_get_error(eng.h)[1])
@@ -249,12 +274,14 @@ def measure(wl, args, steps, warmup, keep_kv_host=False):
         f"{achieved / 1e9:.0f} GB/s per launch ({achieved / PEAK_HBM:.1%} of 8 TB/s)")
     return {"eng": eng, "info": info, "ctx": ctx, "bt_np": bt_np, "w": w, "step_ms": step_ms, "span_ms": span_ms,
             "tok_s": tok_s, "achieved": achieved, "sol_frac": sol_frac, "timed_bytes": timed_bytes, "union": union,
-            "topk_h": topk_h, "logits0": logits0, "tok0": tok0, "kv_host0": kv_host0,
+            "topk_h": topk_h, "logits0": logits0, "tok0": tok0, "kv_host0": kv_host0, "rebuilds": rebuilds,
             "loop": (tokens, pos_all, bt, len_all, logits, h, total_steps)}
 
 
-def run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps):
-    """One more step with per-task timestamps; summary to stderr, records + Chrome JSON to files."""
+def run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps, path=""):
+    """One more step with per-task timestamps (after an untimed traced warm-up step): returns the
+    time shares of trace.fractions; with `path`, also writes the text summary, the records and a
+    Chrome JSON there."""
     import torch
     from decode_megakernel_03_amd import mk, trace
     info = eng.plan_info()
@@ -268,14 +295,21 @@ def run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps):
             raise mk.MkError(st, mk.mk_get_error(eng.h)[1])
         torch.cuda.synchronize()
     eng.sync()
+    mk.mk_set_options(eng.h, flags=args.flags)
+    mk.mk_set_step_outputs(eng.h, argmax_out=tokens)
     tr = buf.cpu().numpy().view(np.uint64)
+    del buf
     tasks, qoff = mk.mk_plan_export(mk.mk_engine_plan(eng.h))
     rec = trace.decode(tr, tasks)
-    log(trace.summary(rec, info.n_workers))
-    os.makedirs(os.path.dirname(os.path.abspath(args.trace)), exist_ok=True)
-    np.save(args.trace + ".npy", rec)
-    trace.chrome_json(rec, args.trace + ".json")
-    mk.mk_set_options(eng.h, flags=args.flags)
+    summ = trace.summary(rec, info.n_workers)
+    log(summ)
+    if path:
+        os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
+        with open(path + ".txt", "w") as f:
+            f.write(summ + "\n")
+        np.save(path + ".npy", rec)
+        trace.chrome_json(rec, path + ".json")
+    return trace.fractions(rec, info.n_workers)
 
 
 def cpu_baseline(wl, w, kv0, tokens, ctx, bt, logits_gpu, topk_gpu):

@@ -948,6 +948,33 @@ mk_status mk_stream_read_bandwidth(const void* buf, size_t bytes, int32_t reps, 
   return st;
 }
 
+mk_status mk_handoff_litmus(int32_t rounds, int32_t words, int32_t workgroups, uint64_t* stale, uint64_t* checked) {
+  if (!stale || !checked || rounds < 1 || rounds > 100000 || words < 1 || words > 65536 || workgroups < 2)
+    return MK_ERR_INVALID_ARG;
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      litmus_occupancy(&per_cu) != hipSuccess)
+    return MK_ERR_HIP;
+  if (workgroups > ncu * per_cu) return MK_ERR_INVALID_ARG;      // every workgroup must be co-resident
+  uint32_t *data = nullptr, *ctl = nullptr;
+  if (hipMalloc(&data, sizeof(uint32_t) * (size_t)words) != hipSuccess) return MK_ERR_OOM;
+  // flag, done and res on lines of their own (256 bytes apart)
+  if (hipMalloc(&ctl, 3 * 256) != hipSuccess) { (void)hipFree(data); return MK_ERR_OOM; }
+  mk_status st = MK_OK;
+  uint32_t res[4] = {0, 0, 0, 0};
+  if (hipMemset(data, 0, sizeof(uint32_t) * (size_t)words) != hipSuccess || hipMemset(ctl, 0, 3 * 256) != hipSuccess ||
+      launch_litmus(data, ctl, ctl + 64, ctl + 128, rounds, words, workgroups, 100000000ull /* 1 s */, nullptr) != hipSuccess ||
+      hipDeviceSynchronize() != hipSuccess || hipMemcpy(res, ctl + 128, sizeof res, hipMemcpyDeviceToHost) != hipSuccess)
+    st = MK_ERR_HIP;
+  (void)hipFree(data);
+  (void)hipFree(ctl);
+  if (st != MK_OK) return st;
+  *stale = res[0];
+  *checked = res[1];
+  if (res[3] != 0 || (int32_t)res[2] != rounds) return MK_ERR_DEVICE;   // a wait hit the watchdog
+  return MK_OK;
+}
+
 // ---- host-only schedule API ---------------------------------------------------------------
 
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* seq_lens_host, int32_t n_workers,

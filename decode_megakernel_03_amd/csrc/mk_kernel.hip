@@ -1952,6 +1952,81 @@ hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, int b
   return hipGetLastError();
 }
 
+// Hand-off litmus test of the step kernel's protocol, across every XCD: in round r one workgroup
+// (the producer, a different one each round) writes `words` words = r with sc1 stores, waits for
+// them (s_waitcnt vmcnt(0)), passes a workgroup barrier and bumps `flag` with one relaxed
+// agent-scope atomic add - exactly what a task does before signalling. Every other workgroup polls
+// `flag` from wave 0 with relaxed agent-scope loads, passes a barrier and reads the words with sc1
+// loads - exactly what a task does after its dependency wait - and counts words that are not r
+// (stale). A consumer then bumps `done`; the next producer waits for every consumer of the previous
+// round before it overwrites the words. Every wait is bounded by the watchdog (res[3] set, and every
+// workgroup leaves its loop once it sees that), so the grid always drains.
+// res: [0] stale words, [1] words checked, [2] rounds completed by workgroup 0, [3] watchdog fired.
+__device__ bool litmus_wait(uint32_t* c, uint32_t target, uint32_t* res, uint64_t wd) {
+  __shared__ int ok_s;
+  const int tx = tid(), lane = tx & 63;
+  if (__builtin_amdgcn_readfirstlane(tx >> 6) == 0) {
+    int ok = 1;
+    const uint64_t t0 = now();
+    uint32_t it = 0;
+    while (__builtin_amdgcn_readfirstlane(ctr_load(c)) < target) {
+      __builtin_amdgcn_s_sleep(1);
+      if ((++it & 15u) == 0) {
+        if (__builtin_amdgcn_readfirstlane(ctr_load(res + 3)) != 0u) { ok = 0; break; }
+        if (now() - t0 > wd) {
+          if (lane == 0) __hip_atomic_store(res + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          ok = 0;
+          break;
+        }
+      }
+    }
+    if (lane == 0) ok_s = ok;
+  }
+  __syncthreads();
+  const bool ok = ok_s != 0;
+  __syncthreads();
+  return ok;
+}
+
+__global__ void __launch_bounds__(NT) handoff_litmus(uint32_t* data, uint32_t* flag, uint32_t* done, uint32_t* res,
+                                                     int rounds, int words, uint64_t wd) {
+  const int G = (int)gridDim.x, me = (int)blockIdx.x, tx = tid();
+  const __amdgpu_buffer_rsrc_t Dt = rsrc(data);
+  uint32_t stale = 0, checked = 0;
+  int r = 1;
+  for (; r <= rounds; ++r) {
+    const int prod = (int)(((unsigned)r * 37u + 11u) % (unsigned)G);
+    if (me == prod) {
+      if (!litmus_wait(done, (uint32_t)(G - 1) * (uint32_t)(r - 1), res, wd)) break;
+      for (int i = tx; i < words; i += NT) stci(Dt, 4u * i, r);
+      drain();
+      __syncthreads();
+      if (tx == 0) ctr_add(flag, 1u);
+    } else {
+      if (!litmus_wait(flag, (uint32_t)r, res, wd)) break;
+      for (int i = tx; i < words; i += NT) {
+        stale += ldci(Dt, 4u * i) != r ? 1u : 0u;
+        ++checked;
+      }
+      __syncthreads();                 // every thread of the consumer has read the round's words
+      if (tx == 0) ctr_add(done, 1u);
+    }
+  }
+  if (stale) atomicAdd(res + 0, stale);
+  if (checked) atomicAdd(res + 1, checked);
+  if (me == 0 && tx == 0) atomicAdd(res + 2, (uint32_t)(r - 1));
+}
+
+hipError_t launch_litmus(uint32_t* data, uint32_t* flag, uint32_t* done, uint32_t* res, int rounds, int words,
+                         int grid, uint64_t wd_ticks, hipStream_t st) {
+  void* args[] = {&data, &flag, &done, &res, &rounds, &words, &wd_ticks};
+  return hipLaunchCooperativeKernel((const void*)handoff_litmus, dim3(grid), dim3(NT), args, 0, st);
+}
+
+hipError_t litmus_occupancy(int* blocks_per_cu) {
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)handoff_litmus, NT, 0);
+}
+
 int split_max() { return SPLIT_MAX; }
 int merge_max() { return MERGE_MAX; }
 int out_max_rows() { return OUT_MAXR; }

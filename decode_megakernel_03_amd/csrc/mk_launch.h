@@ -16,4 +16,8 @@ int merge_max();      // attention splits one (sequence, KV group) may have
 int out_max_rows();   // rows of one OUT task
 // plain streaming read of n16 16-byte words on `blocks` workgroups of 256 threads (measurement)
 hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, int blocks, hipStream_t st);
+// hand-off litmus test (cooperative launch of `grid` workgroups of 256 threads); res[4] as documented
+hipError_t launch_litmus(uint32_t* data, uint32_t* flag, uint32_t* done, uint32_t* res, int rounds, int words,
+                         int grid, uint64_t wd_ticks, hipStream_t st);
+hipError_t litmus_occupancy(int* blocks_per_cu);
 }  // namespace mk

@@ -8,6 +8,7 @@ torch tensors it points at alive.
 
 import ctypes
 import os
+import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libmk.so")
@@ -24,7 +25,7 @@ DESC_WORDS = 16
 EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_decode_step", "mk_set_step_outputs",
             "mk_sync", "mk_get_error", "mk_reset", "mk_destroy", "mk_plan_build", "mk_plan_info_get",
             "mk_plan_export", "mk_plan_validate", "mk_plan_simulate", "mk_engine_plan", "mk_plan_destroy",
-            "mk_stream_read_bandwidth"]
+            "mk_stream_read_bandwidth", "mk_handoff_litmus"]
 
 
 class MkError(RuntimeError):
@@ -84,6 +85,7 @@ def load(path=LIB_PATH):
         "mk_engine_plan": [vp],
         "mk_plan_destroy": [vp],
         "mk_stream_read_bandwidth": [vp, sz, i32, ctypes.POINTER(ctypes.c_double)],
+        "mk_handoff_litmus": [i32, i32, i32, ctypes.POINTER(u64), ctypes.POINTER(u64)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -177,6 +179,13 @@ def mk_stream_read_bandwidth(buf_ptr, nbytes, reps=5):
     return out.value
 
 
+def mk_handoff_litmus(rounds, words, workgroups):
+    """Hand-off protocol self-test; returns (status, stale words, words checked)."""
+    stale, checked = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    st = LIB.mk_handoff_litmus(int(rounds), int(words), int(workgroups), ctypes.byref(stale), ctypes.byref(checked))
+    return st, stale.value, checked.value
+
+
 def mk_plan_build(desc, seq_lens, n_workers, split_keys=0, flags=0):
     h = ctypes.c_void_p()
     _check(LIB.mk_plan_build(ctypes.byref(desc), len(seq_lens), _i32_array(seq_lens), int(n_workers),
@@ -261,15 +270,27 @@ class Engine:
 
     def build_schedule(self, seq_lens):
         mk_build_schedule(self.h, list(seq_lens))
+        self._lens = [int(v) for v in seq_lens]
+        self._steps = 0
+        self.rebuilds = 0
 
     def set_step_outputs(self, **kw):
         self._outs = kw
         mk_set_step_outputs(self.h, **kw)
 
     def step(self, tokens, positions, block_tables, seq_lens, logits_out, stream=None):
+        """One decode step. Every sequence grows by one token per step; when a sequence would outgrow
+        the schedule's attention-split capacity the library refuses the step before launching it
+        (MK_ERR_SCHEDULE_STALE), and the schedule is rebuilt for the current lengths and the step
+        is issued again."""
         st = mk_decode_step(self.h, tokens, positions, block_tables, seq_lens, logits_out, stream)
+        if st == MK_ERR_SCHEDULE_STALE and getattr(self, "_lens", None) is not None:
+            self.build_schedule([n + self._steps for n in self._lens])
+            self.rebuilds += 1
+            st = mk_decode_step(self.h, tokens, positions, block_tables, seq_lens, logits_out, stream)
         if st != MK_OK:
             _check(st, self.h, "mk_decode_step")
+        self._steps += 1
 
     def sync(self):
         st = mk_sync(self.h)
@@ -288,6 +309,10 @@ class Engine:
             self.h = None
 
     def __del__(self):
+        # at interpreter shutdown the HIP runtime (and a profiler attached to it) may already be torn
+        # down: leave the engine to process exit then, and never call into the library
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:

@@ -94,6 +94,34 @@ def summary(rec, n_workers):
     return "\n".join(lines)
 
 
+def fractions(rec, n_workers):
+    """Where the workers' time went in a traced step: each worker's share of the step span spent
+    executing tasks (dependency met -> task end), spinning on dependency counters (task start ->
+    dependency met; the task's first weight block is already in flight then) and idle (between
+    tasks, and after its queue ends while others still run). Also the mean layer time, the polls
+    per dependency wait and the executed time of each op as a share of all executed time."""
+    t0, t1 = rec["start"].min(), rec["end"].max()
+    span = t1 - t0
+    exec_w = np.zeros(n_workers)
+    spin_w = np.zeros(n_workers)
+    np.add.at(exec_w, rec["worker"], rec["end"] - rec["ready"])
+    np.add.at(spin_w, rec["worker"], rec["ready"] - rec["start"])
+    tot = span * n_workers
+    out = {"traced_step_us": round(float(span), 1),
+           "worker_exec_frac": round(float(exec_w.sum() / tot), 4),
+           "worker_spin_frac": round(float(spin_w.sum() / tot), 4),
+           "worker_idle_frac": round(float(1.0 - (exec_w.sum() + spin_w.sum()) / tot), 4),
+           "polls_per_wait": round(float(np.mean(rec["polls"])), 2)}
+    ex = rec["end"] - rec["ready"]
+    out["exec_share_by_op"] = {name: round(float(ex[rec["op"] == op].sum() / ex.sum()), 4)
+                               for op, name in OPS.items() if (rec["op"] == op).any()}
+    ends = [rec["end"][(rec["layer"] == l) & (rec["op"] == 5)].max()
+            for l in sorted(set(rec["layer"].tolist())) if ((rec["layer"] == l) & (rec["op"] == 5)).any()]
+    if len(ends) > 2:
+        out["mean_layer_us"] = round(float(np.mean(np.diff(ends))), 2)
+    return out
+
+
 def chrome_json(rec, path):
     ev = []
     for r in rec:

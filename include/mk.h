@@ -124,7 +124,11 @@ typedef struct {
  * weights. Uses the current HIP device. *out is set only on MK_OK. */
 mk_status mk_create(const mk_model_desc* desc, const mk_weight_ptrs* weights, mk_engine** out);
 
-/* Set tuning options; takes effect at the next mk_build_schedule. */
+/* Set tuning options; takes effect at the next mk_build_schedule. The knobs are the scheduler's:
+ * resident workers per CU, attention split length, the bound on a dependency wait, and flags for
+ * tracing and ablations (P3 "Scheduling and Performance Benchmarks": mostly static scheduling with
+ * dynamic work stealing). MK_ERR_INVALID_ARG for NULL arguments or values out of range
+ * (workers_per_cu > 4, negative fields); the engine's options are then unchanged. */
 mk_status mk_set_options(mk_engine* e, const mk_options* opt);
 
 /* Build the static task schedule for `batch` sequences whose current lengths (host int32 [batch],
@@ -134,7 +138,10 @@ mk_status mk_set_options(mk_engine* e, const mk_options* opt);
  * Synchronous; call again when the batch composition changes. */
 mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens_host);
 
-/* Enqueue one decode step on `stream` (a hipStream_t; NULL = default stream). Device pointers:
+/* Enqueue one decode step on `stream` (a hipStream_t; NULL = default stream): the whole forward
+ * pass of every sequence of the batch as ONE kernel launch (P1 "One persistent kernel for the whole
+ * decode step"; P3 "Key Technologies and Architecture"), reading the paged KV cache through the
+ * block tables (P1 "From demo to a full serving system"). Device pointers, all caller-owned:
  *   tokens int32 [B]                 token being decoded per sequence
  *   positions int32 [B]              its position; must equal seq_lens[b] - 1
  *   block_tables int32 [B, max_pages_per_seq]  page ids; entries past ceil(seq_len/16) unread
@@ -142,13 +149,21 @@ mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens
  *   logits_out float32 [B, V]        written (may be NULL when has_lm_head = 0)
  * The new K/V of every sequence is written into the caches at its position before attention.
  * Asynchronous: returns after the launch. Device-side faults surface as MK_ERR_DEVICE from the
- * next mk_decode_step / mk_sync / mk_get_error. Host-side checks: MK_ERR_NO_SCHEDULE,
- * MK_ERR_SCHEDULE_STALE (lengths tracked on the host from the schedule, +1 per step). */
+ * next mk_decode_step / mk_sync / mk_get_error. Host-side checks, all before anything is launched:
+ * MK_ERR_INVALID_ARG (NULL engine or input, NULL logits_out with an lm_head), MK_ERR_NO_SCHEDULE (no
+ * mk_build_schedule yet), MK_ERR_SCHEDULE_STALE (a sequence would outgrow the schedule's attention
+ * splits: lengths are tracked on the host from the schedule, +1 per launched step; call
+ * mk_build_schedule with the current lengths and issue the step again), a sticky MK_ERR_DEVICE. */
 mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* positions,
                          const int32_t* block_tables, const int32_t* seq_lens, float* logits_out,
                          void* stream);
 
-/* Optional per-step outputs (device pointers, NULL = off), written by every later step:
+/* Optional per-step outputs of the steps launched after this call (device pointers owned by the
+ * caller, NULL = off): the greedy token that feeds the next step (the pages' decode benchmark
+ * generates its output tokens one step after another, P3 "Scheduling and Performance Benchmarks"),
+ * the routed experts of every layer and token (P3 "Key Technologies and Architecture": top-k routed
+ * experts), the final residual stream, a per-task trace and the router logits. MK_ERR_INVALID_ARG
+ * only for a NULL engine. The pointers must stay valid while steps that write them run.
  *   argmax_out int32 [B]       greedy token (first index of the maximum logit)
  *   topk_out int32 [L, B, k]   routed experts per layer and token, ascending expert index
  *   hidden_out float32 [B, H]  residual stream after the last layer
@@ -160,27 +175,55 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
 mk_status mk_set_step_outputs(mk_engine* e, int32_t* argmax_out, int32_t* topk_out,
                               float* hidden_out, uint64_t* trace_out, float* router_logits_out);
 
-/* Wait for the engine's last step and report a device fault, if any, as MK_ERR_DEVICE. */
+/* Wait for the engine's last step (its stream) and report a device fault raised by the kernel
+ * (dependency-wait watchdog, bad page id, position != seq_len - 1) as MK_ERR_DEVICE, which stays
+ * sticky until mk_reset. The caller is the one thread that owns decode (P3 "Scheduling and
+ * Performance Benchmarks": a C++ thread owns the decode loop). MK_ERR_HIP if the runtime fails. */
 mk_status mk_sync(mk_engine* e);
 
-/* Describe the last error in `buf` (NUL-terminated, truncated to n). Synchronizes the engine's
- * last stream to read the device error word. Returns the sticky status (MK_OK if none). */
+/* Describe the last error in `buf` (caller-owned host buffer; NUL-terminated, truncated to n).
+ * Synchronizes the engine's last stream to read the device error word, as mk_sync does (the decode
+ * owner's view of a failed step, P3 "Scheduling and Performance Benchmarks"). Returns the sticky
+ * status (MK_OK if none); with a NULL engine, MK_ERR_INVALID_ARG and "NULL engine" in buf. */
 mk_status mk_get_error(mk_engine* e, char* buf, size_t n);
 
-/* Clear a sticky device error and reset every counter (after MK_ERR_DEVICE). Synchronous. */
+/* Clear a sticky device error and reset every dependency counter and the argmax keys (after
+ * MK_ERR_DEVICE). The counters in device memory stand in for kernel boundaries (P1 "One persistent
+ * kernel for the whole decode step"); an aborted step leaves them part-way, and the next step needs
+ * them at zero. Synchronous (waits for the device). MK_ERR_INVALID_ARG for a NULL engine, MK_ERR_HIP
+ * if the runtime fails. */
 mk_status mk_reset(mk_engine* e);
 
+/* Release the engine: waits for the device, frees the workspace the engine allocated and the
+ * schedule; caller-owned weights, KV cache and step buffers are untouched. NULL is a no-op. Owned,
+ * like every other call on the engine, by the one decode thread (P3 "Scheduling and Performance
+ * Benchmarks"). */
 void mk_destroy(mk_engine* e);
 
 /* Measurement helper: the plain streaming-read bandwidth of the current device, a ceiling to set the
- * step kernel's achieved bandwidth against. Reads `bytes` (rounded down to 16) from the device buffer
+ * step kernel's achieved bandwidth against (decode is bound by HBM bandwidth, P1 "Decode is a
+ * bandwidth game"). Reads `bytes` (rounded down to 16) from the device buffer
  * `buf` (16-byte aligned, owned by the caller, not modified) `reps` times with 16-byte non-temporal
  * loads on 8 workgroups per CU, after one untimed pass; *bytes_per_s = bytes read / elapsed time
  * (HIP events on the default stream). Synchronous. MK_ERR_INVALID_ARG for a NULL or misaligned
  * buffer, bytes < 16 or reps < 1; MK_ERR_HIP / MK_ERR_OOM on runtime failures. */
 mk_status mk_stream_read_bandwidth(const void* buf, size_t bytes, int32_t reps, double* bytes_per_s);
 
+/* Self-test of the hand-off protocol the step kernel relies on (P1 "One persistent kernel for the
+ * whole decode step": tasks hand results to each other through device memory and counters instead of
+ * kernel boundaries). `workgroups` co-resident workgroups (cooperative launch; spread over every XCD)
+ * run `rounds` rounds; in each, one workgroup writes `words` words with the step kernel's producer
+ * sequence (write-through stores, wait for them, barrier, one relaxed counter add) and every other
+ * one polls the counter and reads the words with the step kernel's consumer sequence, counting words
+ * that do not hold the round's value. *stale = such words over all rounds, *checked = words read.
+ * Synchronous; allocates and frees its own small buffers. MK_ERR_INVALID_ARG for NULL outputs,
+ * rounds outside 1..100000, words outside 1..65536, or workgroups < 2 or more than can be resident;
+ * MK_ERR_DEVICE if a wait exceeded its 1 s bound; MK_ERR_HIP / MK_ERR_OOM on runtime failures. */
+mk_status mk_handoff_litmus(int32_t rounds, int32_t words, int32_t workgroups, uint64_t* stale, uint64_t* checked);
+
 /* ---- schedule inspection (host only: no GPU needed) -------------------------------------- */
+/* The static schedule the host builds for a step (P3 "Scheduling and Performance Benchmarks":
+ * mostly static scheduling), inspected, validated and simulated without a GPU. */
 
 typedef struct {
   int32_t n_tasks;           /* descriptors in the step */

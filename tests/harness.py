@@ -107,8 +107,9 @@ def replay_near_ties(run, g_topk, near_tie, max_rounds=32):
     """Reconcile the GPU's expert sets g_topk [L, B, k] with the oracle, layer by layer.
 
     ``run(forced)`` runs the oracle step with ``forced_topk=forced`` and returns its result. The
-    first layer where the two disagree must be a near-tie for every disagreeing token (oracle margin
-    <= near_tie, exactly one expert swapped); the oracle is then rerun with the GPU's sets forced
+    first layer where the two disagree must be a near-tie for every disagreeing token: oracle margin
+    r_(k) - r_(k+1) <= near_tie, and the GPU's set is the oracle's with its rank-k expert replaced by
+    its rank-(k+1) expert (ranks from a stable sort of the oracle's router logits); the oracle is then rerun with the GPU's sets forced
     there, which changes everything after that layer, and the walk continues. Disagreements after
     an unreplayed flip are never judged against an oracle that has already diverged.
     Returns (result, forced); raises RoutingMismatch otherwise.
@@ -126,9 +127,31 @@ def replay_near_ties(run, g_topk, near_tie, max_rounds=32):
             return ref, forced
         for b in diff:
             gs, rs = set(g_topk[l, b].tolist()), set(ref.topk[l, b].tolist())
-            if not (ref.margin[l, b] <= near_tie and len(gs ^ rs) == 2):
+            k = len(rs)
+            # the oracle's ranking of this token's router logits (ties -> lower index, as route())
+            order = np.argsort(-np.asarray(ref.router_logits[l, b]), kind="stable")
+            swap = (rs - gs == {int(order[k - 1])}) and (gs - rs == {int(order[k])})
+            if not (ref.margin[l, b] <= near_tie and swap):
                 raise RoutingMismatch(f"layer {l} token {b}: GPU experts {sorted(gs)} != oracle {sorted(rs)} "
-                                      f"(margin {ref.margin[l, b]:.3g}, earlier near-tie replays {sorted(forced)})",
+                                      f"(oracle ranks k, k+1 = {int(order[k - 1])}, {int(order[k])}; margin "
+                                      f"{ref.margin[l, b]:.3g}; earlier near-tie replays {sorted(forced)})",
                                       ref, forced)
             forced[(l, b)] = sorted(gs)
     raise RoutingMismatch(f"more than {max_rounds} rounds of near-tie replays", ref, forced)
+
+
+def bf16_step_mismatch(g16, h16, floor=1e-5):
+    """Mask of entries where two bf16 arrays (uint16 patterns) differ by more than one bf16 step.
+
+    A K/V entry is an fp32 result rounded to bf16; two fp32 results that differ by reduction order
+    round to the same bf16 or to neighbours, so entries may differ by at most the spacing of bf16
+    at the larger of the two magnitudes (2^(floor(log2|v|) - 7)). Near zero the fp32 values
+    themselves are dominated by rounding noise of the products summed into them, so differences up
+    to ``floor`` in absolute value are accepted there."""
+    gd = oracle.bf16_to_f32(np.asarray(g16, np.uint16)).astype(np.float64)
+    hd = oracle.bf16_to_f32(np.asarray(h16, np.uint16)).astype(np.float64)
+    mag = np.maximum(np.abs(gd), np.abs(hd))
+    with np.errstate(divide="ignore"):
+        step = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7), 0.0)
+    diff = np.abs(gd - hd)
+    return (diff > step) & (diff > floor)

@@ -2,9 +2,11 @@
 (fixed 8K contexts, and ragged log-uniform contexts with a Zipf router bias), each step checked
 against the CPU oracle on the same seeded inputs, in the launch configuration bench.py times.
 
-Gates: router top-k sets bit-exact up to accepted near-ties (oracle margin <= 1e-4, replayed);
-logits (or the residual stream when there is no lm_head) max |d| <= 2e-2 and relative L2 <= 5e-3;
-identical greedy tokens. Steps after the first are teacher-forced: the oracle consumes the GPU's
+Gates: router top-k sets bit-exact up to accepted near-ties (oracle margin <= 1e-4 between its
+rank-k and rank-(k+1) experts, which the GPU swapped; replayed); router logits max |d| <= 5e-5 up to
+the first replayed flip; the new K/V rows of every sequence and layer within one bf16 step of the
+oracle's; logits (or the residual stream when there is no lm_head) max |d| <= 2e-2 and relative
+L2 <= 5e-3; identical greedy tokens. Steps after the first are teacher-forced: the oracle consumes the GPU's
 tokens and starts from a copy of the GPU's KV cache as the step began.
 """
 
@@ -22,6 +24,12 @@ pytestmark = [pytest.mark.gpu, pytest.mark.timeout(900),
               pytest.mark.skipif(not torch.cuda.is_available(), reason="needs an MI355X GPU")]
 
 NEAR_TIE = 1e-4
+# Router logits, element-wise: at most half the near-tie band. A k/(k+1) flip needs the two logits'
+# deviations to close the oracle's margin, so with |d| <= NEAR_TIE / 2 every flip the GPU can make
+# has margin <= NEAR_TIE, i.e. falls in the band the replay accepts. (A tenth of the band, which the
+# small model meets, is out of reach after 48 layers: fp32 reduction-order differences compound
+# through the residual stream.)
+ROUTER_TOL = NEAR_TIE / 2
 MAX_ABS = 2e-2
 MAX_REL_L2 = 5e-3
 
@@ -76,8 +84,12 @@ class Model:
         if check:
             import oracle
             say(f"  [{wl.name}] step {self.step_i}: oracle")
+            kv_last = {}
+
             def run(forced):
-                return oracle.decode_step(self.dims, self.lw, copy.deepcopy(kv0), self.tokens, pos, self.bt_np, pos + 1,
+                kv = copy.deepcopy(kv0)
+                kv_last["kv"] = kv
+                return oracle.decode_step(self.dims, self.lw, kv, self.tokens, pos, self.bt_np, pos + 1,
                                           forced_topk=forced)
             try:
                 ref, replay = harness.replay_near_ties(run, g_topk, NEAR_TIE)
@@ -94,10 +106,33 @@ class Model:
                             f"differs by max|d| {d:.3g} rel {rel:.3g}; router logits max|d|, worst layers: {worst}")
             if replay:
                 say(f"  near-tie replays: {replay}")
-            # the router logits the routing decisions read, element-wise
+            # the router logits the routing decisions read, element-wise (up to the first replayed
+            # flip: later layers of the oracle then run on the GPU's routing, not on its own)
             dl = np.abs(g_rlog.astype(np.float64) - ref.router_logits)
-            stats["router_logits_maxabs"] = float(dl.max())
-            assert dl.max() <= MAX_ABS, f"step {self.step_i}: router logits max|d| {dl.max():.3g}"
+            first = min([l for l, _ in replay], default=wl.n_layers)
+            stats["router_logits_maxabs"] = float(dl[:first].max()) if first else 0.0
+            stats["router_logits_maxabs_by_depth"] = [float(dl[a:a + 12].max()) for a in range(0, wl.n_layers, 12)]
+            # the new K/V rows: the GPU's cache at every sequence's position, every layer, against
+            # the rows the oracle wrote (within one bf16 step; identical patterns for almost all)
+            kvo = kv_last["kv"]
+            nbad = ndiff = ntot = 0
+            for b in range(wl.batch):
+                p_b = int(pos[b])
+                page, slot = int(self.bt_np[b][p_b // wl.page_size]), p_b % wl.page_size
+                for l in range(wl.n_layers):
+                    for dev, host in ((self.k, kvo.k), (self.v, kvo.v)):
+                        g16 = synth.to_u16(dev[l][page, :, slot, :])
+                        h16 = host[l][page, :, slot, :]
+                        nbad += int(harness.bf16_step_mismatch(g16, h16).sum())
+                        ndiff += int((g16 != h16).sum())
+                        ntot += g16.size
+            stats["kv_rows_differ"] = f"{ndiff}/{ntot}"
+            say(f"  [{wl.name}] step {self.step_i}: router max|d| {stats['router_logits_maxabs']:.3g} "
+                f"by depth {stats['router_logits_maxabs_by_depth']}, new KV rows differing {ndiff}/{ntot}")
+            assert nbad == 0, f"step {self.step_i}: {nbad} new K/V entries differ by more than one bf16 step"
+            assert ndiff <= max(2, ntot // 1000), f"step {self.step_i}: {ndiff}/{ntot} new K/V entries differ"
+            assert stats["router_logits_maxabs"] <= ROUTER_TOL, \
+                f"step {self.step_i}: router logits max|d| {stats['router_logits_maxabs']:.3g} > {ROUTER_TOL}"
             outs = [(g_hidden, ref.x_final, "hidden")]
             if wl.lm_head:
                 outs.append((g_logits, ref.logits, "logits"))
