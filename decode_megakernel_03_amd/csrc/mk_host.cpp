@@ -10,11 +10,14 @@
 // the router.
 // Tile counts are derived from the worker count rather than a fixed tile, so a level never ends
 // with a partly filled wave of tiles (P1 "One persistent kernel for the whole decode step": wave
-// quantization). Attention is split per KV group so an output row waits only for the attention it
-// reads; weight loads are issued before dependency waits inside the kernel.
+// quantization). Attention is split per KV group; each group's merges count on their own sub-counters
+// of the layer's attention counter, so an output row may multiply a group's W_o columns as soon as
+// that group's attention has landed (an ablation flag: measured slower than waiting for all groups).
+// Weight loads are issued before dependency waits inside the kernel.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -203,6 +206,9 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   std::vector<int> c_queue(L, -1);
   for (int l = 0; l < L; ++l) {
     for (int g = 0; g < m.HKV; ++g) c_qkv[l][g] = C.alloc();
+    // the attention counter: the merges of KV group g add to its sub-counters g * (CTR_SUB / HKV) ..,
+    // so an output row can also see each group's attention land on its own (P1 "One persistent kernel
+    // for the whole decode step")
     c_rarr[l] = C.alloc(); c_route[l] = C.alloc(); c_h[l] = C.alloc(); c_att[l] = C.alloc();
     if (steal) c_queue[l] = C.alloc();
     for (int i = 0; i < B * m.HKV; ++i) c_aarr[l][i] = C.alloc();
@@ -357,7 +363,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       Proto pr;
       set(pr.t, OP_OUT, l, lv2);
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
-      pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV * nslice;
+      pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV * nslice;   // every merge of every KV group
       pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
       pr.t.w[D_W1] = c_h[l]; pr.t.w[D_T1] = n_gu;
       pr.t.w[D_SIG] = c_x[l + 1];
@@ -466,6 +472,22 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   return MK_OK;
 }
 
+// Every (counter, target) a task waits for: W0/T0, W1/T1, and for an output-row task the attention
+// counter A2 (every merge of the layer, A3).
+struct Waits {
+  int n = 0;
+  std::array<std::array<int, 2>, 3> w;
+  const std::array<int, 2>* begin() const { return w.data(); }
+  const std::array<int, 2>* end() const { return w.data() + n; }
+};
+Waits task_waits(const Task& t, int hkv) {
+  Waits w;
+  if (t.w[D_W0] >= 0) w.w[w.n++] = {t.w[D_W0], t.w[D_T0]};
+  if (t.w[D_W1] >= 0) w.w[w.n++] = {t.w[D_W1], t.w[D_T1]};
+  if (t.w[D_OP] == OP_OUT) w.w[w.n++] = {t.w[D_A2], t.w[D_A3]};
+  return w;
+}
+
 // ---- validation --------------------------------------------------------------------------
 
 mk_status validate_plan(const mk_plan& P, std::string* why) {
@@ -491,10 +513,10 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
   }
   for (auto& [c, v] : sig2_groups) sig[c] += (int)v.size();
   for (auto& t : P.tasks) {
-    const int waits[3][2] = {{t.w[D_W0], t.w[D_T0]}, {t.w[D_W1], t.w[D_T1]},
-                             {t.w[D_OP] == OP_OUT ? t.w[D_A2] : -1, t.w[D_OP] == OP_OUT ? t.w[D_A3] : 0}};
+    const auto waits = task_waits(t, m.HKV);
     for (auto& wt : waits) {
       if (wt[0] < 0) continue;
+      if (wt[0] >= P.n_ctr) { *why = fmt("task %d waits on counter %d of %d", t.w[D_ID], wt[0], P.n_ctr); return MK_ERR_INVALID_ARG; }
       if (wt[1] != sig[wt[0]]) { *why = fmt("task %d (op %d) waits for counter %d >= %d but %d signals exist", t.w[D_ID], t.w[D_OP], wt[0], wt[1], sig[wt[0]]); return MK_ERR_INVALID_ARG; }
       if (prod_level[wt[0]] >= t.w[D_LEVEL]) { *why = fmt("task %d (level %d) depends on counter %d produced at level %d", t.w[D_ID], t.w[D_LEVEL], wt[0], prod_level[wt[0]]); return MK_ERR_INVALID_ARG; }
     }
@@ -550,8 +572,8 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
       }
       for (int q = 0; q < nq; ++q) if (!drained[q]) { *why = fmt("layer %d: expert sub-queue %d has no task", l, q); return MK_ERR_INVALID_ARG; }
       for (auto& t : P.tasks) {
-        const bool uses = t.w[D_W0] == qc || t.w[D_W1] == qc || t.w[D_SIG] == qc || t.w[D_SIG2] == qc ||
-                          (t.w[D_OP] == OP_OUT && t.w[D_A2] == qc);
+        bool uses = t.w[D_SIG] == qc || t.w[D_SIG2] == qc;
+        for (auto& wt : task_waits(t, m.HKV)) uses = uses || wt[0] == qc;
         if (uses) { *why = fmt("task %d waits on or signals the expert queue counter %d", t.w[D_ID], qc); return MK_ERR_INVALID_ARG; }
       }
     } else if ((int)gu.size() != std::min(m.E, m.K * P.B)) { *why = fmt("layer %d: %zu expert slots", l, gu.size()); return MK_ERR_INVALID_ARG; }
@@ -596,9 +618,7 @@ mk_status simulate_plan(const mk_plan& P, uint64_t seed, int stall_worker, int s
   for (int w = 0; w < P.n_workers; ++w) pos[w] = P.qoff[w];
   int remaining = (int)P.tasks.size();
   auto ready = [&](const Task& t, int* c, uint32_t* tg) {
-    const int waits[3][2] = {{t.w[D_W0], t.w[D_T0]}, {t.w[D_W1], t.w[D_T1]},
-                             {t.w[D_OP] == OP_OUT ? t.w[D_A2] : -1, t.w[D_OP] == OP_OUT ? t.w[D_A3] : 0}};
-    for (auto& wt : waits)
+    for (auto& wt : task_waits(t, P.m.HKV))
       if (wt[0] >= 0 && ctr[wt[0]] < (uint32_t)wt[1]) { *c = wt[0]; *tg = (uint32_t)wt[1]; return false; }
     return true;
   };

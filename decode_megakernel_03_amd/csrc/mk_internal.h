@@ -42,7 +42,8 @@ enum Op {
                   // a4 rows per slice: (slot, slice) items drawn from the layer's work queue
   OP_ATTN = 4,    // a0 b, a1 g, a2 k0, a3 k1 (-1 = to seq_len, the split holding the new token),
                   // a4 first partial of (b, g) in the layer, a5 split | nsplit << 16
-  OP_OUT = 5,     // a0 row0, a1 nrows: x_{l+1} = x_l + W_o attn + sum_i w_i W_down[e_i] h_i
+  OP_OUT = 5,     // a0 row0, a1 nrows, a2 attention counter (KV group g's merges on sub-counters
+                  // g*CTR_SUB/HKV ..), a3 its target: x_{l+1} = x_l + W_o attn + sum_i w_i W_down[e_i] h_i
   OP_LMHEAD = 6,  // a0 row0, a1 nrows: logits + running argmax
   OP_MERGE = 7,   // a0 b, a1 g, a2 slice, a3 slices, a4 first partial, a5 nsplit: attention output
   OP_COUNT

@@ -335,14 +335,19 @@ __device__ __forceinline__ void drain_t(CParams& p) {
   drain();
 }
 
-__device__ uint32_t signal(CParams& p, Ctl& ctl, int c, bool want_old) {
+// A signal adds to its worker's sub-counter (waits sum all CTR_SUB). A signal whose old value is used
+// counts on sub-counter 0 only (all of that counter's signals do), so that the old value is the
+// number of earlier signals. A signal of group `grp` >= 0 (of the attention counter's HKV groups)
+// adds to one of that group's CTR_SUB / HKV sub-counters, so that a waiter can count each group.
+template <int HKV = 1>
+__device__ uint32_t signal(CParams& p, Ctl& ctl, int c, bool want_old, int grp = -1) {
   drain();
   __syncthreads();
   uint32_t old = 0;
   if (tid() == 0 && c >= 0) {
-    // a signal whose old value is used counts on sub-counter 0 only (all of that counter's
-    // signals do), so that the old value is the number of earlier signals
-    old = ctr_add(ctr_at(p, c, want_old ? 0 : (int)(blockIdx.x % CTR_SUB)), 1u);
+    constexpr int per = CTR_SUB / HKV;
+    const int sub = want_old ? 0 : grp >= 0 ? grp * per + (int)(blockIdx.x % per) : (int)(blockIdx.x % CTR_SUB);
+    old = ctr_add(ctr_at(p, c, sub), 1u);
     if (want_old) ctl.flag = (int)old;
   }
   if (want_old) {
@@ -1475,7 +1480,7 @@ __device__ __forceinline__ bool op_merge(int task) {
   MARK(2);
   drain_t(p);
   MARK(3);
-  signal(p, ctl, T.sig, false);
+  signal<S::HKV>(p, ctl, T.sig, false, g);   // on KV group g's sub-counters of the attention counter
   return true;
 }
 
@@ -1496,6 +1501,122 @@ __device__ __forceinline__ void stage_f4(float* dst, __amdgpu_buffer_rsrc_t R, u
     const int i = (u * NT + tx) * 4;
     if (i < n) *reinterpret_cast<f4*>(dst + i) = v[u];
   }
+}
+
+// Counter c's signals come in n groups, group g adding to sub-counters g * (CTR_SUB / n) .. (the
+// attention merges of KV group g). Wait until the groups' counts reach `target` each for a longer
+// leading run of groups than `have` (one poll reads the CTR_SUB lines: one load per lane of wave 0,
+// one round trip): returns the number of leading complete groups (> have), or -1 if the step was
+// aborted or the watchdog fired.
+__device__ int wait_prefix(CParams& p, Ctl& ctl, int c, int n, uint32_t target, int have, int task) {
+  const int tx = tid(), lane = tx & 63;
+  if (__builtin_amdgcn_readfirstlane(tx >> 6) == 0) {
+    int k = -1;
+    const uint64_t t0 = now();
+    uint32_t it = 0;
+    const int per = CTR_SUB / n;
+    for (;;) {
+      const uint32_t v = lane < CTR_SUB ? ctr_load(ctr_at(p, c, lane)) : 0u;
+      int run = 0;
+      for (int g = 0; g < n; ++g) {
+        uint32_t sum = 0;
+        for (int i = 0; i < per; ++i) sum += __builtin_amdgcn_readlane(v, g * per + i);
+        if (sum < target) break;
+        run = g + 1;
+      }
+      if (run > have) { k = run; break; }
+      __builtin_amdgcn_s_sleep(1);
+      if ((++it & 15u) == 0) {
+        if (__builtin_amdgcn_readfirstlane(ctr_load(&p.err->abort_flag))) break;
+        if (now() - t0 > p.watchdog_ticks) {
+          if (lane == 0) raise_error(p, DEV_TIMEOUT, task, c, target, 0, (uint32_t)have);
+          break;
+        }
+      }
+    }
+    if (lane == 0) {
+      ctl.flag = k;
+      ctl.t_ready = now();
+    }
+  }
+  __syncthreads();
+  const int k = ctl.flag;
+  __syncthreads();
+  return k;
+}
+
+// O projection of one token's attention vector (rows of W_o already in W), one KV group as soon as it
+// lands (the ablation flag MK_FLAG_OPROJ_PER_GROUP; P1 "One persistent kernel for the whole decode
+// step": the O projection starts when its KV group's attention has landed). Counter c counts every
+// merge of the layer, KV group g's on its own sub-counters (wait_prefix), `target` each. Each round
+// polls every group in one round trip, stages the columns of every newly complete leading group into
+// a_s in one pass and folds their products into the running sums. A lane's 16-byte chunks of a row
+// lie in non-decreasing group order and groups are taken in order, so every row's products are summed
+// in the order of one pass over the whole row: the same bits as the default form, which waits for
+// every group first (measured faster on MI355X, where the four groups' merges land within about a
+// microsecond of each other and each extra round adds a dependent staging round trip).
+template <class S, int NP, int OT, class Emit>
+__device__ __forceinline__ bool oproj_grouped(CParams& p, Ctl& ctl, const WBuf<S::AD, NP>& W, int nrows, int b0, int nt,
+                                              int cbase, int target, bool wait, bool per_group, int task, float* a_s,
+                                              __amdgpu_buffer_rsrc_t At, Emit emit) {
+  constexpr int AD = S::AD, GW = S::HPG * S::D, HKV = S::HKV;
+  using G = Geo<AD>;
+  constexpr int NI = (OT * AD + 4 * NT - 1) / (4 * NT);
+  static_assert(GW % 4 == 0 && HKV <= 64, "");
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  const int lir = lane % G::LPR, rip = lane / G::LPR;
+  float acc[NP][OT];
+#pragma unroll
+  for (int i = 0; i < NP; ++i)
+#pragma unroll
+    for (int t = 0; t < OT; ++t) acc[i][t] = 0.f;
+  int have = 0;
+  while (have < HKV) {
+    const int k = wait ? wait_prefix(p, ctl, cbase, HKV, (uint32_t)target, per_group ? have : HKV - 1, task) : HKV;
+    if (k < 0) return false;
+    // columns [have GW, k GW) of every listed token: all loads first, then the LDS writes
+    const int w = (k - have) * GW, c0 = have * GW;
+    f4 v[NI];
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int idx = (u * NT + tx) * 4, t = idx / AD, e = idx - t * AD;
+      v[u] = (t < nt && e < w) ? ldc4(At, 4u * ((b0 + t) * AD + c0 + e)) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int u = 0; u < NI; ++u) {
+      const int idx = (u * NT + tx) * 4, t = idx / AD, e = idx - t * AD;
+      if (t < nt && e < w) *reinterpret_cast<f4*>(a_s + t * AD + c0 + e) = v[u];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < G::CPL; ++j) {
+      const int e0 = 8 * (lir + G::LPR * j);              // first column of the lane's chunk j
+      const int g = e0 / GW;
+      if (g < have || g >= k) continue;
+#pragma unroll
+      for (int t = 0; t < OT; ++t) {
+        if (t < nt) {
+          const f4* ap = reinterpret_cast<const f4*>(a_s + t * AD + e0);
+          const f4 a0 = ap[0], a1 = ap[1];
+#pragma unroll
+          for (int i = 0; i < NP; ++i) acc[i][t] = dot8(W.w[i][j], a0, a1, acc[i][t]);
+        }
+      }
+    }
+    have = k;
+  }
+#pragma unroll
+  for (int i = 0; i < NP; ++i) {
+    const int r = (i * NWAVE + wave) * G::RPP + rip;
+#pragma unroll
+    for (int t = 0; t < OT; ++t) {
+      if (t < nt) {
+        const float s = wsum<G::LPR>(acc[i][t]);
+        if (lir == 0 && r < nrows) emit(r, t, s);
+      }
+    }
+  }
+  return true;
 }
 
 // Output rows row0..row0+nrows of the layer for every token: the fused residual add that rejoins
@@ -1571,13 +1692,20 @@ __device__ __forceinline__ bool op_out(int task) {
     }
   }
   MARK(1);
-  if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
+  const bool per_group = (p.flags & 8) != 0;
+  if (!per_group && !wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;   // attention of every KV group
   for (int b = 0; b < p.B; ++b) {
-    stage_f4<AD>(a_s, At, 4u * (b * AD), AD);
-    __syncthreads();
+    if (per_group) {      // KV group by KV group as each group's merges land (ablation)
+      if (!oproj_grouped<S, NPO, 1>(p, ctl, WO, nrows, b, 1, T.a2, T.a3 / S::HKV, b == 0, true, T.id, a_s, At,
+                                    [&](int r, int t, float v) { o_s[r] = v; }))
+        return false;
+    } else {
+      stage_f4<AD>(a_s, At, 4u * (b * AD), AD);
+      __syncthreads();
+      compute_block_shared<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
+                                       [&](int r, int t, float v) { o_s[r] = v; });
+    }
     if (b == 0) MARK(2);
-    compute_block_shared<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
-                                     [&](int r, int t, float v) { o_s[r] = v; });
     __syncthreads();
     if (tid() < nrows) {
       const int r = tid(), row = row0 + r;
@@ -1698,8 +1826,8 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   WBuf<AD, NPO> WO;
   load_block<AD, NPO>(WO, 0, nrows, orow);
   __syncthreads();                         // the MoE phase is done with the LDS it shares with a_s
-  if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
   float* a_s = sm + LY::A;
+  if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
   for (int b0 = 0; b0 < B; b0 += OUT_OT) {
     const int nt = B - b0 < OUT_OT ? B - b0 : OUT_OT;
     stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);

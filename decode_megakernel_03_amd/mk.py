@@ -20,6 +20,7 @@ MK_MAX_BATCH = 8
 MK_FLAG_TRACE = 1
 MK_FLAG_NO_PREFETCH = 2
 MK_FLAG_STATIC_EXPERTS = 4
+MK_FLAG_OPROJ_PER_GROUP = 8
 DESC_WORDS = 16
 
 EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_decode_step", "mk_set_step_outputs",
@@ -93,6 +94,11 @@ def load(path=LIB_PATH):
         f.restype = None if name in ("mk_destroy", "mk_plan_destroy") else (vp if name == "mk_engine_plan" else ctypes.c_int)
     return lib
 
+
+# torch brings its own HIP and HSA runtimes, libmk.so links the system ROCm ones; the process works
+# with both only when torch's are loaded first (loading libmk.so first left mk_create without a HIP
+# device once torch had initialised the GPU), so torch is imported before the library is loaded
+import torch  # noqa: E402,F401
 
 # MK_LIBRARY names another build of the same C ABI (e.g. to compare two builds in one process tree)
 LIB = load(os.environ.get("MK_LIBRARY", LIB_PATH))

@@ -117,6 +117,10 @@ typedef struct {
  * from the per-layer work queue that tasks drain and steal from (P3 "Scheduling and Performance
  * Benchmarks": dynamic work stealing). Read by mk_build_schedule / mk_plan_build. */
 #define MK_FLAG_STATIC_EXPERTS 4u
+/* Ablation (batch 1): an output-row task multiplies each KV group's W_o columns as soon as that group's
+ * attention merges have landed, instead of after all groups (P1 "One persistent kernel for the whole
+ * decode step"). Off by default: measured slower on MI355X. Read by mk_decode_step. */
+#define MK_FLAG_OPROJ_PER_GROUP 8u
 
 /* Create an engine for `desc` over caller-owned weights (P1 "One persistent kernel for the whole
  * decode step"). Validates the description, copies the pointer tables to the device and

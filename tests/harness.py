@@ -145,13 +145,13 @@ def bf16_step_mismatch(g16, h16, floor=1e-5):
 
     A K/V entry is an fp32 result rounded to bf16; two fp32 results that differ by reduction order
     round to the same bf16 or to neighbours, so entries may differ by at most the spacing of bf16
-    at the larger of the two magnitudes (2^(floor(log2|v|) - 7)). Near zero the fp32 values
-    themselves are dominated by rounding noise of the products summed into them, so differences up
-    to ``floor`` in absolute value are accepted there."""
+    at the larger of the two magnitudes (2^(floor(log2|v|) - 7)). Differences up to ``floor`` in
+    absolute value are accepted as well: the fp32 values themselves may differ by that much (rounding
+    noise near zero; after many layers, the deviation their inputs carry)."""
     gd = oracle.bf16_to_f32(np.asarray(g16, np.uint16)).astype(np.float64)
     hd = oracle.bf16_to_f32(np.asarray(h16, np.uint16)).astype(np.float64)
     mag = np.maximum(np.abs(gd), np.abs(hd))
     with np.errstate(divide="ignore"):
         step = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7), 0.0)
     diff = np.abs(gd - hd)
-    return (diff > step) & (diff > floor)
+    return diff > step + floor

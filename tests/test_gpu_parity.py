@@ -164,6 +164,16 @@ def test_tiny_first_token_and_page_boundary():
     run_steps(wl, 3, teacher_force=True, ctx=[0, 16])
 
 
+def test_tiny_oproj_per_kv_group():
+    """The output rows multiply each KV group's W_o columns as that group's attention merges land
+    (MK_FLAG_OPROJ_PER_GROUP), with 32-key splits so that every group has several merges: same gates."""
+    from decode_megakernel_03_amd import mk
+    say("test_tiny_oproj_per_kv_group: per-KV-group O projection, 32-key splits, batch 3 ragged")
+    wl = synth.workload("tiny", batch=3, ragged=(17, 200))
+    run_steps(wl, 3, teacher_force=True, split_keys=32, flags=mk.MK_FLAG_OPROJ_PER_GROUP)
+    run_steps(synth.workload("tiny"), 3, split_keys=32, flags=mk.MK_FLAG_OPROJ_PER_GROUP)
+
+
 def test_tiny_split_attention():
     say("test_tiny_split_attention: 32-key attention splits (3 splits + log-sum-exp merge per group)")
     run_steps(synth.workload("tiny"), 4, split_keys=32)

@@ -71,19 +71,23 @@ def test_plan_structure_full_bs1():
     assert (op == 6).sum() == 512                                     # lm_head spread over every worker
     out_rows = tasks[op == 5][:, 3]                                   # rows of each output task
     assert out_rows.sum() == L * 2048 and out_rows.min() >= 1          # every output row once per layer
-    # output rows of layer l wait on the attention merges of all KV groups of layer l only
+    # output rows of layer l wait on the attention merges of layer l only (every KV group's merges
+    # signal the layer's attention counter, each group on sub-counters of its own)
     att = tasks[op == 4]
     out = tasks[op == 5]
     mrg = tasks[op == 7]
     for l in (0, 17, 47):
         m_l = mrg[mrg[:, 1] == l]
-        assert len(m_l) == 4 * 4 and set(m_l[:, 12]) == set(out[out[:, 1] == l][:, 4])   # 4 slices per group
+        o_l = out[out[:, 1] == l]
+        assert len(m_l) == 4 * 4 and set(m_l[:, 12]) == set(o_l[:, 4])  # 4 slices per group
+        for g in range(4):
+            assert (m_l[:, 3] == g).sum() == 4
         a_l = att[att[:, 1] == l]
         assert np.all(a_l[:, 13] == -1) and np.all(a_l[:, 10] == -1)  # splits only signal arrival
         for mt in m_l:                                                # a merge waits for every split of its group
             grp = a_l[(a_l[:, 2] == mt[2]) & (a_l[:, 3] == mt[3])]
             assert mt[8] == grp[0, 12] and mt[9] == len(grp) == mt[7] and set(grp[:, 12]) == {mt[8]}
-        assert np.all(out[out[:, 1] == l][:, 5] == 16)                # output rows wait for all 16 slices
+        assert np.all(o_l[:, 5] == 16)                                 # output rows wait for all 16 slices
     # a merge runs on a worker that ran one of its group's splits
     worker = np.repeat(np.arange(512), np.diff(qoff))
     for i in np.where(op == 7)[0][:64]:
