@@ -203,6 +203,8 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // At batch 1 the union is always top_k experts, so the work is known before the step and the
   // static deal is kept (measured: the queue only moves items between equally loaded workers).
   const bool steal = B > 1 && !(flags & MK_FLAG_STATIC_EXPERTS);
+  // down items per union slot (row blocks of W_down[e], DOWN_ROWS rows each) in queue mode
+  const int down_items = steal ? (int)ceil_div(m.H, down_rows()) : 0;
   std::vector<int> c_queue(L, -1);
   for (int l = 0; l < L; ++l) {
     for (int g = 0; g < m.HKV; ++g) c_qkv[l][g] = C.alloc();
@@ -309,18 +311,21 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     if (steal) {
       // one task per worker at most: each draws (slot, slice) items until the queue is empty, so
       // the routing-dependent expert work goes to whichever workers are free first
-      const int n_items = slots * slices;
+      // the down projection of every union expert joins the queue as row blocks (after every gate/up
+      // item), so that W_down is read once per expert and streams while other slots' gate/up items
+      // are still running; the output rows then only add the experts' results
+      const int n_items = slots * (slices + down_items);
       const int tickets = std::min(n_items, W);
       const int nq = std::min(CTR_SUB, tickets);
       for (int t = 0; t < tickets; ++t) {
         Proto pr;
         set(pr.t, OP_GATEUP, l, lv1);
         pr.t.w[D_A0] = t % nq; pr.t.w[D_A1] = nq; pr.t.w[D_A2] = slices; pr.t.w[D_A3] = c_queue[l];
-        pr.t.w[D_A4] = nf;
+        pr.t.w[D_A4] = nf; pr.t.w[D_A5] = down_items;
         pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
         pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
         pr.t.w[D_SIG] = c_h[l];
-        pr.bytes = (int64_t)n_items * 2 * nf * m.H * 2 / tickets;
+        pr.bytes = ((int64_t)slots * slices * 2 * nf * m.H * 2 + (int64_t)slots * m.H * m.F * 2) / tickets;
         pr.prio = 1;
         levels[lv1].push_back(pr);
         n_gu++;
@@ -364,10 +369,11 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       set(pr.t, OP_OUT, l, lv2);
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
       pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV * nslice;   // every merge of every KV group
+      pr.t.w[D_A4] = down_items > 0 ? 1 : 0;
       pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
       pr.t.w[D_W1] = c_h[l]; pr.t.w[D_T1] = n_gu;
       pr.t.w[D_SIG] = c_x[l + 1];
-      pr.bytes = (int64_t)(e - a) * (m.AD + (int64_t)slots * m.F) * 2;
+      pr.bytes = (int64_t)(e - a) * (m.AD + (down_items > 0 ? 0 : (int64_t)slots * m.F)) * 2;
       pr.prio = 0;
       levels[lv2].push_back(pr);
       n_out++;
@@ -557,14 +563,25 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
       // every FFN row of every union slot once; every sub-queue has a task that drains it
       if (!gu.empty()) { *why = fmt("layer %d mixes static and queued expert slices", l); return MK_ERR_INVALID_ARG; }
       const Task& t0 = *queue_tasks[0];
-      const int qc = t0.w[D_A3], nq = t0.w[D_A1], slices = t0.w[D_A2], nfs = t0.w[D_A4];
+      const int qc = t0.w[D_A3], nq = t0.w[D_A1], slices = t0.w[D_A2], nfs = t0.w[D_A4], qd = t0.w[D_A5];
+      // down items: none, or row blocks that cover every W_down row once
+      if (qd < 0 || (qd > 0 && (qd * down_rows() < m.H || (qd - 1) * down_rows() >= m.H))) {
+        *why = fmt("layer %d: %d down items of %d rows for %d rows", l, qd, down_rows(), m.H);
+        return MK_ERR_INVALID_ARG;
+      }
+      for (auto& t : P.tasks)
+        if (t.w[D_LAYER] == l && t.w[D_OP] == OP_OUT && t.w[D_A4] != (qd > 0 ? 1 : 0)) {
+          *why = fmt("layer %d: output task %d and the expert queue disagree on the down items", l, t.w[D_ID]);
+          return MK_ERR_INVALID_ARG;
+        }
       if (qc >= P.n_ctr || nq < 1 || nq > CTR_SUB || slices < 1 || nfs < 1 || slices * nfs < m.F || (slices - 1) * nfs >= m.F) {
         *why = fmt("layer %d: bad expert queue (counter %d, %d sub-queues, %d slices of %d rows)", l, qc, nq, slices, nfs);
         return MK_ERR_INVALID_ARG;
       }
       std::vector<int> drained(nq, 0);
       for (const Task* t : queue_tasks) {
-        if (t->w[D_A3] != qc || t->w[D_A1] != nq || t->w[D_A2] != slices || t->w[D_A4] != nfs || t->w[D_A0] < 0 || t->w[D_A0] >= nq) {
+        if (t->w[D_A3] != qc || t->w[D_A1] != nq || t->w[D_A2] != slices || t->w[D_A4] != nfs || t->w[D_A5] != qd ||
+            t->w[D_A0] < 0 || t->w[D_A0] >= nq) {
           *why = fmt("layer %d: expert task %d disagrees on the queue", l, t->w[D_ID]);
           return MK_ERR_INVALID_ARG;
         }
@@ -577,6 +594,12 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
         if (uses) { *why = fmt("task %d waits on or signals the expert queue counter %d", t.w[D_ID], qc); return MK_ERR_INVALID_ARG; }
       }
     } else if ((int)gu.size() != std::min(m.E, m.K * P.B)) { *why = fmt("layer %d: %zu expert slots", l, gu.size()); return MK_ERR_INVALID_ARG; }
+    if (queue_tasks.empty())
+      for (auto& t : P.tasks)
+        if (t.w[D_LAYER] == l && t.w[D_OP] == OP_OUT && t.w[D_A4] != 0) {
+          *why = fmt("layer %d: output task %d expects queued down items, the layer has none", l, t.w[D_ID]);
+          return MK_ERR_INVALID_ARG;
+        }
     for (auto& [u, v] : gu) for (int f = 0; f < m.F; ++f) if (v[f] != 1) { *why = fmt("layer %d slot %d ffn row %d written %d times", l, u, f, v[f]); return MK_ERR_INVALID_ARG; }
     for (int b = 0; b < P.B; ++b)
       for (int g = 0; g < m.HKV; ++g) {
@@ -675,6 +698,8 @@ struct mk_engine {
   LayerPtrs* d_layers = nullptr;
   double* d_inv_freq = nullptr;
   float *d_x = nullptr, *d_qkv = nullptr, *d_rlog = nullptr, *d_h = nullptr, *d_attn = nullptr, *d_apart = nullptr;
+  float* d_y = nullptr;
+  uint32_t* d_slot = nullptr;
   RouteTable* d_route = nullptr;
   unsigned long long* d_amax = nullptr;
   uint32_t* d_ctr = nullptr;
@@ -712,7 +737,7 @@ hipError_t dalloc(T** p, size_t n) {
 }
 
 void free_all(mk_engine* e) {
-  void* ps[] = {e->d_layers, e->d_inv_freq, e->d_x, e->d_qkv, e->d_rlog, e->d_h, e->d_attn, e->d_apart,
+  void* ps[] = {e->d_layers, e->d_inv_freq, e->d_x, e->d_qkv, e->d_rlog, e->d_h, e->d_y, e->d_slot, e->d_attn, e->d_apart,
                 e->d_route, e->d_amax, e->d_ctr, e->d_err, e->d_tasks, e->d_qoff};
   for (void* p : ps) if (p) (void)hipFree(p);
 }
@@ -775,6 +800,8 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weight_ptrs* w, mk_engin
             dalloc(&e->d_qkv, (size_t)L * MAXB * m.QKVR) == hipSuccess &&
             dalloc(&e->d_rlog, (size_t)L * MAXB * m.E) == hipSuccess &&
             dalloc(&e->d_h, (size_t)L * MAXB * m.K * m.F) == hipSuccess &&
+            dalloc(&e->d_y, (size_t)L * MAXB * m.K * m.H) == hipSuccess &&
+            dalloc(&e->d_slot, (size_t)L * MAX_SLOTS * CTR_STRIDE) == hipSuccess &&
             dalloc(&e->d_attn, (size_t)L * MAXB * m.AD) == hipSuccess &&
             dalloc(&e->d_route, (size_t)L) == hipSuccess && dalloc(&e->d_amax, MAXB) == hipSuccess &&
             dalloc(&e->d_err, 1) == hipSuccess;
@@ -784,6 +811,7 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weight_ptrs* w, mk_engin
       hipMemset(e->d_amax, 0, sizeof(unsigned long long) * MAXB) != hipSuccess ||
       hipMemset(e->d_err, 0, sizeof(DevError)) != hipSuccess ||
       hipMemset(e->d_x, 0, sizeof(float) * (size_t)(L + 1) * MAXB * m.H) != hipSuccess ||
+      hipMemset(e->d_slot, 0, sizeof(uint32_t) * (size_t)L * MAX_SLOTS * CTR_STRIDE) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess) {
     fprintf(stderr, "mk_create: HIP copy failed\n");
     return fail(MK_ERR_HIP);
@@ -865,6 +893,7 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
   p.layers = e->d_layers; p.embed = (const uint16_t*)e->w.embed; p.lm_head = (const uint16_t*)e->w.lm_head;
   p.final_norm = (const uint16_t*)e->w.final_norm; p.inv_freq = e->d_inv_freq;
   p.x = e->d_x; p.qkv = e->d_qkv; p.rlog = e->d_rlog; p.route = e->d_route; p.h = e->d_h; p.apart = e->d_apart;
+  p.y = e->d_y; p.slot_ctr = e->d_slot;
   p.attn = e->d_attn; p.amax = e->d_amax; p.ctr = e->d_ctr; p.err = e->d_err;
   p.tasks = e->d_tasks; p.qoff = e->d_qoff;
   p.tokens = tokens; p.positions = positions; p.block_tables = block_tables; p.seq_lens = seq_lens;
@@ -922,6 +951,7 @@ mk_status mk_reset(mk_engine* e) {
   HIPCHK(e, hipMemset(e->d_err, 0, sizeof(DevError)));
   if (e->d_ctr) HIPCHK(e, hipMemset(e->d_ctr, 0, (e->ctr_cap * CTR_SUB + 1) * CTR_STRIDE * sizeof(uint32_t)));
   HIPCHK(e, hipMemset(e->d_amax, 0, sizeof(unsigned long long) * MAXB));
+  HIPCHK(e, hipMemset(e->d_slot, 0, sizeof(uint32_t) * (size_t)e->m.L * MAX_SLOTS * CTR_STRIDE));
   HIPCHK(e, hipDeviceSynchronize());
   e->sticky = MK_OK;
   e->msg.clear();

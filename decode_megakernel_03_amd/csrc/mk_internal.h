@@ -15,6 +15,7 @@ constexpr int DESC_WORDS = 16;
 // different counters never share a line (and, across lines, spread over memory channels).
 constexpr int CTR_STRIDE = 64;      // uint32 between sub-counters (one 256-byte line each)
 constexpr int CTR_SUB = 16;         // sub-counters per dependency counter
+constexpr int MAX_SLOTS = 64;       // union slots of one layer (at most min(E, K * MAXB))
 // Trace record per task (MK_FLAG_TRACE): id | worker << 32, t_start, t_ready, t_end, marks.
 constexpr int TRACE_WORDS = 16;
 constexpr int TRACE_MARKS = TRACE_WORDS - 4;   // a task descriptor is 16 int32 = 64 bytes
@@ -39,11 +40,13 @@ enum Op {
   OP_ROUTER = 2,  // a0 row0, a1 nrows, a2 router tiles: logits; the last tile routes (top-k)
   OP_GATEUP = 3,  // static: a0 union slot, a1 f0, a2 nf, a3 -1: h = SiLU(W_gate n) * (W_up n) on rows f0..
                   // queue: a0 own sub-queue, a1 sub-queues, a2 slices per slot, a3 queue counter,
-                  // a4 rows per slice: (slot, slice) items drawn from the layer's work queue
+                  // a4 rows per slice, a5 down items per slot (0: none): the layer's work queue holds
+                  // every (slot, slice) gate/up item, then every (slot, row block) down item
   OP_ATTN = 4,    // a0 b, a1 g, a2 k0, a3 k1 (-1 = to seq_len, the split holding the new token),
                   // a4 first partial of (b, g) in the layer, a5 split | nsplit << 16
   OP_OUT = 5,     // a0 row0, a1 nrows, a2 attention counter (KV group g's merges on sub-counters
-                  // g*CTR_SUB/HKV ..), a3 its target: x_{l+1} = x_l + W_o attn + sum_i w_i W_down[e_i] h_i
+                  // g*CTR_SUB/HKV ..), a3 its target, a4 1 = the down projections come from the queued
+                  // down items (y): x_{l+1} = x_l + W_o attn + sum_i w_i W_down[e_i] h_i
   OP_LMHEAD = 6,  // a0 row0, a1 nrows: logits + running argmax
   OP_MERGE = 7,   // a0 b, a1 g, a2 slice, a3 slices, a4 first partial, a5 nsplit: attention output
   OP_COUNT
@@ -95,6 +98,8 @@ struct Params {
   float* rlog;               // [L][MAXB][E]
   RouteTable* route;         // [L]
   float* h;                  // [L][MAXB][K][F]
+  float* y;                  // [L][MAXB][K][H] down projection of token b's i-th expert (queued down items)
+  uint32_t* slot_ctr;        // [L][64] lines of CTR_STRIDE: gate/up items done per union slot (zeroed per step)
   float* apart;              // [L][parts_per_layer][HPG * (D + 2)]
   float* attn;               // [L][MAXB][HQ * D]
   unsigned long long* amax;  // [MAXB] packed (ordered logit << 32 | ~index)

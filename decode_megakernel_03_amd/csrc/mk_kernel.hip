@@ -44,6 +44,7 @@ using ShapeFull = Shape<2048, 128, 32, 4, 128, 8, 768>;
 constexpr int SPLIT_MAX = 1024;   // keys one attention task may cover (LDS score buffer)
 constexpr int MERGE_MAX = (SPLIT_MAX + 1) / 2;   // splits one (sequence, KV group) may have
 constexpr int OUT_MAXR = 5;       // most rows of one OUT task
+constexpr int DOWN_ROWS = 128;    // W_down rows of one queued down item (192 KB of the full-size expert)
 constexpr int STEAL_PROBES = 4;   // sub-queues an expert task draws from (its own, then 3 more)
 constexpr int SC1 = 16;           // buffer cache-policy bit for agent-coherent access
 
@@ -270,6 +271,41 @@ __device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) 
           if (__builtin_amdgcn_readfirstlane(ctr_load(&p.err->abort_flag))) { ok = 0; break; }
           if (now() - t0 > p.watchdog_ticks) {
             if (lane == 0) raise_error(p, DEV_TIMEOUT, task, c, target, v, 0);
+            ok = 0;
+            break;
+          }
+        }
+      }
+    }
+    if (lane == 0) {
+      ctl.ok = ok;
+      ctl.t_ready = now();
+    }
+  }
+  __syncthreads();
+  const bool ok = ctl.ok != 0;
+  __syncthreads();
+  return ok;
+}
+
+// Block until the single word *w (a union slot's count of finished gate/up items) reaches target
+// (wave 0 polls, the workgroup waits at a barrier). False if the step was aborted or the watchdog fired.
+__device__ bool wait_word(CParams& p, Ctl& ctl, const uint32_t* w, uint32_t target, int task, uint32_t detail) {
+  const int tx = tid(), lane = tx & 63;
+  if (__builtin_amdgcn_readfirstlane(tx >> 6) == 0) {
+    int ok = 1;
+    uint32_t v = __builtin_amdgcn_readfirstlane(ctr_load(w));
+    if (v < target) {
+      const uint64_t t0 = now();
+      uint32_t it = 0;
+      for (;;) {
+        __builtin_amdgcn_s_sleep(1);
+        v = __builtin_amdgcn_readfirstlane(ctr_load(w));
+        if (v >= target) break;
+        if ((++it & 15u) == 0) {
+          if (__builtin_amdgcn_readfirstlane(ctr_load(&p.err->abort_flag))) { ok = 0; break; }
+          if (now() - t0 > p.watchdog_ticks) {
+            if (lane == 0) raise_error(p, DEV_TIMEOUT, task, -1, target, v, detail);
             ok = 0;
             break;
           }
@@ -817,6 +853,7 @@ __device__ __forceinline__ bool op_router(int task) {
 // that only the route table and the weights are on the path after the router.
 template <class S, int TB>
 __device__ __forceinline__ bool op_gateup(int task) {
+  static_assert(TB * S::F <= TB * S::H, "down items stage h where the normed input lives");
   CParams& p = P();
   Ctl& ctl = ctl_s;
   float* sm = smem;
@@ -831,6 +868,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
   // steals from the next ones. The first draw is issued before the dependency waits.
   const bool dyn = T.a3 >= 0;
   const int nq = dyn ? T.a1 : 1;
+  const int qd = dyn ? T.a5 : 0;          // down items per union slot (queue mode)
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   int sq = dyn ? T.a0 : 0;
   // a draw: lane 0 of wave 0 takes the next item of sub-queue q; lanes < nq read every sub-queue's
@@ -867,8 +905,9 @@ __device__ __forceinline__ bool op_gateup(int task) {
   unsigned long long u0 = 0, u1 = 0;
   for (int b = 0; b < p.B; ++b) { u0 |= ctl.mask[b][0]; u1 |= ctl.mask[b][1]; }
   const int n0 = __builtin_popcountll(u0), nu = n0 + __builtin_popcountll(u1);
-  // rows f0..f0+nf of union slot u (the u-th selected expert in ascending order) for its tokens
-  auto run_item = [&](int u, int f0, int nf) {
+  // expert of union slot u (the u-th selected expert in ascending order); thread 0 lists its tokens
+  // (batch row, rank of the expert in that token's selection) in ctl.toks / ctl.trank, ctl.flag
+  auto slot_expert = [&](int u) {
     unsigned long long m = u < n0 ? u0 : u1;
     for (int j = u < n0 ? u : u - n0; j > 0; --j) m &= m - 1;
     const int e = (u < n0 ? 0 : 64) + __builtin_ctzll(m);
@@ -885,6 +924,19 @@ __device__ __forceinline__ bool op_gateup(int task) {
       }
       ctl.flag = nt;
     }
+    return e;
+  };
+  // rows f0..f0+nf of union slot u for its tokens
+  auto run_item = [&](int u, int f0, int nf) -> bool {
+    if (ctl.norm_l != l) {       // a down item used the staging area since: stage the normed input again
+      __syncthreads();
+      if (tid() < MAXB) ctl.toks[tid()] = tid();
+      __syncthreads();
+      stage_norm<S>(p, l, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
+      if (tid() == 0) ctl.norm_l = l;
+      __syncthreads();
+    }
+    const int e = slot_expert(u);
     const uint16_t* wg = Lp.w_gate + (size_t)e * F * H;
     const uint16_t* wu = Lp.w_up + (size_t)e * F * H;
     auto rowptr = [&](int r) { return r < nf ? wg + (size_t)(f0 + r) * H : wu + (size_t)(f0 + r - nf) * H; };
@@ -909,7 +961,69 @@ __device__ __forceinline__ bool op_gateup(int task) {
       const float hv = (g / (1.f + expf(-g))) * up;
       stc(Hb, 4u * ((ctl.toks[t] * K + ctl.trank[t]) * F + f0 + f), hv);
     }
+    if (qd > 0) {
+      // one more finished gate/up item of slot u: its h rows are visible before the count moves
+      drain();
+      __syncthreads();
+      if (tx == 0) ctr_add(p.slot_ctr + ((size_t)l * MAX_SLOTS + u) * CTR_STRIDE, 1u);
+    }
     __syncthreads();      // toks / trank / gu are rewritten by the next item
+    return true;
+  };
+  // down item q of union slot u: rows q*DOWN_ROWS.. of W_down[e] for every token of the slot, once
+  // every gate/up item of the slot is done: y[b][rank][row] = W_down[e][row] . h[b][rank]. Its weight
+  // rows are requested before the slot's count is awaited. The staged h overwrites the normed input.
+  auto run_down = [&](int u, int q, int slices_c) -> bool {
+    constexpr int NPD = 4;
+    const int e = slot_expert(u);
+    const int row0 = q * DOWN_ROWS, nr = H - row0 < DOWN_ROWS ? H - row0 : DOWN_ROWS;
+    const uint16_t* wd = Lp.w_down + ((size_t)e * H + row0) * F;
+    auto rowptr = [&](int r) { return wd + (size_t)r * F; };
+    WBuf<F, NPD> A;
+    load_block<F, NPD>(A, 0, nr, rowptr);
+    if (tid() == 0) ctl.norm_l = -1;
+    __syncthreads();
+    const int ntok = ctl.flag;
+    int yoff[TB], hoff[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      const int bt = t < ntok ? ctl.toks[t] : 0, rk = t < ntok ? ctl.trank[t] : 0;
+      yoff[t] = (bt * K + rk) * H + row0;
+      hoff[t] = (bt * K + rk) * F;
+    }
+    if (!wait_word(p, ctl, p.slot_ctr + ((size_t)l * MAX_SLOTS + u) * CTR_STRIDE, (uint32_t)slices_c, T.id, (uint32_t)u))
+      return false;
+    // h of every token of the slot into LDS: all loads first, then the writes
+    const __amdgpu_buffer_rsrc_t Hr = rsrc(p.h + (size_t)l * MAXB * K * F);
+    constexpr int NI = (TB * F + 4 * NT - 1) / (4 * NT);
+    f4 hv[NI];
+#pragma unroll
+    for (int v = 0; v < NI; ++v) {
+      const int idx = (v * NT + tx) * 4, t = idx / F, f = idx - t * F;
+      int ho = 0;
+#pragma unroll
+      for (int tt = 0; tt < TB; ++tt) if (tt == t) ho = hoff[tt];
+      hv[v] = t < ntok ? ldc4(Hr, 4u * (ho + f)) : f4{0.f, 0.f, 0.f, 0.f};
+    }
+#pragma unroll
+    for (int v = 0; v < NI; ++v) {
+      const int idx = (v * NT + tx) * 4, t = idx / F;
+      if (t < ntok) *reinterpret_cast<f4*>(sm + idx) = hv[v];
+    }
+    __syncthreads();
+    MARK(5);
+    const __amdgpu_buffer_rsrc_t Y = rsrc(p.y + (size_t)l * MAXB * K * H);
+    gemv_stream<F, NPD, TB>(A, true, nr, ntok, rowptr,
+        [&](int r, int t) { return sm + (size_t)t * F; },
+        [&](int r, int t, float v) {
+          int yo = 0;
+#pragma unroll
+          for (int tt = 0; tt < TB; ++tt) if (tt == t) yo = yoff[tt];
+          stc(Y, 4u * (yo + r), v);
+        });
+    MARK(6);
+    __syncthreads();      // toks / trank / the staged h are rewritten by the next item
+    return true;
   };
   if (!dyn) {
     if (T.a0 < nu) run_item(T.a0, T.a1, T.a2);
@@ -920,7 +1034,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
     const int slices = T.a2, nfs = T.a4;
     const int grain = (nu * slices >= 4 * p.n_workers && 2 * nfs <= 32) ? 2 : 1;
     const int slices_c = (slices + grain - 1) / grain, rows = grain * nfs;
-    const int n_items = nu * slices_c;
+    const int n_gu = nu * slices_c;                 // gate/up items first, then the down items
+    const int n_items = n_gu + nu * qd;
     // hand the draw to the workgroup, with the sub-queue that had the most items left in the
     // snapshot (-1: none had any)
     auto publish = [&]() {
@@ -951,8 +1066,13 @@ __device__ __forceinline__ bool op_gateup(int task) {
         continue;
       }
       draw(sq);                         // the next draw, in flight during the item
-      const int u = i / slices_c, j = i - u * slices_c, f0 = j * rows;
-      run_item(u, f0, F - f0 < rows ? F - f0 : rows);
+      if (i < n_gu) {
+        const int u = i / slices_c, j = i - u * slices_c, f0 = j * rows;
+        run_item(u, f0, F - f0 < rows ? F - f0 : rows);
+      } else {
+        const int i2 = i - n_gu, u = i2 / qd;
+        if (!run_down(u, i2 - u * qd, slices_c)) return false;
+      }
       publish();
     }
   }
@@ -1765,6 +1885,51 @@ __device__ __forceinline__ bool op_out_batch(int task) {
       xv = ldc(rsrc(p.x + ((size_t)l * MAXB + b) * H), 4u * row);
     }
   }
+  if (T.a4) {
+    // the down projections were computed by the queued down items: y[b][i][row] for token b's i-th
+    // expert; the MoE term sums w_i y_i in ascending expert order, as the form below does
+    WBuf<AD, NPO> WO;
+    auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * AD; };
+    load_block<AD, NPO>(WO, 0, nrows, orow);
+    if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every expert task (all items)
+    MARK(0);
+    if (tx < B * nrows) {
+      const int b = tx / nrows, r = tx % nrows;
+      const __amdgpu_buffer_rsrc_t Yr = rsrc(p.y + (size_t)l * MAXB * K * H);
+      float yv[K];
+#pragma unroll
+      for (int i = 0; i < K; ++i) yv[i] = ldc(Yr, 4u * ((b * K + i) * H + row0 + r));
+      float moe = 0.f;
+#pragma unroll
+      for (int i = 0; i < K; ++i) moe = moe + rt.w[b][i] * yv[i];
+      mo_s[b * OUT_MAXR + r] = moe;
+      xv_s[b * OUT_MAXR + r] = xv;
+    }
+    MARK(1);
+    float* a_s = sm + LY::A;
+    if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
+    for (int b0 = 0; b0 < B; b0 += OUT_OT) {
+      const int nt = B - b0 < OUT_OT ? B - b0 : OUT_OT;
+      stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
+      __syncthreads();
+      if (b0 == 0) MARK(2);
+      compute_block_shared<AD, NPO, OUT_OT>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
+                                            [&](int r, int t, float v) { o_s[t * OUT_MAXR + r] = v; });
+      __syncthreads();
+      if (tx < nt * nrows) {
+        const int t = tx / nrows, r = tx % nrows, b = b0 + t, row = row0 + r;
+        const float xn = (xv_s[b * OUT_MAXR + r] + o_s[t * OUT_MAXR + r]) + mo_s[b * OUT_MAXR + r];
+        stc(Xn, 4u * (b * H + row), xn);
+        if (p.hidden_out && l == p.L - 1) p.hidden_out[(size_t)b * H + row] = xn;
+      }
+      __syncthreads();
+    }
+    MARK(3);
+    drain_t(p);
+    MARK(4);
+    signal(p, ctl, T.sig, false);
+    return true;
+  }
   // W_down rows of token b: q = i * nrows + r is row row0 + r of its i-th expert
   auto drow_of = [&](int b) {
     return [&, b](int q) {
@@ -1941,6 +2106,8 @@ __device__ void finish(CParams& p, Ctl& ctl) {
   }
   for (int i = tid(); i < p.n_ctr * CTR_SUB; i += NT)
     if (i / CTR_SUB != p.done_ctr) __hip_atomic_store(p.ctr + (size_t)i * CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = tid(); i < p.L * MAX_SLOTS; i += NT)
+    __hip_atomic_store(p.slot_ctr + (size_t)i * CTR_STRIDE, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   drain();
   __syncthreads();
   if (tid() < CTR_SUB) __hip_atomic_store(ctr_at(p, p.done_ctr, tid()), 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2158,5 +2325,6 @@ hipError_t litmus_occupancy(int* blocks_per_cu) {
 int split_max() { return SPLIT_MAX; }
 int merge_max() { return MERGE_MAX; }
 int out_max_rows() { return OUT_MAXR; }
+int down_rows() { return DOWN_ROWS; }
 
 }  // namespace mk

@@ -14,6 +14,7 @@ hipError_t step_occupancy(int shape, int batch, int* blocks_per_cu);
 int split_max();      // keys one attention task may cover
 int merge_max();      // attention splits one (sequence, KV group) may have
 int out_max_rows();   // rows of one OUT task
+int down_rows();      // W_down rows of one queued down item
 // plain streaming read of n16 16-byte words on `blocks` workgroups of 256 threads (measurement)
 hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, int blocks, hipStream_t st);
 // hand-off litmus test (cooperative launch of `grid` workgroups of 256 threads); res[4] as documented
