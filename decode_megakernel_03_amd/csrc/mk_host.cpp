@@ -839,7 +839,7 @@ mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens
     return MK_ERR_INVALID_ARG;
   }
   int per_cu = 0;
-  HIPCHK(e, step_occupancy(e->shape, batch, &per_cu));
+  HIPCHK(e, step_occupancy(e->shape, batch, e->opt.flags, &per_cu));
   const int wpc = std::min(e->opt.workers_per_cu, per_cu);
   if (wpc < 1) { e->msg = "kernel does not fit on a CU"; return MK_ERR_UNSUPPORTED; }
   mk_plan* P = new mk_plan();

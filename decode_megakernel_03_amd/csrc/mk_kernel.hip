@@ -376,7 +376,7 @@ __device__ __forceinline__ void drain_t(CParams& p) {
 // number of earlier signals. A signal of group `grp` >= 0 (of the attention counter's HKV groups)
 // adds to one of that group's CTR_SUB / HKV sub-counters, so that a waiter can count each group.
 template <int HKV = 1>
-__device__ uint32_t signal(CParams& p, Ctl& ctl, int c, bool want_old, int grp = -1) {
+__device__ __forceinline__ uint32_t signal(CParams& p, Ctl& ctl, int c, bool want_old, int grp = -1) {
   drain();
   __syncthreads();
   uint32_t old = 0;
@@ -1025,9 +1025,9 @@ __device__ __forceinline__ bool op_gateup(int task) {
     __syncthreads();      // toks / trank / the staged h are rewritten by the next item
     return true;
   };
-  if (!dyn) {
+  if (TB == 1 || !dyn) {           // one token: static slices only (the queue is never scheduled)
     if (T.a0 < nu) run_item(T.a0, T.a1, T.a2);
-  } else {
+  } else if constexpr (TB > 1) {
     // item size from the step's union: with at least four slices per worker, a draw takes two
     // adjacent slices (fewer draws and larger streams); a small union (skewed routing) keeps
     // single slices so that the work spreads over more workers. Every task derives the same grain.
@@ -1744,7 +1744,7 @@ __device__ __forceinline__ bool oproj_grouped(CParams& p, Ctl& ctl, const WBuf<S
 //   x_{l+1} = (x_l + W_o attn) + sum_i w_i W_down[e_i] h_i   (experts in ascending index).
 // Waits for the routing table (to prefetch the right W_down rows), then for the MoE slices (the
 // MoE term is formed first), then for the attention of every KV group.
-template <class S, int TB>
+template <class S, int TB, int VAR>
 __device__ __forceinline__ bool op_out(int task) {
   CParams& p = P();
   Ctl& ctl = ctl_s;
@@ -1812,10 +1812,12 @@ __device__ __forceinline__ bool op_out(int task) {
     }
   }
   MARK(1);
-  const bool per_group = (p.flags & 8) != 0;
+  // the per-KV-group form is compiled into a kernel instance of its own (VAR 1), so that its code does
+  // not change the register allocation of the default form
+  constexpr bool per_group = VAR == 1;
   if (!per_group && !wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;   // attention of every KV group
   for (int b = 0; b < p.B; ++b) {
-    if (per_group) {      // KV group by KV group as each group's merges land (ablation)
+    if constexpr (per_group) {      // KV group by KV group as each group's merges land (ablation)
       if (!oproj_grouped<S, NPO, 1>(p, ctl, WO, nrows, b, 1, T.a2, T.a3 / S::HKV, b == 0, true, T.id, a_s, At,
                                     [&](int r, int t, float v) { o_s[r] = v; }))
         return false;
@@ -2114,7 +2116,7 @@ __device__ void finish(CParams& p, Ctl& ctl) {
   if (tid() == 0) __hip_atomic_store(top, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <class S, int TB>
+template <class S, int TB, int VAR>
 __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
   CParams& p = P();
   const int qs = cst(p.qoff)[blockIdx.x], qe = cst(p.qoff)[blockIdx.x + 1];
@@ -2151,7 +2153,7 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
       case OP_GATEUP: ok = op_gateup<S, TB>(ti); break;
       case OP_ATTN: ok = op_attn<S, TB>(ti); break;
       case OP_OUT:
-        if constexpr (TB == 1) ok = op_out<S, TB>(ti);
+        if constexpr (TB == 1) ok = op_out<S, TB, VAR>(ti);
         else ok = op_out_batch<S, TB>(ti);
         break;
       case OP_LMHEAD: ok = op_lmhead<S, TB>(ti); break;
@@ -2187,23 +2189,23 @@ constexpr size_t lds_bytes(int tb) {
 static_assert(2 * (lds_bytes<ShapeFull>(1) + sizeof(Ctl)) <= 160 * 1024, "batch-1 kernel: LDS for two workers per CU");
 static_assert(2 * (lds_bytes<ShapeFull>(MAXB) + sizeof(Ctl)) <= 160 * 1024, "batch-8 kernel: LDS for two workers per CU");
 
-template <class S, int TB>
+template <class S, int TB, int VAR = 0>
 static hipError_t launch_one(const Params& p, int grid, hipStream_t st, size_t* lds_out) {
   const size_t lds = lds_bytes<S>(TB);
   if (lds_out) *lds_out = lds;
-  hipError_t e = hipFuncSetAttribute((const void*)mk_step<S, TB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = hipFuncSetAttribute((const void*)mk_step<S, TB, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   Params pp = p;
   void* args[] = {&pp};
-  return hipLaunchCooperativeKernel((const void*)mk_step<S, TB>, dim3(grid), dim3(NT), args, (unsigned)lds, st);
+  return hipLaunchCooperativeKernel((const void*)mk_step<S, TB, VAR>, dim3(grid), dim3(NT), args, (unsigned)lds, st);
 }
 
-template <class S, int TB>
+template <class S, int TB, int VAR = 0>
 static hipError_t occupancy_one(int* blocks_per_cu) {
   const size_t lds = lds_bytes<S>(TB);
-  hipError_t e = hipFuncSetAttribute((const void*)mk_step<S, TB>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  hipError_t e = hipFuncSetAttribute((const void*)mk_step<S, TB, VAR>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)mk_step<S, TB>, NT, lds);
+  return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)mk_step<S, TB, VAR>, NT, lds);
 }
 
 int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F) {
@@ -2214,14 +2216,25 @@ int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F) {
   return -1;
 }
 
+// batch 1 with MK_FLAG_OPROJ_PER_GROUP runs the kernel instance with the per-KV-group O projection
 hipError_t launch_step(int shape, int batch, const Params& p, int grid, hipStream_t st, size_t* lds) {
-  if (shape == 0) return batch == 1 ? launch_one<ShapeSmall, 1>(p, grid, st, lds) : launch_one<ShapeSmall, MAXB>(p, grid, st, lds);
-  return batch == 1 ? launch_one<ShapeFull, 1>(p, grid, st, lds) : launch_one<ShapeFull, MAXB>(p, grid, st, lds);
+  const bool pg = batch == 1 && (p.flags & 8);
+  if (shape == 0) {
+    if (batch > 1) return launch_one<ShapeSmall, MAXB>(p, grid, st, lds);
+    return pg ? launch_one<ShapeSmall, 1, 1>(p, grid, st, lds) : launch_one<ShapeSmall, 1>(p, grid, st, lds);
+  }
+  if (batch > 1) return launch_one<ShapeFull, MAXB>(p, grid, st, lds);
+  return pg ? launch_one<ShapeFull, 1, 1>(p, grid, st, lds) : launch_one<ShapeFull, 1>(p, grid, st, lds);
 }
 
-hipError_t step_occupancy(int shape, int batch, int* blocks_per_cu) {
-  if (shape == 0) return batch == 1 ? occupancy_one<ShapeSmall, 1>(blocks_per_cu) : occupancy_one<ShapeSmall, MAXB>(blocks_per_cu);
-  return batch == 1 ? occupancy_one<ShapeFull, 1>(blocks_per_cu) : occupancy_one<ShapeFull, MAXB>(blocks_per_cu);
+hipError_t step_occupancy(int shape, int batch, int flags, int* blocks_per_cu) {
+  const bool pg = batch == 1 && (flags & 8);
+  if (shape == 0) {
+    if (batch > 1) return occupancy_one<ShapeSmall, MAXB>(blocks_per_cu);
+    return pg ? occupancy_one<ShapeSmall, 1, 1>(blocks_per_cu) : occupancy_one<ShapeSmall, 1>(blocks_per_cu);
+  }
+  if (batch > 1) return occupancy_one<ShapeFull, MAXB>(blocks_per_cu);
+  return pg ? occupancy_one<ShapeFull, 1, 1>(blocks_per_cu) : occupancy_one<ShapeFull, 1>(blocks_per_cu);
 }
 
 // Plain streaming read of n16 16-byte words (a bandwidth ceiling for comparison with the step

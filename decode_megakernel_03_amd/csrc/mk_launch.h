@@ -10,7 +10,7 @@ namespace mk {
 int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F);
 // cooperative launch of one step on `grid` workers (batch 1 or up to 8 instance)
 hipError_t launch_step(int shape, int batch, const Params& p, int grid, hipStream_t st, size_t* lds_bytes);
-hipError_t step_occupancy(int shape, int batch, int* blocks_per_cu);
+hipError_t step_occupancy(int shape, int batch, int flags, int* blocks_per_cu);
 int split_max();      // keys one attention task may cover
 int merge_max();      // attention splits one (sequence, KV group) may have
 int out_max_rows();   // rows of one OUT task
