@@ -1011,7 +1011,7 @@ mk_status mk_handoff_litmus(int32_t rounds, int32_t words, int32_t workgroups, u
   // flag, done and res on lines of their own (256 bytes apart)
   if (hipMalloc(&ctl, 3 * 256) != hipSuccess) { (void)hipFree(data); return MK_ERR_OOM; }
   mk_status st = MK_OK;
-  uint32_t res[4] = {0, 0, 0, 0};
+  uint32_t res[6] = {0, 0, 0, 0, 0, 0};
   if (hipMemset(data, 0, sizeof(uint32_t) * (size_t)words) != hipSuccess || hipMemset(ctl, 0, 3 * 256) != hipSuccess ||
       launch_litmus(data, ctl, ctl + 64, ctl + 128, rounds, words, workgroups, 100000000ull /* 1 s */, nullptr) != hipSuccess ||
       hipDeviceSynchronize() != hipSuccess || hipMemcpy(res, ctl + 128, sizeof res, hipMemcpyDeviceToHost) != hipSuccess)
@@ -1019,9 +1019,9 @@ mk_status mk_handoff_litmus(int32_t rounds, int32_t words, int32_t workgroups, u
   (void)hipFree(data);
   (void)hipFree(ctl);
   if (st != MK_OK) return st;
-  *stale = res[0];
-  *checked = res[1];
-  if (res[3] != 0 || (int32_t)res[2] != rounds) return MK_ERR_DEVICE;   // a wait hit the watchdog
+  *stale = res[0] | ((uint64_t)res[1] << 32);
+  *checked = res[2] | ((uint64_t)res[3] << 32);
+  if (res[5] != 0 || (int32_t)res[4] != rounds) return MK_ERR_DEVICE;   // a wait hit the watchdog
   return MK_OK;
 }
 

@@ -2269,7 +2269,8 @@ hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, int b
 // (stale). A consumer then bumps `done`; the next producer waits for every consumer of the previous
 // round before it overwrites the words. Every wait is bounded by the watchdog (res[3] set, and every
 // workgroup leaves its loop once it sees that), so the grid always drains.
-// res: [0] stale words, [1] words checked, [2] rounds completed by workgroup 0, [3] watchdog fired.
+// res (uint32 words): [0..1] stale words and [2..3] words checked (64-bit), [4] rounds completed by
+// workgroup 0, [5] watchdog fired.
 __device__ bool litmus_wait(uint32_t* c, uint32_t target, uint32_t* res, uint64_t wd) {
   __shared__ int ok_s;
   const int tx = tid(), lane = tx & 63;
@@ -2280,9 +2281,9 @@ __device__ bool litmus_wait(uint32_t* c, uint32_t target, uint32_t* res, uint64_
     while (__builtin_amdgcn_readfirstlane(ctr_load(c)) < target) {
       __builtin_amdgcn_s_sleep(1);
       if ((++it & 15u) == 0) {
-        if (__builtin_amdgcn_readfirstlane(ctr_load(res + 3)) != 0u) { ok = 0; break; }
+        if (__builtin_amdgcn_readfirstlane(ctr_load(res + 5)) != 0u) { ok = 0; break; }
         if (now() - t0 > wd) {
-          if (lane == 0) __hip_atomic_store(res + 3, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          if (lane == 0) __hip_atomic_store(res + 5, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ok = 0;
           break;
         }
@@ -2320,9 +2321,9 @@ __global__ void __launch_bounds__(NT) handoff_litmus(uint32_t* data, uint32_t* f
       if (tx == 0) ctr_add(done, 1u);
     }
   }
-  if (stale) atomicAdd(res + 0, stale);
-  if (checked) atomicAdd(res + 1, checked);
-  if (me == 0 && tx == 0) atomicAdd(res + 2, (uint32_t)(r - 1));
+  if (stale) atomicAdd(reinterpret_cast<unsigned long long*>(res), (unsigned long long)stale);
+  if (checked) atomicAdd(reinterpret_cast<unsigned long long*>(res + 2), (unsigned long long)checked);
+  if (me == 0 && tx == 0) atomicAdd(res + 4, (uint32_t)(r - 1));
 }
 
 hipError_t launch_litmus(uint32_t* data, uint32_t* flag, uint32_t* done, uint32_t* res, int rounds, int words,
