@@ -1025,6 +1025,32 @@ mk_status mk_handoff_litmus(int32_t rounds, int32_t words, int32_t workgroups, u
   return MK_OK;
 }
 
+static_assert(LITMUS_SCRATCH_WORDS == MK_LITMUS_NOALLOC_MAX_WORDS, "the scratch array holds the documented maximum");
+
+mk_status mk_handoff_litmus_noalloc(int32_t rounds, int32_t words, int32_t workgroups, uint64_t* stale, uint64_t* checked) {
+  if (!stale || !checked || rounds < 1 || rounds > 100000 || words < 1 || workgroups < 2) return MK_ERR_INVALID_ARG;
+  if (words > MK_LITMUS_NOALLOC_MAX_WORDS) {
+    fprintf(stderr, "mk_handoff_litmus_noalloc: %d words exceed the scratch array's %d\n", words, MK_LITMUS_NOALLOC_MAX_WORDS);
+    return MK_ERR_INVALID_ARG;
+  }
+  int dev = 0, ncu = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      litmus_occupancy(&per_cu) != hipSuccess)
+    return MK_ERR_HIP;
+  if (workgroups > ncu * per_cu) return MK_ERR_INVALID_ARG;      // every workgroup must be co-resident
+  uint32_t* base = nullptr;
+  uint32_t res[6] = {0, 0, 0, 0, 0, 0};
+  if (litmus_scratch(&base) != hipSuccess ||
+      launch_litmus_scratch(base, rounds, words, workgroups, 100000000ull /* 1 s */, nullptr) != hipSuccess ||
+      hipStreamSynchronize(nullptr) != hipSuccess ||
+      hipMemcpy(res, base + 2 * CTR_STRIDE, sizeof res, hipMemcpyDeviceToHost) != hipSuccess)
+    return MK_ERR_HIP;
+  *stale = res[0] | ((uint64_t)res[1] << 32);
+  *checked = res[2] | ((uint64_t)res[3] << 32);
+  if (res[5] != 0 || (int32_t)res[4] != rounds) return MK_ERR_DEVICE;   // a wait hit the watchdog
+  return MK_OK;
+}
+
 // ---- host-only schedule API ---------------------------------------------------------------
 
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* seq_lens_host, int32_t n_workers,

@@ -22,6 +22,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "mk_internal.h"
 #include "mk_launch.h"
 
@@ -2334,6 +2336,48 @@ hipError_t launch_litmus(uint32_t* data, uint32_t* flag, uint32_t* done, uint32_
 
 hipError_t litmus_occupancy(int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)handoff_litmus, NT, 0);
+}
+
+// ---- the allocation-free variant of the hand-off litmus test -------------------------------
+// Its buffers (flag, done and result lines, then the hand-off words) live in `scratch`, a file-scope
+// device array of a fixed size that every GPU holds until the process ends. Host code never passes
+// the array's name to a kernel (in host code it is a host-side stand-in): the device address of this
+// GPU's copy comes from hipGetSymbolAddress, once per device, and only that address is used.
+constexpr int LITMUS_CTL_WORDS = 3 * CTR_STRIDE;       // flag, done, result: one 256-byte line each
+static __device__ __align__(256) uint32_t scratch[LITMUS_CTL_WORDS + LITMUS_SCRATCH_WORDS];
+
+__global__ void __launch_bounds__(256) fill_zero(uint32_t* p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+constexpr int MAX_DEVICES = 64;
+static uint32_t* scratch_ptr[MAX_DEVICES];
+static std::mutex scratch_mutex;
+
+hipError_t litmus_scratch(uint32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mutex);
+  if (!scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));   // this device's copy (it is current)
+    if (e != hipSuccess) return e;
+    if (!ptr) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = static_cast<uint32_t*>(ptr);
+  }
+  *out = scratch_ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t launch_litmus_scratch(uint32_t* base, int rounds, int words, int grid, uint64_t wd_ticks, hipStream_t st) {
+  const int n = LITMUS_CTL_WORDS + words;
+  hipLaunchKernelGGL(fill_zero, dim3((n + 255) / 256 < 256 ? (n + 255) / 256 : 256), dim3(256), 0, st, base, n);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  return launch_litmus(base + LITMUS_CTL_WORDS, base, base + CTR_STRIDE, base + 2 * CTR_STRIDE, rounds, words, grid,
+                       wd_ticks, st);
 }
 
 int split_max() { return SPLIT_MAX; }

@@ -21,4 +21,9 @@ hipError_t launch_stream_read(const void* src, size_t n16, uint32_t* sink, int b
 hipError_t launch_litmus(uint32_t* data, uint32_t* flag, uint32_t* done, uint32_t* res, int rounds, int words,
                          int grid, uint64_t wd_ticks, hipStream_t st);
 hipError_t litmus_occupancy(int* blocks_per_cu);
+// allocation-free form: this device's address of the file-scope scratch array (looked up once per
+// device), and a launch that clears its control lines and words with a fill kernel, then runs the test
+constexpr int LITMUS_SCRATCH_WORDS = 16384;   // hand-off words the scratch array holds (64 KB)
+hipError_t litmus_scratch(uint32_t** base);
+hipError_t launch_litmus_scratch(uint32_t* base, int rounds, int words, int grid, uint64_t wd_ticks, hipStream_t st);
 }  // namespace mk

@@ -26,7 +26,7 @@ DESC_WORDS = 16
 EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_decode_step", "mk_set_step_outputs",
             "mk_sync", "mk_get_error", "mk_reset", "mk_destroy", "mk_plan_build", "mk_plan_info_get",
             "mk_plan_export", "mk_plan_validate", "mk_plan_simulate", "mk_engine_plan", "mk_plan_destroy",
-            "mk_stream_read_bandwidth", "mk_handoff_litmus"]
+            "mk_stream_read_bandwidth", "mk_handoff_litmus", "mk_handoff_litmus_noalloc"]
 
 
 class MkError(RuntimeError):
@@ -87,6 +87,7 @@ def load(path=LIB_PATH):
         "mk_plan_destroy": [vp],
         "mk_stream_read_bandwidth": [vp, sz, i32, ctypes.POINTER(ctypes.c_double)],
         "mk_handoff_litmus": [i32, i32, i32, ctypes.POINTER(u64), ctypes.POINTER(u64)],
+        "mk_handoff_litmus_noalloc": [i32, i32, i32, ctypes.POINTER(u64), ctypes.POINTER(u64)],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -189,6 +190,16 @@ def mk_handoff_litmus(rounds, words, workgroups):
     """Hand-off protocol self-test; returns (status, stale words, words checked)."""
     stale, checked = ctypes.c_uint64(0), ctypes.c_uint64(0)
     st = LIB.mk_handoff_litmus(int(rounds), int(words), int(workgroups), ctypes.byref(stale), ctypes.byref(checked))
+    return st, stale.value, checked.value
+
+
+MK_LITMUS_NOALLOC_MAX_WORDS = 16384
+
+
+def mk_handoff_litmus_noalloc(rounds, words, workgroups):
+    """The allocation-free form of mk_handoff_litmus (fixed device scratch array); (status, stale, checked)."""
+    stale, checked = ctypes.c_uint64(0), ctypes.c_uint64(0)
+    st = LIB.mk_handoff_litmus_noalloc(int(rounds), int(words), int(workgroups), ctypes.byref(stale), ctypes.byref(checked))
     return st, stale.value, checked.value
 
 

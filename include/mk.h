@@ -225,6 +225,18 @@ mk_status mk_stream_read_bandwidth(const void* buf, size_t bytes, int32_t reps, 
  * MK_ERR_DEVICE if a wait exceeded its 1 s bound; MK_ERR_HIP / MK_ERR_OOM on runtime failures. */
 mk_status mk_handoff_litmus(int32_t rounds, int32_t words, int32_t workgroups, uint64_t* stale, uint64_t* checked);
 
+/* mk_handoff_litmus for callers that cannot allocate device memory (tight serving loops, harnesses
+ * that forbid hipMalloc): the same test and results, with its buffers in a fixed device array that
+ * every GPU the library runs on holds until the process ends (the words plus three 256-byte control
+ * lines, 64.75 KB); the array is cleared by a fill kernel at every call. It calls no hipMalloc, hipFree
+ * or other allocating routine. MK_ERR_INVALID_ARG (and a message on stderr) for words beyond
+ * MK_LITMUS_NOALLOC_MAX_WORDS, otherwise the statuses of mk_handoff_litmus. Calls that overlap on one
+ * GPU (from several threads, or with work still running on other streams that use it) race on the
+ * shared array; the call itself is synchronous on the default stream. */
+#define MK_LITMUS_NOALLOC_MAX_WORDS 16384
+mk_status mk_handoff_litmus_noalloc(int32_t rounds, int32_t words, int32_t workgroups, uint64_t* stale,
+                                    uint64_t* checked);
+
 /* ---- schedule inspection (host only: no GPU needed) -------------------------------------- */
 /* The static schedule the host builds for a step (P3 "Scheduling and Performance Benchmarks":
  * mostly static scheduling), inspected, validated and simulated without a GPU. */
