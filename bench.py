@@ -32,7 +32,7 @@ def log(*a):
 
 def kernel_source_hash():
     h = hashlib.sha256()
-    for f in ("mk_kernel.hip", "mk_host.cpp", "mk_internal.h"):
+    for f in ("mk_kernel.hip", "mk_host.cpp", "mk_internal.h"):    # the kernel and its schedule
         h.update(open(os.path.join(ROOT, "decode_megakernel_03_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -50,11 +50,29 @@ def parse():
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--no-b8", action="store_true", help="with the default workload, skip the batch-8 line in the JSON")
-    ap.add_argument("--trace", default="", help="write the traced step's summary (.txt), records (.npy) and Chrome JSON here")
+    ap.add_argument("--trace", default="", help="write the traced step's summary (.txt) here")
+    ap.add_argument("--trace-records", action="store_true", help="with --trace, also write the records (.npy) and a Chrome JSON")
     ap.add_argument("--no-trace-stats", action="store_true", help="skip the traced step after timing")
     ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a 1 GiB device copy (for scaling HBM counters)")
+                    help="only run a 1 GiB device copy (for scaling the HBM write counter)")
+    ap.add_argument("--read-calibration", action="store_true",
+                    help="only stream 1 GiB with the library's read kernel, 3 dispatches (for scaling the HBM "
+                         "read counter: the same 16-byte non-temporal loads as the step kernel)")
     return ap.parse_args()
+
+
+def read_calibration():
+    import torch
+    from decode_megakernel_03_amd import mk
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda")
+    a.fill_(1)
+    torch.cuda.synchronize()
+    bw = mk.mk_stream_read_bandwidth(a.data_ptr(), n, 2)     # one untimed pass + 2 timed: 3 dispatches
+    torch.cuda.synchronize()
+    del a
+    torch.cuda.empty_cache()
+    print(json.dumps({"read_bytes_per_dispatch": n, "dispatches": 3, "bandwidth_gb_s": round(bw / 1e9, 1)}))
 
 
 def copy_calibration():
@@ -79,6 +97,8 @@ def main():
     import torch
     if args.copy_calibration:
         return copy_calibration()
+    if args.read_calibration:
+        return read_calibration()
     from decode_megakernel_03_amd import metrics, mk, synth
 
     over = {}
@@ -307,8 +327,9 @@ def run_trace(args, eng, tokens, pos_all, bt, len_all, logits, h, total_steps, p
         os.makedirs(os.path.dirname(os.path.abspath(path)), exist_ok=True)
         with open(path + ".txt", "w") as f:
             f.write(summ + "\n")
-        np.save(path + ".npy", rec)
-        trace.chrome_json(rec, path + ".json")
+        if args.trace_records:
+            np.save(path + ".npy", rec)
+            trace.chrome_json(rec, path + ".json")
     return trace.fractions(rec, info.n_workers)
 
 
