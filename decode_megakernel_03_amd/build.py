@@ -19,7 +19,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
           "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-I", os.path.join(ROOT, "include"), "-I", CSRC]
-SOURCES = ["mk_kernel.hip", "mk_host.cpp"]
+SOURCES = ["mk_kernel.hip", "mk_host.cpp", "mk_server.cpp"]
 
 
 def build(verbose=True, csrc=CSRC, out=LIB):

@@ -718,6 +718,8 @@ struct mk_engine {
   std::string msg;
 };
 
+const mk_model_desc& engine_desc(const mk_engine* e) { return e->desc; }
+
 namespace {
 
 mk_status hip_fail(mk_engine* e, hipError_t err, const char* what) {

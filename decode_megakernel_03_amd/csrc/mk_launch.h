@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 
+#include "../../include/mk.h"
 #include "mk_internal.h"
 
 namespace mk {
@@ -27,3 +28,7 @@ constexpr int LITMUS_SCRATCH_WORDS = 16384;   // hand-off words the scratch arra
 hipError_t litmus_scratch(uint32_t** base);
 hipError_t launch_litmus_scratch(uint32_t* base, int rounds, int words, int grid, uint64_t wd_ticks, hipStream_t st);
 }  // namespace mk
+
+// The model description an engine was created with (for the serving loop in mk_server.cpp).
+struct mk_engine;
+const mk_model_desc& engine_desc(const mk_engine* e);

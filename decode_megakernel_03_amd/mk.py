@@ -26,7 +26,10 @@ DESC_WORDS = 16
 EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_decode_step", "mk_set_step_outputs",
             "mk_sync", "mk_get_error", "mk_reset", "mk_destroy", "mk_plan_build", "mk_plan_info_get",
             "mk_plan_export", "mk_plan_validate", "mk_plan_simulate", "mk_engine_plan", "mk_plan_destroy",
-            "mk_stream_read_bandwidth", "mk_handoff_litmus", "mk_handoff_litmus_noalloc"]
+            "mk_stream_read_bandwidth", "mk_handoff_litmus", "mk_handoff_litmus_noalloc",
+            "mk_server_create", "mk_server_submit", "mk_server_pause", "mk_server_resume", "mk_server_run",
+            "mk_server_wait", "mk_server_poll", "mk_server_take", "mk_server_stats", "mk_server_last_step",
+            "mk_server_get_error", "mk_server_destroy"]
 
 
 class MkError(RuntimeError):
@@ -62,6 +65,28 @@ class PlanInfo(ctypes.Structure):
                 ("n_attn_splits", ctypes.c_int32), ("key_capacity_min", ctypes.c_int32)]
 
 
+class ServerConfig(ctypes.Structure):
+    _fields_ = [("max_batch", ctypes.c_int32), ("start_held", ctypes.c_int32), ("topk_out", ctypes.c_void_p),
+                ("router_logits_out", ctypes.c_void_p), ("hidden_out", ctypes.c_void_p), ("logits_out", ctypes.c_void_p)]
+
+
+class Request(ctypes.Structure):
+    _fields_ = [("request_id", ctypes.c_int64), ("prompt_len", ctypes.c_int32), ("first_token", ctypes.c_int32),
+                ("max_new_tokens", ctypes.c_int32), ("n_pages", ctypes.c_int32), ("pages", ctypes.POINTER(ctypes.c_int32))]
+
+
+class ServerStep(ctypes.Structure):
+    _fields_ = [("step", ctypes.c_int64), ("batch", ctypes.c_int32), ("rebuilt", ctypes.c_int32),
+                ("request_id", ctypes.c_int64 * MK_MAX_BATCH), ("position", ctypes.c_int32 * MK_MAX_BATCH),
+                ("token_in", ctypes.c_int32 * MK_MAX_BATCH), ("token_out", ctypes.c_int32 * MK_MAX_BATCH)]
+
+
+class ServerStats(ctypes.Structure):
+    _fields_ = [("steps", ctypes.c_int64), ("tokens", ctypes.c_int64), ("rebuilds", ctypes.c_int64),
+                ("active", ctypes.c_int32), ("pending", ctypes.c_int32), ("finished", ctypes.c_int32),
+                ("paused", ctypes.c_int32), ("busy_seconds", ctypes.c_double)]
+
+
 def load(path=LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m decode_megakernel_03_amd.build`")
@@ -88,6 +113,16 @@ def load(path=LIB_PATH):
         "mk_stream_read_bandwidth": [vp, sz, i32, ctypes.POINTER(ctypes.c_double)],
         "mk_handoff_litmus": [i32, i32, i32, ctypes.POINTER(u64), ctypes.POINTER(u64)],
         "mk_handoff_litmus_noalloc": [i32, i32, i32, ctypes.POINTER(u64), ctypes.POINTER(u64)],
+        "mk_server_create": [vp, ctypes.POINTER(ServerConfig), ctypes.POINTER(vp)],
+        "mk_server_submit": [vp, ctypes.POINTER(Request)],
+        "mk_server_pause": [vp], "mk_server_resume": [vp], "mk_server_run": [vp, ctypes.c_int64],
+        "mk_server_wait": [vp],
+        "mk_server_poll": [vp, ctypes.POINTER(ctypes.c_int64), P32, i32],
+        "mk_server_take": [vp, ctypes.c_int64, P32, i32, P32],
+        "mk_server_stats": [vp, ctypes.POINTER(ServerStats)],
+        "mk_server_last_step": [vp, ctypes.POINTER(ServerStep), ctypes.POINTER(vp)],
+        "mk_server_get_error": [vp, ctypes.c_char_p, sz],
+        "mk_server_destroy": [vp],
     }
     for name, args in sig.items():
         f = getattr(lib, name)
@@ -334,3 +369,86 @@ class Engine:
             self.close()
         except Exception:
             pass
+
+
+# ---------------------------------------------------------------- the serving loop's decode owner
+
+def _server_check(h, st, what):
+    if st != MK_OK:
+        buf = ctypes.create_string_buffer(1024)
+        LIB.mk_server_get_error(h, buf, 1024)
+        raise MkError(st, f"{what}: {buf.value.decode()}")
+
+
+def mk_server_create(engine_h, max_batch, start_held=False, topk_out=None, router_logits_out=None, hidden_out=None,
+                     logits_out=None):
+    cfg = ServerConfig(int(max_batch), int(bool(start_held)), _ptr(topk_out).value, _ptr(router_logits_out).value,
+                       _ptr(hidden_out).value, _ptr(logits_out).value)
+    h = ctypes.c_void_p()
+    _check(LIB.mk_server_create(engine_h, ctypes.byref(cfg), ctypes.byref(h)), engine_h, "mk_server_create")
+    return h
+
+
+def mk_server_submit(h, request_id, pages, prompt_len, first_token, max_new_tokens):
+    arr = _i32_array(pages)
+    req = Request(int(request_id), int(prompt_len), int(first_token), int(max_new_tokens), len(pages),
+                  ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+    _server_check(h, LIB.mk_server_submit(h, ctypes.byref(req)), "mk_server_submit")
+
+
+def mk_server_pause(h):
+    _server_check(h, LIB.mk_server_pause(h), "mk_server_pause")
+
+
+def mk_server_resume(h):
+    _server_check(h, LIB.mk_server_resume(h), "mk_server_resume")
+
+
+def mk_server_run(h, n_steps):
+    _server_check(h, LIB.mk_server_run(h, int(n_steps)), "mk_server_run")
+
+
+def mk_server_wait(h):
+    _server_check(h, LIB.mk_server_wait(h), "mk_server_wait")
+
+
+def mk_server_poll(h, max_items=64):
+    ids = (ctypes.c_int64 * max_items)()
+    nt = (ctypes.c_int32 * max_items)()
+    n = LIB.mk_server_poll(h, ids, nt, max_items)
+    if n < 0:
+        raise MkError(MK_ERR_INVALID_ARG, "mk_server_poll")
+    return [(int(ids[i]), int(nt[i])) for i in range(n)]
+
+
+def mk_server_take(h, request_id, cap=1 << 16):
+    buf = (ctypes.c_int32 * cap)()
+    n = ctypes.c_int32(0)
+    _server_check(h, LIB.mk_server_take(h, int(request_id), buf, cap, ctypes.byref(n)), "mk_server_take")
+    return [int(buf[i]) for i in range(n.value)]
+
+
+def mk_server_stats(h):
+    st = ServerStats()
+    _server_check(h, LIB.mk_server_stats(h, ctypes.byref(st)), "mk_server_stats")
+    return st
+
+
+def mk_server_last_step(h):
+    rec = ServerStep()
+    lp = ctypes.c_void_p()
+    _server_check(h, LIB.mk_server_last_step(h, ctypes.byref(rec), ctypes.byref(lp)), "mk_server_last_step")
+    B = rec.batch
+    return {"step": rec.step, "batch": B, "rebuilt": bool(rec.rebuilt),
+            "request_id": list(rec.request_id[:B]), "position": list(rec.position[:B]),
+            "token_in": list(rec.token_in[:B]), "token_out": list(rec.token_out[:B]), "logits_ptr": lp.value}
+
+
+def mk_server_get_error(h):
+    buf = ctypes.create_string_buffer(1024)
+    st = LIB.mk_server_get_error(h, buf, 1024)
+    return st, buf.value.decode()
+
+
+def mk_server_destroy(h):
+    return LIB.mk_server_destroy(h)

@@ -219,6 +219,31 @@ def refill_sequence(wl, k, v, bt, b, new_ctx, extra_steps, seed):
     return out, token
 
 
+def prefill_pages(wl, k, v, pages, prompt_len, seed):
+    """Synthetic prefill of a new sequence: seeded N(0,1) bf16 K/V for positions [0, prompt_len) in the
+    pages it owns (in position order), in every layer, in place on whatever device k and v live."""
+    need = int((int(prompt_len) + wl.page_size - 1) // wl.page_size)
+    if need > len(pages):
+        raise ValueError(f"{len(pages)} pages cannot hold {prompt_len} positions")
+    if need == 0:
+        return
+    shape = (need, wl.n_kv_heads, wl.page_size, wl.head_dim)
+    for l in range(len(k)):
+        idx = torch.as_tensor(np.asarray(pages[:need], np.int64), device=k[l].device)
+        k[l][idx] = normal_bf16(shape, 1.0, seed, 7000 + 2 * l, k[l].device)
+        v[l][idx] = normal_bf16(shape, 1.0, seed, 7001 + 2 * l, v[l].device)
+
+
+def synthetic_requests(wl, seed, n, ctx=(1024, 32768), new_tokens=(1, 1024)):
+    """n requests of the ragged workload's refill rule: prompt length log-uniform in ctx, output budget
+    uniform in new_tokens (inclusive), first token uniform in [0, V). Returns (prompt_len, max_new, token)."""
+    rng = np.random.default_rng([seed, 17])
+    c = np.floor(np.exp(rng.uniform(math.log(ctx[0]), math.log(ctx[1]), size=n))).astype(np.int64)
+    o = rng.integers(new_tokens[0], new_tokens[1] + 1, size=n)
+    t = rng.integers(0, max(wl.vocab, 1), size=n)
+    return [(int(c[i]), int(o[i]), int(t[i])) for i in range(n)]
+
+
 def first_tokens(wl, seed=2):
     rng = np.random.default_rng([seed, 3])
     return rng.integers(0, max(wl.vocab, 1), size=wl.batch).astype(np.int32)

@@ -237,6 +237,85 @@ mk_status mk_handoff_litmus(int32_t rounds, int32_t words, int32_t workgroups, u
 mk_status mk_handoff_litmus_noalloc(int32_t rounds, int32_t words, int32_t workgroups, uint64_t* stale,
                                     uint64_t* checked);
 
+/* ---- the serving loop's decode owner -------------------------------------------------------
+ * A C++ thread that owns an engine and decodes a continuously changing batch (P3 "Scheduling and
+ * Performance Benchmarks": a C++ thread owns the decode loop while requests, prefill and batch
+ * management run on the control side; P1 "From demo to a full serving system": continuous batching
+ * with ragged lengths). Sequences are submitted with their prefill done (K/V of positions
+ * [0, prompt_len) already in the pages they own) and join the batch at the next step boundary; a
+ * sequence leaves after generating max_new_tokens tokens (greedy: each step's argmax feeds its next
+ * step). Whenever the batch changes, the rows are packed (in admission order), their block tables
+ * uploaded and the schedule rebuilt; a sequence that outgrows its attention splits gets the schedule
+ * rebuilt too. While a server exists, the engine belongs to its thread: the caller must not call any
+ * other function on that engine until mk_server_destroy. Server functions may be called from any one
+ * control thread. */
+typedef struct mk_server mk_server;
+
+typedef struct {
+  int32_t max_batch;          /* rows of the batch, 1..the engine's max_batch */
+  int32_t start_held;         /* 1: start with a step budget of 0 (mk_server_run releases steps) */
+  int32_t* topk_out;          /* optional device outputs of every step, as in mk_set_step_outputs */
+  float* router_logits_out;
+  float* hidden_out;
+  float* logits_out;          /* optional caller-owned [max_batch, vocab] logits (NULL: the server's own) */
+} mk_server_config;
+
+typedef struct {
+  int64_t request_id;         /* the caller's id */
+  int32_t prompt_len;         /* positions already prefilled; decoding starts at this position */
+  int32_t first_token;        /* the token decoded at position prompt_len */
+  int32_t max_new_tokens;     /* tokens to generate (>= 1) */
+  int32_t n_pages;            /* pages the sequence owns, in position order */
+  const int32_t* pages;       /* host array, copied at submit; must cover prompt_len + max_new_tokens positions */
+} mk_request;
+
+typedef struct {              /* composition of the last step */
+  int64_t step;               /* steps run before it */
+  int32_t batch;              /* rows */
+  int32_t rebuilt;            /* 1 if the schedule was rebuilt for it */
+  int64_t request_id[MK_MAX_BATCH];
+  int32_t position[MK_MAX_BATCH];
+  int32_t token_in[MK_MAX_BATCH];
+  int32_t token_out[MK_MAX_BATCH];
+} mk_server_step;
+
+typedef struct {
+  int64_t steps, tokens, rebuilds;
+  int32_t active, pending, finished, paused;
+  double busy_seconds;        /* wall time the owner spent in steps (schedule rebuilds included) */
+} mk_server_stats_t;
+
+/* Start the decode owner over engine e (its step outputs are taken over: argmax by the server, the
+ * optional ones from cfg). Allocates the step buffers (device and pinned host) once. MK_ERR_INVALID_ARG
+ * for NULL arguments or max_batch outside 1..the engine's max_batch; MK_ERR_OOM / MK_ERR_HIP. */
+mk_status mk_server_create(mk_engine* e, const mk_server_config* cfg, mk_server** out);
+/* Queue a prefilled sequence (copied). MK_ERR_INVALID_ARG for a bad request (page ids outside the pool,
+ * too few pages, a token outside the vocabulary); the server's sticky error if it failed. */
+mk_status mk_server_submit(mk_server* s, const mk_request* r);
+/* Hold decode between steps and return once the owner is holding (a prefill may then use the GPU and
+ * the pages), or the server's sticky error. */
+mk_status mk_server_pause(mk_server* s);
+mk_status mk_server_resume(mk_server* s);
+/* Allow n_steps more steps (-1: no limit; 0: hold after the current step). */
+mk_status mk_server_run(mk_server* s, int64_t n_steps);
+/* Block until the owner holds: budget used up, paused, or nothing to decode. Returns the sticky error. */
+mk_status mk_server_wait(mk_server* s);
+/* Finished sequences not yet taken: writes up to max (id, tokens generated) pairs; returns the count,
+ * or -1 for bad arguments. */
+int32_t mk_server_poll(mk_server* s, int64_t* ids, int32_t* n_tokens, int32_t max);
+/* The tokens a finished sequence generated (host buffer of cap); the sequence is then forgotten.
+ * MK_ERR_INVALID_ARG if it is unknown, not finished, or cap is too small (*n = tokens needed). */
+mk_status mk_server_take(mk_server* s, int64_t request_id, int32_t* tokens, int32_t cap, int32_t* n);
+mk_status mk_server_stats(mk_server* s, mk_server_stats_t* out);
+/* The last step's composition, and the device address of its logits [batch, vocab] (valid until the
+ * next step). */
+mk_status mk_server_last_step(mk_server* s, mk_server_step* rec, const float** logits);
+/* Describe the owner's first failure (engine status and message) in buf; returns it (MK_OK if none). */
+mk_status mk_server_get_error(mk_server* s, char* buf, size_t n);
+/* Stop after the current step, join the owner, release the buffers; the engine returns to the caller.
+ * Returns the owner's sticky status. */
+mk_status mk_server_destroy(mk_server* s);
+
 /* ---- schedule inspection (host only: no GPU needed) -------------------------------------- */
 /* The static schedule the host builds for a step (P3 "Scheduling and Performance Benchmarks":
  * mostly static scheduling), inspected, validated and simulated without a GPU. */

@@ -155,3 +155,49 @@ def bf16_step_mismatch(g16, h16, floor=1e-5):
         step = np.where(mag > 0, np.exp2(np.floor(np.log2(np.where(mag > 0, mag, 1.0))) - 7), 0.0)
     diff = np.abs(gd - hd)
     return diff > step + floor
+
+
+def check_full_step(dims, lw, kv0, tokens, positions, block_tables, g_topk, g_rlog, g_logits, g_argmax, near_tie,
+                    router_tol, max_abs=2e-2, max_rel=5e-3, g_kv=None, kv_floor=None):
+    """Gates of one GPU decode step against the oracle run on the same inputs (teacher-forced: the
+    oracle starts from kv0, the KV cache as the step began). Routing: bit-exact up to near-ties
+    (replayed); router logits |d| <= router_tol up to the first replay; logits max |d| and relative L2 per
+    token; greedy tokens equal. With g_kv (a function (layer, page, slot) -> (k16, v16) of the GPU's
+    cache after the step) the new K/V rows are compared too (one bf16 step + kv_floor). Returns stats."""
+    import copy
+    kv_last = {}
+
+    def run(forced):
+        kv = copy.deepcopy(kv0)
+        kv_last["kv"] = kv
+        return oracle.decode_step(dims, lw, kv, np.asarray(tokens, np.int64), np.asarray(positions, np.int64),
+                                  block_tables, np.asarray(positions, np.int64) + 1, forced_topk=forced)
+
+    ref, replay = replay_near_ties(run, g_topk, near_tie)
+    L, B = g_topk.shape[:2]
+    first = min([l for l, _ in replay], default=L)
+    dr = float(np.abs(g_rlog.astype(np.float64) - ref.router_logits)[:first].max()) if first else 0.0
+    assert dr <= router_tol, f"router logits max|d| {dr:.3g} > {router_tol}"
+    stats = {"router_logits_maxabs": dr, "near_ties": len(replay), "min_margin": float(ref.margin.min())}
+    for b in range(B):
+        d = np.abs(g_logits[b].astype(np.float64) - ref.logits[b]).max()
+        rel = np.linalg.norm(g_logits[b].astype(np.float64) - ref.logits[b]) / np.linalg.norm(ref.logits[b])
+        stats["logits_maxabs"] = max(stats.get("logits_maxabs", 0.0), float(d))
+        stats["logits_rel"] = max(stats.get("logits_rel", 0.0), float(rel))
+        assert d <= max_abs and rel <= max_rel, f"token {b}: logits max|d| {d:.3g} rel {rel:.3g}"
+    assert np.array_equal(np.asarray(g_argmax), np.argmax(ref.logits, 1)), "greedy tokens differ"
+    if g_kv is not None:
+        kvo = kv_last["kv"]
+        nbad = ndiff = ntot = 0
+        for b in range(B):
+            p_b = int(positions[b])
+            page, slot = int(block_tables[b][p_b // dims.page_size]), p_b % dims.page_size
+            for l in range(L):
+                gk, gv = g_kv(l, page, slot)
+                for g16, h16 in ((gk, kvo.k[l][page, :, slot, :]), (gv, kvo.v[l][page, :, slot, :])):
+                    nbad += int(bf16_step_mismatch(g16, h16, floor=kv_floor).sum())
+                    ndiff += int((g16 != h16).sum())
+                    ntot += g16.size
+        stats["kv_rows_differ"] = f"{ndiff}/{ntot}"
+        assert nbad == 0 and ndiff <= max(2, ntot // 50), f"new K/V rows: {nbad} beyond tolerance, {ndiff}/{ntot} differ"
+    return stats
