@@ -16,7 +16,8 @@ Sources. The method is described by three web pages about Cohere's decode megake
 
 The megakernel is an execution strategy; what it computes is an ordinary decode step, so the
 oracle is that plain definition written out (``oracle.decode``). Readings taken where the pages
-are silent are listed in ``oracle.decode``'s docstring, each marked "reading".
+are silent are listed in ``oracle.decode``'s docstring, each marked "reading". A prompt's prefill
+(``oracle.prefill``) is the same layers over all prompt positions at once, causally masked.
 
 Pins (tests marked ``not gpu``): bf16 codec exhaustive + library cross-check; GEMV vs fp64 with
 the standard dot-product error bound; RMSNorm closed form and invariants; RoPE vs complex
@@ -24,7 +25,10 @@ multiplication, identity at pos 0, norm and relative-position invariants; attent
 per-key loop, one-key / identical-key / dominant-key special cases, GQA == repeated-KV MHA; paged ==
 contiguous gather; top-k vs brute-force rank counting with constructed ties; router weights vs the
 full softmax renormalised; MoE sparse sum vs a dense loop over every expert with a mask; whole step
-fp32 vs fp64, batch-row independence, zero branch weights -> identity.
+fp32 vs fp64, batch-row independence, zero branch weights -> identity. Prefill: equal to the
+decode step one position at a time, to itself on a split prompt, causal, and a one-position
+prefill equal to a decode step; planted mistakes (mask off by one, no mask, RoPE positions, stale
+keys, unweighted experts) each fail a pin.
 
 Parity unpinned: nothing the pages print can be recomputed here (the pages give no model
 dimensions and no worked example), so no whole-step value is pinned to the pages themselves.
@@ -47,3 +51,4 @@ from .decode import (  # noqa: F401
     expert_ffn,
     silu,
 )
+from . import prefill  # noqa: F401  (oracle.prefill.prefill, oracle.prefill.PrefillResult)
