@@ -109,6 +109,9 @@ struct mk_plan {
   std::vector<int64_t> bytes;     // cost model, per task (queue order)
   int n_ctr = 0, done_ctr = 0, parts_per_layer = 0, n_attn = 0;
   std::vector<int> capacity;      // per sequence: largest seq_len the schedule can serve
+  // most rows one sequence holds in a step (its consecutive positions), hence the most positions a
+  // row advances per step; above 1 the QKV tasks publish the step's K/V (kernel instance 2)
+  int rows_per_seq = 1;
 };
 
 namespace {
@@ -143,9 +146,14 @@ std::vector<std::pair<int, int>> chunks(int len, int size) {
 }
 
 mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, int W, int split_req,
-                     mk_plan* P, std::string* why, int flags = 0) {
+                     mk_plan* P, std::string* why, int flags = 0, int rows_per_seq = 1) {
   const Dims m = dims_of(desc);
-  P->desc = desc; P->m = m; P->B = B; P->n_workers = W;
+  if (rows_per_seq < 1 || rows_per_seq > B) {
+    *why = fmt("rows_per_seq = %d outside 1..batch (%d)", rows_per_seq, B);
+    return MK_ERR_INVALID_ARG;
+  }
+  const bool kv_first = rows_per_seq > 1;
+  P->desc = desc; P->m = m; P->B = B; P->n_workers = W; P->rows_per_seq = rows_per_seq;
   P->seq_lens.assign(seq_lens, seq_lens + B);
   const int SPLITMAX = split_max(), OUTR = out_max_rows();
   for (int b = 0; b < B; ++b) {
@@ -263,8 +271,12 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     std::vector<int> qkv_count(m.HKV, 0);
     for (int g = 0; g < m.HKV; ++g) {
       const int regions[3][2] = {{g * m.HPG * m.D, m.HPG * m.D}, {m.HQ * m.D + g * m.D, m.D}, {(m.HQ + m.HKV) * m.D + g * m.D, m.D}};
-      for (auto& rg : regions)
-        for (auto [a, e] : chunks(rg[1], qkv_tile)) {
+      for (int ri = 0; ri < 3; ++ri) {
+        const auto& rg = regions[ri];
+        // when the QKV tasks publish the step's keys, a K tile is one whole head (RoPE pairs dims
+        // d and d + D/2) and V tiles hold whole 16-byte groups of 8 dims
+        const int tile = !kv_first ? qkv_tile : ri == 1 ? m.D : std::max(8, qkv_tile / 8 * 8);
+        for (auto [a, e] : chunks(rg[1], tile)) {
           Proto pr;
           set(pr.t, OP_QKV, l, lv0);
           pr.t.w[D_A0] = rg[0] + a; pr.t.w[D_A1] = e - a;
@@ -275,6 +287,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           levels[lv0].push_back(pr);
           qkv_count[g]++;
         }
+      }
     }
     for (auto [a, e] : even(m.E, router_tiles)) {
       Proto pr;
@@ -423,34 +436,55 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   std::vector<int64_t> total(W, 0), prev(W, 0);
   std::vector<char> merge_w(W, 0);                              // workers with a merge this layer
   constexpr int64_t AVOID = (int64_t)1 << 50;
+  std::vector<int64_t> lload(W, 0);
+  // the workers in a binary min-heap on (level load, previous level load, total load, index): the
+  // worker a task goes to is the heap's top, exactly the first minimum of a scan in index order
+  std::vector<int> heap(W), at(W);
+  auto less = [&](int a, int b) {
+    return lload[a] != lload[b] ? lload[a] < lload[b] : prev[a] != prev[b] ? prev[a] < prev[b]
+         : total[a] != total[b] ? total[a] < total[b] : a < b;
+  };
+  auto put = [&](int i, int w) { heap[i] = w; at[w] = i; };
+  auto sift_down = [&](int i) {
+    const int w = heap[i];
+    for (;;) {
+      int c = 2 * i + 1;
+      if (c >= W) break;
+      if (c + 1 < W && less(heap[c + 1], heap[c])) ++c;
+      if (!less(heap[c], w)) break;
+      put(i, heap[c]);
+      i = c;
+    }
+    put(i, w);
+  };
   for (int lv = 0; lv < (int)levels.size(); ++lv) {
     auto& lvl = levels[lv];
     std::vector<int> order(lvl.size());
     std::iota(order.begin(), order.end(), 0);
     std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return lvl[a].bytes > lvl[b].bytes; });
-    std::vector<int64_t> lload(W, 0);
+    std::fill(lload.begin(), lload.end(), 0);
     // output rows avoid the merge workers only when the others can take one output task each
     const bool out_level = lv < LPL * L && lv % LPL == LPL - 1 && W - n_merge >= n_out_l;
     if (out_level)
       for (int w = 0; w < W; ++w) lload[w] = merge_w[w] ? AVOID : 0;
+    // merges first go to their fixed workers (placement of the others only sees the sums), then
+    // the heap is built over the level's starting loads
     for (int idx : order) {
-      int best = 0;
-      if (lvl[idx].pin >= 0) {                 // attention merge: on the worker of its split
-        best = split_worker.at(lvl[idx].pin);
-        merge_w[best] = 1;
-        lload[best] += lvl[idx].bytes;
-        total[best] += lvl[idx].bytes;
-        queues[best].push_back({lv, lvl[idx]});
-        continue;
-      }
-      for (int w = 1; w < W; ++w) {
-        const bool better = lload[w] != lload[best] ? lload[w] < lload[best]
-                          : prev[w] != prev[best] ? prev[w] < prev[best]
-                          : total[w] < total[best];
-        if (better) best = w;
-      }
-      lload[best] += lvl[idx].bytes;
+      if (lvl[idx].pin < 0) continue;          // attention merge: on the worker of its split
+      const int w = split_worker.at(lvl[idx].pin);
+      merge_w[w] = 1;
+      lload[w] += lvl[idx].bytes;
+      total[w] += lvl[idx].bytes;
+      queues[w].push_back({lv, lvl[idx]});
+    }
+    for (int w = 0; w < W; ++w) put(w, w);
+    for (int i = W / 2 - 1; i >= 0; --i) sift_down(i);
+    for (int idx : order) {
+      if (lvl[idx].pin >= 0) continue;
+      const int best = heap[0];
+      lload[best] += lvl[idx].bytes;           // only the top's key grows: restore the heap below it
       total[best] += lvl[idx].bytes;
+      sift_down(0);
       queues[best].push_back({lv, lvl[idx]});
       if (lvl[idx].pin <= -2) split_worker[-2 - lvl[idx].pin] = best;
     }
@@ -532,14 +566,33 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
   for (int w = 0; w < P.n_workers; ++w)
     for (int i = P.qoff[w] + 1; i < P.qoff[w + 1]; ++i)
       if (P.tasks[i].w[D_LEVEL] < P.tasks[i - 1].w[D_LEVEL]) { *why = fmt("worker %d queue is not level-ordered at task %d", w, i); return MK_ERR_INVALID_ARG; }
-  // coverage: each output written exactly once
+  // coverage: each output written exactly once (tasks visited per layer; counters that any task
+  // waits on or signals marked once)
+  std::vector<std::vector<const Task*>> by_layer(m.L);
+  std::vector<char> ctr_used(P.n_ctr, 0);
+  for (auto& t : P.tasks) {
+    if (t.w[D_LAYER] >= 0 && t.w[D_LAYER] < m.L) by_layer[t.w[D_LAYER]].push_back(&t);
+    if (t.w[D_SIG] >= 0) ctr_used[t.w[D_SIG]] = 1;
+    if (t.w[D_SIG2] >= 0) ctr_used[t.w[D_SIG2]] = 1;
+    for (auto& wt : task_waits(t, m.HKV)) if (wt[0] >= 0) ctr_used[wt[0]] = 1;
+  }
+  if (P.rows_per_seq > 1)
+    for (auto& t : P.tasks) {
+      if (t.w[D_OP] != OP_QKV || t.w[D_A0] < m.HQ * m.D) continue;
+      const bool is_k = t.w[D_A0] < (m.HQ + m.HKV) * m.D;
+      const int dlo = (t.w[D_A0] - (is_k ? m.HQ : m.HQ + m.HKV) * m.D) % m.D, n = t.w[D_A1];
+      if (is_k ? (dlo != 0 || n != m.D) : (dlo % 8 != 0 || n % 8 != 0 || dlo + n > m.D)) {
+        *why = fmt("task %d: a %s tile [%d, +%d) the QKV task cannot publish", t.w[D_ID], is_k ? "K" : "V", t.w[D_A0], n);
+        return MK_ERR_INVALID_ARG;
+      }
+    }
   for (int l = 0; l < m.L; ++l) {
     std::vector<int> qkv(m.QKVR, 0), out(m.H, 0), rt(m.E, 0);
     std::map<int, std::vector<int>> gu;
-    std::map<int, std::vector<std::pair<int, int>>> att, mrg;
+    std::vector<std::vector<std::pair<int, int>>> att(P.B * m.HKV), mrg(P.B * m.HKV);
     std::vector<const Task*> queue_tasks;
-    for (auto& t : P.tasks) {
-      if (t.w[D_LAYER] != l) continue;
+    for (const Task* tp : by_layer[l]) {
+      const Task& t = *tp;
       switch (t.w[D_OP]) {
         case OP_QKV: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) qkv[r]++; break;
         case OP_ROUTER: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) rt[r]++; break;
@@ -551,8 +604,13 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
           for (int f = t.w[D_A1]; f < t.w[D_A1] + t.w[D_A2]; ++f) v[f]++;
           break;
         }
-        case OP_ATTN: att[t.w[D_A0] * m.HKV + t.w[D_A1]].push_back({t.w[D_A2], t.w[D_A3]}); break;
-        case OP_MERGE: mrg[t.w[D_A0] * m.HKV + t.w[D_A1]].push_back({t.w[D_A2], t.w[D_A3]}); break;
+        case OP_ATTN:
+        case OP_MERGE: {
+          const int b = t.w[D_A0], g = t.w[D_A1];
+          if (b < 0 || b >= P.B || g < 0 || g >= m.HKV) { *why = fmt("task %d: sequence %d group %d out of range", t.w[D_ID], b, g); return MK_ERR_INVALID_ARG; }
+          (t.w[D_OP] == OP_ATTN ? att : mrg)[b * m.HKV + g].push_back({t.w[D_A2], t.w[D_A3]});
+          break;
+        }
       }
     }
     for (int r = 0; r < m.QKVR; ++r) if (qkv[r] != 1) { *why = fmt("layer %d qkv row %d written %d times", l, r, qkv[r]); return MK_ERR_INVALID_ARG; }
@@ -569,9 +627,9 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
         *why = fmt("layer %d: %d down items of %d rows for %d rows", l, qd, down_rows(), m.H);
         return MK_ERR_INVALID_ARG;
       }
-      for (auto& t : P.tasks)
-        if (t.w[D_LAYER] == l && t.w[D_OP] == OP_OUT && t.w[D_A4] != (qd > 0 ? 1 : 0)) {
-          *why = fmt("layer %d: output task %d and the expert queue disagree on the down items", l, t.w[D_ID]);
+      for (const Task* tp : by_layer[l])
+        if (tp->w[D_OP] == OP_OUT && tp->w[D_A4] != (qd > 0 ? 1 : 0)) {
+          *why = fmt("layer %d: output task %d and the expert queue disagree on the down items", l, tp->w[D_ID]);
           return MK_ERR_INVALID_ARG;
         }
       if (qc >= P.n_ctr || nq < 1 || nq > CTR_SUB || slices < 1 || nfs < 1 || slices * nfs < m.F || (slices - 1) * nfs >= m.F) {
@@ -588,22 +646,18 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
         drained[t->w[D_A0]]++;
       }
       for (int q = 0; q < nq; ++q) if (!drained[q]) { *why = fmt("layer %d: expert sub-queue %d has no task", l, q); return MK_ERR_INVALID_ARG; }
-      for (auto& t : P.tasks) {
-        bool uses = t.w[D_SIG] == qc || t.w[D_SIG2] == qc;
-        for (auto& wt : task_waits(t, m.HKV)) uses = uses || wt[0] == qc;
-        if (uses) { *why = fmt("task %d waits on or signals the expert queue counter %d", t.w[D_ID], qc); return MK_ERR_INVALID_ARG; }
-      }
+      if (qc >= 0 && ctr_used[qc]) { *why = fmt("a task waits on or signals the expert queue counter %d", qc); return MK_ERR_INVALID_ARG; }
     } else if ((int)gu.size() != std::min(m.E, m.K * P.B)) { *why = fmt("layer %d: %zu expert slots", l, gu.size()); return MK_ERR_INVALID_ARG; }
     if (queue_tasks.empty())
-      for (auto& t : P.tasks)
-        if (t.w[D_LAYER] == l && t.w[D_OP] == OP_OUT && t.w[D_A4] != 0) {
-          *why = fmt("layer %d: output task %d expects queued down items, the layer has none", l, t.w[D_ID]);
+      for (const Task* tp : by_layer[l])
+        if (tp->w[D_OP] == OP_OUT && tp->w[D_A4] != 0) {
+          *why = fmt("layer %d: output task %d expects queued down items, the layer has none", l, tp->w[D_ID]);
           return MK_ERR_INVALID_ARG;
         }
     for (auto& [u, v] : gu) for (int f = 0; f < m.F; ++f) if (v[f] != 1) { *why = fmt("layer %d slot %d ffn row %d written %d times", l, u, f, v[f]); return MK_ERR_INVALID_ARG; }
     for (int b = 0; b < P.B; ++b)
       for (int g = 0; g < m.HKV; ++g) {
-        auto v = att[b * m.HKV + g];
+        auto& v = att[b * m.HKV + g];
         std::sort(v.begin(), v.end());
         int k = 0;
         for (size_t i = 0; i < v.size(); ++i) {
@@ -613,7 +667,7 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
           k = v[i].second;
         }
         if (v.empty()) { *why = fmt("layer %d seq %d group %d: no attention", l, b, g); return MK_ERR_INVALID_ARG; }
-        auto mv = mrg[b * m.HKV + g];
+        auto& mv = mrg[b * m.HKV + g];
         std::sort(mv.begin(), mv.end());
         bool ok = !mv.empty();
         for (size_t i = 0; ok && i < mv.size(); ++i) ok = mv[i].first == (int)i && mv[i].second == (int)mv.size();
@@ -716,6 +770,10 @@ struct mk_engine {
   hipStream_t last_stream = nullptr;
   mk_status sticky = MK_OK;
   std::string msg;
+  // chunked prefill's step inputs (allocated at its first call): tokens, positions, lengths
+  // [3][max_batch], block tables [max_batch][max_pages], logits [max_batch][V], routed experts
+  int32_t *pf_in = nullptr, *pf_bt = nullptr, *pf_topk = nullptr;
+  float* pf_logits = nullptr;
 };
 
 const mk_model_desc& engine_desc(const mk_engine* e) { return e->desc; }
@@ -725,6 +783,10 @@ namespace {
 mk_status hip_fail(mk_engine* e, hipError_t err, const char* what) {
   if (e) e->msg = fmt("%s: %s", what, hipGetErrorString(err));
   return MK_ERR_HIP;
+}
+
+mk_status hip_ok(mk_engine* e, hipError_t err, const char* what) {
+  return err == hipSuccess ? MK_OK : hip_fail(e, err, what);
 }
 
 #define HIPCHK(e, call)                                              \
@@ -740,7 +802,8 @@ hipError_t dalloc(T** p, size_t n) {
 
 void free_all(mk_engine* e) {
   void* ps[] = {e->d_layers, e->d_inv_freq, e->d_x, e->d_qkv, e->d_rlog, e->d_h, e->d_y, e->d_slot, e->d_attn, e->d_apart,
-                e->d_route, e->d_amax, e->d_ctr, e->d_err, e->d_tasks, e->d_qoff};
+                e->d_route, e->d_amax, e->d_ctr, e->d_err, e->d_tasks, e->d_qoff, e->pf_in, e->pf_bt, e->pf_topk,
+                e->pf_logits};
   for (void* p : ps) if (p) (void)hipFree(p);
 }
 
@@ -835,18 +898,19 @@ mk_status mk_set_options(mk_engine* e, const mk_options* o) {
   return MK_OK;
 }
 
-mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens_host) {
-  if (!e || !seq_lens_host || batch < 1 || batch > e->desc.max_batch) {
-    if (e) e->msg = "mk_build_schedule: bad batch or seq_lens";
+mk_status mk_build_schedule_chunked(mk_engine* e, int32_t batch, const int32_t* seq_lens_host, int32_t rows_per_seq) {
+  if (!e || !seq_lens_host || batch < 1 || batch > e->desc.max_batch || rows_per_seq < 1 || rows_per_seq > batch) {
+    if (e) e->msg = "mk_build_schedule: bad batch, seq_lens or rows_per_seq";
     return MK_ERR_INVALID_ARG;
   }
   int per_cu = 0;
-  HIPCHK(e, step_occupancy(e->shape, batch, e->opt.flags, &per_cu));
+  HIPCHK(e, step_occupancy(e->shape, batch, step_variant(batch, e->opt.flags, rows_per_seq > 1), &per_cu));
   const int wpc = std::min(e->opt.workers_per_cu, per_cu);
   if (wpc < 1) { e->msg = "kernel does not fit on a CU"; return MK_ERR_UNSUPPORTED; }
   mk_plan* P = new mk_plan();
   std::string why;
-  mk_status st = build_plan(e->desc, batch, seq_lens_host, e->n_cu * wpc, e->opt.split_keys, P, &why, e->opt.flags);
+  mk_status st = build_plan(e->desc, batch, seq_lens_host, e->n_cu * wpc, e->opt.split_keys, P, &why, e->opt.flags,
+                            rows_per_seq);
   if (st == MK_OK) st = validate_plan(*P, &why);
   if (st != MK_OK) { e->msg = "mk_build_schedule: " + why; delete P; return st; }
   // (re)size device buffers that depend on the schedule
@@ -865,6 +929,10 @@ mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens
   e->plan = P;
   e->steps_since_build = 0;
   return MK_OK;
+}
+
+mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens_host) {
+  return mk_build_schedule_chunked(e, batch, seq_lens_host, 1);
 }
 
 mk_status mk_set_step_outputs(mk_engine* e, int32_t* argmax_out, int32_t* topk_out, float* hidden_out, uint64_t* trace_out,
@@ -886,9 +954,9 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
   if (!e->plan) { e->msg = "mk_decode_step: no schedule"; return MK_ERR_NO_SCHEDULE; }
   const mk_plan& P = *e->plan;
   for (int b = 0; b < P.B; ++b)
-    if (P.seq_lens[b] + e->steps_since_build > P.capacity[b]) {
-      e->msg = fmt("sequence %d would reach length %d, beyond the schedule's capacity %d", b,
-                   P.seq_lens[b] + e->steps_since_build, P.capacity[b]);
+    if (P.seq_lens[b] + (int64_t)e->steps_since_build * P.rows_per_seq > P.capacity[b]) {
+      e->msg = fmt("row %d would reach length %lld, beyond the schedule's capacity %d", b,
+                   (long long)(P.seq_lens[b] + (int64_t)e->steps_since_build * P.rows_per_seq), P.capacity[b]);
       return MK_ERR_SCHEDULE_STALE;
     }
   Params p{};
@@ -910,7 +978,7 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
   p.watchdog_ticks = (uint64_t)e->opt.watchdog_ms * 100000ull;
   hipStream_t st = (hipStream_t)stream;
   size_t lds = 0;
-  hipError_t err = launch_step(e->shape, P.B, p, P.n_workers, st, &lds);
+  hipError_t err = launch_step(e->shape, P.B, step_variant(P.B, p.flags, P.rows_per_seq > 1), p, P.n_workers, st, &lds);
   if (err != hipSuccess) return hip_fail(e, err, "cooperative launch");
   e->last_stream = st;
   e->steps_since_build++;
@@ -958,6 +1026,87 @@ mk_status mk_reset(mk_engine* e) {
   e->sticky = MK_OK;
   e->msg.clear();
   return MK_OK;
+}
+
+// ---- chunked prefill ----------------------------------------------------------------------
+
+mk_status mk_prefill(mk_engine* e, const int32_t* tokens_host, int32_t n, int32_t start, const int32_t* block_table_host,
+                     float* logits_out, int32_t* topk_out, void* stream) {
+  if (!e) return MK_ERR_INVALID_ARG;
+  if (e->sticky != MK_OK) return e->sticky;
+  const int maxlen = e->desc.max_pages_per_seq * PAGE;
+  if (!tokens_host || !block_table_host || n < 1 || start < 0 || (int64_t)start + n > maxlen) {
+    e->msg = fmt("mk_prefill: bad arguments (n %d, start %d, longest sequence %d)", n, start, maxlen);
+    return MK_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < n; ++i)
+    if (tokens_host[i] < 0 || tokens_host[i] >= e->desc.vocab) {
+      e->msg = fmt("mk_prefill: token %d at %d outside the vocabulary", tokens_host[i], i);
+      return MK_ERR_INVALID_ARG;
+    }
+  const int npages = (int)ceil_div(start + n, PAGE);
+  for (int i = 0; i < npages; ++i)
+    if (block_table_host[i] < 0 || block_table_host[i] >= e->desc.num_pages) {
+      e->msg = fmt("mk_prefill: block table entry %d = %d outside 0..%d", i, block_table_host[i], e->desc.num_pages - 1);
+      return MK_ERR_INVALID_ARG;
+    }
+  const int MB = e->desc.max_batch, MP = e->desc.max_pages_per_seq, L = e->m.L, K = e->m.K;
+  const size_t V = (size_t)std::max(1, e->desc.vocab);
+  if (!e->pf_in) {
+    HIPCHK(e, dalloc(&e->pf_in, 3 * (size_t)MB));
+    HIPCHK(e, dalloc(&e->pf_bt, (size_t)MB * MP));
+    HIPCHK(e, dalloc(&e->pf_topk, (size_t)L * MB * K));
+    HIPCHK(e, dalloc(&e->pf_logits, (size_t)MB * V));
+  }
+  hipStream_t st = (hipStream_t)stream;
+  // every row holds the sequence's block table
+  for (int r = 0; r < MB; ++r)
+    HIPCHK(e, hipMemcpyAsync(e->pf_bt + (size_t)r * MP, block_table_host, sizeof(int32_t) * npages, hipMemcpyHostToDevice, st));
+  // the steps write the routed experts into the prefill's own buffer and nothing else of the caller's
+  int32_t* keep_argmax = e->argmax_out; int32_t* keep_topk = e->topk_out; float* keep_hidden = e->hidden_out;
+  uint64_t* keep_trace = e->trace_out; float* keep_rlog = e->rlog_out;
+  e->argmax_out = nullptr; e->topk_out = topk_out ? e->pf_topk : nullptr; e->hidden_out = nullptr;
+  e->trace_out = nullptr; e->rlog_out = nullptr;
+  const int R = std::min(MB, n);        // rows per step: consecutive positions of the sequence
+  std::vector<int32_t> in(3 * (size_t)MB);
+  mk_status stt = MK_OK;
+  int built_rows = 0;
+  for (int c0 = 0; c0 < n && stt == MK_OK; c0 += R) {
+    const int c = std::min(R, n - c0);
+    for (int r = 0; r < c; ++r) {
+      in[r] = tokens_host[c0 + r];
+      in[MB + r] = start + c0 + r;
+      in[2 * MB + r] = start + c0 + r + 1;
+    }
+    if (c != built_rows) {              // (the last chunk may hold fewer rows)
+      stt = mk_build_schedule_chunked(e, c, in.data() + 2 * MB, c);
+      if (stt != MK_OK) break;
+      built_rows = c;
+    }
+    stt = hip_ok(e, hipMemcpyAsync(e->pf_in, in.data(), sizeof(int32_t) * 3 * MB, hipMemcpyHostToDevice, st), "mk_prefill: copy");
+    if (stt != MK_OK) break;
+    stt = mk_decode_step(e, e->pf_in, e->pf_in + MB, e->pf_bt, e->pf_in + 2 * MB, e->pf_logits, st);
+    if (stt == MK_ERR_SCHEDULE_STALE) {  // the rows outgrew the schedule's attention splits
+      stt = mk_build_schedule_chunked(e, c, in.data() + 2 * MB, c);
+      if (stt == MK_OK) stt = mk_decode_step(e, e->pf_in, e->pf_in + MB, e->pf_bt, e->pf_in + 2 * MB, e->pf_logits, st);
+    }
+    if (stt != MK_OK) break;
+    if (topk_out)                       // [L][c][K] of this chunk -> rows c0.. of the caller's [L][n][K]
+      stt = hip_ok(e, hipMemcpy2DAsync(topk_out + (size_t)c0 * K, sizeof(int32_t) * n * K, e->pf_topk, sizeof(int32_t) * c * K,
+                                       sizeof(int32_t) * c * K, L, hipMemcpyDeviceToDevice, st), "mk_prefill: copy");
+    if (stt == MK_OK && c0 + c == n && logits_out && e->desc.has_lm_head)
+      stt = hip_ok(e, hipMemcpyAsync(logits_out, e->pf_logits + (size_t)(c - 1) * V, sizeof(float) * V,
+                                     hipMemcpyDeviceToDevice, st), "mk_prefill: copy");
+    // the host staging is rewritten by the next chunk
+    if (stt == MK_OK) stt = hip_ok(e, hipStreamSynchronize(st), "mk_prefill: sync");
+    if (stt == MK_OK) stt = mk_sync(e);
+  }
+  e->argmax_out = keep_argmax; e->topk_out = keep_topk; e->hidden_out = keep_hidden;
+  e->trace_out = keep_trace; e->rlog_out = keep_rlog;
+  // the schedule was the prefill's: the next decode step needs one of its own
+  delete e->plan;
+  e->plan = nullptr;
+  return stt;
 }
 
 void mk_destroy(mk_engine* e) {
@@ -1056,7 +1205,7 @@ mk_status mk_handoff_litmus_noalloc(int32_t rounds, int32_t words, int32_t workg
 // ---- host-only schedule API ---------------------------------------------------------------
 
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* seq_lens_host, int32_t n_workers,
-                        int32_t split_keys, uint32_t flags, mk_plan** out) {
+                        int32_t split_keys, uint32_t flags, int32_t rows_per_seq, mk_plan** out) {
   std::string why;
   if (!out) return MK_ERR_INVALID_ARG;
   *out = nullptr;
@@ -1064,7 +1213,7 @@ mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t*
   if (st != MK_OK) { fprintf(stderr, "mk_plan_build: %s\n", why.c_str()); return st; }
   if (!seq_lens_host || batch < 1 || batch > desc->max_batch || n_workers < 1 || split_keys < 0) return MK_ERR_INVALID_ARG;
   mk_plan* P = new mk_plan();
-  st = build_plan(*desc, batch, seq_lens_host, n_workers, split_keys, P, &why, (int)flags);
+  st = build_plan(*desc, batch, seq_lens_host, n_workers, split_keys, P, &why, (int)flags, rows_per_seq);
   if (st != MK_OK) { fprintf(stderr, "mk_plan_build: %s\n", why.c_str()); delete P; return st; }
   *out = P;
   return MK_OK;

@@ -654,8 +654,73 @@ __device__ __forceinline__ TaskHdr read_task(CParams& p, int ti) {
   return T;
 }
 
-// QKV rows (any contiguous range inside one KV group's q, k or v rows).
 template <class S, int TB>
+__device__ __forceinline__ float* rope_tab();
+
+// The cache rows of this step's tokens, published by the QKV task that produced them (kernel
+// instance for batches whose rows are consecutive positions of one sequence: chunked prefill and
+// mixed prefill/decode batches). Tile [row0, row0 + nrows) of the K rows (one whole head, so that
+// RoPE's rotate-half partners are in the tile) or of the V rows: every row's fp32 outputs, already
+// stored and drained by this workgroup, are read back, K rotated by RoPE at the row's position
+// (R3 of the oracle's readings, as the attention forms the new key), both rounded to bf16 and
+// written at the row's slot with write-through stores (R6). The caller drains before it signals, so
+// an attention task that has seen the QKV counter reads every row's key from the cache.
+template <class S, int TB>
+__device__ __forceinline__ bool publish_kv(CParams& p, int l, int row0, int nrows, int task) {
+  constexpr int D = S::D, HQ = S::HQ, HKV = S::HKV;
+  const bool is_k = row0 < (HQ + HKV) * D;
+  const int base = is_k ? HQ * D : (HQ + HKV) * D;
+  const int g = (row0 - base) / D, dlo = (row0 - base) % D;
+  if ((is_k && (dlo != 0 || nrows != D)) || (!is_k && (nrows % 8 != 0 || dlo % 8 != 0 || dlo + nrows > D))) {
+    if (tid() == 0) raise_error(p, DEV_BAD_OP, task, -1, (uint32_t)row0, (uint32_t)nrows, 0);
+    return false;
+  }
+  const auto& Lp = cst(p.layers)[l];
+  uint16_t* cache = is_k ? Lp.k_cache : Lp.v_cache;
+  const int nch = nrows / 8;                       // 8 dims (one 16-byte store) per item
+  uint32_t bad = 0, bad_a = 0, bad_b = 0;          // the first refused item (reported after the loop)
+  for (int i = tid(); i < p.B * nch; i += NT) {
+    const int b = i / nch, d0 = dlo + 8 * (i % nch);
+    const int pos = cst(p.positions)[b];
+    if (pos < 0 || pos >= p.max_pages * PAGE) {
+      if (!bad) { bad = DEV_BAD_POS; bad_a = (uint32_t)pos; bad_b = (uint32_t)b; }
+      continue;
+    }
+    const int page = cst(p.block_tables)[(size_t)b * p.max_pages + pos / PAGE];
+    if (page < 0 || page >= p.num_pages) {
+      if (!bad) { bad = DEV_BAD_PAGE; bad_a = (uint32_t)page; bad_b = (uint32_t)(pos / PAGE); }
+      continue;
+    }
+    const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + ((size_t)l * MAXB + b) * S::QKVR);
+    const uint32_t src = (uint32_t)(base + g * D + d0);
+    const f4 x0 = ldc4(Q, 4u * src), x1 = ldc4(Q, 4u * (src + 4));
+    float r[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    if (is_k) {
+      const int pd0 = d0 < D / 2 ? d0 + D / 2 : d0 - D / 2;
+      const uint32_t ps = (uint32_t)(base + g * D + pd0);
+      const f4 y0 = ldc4(Q, 4u * ps), y1 = ldc4(Q, 4u * (ps + 4));
+      const float y[8] = {y0.x, y0.y, y0.z, y0.w, y1.x, y1.y, y1.z, y1.w};
+      const float* cs = rope_tab<S, TB>() + b * D;   // [D/2] cos, [D/2] sin at pos
+#pragma unroll
+      for (int m = 0; m < 8; ++m) {
+        const int j = (d0 + m) % (D / 2);
+        const float c = cs[j], sn = cs[D / 2 + j];
+        r[m] = d0 < D / 2 ? r[m] * c - y[m] * sn : r[m] * c + y[m] * sn;
+      }
+    }
+    u4 w;
+    w.x = f2bf(r[0]) | (f2bf(r[1]) << 16); w.y = f2bf(r[2]) | (f2bf(r[3]) << 16);
+    w.z = f2bf(r[4]) | (f2bf(r[5]) << 16); w.w = f2bf(r[6]) | (f2bf(r[7]) << 16);
+    const __amdgpu_buffer_rsrc_t C = rsrc(cache + ((size_t)page * HKV + g) * PAGE * D);
+    __builtin_amdgcn_raw_buffer_store_b128(w, C, (uint32_t)(((pos % PAGE) * D + d0) * 2), 0, SC1);
+  }
+  if (bad)
+    raise_error(p, bad, task, -1, bad == DEV_BAD_POS ? (uint32_t)p.max_pages : (uint32_t)p.num_pages, bad_a, bad_b);
+  return __syncthreads_or(bad != 0) == 0;
+}
+
+// QKV rows (any contiguous range inside one KV group's q, k or v rows).
+template <class S, int TB, int VAR>
 __device__ __forceinline__ bool op_qkv(int task) {
   CParams& p = P();
   Ctl& ctl = ctl_s;
@@ -679,6 +744,14 @@ __device__ __forceinline__ bool op_qkv(int task) {
       [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); });
   MARK(1);
   drain_t(p);
+  if constexpr (VAR == 2) {
+    if (row0 >= S::HQ * S::D) {          // a K or V tile: the rows' cache entries, before the signal
+      __syncthreads();                   // every thread's stores of the tile have landed
+      const bool ok = publish_kv<S, TB>(p, T.layer, row0, nrows, T.id);   // (uniform)
+      drain();
+      if (!ok) return false;
+    }
+  }
   MARK(2);
   signal(p, ctl, T.sig, false);
   return true;
@@ -1152,7 +1225,7 @@ __host__ __device__ constexpr int rope_off(int tb) {
 template <class S, int TB>
 __device__ __forceinline__ float* rope_tab() { return smem + rope_off<S>(TB); }
 
-template <class S, int TB>
+template <class S, int TB, int VAR>
 __device__ __forceinline__ bool op_attn(int task) {
   CParams& p = P();
   Ctl& ctl = ctl_s;
@@ -1241,6 +1314,10 @@ __device__ __forceinline__ bool op_attn(int task) {
   // dependent round trip in the P V pass. (Its keys go to wave 0's first key registers once that
   // block's first-chunk products are done: holding them from the start as well would exceed the
   // register budget.)
+  // (When the QKV tasks publish the step's keys - rows of one sequence in one step - keys of this
+  // step's other rows may lie in the range, so nothing is read before the wait.)
+  if constexpr (VAR == 2)
+    if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   load_k(0);
   load_v(0);
   const bool tail = nchunk == 2 && nk - KC <= PAGE;    // uniform in the workgroup
@@ -1253,7 +1330,8 @@ __device__ __forceinline__ bool op_attn(int task) {
       vtl[q] = jv < kend ? ldw(Lp.v_cache + kaddr(jv, 8 * li)) : u4{0u, 0u, 0u, 0u};
     }
   }
-  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+  if constexpr (VAR != 2)
+    if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + ((size_t)l * MAXB + b) * S::QKVR);
   const float rsd = 1.0f / sqrtf((float)D);
   // rotate-half RoPE of 4 dims d0..d0+3 (all on one side of D/2) given x and its partner dims y
@@ -1295,9 +1373,11 @@ __device__ __forceinline__ bool op_attn(int task) {
       knew[4 * li + m] = kw[m];
       vnew[8 * li + 2 * m] = bf1((uint16_t)va); vnew[8 * li + 2 * m + 1] = bf1((uint16_t)vb2);
     }
-    const size_t off = kaddr(pos, 8 * li);
-    *reinterpret_cast<u4*>(Lp.k_cache + off) = u4{kw[0], kw[1], kw[2], kw[3]};
-    *reinterpret_cast<u4*>(Lp.v_cache + off) = u4{vw[0], vw[1], vw[2], vw[3]};
+    if constexpr (VAR != 2) {            // (else the QKV tasks have written them)
+      const size_t off = kaddr(pos, 8 * li);
+      *reinterpret_cast<u4*>(Lp.k_cache + off) = u4{kw[0], kw[1], kw[2], kw[3]};
+      *reinterpret_cast<u4*>(Lp.v_cache + off) = u4{vw[0], vw[1], vw[2], vw[3]};
+    }
   }
   __syncthreads();
   // MFMA A operand, row r = col: with a = r / 4, rows 4a, 4a+1 hold the bf16 high parts of heads
@@ -2150,10 +2230,10 @@ __global__ void __launch_bounds__(NT, 2) mk_step(Params) {
     if (trace) __syncthreads();
     bool ok;
     switch (op) {
-      case OP_QKV: ok = op_qkv<S, TB>(ti); break;
+      case OP_QKV: ok = op_qkv<S, TB, VAR>(ti); break;
       case OP_ROUTER: ok = op_router<S, TB>(ti); break;
       case OP_GATEUP: ok = op_gateup<S, TB>(ti); break;
-      case OP_ATTN: ok = op_attn<S, TB>(ti); break;
+      case OP_ATTN: ok = op_attn<S, TB, VAR>(ti); break;
       case OP_OUT:
         if constexpr (TB == 1) ok = op_out<S, TB, VAR>(ti);
         else ok = op_out_batch<S, TB>(ti);
@@ -2218,25 +2298,29 @@ int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F) {
   return -1;
 }
 
-// batch 1 with MK_FLAG_OPROJ_PER_GROUP runs the kernel instance with the per-KV-group O projection
-hipError_t launch_step(int shape, int batch, const Params& p, int grid, hipStream_t st, size_t* lds) {
-  const bool pg = batch == 1 && (p.flags & 8);
-  if (shape == 0) {
-    if (batch > 1) return launch_one<ShapeSmall, MAXB>(p, grid, st, lds);
-    return pg ? launch_one<ShapeSmall, 1, 1>(p, grid, st, lds) : launch_one<ShapeSmall, 1>(p, grid, st, lds);
-  }
-  if (batch > 1) return launch_one<ShapeFull, MAXB>(p, grid, st, lds);
-  return pg ? launch_one<ShapeFull, 1, 1>(p, grid, st, lds) : launch_one<ShapeFull, 1>(p, grid, st, lds);
+// Kernel instances: batch 1 (VAR 1: the per-KV-group O projection of MK_FLAG_OPROJ_PER_GROUP) and
+// batch > 1 (VAR 2: the QKV tasks publish the step's K/V, for rows of one sequence in one step).
+int step_variant(int batch, int flags, bool kv_first) {
+  if (batch == 1) return (flags & 8) ? 1 : 0;
+  return kv_first ? 2 : 0;
 }
 
-hipError_t step_occupancy(int shape, int batch, int flags, int* blocks_per_cu) {
-  const bool pg = batch == 1 && (flags & 8);
+hipError_t launch_step(int shape, int batch, int var, const Params& p, int grid, hipStream_t st, size_t* lds) {
   if (shape == 0) {
-    if (batch > 1) return occupancy_one<ShapeSmall, MAXB>(blocks_per_cu);
-    return pg ? occupancy_one<ShapeSmall, 1, 1>(blocks_per_cu) : occupancy_one<ShapeSmall, 1>(blocks_per_cu);
+    if (batch > 1) return var == 2 ? launch_one<ShapeSmall, MAXB, 2>(p, grid, st, lds) : launch_one<ShapeSmall, MAXB>(p, grid, st, lds);
+    return var == 1 ? launch_one<ShapeSmall, 1, 1>(p, grid, st, lds) : launch_one<ShapeSmall, 1>(p, grid, st, lds);
   }
-  if (batch > 1) return occupancy_one<ShapeFull, MAXB>(blocks_per_cu);
-  return pg ? occupancy_one<ShapeFull, 1, 1>(blocks_per_cu) : occupancy_one<ShapeFull, 1>(blocks_per_cu);
+  if (batch > 1) return var == 2 ? launch_one<ShapeFull, MAXB, 2>(p, grid, st, lds) : launch_one<ShapeFull, MAXB>(p, grid, st, lds);
+  return var == 1 ? launch_one<ShapeFull, 1, 1>(p, grid, st, lds) : launch_one<ShapeFull, 1>(p, grid, st, lds);
+}
+
+hipError_t step_occupancy(int shape, int batch, int var, int* blocks_per_cu) {
+  if (shape == 0) {
+    if (batch > 1) return var == 2 ? occupancy_one<ShapeSmall, MAXB, 2>(blocks_per_cu) : occupancy_one<ShapeSmall, MAXB>(blocks_per_cu);
+    return var == 1 ? occupancy_one<ShapeSmall, 1, 1>(blocks_per_cu) : occupancy_one<ShapeSmall, 1>(blocks_per_cu);
+  }
+  if (batch > 1) return var == 2 ? occupancy_one<ShapeFull, MAXB, 2>(blocks_per_cu) : occupancy_one<ShapeFull, MAXB>(blocks_per_cu);
+  return var == 1 ? occupancy_one<ShapeFull, 1, 1>(blocks_per_cu) : occupancy_one<ShapeFull, 1>(blocks_per_cu);
 }
 
 // Plain streaming read of n16 16-byte words (a bandwidth ceiling for comparison with the step

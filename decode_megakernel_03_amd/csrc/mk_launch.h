@@ -10,8 +10,11 @@ namespace mk {
 // 0 = hidden 256 small model, 1 = hidden 2048 30B MoE, -1 = no compiled instance
 int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F);
 // cooperative launch of one step on `grid` workers (batch 1 or up to 8 instance)
-hipError_t launch_step(int shape, int batch, const Params& p, int grid, hipStream_t st, size_t* lds_bytes);
-hipError_t step_occupancy(int shape, int batch, int flags, int* blocks_per_cu);
+// kernel instance for a step: 0 plain, 1 per-KV-group O projection (batch 1 with flag 8), 2 the QKV
+// tasks publish the step's K/V (batch > 1 with rows of one sequence in a step)
+int step_variant(int batch, int flags, bool kv_first);
+hipError_t launch_step(int shape, int batch, int var, const Params& p, int grid, hipStream_t st, size_t* lds_bytes);
+hipError_t step_occupancy(int shape, int batch, int var, int* blocks_per_cu);
 int split_max();      // keys one attention task may cover
 int merge_max();      // attention splits one (sequence, KV group) may have
 int out_max_rows();   // rows of one OUT task

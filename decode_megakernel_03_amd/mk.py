@@ -23,7 +23,8 @@ MK_FLAG_STATIC_EXPERTS = 4
 MK_FLAG_OPROJ_PER_GROUP = 8
 DESC_WORDS = 16
 
-EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_decode_step", "mk_set_step_outputs",
+EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_build_schedule_chunked", "mk_prefill",
+            "mk_decode_step", "mk_set_step_outputs",
             "mk_sync", "mk_get_error", "mk_reset", "mk_destroy", "mk_plan_build", "mk_plan_info_get",
             "mk_plan_export", "mk_plan_validate", "mk_plan_simulate", "mk_engine_plan", "mk_plan_destroy",
             "mk_stream_read_bandwidth", "mk_handoff_litmus", "mk_handoff_litmus_noalloc",
@@ -97,13 +98,15 @@ def load(path=LIB_PATH):
         "mk_create": [ctypes.POINTER(ModelDesc), ctypes.POINTER(WeightPtrs), ctypes.POINTER(vp)],
         "mk_set_options": [vp, ctypes.POINTER(Options)],
         "mk_build_schedule": [vp, i32, P32],
+        "mk_build_schedule_chunked": [vp, i32, P32, i32],
+        "mk_prefill": [vp, P32, i32, i32, P32, vp, vp, vp],
         "mk_decode_step": [vp, vp, vp, vp, vp, vp, vp],
         "mk_set_step_outputs": [vp, vp, vp, vp, vp, vp],
         "mk_sync": [vp],
         "mk_get_error": [vp, ctypes.c_char_p, sz],
         "mk_reset": [vp],
         "mk_destroy": [vp],
-        "mk_plan_build": [ctypes.POINTER(ModelDesc), i32, P32, i32, i32, ctypes.c_uint32, ctypes.POINTER(vp)],
+        "mk_plan_build": [ctypes.POINTER(ModelDesc), i32, P32, i32, i32, ctypes.c_uint32, i32, ctypes.POINTER(vp)],
         "mk_plan_info_get": [vp, ctypes.POINTER(PlanInfo)],
         "mk_plan_export": [vp, P32, P32],
         "mk_plan_validate": [vp, ctypes.c_char_p, sz],
@@ -184,6 +187,18 @@ def mk_build_schedule(h, seq_lens):
     _check(LIB.mk_build_schedule(h, len(seq_lens), arr), h, "mk_build_schedule")
 
 
+def mk_build_schedule_chunked(h, seq_lens, rows_per_seq):
+    arr = _i32_array(seq_lens)
+    _check(LIB.mk_build_schedule_chunked(h, len(seq_lens), arr, int(rows_per_seq)), h, "mk_build_schedule_chunked")
+
+
+def mk_prefill(h, tokens, start, block_table, logits_out=None, topk_out=None, stream=None):
+    """Positions [start, start + len(tokens)) of one sequence through the decode kernel (host token and
+    block-table arrays; optional device outputs: last position's logits [V], routed experts [L, n, k])."""
+    _check(LIB.mk_prefill(h, _i32_array(tokens), len(tokens), int(start), _i32_array(block_table), _ptr(logits_out),
+                          _ptr(topk_out), ctypes.c_void_p(stream or 0)), h, "mk_prefill")
+
+
 def mk_decode_step(h, tokens, positions, block_tables, seq_lens, logits_out, stream=None):
     st = LIB.mk_decode_step(h, _ptr(tokens), _ptr(positions), _ptr(block_tables), _ptr(seq_lens), _ptr(logits_out),
                             ctypes.c_void_p(stream or 0))
@@ -238,10 +253,10 @@ def mk_handoff_litmus_noalloc(rounds, words, workgroups):
     return st, stale.value, checked.value
 
 
-def mk_plan_build(desc, seq_lens, n_workers, split_keys=0, flags=0):
+def mk_plan_build(desc, seq_lens, n_workers, split_keys=0, flags=0, rows_per_seq=1):
     h = ctypes.c_void_p()
     _check(LIB.mk_plan_build(ctypes.byref(desc), len(seq_lens), _i32_array(seq_lens), int(n_workers),
-                             int(split_keys), int(flags), ctypes.byref(h)), None, "mk_plan_build")
+                             int(split_keys), int(flags), int(rows_per_seq), ctypes.byref(h)), None, "mk_plan_build")
     return h
 
 
@@ -320,11 +335,19 @@ class Engine:
     def set_options(self, **kw):
         mk_set_options(self.h, **kw)
 
-    def build_schedule(self, seq_lens):
-        mk_build_schedule(self.h, list(seq_lens))
+    def build_schedule(self, seq_lens, rows_per_seq=1):
+        """Schedule for the batch's current lengths; rows_per_seq > 1 when one sequence holds several
+        rows (consecutive positions) of a step."""
+        mk_build_schedule_chunked(self.h, list(seq_lens), rows_per_seq)
         self._lens = [int(v) for v in seq_lens]
+        self._growth = int(rows_per_seq)
         self._steps = 0
         self.rebuilds = 0
+
+    def prefill(self, tokens, start, block_table, logits_out=None, topk_out=None, stream=None):
+        """Chunked prefill of one sequence (mk_prefill); the engine has no schedule afterwards."""
+        mk_prefill(self.h, tokens, start, block_table, logits_out, topk_out, stream)
+        self._lens = None
 
     def set_step_outputs(self, **kw):
         self._outs = kw
@@ -337,8 +360,11 @@ class Engine:
         is issued again."""
         st = mk_decode_step(self.h, tokens, positions, block_tables, seq_lens, logits_out, stream)
         if st == MK_ERR_SCHEDULE_STALE and getattr(self, "_lens", None) is not None:
-            self.build_schedule([n + self._steps for n in self._lens])
-            self.rebuilds += 1
+            # the step's own lengths (rows of one sequence advance by several positions per step)
+            lens = seq_lens.cpu().tolist() if hasattr(seq_lens, "cpu") else [n + self._steps for n in self._lens]
+            rebuilds = self.rebuilds
+            self.build_schedule(lens, self._growth)
+            self.rebuilds = rebuilds + 1
             st = mk_decode_step(self.h, tokens, positions, block_tables, seq_lens, logits_out, stream)
         if st != MK_OK:
             _check(st, self.h, "mk_decode_step")

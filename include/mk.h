@@ -142,6 +142,34 @@ mk_status mk_set_options(mk_engine* e, const mk_options* opt);
  * Synchronous; call again when the batch composition changes. */
 mk_status mk_build_schedule(mk_engine* e, int32_t batch, const int32_t* seq_lens_host);
 
+/* mk_build_schedule for a batch in which one sequence may hold several rows: consecutive positions
+ * of it, one per row, in the same step (chunked prefill, and prefill rows mixed with decode rows:
+ * P3 "Limitations and Future Plans" names prefill and mixed batches as the next step for the
+ * megakernel). rows_per_seq is the most rows any one sequence holds (1 = mk_build_schedule). With
+ * rows_per_seq > 1 the step runs a kernel instance whose QKV tasks write every row's new K/V into
+ * the cache before any attention of the layer reads it, so a row sees the keys of the sequence's
+ * earlier rows in the same step; rows of one sequence must list the same pages. The host tracks
+ * lengths as growing by rows_per_seq per launched step (MK_ERR_SCHEDULE_STALE once a row could
+ * outgrow its attention splits). MK_ERR_INVALID_ARG for rows_per_seq outside 1..batch, otherwise as
+ * mk_build_schedule. */
+mk_status mk_build_schedule_chunked(mk_engine* e, int32_t batch, const int32_t* seq_lens_host,
+                                    int32_t rows_per_seq);
+
+/* Prefill through the decode kernel (P2 body: the pages prefill with separate PyTorch kernels; P3
+ * "Limitations and Future Plans": prefill in the megakernel is their next step): positions
+ * [start, start + n) of ONE sequence, up to max_batch consecutive positions per step, each step
+ * built with mk_build_schedule_chunked. Writes the K/V of every position into the pages of
+ * block_table_host; K/V of positions < start must already be there. Host arrays (read during the
+ * call only): tokens_host int32 [n]; block_table_host int32 [ceil((start + n) / 16)] page ids.
+ * Device outputs, caller-owned, NULL = not wanted: logits_out float32 [V] (position start + n - 1),
+ * topk_out int32 [L, n, k] (routed experts per layer and position, ascending expert index).
+ * Steps run on `stream`; synchronous (returns after the last step). The options, and none of the
+ * outputs set by mk_set_step_outputs, apply. On return the engine has no schedule: build one before
+ * the next mk_decode_step. MK_ERR_INVALID_ARG (bad sizes, a token outside the vocabulary, a page id
+ * outside the cache), MK_ERR_HIP / MK_ERR_DEVICE as mk_decode_step / mk_sync. */
+mk_status mk_prefill(mk_engine* e, const int32_t* tokens_host, int32_t n, int32_t start,
+                     const int32_t* block_table_host, float* logits_out, int32_t* topk_out, void* stream);
+
 /* Enqueue one decode step on `stream` (a hipStream_t; NULL = default stream): the whole forward
  * pass of every sequence of the batch as ONE kernel launch (P1 "One persistent kernel for the whole
  * decode step"; P3 "Key Technologies and Architecture"), reading the paged KV cache through the
@@ -332,10 +360,12 @@ typedef struct {
 } mk_plan_info;
 
 /* Build a schedule without any GPU (for validation and tests): same algorithm as
- * mk_build_schedule for `n_workers` workers; `flags` as in the options struct (MK_FLAG_STATIC_EXPERTS is
- * the one the schedule reads). *out is owned by the caller (mk_plan_destroy). */
+ * mk_build_schedule_chunked for `n_workers` workers; `flags` as in the options struct
+ * (MK_FLAG_STATIC_EXPERTS is the one the schedule reads). *out is owned by the caller
+ * (mk_plan_destroy). */
 mk_status mk_plan_build(const mk_model_desc* desc, int32_t batch, const int32_t* seq_lens_host,
-                        int32_t n_workers, int32_t split_keys, uint32_t flags, mk_plan** out);
+                        int32_t n_workers, int32_t split_keys, uint32_t flags, int32_t rows_per_seq,
+                        mk_plan** out);
 mk_status mk_plan_info_get(const mk_plan* p, mk_plan_info* info);
 /* Copy descriptors (n_tasks x 16 int32) and per-worker queue bounds (n_workers + 1 int32). */
 mk_status mk_plan_export(const mk_plan* p, int32_t* tasks, int32_t* queue_offsets);

@@ -66,11 +66,14 @@ def test_plan_build_rejects_bad_arguments():
     lens = (ctypes.c_int32 * 2)(65, 65)
     P32 = ctypes.POINTER(ctypes.c_int32)
     ok = ctypes.cast(lens, P32)
-    assert mk.LIB.mk_plan_build(ctypes.byref(d), 2, ok, 64, 0, 0, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG  # batch > max_batch
-    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, ok, 0, 0, 0, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG   # no workers
-    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, None, 64, 0, 0, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG
+    assert mk.LIB.mk_plan_build(ctypes.byref(d), 2, ok, 64, 0, 0, 1, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG  # batch > max_batch
+    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, ok, 0, 0, 0, 1, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG   # no workers
+    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, None, 64, 0, 0, 1, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG
     too_long = (ctypes.c_int32 * 1)(8 * 16 + 1)                                                           # > max_pages * 16
-    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, ctypes.cast(too_long, P32), 64, 0, 0, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG
+    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, ctypes.cast(too_long, P32), 64, 0, 0, 1, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG
     zero = (ctypes.c_int32 * 1)(0)
-    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, ctypes.cast(zero, P32), 64, 0, 0, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG
+    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, ctypes.cast(zero, P32), 64, 0, 0, 1, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG
+    one = ctypes.cast((ctypes.c_int32 * 1)(65), P32)
+    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, one, 64, 0, 0, 0, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG   # rows_per_seq 0
+    assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, one, 64, 0, 0, 2, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG   # > batch
     assert not h.value

@@ -243,3 +243,37 @@ def test_stream_read_bandwidth_rejects_bad_arguments():
         with pytest.raises(mk.MkError) as e:
             mk.mk_stream_read_bandwidth(*args)
         assert e.value.status == mk.MK_ERR_INVALID_ARG
+
+
+CHUNKED = [
+    ("tiny", [5, 6, 7, 8], 4, 64),                                   # one sequence, 4 consecutive positions
+    ("tiny", [40, 61, 62, 63, 64, 65, 17], 4, 512),                  # decode rows mixed with a 4-row chunk
+    ("full", list(range(4001, 4009)), 8, 512),                       # a whole step of one prompt
+    ("full", [8193, 300, 301, 302, 303, 304, 305, 17], 6, 512),      # mixed: decode rows and a 6-row chunk
+]
+
+
+@pytest.mark.parametrize("name,lens,rows,workers", CHUNKED)
+def test_chunked_plan_publishes_kv_in_the_qkv_tasks(name, lens, rows, workers):
+    """Schedules for rows of one sequence in one step: valid and deadlock-free, every K tile one whole
+    head (RoPE pairs dims d and d + D/2) and every V tile whole groups of 8 dims (16-byte stores),
+    and the host's capacity leaves room for steps that advance a row by `rows` positions."""
+    wl = synth.workload(name)
+    desc = _desc(wl, len(lens), max(lens) + 8 * 64)
+    plan = mk.mk_plan_build(desc, lens, workers, rows_per_seq=rows)
+    try:
+        st, msg = mk.mk_plan_validate(plan)
+        assert st == mk.MK_OK, msg
+        for seed in range(3):
+            st, msg = mk.mk_plan_simulate(plan, seed)
+            assert st == mk.MK_OK, msg
+        tasks, _ = mk.mk_plan_export(plan)
+        D, HQ, HKV = wl.head_dim, wl.n_q_heads, wl.n_kv_heads
+        qkv = tasks[tasks[:, 0] == 1]                          # OP_QKV: a0 first row, a1 rows
+        k = qkv[(qkv[:, 2] >= HQ * D) & (qkv[:, 2] < (HQ + HKV) * D)]
+        v = qkv[qkv[:, 2] >= (HQ + HKV) * D]
+        assert len(k) == wl.n_layers * HKV and np.all(k[:, 3] == D) and np.all((k[:, 2] - HQ * D) % D == 0)
+        assert np.all(v[:, 3] % 8 == 0) and np.all(v[:, 2] % 8 == 0)
+        assert mk.mk_plan_info_get(plan).key_capacity_min >= min(lens) + 32 * rows
+    finally:
+        mk.mk_plan_destroy(plan)
