@@ -3,12 +3,16 @@
 // decode loop while the control side - requests, prefill, batch management - runs in Python; P1
 // "From demo to a full serving system": continuous batching with ragged lengths).
 //
-// Sequences arrive with their prefill done (their K/V for positions [0, prompt_len) already in the
-// pages they own) and are admitted into free batch rows at the next step boundary; a sequence leaves
-// once it has generated its budget of tokens. Whenever the batch changes, the rows are packed
-// (active sequences in admission order), the block tables re-uploaded and the schedule rebuilt. The
-// control side can pause decode between steps (the pages pause decode while a prefill runs on the
-// same GPU) and can give the owner a step budget (manual stepping, used by the tests).
+// A sequence arrives either with its prefill done elsewhere (its K/V for positions [0, prompt_len)
+// already in the pages it owns) or with its prompt tokens, which the owner then prefills itself:
+// every step, each decoding sequence takes one batch row and the rows left over go to prompt chunks
+// (consecutive positions of one sequence, one per row), so prefill and decode share steps (P3
+// "Limitations and Future Plans": mixed batches are the pages' next step). Sequences are admitted at
+// step boundaries while fewer than max_batch are active; a sequence leaves once it has generated its
+// budget of tokens. Whenever the rows' composition changes, the block tables are re-uploaded and the
+// schedule rebuilt. The control side can pause decode between steps (for a prefill it runs itself on
+// the same GPU, as the pages do) and can give the owner a step budget (manual stepping, used by the
+// tests).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -31,11 +35,19 @@ namespace {
 
 struct Seq {
   int64_t id = -1;
-  int32_t pos = 0;               // position of the token decoded next
-  int32_t token = 0;             // token decoded next
+  int32_t pos = 0;               // next position: a prompt chunk's first row while pos < decode_at
+  int32_t decode_at = 0;         // position of the first decoded token (prompt positions lie before it)
+  int32_t token = 0;             // token decoded at decode_at (and later the last generated one)
   int32_t remaining = 0;         // tokens still to generate
+  std::vector<int32_t> prompt;   // prompt tokens still to prefill are prompt[pos] .. prompt[decode_at - 1]
   std::vector<int32_t> pages;
   std::vector<int32_t> out;      // generated tokens
+  bool prefilling() const { return pos < decode_at; }
+};
+
+struct Row {                     // one batch row of a step
+  int seq;                       // index into the step's active list
+  int32_t pos, token;
 };
 
 }  // namespace
@@ -64,9 +76,9 @@ struct mk_server {
   bool stop = false, pause_req = false, paused = false, busy = false;
   int64_t budget = -1;            // steps still allowed (-1: no limit)
   std::deque<Seq> pending;        // admitted at the next step boundary
-  std::vector<Seq> rows;          // active sequences, one per batch row
+  std::vector<Seq> rows;          // active sequences (admission order)
   std::vector<Seq> done;          // finished, not yet collected
-  int64_t steps = 0, tokens = 0, rebuilds = 0;
+  int64_t steps = 0, tokens = 0, rebuilds = 0, prefill_tokens = 0;
   double busy_s = 0;
   mk_status status = MK_OK;       // first failure of the owner (sticky)
   std::string msg;
@@ -85,24 +97,50 @@ void fail(mk_server* s, mk_status st, const std::string& what) {
   }
 }
 
-// Pack the active rows, upload their block tables and rebuild the schedule (owner thread, unlocked).
-mk_status rebuild(mk_server* s, const std::vector<Seq>& rows) {
+// The step's rows: one per decoding sequence, then the rows left over as prompt chunks, in admission
+// order (owner thread). `key` (sequence id and row count per sequence) identifies the composition.
+std::vector<Row> compose(const std::vector<Seq>& act, int max_batch, std::vector<int64_t>* key, int* rows_per_seq) {
+  std::vector<Row> rows;
+  std::vector<int> cnt(act.size(), 0);
+  for (int i = 0; i < (int)act.size(); ++i)
+    if (!act[i].prefilling()) { rows.push_back({i, act[i].pos, act[i].token}); cnt[i] = 1; }
+  for (int i = 0; i < (int)act.size() && (int)rows.size() < max_batch; ++i) {
+    const Seq& q = act[i];
+    if (!q.prefilling()) continue;
+    const int c = std::min(max_batch - (int)rows.size(), q.decode_at - q.pos);
+    for (int r = 0; r < c; ++r) rows.push_back({i, q.pos + r, q.prompt[q.pos + r]});
+    cnt[i] = c;
+  }
+  key->clear();
+  *rows_per_seq = 1;
+  for (int i = 0; i < (int)act.size(); ++i) {
+    key->push_back(act[i].id);
+    key->push_back(cnt[i]);
+    *rows_per_seq = std::max(*rows_per_seq, cnt[i]);
+  }
+  return rows;
+}
+
+// Upload the rows' block tables and rebuild the schedule (owner thread, unlocked).
+mk_status rebuild(mk_server* s, const std::vector<Seq>& act, const std::vector<Row>& rows, int rows_per_seq) {
   const int B = (int)rows.size(), P = s->desc.max_pages_per_seq;
   std::vector<int32_t> bt((size_t)s->max_batch * P, -1), lens(B);
   for (int b = 0; b < B; ++b) {
-    std::copy(rows[b].pages.begin(), rows[b].pages.end(), bt.begin() + (size_t)b * P);
+    const Seq& q = act[rows[b].seq];
+    std::copy(q.pages.begin(), q.pages.end(), bt.begin() + (size_t)b * P);
     lens[b] = rows[b].pos + 1;
   }
   if (hipMemcpyAsync(s->d_bt, bt.data(), bt.size() * sizeof(int32_t), hipMemcpyHostToDevice, s->stream) != hipSuccess ||
       hipStreamSynchronize(s->stream) != hipSuccess)
     return MK_ERR_HIP;
-  return mk_build_schedule(s->e, B, lens.data());
+  return mk_build_schedule_chunked(s->e, B, lens.data(), rows_per_seq);
 }
 
 void owner_loop(mk_server* s) {
   (void)hipSetDevice(s->device);
   std::unique_lock<std::mutex> lk(s->mu);
-  bool changed = true;
+  std::vector<int64_t> built_key;               // composition the current schedule was built for
+  bool have_schedule = false;
   for (;;) {
     s->cv.wait(lk, [&] {
       if (s->stop || s->pause_req) return true;
@@ -121,19 +159,24 @@ void owner_loop(mk_server* s) {
     while (!s->pending.empty() && (int)s->rows.size() < s->max_batch) {
       s->rows.push_back(std::move(s->pending.front()));
       s->pending.pop_front();
-      changed = true;
     }
-    std::vector<Seq> rows = s->rows;          // the owner's working copy for this step
+    std::vector<Seq> act = s->rows;           // the owner's working copy for this step
     s->busy = true;
     lk.unlock();
 
     const auto t0 = std::chrono::steady_clock::now();
+    std::vector<int64_t> key;
+    int rows_per_seq = 1;
+    const std::vector<Row> rows = compose(act, s->max_batch, &key, &rows_per_seq);
     const int B = (int)rows.size();
     mk_status st = MK_OK;
     std::string what;
+    const bool changed = !have_schedule || key != built_key;
     if (changed) {
-      st = rebuild(s, rows);
+      st = rebuild(s, act, rows, rows_per_seq);
       what = "mk_build_schedule";
+      have_schedule = st == MK_OK;
+      built_key = key;
     }
     for (int b = 0; b < B && st == MK_OK; ++b) {
       s->h_in[b] = rows[b].token;
@@ -152,7 +195,7 @@ void owner_loop(mk_server* s) {
       float* L = s->logits_out ? s->logits_out : s->d_logits;
       st = mk_decode_step(s->e, s->d_tokens, s->d_pos, s->d_bt, s->d_lens, L, s->stream);
       if (st == MK_ERR_SCHEDULE_STALE) {      // a sequence outgrew its attention splits: rebuild, retry
-        st = rebuild(s, rows);
+        st = rebuild(s, act, rows, rows_per_seq);
         rebuilt = st == MK_OK;
         if (st == MK_OK) st = mk_decode_step(s->e, s->d_tokens, s->d_pos, s->d_bt, s->d_lens, L, s->stream);
       }
@@ -176,36 +219,42 @@ void owner_loop(mk_server* s) {
       s->cv.notify_all();
       continue;                               // the owner idles until destroyed
     }
-    changed = false;
     if (rebuilt) s->rebuilds++;
     mk_server_step& rec = s->last;
     rec.step = s->steps;
     rec.batch = B;
+    int n_prefill = 0;
     for (int b = 0; b < MK_MAX_BATCH; ++b) {
-      rec.request_id[b] = b < B ? rows[b].id : -1;
+      const bool pf = b < B && rows[b].pos < act[rows[b].seq].decode_at;
+      n_prefill += pf ? 1 : 0;
+      rec.request_id[b] = b < B ? act[rows[b].seq].id : -1;
       rec.position[b] = b < B ? rows[b].pos : -1;
       rec.token_in[b] = b < B ? rows[b].token : -1;
-      rec.token_out[b] = b < B ? s->h_argmax[b] : -1;
+      rec.token_out[b] = b < B && !pf ? s->h_argmax[b] : -1;   // prompt rows generate nothing
     }
     rec.rebuilt = rebuilt ? 1 : 0;
-    // advance every row; finished sequences leave the batch
-    std::vector<Seq> keep;
+    rec.prefill_rows = n_prefill;
+    // advance every sequence (the active list only grew at the back since the step began); finished
+    // sequences leave the batch
+    std::vector<int> adv(act.size(), 0);
     for (int b = 0; b < B; ++b) {
-      Seq q = std::move(s->rows[b]);
+      Seq& q = s->rows[rows[b].seq];
+      if (rows[b].pos < act[rows[b].seq].decode_at) { adv[rows[b].seq]++; continue; }
       q.out.push_back(s->h_argmax[b]);
       q.token = s->h_argmax[b];
       q.pos += 1;
       q.remaining -= 1;
-      if (q.remaining <= 0) {
-        s->done.push_back(std::move(q));
-        changed = true;
-      } else {
-        keep.push_back(std::move(q));
-      }
+    }
+    for (int i = 0; i < (int)act.size(); ++i) s->rows[i].pos += adv[i];
+    std::vector<Seq> keep;
+    for (auto& q : s->rows) {
+      if (q.remaining <= 0) s->done.push_back(std::move(q));
+      else keep.push_back(std::move(q));
     }
     s->rows = std::move(keep);
     s->steps++;
-    s->tokens += B;
+    s->tokens += B - n_prefill;
+    s->prefill_tokens += n_prefill;
     s->busy_s += dt;
     if (s->budget > 0) s->budget--;
     s->cv.notify_all();
@@ -260,17 +309,27 @@ mk_status mk_server_create(mk_engine* e, const mk_server_config* cfg, mk_server*
 }
 
 mk_status mk_server_submit(mk_server* s, const mk_request* r) {
-  if (!s || !r || r->prompt_len < 0 || r->max_new_tokens < 1 || r->n_pages < 1 || !r->pages ||
-      r->first_token < 0 || r->first_token >= s->desc.vocab)
+  if (!s || !r || r->prompt_len < 0 || r->max_new_tokens < 1 || r->n_pages < 1 || !r->pages)
     return MK_ERR_INVALID_ARG;
-  const int64_t need = (int64_t)r->prompt_len + r->max_new_tokens;     // positions the sequence will hold
+  Seq q;
+  if (r->prompt) {                      // the owner prefills positions [0, prompt_len - 1)
+    if (r->prompt_len < 1) return MK_ERR_INVALID_ARG;
+    for (int i = 0; i < r->prompt_len; ++i)
+      if (r->prompt[i] < 0 || r->prompt[i] >= s->desc.vocab) return MK_ERR_INVALID_ARG;
+    q.prompt.assign(r->prompt, r->prompt + r->prompt_len);
+    q.pos = 0;
+    q.decode_at = r->prompt_len - 1;
+    q.token = r->prompt[r->prompt_len - 1];
+  } else {
+    if (r->first_token < 0 || r->first_token >= s->desc.vocab) return MK_ERR_INVALID_ARG;
+    q.pos = q.decode_at = r->prompt_len;
+    q.token = r->first_token;
+  }
+  const int64_t need = (int64_t)q.decode_at + r->max_new_tokens;     // positions the sequence will hold
   if (r->n_pages > s->desc.max_pages_per_seq || need > (int64_t)r->n_pages * mk::PAGE) return MK_ERR_INVALID_ARG;
   for (int i = 0; i < r->n_pages; ++i)
     if (r->pages[i] < 0 || r->pages[i] >= s->desc.num_pages) return MK_ERR_INVALID_ARG;
-  Seq q;
   q.id = r->request_id;
-  q.pos = r->prompt_len;
-  q.token = r->first_token;
   q.remaining = r->max_new_tokens;
   q.pages.assign(r->pages, r->pages + r->n_pages);
   std::lock_guard<std::mutex> lk(s->mu);
@@ -356,6 +415,7 @@ mk_status mk_server_stats(mk_server* s, mk_server_stats_t* out) {
   out->finished = (int32_t)s->done.size();
   out->paused = s->paused ? 1 : 0;
   out->busy_seconds = s->busy_s;
+  out->prefill_tokens = s->prefill_tokens;
   return s->status;
 }
 

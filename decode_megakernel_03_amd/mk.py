@@ -73,19 +73,21 @@ class ServerConfig(ctypes.Structure):
 
 class Request(ctypes.Structure):
     _fields_ = [("request_id", ctypes.c_int64), ("prompt_len", ctypes.c_int32), ("first_token", ctypes.c_int32),
-                ("max_new_tokens", ctypes.c_int32), ("n_pages", ctypes.c_int32), ("pages", ctypes.POINTER(ctypes.c_int32))]
+                ("max_new_tokens", ctypes.c_int32), ("n_pages", ctypes.c_int32), ("pages", ctypes.POINTER(ctypes.c_int32)),
+                ("prompt", ctypes.POINTER(ctypes.c_int32))]
 
 
 class ServerStep(ctypes.Structure):
     _fields_ = [("step", ctypes.c_int64), ("batch", ctypes.c_int32), ("rebuilt", ctypes.c_int32),
                 ("request_id", ctypes.c_int64 * MK_MAX_BATCH), ("position", ctypes.c_int32 * MK_MAX_BATCH),
-                ("token_in", ctypes.c_int32 * MK_MAX_BATCH), ("token_out", ctypes.c_int32 * MK_MAX_BATCH)]
+                ("token_in", ctypes.c_int32 * MK_MAX_BATCH), ("token_out", ctypes.c_int32 * MK_MAX_BATCH),
+                ("prefill_rows", ctypes.c_int32)]
 
 
 class ServerStats(ctypes.Structure):
     _fields_ = [("steps", ctypes.c_int64), ("tokens", ctypes.c_int64), ("rebuilds", ctypes.c_int64),
                 ("active", ctypes.c_int32), ("pending", ctypes.c_int32), ("finished", ctypes.c_int32),
-                ("paused", ctypes.c_int32), ("busy_seconds", ctypes.c_double)]
+                ("paused", ctypes.c_int32), ("busy_seconds", ctypes.c_double), ("prefill_tokens", ctypes.c_int64)]
 
 
 def load(path=LIB_PATH):
@@ -415,10 +417,16 @@ def mk_server_create(engine_h, max_batch, start_held=False, topk_out=None, route
     return h
 
 
-def mk_server_submit(h, request_id, pages, prompt_len, first_token, max_new_tokens):
+def mk_server_submit(h, request_id, pages, prompt_len, first_token, max_new_tokens, prompt=None):
+    """Queue a sequence: prefilled elsewhere (prompt None: K/V of [0, prompt_len) in its pages, first_token
+    decoded at prompt_len), or with its prompt tokens, which the server prefills itself."""
     arr = _i32_array(pages)
+    pr = None if prompt is None else _i32_array(prompt)
+    if pr is not None:
+        prompt_len, first_token = len(prompt), 0
     req = Request(int(request_id), int(prompt_len), int(first_token), int(max_new_tokens), len(pages),
-                  ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)))
+                  ctypes.cast(arr, ctypes.POINTER(ctypes.c_int32)),
+                  None if pr is None else ctypes.cast(pr, ctypes.POINTER(ctypes.c_int32)))
     _server_check(h, LIB.mk_server_submit(h, ctypes.byref(req)), "mk_server_submit")
 
 
@@ -467,7 +475,8 @@ def mk_server_last_step(h):
     B = rec.batch
     return {"step": rec.step, "batch": B, "rebuilt": bool(rec.rebuilt),
             "request_id": list(rec.request_id[:B]), "position": list(rec.position[:B]),
-            "token_in": list(rec.token_in[:B]), "token_out": list(rec.token_out[:B]), "logits_ptr": lp.value}
+            "token_in": list(rec.token_in[:B]), "token_out": list(rec.token_out[:B]), "logits_ptr": lp.value,
+            "prefill_rows": rec.prefill_rows}
 
 
 def mk_server_get_error(h):

@@ -3,13 +3,15 @@ C++ thread of libmk owning the decode loop (P3 "Scheduling and Performance Bench
 control thread handles control, prefill and batch management while a C++ thread owns decode; P1 "From
 demo to a full serving system": continuous batching with ragged sequence lengths).
 
-``Server`` wraps the library's decode owner (``mk_server_*``): it admits prefilled sequences at step
-boundaries, rebuilds the schedule when the batch changes and runs steps until told to hold.
+``Server`` wraps the library's decode owner (``mk_server_*``): it admits sequences at step
+boundaries, prefills the prompts it is given in chunks that share steps with decoding sequences
+(P3 "Limitations and Future Plans": mixed prefill/decode batches are the pages' next step), rebuilds
+the schedule when the rows' composition changes and runs steps until told to hold.
 ``ControlLoop`` is the control side: it collects finished sequences and returns their pages to a
-``PagePool``, and refills free batch rows from a request source; a refill pauses decode while the new
-sequence's prefill runs on the GPU (the prefill here writes seeded synthetic K/V, standing in for a
-model prefill), then submits the sequence and resumes decode. It can run as a thread of its own
-(``start`` / ``join``) or be driven one boundary at a time (``boundary``).
+``PagePool``, and refills free batch rows from a request source. Requests either carry their prompt
+tokens (the server prefills them, decode never pauses) or come with a ``prefill`` callable that the
+loop runs while decode is paused (the pages' arrangement; the callable here writes seeded synthetic
+K/V). It can run as a thread of its own (``start`` / ``join``) or one boundary at a time (``boundary``).
 """
 
 import collections
@@ -46,8 +48,8 @@ class Server:
                                      logits_out)
         self.max_batch = max_batch
 
-    def submit(self, request_id, pages, prompt_len, first_token, max_new_tokens):
-        mk.mk_server_submit(self.h, request_id, pages, prompt_len, first_token, max_new_tokens)
+    def submit(self, request_id, pages, prompt_len, first_token, max_new_tokens, prompt=None):
+        mk.mk_server_submit(self.h, request_id, pages, prompt_len, first_token, max_new_tokens, prompt)
 
     def pause(self):
         mk.mk_server_pause(self.h)
@@ -83,9 +85,10 @@ class Server:
 
 class ControlLoop:
     """Control side of the serving loop over a ``Server``: keeps every batch row busy from ``requests``
-    (an iterator of (prompt_len, max_new_tokens, first_token)), prefilling each new sequence into pages
-    from ``pool`` while decode is paused, and collects finished sequences (tokens kept in ``results``).
-    ``prefill(pages, prompt_len, seed)`` writes the prompt's K/V; ``page_size`` sizes the allocation."""
+    and collects finished sequences (tokens kept in ``results``), with pages from ``pool``.
+    With ``prefill`` None, requests are (prompt tokens, max_new_tokens) and the server prefills them.
+    Otherwise requests are (prompt_len, max_new_tokens, first_token) and ``prefill(pages, prompt_len,
+    seed)`` writes the prompt's K/V while decode is paused. ``page_size`` sizes the allocation."""
 
     def __init__(self, server, pool, requests, prefill, page_size=16, seed=0, first_id=0):
         self.server, self.pool, self.requests, self.prefill = server, pool, iter(requests), prefill
@@ -116,12 +119,23 @@ class ControlLoop:
         n = 0
         while not self.exhausted and len(self.in_flight) < self.server.max_batch:
             try:
-                prompt_len, max_new, first = next(self.requests)
+                req = next(self.requests)
             except StopIteration:
                 self.exhausted = True
                 break
-            pages = self.pool.alloc((prompt_len + max_new + self.page_size - 1) // self.page_size)
             rid = self.next_id
+            if self.prefill is None:                          # the server prefills the prompt
+                prompt, max_new = [int(t) for t in req[0]], int(req[1])
+                pages = self.pool.alloc((len(prompt) - 1 + max_new + self.page_size - 1) // self.page_size)
+                self.next_id += 1
+                self.server.submit(rid, pages, len(prompt), 0, max_new, prompt=prompt)
+                self.in_flight[rid] = (pages, len(prompt), max_new, prompt[-1])
+                self.budgets[rid] = max_new
+                self.refills += 1
+                n += 1
+                continue
+            prompt_len, max_new, first = req
+            pages = self.pool.alloc((prompt_len + max_new + self.page_size - 1) // self.page_size)
             self.next_id += 1
             t0 = time.perf_counter()
             self.server.pause()                               # decode paused while the prefill runs

@@ -244,6 +244,16 @@ def synthetic_requests(wl, seed, n, ctx=(1024, 32768), new_tokens=(1, 1024)):
     return [(int(c[i]), int(o[i]), int(t[i])) for i in range(n)]
 
 
+def synthetic_prompts(wl, seed, n, ctx=(1, 64), new_tokens=(1, 8)):
+    """n requests that carry their prompts: length log-uniform in ctx, tokens uniform in [0, V), output
+    budget uniform in new_tokens (inclusive). Returns (prompt tokens, max_new)."""
+    rng = np.random.default_rng([seed, 23])
+    c = np.floor(np.exp(rng.uniform(math.log(ctx[0]), math.log(ctx[1] + 1), size=n))).astype(np.int64)
+    c = np.clip(c, ctx[0], ctx[1])
+    o = rng.integers(new_tokens[0], new_tokens[1] + 1, size=n)
+    return [(rng.integers(0, max(wl.vocab, 1), size=int(c[i])).astype(np.int32), int(o[i])) for i in range(n)]
+
+
 def first_tokens(wl, seed=2):
     rng = np.random.default_rng([seed, 3])
     return rng.integers(0, max(wl.vocab, 1), size=wl.batch).astype(np.int32)

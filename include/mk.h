@@ -269,12 +269,15 @@ mk_status mk_handoff_litmus_noalloc(int32_t rounds, int32_t words, int32_t workg
  * A C++ thread that owns an engine and decodes a continuously changing batch (P3 "Scheduling and
  * Performance Benchmarks": a C++ thread owns the decode loop while requests, prefill and batch
  * management run on the control side; P1 "From demo to a full serving system": continuous batching
- * with ragged lengths). Sequences are submitted with their prefill done (K/V of positions
- * [0, prompt_len) already in the pages they own) and join the batch at the next step boundary; a
- * sequence leaves after generating max_new_tokens tokens (greedy: each step's argmax feeds its next
- * step). Whenever the batch changes, the rows are packed (in admission order), their block tables
- * uploaded and the schedule rebuilt; a sequence that outgrows its attention splits gets the schedule
- * rebuilt too. While a server exists, the engine belongs to its thread: the caller must not call any
+ * with ragged lengths). A sequence is submitted either with its prefill done elsewhere (K/V of
+ * positions [0, prompt_len) already in the pages it owns) or with its prompt, which the owner prefills
+ * through the decode kernel: every step, each decoding sequence takes one batch row and the rows left
+ * over go to prompt chunks (consecutive positions of one sequence), so prefill and decode share steps
+ * (P3 "Limitations and Future Plans": mixed batches are the pages' next step). Up to max_batch
+ * sequences are active (admitted at step boundaries, in submission order); a sequence leaves after
+ * generating max_new_tokens tokens (greedy: each step's argmax feeds its next step). Whenever the rows'
+ * composition changes, the block tables are uploaded and the schedule rebuilt; a sequence that
+ * outgrows its attention splits gets the schedule rebuilt too. While a server exists, the engine belongs to its thread: the caller must not call any
  * other function on that engine until mk_server_destroy. Server functions may be called from any one
  * control thread. */
 typedef struct mk_server mk_server;
@@ -290,11 +293,17 @@ typedef struct {
 
 typedef struct {
   int64_t request_id;         /* the caller's id */
-  int32_t prompt_len;         /* positions already prefilled; decoding starts at this position */
-  int32_t first_token;        /* the token decoded at position prompt_len */
+  int32_t prompt_len;         /* prompt == NULL: positions already prefilled, decoding starts there;
+                                 else: prompt tokens (>= 1) */
+  int32_t first_token;        /* prompt == NULL: the token decoded at position prompt_len (else unused) */
   int32_t max_new_tokens;     /* tokens to generate (>= 1) */
   int32_t n_pages;            /* pages the sequence owns, in position order */
-  const int32_t* pages;       /* host array, copied at submit; must cover prompt_len + max_new_tokens positions */
+  const int32_t* pages;       /* host array, copied at submit; must cover the positions the sequence
+                                 will hold: prompt_len + max_new_tokens (prompt: one fewer) */
+  const int32_t* prompt;      /* NULL, or the prompt's prompt_len tokens (host, copied at submit): the
+                                 owner prefills positions [0, prompt_len - 1) in prompt chunks and decodes
+                                 the last prompt token at position prompt_len - 1, whose greedy token is
+                                 the first generated one */
 } mk_request;
 
 typedef struct {              /* composition of the last step */
@@ -304,21 +313,23 @@ typedef struct {              /* composition of the last step */
   int64_t request_id[MK_MAX_BATCH];
   int32_t position[MK_MAX_BATCH];
   int32_t token_in[MK_MAX_BATCH];
-  int32_t token_out[MK_MAX_BATCH];
+  int32_t token_out[MK_MAX_BATCH]; /* -1 for a prompt row (it generates nothing) */
+  int32_t prefill_rows;       /* rows of the step that were prompt positions */
 } mk_server_step;
 
 typedef struct {
-  int64_t steps, tokens, rebuilds;
+  int64_t steps, tokens, rebuilds;  /* tokens: generated ones */
   int32_t active, pending, finished, paused;
   double busy_seconds;        /* wall time the owner spent in steps (schedule rebuilds included) */
+  int64_t prefill_tokens;     /* prompt positions the owner prefilled */
 } mk_server_stats_t;
 
 /* Start the decode owner over engine e (its step outputs are taken over: argmax by the server, the
  * optional ones from cfg). Allocates the step buffers (device and pinned host) once. MK_ERR_INVALID_ARG
  * for NULL arguments or max_batch outside 1..the engine's max_batch; MK_ERR_OOM / MK_ERR_HIP. */
 mk_status mk_server_create(mk_engine* e, const mk_server_config* cfg, mk_server** out);
-/* Queue a prefilled sequence (copied). MK_ERR_INVALID_ARG for a bad request (page ids outside the pool,
- * too few pages, a token outside the vocabulary); the server's sticky error if it failed. */
+/* Queue a sequence (copied). MK_ERR_INVALID_ARG for a bad request (page ids outside the pool, too few
+ * pages, a token outside the vocabulary, an empty prompt); the server's sticky error if it failed. */
 mk_status mk_server_submit(mk_server* s, const mk_request* r);
 /* Hold decode between steps and return once the owner is holding (a prefill may then use the GPU and
  * the pages), or the server's sticky error. */

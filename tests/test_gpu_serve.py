@@ -3,6 +3,8 @@
 * Small model, three batch rows, twelve requests: the control loop runs as a thread of its own and
   keeps the rows busy (continuous batching, refills while decode is paused); every request's tokens
   equal the oracle's greedy decode of that request alone from the K/V its prefill wrote.
+* Small model, four rows, ten requests that carry their prompts: the server prefills them in chunks
+  mixed with decoding rows; every request's tokens equal the oracle's prefill + greedy decode.
 * The 48-layer model on the ragged Zipf-routed batch of eight, stepped one step at a time: the first
   step, the step right after a finished sequence's row is refilled with a new prompt (schedule rebuilt,
   pages reused), and a step after a sequence left without a replacement are each checked against the
@@ -64,6 +66,45 @@ def test_serve_tiny_continuous_batching():
         res = oracle.greedy_decode(dims, dw, kv, [first], [c], bt, [c + 1], o)
         ref = [int(np.argmax(r.logits[0])) for r in res]
         say(f"  request {rid}: prompt {c}, {o} tokens: {got}")
+        assert got == ref, f"request {rid}: GPU {got} != oracle {ref}"
+    eng.close()
+
+
+def test_serve_tiny_prompts_prefilled_in_mixed_batches():
+    """Requests that carry their prompts: the server prefills them in chunks that share steps with the
+    decoding sequences (no pause). Every request's tokens equal the oracle's: its prefill of the prompt
+    but the last token, then greedy decode from the last prompt token, alone."""
+    import oracle
+    import oracle.prefill
+    from decode_megakernel_03_amd import mk, serve
+    say("test_serve_tiny_prompts_prefilled_in_mixed_batches: 4 rows, 10 prompts of 1..40 tokens")
+    wl = synth.workload("tiny", batch=4)
+    w = synth.make_weights(wl, seed=0, device="cuda", gains="uniform")
+    num_pages, max_pages = 64, 4
+    k, v = synth.make_kv(wl, num_pages, device="cuda")
+    eng = mk.Engine(wl, w, k, v, num_pages, max_pages, max_batch=4)
+    reqs = synth.synthetic_prompts(wl, seed=8, n=10, ctx=(1, 40), new_tokens=(1, 6))
+    srv = serve.Server(eng, 4)
+    ctl = serve.ControlLoop(srv, serve.PagePool(np.random.default_rng(4).permutation(num_pages)), reqs, None)
+    ctl.start()
+    ctl.join(timeout=300)
+    st = srv.stats()
+    srv.close()
+    say(f"  {st.steps} steps, {st.tokens} generated, {st.prefill_tokens} prompt positions, {st.rebuilds} rebuilds")
+    assert st.prefill_tokens == sum(len(p) - 1 for p, _ in reqs)
+    dims = harness.dims_of(wl)
+    dw = harness.dense_weights(w)
+    for rid, (prompt, o) in enumerate(reqs):
+        n = len(prompt)
+        kv = oracle.PagedKV(k=[np.zeros((max_pages, wl.n_kv_heads, 16, wl.head_dim), np.uint16) for _ in range(wl.n_layers)],
+                            v=[np.zeros((max_pages, wl.n_kv_heads, 16, wl.head_dim), np.uint16) for _ in range(wl.n_layers)])
+        bt = np.arange(max_pages, dtype=np.int32)[None, :]
+        if n > 1:
+            oracle.prefill.prefill(dims, dw, kv, prompt[:-1].astype(np.int64), bt[0], 0)
+        res = oracle.greedy_decode(dims, dw, kv, [int(prompt[-1])], [n - 1], bt, [n], o)
+        ref = [int(np.argmax(r.logits[0])) for r in res]
+        got = ctl.results[rid]
+        say(f"  request {rid}: prompt {n}, {o} tokens: {got}")
         assert got == ref, f"request {rid}: GPU {got} != oracle {ref}"
     eng.close()
 

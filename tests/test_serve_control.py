@@ -27,8 +27,12 @@ class FakeServer:
         self.paused = False
         self.events.append("resume")
 
-    def submit(self, rid, pages, prompt_len, first, max_new):
-        assert self.paused, "a sequence must be submitted while decode is paused (its prefill just ran)"
+    def submit(self, rid, pages, prompt_len, first, max_new, prompt=None):
+        if prompt is None:
+            assert self.paused, "a prefilled sequence must be submitted while decode is paused (its prefill just ran)"
+        else:
+            assert not self.paused and prompt_len == len(prompt)
+            assert len(pages) * 16 >= prompt_len - 1 + max_new
         self.pending.append([rid, max_new, []])
         self.events.append(("submit", rid))
 
@@ -110,3 +114,19 @@ def test_control_loop_as_a_thread():
     t.join()
     assert sorted(ctl.results) == list(range(12))
     assert all(len(ctl.results[i]) == reqs[i][1] for i in range(12))
+
+
+def test_control_loop_hands_prompts_to_the_server_without_pausing():
+    """Requests that carry their prompts go to the server as they are (it prefills them in steps it
+    shares with decode): no pause, pages for prompt_len - 1 + max_new positions, all collected."""
+    srv = FakeServer(3)
+    pool = PagePool(range(40))
+    reqs = [([5] * n, o) for n, o in [(1, 2), (17, 3), (40, 1), (3, 5), (16, 1)]]
+    ctl = ControlLoop(srv, pool, reqs, None)
+    while not ctl.done():
+        ctl.boundary()
+        srv.step()
+    assert "pause" not in srv.events
+    assert sorted(ctl.results) == list(range(5))
+    assert [len(ctl.results[i]) for i in range(5)] == [2, 3, 1, 5, 1]
+    assert len(pool.free) == 40
