@@ -101,6 +101,10 @@ def main():
         return read_calibration()
     from decode_megakernel_03_amd import metrics, mk, synth
 
+    if args.workload == "prefill":
+        return bench_prefill(args)
+    if args.workload == "serve":
+        return bench_serve(args)
     over = {}
     if args.batch:
         over["batch"] = args.batch
@@ -192,6 +196,96 @@ def main():
     out["roofline"]["frac_of_read_ceiling"] = round(achieved / ceil, 4)
     print(json.dumps(out), flush=True)
     torch.cuda.synchronize()
+
+
+def bench_prefill(args):
+    """Prompt positions per second through mk_prefill (chunks of 8 consecutive positions per step of the
+    decode kernel) on the 48-layer model, one prompt of --context positions (default 2048) from
+    position 0. Bytes per chunk step: dense weights, the union of the chunk's routed experts, lm_head
+    and the sequence's K/V once (the rows of a chunk read the same keys)."""
+    import torch
+    from decode_megakernel_03_amd import metrics, mk, synth
+    P = args.context or 2048
+    wl = synth.workload("full", context=P)
+    log(f"[bench] prefill: generating the 48-layer model; prompt of {P} positions")
+    w = synth.make_weights(wl, seed=0, device="cuda")
+    npg = (P + wl.page_size - 1) // wl.page_size
+    k, v = synth.make_kv(wl, npg, device="cuda")
+    eng = mk.Engine(wl, w, k, v, npg, npg, max_batch=8)
+    prompt = np.random.default_rng(31).integers(0, wl.vocab, P).tolist()
+    bt = list(range(npg))
+    logits = torch.zeros(wl.vocab, dtype=torch.float32, device="cuda")
+    topk = torch.zeros(wl.n_layers, P, wl.top_k, dtype=torch.int32, device="cuda")
+    eng.prefill(prompt[:64], 0, bt, logits_out=logits)          # warm-up (untimed)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    eng.prefill(prompt, 0, bt, logits_out=logits, topk_out=topk)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    eng.sync()
+    th = topk.cpu().numpy()
+    total = 0
+    for c0 in range(0, P, 8):
+        c1 = min(P, c0 + 8)
+        union = [len(np.unique(th[l, c0:c1])) for l in range(wl.n_layers)]
+        total += metrics.weight_bytes(synth.workload("full", batch=c1 - c0), union) + metrics.kv_bytes(wl, [c1])
+    rate = P / wall
+    achieved = total / wall
+    log(f"[bench] prefill: {P} positions in {wall:.3f} s -> {rate:.1f} positions/s; {total / 1e9:.1f} GB -> "
+        f"{achieved / 1e9:.0f} GB/s ({achieved / PEAK_HBM:.1%} of 8 TB/s)")
+    out = {"metric": "prefill positions/s on 1 GPU (chunks of 8 through the decode kernel)", "value": round(rate, 2),
+           "unit": "positions/s", "n_gpus": 1, "steps": (P + 7) // 8, "warmup": 1, "ms_per_step": round(wall * 1e3 / ((P + 7) // 8), 4),
+           "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"prefill: 48-layer parallel-MoE decoder, one prompt of {P} positions from position 0, "
+                                  "bf16 weights and KV, fp32 arithmetic", "prompt": P, "layers": wl.n_layers},
+           "roofline": {"bound": "hbm", "achieved": round(achieved / 1e9, 1), "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                        "frac": round(achieved / PEAK_HBM, 4), "traffic": None,
+                        "note": "wall time of mk_prefill: schedule builds included"},
+           "cpu_baseline": None, "bytes_total": int(total)}
+    eng.close()
+    print(json.dumps(out), flush=True)
+
+
+def bench_serve(args):
+    """The serving loop on the 48-layer model: requests that carry their prompts (log-uniform 64..2048
+    positions, 32..256 new tokens) through the C++ decode owner with eight rows; prompts are prefilled
+    in chunks that share steps with decoding sequences. Reports generated and prompt tokens per second
+    of wall time (schedule rebuilds included) and the owner's step statistics."""
+    import torch
+    from decode_megakernel_03_amd import mk, serve, synth
+    n_req = max(8, args.steps // 4) if args.steps != 128 else 32
+    wl = synth.workload("full_b8")
+    log(f"[bench] serve: generating the 48-layer model; {n_req} requests")
+    w = synth.make_weights(wl, seed=0, device="cuda")
+    reqs = synth.synthetic_prompts(wl, seed=41, n=n_req, ctx=(64, 2048), new_tokens=(32, 256))
+    max_pages = max((len(p) - 1 + o + 15) // 16 for p, o in reqs)
+    num_pages = 8 * max_pages
+    k, v = synth.make_kv(wl, num_pages, device="cuda")
+    eng = mk.Engine(wl, w, k, v, num_pages, max_pages, max_batch=8)
+    srv = serve.Server(eng, 8)
+    ctl = serve.ControlLoop(srv, serve.PagePool(range(num_pages)), reqs, None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ctl.start()
+    ctl.join(timeout=900)
+    wall = time.perf_counter() - t0
+    st = srv.stats()
+    srv.close()
+    eng.close()
+    gen = int(st.tokens)
+    log(f"[bench] serve: {n_req} requests in {wall:.2f} s: {gen} generated ({gen / wall:.1f} tok/s), {st.prefill_tokens} "
+        f"prompt positions; {st.steps} steps, {st.rebuilds} schedule rebuilds, owner busy {st.busy_seconds:.2f} s")
+    out = {"metric": "serving: generated tok/s on 1 GPU (continuous batching, mixed prefill/decode)",
+           "value": round(gen / wall, 2), "unit": "tok/s", "n_gpus": 1, "steps": int(st.steps), "warmup": 0,
+           "ms_per_step": round(st.busy_seconds * 1e3 / max(1, st.steps), 4), "higher_is_better": True,
+           "scaling": "weak", "vs_baseline": None, "dtype": "f32", "data": "synthetic",
+           "config": {"workload": f"serve: 48-layer parallel-MoE decoder, {n_req} requests, prompts log-uniform 64..2048, "
+                                  "32..256 new tokens, 8 rows, prompts prefilled by the server", "requests": n_req},
+           "prompt_positions_per_s": round(st.prefill_tokens / wall, 2),
+           "total_positions_per_s": round((gen + st.prefill_tokens) / wall, 2),
+           "schedule_rebuilds": int(st.rebuilds), "owner_busy_s": round(st.busy_seconds, 3), "wall_s": round(wall, 3),
+           "roofline": None, "cpu_baseline": None}
+    print(json.dumps(out), flush=True)
 
 
 def read_ceiling(nbytes=4 << 30, reps=5):

@@ -431,7 +431,14 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // workers idle in level 0 and prefetch their keys early), then least total load, then index.
   // Each worker's queue is level-ordered, and inside a level its tasks run in priority order
   // (router before QKV, attention before expert slices).
-  std::vector<std::vector<std::pair<int, Proto>>> queues(W);   // (level, proto)
+  // each worker's queue as (level, index in level) references; the descriptors are copied once, at the end
+  struct Ref { int32_t lv, idx; };
+  std::vector<std::vector<Ref>> queues(W);
+  {
+    size_t ntask = 0;
+    for (auto& lvl : levels) ntask += lvl.size();
+    for (auto& q : queues) q.reserve(ntask / W + 16);
+  }
   std::unordered_map<int, int> split_worker;                    // attention split key -> worker
   std::vector<int64_t> total(W, 0), prev(W, 0);
   std::vector<char> merge_w(W, 0);                              // workers with a merge this layer
@@ -475,7 +482,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       merge_w[w] = 1;
       lload[w] += lvl[idx].bytes;
       total[w] += lvl[idx].bytes;
-      queues[w].push_back({lv, lvl[idx]});
+      queues[w].push_back({lv, idx});
     }
     for (int w = 0; w < W; ++w) put(w, w);
     for (int i = W / 2 - 1; i >= 0; --i) sift_down(i);
@@ -485,7 +492,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       lload[best] += lvl[idx].bytes;           // only the top's key grows: restore the heap below it
       total[best] += lvl[idx].bytes;
       sift_down(0);
-      queues[best].push_back({lv, lvl[idx]});
+      queues[best].push_back({lv, idx});
       if (lvl[idx].pin <= -2) split_worker[-2 - lvl[idx].pin] = best;
     }
     if (out_level) {
@@ -495,16 +502,22 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     prev = lload;
   }
   P->tasks.clear(); P->bytes.clear(); P->qoff.assign(W + 1, 0);
+  {
+    size_t ntask = 0;
+    for (auto& q : queues) ntask += q.size();
+    P->tasks.reserve(ntask);
+    P->bytes.reserve(ntask);
+  }
   for (int w = 0; w < W; ++w) {
     auto& q = queues[w];
-    std::stable_sort(q.begin(), q.end(), [](const auto& a, const auto& b) {
-      return a.first != b.first ? a.first < b.first : a.second.prio < b.second.prio;
+    std::stable_sort(q.begin(), q.end(), [&](const Ref& a, const Ref& b) {
+      return a.lv != b.lv ? a.lv < b.lv : levels[a.lv][a.idx].prio < levels[b.lv][b.idx].prio;
     });
     P->qoff[w] = (int32_t)P->tasks.size();
-    for (auto& [lv, pr] : q) {
-      Task t = pr.t;
-      t.w[D_ID] = (int32_t)P->tasks.size();
-      P->tasks.push_back(t);
+    for (const Ref& r : q) {
+      const Proto& pr = levels[r.lv][r.idx];
+      P->tasks.push_back(pr.t);
+      P->tasks.back().w[D_ID] = (int32_t)P->tasks.size() - 1;
       P->bytes.push_back(pr.bytes);
     }
   }
