@@ -28,7 +28,9 @@ full softmax renormalised; MoE sparse sum vs a dense loop over every expert with
 fp32 vs fp64, batch-row independence, zero branch weights -> identity. Prefill: equal to the
 decode step one position at a time, to itself on a split prompt, causal, and a one-position
 prefill equal to a decode step; planted mistakes (mask off by one, no mask, RoPE positions, stale
-keys, unweighted experts) each fail a pin.
+keys, unweighted experts) each fail a pin. FP8 weights: E4M3 decoder vs torch's float8_e4m3fn for all
+256 codes and at the format's landmarks; packed-row layout; an FP8 model with power-of-two row scales
+equals its bf16 twin bit for bit (decode step and prefill), and misapplied scales break the equality.
 
 Parity unpinned: nothing the pages print can be recomputed here (the pages give no model
 dimensions and no worked example), so no whole-step value is pinned to the pages themselves.

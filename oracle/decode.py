@@ -13,7 +13,10 @@ What the pages fix
   Architecture"); RoPE is applied to queries and keys (same section).
 * Attention reads a paged KV cache through per-sequence block tables, with ragged sequence
   lengths in one batch (P1 "From demo to a full serving system"; P3 "Key Technologies").
-* Weights and KV cache are BF16 (P1 "Decode is a bandwidth game"; P2 body).
+* Weights and KV cache are BF16 (P1 "Decode is a bandwidth game"; P2 body). The FP8 variant
+  (P3 "Limitations and Future Plans" names FP8/FP4 kernels as the next step) stores the matrices
+  as E4M3 codes with a float32 scale per row (``oracle.fp8``); the step is the same over the
+  dequantized weights.
 
 Readings (the pages are silent; each is the plainest choice the rest supports)
 -------------------------------------------------------------------------------
@@ -39,7 +42,8 @@ R10 Greedy decoding takes the first index of the maximum logit.
 
 Storage conventions (they are the boundary's layouts too)
 --------------------------------------------------------
-bf16 tensors are uint16 bit patterns. embed/lm_head [V, H]; norms [H]; w_qkv [(Hq+2Hkv)*D, H]
+bf16 tensors are uint16 bit patterns (FP8 matrices: uint8 packed rows of K codes + 16 scale bytes,
+see ``oracle.fp8``). embed/lm_head [V, H]; norms [H]; w_qkv [(Hq+2Hkv)*D, H]
 with rows ordered q heads, then k heads, then v heads; w_o [H, Hq*D]; w_router [E, H];
 w_gate/w_up [E, F, H]; w_down [E, H, F]; KV cache per layer [num_pages, Hkv, page, D] for K and
 for V separately; block_tables [B, max_pages] int32 (page ids, -1 where unused).
@@ -51,6 +55,7 @@ from typing import Optional
 import numpy as np
 
 from .bf16 import bf16_to_f32, f32_to_bf16, f64_to_bf16
+from .fp8 import dequant_rows
 
 
 @dataclass(frozen=True)
@@ -131,8 +136,12 @@ class StepResult:
 # pieces
 # ----------------------------------------------------------------------------------------------
 
-def _dec(u16, dtype):
-    return bf16_to_f32(u16).astype(dtype, copy=False)
+def _dec(a, dtype):
+    """A stored tensor as values in ``dtype``: bf16 bit patterns (uint16), or a matrix of packed FP8
+    rows (uint8: E4M3 codes and a float32 scale per row, ``oracle.fp8``) dequantized."""
+    if a.dtype == np.uint8:
+        return dequant_rows(a, dtype)
+    return bf16_to_f32(a).astype(dtype, copy=False)
 
 
 def rmsnorm(x, gain, eps, dtype=np.float32):
