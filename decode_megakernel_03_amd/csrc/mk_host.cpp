@@ -59,6 +59,7 @@ void put(char* buf, size_t n, const std::string& s) {
 
 struct Dims {
   int L, H, HQ, HKV, D, E, K, F, V, HPG, QKVR, AD, PART;
+  int wb;      // bytes per matrix weight (2 bf16, 1 FP8), for the schedule's cost model
   bool lm;
 };
 
@@ -68,6 +69,7 @@ Dims dims_of(const mk_model_desc& d) {
   m.E = d.n_experts; m.K = d.top_k; m.F = d.expert_ffn; m.V = d.vocab;
   m.HPG = m.HQ / m.HKV; m.QKVR = (m.HQ + 2 * m.HKV) * m.D; m.AD = m.HQ * m.D;
   m.PART = m.HPG * (m.D + 2);
+  m.wb = d.weight_format == MK_WEIGHTS_FP8 ? 1 : 2;
   m.lm = d.has_lm_head != 0;
   return m;
 }
@@ -80,7 +82,11 @@ mk_status check_desc(const mk_model_desc* d, std::string* why) {
   }
   if (d->max_batch < 1 || d->max_batch > MK_MAX_BATCH) { *why = fmt("max_batch %d outside 1..%d", d->max_batch, MK_MAX_BATCH); return MK_ERR_INVALID_ARG; }
   if (d->page_size != PAGE) { *why = fmt("page_size %d unsupported (16)", d->page_size); return MK_ERR_UNSUPPORTED; }
-  if (shape_id(d->hidden, d->head_dim, d->n_q_heads, d->n_kv_heads, d->n_experts, d->top_k, d->expert_ffn) < 0) {
+  if (d->weight_format != MK_WEIGHTS_BF16 && d->weight_format != MK_WEIGHTS_FP8) {
+    *why = fmt("weight_format %d unknown", d->weight_format); return MK_ERR_INVALID_ARG;
+  }
+  if (shape_id(d->hidden, d->head_dim, d->n_q_heads, d->n_kv_heads, d->n_experts, d->top_k, d->expert_ffn,
+               d->weight_format == MK_WEIGHTS_FP8) < 0) {
     *why = "no compiled kernel for this (hidden, head_dim, heads, experts, top_k, expert_ffn)"; return MK_ERR_UNSUPPORTED;
   }
   if (!(d->rms_eps > 0.f) || !(d->rope_theta > 0.f)) { *why = "rms_eps and rope_theta must be > 0"; return MK_ERR_INVALID_ARG; }
@@ -282,7 +288,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.t.w[D_A0] = rg[0] + a; pr.t.w[D_A1] = e - a;
           pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;   // target filled below
           pr.t.w[D_SIG] = c_qkv[l][g];
-          pr.bytes = (int64_t)(e - a) * m.H * 2;
+          pr.bytes = (int64_t)(e - a) * m.H * m.wb;
           pr.prio = 1;
           levels[lv0].push_back(pr);
           qkv_count[g]++;
@@ -295,7 +301,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a; pr.t.w[D_A2] = router_tiles;
       pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;   // target filled below
       pr.t.w[D_SIG] = c_rarr[l]; pr.t.w[D_SIG2] = c_route[l];
-      pr.bytes = (int64_t)(e - a) * m.H * 2;
+      pr.bytes = (int64_t)(e - a) * m.H * m.wb;
       pr.prio = 0;
       levels[lv0].push_back(pr);
     }
@@ -338,7 +344,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
         pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
         pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
         pr.t.w[D_SIG] = c_h[l];
-        pr.bytes = ((int64_t)slots * slices * 2 * nf * m.H * 2 + (int64_t)slots * m.H * m.F * 2) / tickets;
+        pr.bytes = ((int64_t)slots * slices * 2 * nf * m.H * m.wb + (int64_t)slots * m.H * m.F * m.wb) / tickets;
         pr.prio = 1;
         levels[lv1].push_back(pr);
         n_gu++;
@@ -353,7 +359,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
           pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
           pr.t.w[D_SIG] = c_h[l];
-          pr.bytes = (int64_t)2 * (f1 - f0) * m.H * 2;
+          pr.bytes = (int64_t)2 * (f1 - f0) * m.H * m.wb;
           pr.prio = 1;
           levels[lv1].push_back(pr);
           n_gu++;
@@ -386,7 +392,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
       pr.t.w[D_W1] = c_h[l]; pr.t.w[D_T1] = n_gu;
       pr.t.w[D_SIG] = c_x[l + 1];
-      pr.bytes = (int64_t)(e - a) * (m.AD + (down_items > 0 ? 0 : (int64_t)slots * m.F)) * 2;
+      pr.bytes = (int64_t)(e - a) * (m.AD + (down_items > 0 ? 0 : (int64_t)slots * m.F)) * m.wb;
       pr.prio = 0;
       levels[lv2].push_back(pr);
       n_out++;
@@ -412,7 +418,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       set(pr.t, OP_LMHEAD, L, LPL * L);
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
       pr.t.w[D_W0] = c_x[L]; pr.t.w[D_T0] = n_out_per_layer;
-      pr.bytes = (int64_t)(e - a) * m.H * 2;
+      pr.bytes = (int64_t)(e - a) * m.H * m.wb;
       pr.prio = 0;
       levels[LPL * L].push_back(pr);
     }
@@ -847,7 +853,8 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weight_ptrs* w, mk_engin
   e->desc = *desc;
   e->m = dims_of(*desc);
   e->w = *w;
-  e->shape = shape_id(desc->hidden, desc->head_dim, desc->n_q_heads, desc->n_kv_heads, desc->n_experts, desc->top_k, desc->expert_ffn);
+  e->shape = shape_id(desc->hidden, desc->head_dim, desc->n_q_heads, desc->n_kv_heads, desc->n_experts, desc->top_k,
+                      desc->expert_ffn, desc->weight_format == MK_WEIGHTS_FP8);
   e->opt.workers_per_cu = 2;
   e->opt.watchdog_ms = 2000;
   auto fail = [&](mk_status s) { free_all(e); delete e; return s; };
@@ -915,6 +922,10 @@ mk_status mk_build_schedule_chunked(mk_engine* e, int32_t batch, const int32_t* 
   if (!e || !seq_lens_host || batch < 1 || batch > e->desc.max_batch || rows_per_seq < 1 || rows_per_seq > batch) {
     if (e) e->msg = "mk_build_schedule: bad batch, seq_lens or rows_per_seq";
     return MK_ERR_INVALID_ARG;
+  }
+  if (e->desc.weight_format == MK_WEIGHTS_FP8 && batch == 1 && (e->opt.flags & MK_FLAG_OPROJ_PER_GROUP)) {
+    e->msg = "mk_build_schedule: MK_FLAG_OPROJ_PER_GROUP (an ablation) exists for bf16 matrices only";
+    return MK_ERR_UNSUPPORTED;
   }
   int per_cu = 0;
   HIPCHK(e, step_occupancy(e->shape, batch, step_variant(batch, e->opt.flags, rows_per_seq > 1), &per_cu));

@@ -32,9 +32,15 @@ namespace mk {
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int H_, int D_, int HQ_, int HKV_, int E_, int K_, int F_>
+template <int H_, int D_, int HQ_, int HKV_, int E_, int K_, int F_, int W8_ = 0>
 struct Shape {
   static constexpr int H = H_, D = D_, HQ = HQ_, HKV = HKV_, E = E_, K = K_, F = F_;
+  // matrices (QKV, O, router, experts, lm_head): 0 bf16 rows; 1 FP8 rows (OCP E4M3 codes, then the
+  // row's float32 scale in a 16-byte tail; P3 "Limitations and Future Plans" names FP8 kernels as
+  // the next step). kw(k): 16-bit words of weights in a row of k inputs; rw(k): the row's stride.
+  static constexpr int W8 = W8_;
+  static constexpr int kw(int k) { return W8 ? k / 2 : k; }
+  static constexpr int rw(int k) { return W8 ? k / 2 + 8 : k; }
   static constexpr int HPG = HQ / HKV;           // query heads per KV head (GQA group)
   static constexpr int QKVR = (HQ + 2 * HKV) * D;
   static constexpr int AD = HQ * D;              // attention output width
@@ -42,6 +48,8 @@ struct Shape {
 };
 using ShapeSmall = Shape<256, 32, 8, 2, 8, 2, 128>;
 using ShapeFull = Shape<2048, 128, 32, 4, 128, 8, 768>;
+using ShapeSmall8 = Shape<256, 32, 8, 2, 8, 2, 128, 1>;
+using ShapeFull8 = Shape<2048, 128, 32, 4, 128, 8, 768, 1>;
 
 constexpr int SPLIT_MAX = 1024;   // keys one attention task may cover (LDS score buffer)
 constexpr int MERGE_MAX = (SPLIT_MAX + 1) / 2;   // splits one (sequence, KV group) may have
@@ -138,6 +146,23 @@ __device__ __forceinline__ float dot8(u4 w, f4 a0, f4 a1, float acc) {
   acc = __builtin_fmaf(bf_hi(w.z), a1.y, acc);
   acc = __builtin_fmaf(bf_lo(w.w), a1.z, acc);
   acc = __builtin_fmaf(bf_hi(w.w), a1.w, acc);
+  return acc;
+}
+
+// acc += sum_m w[m] * a[m] over the 16 E4M3 codes of w (bytes in element order), in element order;
+// the hardware conversion takes two codes of a 16-bit half at a time
+typedef float f2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot16e4m3(u4 w, f4 a0, f4 a1, f4 a2, f4 a3, float acc) {
+  const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+  const f4 a[4] = {a0, a1, a2, a3};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], true);
+    acc = __builtin_fmaf(lo.x, a[k].x, acc);
+    acc = __builtin_fmaf(lo.y, a[k].y, acc);
+    acc = __builtin_fmaf(hi.x, a[k].z, acc);
+    acc = __builtin_fmaf(hi.y, a[k].w, acc);
+  }
   return acc;
 }
 
@@ -415,17 +440,21 @@ struct Geo {
   static_assert(CPR % LPR == 0, "row length must be a multiple of 8*LPR");
 };
 
-template <int KD, int NP>
+// A block of NP row passes: 16-byte loads of weights (KD = 16-bit words of weights per row) and,
+// for FP8 rows (W8), each row's scale
+template <int KD, int NP, int W8 = 0>
 struct WBuf {
   u4 w[NP][Geo<KD>::CPL];
+  float s[W8 ? NP : 1];
 };
 
 template <int KD, int NP>
 __device__ __forceinline__ int block_rows() { return NP * NWAVE * Geo<KD>::RPP; }
 
-// RowPtr(r) -> const uint16_t* start of row r (only called for r < nrows)
-template <int KD, int NP, class RowPtr>
-__device__ __forceinline__ void load_block(WBuf<KD, NP>& b, int blk, int nrows, RowPtr rowptr) {
+// RowPtr(r) -> const uint16_t* start of row r (only called for r < nrows); an FP8 row's scale is the
+// float right after its KD words of codes
+template <int KD, int NP, int W8 = 0, class RowPtr>
+__device__ __forceinline__ void load_block(WBuf<KD, NP, W8>& b, int blk, int nrows, RowPtr rowptr) {
   using G = Geo<KD>;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
@@ -436,18 +465,22 @@ __device__ __forceinline__ void load_block(WBuf<KD, NP>& b, int blk, int nrows, 
       const uint16_t* src = rowptr(r) + 8 * lir;
 #pragma unroll
       for (int j = 0; j < G::CPL; ++j) b.w[i][j] = ldw(src + 8 * G::LPR * j);
+      if constexpr (W8) b.s[i] = *reinterpret_cast<const float*>(rowptr(r) + KD);
     } else {
 #pragma unroll
       for (int j = 0; j < G::CPL; ++j) b.w[i][j] = u4{0u, 0u, 0u, 0u};
+      if constexpr (W8) b.s[i] = 0.f;
     }
   }
 }
 
 // ActOf(r, t) -> const float* LDS activations (KD floats) for row r, token t
 // Emit(r, t, value) is called on the lane with lir == 0 of each row (value = full dot product)
-template <int KD, int NP, int TB, class ActOf, class Emit>
-__device__ __forceinline__ void compute_block(const WBuf<KD, NP>& b, int blk, int nrows, int ntok,
+// (FP8 rows: 16 inputs per 16-byte load, and each row's sum times its scale)
+template <int KD, int NP, int TB, int W8 = 0, class ActOf, class Emit>
+__device__ __forceinline__ void compute_block(const WBuf<KD, NP, W8>& b, int blk, int nrows, int ntok,
                                               ActOf act_of, Emit emit) {
+  constexpr int EPC = W8 ? 16 : 8;
   using G = Geo<KD>;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
@@ -458,14 +491,16 @@ __device__ __forceinline__ void compute_block(const WBuf<KD, NP>& b, int blk, in
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       if (t < ntok) {
-        const float* a = act_of(rr, t) + 8 * lir;
+        const float* a = act_of(rr, t) + EPC * lir;
         float acc = 0.f;
 #pragma unroll
         for (int j = 0; j < G::CPL; ++j) {
-          const f4* ap = reinterpret_cast<const f4*>(a + 8 * G::LPR * j);
-          acc = dot8(b.w[i][j], ap[0], ap[1], acc);
+          const f4* ap = reinterpret_cast<const f4*>(a + EPC * G::LPR * j);
+          if constexpr (W8) acc = dot16e4m3(b.w[i][j], ap[0], ap[1], ap[2], ap[3], acc);
+          else acc = dot8(b.w[i][j], ap[0], ap[1], acc);
         }
         acc = wsum<G::LPR>(acc);
+        if constexpr (W8) acc *= b.s[i];
         if (lir == 0 && r < nrows) emit(r, t, acc);
       }
     }
@@ -482,10 +517,11 @@ __device__ __forceinline__ void compute_block(const WBuf<KD, NP>& b, int blk, in
 // tokens). A pair is computed whole once its first token is in range (act_of must return readable
 // LDS for every t < TB); the second token's result is emitted only if it is in range. Same per-row
 // order of products.
-template <int KD, int NP, int TB, int TG = 1, class ActOf, class Emit>
-__device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int blk, int nrows, int ntok,
+template <int KD, int NP, int TB, int TG = 1, int W8 = 0, class ActOf, class Emit>
+__device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, W8>& b, int blk, int nrows, int ntok,
                                                      ActOf act_of, Emit emit) {
   using G = Geo<KD>;
+  constexpr int EPC = W8 ? 16 : 8;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
   if constexpr (TG == 2) {
@@ -493,15 +529,35 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int 
 #pragma unroll
     for (int t0 = 0; t0 < TB; t0 += 2) {
       if (t0 < ntok) {
-        const float* pa = act_of(0, t0) + 8 * lir;
-        const float* pb = act_of(0, t0 + 1) + 8 * lir;
+        const float* pa = act_of(0, t0) + EPC * lir;
+        const float* pb = act_of(0, t0 + 1) + EPC * lir;
         float acc0[NP], acc1[NP];
 #pragma unroll
         for (int i = 0; i < NP; ++i) { acc0[i] = 0.f; acc1[i] = 0.f; }
 #pragma unroll
         for (int j = 0; j < G::CPL; ++j) {
-          const f4* qa = reinterpret_cast<const f4*>(pa + 8 * G::LPR * j);
-          const f4* qb = reinterpret_cast<const f4*>(pb + 8 * G::LPR * j);
+          const f4* qa = reinterpret_cast<const f4*>(pa + EPC * G::LPR * j);
+          const f4* qb = reinterpret_cast<const f4*>(pb + EPC * G::LPR * j);
+          if constexpr (W8) {
+            // 16 codes per load: the pair's two tokens share each conversion
+            const f4 a[4] = {qa[0], qa[1], qa[2], qa[3]}, c[4] = {qb[0], qb[1], qb[2], qb[3]};
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+              const u4 w = b.w[i][j];
+              const uint32_t wd[4] = {w.x, w.y, w.z, w.w};
+              float x = acc0[i], y = acc1[i];
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], false), hi = __builtin_amdgcn_cvt_pk_f32_fp8(wd[k], true);
+                x = __builtin_fmaf(lo.x, a[k].x, x); y = __builtin_fmaf(lo.x, c[k].x, y);
+                x = __builtin_fmaf(lo.y, a[k].y, x); y = __builtin_fmaf(lo.y, c[k].y, y);
+                x = __builtin_fmaf(hi.x, a[k].z, x); y = __builtin_fmaf(hi.x, c[k].z, y);
+                x = __builtin_fmaf(hi.y, a[k].w, x); y = __builtin_fmaf(hi.y, c[k].w, y);
+              }
+              acc0[i] = x; acc1[i] = y;
+            }
+            continue;
+          }
           const f4 a0 = qa[0], a1 = qa[1], b0 = qb[0], b1 = qb[1];
 #pragma unroll
           for (int i = 0; i < NP; ++i) {
@@ -523,7 +579,8 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int 
 #pragma unroll
         for (int i = 0; i < NP; ++i) {
           const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
-          const float v0 = wsum<G::LPR>(acc0[i]), v1 = wsum<G::LPR>(acc1[i]);
+          float v0 = wsum<G::LPR>(acc0[i]), v1 = wsum<G::LPR>(acc1[i]);
+          if constexpr (W8) { v0 *= b.s[i]; v1 *= b.s[i]; }
           if (lir == 0 && r < nrows) {
             emit(r, t0, v0);
             if (t0 + 1 < ntok) emit(r, t0 + 1, v1);
@@ -536,21 +593,28 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int 
 #pragma unroll
   for (int t = 0; t < TB; ++t) {
     if (t < ntok) {
-      const float* a = act_of(0, t) + 8 * lir;
+      const float* a = act_of(0, t) + EPC * lir;
       float acc[NP];
 #pragma unroll
       for (int i = 0; i < NP; ++i) acc[i] = 0.f;
 #pragma unroll
       for (int j = 0; j < G::CPL; ++j) {
-        const f4* ap = reinterpret_cast<const f4*>(a + 8 * G::LPR * j);
-        const f4 a0 = ap[0], a1 = ap[1];
+        const f4* ap = reinterpret_cast<const f4*>(a + EPC * G::LPR * j);
+        if constexpr (W8) {
+          const f4 a0 = ap[0], a1 = ap[1], a2 = ap[2], a3 = ap[3];
 #pragma unroll
-        for (int i = 0; i < NP; ++i) acc[i] = dot8(b.w[i][j], a0, a1, acc[i]);
+          for (int i = 0; i < NP; ++i) acc[i] = dot16e4m3(b.w[i][j], a0, a1, a2, a3, acc[i]);
+        } else {
+          const f4 a0 = ap[0], a1 = ap[1];
+#pragma unroll
+          for (int i = 0; i < NP; ++i) acc[i] = dot8(b.w[i][j], a0, a1, acc[i]);
+        }
       }
 #pragma unroll
       for (int i = 0; i < NP; ++i) {
         const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
-        const float v = wsum<G::LPR>(acc[i]);
+        float v = wsum<G::LPR>(acc[i]);
+        if constexpr (W8) v *= b.s[i];
         if (lir == 0 && r < nrows) emit(r, t, v);
       }
     }
@@ -559,18 +623,18 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP>& b, int 
 
 // Stream `nrows` rows; block 0 may already be loaded into A (prefetched before a dependency wait).
 // The activations are shared by all rows (ActOf ignores its row argument).
-template <int KD, int NP, int TB, int TG = 1, class RowPtr, class ActOf, class Emit>
-__device__ __forceinline__ void gemv_stream(WBuf<KD, NP>& A, bool a_loaded, int nrows, int ntok,
+template <int KD, int NP, int TB, int TG = 1, int W8 = 0, class RowPtr, class ActOf, class Emit>
+__device__ __forceinline__ void gemv_stream(WBuf<KD, NP, W8>& A, bool a_loaded, int nrows, int ntok,
                                             RowPtr rowptr, ActOf act_of, Emit emit) {
   const int nblk = (nrows + block_rows<KD, NP>() - 1) / block_rows<KD, NP>();
-  WBuf<KD, NP> B;
-  if (!a_loaded) load_block<KD, NP>(A, 0, nrows, rowptr);
+  WBuf<KD, NP, W8> B;
+  if (!a_loaded) load_block<KD, NP, W8>(A, 0, nrows, rowptr);
   for (int blk = 0; blk < nblk; blk += 2) {
-    if (blk + 1 < nblk) load_block<KD, NP>(B, blk + 1, nrows, rowptr);
-    compute_block_shared<KD, NP, TB, TG>(A, blk, nrows, ntok, act_of, emit);
+    if (blk + 1 < nblk) load_block<KD, NP, W8>(B, blk + 1, nrows, rowptr);
+    compute_block_shared<KD, NP, TB, TG, W8>(A, blk, nrows, ntok, act_of, emit);
     if (blk + 1 < nblk) {
-      if (blk + 2 < nblk) load_block<KD, NP>(A, blk + 2, nrows, rowptr);
-      compute_block_shared<KD, NP, TB, TG>(B, blk + 1, nrows, ntok, act_of, emit);
+      if (blk + 2 < nblk) load_block<KD, NP, W8>(A, blk + 2, nrows, rowptr);
+      compute_block_shared<KD, NP, TB, TG, W8>(B, blk + 1, nrows, ntok, act_of, emit);
     }
   }
 }
@@ -726,20 +790,22 @@ __device__ __forceinline__ bool op_qkv(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? 4 : 8;   // a whole 16-row tile in flight before the wait
+  // a whole 16-row tile in flight before the wait (FP8 rows: 4 passes too, the register budget of the
+  // batch form's token pairs)
+  constexpr int H = S::H, KW = S::kw(H), NP = (Geo<KW>::CPL >= 4 || S::W8) ? 4 : 8;
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
-  auto rowptr = [&](int r) { return Lp.w_qkv + (size_t)(row0 + r) * H; };
-  WBuf<H, NP> A;
+  auto rowptr = [&](int r) { return Lp.w_qkv + (size_t)(row0 + r) * S::rw(H); };
+  WBuf<KW, NP, S::W8> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
+  if (pre) load_block<KW, NP, S::W8>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
   stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
   MARK(0);
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + (size_t)T.layer * MAXB * S::QKVR);
-  gemv_stream<H, NP, TB, (TB > 1 ? 2 : 1)>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::W8>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); });
   MARK(1);
@@ -890,13 +956,13 @@ __device__ __forceinline__ bool op_router(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, E = S::E, NP = (Geo<H>::CPL >= 4) ? 4 : 8;
+  constexpr int H = S::H, E = S::E, KW = S::kw(H), NP = (Geo<KW>::CPL >= 4 || S::W8) ? 4 : 8;
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
-  auto rowptr = [&](int r) { return Lp.w_router + (size_t)(row0 + r) * H; };
-  WBuf<H, NP> A;
+  auto rowptr = [&](int r) { return Lp.w_router + (size_t)(row0 + r) * S::rw(H); };
+  WBuf<KW, NP, S::W8> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
+  if (pre) load_block<KW, NP, S::W8>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
@@ -904,7 +970,7 @@ __device__ __forceinline__ bool op_router(int task) {
   MARK(0);
   const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)T.layer * MAXB * E);
   const float* bias = p.has_bias ? Lp.router_bias : nullptr;
-  gemv_stream<H, NP, TB, (TB > 1 ? 2 : 1)>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::W8>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) {
         const int e = row0 + r;
@@ -933,7 +999,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, F = S::F, K = S::K, NP = (Geo<H>::CPL >= 4) ? 2 : 4;
+  constexpr int H = S::H, F = S::F, K = S::K, KWH = S::kw(H), NP = (Geo<KWH>::CPL >= 4) ? 2 : 4;
   const int l = T.layer;
   const auto& Lp = cst(p.layers)[l];
   // Queue mode (a3 >= 0, P3 "Scheduling and Performance Benchmarks": dynamic work stealing): the
@@ -1012,11 +1078,11 @@ __device__ __forceinline__ bool op_gateup(int task) {
       __syncthreads();
     }
     const int e = slot_expert(u);
-    const uint16_t* wg = Lp.w_gate + (size_t)e * F * H;
-    const uint16_t* wu = Lp.w_up + (size_t)e * F * H;
-    auto rowptr = [&](int r) { return r < nf ? wg + (size_t)(f0 + r) * H : wu + (size_t)(f0 + r - nf) * H; };
-    WBuf<H, NP> A;
-    load_block<H, NP>(A, 0, 2 * nf, rowptr);
+    const uint16_t* wg = Lp.w_gate + (size_t)e * F * S::rw(H);
+    const uint16_t* wu = Lp.w_up + (size_t)e * F * S::rw(H);
+    auto rowptr = [&](int r) { return r < nf ? wg + (size_t)(f0 + r) * S::rw(H) : wu + (size_t)(f0 + r - nf) * S::rw(H); };
+    WBuf<KWH, NP, S::W8> A;
+    load_block<KWH, NP, S::W8>(A, 0, 2 * nf, rowptr);
     __syncthreads();
     const int ntok = ctl.flag;
     MARK(1);
@@ -1024,7 +1090,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
 #pragma unroll
     for (int t = 0; t < TB; ++t) brow[t] = t < ntok ? ctl.toks[t] : 0;
     float* gu = sm + (size_t)TB * H;                 // [TB][2 nf]
-    gemv_stream<H, NP, TB>(A, true, 2 * nf, ntok, rowptr,
+    gemv_stream<KWH, NP, TB, 1, S::W8>(A, true, 2 * nf, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)brow[t] * H; },
         [&](int r, int t, float v) { gu[t * 2 * nf + r] = v; });
     __syncthreads();
@@ -1052,10 +1118,10 @@ __device__ __forceinline__ bool op_gateup(int task) {
     constexpr int NPD = 4;
     const int e = slot_expert(u);
     const int row0 = q * DOWN_ROWS, nr = H - row0 < DOWN_ROWS ? H - row0 : DOWN_ROWS;
-    const uint16_t* wd = Lp.w_down + ((size_t)e * H + row0) * F;
-    auto rowptr = [&](int r) { return wd + (size_t)r * F; };
-    WBuf<F, NPD> A;
-    load_block<F, NPD>(A, 0, nr, rowptr);
+    const uint16_t* wd = Lp.w_down + ((size_t)e * H + row0) * S::rw(F);
+    auto rowptr = [&](int r) { return wd + (size_t)r * S::rw(F); };
+    WBuf<S::kw(F), NPD, S::W8> A;
+    load_block<S::kw(F), NPD, S::W8>(A, 0, nr, rowptr);
     if (tid() == 0) ctl.norm_l = -1;
     __syncthreads();
     const int ntok = ctl.flag;
@@ -1088,7 +1154,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
     __syncthreads();
     MARK(5);
     const __amdgpu_buffer_rsrc_t Y = rsrc(p.y + (size_t)l * MAXB * K * H);
-    gemv_stream<F, NPD, TB>(A, true, nr, ntok, rowptr,
+    gemv_stream<S::kw(F), NPD, TB, 1, S::W8>(A, true, nr, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)t * F; },
         [&](int r, int t, float v) {
           int yo = 0;
@@ -1758,11 +1824,12 @@ __device__ int wait_prefix(CParams& p, Ctl& ctl, int c, int n, uint32_t target, 
 // every group first (measured faster on MI355X, where the four groups' merges land within about a
 // microsecond of each other and each extra round adds a dependent staging round trip).
 template <class S, int NP, int OT, class Emit>
-__device__ __forceinline__ bool oproj_grouped(CParams& p, Ctl& ctl, const WBuf<S::AD, NP>& W, int nrows, int b0, int nt,
+__device__ __forceinline__ bool oproj_grouped(CParams& p, Ctl& ctl, const WBuf<S::kw(S::AD), NP, S::W8>& W, int nrows, int b0, int nt,
                                               int cbase, int target, bool wait, bool per_group, int task, float* a_s,
                                               __amdgpu_buffer_rsrc_t At, Emit emit) {
   constexpr int AD = S::AD, GW = S::HPG * S::D, HKV = S::HKV;
-  using G = Geo<AD>;
+  static_assert(!S::W8, "the per-KV-group O projection (an ablation) exists for bf16 matrices only");
+  using G = Geo<S::kw(AD)>;
   constexpr int NI = (OT * AD + 4 * NT - 1) / (4 * NT);
   static_assert(GW % 4 == 0 && HKV <= 64, "");
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
@@ -1833,14 +1900,14 @@ __device__ __forceinline__ bool op_out(int task) {
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
   constexpr int H = S::H, AD = S::AD, F = S::F, K = S::K;
-  constexpr int NPO = (OUT_MAXR + NWAVE * Geo<AD>::RPP - 1) / (NWAVE * Geo<AD>::RPP);
-  constexpr int NPD = (OUT_MAXR * K + NWAVE * Geo<F>::RPP - 1) / (NWAVE * Geo<F>::RPP);
+  constexpr int NPO = (OUT_MAXR + NWAVE * Geo<S::kw(AD)>::RPP - 1) / (NWAVE * Geo<S::kw(AD)>::RPP);
+  constexpr int NPD = (OUT_MAXR * K + NWAVE * Geo<S::kw(F)>::RPP - 1) / (NWAVE * Geo<S::kw(F)>::RPP);
   const int l = T.layer, row0 = T.a0, nrows = T.a1;
   const auto& Lp = cst(p.layers)[l];
-  auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * AD; };
-  WBuf<AD, NPO> WO;
+  auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * S::rw(AD); };
+  WBuf<S::kw(AD), NPO, S::W8> WO;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<AD, NPO>(WO, 0, nrows, orow);
+  if (pre) load_block<S::kw(AD), NPO, S::W8>(WO, 0, nrows, orow);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;      // routing known
   load_route(p, l);
   const RouteTable& rt = ctl.rt;
@@ -1848,7 +1915,7 @@ __device__ __forceinline__ bool op_out(int task) {
   float* h_s = sm + AD;                                                // [K][F]
   float* o_s = h_s + K * F;                                            // [OUT_MAXR]
   float* y_s = o_s + OUT_MAXR;                                         // [K][OUT_MAXR]
-  if (!pre) load_block<AD, NPO>(WO, 0, nrows, orow);
+  if (!pre) load_block<S::kw(AD), NPO, S::W8>(WO, 0, nrows, orow);
   float* mo_s = y_s + K * OUT_MAXR;                                    // [MAXB][OUT_MAXR] MoE term
   float* xv_s = mo_s + MAXB * OUT_MAXR;                                // [MAXB][OUT_MAXR] x_l rows
   const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
@@ -1865,15 +1932,15 @@ __device__ __forceinline__ bool op_out(int task) {
       int e = 0;
 #pragma unroll
       for (int ii = 0; ii < K; ++ii) if (ii == i) e = sel[ii];
-      return Lp.w_down + ((size_t)e * H + row0 + r) * F;
+      return Lp.w_down + ((size_t)e * H + row0 + r) * S::rw(F);
     };
-    WBuf<F, NPD> WD;
-    load_block<F, NPD>(WD, 0, K * nrows, drow);
+    WBuf<S::kw(F), NPD, S::W8> WD;
+    load_block<S::kw(F), NPD, S::W8>(WD, 0, K * nrows, drow);
     if (b == 0 && !wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every MoE slice
     stage_f4<K * F>(h_s, Hb, 4u * (b * K * F), K * F);
     __syncthreads();
     if (b == 0) MARK(0);
-    compute_block<F, NPD, 1>(WD, 0, K * nrows, 1, [&](int q, int t) { return h_s + (q / nrows) * F; },
+    compute_block<S::kw(F), NPD, 1, S::W8>(WD, 0, K * nrows, 1, [&](int q, int t) { return h_s + (q / nrows) * F; },
                              [&](int q, int t, float v) { y_s[(q / nrows) * OUT_MAXR + q % nrows] = v; });
     __syncthreads();
     if (tid() < nrows) {
@@ -1906,7 +1973,7 @@ __device__ __forceinline__ bool op_out(int task) {
     } else {
       stage_f4<AD>(a_s, At, 4u * (b * AD), AD);
       __syncthreads();
-      compute_block_shared<AD, NPO, 1>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
+      compute_block_shared<S::kw(AD), NPO, 1, 1, S::W8>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
                                        [&](int r, int t, float v) { o_s[r] = v; });
     }
     if (b == 0) MARK(2);
@@ -1941,8 +2008,8 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   const TaskHdr T = read_task(p, task);
   constexpr int H = S::H, AD = S::AD, F = S::F, K = S::K, KF = K * F;
   using LY = OutLds<S>;
-  constexpr int NPO = (OUT_MAXR + NWAVE * Geo<AD>::RPP - 1) / (NWAVE * Geo<AD>::RPP);
-  constexpr int NPD = (OUT_MAXR * K + NWAVE * Geo<F>::RPP - 1) / (NWAVE * Geo<F>::RPP);
+  constexpr int NPO = (OUT_MAXR + NWAVE * Geo<S::kw(AD)>::RPP - 1) / (NWAVE * Geo<S::kw(AD)>::RPP);
+  constexpr int NPD = (OUT_MAXR * K + NWAVE * Geo<S::kw(F)>::RPP - 1) / (NWAVE * Geo<S::kw(F)>::RPP);
   constexpr int HI = (KF + 4 * NT - 1) / (4 * NT);
   const int l = T.layer, row0 = T.a0, nrows = T.a1, B = p.B;
   const auto& Lp = cst(p.layers)[l];
@@ -1972,9 +2039,9 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   if (T.a4) {
     // the down projections were computed by the queued down items: y[b][i][row] for token b's i-th
     // expert; the MoE term sums w_i y_i in ascending expert order, as the form below does
-    WBuf<AD, NPO> WO;
-    auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * AD; };
-    load_block<AD, NPO>(WO, 0, nrows, orow);
+    WBuf<S::kw(AD), NPO, S::W8> WO;
+    auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * S::rw(AD); };
+    load_block<S::kw(AD), NPO, S::W8>(WO, 0, nrows, orow);
     if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every expert task (all items)
     MARK(0);
     if (tx < B * nrows) {
@@ -1997,7 +2064,7 @@ __device__ __forceinline__ bool op_out_batch(int task) {
       stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
       __syncthreads();
       if (b0 == 0) MARK(2);
-      compute_block_shared<AD, NPO, OUT_OT>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
+      compute_block_shared<S::kw(AD), NPO, OUT_OT, 1, S::W8>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
                                             [&](int r, int t, float v) { o_s[t * OUT_MAXR + r] = v; });
       __syncthreads();
       if (tx < nt * nrows) {
@@ -2018,7 +2085,7 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   auto drow_of = [&](int b) {
     return [&, b](int q) {
       const int i = q / nrows, r = q - i * nrows;
-      return Lp.w_down + ((size_t)rt.sel[b][i] * H + row0 + r) * F;
+      return Lp.w_down + ((size_t)rt.sel[b][i] * H + row0 + r) * S::rw(F);
     };
   };
   f4 hv[HI];
@@ -2037,8 +2104,8 @@ __device__ __forceinline__ bool op_out_batch(int task) {
     }
   };
   // token b's MoE term from its W_down rows (in W) and its h (staged at hs)
-  auto moe_token = [&](const WBuf<F, NPD>& W, const float* hs, int b) {
-    compute_block<F, NPD, 1>(W, 0, K * nrows, 1, [&](int q, int t) { return hs + (q / nrows) * F; },
+  auto moe_token = [&](const WBuf<S::kw(F), NPD, S::W8>& W, const float* hs, int b) {
+    compute_block<S::kw(F), NPD, 1, S::W8>(W, 0, K * nrows, 1, [&](int q, int t) { return hs + (q / nrows) * F; },
                              [&](int q, int t, float v) { y_s[(q / nrows) * OUT_MAXR + q % nrows] = v; });
     __syncthreads();
     if (tx < nrows) {
@@ -2049,19 +2116,19 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   };
   float* hA = sm + LY::HA;
   float* hB = sm + LY::HB;
-  WBuf<F, NPD> WA, WB;
-  load_block<F, NPD>(WA, 0, K * nrows, drow_of(0));
+  WBuf<S::kw(F), NPD, S::W8> WA, WB;
+  load_block<S::kw(F), NPD, S::W8>(WA, 0, K * nrows, drow_of(0));
   if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every MoE slice
   h_issue(0);
   h_put(hA);
   MARK(0);
   for (int b = 0; b < B; b += 2) {
     const bool has1 = b + 1 < B;
-    if (has1) { load_block<F, NPD>(WB, 0, K * nrows, drow_of(b + 1)); h_issue(b + 1); }
+    if (has1) { load_block<S::kw(F), NPD, S::W8>(WB, 0, K * nrows, drow_of(b + 1)); h_issue(b + 1); }
     __syncthreads();                       // hA staged; the previous token is done with y_s
     moe_token(WA, hA, b);
     if (has1) h_put(hB);
-    if (b + 2 < B) { load_block<F, NPD>(WA, 0, K * nrows, drow_of(b + 2)); h_issue(b + 2); }
+    if (b + 2 < B) { load_block<S::kw(F), NPD, S::W8>(WA, 0, K * nrows, drow_of(b + 2)); h_issue(b + 2); }
     if (has1) {
       __syncthreads();                     // hB staged; token b is done with y_s and hA
       moe_token(WB, hB, b + 1);
@@ -2071,9 +2138,9 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   if (tx < B * nrows) xv_s[(tx / nrows) * OUT_MAXR + tx % nrows] = xv;
   MARK(1);
   // O projection of OUT_OT tokens per pass over the W_o rows
-  auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * AD; };
-  WBuf<AD, NPO> WO;
-  load_block<AD, NPO>(WO, 0, nrows, orow);
+  auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * S::rw(AD); };
+  WBuf<S::kw(AD), NPO, S::W8> WO;
+  load_block<S::kw(AD), NPO, S::W8>(WO, 0, nrows, orow);
   __syncthreads();                         // the MoE phase is done with the LDS it shares with a_s
   float* a_s = sm + LY::A;
   if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
@@ -2082,7 +2149,7 @@ __device__ __forceinline__ bool op_out_batch(int task) {
     stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
     __syncthreads();
     if (b0 == 0) MARK(2);
-    compute_block_shared<AD, NPO, OUT_OT>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
+    compute_block_shared<S::kw(AD), NPO, OUT_OT, 1, S::W8>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
                                           [&](int r, int t, float v) { o_s[t * OUT_MAXR + r] = v; });
     __syncthreads();
     if (tx < nt * nrows) {
@@ -2109,12 +2176,12 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
   // several tokens: more row passes per block, so that each activation read from LDS serves more rows
-  constexpr int H = S::H, NP = (Geo<H>::CPL >= 4) ? (TB > 1 ? 4 : 2) : 4, RPP = Geo<H>::RPP;
+  constexpr int H = S::H, KW = S::kw(H), NP = (Geo<KW>::CPL >= 4) ? (TB > 1 ? 4 : 2) : 4, RPP = Geo<KW>::RPP;
   const int row0 = T.a0, nrows = T.a1;
-  auto rowptr = [&](int r) { return p.lm_head + (size_t)(row0 + r) * H; };
-  WBuf<H, NP> A;
+  auto rowptr = [&](int r) { return p.lm_head + (size_t)(row0 + r) * S::rw(H); };
+  WBuf<KW, NP, S::W8> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<H, NP>(A, 0, nrows, rowptr);
+  if (pre) load_block<KW, NP, S::W8>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
@@ -2125,7 +2192,7 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   for (int t = 0; t < TB; ++t) { bv[t] = -INFINITY; bi[t] = 0x7fffffff; }
   float* logits = p.logits;
   const int V = p.V;
-  gemv_stream<H, NP, TB>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<KW, NP, TB, 1, S::W8>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) {
         const int row = row0 + r;
@@ -2138,8 +2205,8 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   float* cv = sm + (size_t)TB * H;                                 // [NWAVE * RPP][TB]
   int* ci = reinterpret_cast<int*>(cv + NWAVE * RPP * TB);
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
-  if (lane % Geo<H>::LPR == 0) {
-    const int slot = wave * RPP + lane / Geo<H>::LPR;
+  if (lane % Geo<KW>::LPR == 0) {
+    const int slot = wave * RPP + lane / Geo<KW>::LPR;
 #pragma unroll
     for (int t = 0; t < TB; ++t) { cv[slot * TB + t] = bv[t]; ci[slot * TB + t] = bi[t]; }
   }
@@ -2290,12 +2357,14 @@ static hipError_t occupancy_one(int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)mk_step<S, TB, VAR>, NT, lds);
 }
 
-int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F) {
+// 0 / 1: the small and the full shape with bf16 matrices; 2 / 3: the same with FP8 matrices
+int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F, int w8) {
+  int id = -1;
   if (H == ShapeSmall::H && D == ShapeSmall::D && HQ == ShapeSmall::HQ && HKV == ShapeSmall::HKV &&
-      E == ShapeSmall::E && K == ShapeSmall::K && F == ShapeSmall::F) return 0;
+      E == ShapeSmall::E && K == ShapeSmall::K && F == ShapeSmall::F) id = 0;
   if (H == ShapeFull::H && D == ShapeFull::D && HQ == ShapeFull::HQ && HKV == ShapeFull::HKV &&
-      E == ShapeFull::E && K == ShapeFull::K && F == ShapeFull::F) return 1;
-  return -1;
+      E == ShapeFull::E && K == ShapeFull::K && F == ShapeFull::F) id = 1;
+  return id < 0 ? -1 : id + (w8 ? 2 : 0);
 }
 
 // Kernel instances: batch 1 (VAR 1: the per-KV-group O projection of MK_FLAG_OPROJ_PER_GROUP) and
@@ -2306,6 +2375,15 @@ int step_variant(int batch, int flags, bool kv_first) {
 }
 
 hipError_t launch_step(int shape, int batch, int var, const Params& p, int grid, hipStream_t st, size_t* lds) {
+  if (shape >= 2) {              // FP8 matrices: kernel instances 0 and 2
+    if (var == 1) return hipErrorInvalidValue;
+    if (shape == 2) {
+      if (batch > 1) return var == 2 ? launch_one<ShapeSmall8, MAXB, 2>(p, grid, st, lds) : launch_one<ShapeSmall8, MAXB>(p, grid, st, lds);
+      return launch_one<ShapeSmall8, 1>(p, grid, st, lds);
+    }
+    if (batch > 1) return var == 2 ? launch_one<ShapeFull8, MAXB, 2>(p, grid, st, lds) : launch_one<ShapeFull8, MAXB>(p, grid, st, lds);
+    return launch_one<ShapeFull8, 1>(p, grid, st, lds);
+  }
   if (shape == 0) {
     if (batch > 1) return var == 2 ? launch_one<ShapeSmall, MAXB, 2>(p, grid, st, lds) : launch_one<ShapeSmall, MAXB>(p, grid, st, lds);
     return var == 1 ? launch_one<ShapeSmall, 1, 1>(p, grid, st, lds) : launch_one<ShapeSmall, 1>(p, grid, st, lds);
@@ -2315,6 +2393,15 @@ hipError_t launch_step(int shape, int batch, int var, const Params& p, int grid,
 }
 
 hipError_t step_occupancy(int shape, int batch, int var, int* blocks_per_cu) {
+  if (shape >= 2) {
+    if (var == 1) return hipErrorInvalidValue;
+    if (shape == 2) {
+      if (batch > 1) return var == 2 ? occupancy_one<ShapeSmall8, MAXB, 2>(blocks_per_cu) : occupancy_one<ShapeSmall8, MAXB>(blocks_per_cu);
+      return occupancy_one<ShapeSmall8, 1>(blocks_per_cu);
+    }
+    if (batch > 1) return var == 2 ? occupancy_one<ShapeFull8, MAXB, 2>(blocks_per_cu) : occupancy_one<ShapeFull8, MAXB>(blocks_per_cu);
+    return occupancy_one<ShapeFull8, 1>(blocks_per_cu);
+  }
   if (shape == 0) {
     if (batch > 1) return var == 2 ? occupancy_one<ShapeSmall, MAXB, 2>(blocks_per_cu) : occupancy_one<ShapeSmall, MAXB>(blocks_per_cu);
     return var == 1 ? occupancy_one<ShapeSmall, 1, 1>(blocks_per_cu) : occupancy_one<ShapeSmall, 1>(blocks_per_cu);

@@ -16,12 +16,19 @@ import numpy as np
 BF16 = 2
 
 
+def matrix_bytes(wl, rows, k):
+    """Stored bytes of a matrix of ``rows`` rows of ``k`` inputs: bf16, or FP8 rows of k codes plus a
+    16-byte tail holding the row's scale."""
+    return rows * (k + 16) if getattr(wl, "weights", "bf16") == "fp8" else rows * k * BF16
+
+
 def weight_bytes(wl, union_per_layer):
     """Weight bytes a step must read. ``union_per_layer``: distinct experts per layer (len L)."""
-    H, D = wl.hidden, wl.head_dim
-    dense = (wl.qkv_rows * H + H * wl.n_q_heads * D + wl.n_experts * H + H) * BF16
-    expert = 3 * wl.expert_ffn * H * BF16
-    lm = (wl.vocab * H + H) * BF16 if wl.lm_head else 0
+    H, D, F = wl.hidden, wl.head_dim, wl.expert_ffn
+    dense = (matrix_bytes(wl, wl.qkv_rows, H) + matrix_bytes(wl, H, wl.n_q_heads * D)
+             + matrix_bytes(wl, wl.n_experts, H) + H * BF16)
+    expert = 2 * matrix_bytes(wl, F, H) + matrix_bytes(wl, H, F)
+    lm = matrix_bytes(wl, wl.vocab, H) + H * BF16 if wl.lm_head else 0
     embed = wl.batch * H * BF16
     return int(wl.n_layers * dense + expert * int(np.sum(union_per_layer)) + lm + embed)
 

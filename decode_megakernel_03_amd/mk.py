@@ -15,7 +15,9 @@ LIB_PATH = os.path.join(HERE, "libmk.so")
 
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_OOM = 0, -1, -2, -3, -4
 MK_ERR_NO_SCHEDULE, MK_ERR_SCHEDULE_STALE, MK_ERR_DEVICE = -5, -6, -7
-MK_ABI_VERSION = 1
+MK_ABI_VERSION = 2
+MK_WEIGHTS_BF16 = 0
+MK_WEIGHTS_FP8 = 1
 MK_MAX_BATCH = 8
 MK_FLAG_TRACE = 1
 MK_FLAG_NO_PREFETCH = 2
@@ -43,7 +45,7 @@ class ModelDesc(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "abi_version", "n_layers", "hidden", "n_q_heads", "n_kv_heads", "head_dim", "n_experts", "top_k",
         "expert_ffn", "vocab", "page_size", "num_pages", "max_batch", "max_pages_per_seq", "has_router_bias",
-        "has_lm_head")] + [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float)]
+        "has_lm_head")] + [("rope_theta", ctypes.c_float), ("rms_eps", ctypes.c_float), ("weight_format", ctypes.c_int32)]
 
 
 _PP = ctypes.POINTER(ctypes.c_void_p)
@@ -159,7 +161,8 @@ def model_desc(wl, num_pages, max_pages_per_seq, max_batch=None, has_router_bias
     return ModelDesc(MK_ABI_VERSION, wl.n_layers, wl.hidden, wl.n_q_heads, wl.n_kv_heads, wl.head_dim,
                      wl.n_experts, wl.top_k, wl.expert_ffn, wl.vocab, wl.page_size, int(num_pages),
                      int(max_batch or wl.batch), int(max_pages_per_seq), int(bool(has_router_bias)),
-                     int(bool(wl.lm_head)), float(wl.rope_theta), float(wl.rms_eps))
+                     int(bool(wl.lm_head)), float(wl.rope_theta), float(wl.rms_eps),
+                     MK_WEIGHTS_FP8 if getattr(wl, "weights", "bf16") == "fp8" else MK_WEIGHTS_BF16)
 
 
 # ---------------------------------------------------------------- same-name wrappers

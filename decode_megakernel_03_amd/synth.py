@@ -18,8 +18,11 @@ Workloads (shapes follow the parallel-MoE decoders the method is benchmarked on,
                 block tables and a Zipf(1.1) router bias.
 * ``ragged_uniform`` - the ragged batch without the router bias (uniform-routing control).
 * ``long``    - the same model at batch 1 with 262144 context.
+* ``tiny_fp8``, ``full_fp8``, ``full_b8_fp8`` - ``tiny``, ``full`` and ``full_b8`` with FP8 matrices.
 
-Distributions: weights N(0, 0.02) rounded to bf16; norm gains 1.0 (or U(0.5, 1.5) when asked,
+Distributions: weights N(0, 0.02) rounded to bf16 (FP8 workloads: each matrix row of those then
+stored as OCP E4M3 codes with a float32 absmax scale, max |w| / 448, codes rounded to nearest even);
+norm gains 1.0 (or U(0.5, 1.5) when asked,
 so that gain mistakes cannot hide); K/V N(0, 1) rounded to bf16; tokens uniform in [0, V).
 Every tensor has its own generator seeded from (seed, tensor index).
 """
@@ -53,6 +56,7 @@ class Workload:
     zipf_s: float = 0.0     # router bias exponent (0 = no bias)
     lm_head: bool = True    # False: the step ends at the residual stream (single-layer test)
     embed_std: float = 0.02 # the single-layer test feeds N(0, 1) rows as the layer input
+    weights: str = "bf16"   # matrix storage: "bf16" or "fp8" (E4M3 codes + float32 row scale)
 
     @property
     def qkv_rows(self):
@@ -73,6 +77,11 @@ WORKLOADS = {
     # the uniform-routing control of the ragged batch (same contexts and pages, no router bias)
     "ragged_uniform": Workload("ragged_uniform", **_FULL, batch=8, context=0, steps=1024, ragged=(1024, 32768)),
     "long": Workload("long", **_FULL, batch=1, context=262144, steps=256),
+    "tiny_fp8": Workload("tiny_fp8", n_layers=2, hidden=256, n_q_heads=8, n_kv_heads=2, head_dim=32,
+                         n_experts=8, top_k=2, expert_ffn=128, vocab=1024, batch=1, context=64, steps=16,
+                         weights="fp8"),
+    "full_fp8": Workload("full_fp8", **_FULL, batch=1, context=8192, steps=1024, weights="fp8"),
+    "full_b8_fp8": Workload("full_b8_fp8", **_FULL, batch=8, context=8192, steps=1024, weights="fp8"),
 }
 
 
@@ -120,8 +129,26 @@ def zipf_router_bias(wl, seed=4):
     return out
 
 
+FP8_MAX = 448.0          # largest finite OCP E4M3 value
+
+
+def quantize_rows_fp8(t):
+    """A bf16 matrix [..., K] as packed FP8 rows uint8 [..., K + 16]: scale s = max |row| / 448 (1 for a
+    zero row), codes E4M3(row / s) rounded to nearest even, then the float32 scale and 12 zero bytes."""
+    x = t.float()
+    amax = x.abs().amax(dim=-1, keepdim=True)
+    scale = torch.where(amax > 0, amax / FP8_MAX, torch.ones_like(amax))
+    codes = (x / scale).clamp(-FP8_MAX, FP8_MAX).to(torch.float8_e4m3fn).view(torch.uint8)
+    del x
+    tail = torch.zeros(codes.shape[:-1] + (16,), dtype=torch.uint8, device=codes.device)
+    tail[..., :4] = scale.to(torch.float32).contiguous().view(torch.uint8)
+    return torch.cat([codes, tail], dim=-1).contiguous()
+
+
 def make_weights(wl, seed=0, device="cpu", gains="ones", router_bias=None):
-    """All model weights as torch tensors on ``device`` (bf16 unless noted)."""
+    """All model weights as torch tensors on ``device`` (bf16 unless noted; with FP8 weights every
+    matrix is uint8 packed rows, ``quantize_rows_fp8``)."""
+    mat = quantize_rows_fp8 if wl.weights == "fp8" else (lambda t: t)
     H, V = wl.hidden, wl.vocab
     w = {}
     i = 0
@@ -138,18 +165,18 @@ def make_weights(wl, seed=0, device="cpu", gains="ones", router_bias=None):
 
     w["embed"] = normal_bf16((V, H), wl.embed_std, seed, nxt(), device)
     lm_idx = nxt()
-    w["lm_head"] = normal_bf16((V, H), 0.02, seed, lm_idx, device) if wl.lm_head else None
+    w["lm_head"] = mat(normal_bf16((V, H), 0.02, seed, lm_idx, device)) if wl.lm_head else None
     w["final_norm"] = gain(nxt())
     layers = []
     for l in range(wl.n_layers):
         lw = {
             "attn_norm": gain(nxt()),
-            "w_qkv": normal_bf16((wl.qkv_rows, H), 0.02, seed, nxt(), device),
-            "w_o": normal_bf16((H, wl.n_q_heads * wl.head_dim), 0.02, seed, nxt(), device),
-            "w_router": normal_bf16((wl.n_experts, H), 0.02, seed, nxt(), device),
-            "w_gate": normal_bf16((wl.n_experts, wl.expert_ffn, H), 0.02, seed, nxt(), device),
-            "w_up": normal_bf16((wl.n_experts, wl.expert_ffn, H), 0.02, seed, nxt(), device),
-            "w_down": normal_bf16((wl.n_experts, H, wl.expert_ffn), 0.02, seed, nxt(), device),
+            "w_qkv": mat(normal_bf16((wl.qkv_rows, H), 0.02, seed, nxt(), device)),
+            "w_o": mat(normal_bf16((H, wl.n_q_heads * wl.head_dim), 0.02, seed, nxt(), device)),
+            "w_router": mat(normal_bf16((wl.n_experts, H), 0.02, seed, nxt(), device)),
+            "w_gate": mat(normal_bf16((wl.n_experts, wl.expert_ffn, H), 0.02, seed, nxt(), device)),
+            "w_up": mat(normal_bf16((wl.n_experts, wl.expert_ffn, H), 0.02, seed, nxt(), device)),
+            "w_down": mat(normal_bf16((wl.n_experts, H, wl.expert_ffn), 0.02, seed, nxt(), device)),
             "router_bias": None,
         }
         if router_bias is not None:
@@ -262,3 +289,11 @@ def first_tokens(wl, seed=2):
 def to_u16(t):
     """bf16 torch tensor (any device) -> numpy uint16 bit patterns on the host."""
     return t.detach().to("cpu").contiguous().view(torch.int16).numpy().view(np.uint16)
+
+
+def to_host(t):
+    """A stored tensor on the host as the oracle reads it: bf16 -> uint16 patterns; packed FP8 rows
+    (uint8) -> uint8."""
+    if t.dtype == torch.uint8:
+        return t.detach().to("cpu").contiguous().numpy()
+    return to_u16(t)

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 1
+#define MK_ABI_VERSION 2
 #define MK_MAX_BATCH 8 /* batch sizes up to 8 (P2 body; P3 "Limitations and Future Plans") */
 
 typedef struct mk_engine mk_engine;
@@ -74,7 +74,18 @@ typedef struct {
   int32_t has_lm_head;       /* 0: the step ends at the residual stream (no logits) */
   float rope_theta;          /* RoPE base (rotate-half, full head_dim) */
   float rms_eps;             /* RMSNorm epsilon */
+  int32_t weight_format;     /* MK_WEIGHTS_BF16 or MK_WEIGHTS_FP8: the storage of every matrix */
 } mk_model_desc;
+
+/* Matrix storage (mk_model_desc.weight_format). The matrices are w_qkv, w_o, w_router, w_gate, w_up,
+ * w_down and lm_head; embed, the norm gains and the KV cache are bf16 in both.
+ *   MK_WEIGHTS_BF16  a matrix [R, C] is R rows of C bf16.
+ *   MK_WEIGHTS_FP8   FP8 weights (P3 "Limitations and Future Plans": FP8/FP4 megakernels are the
+ *                    pages' next step): a matrix [R, C] is R rows of C + 16 bytes - the row's C OCP
+ *                    E4M3 codes, then its float32 scale and 12 zero bytes (each row 16-byte aligned);
+ *                    weight = E4M3 value of the code * row scale. C must be a multiple of 16. */
+#define MK_WEIGHTS_BF16 0
+#define MK_WEIGHTS_FP8 1
 
 /* Weight and KV-cache pointers (all device pointers; host arrays of per-layer pointers of length
  * n_layers). Layouts, row-major:

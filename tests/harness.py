@@ -40,20 +40,20 @@ class LazyWeights:
             lw = self.w["layers"][l]
             rb = lw["router_bias"]
             return oracle.decode.LayerWeights(
-                attn_norm=synth.to_u16(lw["attn_norm"]), w_qkv=synth.to_u16(lw["w_qkv"]),
-                w_o=synth.to_u16(lw["w_o"]), w_router=synth.to_u16(lw["w_router"]),
+                attn_norm=synth.to_u16(lw["attn_norm"]), w_qkv=synth.to_host(lw["w_qkv"]),
+                w_o=synth.to_host(lw["w_o"]), w_router=synth.to_host(lw["w_router"]),
                 router_bias=None if rb is None else rb.detach().cpu().numpy().astype(np.float32),
                 w_gate=None, w_up=None, w_down=None)
         return self._get(("layer", l), mk)
 
     def expert(self, l, e):
         lw = self.w["layers"][l]
-        return self._get(("expert", l, int(e)), lambda: (synth.to_u16(lw["w_gate"][int(e)]),
-                                                          synth.to_u16(lw["w_up"][int(e)]),
-                                                          synth.to_u16(lw["w_down"][int(e)])))
+        return self._get(("expert", l, int(e)), lambda: (synth.to_host(lw["w_gate"][int(e)]),
+                                                          synth.to_host(lw["w_up"][int(e)]),
+                                                          synth.to_host(lw["w_down"][int(e)])))
 
     def lm_head_rows(self, start, stop):
-        return self._get(("lm", start, stop), lambda: synth.to_u16(self.w["lm_head"][start:stop]))
+        return self._get(("lm", start, stop), lambda: synth.to_host(self.w["lm_head"][start:stop]))
 
     def drop_layers(self):
         """Forget cached per-layer tensors (bounded host memory for long models)."""
@@ -66,13 +66,13 @@ def dense_weights(w):
     for lw in w["layers"]:
         rb = lw["router_bias"]
         layers.append(oracle.decode.LayerWeights(
-            attn_norm=synth.to_u16(lw["attn_norm"]), w_qkv=synth.to_u16(lw["w_qkv"]),
-            w_o=synth.to_u16(lw["w_o"]), w_router=synth.to_u16(lw["w_router"]),
+            attn_norm=synth.to_u16(lw["attn_norm"]), w_qkv=synth.to_host(lw["w_qkv"]),
+            w_o=synth.to_host(lw["w_o"]), w_router=synth.to_host(lw["w_router"]),
             router_bias=None if rb is None else rb.detach().cpu().numpy().astype(np.float32),
-            w_gate=synth.to_u16(lw["w_gate"]), w_up=synth.to_u16(lw["w_up"]),
-            w_down=synth.to_u16(lw["w_down"])))
+            w_gate=synth.to_host(lw["w_gate"]), w_up=synth.to_host(lw["w_up"]),
+            w_down=synth.to_host(lw["w_down"])))
     return oracle.DenseWeights(embed=synth.to_u16(w["embed"]),
-                               lm_head=None if w["lm_head"] is None else synth.to_u16(w["lm_head"]),
+                               lm_head=None if w["lm_head"] is None else synth.to_host(w["lm_head"]),
                                final_norm=synth.to_u16(w["final_norm"]), layers=layers)
 
 

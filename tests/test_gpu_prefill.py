@@ -1,7 +1,7 @@
 """Prefill through the decode kernel on the GPU, against the oracle.
 
-* Small model: a 19-position prompt (chunks of 8, 8 and 3 rows of one sequence) written by
-  ``mk_prefill`` from position 0 and after 21 cached positions, against ``oracle.prefill``: routing
+* Small model (bf16 and FP8 matrices): a 19-position prompt (chunks of 8, 8 and 3 rows of one
+  sequence) written by ``mk_prefill`` from position 0 and after 21 cached positions, against ``oracle.prefill``: routing
   (near-tie replay as everywhere), the last position's logits, the K/V of every prompt position; then
   four greedy decode steps from the prompt's K/V equal the oracle's greedy decode.
 * Small model, a mixed batch: two decode rows and a five-row chunk of a third sequence's prompt in
@@ -89,12 +89,13 @@ def prompt_rows_check(dims, kd, vd, kv_ref, bt_row, positions, max_frac):
 
 
 @pytest.mark.parametrize("start", [0, 21], ids=["from-position-0", "after-21-cached"])
-def test_tiny_prefill_then_decode(start):
+@pytest.mark.parametrize("name", ["tiny", "tiny_fp8"])
+def test_tiny_prefill_then_decode(name, start):
     import oracle
     from decode_megakernel_03_amd import mk
     n = 19
-    say(f"test_tiny_prefill_then_decode: prompt of {n} at position {start}, chunks of 8")
-    wl = synth.workload("tiny", steps=n + 8)
+    say(f"test_tiny_prefill_then_decode: {name}, prompt of {n} at position {start}, chunks of 8")
+    wl = synth.workload(name, steps=n + 8)
     s = harness.tiny_setup(wl, ctx=[start], gains="uniform")
     dims = harness.dims_of(wl)
     dw = harness.dense_weights(s["w"])

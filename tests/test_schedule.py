@@ -35,6 +35,8 @@ CASES = [
     ("full", [262145], 512),
     ("full", [8193], 64),
     ("layer", [8193], 512),
+    ("full_fp8", [8193], 512),
+    ("full_b8_fp8", [8193] * 8, 512),
 ]
 
 
