@@ -336,9 +336,12 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       const int n_items = slots * (slices + down_items);
       const int tickets = std::min(n_items, W);
       const int nq = std::min(CTR_SUB, tickets);
+      // the tickets follow the attention merges in each worker's queue (same level, after them):
+      // a merge then runs as soon as its group's splits are in, instead of after that worker has
+      // drained the queue (measured on MI355X: +0.6 % at batch 8)
       for (int t = 0; t < tickets; ++t) {
         Proto pr;
-        set(pr.t, OP_GATEUP, l, lv1);
+        set(pr.t, OP_GATEUP, l, lvm);
         pr.t.w[D_A0] = t % nq; pr.t.w[D_A1] = nq; pr.t.w[D_A2] = slices; pr.t.w[D_A3] = c_queue[l];
         pr.t.w[D_A4] = nf; pr.t.w[D_A5] = down_items;
         pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
@@ -346,7 +349,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
         pr.t.w[D_SIG] = c_h[l];
         pr.bytes = ((int64_t)slots * slices * 2 * nf * m.H * m.wb + (int64_t)slots * m.H * m.F * m.wb) / tickets;
         pr.prio = 1;
-        levels[lv1].push_back(pr);
+        levels[lvm].push_back(pr);
         n_gu++;
       }
     } else {
