@@ -35,6 +35,10 @@ EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_build_schedu
             "mk_server_get_error", "mk_server_destroy"]
 
 
+# bound at import: during interpreter shutdown the module globals (sys among them) may already be None
+_finalizing = sys.is_finalizing
+
+
 class MkError(RuntimeError):
     def __init__(self, status, msg):
         super().__init__(f"libmk status {status}: {msg}")
@@ -394,7 +398,7 @@ class Engine:
     def __del__(self):
         # at interpreter shutdown the HIP runtime (and a profiler attached to it) may already be torn
         # down: leave the engine to process exit then, and never call into the library
-        if sys.is_finalizing():
+        if _finalizing():
             return
         try:
             self.close()
