@@ -229,6 +229,10 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   const bool steal = B > 1 && !(flags & MK_FLAG_STATIC_EXPERTS);
   // down items per union slot (row blocks of W_down[e], DOWN_ROWS rows each) in queue mode
   const int down_items = steal ? (int)ceil_div(m.H, down_rows()) : 0;
+  // O-projection row blocks of OPROJ_ROWS rows, queued after the down items (bf16 matrices: the FP8
+  // kernel instances are compiled without them); the output rows then only add up
+  constexpr int OPROJ_ROWS = 16;
+  const int oproj_items = steal && desc.weight_format == MK_WEIGHTS_BF16 ? (int)ceil_div(m.H, OPROJ_ROWS) : 0;
   std::vector<int> c_queue(L, -1);
   for (int l = 0; l < L; ++l) {
     for (int g = 0; g < m.HKV; ++g) c_qkv[l][g] = C.alloc();
@@ -280,6 +284,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   if (W - n_merge >= (int)ceil_div(m.H, OUTR)) n_out_l = std::min(n_out_l, W - n_merge);
   auto split_key = [&](int l, int b, int g, int s) { return ((l * B + b) * m.HKV + g) * 65536 + s; };
   std::vector<std::vector<Proto>> levels(LPL * L + 1);
+  int n_out_layer = 0;                      // output-row tasks per layer when they are not n_out_l
   int n_attn = 0;
   for (int l = 0; l < L; ++l) {
     const int lv0 = LPL * l, lv1 = LPL * l + 1, lvm = LPL * l + 2, lv2 = LPL * l + 3;
@@ -343,7 +348,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       // the down projection of every union expert joins the queue as row blocks (after every gate/up
       // item), so that W_down is read once per expert and streams while other slots' gate/up items
       // are still running; the output rows then only add the experts' results
-      const int n_items = slots * (slices + down_items);
+      const int n_items = slots * (slices + down_items) + oproj_items;
       const int tickets = std::min(n_items, W);
       const int nq = std::min(CTR_SUB, tickets);
       // the tickets follow the attention merges in each worker's queue (same level, after them):
@@ -353,7 +358,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
         Proto pr;
         set(pr.t, OP_GATEUP, l, lvm);
         pr.t.w[D_A0] = t % nq; pr.t.w[D_A1] = nq; pr.t.w[D_A2] = slices; pr.t.w[D_A3] = c_queue[l];
-        pr.t.w[D_A4] = nf; pr.t.w[D_A5] = down_items;
+        pr.t.w[D_A4] = nf; pr.t.w[D_A5] = down_items | (oproj_items << 16);
         pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
         pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
         pr.t.w[D_SIG] = c_h[l];
@@ -394,8 +399,26 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.pin = split_key(l, b, g, (int)((int64_t)q * nsplit[b] / nslice));
           levels[lvm].push_back(pr);
         }
-    // level 3: output rows (O-proj + expert down-proj + residual)
+    // level 3: output rows (O-proj + expert down-proj + residual); with queued O-projection items,
+    // x_l+1 = (x_l + o) + MoE term in blocks of up to 32 rows (one thread per row and token)
     int n_out = 0;
+    if (oproj_items > 0)
+      for (auto [a, e] : chunks(m.H, std::max(1, std::min(32, NT / B)))) {
+        Proto pr;
+        set(pr.t, OP_OUT, l, lv2);
+        pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
+        pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV * nslice;   // (every merge: already in)
+        pr.t.w[D_A4] = 4 | 1;
+        pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
+        pr.t.w[D_W1] = c_h[l]; pr.t.w[D_T1] = n_gu;
+        pr.t.w[D_SIG] = c_x[l + 1];
+        pr.bytes = (int64_t)(e - a) * B * (m.K + 2) * 4;
+        pr.prio = 0;
+        levels[lv2].push_back(pr);
+        n_out++;
+      }
+    if (oproj_items > 0) n_out_layer = n_out;
+    if (oproj_items == 0)
     for (auto [a, e] : even(m.H, n_out_l)) {
       Proto pr;
       set(pr.t, OP_OUT, l, lv2);
@@ -419,7 +442,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     }
     (void)n_out;
   }
-  const int n_out_per_layer = n_out_l;
+  const int n_out_per_layer = n_out_layer > 0 ? n_out_layer : n_out_l;
   for (auto& lvl : levels)
     for (auto& pr : lvl)
       if ((pr.t.w[D_OP] == OP_QKV || pr.t.w[D_OP] == OP_ROUTER || pr.t.w[D_OP] == OP_GATEUP) && pr.t.w[D_W0] >= 0 &&
@@ -628,7 +651,12 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
       switch (t.w[D_OP]) {
         case OP_QKV: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) qkv[r]++; break;
         case OP_ROUTER: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) rt[r]++; break;
-        case OP_OUT: for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) out[r]++; break;
+        case OP_OUT:
+          if ((t.w[D_A4] & ~5) || ((t.w[D_A4] & 4) && (!(t.w[D_A4] & 1) || P.B * t.w[D_A1] > NT))) {
+            *why = fmt("output task %d: mode %d with %d rows", t.w[D_ID], t.w[D_A4], t.w[D_A1]); return MK_ERR_INVALID_ARG;
+          }
+          for (int r = t.w[D_A0]; r < t.w[D_A0] + t.w[D_A1]; ++r) out[r]++;
+          break;
         case OP_GATEUP: {
           if (t.w[D_A3] >= 0) { queue_tasks.push_back(&t); break; }
           auto& v = gu[t.w[D_A0]];
@@ -653,14 +681,27 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
       // every FFN row of every union slot once; every sub-queue has a task that drains it
       if (!gu.empty()) { *why = fmt("layer %d mixes static and queued expert slices", l); return MK_ERR_INVALID_ARG; }
       const Task& t0 = *queue_tasks[0];
-      const int qc = t0.w[D_A3], nq = t0.w[D_A1], slices = t0.w[D_A2], nfs = t0.w[D_A4], qd = t0.w[D_A5];
+      const int qc = t0.w[D_A3], nq = t0.w[D_A1], slices = t0.w[D_A2], nfs = t0.w[D_A4], qd = t0.w[D_A5] & 0xffff;
+      const int n_oi = t0.w[D_A5] >> 16;
+      // O-projection items: bf16 matrices only; they wait on counter qc - 1, which must be the
+      // attention counter the layer's output rows name; every output row then adds o
+      if (n_oi < 0 || n_oi > m.H || (n_oi > 0 && P.desc.weight_format != MK_WEIGHTS_BF16)) {
+        *why = fmt("layer %d: %d O-projection items", l, n_oi); return MK_ERR_INVALID_ARG;
+      }
+      for (const Task* tp : by_layer[l])
+        if (tp->w[D_OP] == OP_OUT && (((tp->w[D_A4] & 4) != 0) != (n_oi > 0) ||
+            (n_oi > 0 && (tp->w[D_A2] != qc - 1 || tp->w[D_A3] != P.B * m.HKV * std::max(1, m.HPG * m.D / 256))))) {
+          // (the kernel's O-projection items wait for B * HKV * max(1, HPG * D / 256) merges on qc - 1)
+          *why = fmt("layer %d: output task %d and the O-projection items disagree", l, tp->w[D_ID]);
+          return MK_ERR_INVALID_ARG;
+        }
       // down items: none, or row blocks that cover every W_down row once
       if (qd < 0 || (qd > 0 && (qd * down_rows() < m.H || (qd - 1) * down_rows() >= m.H))) {
         *why = fmt("layer %d: %d down items of %d rows for %d rows", l, qd, down_rows(), m.H);
         return MK_ERR_INVALID_ARG;
       }
       for (const Task* tp : by_layer[l])
-        if (tp->w[D_OP] == OP_OUT && tp->w[D_A4] != (qd > 0 ? 1 : 0)) {
+        if (tp->w[D_OP] == OP_OUT && (tp->w[D_A4] & 1) != (qd > 0 ? 1 : 0)) {
           *why = fmt("layer %d: output task %d and the expert queue disagree on the down items", l, tp->w[D_ID]);
           return MK_ERR_INVALID_ARG;
         }
@@ -670,7 +711,7 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
       }
       std::vector<int> drained(nq, 0);
       for (const Task* t : queue_tasks) {
-        if (t->w[D_A3] != qc || t->w[D_A1] != nq || t->w[D_A2] != slices || t->w[D_A4] != nfs || t->w[D_A5] != qd ||
+        if (t->w[D_A3] != qc || t->w[D_A1] != nq || t->w[D_A2] != slices || t->w[D_A4] != nfs || t->w[D_A5] != t0.w[D_A5] ||
             t->w[D_A0] < 0 || t->w[D_A0] >= nq) {
           *why = fmt("layer %d: expert task %d disagrees on the queue", l, t->w[D_ID]);
           return MK_ERR_INVALID_ARG;
@@ -682,7 +723,7 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
     } else if ((int)gu.size() != std::min(m.E, m.K * P.B)) { *why = fmt("layer %d: %zu expert slots", l, gu.size()); return MK_ERR_INVALID_ARG; }
     if (queue_tasks.empty())
       for (const Task* tp : by_layer[l])
-        if (tp->w[D_OP] == OP_OUT && tp->w[D_A4] != 0) {
+        if (tp->w[D_OP] == OP_OUT && tp->w[D_A4] != 0) {   // (no queue: no queued items to add)
           *why = fmt("layer %d: output task %d expects queued down items, the layer has none", l, tp->w[D_ID]);
           return MK_ERR_INVALID_ARG;
         }
@@ -785,6 +826,7 @@ struct mk_engine {
   double* d_inv_freq = nullptr;
   float *d_x = nullptr, *d_qkv = nullptr, *d_rlog = nullptr, *d_h = nullptr, *d_attn = nullptr, *d_apart = nullptr;
   float* d_y = nullptr;
+  float* d_o = nullptr;
   uint32_t* d_slot = nullptr;
   RouteTable* d_route = nullptr;
   unsigned long long* d_amax = nullptr;
@@ -833,7 +875,7 @@ hipError_t dalloc(T** p, size_t n) {
 }
 
 void free_all(mk_engine* e) {
-  void* ps[] = {e->d_layers, e->d_inv_freq, e->d_x, e->d_qkv, e->d_rlog, e->d_h, e->d_y, e->d_slot, e->d_attn, e->d_apart,
+  void* ps[] = {e->d_layers, e->d_inv_freq, e->d_x, e->d_qkv, e->d_rlog, e->d_h, e->d_y, e->d_o, e->d_slot, e->d_attn, e->d_apart,
                 e->d_route, e->d_amax, e->d_ctr, e->d_err, e->d_tasks, e->d_qoff, e->pf_in, e->pf_bt, e->pf_topk,
                 e->pf_logits};
   for (void* p : ps) if (p) (void)hipFree(p);
@@ -899,6 +941,7 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weight_ptrs* w, mk_engin
             dalloc(&e->d_rlog, (size_t)L * MAXB * m.E) == hipSuccess &&
             dalloc(&e->d_h, (size_t)L * MAXB * m.K * m.F) == hipSuccess &&
             dalloc(&e->d_y, (size_t)L * MAXB * m.K * m.H) == hipSuccess &&
+            dalloc(&e->d_o, (size_t)L * MAXB * m.H) == hipSuccess &&
             dalloc(&e->d_slot, (size_t)L * MAX_SLOTS * CTR_STRIDE) == hipSuccess &&
             dalloc(&e->d_attn, (size_t)L * MAXB * m.AD) == hipSuccess &&
             dalloc(&e->d_route, (size_t)L) == hipSuccess && dalloc(&e->d_amax, MAXB) == hipSuccess &&
@@ -1000,7 +1043,7 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
   p.layers = e->d_layers; p.embed = (const uint16_t*)e->w.embed; p.lm_head = (const uint16_t*)e->w.lm_head;
   p.final_norm = (const uint16_t*)e->w.final_norm; p.inv_freq = e->d_inv_freq;
   p.x = e->d_x; p.qkv = e->d_qkv; p.rlog = e->d_rlog; p.route = e->d_route; p.h = e->d_h; p.apart = e->d_apart;
-  p.y = e->d_y; p.slot_ctr = e->d_slot;
+  p.y = e->d_y; p.o = e->d_o; p.slot_ctr = e->d_slot;
   p.attn = e->d_attn; p.amax = e->d_amax; p.ctr = e->d_ctr; p.err = e->d_err;
   p.tasks = e->d_tasks; p.qoff = e->d_qoff;
   p.tokens = tokens; p.positions = positions; p.block_tables = block_tables; p.seq_lens = seq_lens;

@@ -40,13 +40,16 @@ enum Op {
   OP_ROUTER = 2,  // a0 row0, a1 nrows, a2 router tiles: logits; the last tile routes (top-k)
   OP_GATEUP = 3,  // static: a0 union slot, a1 f0, a2 nf, a3 -1: h = SiLU(W_gate n) * (W_up n) on rows f0..
                   // queue: a0 own sub-queue, a1 sub-queues, a2 slices per slot, a3 queue counter,
-                  // a4 rows per slice, a5 down items per slot (0: none): the layer's work queue holds
-                  // every (slot, slice) gate/up item, then every (slot, row block) down item
+                  // a4 rows per slice, a5 down items per slot (0: none) | O-projection items << 16:
+                  // the layer's work queue holds every (slot, slice) gate/up item, then every (slot,
+                  // row block) down item, then the O-projection row blocks (they wait on the
+                  // attention counter, which is the queue counter - 1)
   OP_ATTN = 4,    // a0 b, a1 g, a2 k0, a3 k1 (-1 = to seq_len, the split holding the new token),
                   // a4 first partial of (b, g) in the layer, a5 split | nsplit << 16
   OP_OUT = 5,     // a0 row0, a1 nrows, a2 attention counter (KV group g's merges on sub-counters
-                  // g*CTR_SUB/HKV ..), a3 its target, a4 1 = the down projections come from the queued
-                  // down items (y): x_{l+1} = x_l + W_o attn + sum_i w_i W_down[e_i] h_i
+                  // g*CTR_SUB/HKV ..), a3 its target, a4 bits: 1 = the down projections come from the
+                  // queued down items (y): x_{l+1} = x_l + W_o attn + sum_i w_i W_down[e_i] h_i;
+                  // 4 = the O projection comes from the queued O-projection items (o) as well
   OP_LMHEAD = 6,  // a0 row0, a1 nrows: logits + running argmax
   OP_MERGE = 7,   // a0 b, a1 g, a2 slice, a3 slices, a4 first partial, a5 nsplit: attention output
   OP_COUNT
@@ -99,6 +102,7 @@ struct Params {
   RouteTable* route;         // [L]
   float* h;                  // [L][MAXB][K][F]
   float* y;                  // [L][MAXB][K][H] down projection of token b's i-th expert (queued down items)
+  float* o;                  // [L][MAXB][H] O projection of token b's attention (queued O-projection items)
   uint32_t* slot_ctr;        // [L][64] lines of CTR_STRIDE: gate/up items done per union slot (zeroed per step)
   float* apart;              // [L][parts_per_layer][HPG * (D + 2)]
   float* attn;               // [L][MAXB][HQ * D]

@@ -783,6 +783,25 @@ __device__ __forceinline__ bool publish_kv(CParams& p, int l, int row0, int nrow
   return __syncthreads_or(bad != 0) == 0;
 }
 
+// dst[0, n) = the n floats at byte offset off of R (n a multiple of 4, at most NMAX): every load of
+// the thread is issued before its first LDS write, so the staging costs one round trip
+template <int NMAX>
+__device__ __forceinline__ void stage_f4(float* dst, __amdgpu_buffer_rsrc_t R, uint32_t off, int n) {
+  constexpr int NI = (NMAX + 4 * NT - 1) / (4 * NT);
+  const int tx = tid();
+  f4 v[NI];
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int i = (u * NT + tx) * 4;
+    v[u] = i < n ? ldc4(R, off + 4u * i) : f4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int u = 0; u < NI; ++u) {
+    const int i = (u * NT + tx) * 4;
+    if (i < n) *reinterpret_cast<f4*>(dst + i) = v[u];
+  }
+}
+
 // QKV rows (any contiguous range inside one KV group's q, k or v rows).
 template <class S, int TB, int VAR>
 __device__ __forceinline__ bool op_qkv(int task) {
@@ -1009,7 +1028,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
   // steals from the next ones. The first draw is issued before the dependency waits.
   const bool dyn = T.a3 >= 0;
   const int nq = dyn ? T.a1 : 1;
-  const int qd = dyn ? T.a5 : 0;          // down items per union slot (queue mode)
+  const int qd = dyn ? (T.a5 & 0xffff) : 0;   // down items per union slot (queue mode)
+  const int n_oi = dyn ? (T.a5 >> 16) : 0;    // O-projection items after them (queue mode)
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   int sq = dyn ? T.a0 : 0;
   // a draw: lane 0 of wave 0 takes the next item of sub-queue q; lanes < nq read every sub-queue's
@@ -1166,6 +1186,35 @@ __device__ __forceinline__ bool op_gateup(int task) {
     __syncthreads();      // toks / trank / the staged h are rewritten by the next item
     return true;
   };
+  // O-projection item j (after the down items): rows j*orows .. of W_o for every token,
+  // o[l][b][row] = W_o[row] . attn[b], once every attention merge of the layer is in (the attention
+  // counter is the one allocated right before the queue's); the output rows add it afterwards. Drawn
+  // by the workers that run out of expert work first, so it overlaps the last expert items. One row
+  // pass per block (the register budget of this op); OQT tokens' attention staged at a time.
+  auto run_oproj = [&](int j, int orows) -> bool {
+    constexpr int AD = S::AD, OQT = 4;
+    constexpr int NSL = S::HPG * S::D / 256 > 1 ? S::HPG * S::D / 256 : 1;   // merges per (token, group)
+    const int r0 = j * orows, nr = H - r0 < orows ? H - r0 : orows;
+    if (nr <= 0) return true;            // (no rows left for this block)
+    auto orow = [&](int r) { return Lp.w_o + (size_t)(r0 + r) * S::rw(AD); };
+    WBuf<S::kw(AD), 1, S::W8> A;
+    load_block<S::kw(AD), 1, S::W8>(A, 0, nr, orow);
+    if (tid() == 0) ctl.norm_l = -1;     // the staged normed input is overwritten below
+    if (!wait_ge(p, ctl, T.a3 - 1, (uint32_t)(p.B * S::HKV * NSL), T.id)) return false;
+    const __amdgpu_buffer_rsrc_t At = rsrc(p.attn + (size_t)l * MAXB * AD);
+    const __amdgpu_buffer_rsrc_t Ob = rsrc(p.o + (size_t)l * MAXB * H);
+    for (int b0 = 0; b0 < p.B; b0 += OQT) {
+      const int nt = p.B - b0 < OQT ? p.B - b0 : OQT;
+      __syncthreads();                   // every wave is done with the previous tokens' attention
+      stage_f4<OQT * AD>(sm, At, 4u * (b0 * AD), nt * AD);
+      __syncthreads();
+      gemv_stream<S::kw(AD), 1, OQT, 1, S::W8>(A, b0 == 0, nr, nt, orow,
+          [&](int r, int t) { return sm + (size_t)t * AD; },
+          [&](int r, int t, float v) { stc(Ob, 4u * ((b0 + t) * H + r0 + r), v); });
+    }
+    __syncthreads();                     // the staging area is free for the next item
+    return true;
+  };
   if (TB == 1 || !dyn) {           // one token: static slices only (the queue is never scheduled)
     if (T.a0 < nu) run_item(T.a0, T.a1, T.a2);
   } else if constexpr (TB > 1) {
@@ -1175,8 +1224,10 @@ __device__ __forceinline__ bool op_gateup(int task) {
     const int slices = T.a2, nfs = T.a4;
     const int grain = (nu * slices >= 4 * p.n_workers && 2 * nfs <= 32) ? 2 : 1;
     const int slices_c = (slices + grain - 1) / grain, rows = grain * nfs;
-    const int n_gu = nu * slices_c;                 // gate/up items first, then the down items
-    const int n_items = n_gu + nu * qd;
+    const int n_gu = nu * slices_c;                 // gate/up items first, then the down items,
+    const int n_dn = n_gu + nu * qd;                // then the O-projection items
+    const int n_items = n_dn + n_oi;
+    const int orows = n_oi > 0 ? (H + n_oi - 1) / n_oi : 0;
     // hand the draw to the workgroup, with the sub-queue that had the most items left in the
     // snapshot (-1: none had any)
     auto publish = [&]() {
@@ -1210,9 +1261,17 @@ __device__ __forceinline__ bool op_gateup(int task) {
       if (i < n_gu) {
         const int u = i / slices_c, j = i - u * slices_c, f0 = j * rows;
         run_item(u, f0, F - f0 < rows ? F - f0 : rows);
-      } else {
-        const int i2 = i - n_gu, u = i2 / qd;
+      } else if (i >= n_gu + n_oi) {
+        const int i2 = i - n_gu - n_oi, u = i2 / qd;
         if (!run_down(u, i2 - u * qd, slices_c)) return false;
+      } else {
+        // (compiled for bf16 matrices only: in the FP8 instances the extra GEMV path costs 15 more
+        // spilled registers, and the schedule gives them no such items)
+        if constexpr (!S::W8) {
+          if (!run_oproj(i - n_gu, orows)) return false;
+        } else {
+          return false;                  // (the host's validator refuses such a schedule)
+        }
       }
       publish();
     }
@@ -1752,24 +1811,6 @@ __device__ __forceinline__ bool op_merge(int task) {
   return true;
 }
 
-// dst[0, n) = the n floats at byte offset off of R (n a multiple of 4, at most NMAX): every load of
-// the thread is issued before its first LDS write, so the staging costs one round trip
-template <int NMAX>
-__device__ __forceinline__ void stage_f4(float* dst, __amdgpu_buffer_rsrc_t R, uint32_t off, int n) {
-  constexpr int NI = (NMAX + 4 * NT - 1) / (4 * NT);
-  const int tx = tid();
-  f4 v[NI];
-#pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int i = (u * NT + tx) * 4;
-    v[u] = i < n ? ldc4(R, off + 4u * i) : f4{0.f, 0.f, 0.f, 0.f};
-  }
-#pragma unroll
-  for (int u = 0; u < NI; ++u) {
-    const int i = (u * NT + tx) * 4;
-    if (i < n) *reinterpret_cast<f4*>(dst + i) = v[u];
-  }
-}
 
 // Counter c's signals come in n groups, group g adding to sub-counters g * (CTR_SUB / n) .. (the
 // attention merges of KV group g). Wait until the groups' counts reach `target` each for a longer
@@ -2035,6 +2076,32 @@ __device__ __forceinline__ bool op_out_batch(int task) {
     } else {
       xv = ldc(rsrc(p.x + ((size_t)l * MAXB + b) * H), 4u * row);
     }
+  }
+  if (T.a4 & 4) {
+    // the O projection and the down projections were computed by queued items (o[l][b][row] and
+    // y[b][i][row]): x_l+1 = (x_l + o) + MoE term, the MoE term in ascending expert order - the same
+    // sums in the same order as the form below
+    if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every expert task (all items)
+    MARK(0);
+    if (tx < B * nrows) {
+      const int b = tx / nrows, r = tx % nrows, row = row0 + r;
+      const __amdgpu_buffer_rsrc_t Yr = rsrc(p.y + (size_t)l * MAXB * K * H);
+      const __amdgpu_buffer_rsrc_t Ob = rsrc(p.o + (size_t)l * MAXB * H);
+      float yv[K];
+#pragma unroll
+      for (int i = 0; i < K; ++i) yv[i] = ldc(Yr, 4u * ((b * K + i) * H + row));
+      const float ov = ldc(Ob, 4u * (b * H + row));
+      float moe = 0.f;
+#pragma unroll
+      for (int i = 0; i < K; ++i) moe = moe + rt.w[b][i] * yv[i];
+      const float xn = (xv + ov) + moe;
+      stc(Xn, 4u * (b * H + row), xn);
+      if (p.hidden_out && l == p.L - 1) p.hidden_out[(size_t)b * H + row] = xn;
+    }
+    MARK(3);
+    drain_t(p);
+    signal(p, ctl, T.sig, false);
+    return true;
   }
   if (T.a4) {
     // the down projections were computed by the queued down items: y[b][i][row] for token b's i-th
