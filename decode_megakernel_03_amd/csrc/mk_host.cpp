@@ -232,7 +232,9 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // O-projection row blocks of OPROJ_ROWS rows, queued after the down items (bf16 matrices: the FP8
   // kernel instances are compiled without them); the output rows then only add up
   constexpr int OPROJ_ROWS = 16;
-  const int oproj_items = steal && desc.weight_format == MK_WEIGHTS_BF16 ? (int)ceil_div(m.H, OPROJ_ROWS) : 0;
+  // (each row block once per group of 4 tokens: the kernel's items stage 4 tokens' attention)
+  const int oproj_items = steal && desc.weight_format == MK_WEIGHTS_BF16
+                        ? (int)ceil_div(m.H, OPROJ_ROWS) * (int)ceil_div(B, 4) : 0;
   std::vector<int> c_queue(L, -1);
   for (int l = 0; l < L; ++l) {
     for (int g = 0; g < m.HKV; ++g) c_qkv[l][g] = C.alloc();
@@ -685,7 +687,8 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
       const int n_oi = t0.w[D_A5] >> 16;
       // O-projection items: bf16 matrices only; they wait on counter qc - 1, which must be the
       // attention counter the layer's output rows name; every output row then adds o
-      if (n_oi < 0 || n_oi > m.H || (n_oi > 0 && P.desc.weight_format != MK_WEIGHTS_BF16)) {
+      if (n_oi < 0 || n_oi > m.H * (int)ceil_div(P.B, 4) || n_oi % (int)ceil_div(P.B, 4) != 0 ||
+          (n_oi > 0 && P.desc.weight_format != MK_WEIGHTS_BF16)) {
         *why = fmt("layer %d: %d O-projection items", l, n_oi); return MK_ERR_INVALID_ARG;
       }
       for (const Task* tp : by_layer[l])

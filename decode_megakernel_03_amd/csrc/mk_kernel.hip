@@ -1186,16 +1186,19 @@ __device__ __forceinline__ bool op_gateup(int task) {
     __syncthreads();      // toks / trank / the staged h are rewritten by the next item
     return true;
   };
-  // O-projection item j (after the down items): rows j*orows .. of W_o for every token,
-  // o[l][b][row] = W_o[row] . attn[b], once every attention merge of the layer is in (the attention
-  // counter is the one allocated right before the queue's); the output rows add it afterwards. Drawn
-  // by the workers that run out of expert work first, so it overlaps the last expert items. One row
-  // pass per block (the register budget of this op); OQT tokens' attention staged at a time.
-  auto run_oproj = [&](int j, int orows) -> bool {
-    constexpr int AD = S::AD, OQT = 4;
+  // O-projection item j (between the gate/up and the down items): rows of W_o for a group of OQT
+  // tokens, o[l][b][row] = W_o[row] . attn[b], once every attention merge of the layer is in (the
+  // attention counter is the one allocated right before the queue's); the output rows add it
+  // afterwards. Item j is row block j / ntg for token group j % ntg (ntg groups of OQT tokens), so an
+  // item stages its tokens' attention once. One row pass per block (the register budget of this op).
+  constexpr int OQT = 4;
+  auto run_oproj = [&](int j, int orows, int ntg) -> bool {
+    constexpr int AD = S::AD;
     constexpr int NSL = S::HPG * S::D / 256 > 1 ? S::HPG * S::D / 256 : 1;   // merges per (token, group)
-    const int r0 = j * orows, nr = H - r0 < orows ? H - r0 : orows;
-    if (nr <= 0) return true;            // (no rows left for this block)
+    const int rb = j / ntg, b0 = (j - rb * ntg) * OQT;
+    const int r0 = rb * orows, nr = H - r0 < orows ? H - r0 : orows;
+    const int nt = p.B - b0 < OQT ? p.B - b0 : OQT;
+    if (nr <= 0 || nt <= 0) return true;     // (no rows or tokens left for this item)
     auto orow = [&](int r) { return Lp.w_o + (size_t)(r0 + r) * S::rw(AD); };
     WBuf<S::kw(AD), 1, S::W8> A;
     load_block<S::kw(AD), 1, S::W8>(A, 0, nr, orow);
@@ -1203,15 +1206,12 @@ __device__ __forceinline__ bool op_gateup(int task) {
     if (!wait_ge(p, ctl, T.a3 - 1, (uint32_t)(p.B * S::HKV * NSL), T.id)) return false;
     const __amdgpu_buffer_rsrc_t At = rsrc(p.attn + (size_t)l * MAXB * AD);
     const __amdgpu_buffer_rsrc_t Ob = rsrc(p.o + (size_t)l * MAXB * H);
-    for (int b0 = 0; b0 < p.B; b0 += OQT) {
-      const int nt = p.B - b0 < OQT ? p.B - b0 : OQT;
-      __syncthreads();                   // every wave is done with the previous tokens' attention
-      stage_f4<OQT * AD>(sm, At, 4u * (b0 * AD), nt * AD);
-      __syncthreads();
-      gemv_stream<S::kw(AD), 1, OQT, 1, S::W8>(A, b0 == 0, nr, nt, orow,
-          [&](int r, int t) { return sm + (size_t)t * AD; },
-          [&](int r, int t, float v) { stc(Ob, 4u * ((b0 + t) * H + r0 + r), v); });
-    }
+    __syncthreads();                     // every wave is done with the previous item's LDS
+    stage_f4<OQT * AD>(sm, At, 4u * (b0 * AD), nt * AD);
+    __syncthreads();
+    gemv_stream<S::kw(AD), 1, OQT, 1, S::W8>(A, true, nr, nt, orow,
+        [&](int r, int t) { return sm + (size_t)t * AD; },
+        [&](int r, int t, float v) { stc(Ob, 4u * ((b0 + t) * H + r0 + r), v); });
     __syncthreads();                     // the staging area is free for the next item
     return true;
   };
@@ -1227,7 +1227,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
     const int n_gu = nu * slices_c;                 // gate/up items first, then the down items,
     const int n_dn = n_gu + nu * qd;                // then the O-projection items
     const int n_items = n_dn + n_oi;
-    const int orows = n_oi > 0 ? (H + n_oi - 1) / n_oi : 0;
+    const int ntg = (p.B + OQT - 1) / OQT;          // token groups of the O-projection items
+    const int orows = n_oi > 0 ? (H + n_oi / ntg - 1) / (n_oi / ntg) : 0;
     // hand the draw to the workgroup, with the sub-queue that had the most items left in the
     // snapshot (-1: none had any)
     auto publish = [&]() {
@@ -1268,7 +1269,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
         // (compiled for bf16 matrices only: in the FP8 instances the extra GEMV path costs 15 more
         // spilled registers, and the schedule gives them no such items)
         if constexpr (!S::W8) {
-          if (!run_oproj(i - n_gu, orows)) return false;
+          if (!run_oproj(i - n_gu, orows, ntg)) return false;
         } else {
           return false;                  // (the host's validator refuses such a schedule)
         }
