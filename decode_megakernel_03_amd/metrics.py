@@ -17,9 +17,15 @@ BF16 = 2
 
 
 def matrix_bytes(wl, rows, k):
-    """Stored bytes of a matrix of ``rows`` rows of ``k`` inputs: bf16, or FP8 rows of k codes plus a
-    16-byte tail holding the row's scale."""
-    return rows * (k + 16) if getattr(wl, "weights", "bf16") == "fp8" else rows * k * BF16
+    """Stored bytes of a matrix of ``rows`` rows of ``k`` inputs: bf16; FP8 rows of k codes plus a
+    16-byte tail holding the row's scale; or MXFP4 rows of k/2 code bytes and k/32 scale bytes padded
+    to 16 bytes."""
+    fmt = getattr(wl, "weights", "bf16")
+    if fmt == "fp8":
+        return rows * (k + 16)
+    if fmt == "mxfp4":
+        return rows * ((k // 2 + k // 32 + 15) // 16 * 16)
+    return rows * k * BF16
 
 
 def weight_bytes(wl, union_per_layer):

@@ -19,9 +19,12 @@ Workloads (shapes follow the parallel-MoE decoders the method is benchmarked on,
 * ``ragged_uniform`` - the ragged batch without the router bias (uniform-routing control).
 * ``long``    - the same model at batch 1 with 262144 context.
 * ``tiny_fp8``, ``full_fp8``, ``full_b8_fp8`` - ``tiny``, ``full`` and ``full_b8`` with FP8 matrices.
+* ``tiny_mxfp4``, ``full_mxfp4``, ``full_b8_mxfp4`` - the same with MXFP4 matrices.
 
 Distributions: weights N(0, 0.02) rounded to bf16 (FP8 workloads: each matrix row of those then
-stored as OCP E4M3 codes with a float32 absmax scale, max |w| / 448, codes rounded to nearest even);
+stored as OCP E4M3 codes with a float32 absmax scale, max |w| / 448, codes rounded to nearest even;
+MXFP4 workloads: each block of 32 inputs of a row stored as E2M1 codes with a shared power-of-two
+scale 2^(floor(log2 max |w|) - 2), codes rounded to nearest even and clamped to +-6);
 norm gains 1.0 (or U(0.5, 1.5) when asked,
 so that gain mistakes cannot hide); K/V N(0, 1) rounded to bf16; tokens uniform in [0, V).
 Every tensor has its own generator seeded from (seed, tensor index).
@@ -56,7 +59,8 @@ class Workload:
     zipf_s: float = 0.0     # router bias exponent (0 = no bias)
     lm_head: bool = True    # False: the step ends at the residual stream (single-layer test)
     embed_std: float = 0.02 # the single-layer test feeds N(0, 1) rows as the layer input
-    weights: str = "bf16"   # matrix storage: "bf16" or "fp8" (E4M3 codes + float32 row scale)
+    weights: str = "bf16"   # matrix storage: "bf16", "fp8" (E4M3 codes + float32 row scale) or
+                            # "mxfp4" (E2M1 codes, an E8M0 scale per block of 32)
 
     @property
     def qkv_rows(self):
@@ -82,6 +86,11 @@ WORKLOADS = {
                          weights="fp8"),
     "full_fp8": Workload("full_fp8", **_FULL, batch=1, context=8192, steps=1024, weights="fp8"),
     "full_b8_fp8": Workload("full_b8_fp8", **_FULL, batch=8, context=8192, steps=1024, weights="fp8"),
+    "tiny_mxfp4": Workload("tiny_mxfp4", n_layers=2, hidden=256, n_q_heads=8, n_kv_heads=2, head_dim=32,
+                           n_experts=8, top_k=2, expert_ffn=128, vocab=1024, batch=1, context=64, steps=16,
+                           weights="mxfp4"),
+    "full_mxfp4": Workload("full_mxfp4", **_FULL, batch=1, context=8192, steps=1024, weights="mxfp4"),
+    "full_b8_mxfp4": Workload("full_b8_mxfp4", **_FULL, batch=8, context=8192, steps=1024, weights="mxfp4"),
 }
 
 
@@ -145,12 +154,51 @@ def quantize_rows_fp8(t):
     return torch.cat([codes, tail], dim=-1).contiguous()
 
 
+# E2M1 magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 are codes 0..7; a magnitude rounds to the code that counts
+# the midpoints below it, a tie going to the even code (the midpoints 0.25, 1.25, 2.5 and 5 round
+# down, 0.75, 1.75 and 3.5 up)
+_E2M1_MID_DOWN = (0.25, 1.25, 2.5, 5.0)
+_E2M1_MID_UP = (0.75, 1.75, 3.5)
+
+
+def mxfp4_row_bytes(k):
+    """Bytes of one packed MXFP4 row of ``k`` inputs: k/2 code bytes and k/32 scale bytes, padded to 16."""
+    return (k // 2 + k // 32 + 15) // 16 * 16
+
+
+def quantize_rows_mxfp4(t):
+    """A bf16 matrix [..., K] (K a multiple of 32) as packed MXFP4 rows uint8 [..., mxfp4_row_bytes(K)]:
+    per block of 32 inputs the E8M0 scale byte 127 + floor(log2 max |w|) - 2 (127 for a zero block),
+    codes E2M1(w / scale) rounded to nearest even and clamped to 6; two codes per byte, the even
+    element in the low nibble; then the K/32 scale bytes and zero bytes."""
+    k = t.shape[-1]
+    assert k % 32 == 0
+    x = t.float().reshape(t.shape[:-1] + (k // 32, 32))
+    amax = x.abs().amax(dim=-1, keepdim=True)
+    e = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2, torch.zeros_like(amax)).clamp(-127, 127)
+    a = (x * torch.exp2(-e)).reshape(t.shape)
+    del x
+    mag = a.abs()
+    code = torch.zeros(mag.shape, dtype=torch.uint8, device=t.device)
+    for m in _E2M1_MID_DOWN:
+        code += (mag > m).to(torch.uint8)
+    for m in _E2M1_MID_UP:
+        code += (mag >= m).to(torch.uint8)
+    code |= (a < 0).to(torch.uint8) << 3
+    del a, mag
+    out = torch.zeros(t.shape[:-1] + (mxfp4_row_bytes(k),), dtype=torch.uint8, device=t.device)
+    out[..., : k // 2] = code[..., 0::2] | (code[..., 1::2] << 4)
+    out[..., k // 2: k // 2 + k // 32] = (e[..., 0] + 127).to(torch.uint8)
+    return out
+
+
 def make_weights(wl, seed=0, device="cpu", gains="ones", router_bias=None):
-    """All model weights as torch tensors on ``device`` (bf16 unless noted; with FP8 weights every
-    matrix is uint8 packed rows, ``quantize_rows_fp8``)."""
-    mat = quantize_rows_fp8 if wl.weights == "fp8" else (lambda t: t)
+    """All model weights as torch tensors on ``device`` (bf16 unless noted; with FP8 or MXFP4 weights
+    every matrix is uint8 packed rows, ``quantize_rows_fp8`` / ``quantize_rows_mxfp4``). The dict's
+    "format" names the matrix storage (the workload's ``weights``)."""
+    mat = {"fp8": quantize_rows_fp8, "mxfp4": quantize_rows_mxfp4}.get(wl.weights, lambda t: t)
     H, V = wl.hidden, wl.vocab
-    w = {}
+    w = {"format": wl.weights}
     i = 0
 
     def nxt():
@@ -292,8 +340,8 @@ def to_u16(t):
 
 
 def to_host(t):
-    """A stored tensor on the host as the oracle reads it: bf16 -> uint16 patterns; packed FP8 rows
-    (uint8) -> uint8."""
+    """A stored tensor on the host as the oracle reads it: bf16 -> uint16 patterns; packed FP8 or
+    MXFP4 rows (uint8) -> uint8."""
     if t.dtype == torch.uint8:
         return t.detach().to("cpu").contiguous().numpy()
     return to_u16(t)

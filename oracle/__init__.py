@@ -31,6 +31,9 @@ prefill equal to a decode step; planted mistakes (mask off by one, no mask, RoPE
 keys, unweighted experts) each fail a pin. FP8 weights: E4M3 decoder vs torch's float8_e4m3fn for all
 256 codes and at the format's landmarks; packed-row layout; an FP8 model with power-of-two row scales
 equals its bf16 twin bit for bit (decode step and prefill), and misapplied scales break the equality.
+MXFP4 weights: E2M1 decoder vs the element table of the OCP MX specification, E8M0 decoder vs torch's
+float8_e8m0fnu for all 256 codes, packed-row layout byte by byte, and an MXFP4 model equal to its
+bf16 twin bit for bit (swapped nibbles, shifted or dropped block scales break the equality).
 
 Parity unpinned: nothing the pages print can be recomputed here (the pages give no model
 dimensions and no worked example), so no whole-step value is pinned to the pages themselves.
@@ -53,4 +56,4 @@ from .decode import (  # noqa: F401
     expert_ffn,
     silu,
 )
-from . import prefill  # noqa: F401  (oracle.prefill.prefill, oracle.prefill.PrefillResult)
+from . import mxfp4, prefill  # noqa: F401  (oracle.prefill.prefill, oracle.mxfp4.Mxfp4Rows)

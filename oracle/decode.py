@@ -16,7 +16,8 @@ What the pages fix
 * Weights and KV cache are BF16 (P1 "Decode is a bandwidth game"; P2 body). The FP8 variant
   (P3 "Limitations and Future Plans" names FP8/FP4 kernels as the next step) stores the matrices
   as E4M3 codes with a float32 scale per row (``oracle.fp8``); the step is the same over the
-  dequantized weights.
+  dequantized weights; likewise the MXFP4 variant (``oracle.mxfp4``: E2M1 codes in blocks of 32
+  sharing a power-of-two scale).
 
 Readings (the pages are silent; each is the plainest choice the rest supports)
 -------------------------------------------------------------------------------
@@ -56,6 +57,7 @@ import numpy as np
 
 from .bf16 import bf16_to_f32, f32_to_bf16, f64_to_bf16
 from .fp8 import dequant_rows
+from .mxfp4 import Mxfp4Rows, dequant_rows as mx_dequant_rows
 
 
 @dataclass(frozen=True)
@@ -137,8 +139,11 @@ class StepResult:
 # ----------------------------------------------------------------------------------------------
 
 def _dec(a, dtype):
-    """A stored tensor as values in ``dtype``: bf16 bit patterns (uint16), or a matrix of packed FP8
-    rows (uint8: E4M3 codes and a float32 scale per row, ``oracle.fp8``) dequantized."""
+    """A stored tensor as values in ``dtype``: bf16 bit patterns (uint16), a matrix of packed MXFP4
+    rows (``oracle.mxfp4.Mxfp4Rows``) or of packed FP8 rows (other uint8: E4M3 codes and a float32
+    scale per row, ``oracle.fp8``), dequantized."""
+    if isinstance(a, Mxfp4Rows):
+        return mx_dequant_rows(a, dtype)
     if a.dtype == np.uint8:
         return dequant_rows(a, dtype)
     return bf16_to_f32(a).astype(dtype, copy=False)

@@ -19,6 +19,15 @@ def dims_of(wl):
                        rope_theta=wl.rope_theta, rms_eps=wl.rms_eps)
 
 
+def host_matrix(w, t):
+    """A generated matrix as the oracle reads it: ``synth.to_host``, and packed MXFP4 rows wrapped as
+    ``oracle.mxfp4.Mxfp4Rows`` (their K follows from the row length)."""
+    a = synth.to_host(t)
+    if w.get("format") == "mxfp4":
+        return oracle.mxfp4.Mxfp4Rows(a, oracle.mxfp4.k_of_row_bytes(a.shape[-1]))
+    return a
+
+
 class LazyWeights:
     """Oracle weight provider over generated torch tensors; copies to host on first touch."""
 
@@ -40,20 +49,20 @@ class LazyWeights:
             lw = self.w["layers"][l]
             rb = lw["router_bias"]
             return oracle.decode.LayerWeights(
-                attn_norm=synth.to_u16(lw["attn_norm"]), w_qkv=synth.to_host(lw["w_qkv"]),
-                w_o=synth.to_host(lw["w_o"]), w_router=synth.to_host(lw["w_router"]),
+                attn_norm=synth.to_u16(lw["attn_norm"]), w_qkv=host_matrix(self.w, lw["w_qkv"]),
+                w_o=host_matrix(self.w, lw["w_o"]), w_router=host_matrix(self.w, lw["w_router"]),
                 router_bias=None if rb is None else rb.detach().cpu().numpy().astype(np.float32),
                 w_gate=None, w_up=None, w_down=None)
         return self._get(("layer", l), mk)
 
     def expert(self, l, e):
         lw = self.w["layers"][l]
-        return self._get(("expert", l, int(e)), lambda: (synth.to_host(lw["w_gate"][int(e)]),
-                                                          synth.to_host(lw["w_up"][int(e)]),
-                                                          synth.to_host(lw["w_down"][int(e)])))
+        return self._get(("expert", l, int(e)), lambda: (host_matrix(self.w, lw["w_gate"][int(e)]),
+                                                          host_matrix(self.w, lw["w_up"][int(e)]),
+                                                          host_matrix(self.w, lw["w_down"][int(e)])))
 
     def lm_head_rows(self, start, stop):
-        return self._get(("lm", start, stop), lambda: synth.to_host(self.w["lm_head"][start:stop]))
+        return self._get(("lm", start, stop), lambda: host_matrix(self.w, self.w["lm_head"][start:stop]))
 
     def drop_layers(self):
         """Forget cached per-layer tensors (bounded host memory for long models)."""
@@ -66,13 +75,13 @@ def dense_weights(w):
     for lw in w["layers"]:
         rb = lw["router_bias"]
         layers.append(oracle.decode.LayerWeights(
-            attn_norm=synth.to_u16(lw["attn_norm"]), w_qkv=synth.to_host(lw["w_qkv"]),
-            w_o=synth.to_host(lw["w_o"]), w_router=synth.to_host(lw["w_router"]),
+            attn_norm=synth.to_u16(lw["attn_norm"]), w_qkv=host_matrix(w, lw["w_qkv"]),
+            w_o=host_matrix(w, lw["w_o"]), w_router=host_matrix(w, lw["w_router"]),
             router_bias=None if rb is None else rb.detach().cpu().numpy().astype(np.float32),
-            w_gate=synth.to_host(lw["w_gate"]), w_up=synth.to_host(lw["w_up"]),
-            w_down=synth.to_host(lw["w_down"])))
+            w_gate=host_matrix(w, lw["w_gate"]), w_up=host_matrix(w, lw["w_up"]),
+            w_down=host_matrix(w, lw["w_down"])))
     return oracle.DenseWeights(embed=synth.to_u16(w["embed"]),
-                               lm_head=None if w["lm_head"] is None else synth.to_host(w["lm_head"]),
+                               lm_head=None if w["lm_head"] is None else host_matrix(w, w["lm_head"]),
                                final_norm=synth.to_u16(w["final_norm"]), layers=layers)
 
 
