@@ -22,6 +22,9 @@ import numpy as np
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+_WEIGHTS_DESC = {"bf16": "bf16 weights and KV",
+                 "fp8": "FP8 E4M3 matrices with per-row scales, bf16 embedding, norms and KV",
+                 "mxfp4": "MXFP4 matrices (E2M1, E8M0 scale per 32), bf16 embedding, norms and KV"}
 PEAK_HBM = 8.0e12          # MI355X HBM3E, bytes/s
 METRIC = "decode tok/s on 1 GPU at bs1 & bs8, 8K ctx; % of HBM speed-of-light"
 
@@ -150,7 +153,7 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{wl.name}: {wl.n_layers}-layer parallel-MoE decoder, batch {B}, context {int(ctx.max())}"
-                               f"{' (ragged)' if wl.ragged else ''}, bf16 weights and KV, fp32 arithmetic",
+                               f"{' (ragged)' if wl.ragged else ''}, {_WEIGHTS_DESC[wl.weights]}, fp32 arithmetic",
                    "batch": B, "context": int(ctx.max()), "layers": wl.n_layers, "hidden": wl.hidden,
                    "experts": f"{wl.n_experts} top-{wl.top_k}", "vocab": wl.vocab,
                    "workers": info.n_workers, "tasks_per_step": info.n_tasks},

@@ -59,7 +59,7 @@ void put(char* buf, size_t n, const std::string& s) {
 
 struct Dims {
   int L, H, HQ, HKV, D, E, K, F, V, HPG, QKVR, AD, PART;
-  int wb;      // bytes per matrix weight (2 bf16, 1 FP8), for the schedule's cost model
+  int wb32;    // bytes per 32 matrix weights (64 bf16, 32 FP8, 17 MXFP4), for the schedule's cost model
   bool lm;
 };
 
@@ -69,7 +69,7 @@ Dims dims_of(const mk_model_desc& d) {
   m.E = d.n_experts; m.K = d.top_k; m.F = d.expert_ffn; m.V = d.vocab;
   m.HPG = m.HQ / m.HKV; m.QKVR = (m.HQ + 2 * m.HKV) * m.D; m.AD = m.HQ * m.D;
   m.PART = m.HPG * (m.D + 2);
-  m.wb = d.weight_format == MK_WEIGHTS_FP8 ? 1 : 2;
+  m.wb32 = d.weight_format == MK_WEIGHTS_MXFP4 ? 17 : d.weight_format == MK_WEIGHTS_FP8 ? 32 : 64;
   m.lm = d.has_lm_head != 0;
   return m;
 }
@@ -82,11 +82,11 @@ mk_status check_desc(const mk_model_desc* d, std::string* why) {
   }
   if (d->max_batch < 1 || d->max_batch > MK_MAX_BATCH) { *why = fmt("max_batch %d outside 1..%d", d->max_batch, MK_MAX_BATCH); return MK_ERR_INVALID_ARG; }
   if (d->page_size != PAGE) { *why = fmt("page_size %d unsupported (16)", d->page_size); return MK_ERR_UNSUPPORTED; }
-  if (d->weight_format != MK_WEIGHTS_BF16 && d->weight_format != MK_WEIGHTS_FP8) {
+  if (d->weight_format != MK_WEIGHTS_BF16 && d->weight_format != MK_WEIGHTS_FP8 && d->weight_format != MK_WEIGHTS_MXFP4) {
     *why = fmt("weight_format %d unknown", d->weight_format); return MK_ERR_INVALID_ARG;
   }
   if (shape_id(d->hidden, d->head_dim, d->n_q_heads, d->n_kv_heads, d->n_experts, d->top_k, d->expert_ffn,
-               d->weight_format == MK_WEIGHTS_FP8) < 0) {
+               d->weight_format) < 0) {
     *why = "no compiled kernel for this (hidden, head_dim, heads, experts, top_k, expert_ffn)"; return MK_ERR_UNSUPPORTED;
   }
   if (!(d->rms_eps > 0.f) || !(d->rope_theta > 0.f)) { *why = "rms_eps and rope_theta must be > 0"; return MK_ERR_INVALID_ARG; }
@@ -229,8 +229,9 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   const bool steal = B > 1 && !(flags & MK_FLAG_STATIC_EXPERTS);
   // down items per union slot (row blocks of W_down[e], DOWN_ROWS rows each) in queue mode
   const int down_items = steal ? (int)ceil_div(m.H, down_rows()) : 0;
-  // O-projection row blocks of OPROJ_ROWS rows, queued after the down items (bf16 matrices: the FP8
-  // kernel instances are compiled without them); the output rows then only add up
+  // O-projection row blocks of OPROJ_ROWS rows, queued between the gate/up and the down items (bf16
+  // matrices: the FP8 and MXFP4 kernel instances are compiled without them); the output rows then
+  // only add up
   constexpr int OPROJ_ROWS = 16;
   // (each row block once per group of 4 tokens: the kernel's items stage 4 tokens' attention)
   const int oproj_items = steal && desc.weight_format == MK_WEIGHTS_BF16
@@ -305,7 +306,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.t.w[D_A0] = rg[0] + a; pr.t.w[D_A1] = e - a;
           pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;   // target filled below
           pr.t.w[D_SIG] = c_qkv[l][g];
-          pr.bytes = (int64_t)(e - a) * m.H * m.wb;
+          pr.bytes = (int64_t)(e - a) * m.H * m.wb32 / 32;
           pr.prio = 1;
           levels[lv0].push_back(pr);
           qkv_count[g]++;
@@ -318,7 +319,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a; pr.t.w[D_A2] = router_tiles;
       pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;   // target filled below
       pr.t.w[D_SIG] = c_rarr[l]; pr.t.w[D_SIG2] = c_route[l];
-      pr.bytes = (int64_t)(e - a) * m.H * m.wb;
+      pr.bytes = (int64_t)(e - a) * m.H * m.wb32 / 32;
       pr.prio = 0;
       levels[lv0].push_back(pr);
     }
@@ -364,7 +365,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
         pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
         pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
         pr.t.w[D_SIG] = c_h[l];
-        pr.bytes = ((int64_t)slots * slices * 2 * nf * m.H * m.wb + (int64_t)slots * m.H * m.F * m.wb) / tickets;
+        pr.bytes = ((int64_t)slots * slices * 2 * nf * m.H * m.wb32 / 32 + (int64_t)slots * m.H * m.F * m.wb32 / 32) / tickets;
         pr.prio = 1;
         levels[lvm].push_back(pr);
         n_gu++;
@@ -379,7 +380,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.t.w[D_W0] = c_x[l]; pr.t.w[D_T0] = -1;        // x_l complete (target filled below)
           pr.t.w[D_W1] = c_rarr[l]; pr.t.w[D_T1] = router_tiles;   // every router logit written
           pr.t.w[D_SIG] = c_h[l];
-          pr.bytes = (int64_t)2 * (f1 - f0) * m.H * m.wb;
+          pr.bytes = (int64_t)2 * (f1 - f0) * m.H * m.wb32 / 32;
           pr.prio = 1;
           levels[lv1].push_back(pr);
           n_gu++;
@@ -430,7 +431,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
       pr.t.w[D_W1] = c_h[l]; pr.t.w[D_T1] = n_gu;
       pr.t.w[D_SIG] = c_x[l + 1];
-      pr.bytes = (int64_t)(e - a) * (m.AD + (down_items > 0 ? 0 : (int64_t)slots * m.F)) * m.wb;
+      pr.bytes = (int64_t)(e - a) * (m.AD + (down_items > 0 ? 0 : (int64_t)slots * m.F)) * m.wb32 / 32;
       pr.prio = 0;
       levels[lv2].push_back(pr);
       n_out++;
@@ -456,7 +457,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       set(pr.t, OP_LMHEAD, L, LPL * L);
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
       pr.t.w[D_W0] = c_x[L]; pr.t.w[D_T0] = n_out_per_layer;
-      pr.bytes = (int64_t)(e - a) * m.H * m.wb;
+      pr.bytes = (int64_t)(e - a) * m.H * m.wb32 / 32;
       pr.prio = 0;
       levels[LPL * L].push_back(pr);
     }
@@ -912,7 +913,7 @@ mk_status mk_create(const mk_model_desc* desc, const mk_weight_ptrs* w, mk_engin
   e->m = dims_of(*desc);
   e->w = *w;
   e->shape = shape_id(desc->hidden, desc->head_dim, desc->n_q_heads, desc->n_kv_heads, desc->n_experts, desc->top_k,
-                      desc->expert_ffn, desc->weight_format == MK_WEIGHTS_FP8);
+                      desc->expert_ffn, desc->weight_format);
   e->opt.workers_per_cu = 2;
   e->opt.watchdog_ms = 2000;
   auto fail = [&](mk_status s) { free_all(e); delete e; return s; };
@@ -982,7 +983,7 @@ mk_status mk_build_schedule_chunked(mk_engine* e, int32_t batch, const int32_t* 
     if (e) e->msg = "mk_build_schedule: bad batch, seq_lens or rows_per_seq";
     return MK_ERR_INVALID_ARG;
   }
-  if (e->desc.weight_format == MK_WEIGHTS_FP8 && batch == 1 && (e->opt.flags & MK_FLAG_OPROJ_PER_GROUP)) {
+  if (e->desc.weight_format != MK_WEIGHTS_BF16 && batch == 1 && (e->opt.flags & MK_FLAG_OPROJ_PER_GROUP)) {
     e->msg = "mk_build_schedule: MK_FLAG_OPROJ_PER_GROUP (an ablation) exists for bf16 matrices only";
     return MK_ERR_UNSUPPORTED;
   }

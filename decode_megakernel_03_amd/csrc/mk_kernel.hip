@@ -32,15 +32,17 @@ namespace mk {
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 
-template <int H_, int D_, int HQ_, int HKV_, int E_, int K_, int F_, int W8_ = 0>
+template <int H_, int D_, int HQ_, int HKV_, int E_, int K_, int F_, int WF_ = 0>
 struct Shape {
   static constexpr int H = H_, D = D_, HQ = HQ_, HKV = HKV_, E = E_, K = K_, F = F_;
   // matrices (QKV, O, router, experts, lm_head): 0 bf16 rows; 1 FP8 rows (OCP E4M3 codes, then the
-  // row's float32 scale in a 16-byte tail; P3 "Limitations and Future Plans" names FP8 kernels as
-  // the next step). kw(k): 16-bit words of weights in a row of k inputs; rw(k): the row's stride.
-  static constexpr int W8 = W8_;
-  static constexpr int kw(int k) { return W8 ? k / 2 : k; }
-  static constexpr int rw(int k) { return W8 ? k / 2 + 8 : k; }
+  // row's float32 scale in a 16-byte tail); 2 MXFP4 rows (E2M1 codes two to a byte, then one E8M0
+  // scale byte per block of 32 inputs, padded to 16 bytes). P3 "Limitations and Future Plans" names
+  // FP8/FP4 kernels as the next step. kw(k): 16-bit words of codes in a row of k inputs; rw(k): the
+  // row's stride in 16-bit words.
+  static constexpr int WF = WF_;
+  static constexpr int kw(int k) { return WF == 2 ? k / 4 : WF == 1 ? k / 2 : k; }
+  static constexpr int rw(int k) { return WF == 2 ? (k / 2 + k / 32 + 15) / 16 * 8 : WF == 1 ? k / 2 + 8 : k; }
   static constexpr int HPG = HQ / HKV;           // query heads per KV head (GQA group)
   static constexpr int QKVR = (HQ + 2 * HKV) * D;
   static constexpr int AD = HQ * D;              // attention output width
@@ -50,10 +52,13 @@ using ShapeSmall = Shape<256, 32, 8, 2, 8, 2, 128>;
 using ShapeFull = Shape<2048, 128, 32, 4, 128, 8, 768>;
 using ShapeSmall8 = Shape<256, 32, 8, 2, 8, 2, 128, 1>;
 using ShapeFull8 = Shape<2048, 128, 32, 4, 128, 8, 768, 1>;
+using ShapeSmall4 = Shape<256, 32, 8, 2, 8, 2, 128, 2>;
+using ShapeFull4 = Shape<2048, 128, 32, 4, 128, 8, 768, 2>;
 
 constexpr int SPLIT_MAX = 1024;   // keys one attention task may cover (LDS score buffer)
 constexpr int MERGE_MAX = (SPLIT_MAX + 1) / 2;   // splits one (sequence, KV group) may have
 constexpr int OUT_MAXR = 5;       // most rows of one OUT task
+constexpr int OUT_OT = 4;         // tokens whose attention vectors an OUT task stages together
 constexpr int DOWN_ROWS = 128;    // W_down rows of one queued down item (192 KB of the full-size expert)
 constexpr int STEAL_PROBES = 4;   // sub-queues an expert task draws from (its own, then 3 more)
 constexpr int SC1 = 16;           // buffer cache-policy bit for agent-coherent access
@@ -149,6 +154,11 @@ __device__ __forceinline__ float dot8(u4 w, f4 a0, f4 a1, float acc) {
   return acc;
 }
 
+// Value of an E8M0 scale byte: 2^(e - 127); e = 0 is the subnormal 2^-127, e = 255 NaN
+__device__ __forceinline__ float e8m0(uint32_t e) {
+  return __uint_as_float(e == 255u ? 0x7fc00000u : e ? e << 23 : 0x00400000u);
+}
+
 // acc += sum_m w[m] * a[m] over the 16 E4M3 codes of w (bytes in element order), in element order;
 // the hardware conversion takes two codes of a 16-bit half at a time
 typedef float f2 __attribute__((ext_vector_type(2)));
@@ -163,6 +173,30 @@ __device__ __forceinline__ float dot16e4m3(u4 w, f4 a0, f4 a1, f4 a2, f4 a3, flo
     acc = __builtin_fmaf(hi.x, a[k].z, acc);
     acc = __builtin_fmaf(hi.y, a[k].w, acc);
   }
+  return acc;
+}
+
+// The 8 E2M1 codes of a dword (element 2i in the low nibble of byte i) times the block scale s (a
+// power of two, so every product is exact in the normal range), in element order
+struct f8v { float v[8]; };
+__device__ __forceinline__ f8v dec8e2m1(uint32_t w, float s) {
+  const f2 b0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 0);
+  const f2 b1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 1);
+  const f2 b2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 2);
+  const f2 b3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 3);
+  return f8v{{b0.x, b0.y, b1.x, b1.y, b2.x, b2.y, b3.x, b3.y}};
+}
+
+// acc += sum_m w[m] * a[m] over 8 decoded weights and 8 activations, in element order
+__device__ __forceinline__ float dot8f(const f8v& w, f4 a0, f4 a1, float acc) {
+  acc = __builtin_fmaf(w.v[0], a0.x, acc);
+  acc = __builtin_fmaf(w.v[1], a0.y, acc);
+  acc = __builtin_fmaf(w.v[2], a0.z, acc);
+  acc = __builtin_fmaf(w.v[3], a0.w, acc);
+  acc = __builtin_fmaf(w.v[4], a1.x, acc);
+  acc = __builtin_fmaf(w.v[5], a1.y, acc);
+  acc = __builtin_fmaf(w.v[6], a1.z, acc);
+  acc = __builtin_fmaf(w.v[7], a1.w, acc);
   return acc;
 }
 
@@ -271,7 +305,7 @@ __device__ __forceinline__ uint32_t ctr_sum(CParams& p, int c, int lane) {
 
 // Block until counter c >= target (wave 0 polls, the workgroup waits at a barrier). Returns false
 // if the step was aborted or this wait exceeded the watchdog (which then aborts the step).
-__device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) {
+__device__ __forceinline__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) {
   if (c < 0) return true;
   const int tx = tid(), lane = tx & 63;
   if (__builtin_amdgcn_readfirstlane(tx >> 6) == 0) {
@@ -317,7 +351,7 @@ __device__ bool wait_ge(CParams& p, Ctl& ctl, int c, uint32_t target, int task) 
 
 // Block until the single word *w (a union slot's count of finished gate/up items) reaches target
 // (wave 0 polls, the workgroup waits at a barrier). False if the step was aborted or the watchdog fired.
-__device__ bool wait_word(CParams& p, Ctl& ctl, const uint32_t* w, uint32_t target, int task, uint32_t detail) {
+__device__ __forceinline__ bool wait_word(CParams& p, Ctl& ctl, const uint32_t* w, uint32_t target, int task, uint32_t detail) {
   const int tx = tid(), lane = tx & 63;
   if (__builtin_amdgcn_readfirstlane(tx >> 6) == 0) {
     int ok = 1;
@@ -351,7 +385,7 @@ __device__ bool wait_word(CParams& p, Ctl& ctl, const uint32_t* w, uint32_t targ
 }
 
 // Block until counter c0 >= t0 and counter c1 >= t1, polling both in the same round trip.
-__device__ bool wait_ge2(CParams& p, Ctl& ctl, int c0, uint32_t t0, int c1, uint32_t t1, int task) {
+__device__ __forceinline__ bool wait_ge2(CParams& p, Ctl& ctl, int c0, uint32_t t0, int c1, uint32_t t1, int task) {
   const int tx = tid(), lane = tx & 63;
   if (__builtin_amdgcn_readfirstlane(tx >> 6) == 0) {
     int ok = 1;
@@ -434,27 +468,28 @@ __device__ __forceinline__ bool aborted(CParams& p) { return ctr_load(&p.err->ab
 template <int KD>
 struct Geo {
   static constexpr int CPR = KD / 8;
-  static constexpr int LPR = (CPR % 64 == 0) ? 64 : (CPR % 32 == 0) ? 32 : (CPR % 16 == 0) ? 16 : 8;
+  static constexpr int LPR = (CPR % 64 == 0) ? 64 : (CPR % 32 == 0) ? 32 : (CPR % 16 == 0) ? 16 : (CPR % 8 == 0) ? 8 : 4;
   static constexpr int RPP = 64 / LPR;
   static constexpr int CPL = CPR / LPR;
-  static_assert(CPR % LPR == 0, "row length must be a multiple of 8*LPR");
+  static_assert(CPR % LPR == 0, "row length must be a multiple of 8*LPR words");
 };
 
-// A block of NP row passes: 16-byte loads of weights (KD = 16-bit words of weights per row) and,
-// for FP8 rows (W8), each row's scale
-template <int KD, int NP, int W8 = 0>
+// A block of NP row passes: 16-byte loads of weights (KD = 16-bit words of codes per row) and,
+// for FP8 rows (WF 1), each row's scale; for MXFP4 rows (WF 2), each 16-byte chunk's block scale
+template <int KD, int NP, int WF = 0>
 struct WBuf {
   u4 w[NP][Geo<KD>::CPL];
-  float s[W8 ? NP : 1];
+  float s[WF == 2 ? NP * Geo<KD>::CPL : WF == 1 ? NP : 1];
 };
 
 template <int KD, int NP>
 __device__ __forceinline__ int block_rows() { return NP * NWAVE * Geo<KD>::RPP; }
 
 // RowPtr(r) -> const uint16_t* start of row r (only called for r < nrows); an FP8 row's scale is the
-// float right after its KD words of codes
-template <int KD, int NP, int W8 = 0, class RowPtr>
-__device__ __forceinline__ void load_block(WBuf<KD, NP, W8>& b, int blk, int nrows, RowPtr rowptr) {
+// float right after its KD words of codes; an MXFP4 row's block scales are the bytes right after
+// its codes, one per 16-byte chunk (chunk c of the row: byte c)
+template <int KD, int NP, int WF = 0, class RowPtr>
+__device__ __forceinline__ void load_block(WBuf<KD, NP, WF>& b, int blk, int nrows, RowPtr rowptr) {
   using G = Geo<KD>;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
@@ -465,22 +500,32 @@ __device__ __forceinline__ void load_block(WBuf<KD, NP, W8>& b, int blk, int nro
       const uint16_t* src = rowptr(r) + 8 * lir;
 #pragma unroll
       for (int j = 0; j < G::CPL; ++j) b.w[i][j] = ldw(src + 8 * G::LPR * j);
-      if constexpr (W8) b.s[i] = *reinterpret_cast<const float*>(rowptr(r) + KD);
+      if constexpr (WF == 1) b.s[i] = *reinterpret_cast<const float*>(rowptr(r) + KD);
+      if constexpr (WF == 2) {
+        const uint8_t* sb = reinterpret_cast<const uint8_t*>(rowptr(r) + KD) + lir;
+#pragma unroll
+        for (int j = 0; j < G::CPL; ++j) b.s[i * G::CPL + j] = e8m0(sb[G::LPR * j]);
+      }
     } else {
 #pragma unroll
       for (int j = 0; j < G::CPL; ++j) b.w[i][j] = u4{0u, 0u, 0u, 0u};
-      if constexpr (W8) b.s[i] = 0.f;
+      if constexpr (WF == 1) b.s[i] = 0.f;
+      if constexpr (WF == 2) {
+#pragma unroll
+        for (int j = 0; j < G::CPL; ++j) b.s[i * G::CPL + j] = 0.f;
+      }
     }
   }
 }
 
 // ActOf(r, t) -> const float* LDS activations (KD floats) for row r, token t
 // Emit(r, t, value) is called on the lane with lir == 0 of each row (value = full dot product)
-// (FP8 rows: 16 inputs per 16-byte load, and each row's sum times its scale)
-template <int KD, int NP, int TB, int W8 = 0, class ActOf, class Emit>
-__device__ __forceinline__ void compute_block(const WBuf<KD, NP, W8>& b, int blk, int nrows, int ntok,
+// (FP8 rows: 16 inputs per 16-byte load, and each row's sum times its scale; MXFP4 rows: 32 inputs
+// per load, each chunk's sum times its block scale)
+template <int KD, int NP, int TB, int WF = 0, class ActOf, class Emit>
+__device__ __forceinline__ void compute_block(const WBuf<KD, NP, WF>& b, int blk, int nrows, int ntok,
                                               ActOf act_of, Emit emit) {
-  constexpr int EPC = W8 ? 16 : 8;
+  constexpr int EPC = WF == 2 ? 32 : WF == 1 ? 16 : 8;
   using G = Geo<KD>;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
@@ -496,11 +541,18 @@ __device__ __forceinline__ void compute_block(const WBuf<KD, NP, W8>& b, int blk
 #pragma unroll
         for (int j = 0; j < G::CPL; ++j) {
           const f4* ap = reinterpret_cast<const f4*>(a + EPC * G::LPR * j);
-          if constexpr (W8) acc = dot16e4m3(b.w[i][j], ap[0], ap[1], ap[2], ap[3], acc);
+          if constexpr (WF == 2) {
+            const u4 w = b.w[i][j];
+            const float sc = b.s[i * G::CPL + j];
+            acc = dot8f(dec8e2m1(w.x, sc), ap[0], ap[1], acc);
+            acc = dot8f(dec8e2m1(w.y, sc), ap[2], ap[3], acc);
+            acc = dot8f(dec8e2m1(w.z, sc), ap[4], ap[5], acc);
+            acc = dot8f(dec8e2m1(w.w, sc), ap[6], ap[7], acc);
+          } else if constexpr (WF == 1) acc = dot16e4m3(b.w[i][j], ap[0], ap[1], ap[2], ap[3], acc);
           else acc = dot8(b.w[i][j], ap[0], ap[1], acc);
         }
         acc = wsum<G::LPR>(acc);
-        if constexpr (W8) acc *= b.s[i];
+        if constexpr (WF == 1) acc *= b.s[i];
         if (lir == 0 && r < nrows) emit(r, t, acc);
       }
     }
@@ -517,11 +569,11 @@ __device__ __forceinline__ void compute_block(const WBuf<KD, NP, W8>& b, int blk
 // tokens). A pair is computed whole once its first token is in range (act_of must return readable
 // LDS for every t < TB); the second token's result is emitted only if it is in range. Same per-row
 // order of products.
-template <int KD, int NP, int TB, int TG = 1, int W8 = 0, class ActOf, class Emit>
-__device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, W8>& b, int blk, int nrows, int ntok,
+template <int KD, int NP, int TB, int TG = 1, int WF = 0, class ActOf, class Emit>
+__device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, WF>& b, int blk, int nrows, int ntok,
                                                      ActOf act_of, Emit emit) {
   using G = Geo<KD>;
-  constexpr int EPC = W8 ? 16 : 8;
+  constexpr int EPC = WF == 2 ? 32 : WF == 1 ? 16 : 8;
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int rip = lane / G::LPR, lir = lane % G::LPR;
   if constexpr (TG == 2) {
@@ -538,7 +590,23 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, W8>& b, 
         for (int j = 0; j < G::CPL; ++j) {
           const f4* qa = reinterpret_cast<const f4*>(pa + EPC * G::LPR * j);
           const f4* qb = reinterpret_cast<const f4*>(pb + EPC * G::LPR * j);
-          if constexpr (W8) {
+          if constexpr (WF == 2) {
+            // 32 codes per load, a dword (8 codes) at a time: the pair's two tokens share each
+            // conversion
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const f4 a0 = qa[2 * k], a1 = qa[2 * k + 1], c0 = qb[2 * k], c1 = qb[2 * k + 1];
+#pragma unroll
+              for (int i = 0; i < NP; ++i) {
+                const u4 w = b.w[i][j];
+                const f8v d = dec8e2m1(k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w, b.s[i * G::CPL + j]);
+                acc0[i] = dot8f(d, a0, a1, acc0[i]);
+                acc1[i] = dot8f(d, c0, c1, acc1[i]);
+              }
+            }
+            continue;
+          }
+          if constexpr (WF == 1) {
             // 16 codes per load: the pair's two tokens share each conversion
             const f4 a[4] = {qa[0], qa[1], qa[2], qa[3]}, c[4] = {qb[0], qb[1], qb[2], qb[3]};
 #pragma unroll
@@ -580,11 +648,89 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, W8>& b, 
         for (int i = 0; i < NP; ++i) {
           const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
           float v0 = wsum<G::LPR>(acc0[i]), v1 = wsum<G::LPR>(acc1[i]);
-          if constexpr (W8) { v0 *= b.s[i]; v1 *= b.s[i]; }
+          if constexpr (WF == 1) { v0 *= b.s[i]; v1 *= b.s[i]; }
           if (lir == 0 && r < nrows) {
             emit(r, t0, v0);
             if (t0 + 1 < ntok) emit(r, t0 + 1, v1);
           }
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (WF == 2 && TB == OUT_OT) {
+    // (the output rows' O projection: conversions per token - sharing them across its OUT_OT tokens
+    // pushed the whole step kernel past its register budget)
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      if (t < ntok) {
+        const float* a = act_of(0, t) + EPC * lir;
+        float acc[NP];
+#pragma unroll
+        for (int i = 0; i < NP; ++i) acc[i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < G::CPL; ++j) {
+          const f4* ap = reinterpret_cast<const f4*>(a + EPC * G::LPR * j);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const f4 a0 = ap[2 * k], a1 = ap[2 * k + 1];
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+              const u4 w = b.w[i][j];
+              acc[i] = dot8f(dec8e2m1(k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w, b.s[i * G::CPL + j]), a0, a1, acc[i]);
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
+          const float v = wsum<G::LPR>(acc[i]);
+          if (lir == 0 && r < nrows) emit(r, t, v);
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (WF == 2) {
+    // MXFP4: each dword's conversions serve every token of the batch (a pass's 8 decoded weights
+    // meet each token's 8 activations); per row and token the same order of products
+    float acc[TB][NP];
+#pragma unroll
+    for (int t = 0; t < TB; ++t)
+#pragma unroll
+      for (int i = 0; i < NP; ++i) acc[t][i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < G::CPL; ++j) {
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        f4 a0[TB], a1[TB];
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+          if (t < ntok) {
+            const f4* ap = reinterpret_cast<const f4*>(act_of(0, t) + EPC * lir + EPC * G::LPR * j) + 2 * k;
+            a0[t] = ap[0]; a1[t] = ap[1];
+          } else {
+            a0[t] = f4{0.f, 0.f, 0.f, 0.f}; a1[t] = a0[t];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const u4 w = b.w[i][j];
+          const f8v d = dec8e2m1(k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w, b.s[i * G::CPL + j]);
+#pragma unroll
+          for (int t = 0; t < TB; ++t)
+            if (t < ntok) acc[t][i] = dot8f(d, a0[t], a1[t], acc[t][i]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TB; ++t) {
+      if (t < ntok) {
+#pragma unroll
+        for (int i = 0; i < NP; ++i) {
+          const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
+          const float v = wsum<G::LPR>(acc[t][i]);
+          if (lir == 0 && r < nrows) emit(r, t, v);
         }
       }
     }
@@ -600,7 +746,7 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, W8>& b, 
 #pragma unroll
       for (int j = 0; j < G::CPL; ++j) {
         const f4* ap = reinterpret_cast<const f4*>(a + EPC * G::LPR * j);
-        if constexpr (W8) {
+        if constexpr (WF == 1) {
           const f4 a0 = ap[0], a1 = ap[1], a2 = ap[2], a3 = ap[3];
 #pragma unroll
           for (int i = 0; i < NP; ++i) acc[i] = dot16e4m3(b.w[i][j], a0, a1, a2, a3, acc[i]);
@@ -614,7 +760,7 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, W8>& b, 
       for (int i = 0; i < NP; ++i) {
         const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
         float v = wsum<G::LPR>(acc[i]);
-        if constexpr (W8) v *= b.s[i];
+        if constexpr (WF == 1) v *= b.s[i];
         if (lir == 0 && r < nrows) emit(r, t, v);
       }
     }
@@ -623,18 +769,18 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, W8>& b, 
 
 // Stream `nrows` rows; block 0 may already be loaded into A (prefetched before a dependency wait).
 // The activations are shared by all rows (ActOf ignores its row argument).
-template <int KD, int NP, int TB, int TG = 1, int W8 = 0, class RowPtr, class ActOf, class Emit>
-__device__ __forceinline__ void gemv_stream(WBuf<KD, NP, W8>& A, bool a_loaded, int nrows, int ntok,
+template <int KD, int NP, int TB, int TG = 1, int WF = 0, class RowPtr, class ActOf, class Emit>
+__device__ __forceinline__ void gemv_stream(WBuf<KD, NP, WF>& A, bool a_loaded, int nrows, int ntok,
                                             RowPtr rowptr, ActOf act_of, Emit emit) {
   const int nblk = (nrows + block_rows<KD, NP>() - 1) / block_rows<KD, NP>();
-  WBuf<KD, NP, W8> B;
-  if (!a_loaded) load_block<KD, NP, W8>(A, 0, nrows, rowptr);
+  WBuf<KD, NP, WF> B;
+  if (!a_loaded) load_block<KD, NP, WF>(A, 0, nrows, rowptr);
   for (int blk = 0; blk < nblk; blk += 2) {
-    if (blk + 1 < nblk) load_block<KD, NP, W8>(B, blk + 1, nrows, rowptr);
-    compute_block_shared<KD, NP, TB, TG, W8>(A, blk, nrows, ntok, act_of, emit);
+    if (blk + 1 < nblk) load_block<KD, NP, WF>(B, blk + 1, nrows, rowptr);
+    compute_block_shared<KD, NP, TB, TG, WF>(A, blk, nrows, ntok, act_of, emit);
     if (blk + 1 < nblk) {
-      if (blk + 2 < nblk) load_block<KD, NP, W8>(A, blk + 2, nrows, rowptr);
-      compute_block_shared<KD, NP, TB, TG, W8>(B, blk + 1, nrows, ntok, act_of, emit);
+      if (blk + 2 < nblk) load_block<KD, NP, WF>(A, blk + 2, nrows, rowptr);
+      compute_block_shared<KD, NP, TB, TG, WF>(B, blk + 1, nrows, ntok, act_of, emit);
     }
   }
 }
@@ -645,7 +791,7 @@ __device__ __forceinline__ void gemv_stream(WBuf<KD, NP, W8>& A, bool a_loaded, 
 // layer). x_0 is the token's embedding row; x_l (l >= 1) comes from the previous layer's OUT
 // tasks. One wave per token: each lane sums H/64 squares, then a wave tree.
 template <class S>
-__device__ void stage_norm(CParams& p, int l, const int* toks, int ntok, const uint16_t* gain,
+__device__ __forceinline__ void stage_norm(CParams& p, int l, const int* toks, int ntok, const uint16_t* gain,
                            float* act, int task) {
   constexpr int H = S::H;
   constexpr int G4 = H / 256;            // groups of 4 consecutive floats per lane
@@ -811,20 +957,20 @@ __device__ __forceinline__ bool op_qkv(int task) {
   const TaskHdr T = read_task(p, task);
   // a whole 16-row tile in flight before the wait (FP8 rows: 4 passes too, the register budget of the
   // batch form's token pairs)
-  constexpr int H = S::H, KW = S::kw(H), NP = (Geo<KW>::CPL >= 4 || S::W8) ? 4 : 8;
+  constexpr int H = S::H, KW = S::kw(H), NP = (Geo<KW>::CPL >= 4 || S::WF) ? 4 : 8;
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_qkv + (size_t)(row0 + r) * S::rw(H); };
-  WBuf<KW, NP, S::W8> A;
+  WBuf<KW, NP, S::WF> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<KW, NP, S::W8>(A, 0, nrows, rowptr);
+  if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
   stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
   MARK(0);
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + (size_t)T.layer * MAXB * S::QKVR);
-  gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::W8>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::WF>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); });
   MARK(1);
@@ -975,13 +1121,13 @@ __device__ __forceinline__ bool op_router(int task) {
   Ctl& ctl = ctl_s;
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
-  constexpr int H = S::H, E = S::E, KW = S::kw(H), NP = (Geo<KW>::CPL >= 4 || S::W8) ? 4 : 8;
+  constexpr int H = S::H, E = S::E, KW = S::kw(H), NP = (Geo<KW>::CPL >= 4 || S::WF) ? 4 : 8;
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_router + (size_t)(row0 + r) * S::rw(H); };
-  WBuf<KW, NP, S::W8> A;
+  WBuf<KW, NP, S::WF> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<KW, NP, S::W8>(A, 0, nrows, rowptr);
+  if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
@@ -989,7 +1135,7 @@ __device__ __forceinline__ bool op_router(int task) {
   MARK(0);
   const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)T.layer * MAXB * E);
   const float* bias = p.has_bias ? Lp.router_bias : nullptr;
-  gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::W8>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::WF>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) {
         const int e = row0 + r;
@@ -1101,8 +1247,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
     const uint16_t* wg = Lp.w_gate + (size_t)e * F * S::rw(H);
     const uint16_t* wu = Lp.w_up + (size_t)e * F * S::rw(H);
     auto rowptr = [&](int r) { return r < nf ? wg + (size_t)(f0 + r) * S::rw(H) : wu + (size_t)(f0 + r - nf) * S::rw(H); };
-    WBuf<KWH, NP, S::W8> A;
-    load_block<KWH, NP, S::W8>(A, 0, 2 * nf, rowptr);
+    WBuf<KWH, NP, S::WF> A;
+    load_block<KWH, NP, S::WF>(A, 0, 2 * nf, rowptr);
     __syncthreads();
     const int ntok = ctl.flag;
     MARK(1);
@@ -1110,7 +1256,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
 #pragma unroll
     for (int t = 0; t < TB; ++t) brow[t] = t < ntok ? ctl.toks[t] : 0;
     float* gu = sm + (size_t)TB * H;                 // [TB][2 nf]
-    gemv_stream<KWH, NP, TB, 1, S::W8>(A, true, 2 * nf, ntok, rowptr,
+    gemv_stream<KWH, NP, TB, 1, S::WF>(A, true, 2 * nf, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)brow[t] * H; },
         [&](int r, int t, float v) { gu[t * 2 * nf + r] = v; });
     __syncthreads();
@@ -1135,13 +1281,14 @@ __device__ __forceinline__ bool op_gateup(int task) {
   // every gate/up item of the slot is done: y[b][rank][row] = W_down[e][row] . h[b][rank]. Its weight
   // rows are requested before the slot's count is awaited. The staged h overwrites the normed input.
   auto run_down = [&](int u, int q, int slices_c) -> bool {
-    constexpr int NPD = 4;
+    // (MXFP4: two passes of 8 rows per wave - a block of the same 64 rows' bytes, half the registers)
+    constexpr int NPD = S::WF == 2 ? 2 : 4;
     const int e = slot_expert(u);
     const int row0 = q * DOWN_ROWS, nr = H - row0 < DOWN_ROWS ? H - row0 : DOWN_ROWS;
     const uint16_t* wd = Lp.w_down + ((size_t)e * H + row0) * S::rw(F);
     auto rowptr = [&](int r) { return wd + (size_t)r * S::rw(F); };
-    WBuf<S::kw(F), NPD, S::W8> A;
-    load_block<S::kw(F), NPD, S::W8>(A, 0, nr, rowptr);
+    WBuf<S::kw(F), NPD, S::WF> A;
+    load_block<S::kw(F), NPD, S::WF>(A, 0, nr, rowptr);
     if (tid() == 0) ctl.norm_l = -1;
     __syncthreads();
     const int ntok = ctl.flag;
@@ -1174,7 +1321,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
     __syncthreads();
     MARK(5);
     const __amdgpu_buffer_rsrc_t Y = rsrc(p.y + (size_t)l * MAXB * K * H);
-    gemv_stream<S::kw(F), NPD, TB, 1, S::W8>(A, true, nr, ntok, rowptr,
+    gemv_stream<S::kw(F), NPD, TB, 1, S::WF>(A, true, nr, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)t * F; },
         [&](int r, int t, float v) {
           int yo = 0;
@@ -1200,8 +1347,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
     const int nt = p.B - b0 < OQT ? p.B - b0 : OQT;
     if (nr <= 0 || nt <= 0) return true;     // (no rows or tokens left for this item)
     auto orow = [&](int r) { return Lp.w_o + (size_t)(r0 + r) * S::rw(AD); };
-    WBuf<S::kw(AD), 1, S::W8> A;
-    load_block<S::kw(AD), 1, S::W8>(A, 0, nr, orow);
+    WBuf<S::kw(AD), 1, S::WF> A;
+    load_block<S::kw(AD), 1, S::WF>(A, 0, nr, orow);
     if (tid() == 0) ctl.norm_l = -1;     // the staged normed input is overwritten below
     if (!wait_ge(p, ctl, T.a3 - 1, (uint32_t)(p.B * S::HKV * NSL), T.id)) return false;
     const __amdgpu_buffer_rsrc_t At = rsrc(p.attn + (size_t)l * MAXB * AD);
@@ -1209,7 +1356,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
     __syncthreads();                     // every wave is done with the previous item's LDS
     stage_f4<OQT * AD>(sm, At, 4u * (b0 * AD), nt * AD);
     __syncthreads();
-    gemv_stream<S::kw(AD), 1, OQT, 1, S::W8>(A, true, nr, nt, orow,
+    gemv_stream<S::kw(AD), 1, OQT, 1, S::WF>(A, true, nr, nt, orow,
         [&](int r, int t) { return sm + (size_t)t * AD; },
         [&](int r, int t, float v) { stc(Ob, 4u * ((b0 + t) * H + r0 + r), v); });
     __syncthreads();                     // the staging area is free for the next item
@@ -1268,7 +1415,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
       } else {
         // (compiled for bf16 matrices only: in the FP8 instances the extra GEMV path costs 15 more
         // spilled registers, and the schedule gives them no such items)
-        if constexpr (!S::W8) {
+        if constexpr (!S::WF) {
           if (!run_oproj(i - n_gu, orows, ntg)) return false;
         } else {
           return false;                  // (the host's validator refuses such a schedule)
@@ -1315,7 +1462,6 @@ struct AttnLds {
   static constexpr int END = al(QF + HPG * D);
 };
 
-constexpr int OUT_OT = 4;   // tokens whose attention vectors are staged together
 
 template <class S>
 struct OutLds {   // LDS layout of a batched output task, in floats
@@ -1866,11 +2012,11 @@ __device__ int wait_prefix(CParams& p, Ctl& ctl, int c, int n, uint32_t target, 
 // every group first (measured faster on MI355X, where the four groups' merges land within about a
 // microsecond of each other and each extra round adds a dependent staging round trip).
 template <class S, int NP, int OT, class Emit>
-__device__ __forceinline__ bool oproj_grouped(CParams& p, Ctl& ctl, const WBuf<S::kw(S::AD), NP, S::W8>& W, int nrows, int b0, int nt,
+__device__ __forceinline__ bool oproj_grouped(CParams& p, Ctl& ctl, const WBuf<S::kw(S::AD), NP, S::WF>& W, int nrows, int b0, int nt,
                                               int cbase, int target, bool wait, bool per_group, int task, float* a_s,
                                               __amdgpu_buffer_rsrc_t At, Emit emit) {
   constexpr int AD = S::AD, GW = S::HPG * S::D, HKV = S::HKV;
-  static_assert(!S::W8, "the per-KV-group O projection (an ablation) exists for bf16 matrices only");
+  static_assert(!S::WF, "the per-KV-group O projection (an ablation) exists for bf16 matrices only");
   using G = Geo<S::kw(AD)>;
   constexpr int NI = (OT * AD + 4 * NT - 1) / (4 * NT);
   static_assert(GW % 4 == 0 && HKV <= 64, "");
@@ -1947,9 +2093,9 @@ __device__ __forceinline__ bool op_out(int task) {
   const int l = T.layer, row0 = T.a0, nrows = T.a1;
   const auto& Lp = cst(p.layers)[l];
   auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * S::rw(AD); };
-  WBuf<S::kw(AD), NPO, S::W8> WO;
+  WBuf<S::kw(AD), NPO, S::WF> WO;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<S::kw(AD), NPO, S::W8>(WO, 0, nrows, orow);
+  if (pre) load_block<S::kw(AD), NPO, S::WF>(WO, 0, nrows, orow);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;      // routing known
   load_route(p, l);
   const RouteTable& rt = ctl.rt;
@@ -1957,7 +2103,7 @@ __device__ __forceinline__ bool op_out(int task) {
   float* h_s = sm + AD;                                                // [K][F]
   float* o_s = h_s + K * F;                                            // [OUT_MAXR]
   float* y_s = o_s + OUT_MAXR;                                         // [K][OUT_MAXR]
-  if (!pre) load_block<S::kw(AD), NPO, S::W8>(WO, 0, nrows, orow);
+  if (!pre) load_block<S::kw(AD), NPO, S::WF>(WO, 0, nrows, orow);
   float* mo_s = y_s + K * OUT_MAXR;                                    // [MAXB][OUT_MAXR] MoE term
   float* xv_s = mo_s + MAXB * OUT_MAXR;                                // [MAXB][OUT_MAXR] x_l rows
   const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
@@ -1976,13 +2122,13 @@ __device__ __forceinline__ bool op_out(int task) {
       for (int ii = 0; ii < K; ++ii) if (ii == i) e = sel[ii];
       return Lp.w_down + ((size_t)e * H + row0 + r) * S::rw(F);
     };
-    WBuf<S::kw(F), NPD, S::W8> WD;
-    load_block<S::kw(F), NPD, S::W8>(WD, 0, K * nrows, drow);
+    WBuf<S::kw(F), NPD, S::WF> WD;
+    load_block<S::kw(F), NPD, S::WF>(WD, 0, K * nrows, drow);
     if (b == 0 && !wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every MoE slice
     stage_f4<K * F>(h_s, Hb, 4u * (b * K * F), K * F);
     __syncthreads();
     if (b == 0) MARK(0);
-    compute_block<S::kw(F), NPD, 1, S::W8>(WD, 0, K * nrows, 1, [&](int q, int t) { return h_s + (q / nrows) * F; },
+    compute_block<S::kw(F), NPD, 1, S::WF>(WD, 0, K * nrows, 1, [&](int q, int t) { return h_s + (q / nrows) * F; },
                              [&](int q, int t, float v) { y_s[(q / nrows) * OUT_MAXR + q % nrows] = v; });
     __syncthreads();
     if (tid() < nrows) {
@@ -2015,7 +2161,7 @@ __device__ __forceinline__ bool op_out(int task) {
     } else {
       stage_f4<AD>(a_s, At, 4u * (b * AD), AD);
       __syncthreads();
-      compute_block_shared<S::kw(AD), NPO, 1, 1, S::W8>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
+      compute_block_shared<S::kw(AD), NPO, 1, 1, S::WF>(WO, 0, nrows, 1, [&](int r, int t) { return a_s; },
                                        [&](int r, int t, float v) { o_s[r] = v; });
     }
     if (b == 0) MARK(2);
@@ -2107,9 +2253,9 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   if (T.a4) {
     // the down projections were computed by the queued down items: y[b][i][row] for token b's i-th
     // expert; the MoE term sums w_i y_i in ascending expert order, as the form below does
-    WBuf<S::kw(AD), NPO, S::W8> WO;
+    WBuf<S::kw(AD), NPO, S::WF> WO;
     auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * S::rw(AD); };
-    load_block<S::kw(AD), NPO, S::W8>(WO, 0, nrows, orow);
+    load_block<S::kw(AD), NPO, S::WF>(WO, 0, nrows, orow);
     if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every expert task (all items)
     MARK(0);
     if (tx < B * nrows) {
@@ -2132,7 +2278,7 @@ __device__ __forceinline__ bool op_out_batch(int task) {
       stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
       __syncthreads();
       if (b0 == 0) MARK(2);
-      compute_block_shared<S::kw(AD), NPO, OUT_OT, 1, S::W8>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
+      compute_block_shared<S::kw(AD), NPO, OUT_OT, 1, S::WF>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
                                             [&](int r, int t, float v) { o_s[t * OUT_MAXR + r] = v; });
       __syncthreads();
       if (tx < nt * nrows) {
@@ -2172,8 +2318,8 @@ __device__ __forceinline__ bool op_out_batch(int task) {
     }
   };
   // token b's MoE term from its W_down rows (in W) and its h (staged at hs)
-  auto moe_token = [&](const WBuf<S::kw(F), NPD, S::W8>& W, const float* hs, int b) {
-    compute_block<S::kw(F), NPD, 1, S::W8>(W, 0, K * nrows, 1, [&](int q, int t) { return hs + (q / nrows) * F; },
+  auto moe_token = [&](const WBuf<S::kw(F), NPD, S::WF>& W, const float* hs, int b) {
+    compute_block<S::kw(F), NPD, 1, S::WF>(W, 0, K * nrows, 1, [&](int q, int t) { return hs + (q / nrows) * F; },
                              [&](int q, int t, float v) { y_s[(q / nrows) * OUT_MAXR + q % nrows] = v; });
     __syncthreads();
     if (tx < nrows) {
@@ -2184,19 +2330,19 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   };
   float* hA = sm + LY::HA;
   float* hB = sm + LY::HB;
-  WBuf<S::kw(F), NPD, S::W8> WA, WB;
-  load_block<S::kw(F), NPD, S::W8>(WA, 0, K * nrows, drow_of(0));
+  WBuf<S::kw(F), NPD, S::WF> WA, WB;
+  load_block<S::kw(F), NPD, S::WF>(WA, 0, K * nrows, drow_of(0));
   if (!wait_ge(p, ctl, T.w1, (uint32_t)T.t1, T.id)) return false;   // every MoE slice
   h_issue(0);
   h_put(hA);
   MARK(0);
   for (int b = 0; b < B; b += 2) {
     const bool has1 = b + 1 < B;
-    if (has1) { load_block<S::kw(F), NPD, S::W8>(WB, 0, K * nrows, drow_of(b + 1)); h_issue(b + 1); }
+    if (has1) { load_block<S::kw(F), NPD, S::WF>(WB, 0, K * nrows, drow_of(b + 1)); h_issue(b + 1); }
     __syncthreads();                       // hA staged; the previous token is done with y_s
     moe_token(WA, hA, b);
     if (has1) h_put(hB);
-    if (b + 2 < B) { load_block<S::kw(F), NPD, S::W8>(WA, 0, K * nrows, drow_of(b + 2)); h_issue(b + 2); }
+    if (b + 2 < B) { load_block<S::kw(F), NPD, S::WF>(WA, 0, K * nrows, drow_of(b + 2)); h_issue(b + 2); }
     if (has1) {
       __syncthreads();                     // hB staged; token b is done with y_s and hA
       moe_token(WB, hB, b + 1);
@@ -2207,8 +2353,8 @@ __device__ __forceinline__ bool op_out_batch(int task) {
   MARK(1);
   // O projection of OUT_OT tokens per pass over the W_o rows
   auto orow = [&](int r) { return Lp.w_o + (size_t)(row0 + r) * S::rw(AD); };
-  WBuf<S::kw(AD), NPO, S::W8> WO;
-  load_block<S::kw(AD), NPO, S::W8>(WO, 0, nrows, orow);
+  WBuf<S::kw(AD), NPO, S::WF> WO;
+  load_block<S::kw(AD), NPO, S::WF>(WO, 0, nrows, orow);
   __syncthreads();                         // the MoE phase is done with the LDS it shares with a_s
   float* a_s = sm + LY::A;
   if (!wait_ge(p, ctl, T.a2, (uint32_t)T.a3, T.id)) return false;      // attention of every KV group
@@ -2217,7 +2363,7 @@ __device__ __forceinline__ bool op_out_batch(int task) {
     stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
     __syncthreads();
     if (b0 == 0) MARK(2);
-    compute_block_shared<S::kw(AD), NPO, OUT_OT, 1, S::W8>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
+    compute_block_shared<S::kw(AD), NPO, OUT_OT, 1, S::WF>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
                                           [&](int r, int t, float v) { o_s[t * OUT_MAXR + r] = v; });
     __syncthreads();
     if (tx < nt * nrows) {
@@ -2247,9 +2393,9 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   constexpr int H = S::H, KW = S::kw(H), NP = (Geo<KW>::CPL >= 4) ? (TB > 1 ? 4 : 2) : 4, RPP = Geo<KW>::RPP;
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return p.lm_head + (size_t)(row0 + r) * S::rw(H); };
-  WBuf<KW, NP, S::W8> A;
+  WBuf<KW, NP, S::WF> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<KW, NP, S::W8>(A, 0, nrows, rowptr);
+  if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
   if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
   if (tid() < MAXB) ctl.toks[tid()] = tid();
   __syncthreads();
@@ -2260,7 +2406,7 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   for (int t = 0; t < TB; ++t) { bv[t] = -INFINITY; bi[t] = 0x7fffffff; }
   float* logits = p.logits;
   const int V = p.V;
-  gemv_stream<KW, NP, TB, 1, S::W8>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<KW, NP, TB, 1, S::WF>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) {
         const int row = row0 + r;
@@ -2425,14 +2571,15 @@ static hipError_t occupancy_one(int* blocks_per_cu) {
   return hipOccupancyMaxActiveBlocksPerMultiprocessor(blocks_per_cu, (const void*)mk_step<S, TB, VAR>, NT, lds);
 }
 
-// 0 / 1: the small and the full shape with bf16 matrices; 2 / 3: the same with FP8 matrices
-int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F, int w8) {
+// 0 / 1: the small and the full shape with bf16 matrices; 2 / 3: the same with FP8 matrices; 4 / 5:
+// with MXFP4 matrices
+int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F, int wf) {
   int id = -1;
   if (H == ShapeSmall::H && D == ShapeSmall::D && HQ == ShapeSmall::HQ && HKV == ShapeSmall::HKV &&
       E == ShapeSmall::E && K == ShapeSmall::K && F == ShapeSmall::F) id = 0;
   if (H == ShapeFull::H && D == ShapeFull::D && HQ == ShapeFull::HQ && HKV == ShapeFull::HKV &&
       E == ShapeFull::E && K == ShapeFull::K && F == ShapeFull::F) id = 1;
-  return id < 0 ? -1 : id + (w8 ? 2 : 0);
+  return id < 0 || wf < 0 || wf > 2 ? -1 : id + 2 * wf;
 }
 
 // Kernel instances: batch 1 (VAR 1: the per-KV-group O projection of MK_FLAG_OPROJ_PER_GROUP) and
@@ -2442,40 +2589,52 @@ int step_variant(int batch, int flags, bool kv_first) {
   return kv_first ? 2 : 0;
 }
 
+// The instance of shape S for (batch, var), run through fn.run<S, TB, VAR>(); VAR 1 exists for bf16
+// matrices only
+template <class S, class Fn>
+static hipError_t with_instance(int batch, int var, const Fn& fn) {
+  if (batch > 1) return var == 2 ? fn.template run<S, MAXB, 2>() : fn.template run<S, MAXB, 0>();
+  if (var == 1) {
+    if constexpr (S::WF == 0) return fn.template run<S, 1, 1>();
+    else return hipErrorInvalidValue;
+  }
+  return fn.template run<S, 1, 0>();
+}
+
+template <class Fn>
+static hipError_t with_shape(int shape, int batch, int var, const Fn& fn) {
+  switch (shape) {
+    case 0: return with_instance<ShapeSmall>(batch, var, fn);
+    case 1: return with_instance<ShapeFull>(batch, var, fn);
+    case 2: return with_instance<ShapeSmall8>(batch, var, fn);
+    case 3: return with_instance<ShapeFull8>(batch, var, fn);
+    case 4: return with_instance<ShapeSmall4>(batch, var, fn);
+    case 5: return with_instance<ShapeFull4>(batch, var, fn);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+struct LaunchFn {
+  const Params& p;
+  int grid;
+  hipStream_t st;
+  size_t* lds;
+  template <class S, int TB, int VAR>
+  hipError_t run() const { return launch_one<S, TB, VAR>(p, grid, st, lds); }
+};
+
+struct OccupancyFn {
+  int* blocks_per_cu;
+  template <class S, int TB, int VAR>
+  hipError_t run() const { return occupancy_one<S, TB, VAR>(blocks_per_cu); }
+};
+
 hipError_t launch_step(int shape, int batch, int var, const Params& p, int grid, hipStream_t st, size_t* lds) {
-  if (shape >= 2) {              // FP8 matrices: kernel instances 0 and 2
-    if (var == 1) return hipErrorInvalidValue;
-    if (shape == 2) {
-      if (batch > 1) return var == 2 ? launch_one<ShapeSmall8, MAXB, 2>(p, grid, st, lds) : launch_one<ShapeSmall8, MAXB>(p, grid, st, lds);
-      return launch_one<ShapeSmall8, 1>(p, grid, st, lds);
-    }
-    if (batch > 1) return var == 2 ? launch_one<ShapeFull8, MAXB, 2>(p, grid, st, lds) : launch_one<ShapeFull8, MAXB>(p, grid, st, lds);
-    return launch_one<ShapeFull8, 1>(p, grid, st, lds);
-  }
-  if (shape == 0) {
-    if (batch > 1) return var == 2 ? launch_one<ShapeSmall, MAXB, 2>(p, grid, st, lds) : launch_one<ShapeSmall, MAXB>(p, grid, st, lds);
-    return var == 1 ? launch_one<ShapeSmall, 1, 1>(p, grid, st, lds) : launch_one<ShapeSmall, 1>(p, grid, st, lds);
-  }
-  if (batch > 1) return var == 2 ? launch_one<ShapeFull, MAXB, 2>(p, grid, st, lds) : launch_one<ShapeFull, MAXB>(p, grid, st, lds);
-  return var == 1 ? launch_one<ShapeFull, 1, 1>(p, grid, st, lds) : launch_one<ShapeFull, 1>(p, grid, st, lds);
+  return with_shape(shape, batch, var, LaunchFn{p, grid, st, lds});
 }
 
 hipError_t step_occupancy(int shape, int batch, int var, int* blocks_per_cu) {
-  if (shape >= 2) {
-    if (var == 1) return hipErrorInvalidValue;
-    if (shape == 2) {
-      if (batch > 1) return var == 2 ? occupancy_one<ShapeSmall8, MAXB, 2>(blocks_per_cu) : occupancy_one<ShapeSmall8, MAXB>(blocks_per_cu);
-      return occupancy_one<ShapeSmall8, 1>(blocks_per_cu);
-    }
-    if (batch > 1) return var == 2 ? occupancy_one<ShapeFull8, MAXB, 2>(blocks_per_cu) : occupancy_one<ShapeFull8, MAXB>(blocks_per_cu);
-    return occupancy_one<ShapeFull8, 1>(blocks_per_cu);
-  }
-  if (shape == 0) {
-    if (batch > 1) return var == 2 ? occupancy_one<ShapeSmall, MAXB, 2>(blocks_per_cu) : occupancy_one<ShapeSmall, MAXB>(blocks_per_cu);
-    return var == 1 ? occupancy_one<ShapeSmall, 1, 1>(blocks_per_cu) : occupancy_one<ShapeSmall, 1>(blocks_per_cu);
-  }
-  if (batch > 1) return var == 2 ? occupancy_one<ShapeFull, MAXB, 2>(blocks_per_cu) : occupancy_one<ShapeFull, MAXB>(blocks_per_cu);
-  return var == 1 ? occupancy_one<ShapeFull, 1, 1>(blocks_per_cu) : occupancy_one<ShapeFull, 1>(blocks_per_cu);
+  return with_shape(shape, batch, var, OccupancyFn{blocks_per_cu});
 }
 
 // Plain streaming read of n16 16-byte words (a bandwidth ceiling for comparison with the step

@@ -7,8 +7,9 @@
 #include "mk_internal.h"
 
 namespace mk {
-// 0 = hidden 256 small model, 1 = hidden 2048 30B MoE, -1 = no compiled instance
-int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F, int w8);
+// 0 = hidden 256 small model, 1 = hidden 2048 30B MoE, plus 2 * weight format (MK_WEIGHTS_*);
+// -1 = no compiled instance
+int shape_id(int H, int D, int HQ, int HKV, int E, int K, int F, int wf);
 // cooperative launch of one step on `grid` workers (batch 1 or up to 8 instance)
 // kernel instance for a step: 0 plain, 1 per-KV-group O projection (batch 1 with flag 8), 2 the QKV
 // tasks publish the step's K/V (batch > 1 with rows of one sequence in a step)

@@ -18,6 +18,8 @@ MK_ERR_NO_SCHEDULE, MK_ERR_SCHEDULE_STALE, MK_ERR_DEVICE = -5, -6, -7
 MK_ABI_VERSION = 2
 MK_WEIGHTS_BF16 = 0
 MK_WEIGHTS_FP8 = 1
+MK_WEIGHTS_MXFP4 = 2
+_WEIGHT_FORMATS = {"bf16": MK_WEIGHTS_BF16, "fp8": MK_WEIGHTS_FP8, "mxfp4": MK_WEIGHTS_MXFP4}
 MK_MAX_BATCH = 8
 MK_FLAG_TRACE = 1
 MK_FLAG_NO_PREFETCH = 2
@@ -166,7 +168,7 @@ def model_desc(wl, num_pages, max_pages_per_seq, max_batch=None, has_router_bias
                      wl.n_experts, wl.top_k, wl.expert_ffn, wl.vocab, wl.page_size, int(num_pages),
                      int(max_batch or wl.batch), int(max_pages_per_seq), int(bool(has_router_bias)),
                      int(bool(wl.lm_head)), float(wl.rope_theta), float(wl.rms_eps),
-                     MK_WEIGHTS_FP8 if getattr(wl, "weights", "bf16") == "fp8" else MK_WEIGHTS_BF16)
+                     _WEIGHT_FORMATS[getattr(wl, "weights", "bf16")])
 
 
 # ---------------------------------------------------------------- same-name wrappers

@@ -74,18 +74,26 @@ typedef struct {
   int32_t has_lm_head;       /* 0: the step ends at the residual stream (no logits) */
   float rope_theta;          /* RoPE base (rotate-half, full head_dim) */
   float rms_eps;             /* RMSNorm epsilon */
-  int32_t weight_format;     /* MK_WEIGHTS_BF16 or MK_WEIGHTS_FP8: the storage of every matrix */
+  int32_t weight_format;     /* MK_WEIGHTS_BF16, _FP8 or _MXFP4: the storage of every matrix */
 } mk_model_desc;
 
 /* Matrix storage (mk_model_desc.weight_format). The matrices are w_qkv, w_o, w_router, w_gate, w_up,
- * w_down and lm_head; embed, the norm gains and the KV cache are bf16 in both.
+ * w_down and lm_head; embed, the norm gains and the KV cache are bf16 in every format.
  *   MK_WEIGHTS_BF16  a matrix [R, C] is R rows of C bf16.
  *   MK_WEIGHTS_FP8   FP8 weights (P3 "Limitations and Future Plans": FP8/FP4 megakernels are the
  *                    pages' next step): a matrix [R, C] is R rows of C + 16 bytes - the row's C OCP
  *                    E4M3 codes, then its float32 scale and 12 zero bytes (each row 16-byte aligned);
- *                    weight = E4M3 value of the code * row scale. C must be a multiple of 16. */
+ *                    weight = E4M3 value of the code * row scale. C must be a multiple of 16.
+ *   MK_WEIGHTS_MXFP4 FP4 weights in the OCP microscaling format (MX v1.0 MXFP4): a matrix [R, C] is
+ *                    R rows of roundup16(C/2 + C/32) bytes - C/2 bytes of E2M1 codes (element 2i
+ *                    in the low nibble of byte i, element 2i + 1 in the high nibble), then the C/32
+ *                    E8M0 scale bytes of the row's blocks of 32 elements, then zero bytes; weight =
+ *                    E2M1 value of the code * 2^(scale - 127) (scale 255 is NaN). C must be a
+ *                    multiple of 32. The per-KV-group O projection flag is refused with FP8 and
+ *                    MXFP4 matrices alike. */
 #define MK_WEIGHTS_BF16 0
 #define MK_WEIGHTS_FP8 1
+#define MK_WEIGHTS_MXFP4 2
 
 /* Weight and KV-cache pointers (all device pointers; host arrays of per-layer pointers of length
  * n_layers). Layouts, row-major:

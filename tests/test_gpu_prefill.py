@@ -1,6 +1,6 @@
 """Prefill through the decode kernel on the GPU, against the oracle.
 
-* Small model (bf16 and FP8 matrices): a 19-position prompt (chunks of 8, 8 and 3 rows of one
+* Small model (bf16, FP8 and MXFP4 matrices): a 19-position prompt (chunks of 8, 8 and 3 rows of one
   sequence) written by ``mk_prefill`` from position 0 and after 21 cached positions, against ``oracle.prefill``: routing
   (near-tie replay as everywhere), the last position's logits, the K/V of every prompt position; then
   four greedy decode steps from the prompt's K/V equal the oracle's greedy decode.
@@ -89,7 +89,7 @@ def prompt_rows_check(dims, kd, vd, kv_ref, bt_row, positions, max_frac):
 
 
 @pytest.mark.parametrize("start", [0, 21], ids=["from-position-0", "after-21-cached"])
-@pytest.mark.parametrize("name", ["tiny", "tiny_fp8"])
+@pytest.mark.parametrize("name", ["tiny", "tiny_fp8", "tiny_mxfp4"])
 def test_tiny_prefill_then_decode(name, start):
     import oracle
     from decode_megakernel_03_amd import mk

@@ -37,6 +37,8 @@ CASES = [
     ("layer", [8193], 512),
     ("full_fp8", [8193], 512),
     ("full_b8_fp8", [8193] * 8, 512),
+    ("full_mxfp4", [8193], 512),
+    ("full_b8_mxfp4", [8193] * 8, 512),
 ]
 
 
