@@ -230,11 +230,11 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // down items per union slot (row blocks of W_down[e], DOWN_ROWS rows each) in queue mode
   const int down_items = steal ? (int)ceil_div(m.H, down_rows()) : 0;
   // O-projection row blocks of OPROJ_ROWS rows, queued between the gate/up and the down items (bf16
-  // matrices: the FP8 and MXFP4 kernel instances are compiled without them); the output rows then
+  // and MXFP4 matrices: the FP8 kernel instances are compiled without them); the output rows then
   // only add up
   constexpr int OPROJ_ROWS = 16;
   // (each row block once per group of 4 tokens: the kernel's items stage 4 tokens' attention)
-  const int oproj_items = steal && desc.weight_format == MK_WEIGHTS_BF16
+  const int oproj_items = steal && desc.weight_format != MK_WEIGHTS_FP8
                         ? (int)ceil_div(m.H, OPROJ_ROWS) * (int)ceil_div(B, 4) : 0;
   std::vector<int> c_queue(L, -1);
   for (int l = 0; l < L; ++l) {
@@ -686,10 +686,10 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
       const Task& t0 = *queue_tasks[0];
       const int qc = t0.w[D_A3], nq = t0.w[D_A1], slices = t0.w[D_A2], nfs = t0.w[D_A4], qd = t0.w[D_A5] & 0xffff;
       const int n_oi = t0.w[D_A5] >> 16;
-      // O-projection items: bf16 matrices only; they wait on counter qc - 1, which must be the
+      // O-projection items: bf16 and MXFP4 matrices only; they wait on counter qc - 1, which must be the
       // attention counter the layer's output rows name; every output row then adds o
       if (n_oi < 0 || n_oi > m.H * (int)ceil_div(P.B, 4) || n_oi % (int)ceil_div(P.B, 4) != 0 ||
-          (n_oi > 0 && P.desc.weight_format != MK_WEIGHTS_BF16)) {
+          (n_oi > 0 && P.desc.weight_format == MK_WEIGHTS_FP8)) {
         *why = fmt("layer %d: %d O-projection items", l, n_oi); return MK_ERR_INVALID_ARG;
       }
       for (const Task* tp : by_layer[l])

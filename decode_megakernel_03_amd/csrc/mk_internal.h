@@ -41,9 +41,9 @@ enum Op {
   OP_GATEUP = 3,  // static: a0 union slot, a1 f0, a2 nf, a3 -1: h = SiLU(W_gate n) * (W_up n) on rows f0..
                   // queue: a0 own sub-queue, a1 sub-queues, a2 slices per slot, a3 queue counter,
                   // a4 rows per slice, a5 down items per slot (0: none) | O-projection items << 16:
-                  // the layer's work queue holds every (slot, slice) gate/up item, then every (slot,
-                  // row block) down item, then the O-projection row blocks (they wait on the
-                  // attention counter, which is the queue counter - 1)
+                  // the layer's work queue holds every (slot, slice) gate/up item, then the
+                  // O-projection row blocks (they wait on the attention counter, which is the queue
+                  // counter - 1; bf16 and MXFP4 matrices), then every (slot, row block) down item
   OP_ATTN = 4,    // a0 b, a1 g, a2 k0, a3 k1 (-1 = to seq_len, the split holding the new token),
                   // a4 first partial of (b, g) in the layer, a5 split | nsplit << 16
   OP_OUT = 5,     // a0 row0, a1 nrows, a2 attention counter (KV group g's merges on sub-counters

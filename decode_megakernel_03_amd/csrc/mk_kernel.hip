@@ -569,6 +569,10 @@ __device__ __forceinline__ void compute_block(const WBuf<KD, NP, WF>& b, int blk
 // tokens). A pair is computed whole once its first token is in range (act_of must return readable
 // LDS for every t < TB); the second token's result is emitted only if it is in range. Same per-row
 // order of products.
+//
+// TG = 4 (MXFP4 rows that every token of the batch multiplies: lm_head, the O projection): groups of
+// up to 4 tokens share each conversion, under the same rule; bf16 and FP8 rows take the tokens one
+// at a time there (TG_ROWS below).
 template <int KD, int NP, int TB, int TG = 1, int WF = 0, class ActOf, class Emit>
 __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, WF>& b, int blk, int nrows, int ntok,
                                                      ActOf act_of, Emit emit) {
@@ -658,9 +662,64 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, WF>& b, 
     }
     return;
   }
-  if constexpr (WF == 2 && TB == OUT_OT) {
-    // (the output rows' O projection: conversions per token - sharing them across its OUT_OT tokens
-    // pushed the whole step kernel past its register budget)
+  if constexpr (WF == 2 && TG == 4) {
+    // MXFP4, tokens in groups of up to 4 (every token of the batch multiplies every row: lm_head, the
+    // O projection): each dword's conversions serve the group (a pass's 8 decoded weights meet each
+    // token's 8 activations). A group is computed whole once its first token is in range (act_of
+    // must return readable LDS for every t < TB); results are emitted for tokens in range only
+    constexpr int TQ = TB < 4 ? TB : 4;
+#pragma unroll
+    for (int t0 = 0; t0 < TB; t0 += TQ) {
+      if (t0 < ntok) {
+        float acc[TQ][NP];
+#pragma unroll
+        for (int t = 0; t < TQ; ++t)
+#pragma unroll
+          for (int i = 0; i < NP; ++i) acc[t][i] = 0.f;
+#pragma unroll
+        for (int j = 0; j < G::CPL; ++j) {
+          // (the chunk's 4 dwords in a loop that is not unrolled: unrolled, the compiler hoisted
+          // every conversion and activation read of the chunk ahead of the products)
+          u4 wv[NP];
+          float sc[NP];
+#pragma unroll
+          for (int i = 0; i < NP; ++i) { wv[i] = b.w[i][j]; sc[i] = b.s[i * G::CPL + j]; }
+          const f4* ab[TQ];
+#pragma unroll
+          for (int t = 0; t < TQ; ++t) ab[t] = reinterpret_cast<const f4*>(act_of(0, t0 + t) + EPC * lir + EPC * G::LPR * j);
+#pragma unroll 1
+          for (int k = 0; k < 4; ++k) {
+            f4 a0[TQ], a1[TQ];
+#pragma unroll
+            for (int t = 0; t < TQ; ++t) {
+              a0[t] = ab[t][2 * k];
+              a1[t] = ab[t][2 * k + 1];
+            }
+#pragma unroll
+            for (int i = 0; i < NP; ++i) {
+              const f8v d = dec8e2m1(wv[i].x, sc[i]);
+#pragma unroll
+              for (int t = 0; t < TQ; ++t) acc[t][i] = dot8f(d, a0[t], a1[t], acc[t][i]);
+              wv[i] = u4{wv[i].y, wv[i].z, wv[i].w, 0u};
+            }
+          }
+        }
+#pragma unroll
+        for (int t = 0; t < TQ; ++t) {
+#pragma unroll
+          for (int i = 0; i < NP; ++i) {
+            const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
+            const float v = wsum<G::LPR>(acc[t][i]);
+            if (lir == 0 && r < nrows && t0 + t < ntok) emit(r, t0 + t, v);
+          }
+        }
+      }
+    }
+    return;
+  }
+  if constexpr (WF == 2) {
+    // MXFP4, one token at a time (items whose rows few tokens share: expert gate/up and down); the
+    // chunk's dwords in a loop that is not unrolled, as above
 #pragma unroll
     for (int t = 0; t < TB; ++t) {
       if (t < ntok) {
@@ -671,13 +730,17 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, WF>& b, 
 #pragma unroll
         for (int j = 0; j < G::CPL; ++j) {
           const f4* ap = reinterpret_cast<const f4*>(a + EPC * G::LPR * j);
+          u4 wv[NP];
+          float sc[NP];
 #pragma unroll
+          for (int i = 0; i < NP; ++i) { wv[i] = b.w[i][j]; sc[i] = b.s[i * G::CPL + j]; }
+#pragma unroll 1
           for (int k = 0; k < 4; ++k) {
             const f4 a0 = ap[2 * k], a1 = ap[2 * k + 1];
 #pragma unroll
             for (int i = 0; i < NP; ++i) {
-              const u4 w = b.w[i][j];
-              acc[i] = dot8f(dec8e2m1(k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w, b.s[i * G::CPL + j]), a0, a1, acc[i]);
+              acc[i] = dot8f(dec8e2m1(wv[i].x, sc[i]), a0, a1, acc[i]);
+              wv[i] = u4{wv[i].y, wv[i].z, wv[i].w, 0u};
             }
           }
         }
@@ -685,51 +748,6 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, WF>& b, 
         for (int i = 0; i < NP; ++i) {
           const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
           const float v = wsum<G::LPR>(acc[i]);
-          if (lir == 0 && r < nrows) emit(r, t, v);
-        }
-      }
-    }
-    return;
-  }
-  if constexpr (WF == 2) {
-    // MXFP4: each dword's conversions serve every token of the batch (a pass's 8 decoded weights
-    // meet each token's 8 activations); per row and token the same order of products
-    float acc[TB][NP];
-#pragma unroll
-    for (int t = 0; t < TB; ++t)
-#pragma unroll
-      for (int i = 0; i < NP; ++i) acc[t][i] = 0.f;
-#pragma unroll
-    for (int j = 0; j < G::CPL; ++j) {
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        f4 a0[TB], a1[TB];
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-          if (t < ntok) {
-            const f4* ap = reinterpret_cast<const f4*>(act_of(0, t) + EPC * lir + EPC * G::LPR * j) + 2 * k;
-            a0[t] = ap[0]; a1[t] = ap[1];
-          } else {
-            a0[t] = f4{0.f, 0.f, 0.f, 0.f}; a1[t] = a0[t];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          const u4 w = b.w[i][j];
-          const f8v d = dec8e2m1(k == 0 ? w.x : k == 1 ? w.y : k == 2 ? w.z : w.w, b.s[i * G::CPL + j]);
-#pragma unroll
-          for (int t = 0; t < TB; ++t)
-            if (t < ntok) acc[t][i] = dot8f(d, a0[t], a1[t], acc[t][i]);
-        }
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < TB; ++t) {
-      if (t < ntok) {
-#pragma unroll
-        for (int i = 0; i < NP; ++i) {
-          const int r = ((blk * NP + i) * NWAVE + wave) * G::RPP + rip;
-          const float v = wsum<G::LPR>(acc[t][i]);
           if (lir == 0 && r < nrows) emit(r, t, v);
         }
       }
@@ -766,6 +784,10 @@ __device__ __forceinline__ void compute_block_shared(const WBuf<KD, NP, WF>& b, 
     }
   }
 }
+
+// token grouping of a GEMV whose rows every token of the step multiplies, besides QKV and router
+template <class S>
+constexpr int TG_ROWS = S::WF == 2 ? 4 : 1;
 
 // Stream `nrows` rows; block 0 may already be loaded into A (prefetched before a dependency wait).
 // The activations are shared by all rows (ActOf ignores its row argument).
@@ -1356,7 +1378,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
     __syncthreads();                     // every wave is done with the previous item's LDS
     stage_f4<OQT * AD>(sm, At, 4u * (b0 * AD), nt * AD);
     __syncthreads();
-    gemv_stream<S::kw(AD), 1, OQT, 1, S::WF>(A, true, nr, nt, orow,
+    gemv_stream<S::kw(AD), 1, OQT, TG_ROWS<S>, S::WF>(A, true, nr, nt, orow,
         [&](int r, int t) { return sm + (size_t)t * AD; },
         [&](int r, int t, float v) { stc(Ob, 4u * ((b0 + t) * H + r0 + r), v); });
     __syncthreads();                     // the staging area is free for the next item
@@ -1413,9 +1435,9 @@ __device__ __forceinline__ bool op_gateup(int task) {
         const int i2 = i - n_gu - n_oi, u = i2 / qd;
         if (!run_down(u, i2 - u * qd, slices_c)) return false;
       } else {
-        // (compiled for bf16 matrices only: in the FP8 instances the extra GEMV path costs 15 more
-        // spilled registers, and the schedule gives them no such items)
-        if constexpr (!S::WF) {
+        // (compiled for bf16 and MXFP4 matrices: in the FP8 instances the extra GEMV path costs 15
+        // more spilled registers, and the schedule gives them no such items)
+        if constexpr (S::WF != 1) {
           if (!run_oproj(i - n_gu, orows, ntg)) return false;
         } else {
           return false;                  // (the host's validator refuses such a schedule)
@@ -2278,7 +2300,7 @@ __device__ __forceinline__ bool op_out_batch(int task) {
       stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
       __syncthreads();
       if (b0 == 0) MARK(2);
-      compute_block_shared<S::kw(AD), NPO, OUT_OT, 1, S::WF>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
+      compute_block_shared<S::kw(AD), NPO, OUT_OT, TG_ROWS<S>, S::WF>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
                                             [&](int r, int t, float v) { o_s[t * OUT_MAXR + r] = v; });
       __syncthreads();
       if (tx < nt * nrows) {
@@ -2363,7 +2385,7 @@ __device__ __forceinline__ bool op_out_batch(int task) {
     stage_f4<OUT_OT * AD>(a_s, At, 4u * (b0 * AD), nt * AD);
     __syncthreads();
     if (b0 == 0) MARK(2);
-    compute_block_shared<S::kw(AD), NPO, OUT_OT, 1, S::WF>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
+    compute_block_shared<S::kw(AD), NPO, OUT_OT, TG_ROWS<S>, S::WF>(WO, 0, nrows, nt, [&](int r, int t) { return a_s + t * AD; },
                                           [&](int r, int t, float v) { o_s[t * OUT_MAXR + r] = v; });
     __syncthreads();
     if (tx < nt * nrows) {
@@ -2406,7 +2428,7 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   for (int t = 0; t < TB; ++t) { bv[t] = -INFINITY; bi[t] = 0x7fffffff; }
   float* logits = p.logits;
   const int V = p.V;
-  gemv_stream<KW, NP, TB, 1, S::WF>(A, pre, nrows, p.B, rowptr,
+  gemv_stream<KW, NP, TB, TG_ROWS<S>, S::WF>(A, pre, nrows, p.B, rowptr,
       [&](int r, int t) { return sm + (size_t)t * H; },
       [&](int r, int t, float v) {
         const int row = row0 + r;
