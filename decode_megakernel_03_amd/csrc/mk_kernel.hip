@@ -807,12 +807,110 @@ __device__ __forceinline__ void gemv_stream(WBuf<KD, NP, WF>& A, bool a_loaded, 
   }
 }
 
+// ------------------------------------------------------------------------------ matrix-core rows
+//
+// bf16 rows times the step's tokens on the matrix cores (batch > 1, bf16 matrices; P3 "Key
+// Technologies and Architecture": the dense contractions on the tensor cores). The activations stay
+// fp32 in LDS; each lane splits the 8 it feeds into three bf16 parts, hi = bf16(x), lo = bf16(x - hi),
+// lo2 = bf16(x - hi - lo) (each difference exact), which hold x to 2^-27 of its magnitude, so a row's
+// products carry the error of an fp32 sum, as the vector-ALU form does. A row block is 16 rows; each
+// wave covers a quarter of the inputs with v_mfma_f32_16x16x32_bf16 (A = 16 rows x 32 inputs, one
+// 16-byte load per lane). Two products per 32-input block: B1's column c is token c % 8's hi part
+// (c < 8) or lo part (c >= 8), B2's is its lo2 part (c < 8) or zero, accumulated in one chain. The
+// four waves' 16 x 16 sums are added in LDS in wave order, then column t + column t + 8.
+
+typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+
+template <class S>
+struct MRows {
+  static constexpr int KB = S::H / 32;        // 32-input blocks of a row
+  static constexpr int KBW = KB / NWAVE;      // blocks per wave
+  static constexpr int AS = S::H + 4;         // LDS row stride of the staged activations (floats;
+                                              // the pad puts the 8 tokens' reads in distinct banks)
+  static constexpr int RED = MAXB * AS;       // then [NWAVE][16][16] float partial sums
+  static constexpr int END = RED + NWAVE * 256;
+  static_assert(KB % NWAVE == 0 && AS % 4 == 0, "");
+  u4 a[KBW];
+};
+
+// A operand of row block rb (rows rb*16 ..): lane l holds row l % 16, inputs 8 (l / 16) .. + 7 of
+// each of its wave's 32-input blocks; rows at or past nrows are zeros
+template <class S, class RowPtr>
+__device__ __forceinline__ void mrows_load(MRows<S>& A, int rb, int nrows, RowPtr rowptr) {
+  using M = MRows<S>;
+  const int lane = tid() & 63, wave = __builtin_amdgcn_readfirstlane(tid() >> 6);
+  const int r = rb * 16 + (lane & 15);
+  if (r < nrows) {
+    const uint16_t* src = rowptr(r) + 32 * M::KBW * wave + 8 * (lane >> 4);
+#pragma unroll
+    for (int kb = 0; kb < M::KBW; ++kb) A.a[kb] = ldw(src + 32 * kb);
+  } else {
+#pragma unroll
+    for (int kb = 0; kb < M::KBW; ++kb) A.a[kb] = u4{0u, 0u, 0u, 0u};
+  }
+}
+
+// two bf16 of a float pair, packed (round to nearest even)
+__device__ __forceinline__ uint32_t pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2{a, b}, bf2v));
+}
+
+// Products of row block rb with the staged tokens (act: [MAXB][AS] fp32); emit(r, t, value) for rows
+// r < nrows and tokens t < ntok, on threads 0..127 (thread 8 i + t: row rb*16 + i, token t). Ends
+// with a barrier.
+template <class S, class Emit>
+__device__ __forceinline__ void mrows_compute(const MRows<S>& A, int rb, int nrows, int ntok, const float* act,
+                                              float* red, Emit emit) {
+  using M = MRows<S>;
+  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
+  const int col = lane & 15, kq = lane >> 4;
+  const bool first = col < 8;
+  const float* xs = act + (col & 7) * M::AS + 32 * M::KBW * wave + 8 * kq;
+  f4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kb = 0; kb < M::KBW; ++kb) {
+    const f4 x0 = *reinterpret_cast<const f4*>(xs + 32 * kb), x1 = *reinterpret_cast<const f4*>(xs + 32 * kb + 4);
+    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t b1[4], b2[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const uint32_t h = pk_bf16(x[2 * m], x[2 * m + 1]);
+      const float r0 = x[2 * m] - bf_lo(h), r1 = x[2 * m + 1] - bf_hi(h);
+      const uint32_t l = pk_bf16(r0, r1);
+      const uint32_t l2 = pk_bf16(r0 - bf_lo(l), r1 - bf_hi(l));
+      b1[m] = first ? h : l;
+      b2[m] = first ? l2 : 0u;
+    }
+    const bf8v a = __builtin_bit_cast(bf8v, A.a[kb]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf8v, u4{b1[0], b1[1], b1[2], b1[3]}), acc, 0, 0, 0);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf8v, u4{b2[0], b2[1], b2[2], b2[3]}), acc, 0, 0, 0);
+  }
+  // (the product's lane holds column col, rows 4 kq .. 4 kq + 3)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * kq + i) * 16 + col] = acc[i];
+  __syncthreads();
+  if (tx < 128) {
+    const int i = tx >> 3, t = tx & 7;
+    float a0 = red[i * 16 + t], a1 = red[i * 16 + 8 + t];
+#pragma unroll
+    for (int w = 1; w < NWAVE; ++w) {
+      a0 += red[(w * 16 + i) * 16 + t];
+      a1 += red[(w * 16 + i) * 16 + 8 + t];
+    }
+    const int r = rb * 16 + i;
+    if (r < nrows && t < ntok) emit(r, t, a0 + a1);
+  }
+  __syncthreads();
+}
+
 // ------------------------------------------------------------------------------ norm staging
 
 // act[t][H] = RMSNorm(x_l[b_t]) * gain for the listed tokens (P1: one shared normed input per
 // layer). x_0 is the token's embedding row; x_l (l >= 1) comes from the previous layer's OUT
 // tasks. One wave per token: each lane sums H/64 squares, then a wave tree.
-template <class S>
+// AS: the row stride of act (floats; the matrix-core form pads its rows).
+template <class S, int AS = S::H>
 __device__ __forceinline__ void stage_norm(CParams& p, int l, const int* toks, int ntok, const uint16_t* gain,
                            float* act, int task) {
   constexpr int H = S::H;
@@ -861,7 +959,7 @@ __device__ __forceinline__ void stage_norm(CParams& p, int l, const int* toks, i
       o.y = (v[4 * k + 1] * inv) * gg[1];
       o.z = (v[4 * k + 2] * inv) * gg[2];
       o.w = (v[4 * k + 3] * inv) * gg[3];
-      *reinterpret_cast<f4*>(act + (size_t)t * H + 4 * lane + 256 * k) = o;
+      *reinterpret_cast<f4*>(act + (size_t)t * AS + 4 * lane + 256 * k) = o;
     }
   }
   __syncthreads();
@@ -983,18 +1081,32 @@ __device__ __forceinline__ bool op_qkv(int task) {
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_qkv + (size_t)(row0 + r) * S::rw(H); };
-  WBuf<KW, NP, S::WF> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
-  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  if (tid() < MAXB) ctl.toks[tid()] = tid();
-  __syncthreads();
-  stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
-  MARK(0);
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + (size_t)T.layer * MAXB * S::QKVR);
-  gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::WF>(A, pre, nrows, p.B, rowptr,
-      [&](int r, int t) { return sm + (size_t)t * H; },
-      [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); });
+  auto emit = [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); };
+  if constexpr (TB > 1 && S::WF == 0) {          // several tokens, bf16 rows: the matrix cores
+    MRows<S> A;
+    if (pre) mrows_load<S>(A, 0, nrows, rowptr);
+    if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+    if (tid() < MAXB) ctl.toks[tid()] = tid();
+    __syncthreads();
+    stage_norm<S, MRows<S>::AS>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
+    MARK(0);
+    for (int rb = 0; rb * 16 < nrows; ++rb) {
+      if (rb > 0 || !pre) mrows_load<S>(A, rb, nrows, rowptr);
+      mrows_compute<S>(A, rb, nrows, p.B, sm, sm + MRows<S>::RED, emit);
+    }
+  } else {
+    WBuf<KW, NP, S::WF> A;
+    if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
+    if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+    if (tid() < MAXB) ctl.toks[tid()] = tid();
+    __syncthreads();
+    stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
+    MARK(0);
+    gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::WF>(A, pre, nrows, p.B, rowptr,
+        [&](int r, int t) { return sm + (size_t)t * H; }, emit);
+  }
   MARK(1);
   drain_t(p);
   if constexpr (VAR == 2) {
@@ -1147,22 +1259,36 @@ __device__ __forceinline__ bool op_router(int task) {
   const auto& Lp = cst(p.layers)[T.layer];
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return Lp.w_router + (size_t)(row0 + r) * S::rw(H); };
-  WBuf<KW, NP, S::WF> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
-  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  if (tid() < MAXB) ctl.toks[tid()] = tid();
-  __syncthreads();
-  stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
-  MARK(0);
   const __amdgpu_buffer_rsrc_t R = rsrc(p.rlog + (size_t)T.layer * MAXB * E);
   const float* bias = p.has_bias ? Lp.router_bias : nullptr;
-  gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::WF>(A, pre, nrows, p.B, rowptr,
-      [&](int r, int t) { return sm + (size_t)t * H; },
-      [&](int r, int t, float v) {
-        const int e = row0 + r;
-        stc(R, 4u * (t * E + e), bias ? v + bias[e] : v);
-      });
+  auto emit = [&](int r, int t, float v) {
+    const int e = row0 + r;
+    stc(R, 4u * (t * E + e), bias ? v + bias[e] : v);
+  };
+  if constexpr (TB > 1 && S::WF == 0) {          // several tokens, bf16 rows: the matrix cores
+    MRows<S> A;
+    if (pre) mrows_load<S>(A, 0, nrows, rowptr);
+    if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+    if (tid() < MAXB) ctl.toks[tid()] = tid();
+    __syncthreads();
+    stage_norm<S, MRows<S>::AS>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
+    MARK(0);
+    for (int rb = 0; rb * 16 < nrows; ++rb) {
+      if (rb > 0 || !pre) mrows_load<S>(A, rb, nrows, rowptr);
+      mrows_compute<S>(A, rb, nrows, p.B, sm, sm + MRows<S>::RED, emit);
+    }
+  } else {
+    WBuf<KW, NP, S::WF> A;
+    if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
+    if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+    if (tid() < MAXB) ctl.toks[tid()] = tid();
+    __syncthreads();
+    stage_norm<S>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
+    MARK(0);
+    gemv_stream<KW, NP, TB, (TB > 1 ? 2 : 1), S::WF>(A, pre, nrows, p.B, rowptr,
+        [&](int r, int t) { return sm + (size_t)t * H; }, emit);
+  }
   MARK(1);
   const uint32_t old = signal(p, ctl, T.sig, true);
   MARK(2);
@@ -1501,7 +1627,8 @@ struct OutLds {   // LDS layout of a batched output task, in floats
 // attention buffers, OUT staging, routing scratch), then the step's RoPE table.
 template <class S>
 __host__ __device__ constexpr int rope_off(int tb) {
-  const int act = tb * S::H + tb * 2 * 64 + 1024;
+  int act = tb * S::H + tb * 2 * 64 + 1024;
+  if (tb > 1 && MRows<S>::END + 256 > act) act = MRows<S>::END + 256;   // matrix-core staging + argmax
   const int att = AttnLds<S>::END;
   const int out1 = S::AD + S::K * S::F + OUT_MAXR + S::K * OUT_MAXR + 2 * MAXB * OUT_MAXR;
   const int out = tb > 1 && OutLds<S>::END > out1 ? OutLds<S>::END : out1;
@@ -2415,52 +2542,98 @@ __device__ __forceinline__ bool op_lmhead(int task) {
   constexpr int H = S::H, KW = S::kw(H), NP = (Geo<KW>::CPL >= 4) ? (TB > 1 ? 4 : 2) : 4, RPP = Geo<KW>::RPP;
   const int row0 = T.a0, nrows = T.a1;
   auto rowptr = [&](int r) { return p.lm_head + (size_t)(row0 + r) * S::rw(H); };
-  WBuf<KW, NP, S::WF> A;
   const bool pre = !(p.flags & 2);
-  if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
-  if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
-  if (tid() < MAXB) ctl.toks[tid()] = tid();
-  __syncthreads();
-  stage_norm<S>(p, p.L, ctl.toks, p.B, p.final_norm, sm, T.id);
-  float bv[TB];
-  int bi[TB];
-#pragma unroll
-  for (int t = 0; t < TB; ++t) { bv[t] = -INFINITY; bi[t] = 0x7fffffff; }
   float* logits = p.logits;
   const int V = p.V;
-  gemv_stream<KW, NP, TB, TG_ROWS<S>, S::WF>(A, pre, nrows, p.B, rowptr,
-      [&](int r, int t) { return sm + (size_t)t * H; },
-      [&](int r, int t, float v) {
-        const int row = row0 + r;
-        if (logits) __builtin_nontemporal_store(v, logits + (size_t)t * V + row);
-#pragma unroll
-        for (int tt = 0; tt < TB; ++tt)
-          if (tt == t && (v > bv[tt] || (v == bv[tt] && row < bi[tt]))) { bv[tt] = v; bi[tt] = row; }
-      });
-  // combine the emitting lanes (lir == 0) of every wave, then one atomic per token
-  float* cv = sm + (size_t)TB * H;                                 // [NWAVE * RPP][TB]
-  int* ci = reinterpret_cast<int*>(cv + NWAVE * RPP * TB);
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
-  if (lane % Geo<KW>::LPR == 0) {
-    const int slot = wave * RPP + lane / Geo<KW>::LPR;
-#pragma unroll
-    for (int t = 0; t < TB; ++t) { cv[slot * TB + t] = bv[t]; ci[slot * TB + t] = bi[t]; }
-  }
-  __syncthreads();
-  if (tid() < p.B) {
-    const int t = tid();
-    float best = -INFINITY;
-    int besti = 0x7fffffff;
-    for (int s = 0; s < NWAVE * RPP; ++s) {
-      const float v = cv[s * TB + t];
-      const int i = ci[s * TB + t];
-      if (v > best || (v == best && i < besti)) { best = v; besti = i; }
-    }
+  // the running greedy argmax key of token t (first index of the maximum) into p.amax[t]
+  auto publish = [&](int t, float best, int besti) {
     if (besti != 0x7fffffff) {
       uint32_t u = __float_as_uint(best);
       u = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
       const unsigned long long key = ((unsigned long long)u << 32) | (0xffffffffu - (uint32_t)besti);
       __hip_atomic_fetch_max(p.amax + t, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  };
+  if constexpr (TB > 1 && S::WF == 0) {          // several tokens, bf16 rows: the matrix cores
+    MRows<S> A, A2;
+    if (pre) mrows_load<S>(A, 0, nrows, rowptr);
+    if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+    if (tid() < MAXB) ctl.toks[tid()] = tid();
+    __syncthreads();
+    stage_norm<S, MRows<S>::AS>(p, p.L, ctl.toks, p.B, p.final_norm, sm, T.id);
+    if (!pre) mrows_load<S>(A, 0, nrows, rowptr);
+    // thread 8 i + t sees rows i, i + 16, ... of token t, in ascending order
+    float bv = -INFINITY;
+    int bi = 0x7fffffff;
+    auto em = [&](int r, int t, float v) {
+      const int row = row0 + r;
+      if (logits) __builtin_nontemporal_store(v, logits + (size_t)t * V + row);
+      if (v > bv || (v == bv && row < bi)) { bv = v; bi = row; }
+    };
+    const int nblk = (nrows + 15) / 16;
+    float* red = sm + MRows<S>::RED;
+    for (int rb = 0; rb < nblk; rb += 2) {
+      if (rb + 1 < nblk) mrows_load<S>(A2, rb + 1, nrows, rowptr);
+      mrows_compute<S>(A, rb, nrows, p.B, sm, red, em);
+      if (rb + 1 < nblk) {
+        if (rb + 2 < nblk) mrows_load<S>(A, rb + 2, nrows, rowptr);
+        mrows_compute<S>(A2, rb + 1, nrows, p.B, sm, red, em);
+      }
+    }
+    float* cv = sm + MRows<S>::END;                 // [16][8]
+    int* ci = reinterpret_cast<int*>(cv + 128);
+    if (tx < 128) { cv[tx] = bv; ci[tx] = bi; }
+    __syncthreads();
+    if (tx < p.B) {
+      float best = -INFINITY;
+      int besti = 0x7fffffff;
+      for (int i = 0; i < 16; ++i) {
+        const float v = cv[8 * i + tx];
+        const int ii = ci[8 * i + tx];
+        if (v > best || (v == best && ii < besti)) { best = v; besti = ii; }
+      }
+      publish(tx, best, besti);
+    }
+  } else {
+    WBuf<KW, NP, S::WF> A;
+    if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
+    if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
+    if (tid() < MAXB) ctl.toks[tid()] = tid();
+    __syncthreads();
+    stage_norm<S>(p, p.L, ctl.toks, p.B, p.final_norm, sm, T.id);
+    float bv[TB];
+    int bi[TB];
+#pragma unroll
+    for (int t = 0; t < TB; ++t) { bv[t] = -INFINITY; bi[t] = 0x7fffffff; }
+    gemv_stream<KW, NP, TB, TG_ROWS<S>, S::WF>(A, pre, nrows, p.B, rowptr,
+        [&](int r, int t) { return sm + (size_t)t * H; },
+        [&](int r, int t, float v) {
+          const int row = row0 + r;
+          if (logits) __builtin_nontemporal_store(v, logits + (size_t)t * V + row);
+#pragma unroll
+          for (int tt = 0; tt < TB; ++tt)
+            if (tt == t && (v > bv[tt] || (v == bv[tt] && row < bi[tt]))) { bv[tt] = v; bi[tt] = row; }
+        });
+    // combine the emitting lanes (lir == 0) of every wave, then one atomic per token
+    float* cv = sm + (size_t)TB * H;                                 // [NWAVE * RPP][TB]
+    int* ci = reinterpret_cast<int*>(cv + NWAVE * RPP * TB);
+    if (lane % Geo<KW>::LPR == 0) {
+      const int slot = wave * RPP + lane / Geo<KW>::LPR;
+#pragma unroll
+      for (int t = 0; t < TB; ++t) { cv[slot * TB + t] = bv[t]; ci[slot * TB + t] = bi[t]; }
+    }
+    __syncthreads();
+    if (tid() < p.B) {
+      const int t = tid();
+      float best = -INFINITY;
+      int besti = 0x7fffffff;
+      for (int s = 0; s < NWAVE * RPP; ++s) {
+        const float v = cv[s * TB + t];
+        const int i = ci[s * TB + t];
+        if (v > best || (v == best && i < besti)) { best = v; besti = i; }
+      }
+      publish(t, best, besti);
     }
   }
   signal(p, ctl, T.sig, false);
