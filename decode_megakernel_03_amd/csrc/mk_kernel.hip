@@ -23,6 +23,7 @@
 #include <stdint.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "mk_internal.h"
 #include "mk_launch.h"
@@ -809,45 +810,73 @@ __device__ __forceinline__ void gemv_stream(WBuf<KD, NP, WF>& A, bool a_loaded, 
 
 // ------------------------------------------------------------------------------ matrix-core rows
 //
-// bf16 rows times the step's tokens on the matrix cores (batch > 1, bf16 matrices; P3 "Key
-// Technologies and Architecture": the dense contractions on the tensor cores). The activations stay
-// fp32 in LDS; each lane splits the 8 it feeds into three bf16 parts, hi = bf16(x), lo = bf16(x - hi),
-// lo2 = bf16(x - hi - lo) (each difference exact), which hold x to 2^-27 of its magnitude, so a row's
-// products carry the error of an fp32 sum, as the vector-ALU form does. A row block is 16 rows; each
-// wave covers a quarter of the inputs with v_mfma_f32_16x16x32_bf16 (A = 16 rows x 32 inputs, one
-// 16-byte load per lane). Two products per 32-input block: B1's column c is token c % 8's hi part
-// (c < 8) or lo part (c >= 8), B2's is its lo2 part (c < 8) or zero, accumulated in one chain. The
-// four waves' 16 x 16 sums are added in LDS in wave order, then column t + column t + 8.
+// Rows of a matrix times the step's tokens on the matrix cores (batch > 1; P3 "Key Technologies and
+// Architecture": the dense contractions on the tensor cores), with v_mfma_f32_16x16x32_bf16.
+//
+// A operand: a row block is 16 rows; each wave covers a quarter of the inputs. Lane l holds row
+// l % 16 and, per load, EPL consecutive inputs of it: lane group q = l / 16 the q-th EPL inputs of
+// the load's span of 4 EPL. A product takes 8 of each lane's inputs (the k index of the product
+// is a permutation of the inputs, the same for both operands). bf16 rows: 8 inputs per 16-byte
+// load. FP8 rows: 16 codes per 16-byte load, converted to bf16 (exact: E4M3 values have 4
+// significant bits), the row's scale applied to the finished sum. MXFP4 rows: 16 codes per 8-byte
+// load, converted to bf16 with their block's scale (exact: a 2-bit significand times a power of two).
+//
+// B operand: the activations stay fp32 in LDS; each lane splits the 8 it feeds into three bf16
+// parts, hi = bf16(x), lo = bf16(x - hi), lo2 = bf16(x - hi - lo): each difference is exact and x is
+// their exact sum, so the products are exact and a row carries the error of an fp32 sum, as the
+// vector-ALU form does. Two products per 8 inputs in one accumulator chain: column c of the first is
+// token c % 8's hi part (c < 8) or lo part (c >= 8), of the second its lo2 part (c < 8) or zero.
+// The four waves' 16 x 16 sums are added in LDS in wave order, then column t + column t + 8.
 
 typedef __bf16 bf8v __attribute__((ext_vector_type(8)));
 typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
 template <class S>
 struct MRows {
-  static constexpr int KB = S::H / 32;        // 32-input blocks of a row
-  static constexpr int KBW = KB / NWAVE;      // blocks per wave
+  static constexpr int WF = S::WF;
+  static constexpr int EPL = WF == 0 ? 8 : 16;     // inputs of a lane per load
+  static constexpr int SPAN = 4 * EPL;             // inputs of a wave per load
+  static constexpr int NL = S::H / NWAVE / SPAN;   // loads per wave and row block
   static constexpr int AS = S::H + 4;         // LDS row stride of the staged activations (floats;
                                               // the pad puts the 8 tokens' reads in distinct banks)
   static constexpr int RED = MAXB * AS;       // then [NWAVE][16][16] float partial sums
-  static constexpr int END = RED + NWAVE * 256;
-  static_assert(KB % NWAVE == 0 && AS % 4 == 0, "");
-  u4 a[KBW];
+  static constexpr int SC = RED + NWAVE * 256;   // then [16] row scales (FP8)
+  static constexpr int END = SC + 16;
+  static_assert((S::H / NWAVE) % SPAN == 0 && AS % 4 == 0, "");
+  typedef typename std::conditional<WF == 2, u2, u4>::type LT;
+  LT a[NL];
+  float s[WF == 2 ? NL : 1];                  // MXFP4: each load's block scale; FP8: the row's scale
 };
 
-// A operand of row block rb (rows rb*16 ..): lane l holds row l % 16, inputs 8 (l / 16) .. + 7 of
-// each of its wave's 32-input blocks; rows at or past nrows are zeros
+// A operand of row block rb (rows rb*16 ..); rows at or past nrows are zeros
 template <class S, class RowPtr>
 __device__ __forceinline__ void mrows_load(MRows<S>& A, int rb, int nrows, RowPtr rowptr) {
   using M = MRows<S>;
   const int lane = tid() & 63, wave = __builtin_amdgcn_readfirstlane(tid() >> 6);
   const int r = rb * 16 + (lane & 15);
+  const int e0 = S::H / NWAVE * wave + M::EPL * (lane >> 4);     // first input of the lane's load 0
   if (r < nrows) {
-    const uint16_t* src = rowptr(r) + 32 * M::KBW * wave + 8 * (lane >> 4);
+    const uint16_t* row = rowptr(r);
+    const uint8_t* rb8 = reinterpret_cast<const uint8_t*>(row);
 #pragma unroll
-    for (int kb = 0; kb < M::KBW; ++kb) A.a[kb] = ldw(src + 32 * kb);
+    for (int j = 0; j < M::NL; ++j) {
+      const int e = e0 + M::SPAN * j;
+      if constexpr (M::WF == 0) A.a[j] = ldw(row + e);
+      if constexpr (M::WF == 1) A.a[j] = ldw(rb8 + e);
+      if constexpr (M::WF == 2) {
+        A.a[j] = __builtin_nontemporal_load(reinterpret_cast<const u2*>(rb8 + e / 2));
+        A.s[j] = e8m0(rb8[S::H / 2 + e / 32]);
+      }
+    }
+    if constexpr (M::WF == 1) A.s[0] = *reinterpret_cast<const float*>(rb8 + S::H);
   } else {
 #pragma unroll
-    for (int kb = 0; kb < M::KBW; ++kb) A.a[kb] = u4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < M::NL; ++j) {
+      if constexpr (M::WF == 2) { A.a[j] = u2{0u, 0u}; A.s[j] = 0.f; }
+      else A.a[j] = u4{0u, 0u, 0u, 0u};
+    }
+    if constexpr (M::WF == 1) A.s[0] = 0.f;
   }
 }
 
@@ -866,29 +895,62 @@ __device__ __forceinline__ void mrows_compute(const MRows<S>& A, int rb, int nro
   const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
   const int col = lane & 15, kq = lane >> 4;
   const bool first = col < 8;
-  const float* xs = act + (col & 7) * M::AS + 32 * M::KBW * wave + 8 * kq;
+  const float* xs = act + (col & 7) * M::AS + S::H / NWAVE * wave + M::EPL * kq;
   f4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int kb = 0; kb < M::KBW; ++kb) {
-    const f4 x0 = *reinterpret_cast<const f4*>(xs + 32 * kb), x1 = *reinterpret_cast<const f4*>(xs + 32 * kb + 4);
-    const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-    uint32_t b1[4], b2[4];
+  for (int j = 0; j < M::NL; ++j) {
+    u4 af[M::EPL / 8];                 // the lane's inputs as bf16, 8 per product
+    if constexpr (M::WF == 0) af[0] = A.a[j];
+    if constexpr (M::WF == 1) {
+      const uint32_t w[4] = {A.a[j].x, A.a[j].y, A.a[j].z, A.a[j].w};
+      uint32_t d[8];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const uint32_t h = pk_bf16(x[2 * m], x[2 * m + 1]);
-      const float r0 = x[2 * m] - bf_lo(h), r1 = x[2 * m + 1] - bf_hi(h);
-      const uint32_t l = pk_bf16(r0, r1);
-      const uint32_t l2 = pk_bf16(r0 - bf_lo(l), r1 - bf_hi(l));
-      b1[m] = first ? h : l;
-      b2[m] = first ? l2 : 0u;
+      for (int m = 0; m < 4; ++m) {
+        d[2 * m] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[m], 1.0f, false));
+        d[2 * m + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w[m], 1.0f, true));
+      }
+      af[0] = u4{d[0], d[1], d[2], d[3]};
+      af[1] = u4{d[4], d[5], d[6], d[7]};
     }
-    const bf8v a = __builtin_bit_cast(bf8v, A.a[kb]);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf8v, u4{b1[0], b1[1], b1[2], b1[3]}), acc, 0, 0, 0);
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf8v, u4{b2[0], b2[1], b2[2], b2[3]}), acc, 0, 0, 0);
+    if constexpr (M::WF == 2) {
+      const uint32_t w[2] = {A.a[j].x, A.a[j].y};
+      const float sc = A.s[j];
+      uint32_t d[8];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        d[4 * m] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[m], sc, 0));
+        d[4 * m + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[m], sc, 1));
+        d[4 * m + 2] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[m], sc, 2));
+        d[4 * m + 3] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w[m], sc, 3));
+      }
+      af[0] = u4{d[0], d[1], d[2], d[3]};
+      af[1] = u4{d[4], d[5], d[6], d[7]};
+    }
+#pragma unroll
+    for (int m = 0; m < M::EPL / 8; ++m) {
+      const float* xp = xs + M::SPAN * j + 8 * m;
+      const f4 x0 = *reinterpret_cast<const f4*>(xp), x1 = *reinterpret_cast<const f4*>(xp + 4);
+      const float x[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t b1[4], b2[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t h = pk_bf16(x[2 * q], x[2 * q + 1]);
+        const float r0 = x[2 * q] - bf_lo(h), r1 = x[2 * q + 1] - bf_hi(h);
+        const uint32_t l = pk_bf16(r0, r1);
+        const uint32_t l2 = pk_bf16(r0 - bf_lo(l), r1 - bf_hi(l));
+        b1[q] = first ? h : l;
+        b2[q] = first ? l2 : 0u;
+      }
+      const bf8v a = __builtin_bit_cast(bf8v, af[m]);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf8v, u4{b1[0], b1[1], b1[2], b1[3]}), acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, __builtin_bit_cast(bf8v, u4{b2[0], b2[1], b2[2], b2[3]}), acc, 0, 0, 0);
+    }
   }
   // (the product's lane holds column col, rows 4 kq .. 4 kq + 3)
 #pragma unroll
   for (int i = 0; i < 4; ++i) red[(wave * 16 + 4 * kq + i) * 16 + col] = acc[i];
+  if constexpr (M::WF == 1)
+    if (wave == 0 && kq == 0) red[M::SC - M::RED + col] = A.s[0];     // row col's scale
   __syncthreads();
   if (tx < 128) {
     const int i = tx >> 3, t = tx & 7;
@@ -898,8 +960,10 @@ __device__ __forceinline__ void mrows_compute(const MRows<S>& A, int rb, int nro
       a0 += red[(w * 16 + i) * 16 + t];
       a1 += red[(w * 16 + i) * 16 + 8 + t];
     }
+    float v = a0 + a1;
+    if constexpr (M::WF == 1) v *= red[M::SC - M::RED + i];
     const int r = rb * 16 + i;
-    if (r < nrows && t < ntok) emit(r, t, a0 + a1);
+    if (r < nrows && t < ntok) emit(r, t, v);
   }
   __syncthreads();
 }
@@ -1084,7 +1148,7 @@ __device__ __forceinline__ bool op_qkv(int task) {
   const bool pre = !(p.flags & 2);
   const __amdgpu_buffer_rsrc_t Q = rsrc(p.qkv + (size_t)T.layer * MAXB * S::QKVR);
   auto emit = [&](int r, int t, float v) { stc(Q, 4u * (t * S::QKVR + row0 + r), v); };
-  if constexpr (TB > 1 && S::WF == 0) {          // several tokens, bf16 rows: the matrix cores
+  if constexpr (TB > 1) {                        // several tokens: the matrix cores
     MRows<S> A;
     if (pre) mrows_load<S>(A, 0, nrows, rowptr);
     if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
@@ -1266,7 +1330,7 @@ __device__ __forceinline__ bool op_router(int task) {
     const int e = row0 + r;
     stc(R, 4u * (t * E + e), bias ? v + bias[e] : v);
   };
-  if constexpr (TB > 1 && S::WF == 0) {          // several tokens, bf16 rows: the matrix cores
+  if constexpr (TB > 1) {                        // several tokens: the matrix cores
     MRows<S> A;
     if (pre) mrows_load<S>(A, 0, nrows, rowptr);
     if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
@@ -2555,7 +2619,7 @@ __device__ __forceinline__ bool op_lmhead(int task) {
       __hip_atomic_fetch_max(p.amax + t, key, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   };
-  if constexpr (TB > 1 && S::WF == 0) {          // several tokens, bf16 rows: the matrix cores
+  if constexpr (TB > 1) {                        // several tokens: the matrix cores
     MRows<S> A, A2;
     if (pre) mrows_load<S>(A, 0, nrows, rowptr);
     if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
