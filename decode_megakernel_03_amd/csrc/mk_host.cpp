@@ -114,8 +114,6 @@ struct mk_plan {
   std::vector<int32_t> qoff;      // n_workers + 1
   std::vector<int64_t> bytes;     // cost model, per task (queue order)
   int n_ctr = 0, done_ctr = 0, parts_per_layer = 0, n_attn = 0;
-  int att_sig = 1;                // signals on a layer's attention counter per (sequence, KV group)
-  bool split_merge = false;       // the last split of each (sequence, KV group) merges (no merge tasks)
   std::vector<int> capacity;      // per sequence: largest seq_len the schedule can serve
   // most rows one sequence holds in a step (its consecutive positions), hence the most positions a
   // row advances per step; above 1 the QKV tasks publish the step's K/V (kernel instance 2)
@@ -280,16 +278,11 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   // levels per layer: QKV + router | attention splits + expert slices | attention merges | output rows
   constexpr int LPL = 4;
   const int nslice = std::max(1, m.HPG * m.D / 256);       // merge tasks per (sequence, KV group)
-  // with MK_FLAG_SPLIT_MERGE the last split of each (sequence, KV group) merges instead
-  const bool split_merge = (flags & MK_FLAG_SPLIT_MERGE) != 0;
-  const int att_sig = split_merge ? 1 : nslice;
-  P->att_sig = att_sig;
-  P->split_merge = split_merge;
   // output rows: OUT_ROWS per task, except that the workers of the attention merges, which reach
   // their OUT task only after the merge, get none when the others can take every row in tasks of
   // at most OUTR rows
   constexpr int OUT_ROWS = 4;
-  const int n_merge = split_merge ? 0 : B * m.HKV * nslice;
+  const int n_merge = B * m.HKV * nslice;
   int n_out_l = (int)ceil_div(m.H, std::min(OUT_ROWS, OUTR));
   if (W - n_merge >= (int)ceil_div(m.H, OUTR)) n_out_l = std::min(n_out_l, W - n_merge);
   auto split_key = [&](int l, int b, int g, int s) { return ((l * B + b) * m.HKV + g) * 65536 + s; };
@@ -344,7 +337,6 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
           pr.t.w[D_A5] = s | (nsplit[b] << 16);
           pr.t.w[D_W0] = c_qkv[l][g]; pr.t.w[D_T0] = qkv_count[g];
           pr.t.w[D_SIG] = c_aarr[l][b * m.HKV + g];
-          if (split_merge) pr.t.w[D_SIG2] = c_att[l];
           const int keys = last ? seq_lens[b] - k0 : split;
           pr.bytes = (int64_t)keys * m.D * 2 * 2;
           pr.prio = 0;
@@ -396,7 +388,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
     }
     // level 2: attention merges, nslice per (sequence, KV group), each on the worker of one of the
     // group's splits (that worker is done with the step's heavy streams by then)
-    for (int b = 0; b < B && !split_merge; ++b)
+    for (int b = 0; b < B; ++b)
       for (int g = 0; g < m.HKV; ++g)
         for (int q = 0; q < nslice; ++q) {
           Proto pr;
@@ -418,7 +410,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
         Proto pr;
         set(pr.t, OP_OUT, l, lv2);
         pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
-        pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV * att_sig;   // (every merge: already in)
+        pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV * nslice;   // (every merge: already in)
         pr.t.w[D_A4] = 4 | 1;
         pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
         pr.t.w[D_W1] = c_h[l]; pr.t.w[D_T1] = n_gu;
@@ -434,7 +426,7 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
       Proto pr;
       set(pr.t, OP_OUT, l, lv2);
       pr.t.w[D_A0] = a; pr.t.w[D_A1] = e - a;
-      pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV * att_sig;   // every merge of every KV group
+      pr.t.w[D_A2] = c_att[l]; pr.t.w[D_A3] = B * m.HKV * nslice;   // every merge of every KV group
       pr.t.w[D_A4] = down_items > 0 ? 1 : 0;
       pr.t.w[D_W0] = c_route[l]; pr.t.w[D_T0] = 1;
       pr.t.w[D_W1] = c_h[l]; pr.t.w[D_T1] = n_gu;
@@ -656,7 +648,6 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
     std::vector<int> qkv(m.QKVR, 0), out(m.H, 0), rt(m.E, 0);
     std::map<int, std::vector<int>> gu;
     std::vector<std::vector<std::pair<int, int>>> att(P.B * m.HKV), mrg(P.B * m.HKV);
-    std::vector<int> att_merging(P.B * m.HKV, 0);   // splits that merge if they arrive last
     std::vector<const Task*> queue_tasks;
     for (const Task* tp : by_layer[l]) {
       const Task& t = *tp;
@@ -681,7 +672,6 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
           const int b = t.w[D_A0], g = t.w[D_A1];
           if (b < 0 || b >= P.B || g < 0 || g >= m.HKV) { *why = fmt("task %d: sequence %d group %d out of range", t.w[D_ID], b, g); return MK_ERR_INVALID_ARG; }
           (t.w[D_OP] == OP_ATTN ? att : mrg)[b * m.HKV + g].push_back({t.w[D_A2], t.w[D_A3]});
-          if (t.w[D_OP] == OP_ATTN && t.w[D_SIG2] >= 0) att_merging[b * m.HKV + g]++;
           break;
         }
       }
@@ -704,8 +694,8 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
       }
       for (const Task* tp : by_layer[l])
         if (tp->w[D_OP] == OP_OUT && (((tp->w[D_A4] & 4) != 0) != (n_oi > 0) ||
-            (n_oi > 0 && (tp->w[D_A2] != qc - 1 || tp->w[D_A3] != P.B * m.HKV * P.att_sig)))) {
-          // (the kernel's O-projection items wait for B * HKV * att_sig signals on qc - 1)
+            (n_oi > 0 && (tp->w[D_A2] != qc - 1 || tp->w[D_A3] != P.B * m.HKV * std::max(1, m.HPG * m.D / 256))))) {
+          // (the kernel's O-projection items wait for B * HKV * max(1, HPG * D / 256) merges on qc - 1)
           *why = fmt("layer %d: output task %d and the O-projection items disagree", l, tp->w[D_ID]);
           return MK_ERR_INVALID_ARG;
         }
@@ -756,9 +746,7 @@ mk_status validate_plan(const mk_plan& P, std::string* why) {
         if (v.empty()) { *why = fmt("layer %d seq %d group %d: no attention", l, b, g); return MK_ERR_INVALID_ARG; }
         auto& mv = mrg[b * m.HKV + g];
         std::sort(mv.begin(), mv.end());
-        // either merge tasks cover the output once, or every split may merge (the last one does)
-        bool ok = P.split_merge ? mv.empty() && att_merging[b * m.HKV + g] == (int)v.size()
-                                : !mv.empty() && att_merging[b * m.HKV + g] == 0;
+        bool ok = !mv.empty();
         for (size_t i = 0; ok && i < mv.size(); ++i) ok = mv[i].first == (int)i && mv[i].second == (int)mv.size();
         if (!ok) { *why = fmt("layer %d seq %d group %d: merge slices do not cover the output once", l, b, g); return MK_ERR_INVALID_ARG; }
       }
@@ -820,8 +808,6 @@ mk_status simulate_plan(const mk_plan& P, uint64_t seed, int stall_worker, int s
       const uint32_t old = ctr[t.w[D_SIG]]++;
       // last arriver of the router tiles publishes the routing table
       if (t.w[D_SIG2] >= 0 && t.w[D_OP] == OP_ROUTER && old + 1 == (uint32_t)t.w[D_A2]) ctr[t.w[D_SIG2]]++;
-      // last arriving split of a (sequence, KV group) merges it and signals the attention counter
-      if (t.w[D_SIG2] >= 0 && t.w[D_OP] == OP_ATTN && old + 1 == (uint32_t)(t.w[D_A5] >> 16)) ctr[t.w[D_SIG2]]++;
     } else if (t.w[D_SIG2] >= 0) {
       ctr[t.w[D_SIG2]]++;
     }
@@ -1071,7 +1057,6 @@ mk_status mk_decode_step(mk_engine* e, const int32_t* tokens, const int32_t* pos
   p.trace = (unsigned long long*)e->trace_out;
   p.L = e->m.L; p.V = e->m.V; p.B = P.B; p.max_pages = e->desc.max_pages_per_seq; p.num_pages = e->desc.num_pages;
   p.parts_per_layer = P.parts_per_layer; p.n_workers = P.n_workers; p.n_ctr = P.n_ctr; p.done_ctr = P.done_ctr;
-  p.att_sig = P.att_sig;
   p.flags = e->opt.flags; p.has_lm_head = e->desc.has_lm_head; p.has_bias = e->desc.has_router_bias;
   p.eps = e->desc.rms_eps;
   p.watchdog_ticks = (uint64_t)e->opt.watchdog_ms * 100000ull;

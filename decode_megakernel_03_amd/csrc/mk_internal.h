@@ -45,9 +45,7 @@ enum Op {
                   // O-projection row blocks (they wait on the attention counter, which is the queue
                   // counter - 1; bf16 and MXFP4 matrices), then every (slot, row block) down item
   OP_ATTN = 4,    // a0 b, a1 g, a2 k0, a3 k1 (-1 = to seq_len, the split holding the new token),
-                  // a4 first partial of (b, g) in the layer, a5 split | nsplit << 16; sig = the
-                  // group's arrival counter; sig2 >= 0: the split of (b, g) that arrives last merges
-                  // every output of the group and signals sig2 (the attention counter) once
+                  // a4 first partial of (b, g) in the layer, a5 split | nsplit << 16
   OP_OUT = 5,     // a0 row0, a1 nrows, a2 attention counter (KV group g's merges on sub-counters
                   // g*CTR_SUB/HKV ..), a3 its target, a4 bits: 1 = the down projections come from the
                   // queued down items (y): x_{l+1} = x_l + W_o attn + sum_i w_i W_down[e_i] h_i;
@@ -129,8 +127,6 @@ struct Params {
   int32_t L, V, B, max_pages, num_pages, parts_per_layer, n_workers, n_ctr;
   int32_t done_ctr;          // counter index used for end-of-step detection
   int32_t flags, has_lm_head, has_bias;
-  int32_t att_sig;           // signals on a layer's attention counter per (sequence, KV group): one
-                             // per merge task, or 1 when the last split of the group merges
   float eps;
   uint64_t watchdog_ticks;   // 100 MHz ticks
 };

@@ -1553,6 +1553,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
   constexpr int OQT = 4;
   auto run_oproj = [&](int j, int orows, int ntg) -> bool {
     constexpr int AD = S::AD;
+    constexpr int NSL = S::HPG * S::D / 256 > 1 ? S::HPG * S::D / 256 : 1;   // merges per (token, group)
     const int rb = j / ntg, b0 = (j - rb * ntg) * OQT;
     const int r0 = rb * orows, nr = H - r0 < orows ? H - r0 : orows;
     const int nt = p.B - b0 < OQT ? p.B - b0 : OQT;
@@ -1561,7 +1562,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
     WBuf<S::kw(AD), 1, S::WF> A;
     load_block<S::kw(AD), 1, S::WF>(A, 0, nr, orow);
     if (tid() == 0) ctl.norm_l = -1;     // the staged normed input is overwritten below
-    if (!wait_ge(p, ctl, T.a3 - 1, (uint32_t)(p.B * S::HKV * p.att_sig), T.id)) return false;
+    if (!wait_ge(p, ctl, T.a3 - 1, (uint32_t)(p.B * S::HKV * NSL), T.id)) return false;
     const __amdgpu_buffer_rsrc_t At = rsrc(p.attn + (size_t)l * MAXB * AD);
     const __amdgpu_buffer_rsrc_t Ob = rsrc(p.o + (size_t)l * MAXB * H);
     __syncthreads();                     // every wave is done with the previous item's LDS
@@ -1708,88 +1709,6 @@ __host__ __device__ constexpr int rope_off(int tb) {
 // cos and sin of pos_b * inv_freq[i] for every sequence b of the step: [b][0..D/2) cos, [D/2..D) sin
 template <class S, int TB>
 __device__ __forceinline__ float* rope_tab() { return smem + rope_off<S>(TB); }
-
-// Every output of the attention of (sequence b, KV group g), from the nsplit partials: the same
-// log-sum-exp combine as op_merge (the same per-head maxima, scales and sums, and each output summed
-// in split order, so the results are those of the merge tasks bit for bit), for all HPG * D outputs
-// in one workgroup: thread tx takes outputs tx + NT k (k < MO), CH partials per round trip. Run by
-// the split of (b, g) that arrives last (P1 "One persistent kernel for the whole decode step": the
-// merge runs where the last partial lands, without a further hop).
-template <class S>
-__device__ __forceinline__ bool merge_group(CParams& p, Ctl& ctl, int l, int b, int g, int pbase, int nsplit, int task) {
-  constexpr int D = S::D, HPG = S::HPG, OUTS = HPG * D, MO = (OUTS + NT - 1) / NT, CH = 32;
-  static_assert(HPG <= 2 * NWAVE && MERGE_MAX % 4 == 0, "");
-  float* sm = smem;
-  const int tx = tid(), lane = tx & 63, wave = __builtin_amdgcn_readfirstlane(tx >> 6);
-  if (nsplit < 1 || nsplit > MERGE_MAX) {
-    if (tx == 0) raise_error(p, DEV_STALE, task, -1, 1u, (uint32_t)nsplit, (uint32_t)b);
-    return false;
-  }
-  const __amdgpu_buffer_rsrc_t P0 = rsrc(p.apart + ((size_t)l * p.parts_per_layer + pbase) * S::PART);
-  constexpr int SST = MERGE_MAX;
-  float* msl = sm;                                 // [2 HPG][MERGE_MAX]: m (then the scale), then l
-  float* linv = sm + MERGE_MAX * 2 * 2 * NWAVE;    // [HPG]
-  __syncthreads();                                 // (the split's own LDS is done with)
-  float ob[MO][CH];
-#pragma unroll
-  for (int k = 0; k < MO; ++k)
-#pragma unroll
-    for (int u = 0; u < CH; ++u)
-      ob[k][u] = u < nsplit && tx + NT * k < OUTS ? ldc(P0, 4u * (u * S::PART + 2 * HPG + tx + NT * k)) : 0.f;
-  for (int i = tx; i < nsplit * 2 * HPG; i += NT) {
-    const int s2 = i / (2 * HPG), j = i % (2 * HPG);
-    msl[j * SST + s2] = ldc(P0, 4u * (s2 * S::PART + j));
-  }
-  __syncthreads();
-  {
-    const int h = 2 * wave + (lane >> 5), sl = lane & 31;
-    float M = -INFINITY;
-    if (h < HPG)
-      for (int s2 = sl; s2 < nsplit; s2 += 32) M = fmaxf(M, msl[h * SST + s2]);
-    M = wmax<32>(M);
-    float Lsum = 0.f;
-    if (h < HPG)
-      for (int s2 = sl; s2 < nsplit; s2 += 32) {
-        const float ms = msl[h * SST + s2];
-        const float sc = ms == -INFINITY ? 0.f : expf(ms - M);
-        msl[h * SST + s2] = sc;
-        Lsum = __builtin_fmaf(msl[(HPG + h) * SST + s2], sc, Lsum);
-      }
-    Lsum = wsum<32>(Lsum);
-    if (h < HPG && sl == 0) linv[h] = Lsum;
-  }
-  __syncthreads();
-  float acc[MO];
-#pragma unroll
-  for (int k = 0; k < MO; ++k) acc[k] = 0.f;
-  for (int s0 = 0; s0 < nsplit; s0 += CH) {
-    if (s0 > 0) {
-#pragma unroll
-      for (int k = 0; k < MO; ++k)
-#pragma unroll
-        for (int u = 0; u < CH; ++u)
-          ob[k][u] = s0 + u < nsplit && tx + NT * k < OUTS ? ldc(P0, 4u * ((s0 + u) * S::PART + 2 * HPG + tx + NT * k)) : 0.f;
-    }
-#pragma unroll
-    for (int k = 0; k < MO; ++k) {
-      const int hh = tx + NT * k < OUTS ? (tx + NT * k) / D : 0;
-      float sc[CH];                    // all scales first (16-byte LDS reads), then the sum
-#pragma unroll
-      for (int u4 = 0; u4 < CH / 4; ++u4) {
-        const f4 v = *reinterpret_cast<const f4*>(msl + hh * SST + s0 + 4 * u4);
-#pragma unroll
-        for (int c = 0; c < 4; ++c) sc[4 * u4 + c] = s0 + 4 * u4 + c < nsplit ? v[c] : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < CH; ++u) acc[k] = __builtin_fmaf(ob[k][u], sc[u], acc[k]);
-    }
-  }
-  const __amdgpu_buffer_rsrc_t A = rsrc(p.attn + ((size_t)l * MAXB + b) * S::AD + g * HPG * D);
-#pragma unroll
-  for (int k = 0; k < MO; ++k)
-    if (tx + NT * k < OUTS) stc(A, 4u * (tx + NT * k), acc[k] / linv[(tx + NT * k) / D]);
-  return true;
-}
 
 template <class S, int TB, int VAR>
 __device__ __forceinline__ bool op_attn(int task) {
@@ -2162,16 +2081,7 @@ __device__ __forceinline__ bool op_attn(int task) {
   MARK(4);
   drain_t(p);
   MARK(5);
-  if (T.sig2 < 0) {                    // merge tasks combine the partials
-    signal(p, ctl, T.sig, false);
-    return true;
-  }
-  // the split of (b, g) that arrives last merges the group's partials
-  const uint32_t old = signal(p, ctl, T.sig, true);
-  if (old + 1 != (uint32_t)nsplit) return true;
-  if (!merge_group<S>(p, ctl, l, b, g, pbase, nsplit, T.id)) return false;
-  drain_t(p);
-  signal<S::HKV>(p, ctl, T.sig2, false, g);   // on KV group g's sub-counters of the attention counter
+  signal(p, ctl, T.sig, false);
   return true;
 }
 

@@ -25,7 +25,6 @@ MK_FLAG_TRACE = 1
 MK_FLAG_NO_PREFETCH = 2
 MK_FLAG_STATIC_EXPERTS = 4
 MK_FLAG_OPROJ_PER_GROUP = 8
-MK_FLAG_SPLIT_MERGE = 16
 DESC_WORDS = 16
 
 EXPORTED = ["mk_create", "mk_set_options", "mk_build_schedule", "mk_build_schedule_chunked", "mk_prefill",

@@ -140,12 +140,6 @@ typedef struct {
  * attention merges have landed, instead of after all groups (P1 "One persistent kernel for the whole
  * decode step"). Off by default: measured slower on MI355X. Read by mk_decode_step. */
 #define MK_FLAG_OPROJ_PER_GROUP 8u
-/* Ablation: the split of each (sequence, KV group) that arrives last merges the group's attention
- * partials (every output, in one workgroup) in place of merge tasks (P1 "One persistent kernel for
- * the whole decode step"): one dependency hop fewer per layer, but one workgroup does the work of
- * the group's merge tasks. The results are bitwise those of the merge tasks. Off by default:
- * measured slower on MI355X. Read by mk_build_schedule / mk_plan_build. */
-#define MK_FLAG_SPLIT_MERGE 16u
 
 /* Create an engine for `desc` over caller-owned weights (P1 "One persistent kernel for the whole
  * decode step"). Validates the description, copies the pointer tables to the device and

@@ -217,20 +217,6 @@ def test_full_model_batch1_oproj_per_kv_group():
         m.close()
 
 
-def test_full_model_split_merge_batch1_and_batch8():
-    """MK_FLAG_SPLIT_MERGE: the last split of each (sequence, KV group) merges the group's partials
-    in place of merge tasks; the same gates at batch 1 (two steps) and batch 8 (one step)."""
-    from decode_megakernel_03_amd import mk
-    say("test_full_model_split_merge_batch1_and_batch8")
-    for name, steps in (("full", 2), ("full_b8", 1)):
-        m = Model(synth.workload(name), steps=steps, flags=mk.MK_FLAG_SPLIT_MERGE)
-        try:
-            for s in range(steps):
-                m.step_and_check()
-        finally:
-            m.close()
-
-
 def test_full_model_batch1_256_greedy_steps():
     """48-layer model, batch 1, 8192 context, 256 greedy steps on the device: steps 0, 127 and 255
     checked against the oracle (teacher-forced on the GPU's tokens and KV state), the rest run

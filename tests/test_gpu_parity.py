@@ -198,16 +198,6 @@ def test_tiny_oproj_per_kv_group():
     run_steps(synth.workload("tiny"), 3, split_keys=32, flags=mk.MK_FLAG_OPROJ_PER_GROUP)
 
 
-def test_tiny_split_merge():
-    """MK_FLAG_SPLIT_MERGE (the last split of each group merges, no merge tasks) with 32-key splits,
-    so that every group has several splits to merge: batch 1 free-running, then a ragged batch of 3."""
-    from decode_megakernel_03_amd import mk
-    say("test_tiny_split_merge: last-arriving split merges, 32-key splits")
-    run_steps(synth.workload("tiny"), 4, split_keys=32, flags=mk.MK_FLAG_SPLIT_MERGE)
-    run_steps(synth.workload("tiny", batch=3, ragged=(17, 200)), 3, teacher_force=True, split_keys=32,
-              flags=mk.MK_FLAG_SPLIT_MERGE)
-
-
 def test_tiny_split_attention():
     say("test_tiny_split_attention: 32-key attention splits (3 splits + log-sum-exp merge per group)")
     run_steps(synth.workload("tiny"), 4, split_keys=32)

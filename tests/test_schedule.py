@@ -42,8 +42,7 @@ CASES = [
 ]
 
 
-@pytest.mark.parametrize("flags", [0, mk.MK_FLAG_STATIC_EXPERTS, mk.MK_FLAG_SPLIT_MERGE],
-                         ids=["queue", "static", "split-merge"])
+@pytest.mark.parametrize("flags", [0, mk.MK_FLAG_STATIC_EXPERTS], ids=["queue", "static"])
 @pytest.mark.parametrize("name,lens,workers", CASES)
 def test_plan_valid_and_deadlock_free(name, lens, workers, flags):
     wl = synth.workload(name)
@@ -282,28 +281,3 @@ def test_chunked_plan_publishes_kv_in_the_qkv_tasks(name, lens, rows, workers):
         assert mk.mk_plan_info_get(plan).key_capacity_min >= min(lens) + 32 * rows
     finally:
         mk.mk_plan_destroy(plan)
-
-
-@pytest.mark.parametrize("name,lens", [("full", [8193]), ("full", [8193] * 8), ("tiny", [65, 17, 200])])
-def test_split_merge_plan_has_no_merge_tasks(name, lens):
-    """MK_FLAG_SPLIT_MERGE: no merge tasks; every attention split may merge its group (SIG2 = the
-    layer's attention counter, which the output rows wait on for one signal per (sequence, group))."""
-    wl = synth.workload(name)
-    desc = _desc(wl, len(lens), max(lens))
-    plan = mk.mk_plan_build(desc, lens, 512, flags=mk.MK_FLAG_SPLIT_MERGE)
-    try:
-        st, msg = mk.mk_plan_validate(plan)
-        assert st == mk.MK_OK, msg
-        tasks, _ = mk.mk_plan_export(plan)
-    finally:
-        mk.mk_plan_destroy(plan)
-    op = tasks[:, 0]
-    assert (op == 7).sum() == 0
-    att, out = tasks[op == 4], tasks[op == 5]
-    D_A2, D_A3, D_SIG2 = 4, 5, 13
-    assert (att[:, D_SIG2] >= 0).all()
-    for l in range(wl.n_layers):
-        a = att[att[:, 1] == l]
-        o = out[out[:, 1] == l]
-        assert len(set(a[:, D_SIG2])) == 1 and (o[:, D_A2] == a[0, D_SIG2]).all()
-        assert (o[:, D_A3] == len(lens) * wl.n_kv_heads).all()
