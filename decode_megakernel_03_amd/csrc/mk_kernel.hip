@@ -968,6 +968,24 @@ __device__ __forceinline__ void mrows_compute(const MRows<S>& A, int rb, int nro
   __syncthreads();
 }
 
+// Every row block of nrows rows, the next block's loads in flight while one is multiplied (block 0
+// may already be loaded into A, before a dependency wait)
+template <class S, class RowPtr, class Emit>
+__device__ __forceinline__ void mrows_stream(MRows<S>& A, bool a_loaded, int nrows, int ntok, RowPtr rowptr,
+                                             const float* act, float* red, Emit emit) {
+  const int nblk = (nrows + 15) / 16;
+  MRows<S> A2;
+  if (!a_loaded) mrows_load<S>(A, 0, nrows, rowptr);
+  for (int rb = 0; rb < nblk; rb += 2) {
+    if (rb + 1 < nblk) mrows_load<S>(A2, rb + 1, nrows, rowptr);
+    mrows_compute<S>(A, rb, nrows, ntok, act, red, emit);
+    if (rb + 1 < nblk) {
+      if (rb + 2 < nblk) mrows_load<S>(A, rb + 2, nrows, rowptr);
+      mrows_compute<S>(A2, rb + 1, nrows, ntok, act, red, emit);
+    }
+  }
+}
+
 // ------------------------------------------------------------------------------ norm staging
 
 // act[t][H] = RMSNorm(x_l[b_t]) * gain for the listed tokens (P1: one shared normed input per
@@ -1156,10 +1174,7 @@ __device__ __forceinline__ bool op_qkv(int task) {
     __syncthreads();
     stage_norm<S, MRows<S>::AS>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
     MARK(0);
-    for (int rb = 0; rb * 16 < nrows; ++rb) {
-      if (rb > 0 || !pre) mrows_load<S>(A, rb, nrows, rowptr);
-      mrows_compute<S>(A, rb, nrows, p.B, sm, sm + MRows<S>::RED, emit);
-    }
+    mrows_stream<S>(A, pre, nrows, p.B, rowptr, sm, sm + MRows<S>::RED, emit);
   } else {
     WBuf<KW, NP, S::WF> A;
     if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
@@ -1338,10 +1353,7 @@ __device__ __forceinline__ bool op_router(int task) {
     __syncthreads();
     stage_norm<S, MRows<S>::AS>(p, T.layer, ctl.toks, p.B, Lp.attn_norm, sm, T.id);
     MARK(0);
-    for (int rb = 0; rb * 16 < nrows; ++rb) {
-      if (rb > 0 || !pre) mrows_load<S>(A, rb, nrows, rowptr);
-      mrows_compute<S>(A, rb, nrows, p.B, sm, sm + MRows<S>::RED, emit);
-    }
+    mrows_stream<S>(A, pre, nrows, p.B, rowptr, sm, sm + MRows<S>::RED, emit);
   } else {
     WBuf<KW, NP, S::WF> A;
     if (pre) load_block<KW, NP, S::WF>(A, 0, nrows, rowptr);
@@ -2620,13 +2632,12 @@ __device__ __forceinline__ bool op_lmhead(int task) {
     }
   };
   if constexpr (TB > 1) {                        // several tokens: the matrix cores
-    MRows<S> A, A2;
+    MRows<S> A;
     if (pre) mrows_load<S>(A, 0, nrows, rowptr);
     if (!wait_ge(p, ctl, T.w0, (uint32_t)T.t0, T.id)) return false;
     if (tid() < MAXB) ctl.toks[tid()] = tid();
     __syncthreads();
     stage_norm<S, MRows<S>::AS>(p, p.L, ctl.toks, p.B, p.final_norm, sm, T.id);
-    if (!pre) mrows_load<S>(A, 0, nrows, rowptr);
     // thread 8 i + t sees rows i, i + 16, ... of token t, in ascending order
     float bv = -INFINITY;
     int bi = 0x7fffffff;
@@ -2635,16 +2646,7 @@ __device__ __forceinline__ bool op_lmhead(int task) {
       if (logits) __builtin_nontemporal_store(v, logits + (size_t)t * V + row);
       if (v > bv || (v == bv && row < bi)) { bv = v; bi = row; }
     };
-    const int nblk = (nrows + 15) / 16;
-    float* red = sm + MRows<S>::RED;
-    for (int rb = 0; rb < nblk; rb += 2) {
-      if (rb + 1 < nblk) mrows_load<S>(A2, rb + 1, nrows, rowptr);
-      mrows_compute<S>(A, rb, nrows, p.B, sm, red, em);
-      if (rb + 1 < nblk) {
-        if (rb + 2 < nblk) mrows_load<S>(A, rb + 2, nrows, rowptr);
-        mrows_compute<S>(A2, rb + 1, nrows, p.B, sm, red, em);
-      }
-    }
+    mrows_stream<S>(A, pre, nrows, p.B, rowptr, sm, sm + MRows<S>::RED, em);
     float* cv = sm + MRows<S>::END;                 // [16][8]
     int* ci = reinterpret_cast<int*>(cv + 128);
     if (tx < 128) { cv[tx] = bv; ci[tx] = bi; }
