@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--workers-per-cu", type=int, default=0)
     ap.add_argument("--split-keys", type=int, default=0)
     ap.add_argument("--flags", type=int, default=0)
+    ap.add_argument("--refresh-keys", type=int, default=-1,
+                    help="rebuild the schedule once a sequence has grown this many keys past the lengths it was "
+                         "built for (-1: half an attention split, as the engine does; 0: only when stale)")
     ap.add_argument("--no-b8", action="store_true", help="with the default workload, skip the batch-8 line in the JSON")
     ap.add_argument("--trace", default="", help="write the traced step's summary (.txt) here")
     ap.add_argument("--trace-records", action="store_true", help="with --trace, also write the records (.npy) and a Chrome JSON")
@@ -348,6 +351,8 @@ def measure(wl, args, steps, warmup, keep_kv_host=False):
     stream = torch.cuda.current_stream()
     h = stream.cuda_stream
     rebuilds = []
+    built_at = 0
+    refresh = args.refresh_keys if args.refresh_keys >= 0 else eng.refresh_keys
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(total_steps)]
     for s in range(total_steps):
@@ -356,6 +361,12 @@ def measure(wl, args, steps, warmup, keep_kv_host=False):
             torch.cuda.synchronize()
             log(f"[bench] warmup done ({warmup} steps); timing {steps} steps")
             t_wall = time.perf_counter()
+        if refresh > 0 and s > 0 and s - built_at >= refresh:
+            # the open-ended last attention split has absorbed refresh_keys new keys per sequence:
+            # rebuild for the current lengths (host work inside the timed region)
+            mk.mk_build_schedule(eng.h, (ctx + 1 + s).tolist())
+            rebuilds.append(s)
+            built_at = s
         starts[s].record(stream)
         st = mk.mk_decode_step(eng.h, tokens, pos_all[s], bt, len_all[s], logits, h)
         if st == mk.MK_ERR_SCHEDULE_STALE:
@@ -363,6 +374,7 @@ def measure(wl, args, steps, warmup, keep_kv_host=False):
             # work inside the timed region, as a serving loop would pay it) and issue the step again
             mk.mk_build_schedule(eng.h, (ctx + 1 + s).tolist())
             rebuilds.append(s)
+            built_at = s
             log(f"[bench] step {s}: schedule rebuilt for lengths {(ctx + 1 + s).tolist()[:4]}")
             st = mk.mk_decode_step(eng.h, tokens, pos_all[s], bt, len_all[s], logits, h)
         ends[s].record(stream)

@@ -1318,6 +1318,7 @@ mk_status mk_plan_info_get(const mk_plan* P, mk_plan_info* info) {
   info->bytes_max_worker = *std::max_element(per.begin(), per.end());
   info->n_attn_splits = P->n_attn;
   info->key_capacity_min = *std::min_element(P->capacity.begin(), P->capacity.end());
+  info->split_keys = P->split_keys;
   return MK_OK;
 }
 

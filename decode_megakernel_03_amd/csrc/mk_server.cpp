@@ -136,10 +136,20 @@ mk_status rebuild(mk_server* s, const std::vector<Seq>& act, const std::vector<R
   return mk_build_schedule_chunked(s->e, B, lens.data(), rows_per_seq);
 }
 
+// Keys a row may grow past the length its schedule was built for before the owner rebuilds it: half
+// an attention split (the open-ended last split takes every new key and lies on the critical path)
+int refresh_keys(mk_server* s) {
+  mk_plan_info info{};
+  if (mk_plan_info_get(mk_engine_plan(s->e), &info) != MK_OK || info.split_keys < 2) return 1 << 30;
+  return info.split_keys / 2;
+}
+
 void owner_loop(mk_server* s) {
   (void)hipSetDevice(s->device);
   std::unique_lock<std::mutex> lk(s->mu);
   std::vector<int64_t> built_key;               // composition the current schedule was built for
+  std::vector<int> built_len;                   // and each row's length then
+  int refresh = 1 << 30;
   bool have_schedule = false;
   for (;;) {
     s->cv.wait(lk, [&] {
@@ -171,12 +181,16 @@ void owner_loop(mk_server* s) {
     const int B = (int)rows.size();
     mk_status st = MK_OK;
     std::string what;
-    const bool changed = !have_schedule || key != built_key;
+    bool changed = !have_schedule || key != built_key || (int)built_len.size() != B;
+    for (int b = 0; b < B && !changed; ++b) changed = rows[b].pos + 1 - built_len[b] >= refresh;
     if (changed) {
       st = rebuild(s, act, rows, rows_per_seq);
       what = "mk_build_schedule";
       have_schedule = st == MK_OK;
       built_key = key;
+      built_len.resize(B);
+      for (int b = 0; b < B; ++b) built_len[b] = rows[b].pos + 1;
+      if (have_schedule) refresh = refresh_keys(s);
     }
     for (int b = 0; b < B && st == MK_OK; ++b) {
       s->h_in[b] = rows[b].token;
@@ -197,6 +211,8 @@ void owner_loop(mk_server* s) {
       if (st == MK_ERR_SCHEDULE_STALE) {      // a sequence outgrew its attention splits: rebuild, retry
         st = rebuild(s, act, rows, rows_per_seq);
         rebuilt = st == MK_OK;
+        built_len.resize(B);
+        for (int b = 0; b < B; ++b) built_len[b] = rows[b].pos + 1;
         if (st == MK_OK) st = mk_decode_step(s->e, s->d_tokens, s->d_pos, s->d_bt, s->d_lens, L, s->stream);
       }
       what = "mk_decode_step";

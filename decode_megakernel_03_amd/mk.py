@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(HERE, "libmk.so")
 
 MK_OK, MK_ERR_INVALID_ARG, MK_ERR_UNSUPPORTED, MK_ERR_HIP, MK_ERR_OOM = 0, -1, -2, -3, -4
 MK_ERR_NO_SCHEDULE, MK_ERR_SCHEDULE_STALE, MK_ERR_DEVICE = -5, -6, -7
-MK_ABI_VERSION = 2
+MK_ABI_VERSION = 3
 MK_WEIGHTS_BF16 = 0
 MK_WEIGHTS_FP8 = 1
 MK_WEIGHTS_MXFP4 = 2
@@ -71,7 +71,8 @@ class Options(ctypes.Structure):
 class PlanInfo(ctypes.Structure):
     _fields_ = [("n_tasks", ctypes.c_int32), ("n_workers", ctypes.c_int32), ("n_counters", ctypes.c_int32),
                 ("max_queue", ctypes.c_int32), ("bytes_total", ctypes.c_int64), ("bytes_max_worker", ctypes.c_int64),
-                ("n_attn_splits", ctypes.c_int32), ("key_capacity_min", ctypes.c_int32)]
+                ("n_attn_splits", ctypes.c_int32), ("key_capacity_min", ctypes.c_int32),
+                ("split_keys", ctypes.c_int32)]
 
 
 class ServerConfig(ctypes.Structure):
@@ -354,6 +355,8 @@ class Engine:
         self._growth = int(rows_per_seq)
         self._steps = 0
         self.rebuilds = 0
+        # keys a sequence may grow past these lengths before the step rebuilds the schedule
+        self.refresh_keys = max(1, self.plan_info().split_keys // 2)
 
     def prefill(self, tokens, start, block_table, logits_out=None, topk_out=None, stream=None):
         """Chunked prefill of one sequence (mk_prefill); the engine has no schedule afterwards."""
@@ -365,10 +368,19 @@ class Engine:
         mk_set_step_outputs(self.h, **kw)
 
     def step(self, tokens, positions, block_tables, seq_lens, logits_out, stream=None):
-        """One decode step. Every sequence grows by one token per step; when a sequence would outgrow
-        the schedule's attention-split capacity the library refuses the step before launching it
-        (MK_ERR_SCHEDULE_STALE), and the schedule is rebuilt for the current lengths and the step
-        is issued again."""
+        """One decode step. Every sequence grows by one token per step, and the keys past the lengths
+        the schedule was built for land in each sequence's open-ended last attention split: once a
+        sequence has grown by refresh_keys (half a split) the schedule is rebuilt for the step's
+        lengths (given as a tensor: one host read then). When a sequence would outgrow the splits'
+        capacity the library refuses the step before launching it (MK_ERR_SCHEDULE_STALE); the
+        schedule is then rebuilt for the current lengths and the step is issued again."""
+        if (getattr(self, "_lens", None) is not None and hasattr(seq_lens, "cpu")
+                and self._steps * self._growth >= self.refresh_keys):
+            lens = seq_lens.cpu().tolist()
+            if max(n - b for n, b in zip(lens, self._lens)) >= self.refresh_keys:
+                rebuilds = self.rebuilds
+                self.build_schedule(lens, self._growth)
+                self.rebuilds = rebuilds + 1
         st = mk_decode_step(self.h, tokens, positions, block_tables, seq_lens, logits_out, stream)
         if st == MK_ERR_SCHEDULE_STALE and getattr(self, "_lens", None) is not None:
             # the step's own lengths (rows of one sequence advance by several positions per step)

@@ -34,7 +34,7 @@
 extern "C" {
 #endif
 
-#define MK_ABI_VERSION 2
+#define MK_ABI_VERSION 3
 #define MK_MAX_BATCH 8 /* batch sizes up to 8 (P2 body; P3 "Limitations and Future Plans") */
 
 typedef struct mk_engine mk_engine;
@@ -387,6 +387,12 @@ typedef struct {
   int64_t bytes_max_worker;  /* largest per-worker byte load (cost model) */
   int32_t n_attn_splits;     /* attention split tasks */
   int32_t key_capacity_min;  /* smallest per-sequence key capacity before MK_ERR_SCHEDULE_STALE */
+  int32_t split_keys;        /* keys per attention split. Every key past the lengths the schedule was
+                              * built for lands in its sequence's open-ended last split, which grows by
+                              * one key per step, and that split's length is on the critical path:
+                              * rebuilding once a sequence has grown by split_keys / 2 keeps it below
+                              * 1.5 x split_keys (the serving loop does; so do the binding and the
+                              * benchmark). */
 } mk_plan_info;
 
 /* Build a schedule without any GPU (for validation and tests): same algorithm as

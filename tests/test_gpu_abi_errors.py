@@ -89,19 +89,25 @@ def test_schedule_stale_is_refused_before_launch():
     eng.close()
 
 
-def test_engine_rebuilds_a_stale_schedule_and_stays_exact():
-    """1100 greedy steps of the small model from context 64: the schedule's attention splits run out
-    of room after ~1000 steps, Engine.step rebuilds it, and the step after the rebuild and the last
-    step match the oracle (teacher-forced on the GPU's tokens and KV cache)."""
+def _run_long(refresh_off):
+    """1100 greedy steps of the small model from context 64 through Engine.step, with the oracle
+    (teacher-forced on the GPU's tokens and KV cache) at the first rebuild and at the last step."""
     from decode_megakernel_03_amd import mk
     import oracle
-    say("test_engine_rebuilds_a_stale_schedule_and_stays_exact: tiny engine, 1100 steps")
     n_steps = 1100
     wl, s, eng, kd, vd = _engine(n_steps + 1)
     eng.build_schedule((s["ctx"] + 1).tolist())
     cap = eng.plan_info().key_capacity_min
-    assert cap - int(s["ctx"][0]) - 1 < n_steps                      # a rebuild is needed
-    rebuild_at = cap - int(s["ctx"][0])                              # first step refused by the old schedule
+    refresh = eng.refresh_keys
+    assert refresh == eng.plan_info().split_keys // 2 and refresh > 0
+    if refresh_off:
+        eng.refresh_keys = 1 << 30                                    # (for the first schedule only)
+        assert cap - int(s["ctx"][0]) - 1 < n_steps                   # a rebuild is needed
+        first = cap - int(s["ctx"][0])                                # first step refused by the old schedule
+        expect = 1 + (n_steps - 1 - first) // refresh                 # (the new schedule refreshes again)
+    else:
+        first = refresh                                               # the step that rebuilds first
+        expect = (n_steps - 1) // refresh
     argmax = torch.zeros(1, dtype=torch.int32, device="cuda")
     eng.set_step_outputs(argmax_out=argmax)
     logits = torch.zeros(1, wl.vocab, dtype=torch.float32, device="cuda")
@@ -110,7 +116,7 @@ def test_engine_rebuilds_a_stale_schedule_and_stays_exact():
     bt = torch.from_numpy(s["block_tables"]).cuda()
     tok = s["tokens"].astype(np.int64)
     for step in range(n_steps):
-        check = step in (rebuild_at, n_steps - 1)
+        check = step in (first, n_steps - 1)
         kv0 = harness.host_kv(kd, vd) if check else None
         pos = s["ctx"].astype(np.int64) + step
         eng.step(torch.from_numpy(tok.astype(np.int32)).cuda(), torch.from_numpy(pos.astype(np.int32)).cuda(), bt,
@@ -122,6 +128,23 @@ def test_engine_rebuilds_a_stale_schedule_and_stays_exact():
             say(f"  step {step} (position {int(pos[0])}): max|dlogit| {d:.2e}, rebuilds so far {eng.rebuilds}")
             assert d <= 2e-2
             assert int(argmax.item()) == int(np.argmax(ref.logits[0]))
+            if step == first:
+                assert eng.rebuilds == 1
         tok = argmax.cpu().numpy().astype(np.int64)
-    assert eng.rebuilds == 1
+    assert eng.rebuilds == expect, (eng.rebuilds, expect)
     eng.close()
+
+
+def test_engine_refreshes_its_schedule_and_stays_exact():
+    """Engine.step rebuilds the schedule each time a sequence has grown by half an attention split
+    (the open-ended last split would otherwise take every new key): 1100 steps, exact after the first
+    rebuild and at the end."""
+    say("test_engine_refreshes_its_schedule_and_stays_exact: tiny engine, 1100 steps")
+    _run_long(refresh_off=False)
+
+
+def test_engine_rebuilds_a_stale_schedule_and_stays_exact():
+    """With the refresh switched off for the first schedule, its attention splits run out of room
+    after ~1000 steps; the library refuses that step, Engine.step rebuilds and issues it again."""
+    say("test_engine_rebuilds_a_stale_schedule_and_stays_exact: tiny engine, 1100 steps")
+    _run_long(refresh_off=True)

@@ -281,3 +281,21 @@ def test_chunked_plan_publishes_kv_in_the_qkv_tasks(name, lens, rows, workers):
         assert mk.mk_plan_info_get(plan).key_capacity_min >= min(lens) + 32 * rows
     finally:
         mk.mk_plan_destroy(plan)
+
+
+@pytest.mark.parametrize("name,lens", [("full", [8193]), ("full", [8193] * 8), ("tiny", [65])])
+def test_plan_info_reports_its_split_length(name, lens):
+    """mk_plan_info.split_keys is the split the plan uses: the attention tasks of a sequence cover
+    split_keys keys each, except the open-ended last one."""
+    wl = synth.workload(name)
+    desc = _desc(wl, len(lens), max(lens))
+    plan = mk.mk_plan_build(desc, lens, 512)
+    try:
+        info = mk.mk_plan_info_get(plan)
+        tasks, _ = mk.mk_plan_export(plan)
+    finally:
+        mk.mk_plan_destroy(plan)
+    att = tasks[tasks[:, 0] == 4]
+    closed = att[att[:, 5] >= 0]
+    assert info.split_keys >= 16 and info.split_keys % 16 == 0
+    assert len(closed) == 0 or (closed[:, 5] - closed[:, 4] == info.split_keys).all()
