@@ -54,7 +54,7 @@ def parse():
     ap.add_argument("--flags", type=int, default=0)
     ap.add_argument("--refresh-keys", type=int, default=-1,
                     help="rebuild the schedule once a sequence has grown this many keys past the lengths it was "
-                         "built for (-1: half an attention split, as the engine does; 0: only when stale)")
+                         "built for (-1: a quarter of an attention split, as the engine does; 0: only when stale)")
     ap.add_argument("--no-b8", action="store_true", help="with the default workload, skip the batch-8 line in the JSON")
     ap.add_argument("--trace", default="", help="write the traced step's summary (.txt) here")
     ap.add_argument("--trace-records", action="store_true", help="with --trace, also write the records (.npy) and a Chrome JSON")

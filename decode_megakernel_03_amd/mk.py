@@ -356,7 +356,7 @@ class Engine:
         self._steps = 0
         self.rebuilds = 0
         # keys a sequence may grow past these lengths before the step rebuilds the schedule
-        self.refresh_keys = max(1, self.plan_info().split_keys // 2)
+        self.refresh_keys = max(1, self.plan_info().split_keys // 4)
 
     def prefill(self, tokens, start, block_table, logits_out=None, topk_out=None, stream=None):
         """Chunked prefill of one sequence (mk_prefill); the engine has no schedule afterwards."""
@@ -370,7 +370,7 @@ class Engine:
     def step(self, tokens, positions, block_tables, seq_lens, logits_out, stream=None):
         """One decode step. Every sequence grows by one token per step, and the keys past the lengths
         the schedule was built for land in each sequence's open-ended last attention split: once a
-        sequence has grown by refresh_keys (half a split) the schedule is rebuilt for the step's
+        sequence has grown by refresh_keys (a quarter of a split) the schedule is rebuilt for the step's
         lengths (given as a tensor: one host read then). When a sequence would outgrow the splits'
         capacity the library refuses the step before launching it (MK_ERR_SCHEDULE_STALE); the
         schedule is then rebuilt for the current lengths and the step is issued again."""

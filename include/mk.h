@@ -390,8 +390,8 @@ typedef struct {
   int32_t split_keys;        /* keys per attention split. Every key past the lengths the schedule was
                               * built for lands in its sequence's open-ended last split, which grows by
                               * one key per step, and that split's length is on the critical path:
-                              * rebuilding once a sequence has grown by split_keys / 2 keeps it below
-                              * 1.5 x split_keys (the serving loop does; so do the binding and the
+                              * rebuilding once a sequence has grown by split_keys / 4 keeps it below
+                              * 1.25 x split_keys (the serving loop does; so do the binding and the
                               * benchmark). */
 } mk_plan_info;
 

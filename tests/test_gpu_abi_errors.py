@@ -99,7 +99,7 @@ def _run_long(refresh_off):
     eng.build_schedule((s["ctx"] + 1).tolist())
     cap = eng.plan_info().key_capacity_min
     refresh = eng.refresh_keys
-    assert refresh == eng.plan_info().split_keys // 2 and refresh > 0
+    assert refresh == eng.plan_info().split_keys // 4 and refresh > 0
     if refresh_off:
         eng.refresh_keys = 1 << 30                                    # (for the first schedule only)
         assert cap - int(s["ctx"][0]) - 1 < n_steps                   # a rebuild is needed
@@ -136,7 +136,7 @@ def _run_long(refresh_off):
 
 
 def test_engine_refreshes_its_schedule_and_stays_exact():
-    """Engine.step rebuilds the schedule each time a sequence has grown by half an attention split
+    """Engine.step rebuilds the schedule each time a sequence has grown by a quarter of an attention split
     (the open-ended last split would otherwise take every new key): 1100 steps, exact after the first
     rebuild and at the end."""
     say("test_engine_refreshes_its_schedule_and_stays_exact: tiny engine, 1100 steps")
