@@ -391,8 +391,8 @@ typedef struct {
                               * built for lands in its sequence's open-ended last split, which grows by
                               * one key per step, and that split's length is on the critical path:
                               * rebuilding once a sequence has grown by split_keys / 4 keeps it below
-                              * 1.25 x split_keys (the serving loop does; so do the binding and the
-                              * benchmark). */
+                              * 1.25 x split_keys (the binding and the benchmark do; the serving loop,
+                              * which also rebuilds at every change of its batch, at split_keys / 2). */
 } mk_plan_info;
 
 /* Build a schedule without any GPU (for validation and tests): same algorithm as
