@@ -1438,10 +1438,13 @@ __device__ __forceinline__ bool op_gateup(int task) {
   const int n0 = __builtin_popcountll(u0), nu = n0 + __builtin_popcountll(u1);
   // expert of union slot u (the u-th selected expert in ascending order); thread 0 lists its tokens
   // (batch row, rank of the expert in that token's selection) in ctl.toks / ctl.trank, ctl.flag
-  auto slot_expert = [&](int u) {
+  auto expert_of = [&](int u) {
     unsigned long long m = u < n0 ? u0 : u1;
     for (int j = u < n0 ? u : u - n0; j > 0; --j) m &= m - 1;
-    const int e = (u < n0 ? 0 : 64) + __builtin_ctzll(m);
+    return (u < n0 ? 0 : 64) + __builtin_ctzll(m);
+  };
+  auto slot_expert = [&](int u) {
+    const int e = expert_of(u);
     if (tx == 0) {
       int nt = 0;
       for (int b = 0; b < p.B; ++b) {
@@ -1457,8 +1460,34 @@ __device__ __forceinline__ bool op_gateup(int task) {
     }
     return e;
   };
-  // rows f0..f0+nf of union slot u for its tokens
-  auto run_item = [&](int u, int f0, int nf) -> bool {
+  // the 2 nf rows of an item: W_gate[e] rows f0.., then W_up[e] rows f0..
+  auto gu_rows = [&](int e, int f0, int nf) {
+    const uint16_t* wg = Lp.w_gate + (size_t)e * F * S::rw(H);
+    const uint16_t* wu = Lp.w_up + (size_t)e * F * S::rw(H);
+    return [=](int r) { return r < nf ? wg + (size_t)(f0 + r) * S::rw(H) : wu + (size_t)(f0 + r - nf) * S::rw(H); };
+  };
+  int slices_c = 1, rows = 1, n_gu = 0, n_items = 0;   // the queue's item geometry (queue mode)
+  // hand the draw to the workgroup, with the sub-queue that had the most items left in the
+  // snapshot (-1: none had any)
+  auto publish = [&]() {
+    if (wave == 0) {
+      const int64_t first = (int64_t)head * nq + lane;
+      const int rem = lane < nq && first < n_items ? (int)((n_items - first + nq - 1) / nq) : 0;
+      const int best = (int)wmax<64>((float)rem);
+      const unsigned long long who = __ballot(rem == best && rem > 0);
+      if (lane == 0) {
+        ctl.item = (int)kreq;
+        ctl.steal = who ? __builtin_ctzll(who) : -1;
+      }
+    }
+    __syncthreads();
+  };
+  // rows f0..f0+nf of union slot u for its tokens. A holds the item's first weight block when
+  // `loaded` (requested by the previous item). With `chain` (queue mode), once the item's weights
+  // are consumed the next draw is published and, when it is a gate/up item, its first weight block
+  // is requested before this item's stores and drain, so that the worker never waits a whole memory
+  // round trip between two items. Returns whether it did.
+  auto run_item = [&](int u, int f0, int nf, WBuf<KWH, NP, S::WF>& A, bool loaded, bool chain) -> bool {
     if (ctl.norm_l != l) {       // a down item used the staging area since: stage the normed input again
       __syncthreads();
       if (tid() < MAXB) ctl.toks[tid()] = tid();
@@ -1468,11 +1497,8 @@ __device__ __forceinline__ bool op_gateup(int task) {
       __syncthreads();
     }
     const int e = slot_expert(u);
-    const uint16_t* wg = Lp.w_gate + (size_t)e * F * S::rw(H);
-    const uint16_t* wu = Lp.w_up + (size_t)e * F * S::rw(H);
-    auto rowptr = [&](int r) { return r < nf ? wg + (size_t)(f0 + r) * S::rw(H) : wu + (size_t)(f0 + r - nf) * S::rw(H); };
-    WBuf<KWH, NP, S::WF> A;
-    load_block<KWH, NP, S::WF>(A, 0, 2 * nf, rowptr);
+    const auto rowptr = gu_rows(e, f0, nf);
+    if (!loaded) load_block<KWH, NP, S::WF>(A, 0, 2 * nf, rowptr);
     __syncthreads();
     const int ntok = ctl.flag;
     MARK(1);
@@ -1483,7 +1509,18 @@ __device__ __forceinline__ bool op_gateup(int task) {
     gemv_stream<KWH, NP, TB, 1, S::WF>(A, true, 2 * nf, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)brow[t] * H; },
         [&](int r, int t, float v) { gu[t * 2 * nf + r] = v; });
-    __syncthreads();
+    bool next = false;
+    if (chain) {
+      publish();                           // (a barrier: gu is complete too)
+      const int in = sq + nq * ctl.item;
+      if (in < n_gu) {
+        const int un = in / slices_c, fn = (in - un * slices_c) * rows, nfn = F - fn < rows ? F - fn : rows;
+        load_block<KWH, NP, S::WF>(A, 0, 2 * nfn, gu_rows(expert_of(un), fn, nfn));
+        next = true;
+      }
+    } else {
+      __syncthreads();
+    }
     MARK(2);
     const __amdgpu_buffer_rsrc_t Hb = rsrc(p.h + (size_t)l * MAXB * K * F);
     for (int i = tid(); i < ntok * nf; i += NT) {
@@ -1499,12 +1536,12 @@ __device__ __forceinline__ bool op_gateup(int task) {
       if (tx == 0) ctr_add(p.slot_ctr + ((size_t)l * MAX_SLOTS + u) * CTR_STRIDE, 1u);
     }
     __syncthreads();      // toks / trank / gu are rewritten by the next item
-    return true;
+    return next;
   };
   // down item q of union slot u: rows q*DOWN_ROWS.. of W_down[e] for every token of the slot, once
   // every gate/up item of the slot is done: y[b][rank][row] = W_down[e][row] . h[b][rank]. Its weight
   // rows are requested before the slot's count is awaited. The staged h overwrites the normed input.
-  auto run_down = [&](int u, int q, int slices_c) -> bool {
+  auto run_down = [&](int u, int q) -> bool {
     // (MXFP4: two passes of 8 rows per wave - a block of the same 64 rows' bytes, half the registers)
     constexpr int NPD = S::WF == 2 ? 2 : 4;
     const int e = slot_expert(u);
@@ -1587,37 +1624,54 @@ __device__ __forceinline__ bool op_gateup(int task) {
     return true;
   };
   if (TB == 1 || !dyn) {           // one token: static slices only (the queue is never scheduled)
-    if (T.a0 < nu) run_item(T.a0, T.a1, T.a2);
+    if (T.a0 < nu) {
+      WBuf<KWH, NP, S::WF> A;
+      run_item(T.a0, T.a1, T.a2, A, false, false);
+    }
   } else if constexpr (TB > 1) {
-    // item size from the step's union: with at least four slices per worker, a draw takes two
-    // adjacent slices (fewer draws and larger streams); a small union (skewed routing) keeps
-    // single slices so that the work spreads over more workers. Every task derives the same grain.
+    // item size from the step's union: with at least four slices per worker, a draw takes three
+    // adjacent slices (two for MXFP4 rows, whose decode makes an item's bytes slower to consume) -
+    // fewer draws and longer streams; a small union (skewed routing) keeps single slices so that the
+    // work spreads over more workers. Every task derives the same grain. Measured on MI355X (batch 8,
+    // 8K context, tok/s): bf16 1165 / 1183 / 1157 and FP8 1274 / 1288 / 1231 with two / three /
+    // four slices, MXFP4 1201 / 1188 with two / three; grain 2 under skewed routing: 1278 vs 1361.
+    constexpr int GMAX = S::WF == 2 ? 2 : 3;
     const int slices = T.a2, nfs = T.a4;
-    const int grain = (nu * slices >= 4 * p.n_workers && 2 * nfs <= 32) ? 2 : 1;
-    const int slices_c = (slices + grain - 1) / grain, rows = grain * nfs;
-    const int n_gu = nu * slices_c;                 // gate/up items first, then the down items,
+    const int grain = (nu * slices >= 4 * p.n_workers && GMAX * nfs <= 48) ? GMAX : 1;
+    slices_c = (slices + grain - 1) / grain;
+    rows = grain * nfs;
+    n_gu = nu * slices_c;                           // gate/up items first, then the down items,
     const int n_dn = n_gu + nu * qd;                // then the O-projection items
-    const int n_items = n_dn + n_oi;
+    n_items = n_dn + n_oi;
     const int ntg = (p.B + OQT - 1) / OQT;          // token groups of the O-projection items
     const int orows = n_oi > 0 ? (H + n_oi / ntg - 1) / (n_oi / ntg) : 0;
-    // hand the draw to the workgroup, with the sub-queue that had the most items left in the
-    // snapshot (-1: none had any)
-    auto publish = [&]() {
-      if (wave == 0) {
-        const int64_t first = (int64_t)head * nq + lane;
-        const int rem = lane < nq && first < n_items ? (int)((n_items - first + nq - 1) / nq) : 0;
-        const int best = (int)wmax<64>((float)rem);
-        const unsigned long long who = __ballot(rem == best && rem > 0);
-        if (lane == 0) {
-          ctl.item = (int)kreq;
-          ctl.steal = who ? __builtin_ctzll(who) : -1;
-        }
-      }
-      __syncthreads();
-    };
     publish();
     int probes = 1;
-    for (;;) {
+    bool more = true;
+    {
+      // the gate/up items, which head every sub-queue: each one requests the next one's first
+      // weight block (A stays in registers from one item to the next)
+      WBuf<KWH, NP, S::WF> A;
+      bool pre = false;
+      for (;;) {
+        const int k = ctl.item, steal_q = ctl.steal;
+        __syncthreads();    // every thread has read the draw
+        const int i = sq + nq * k;
+        if (i >= n_items) {               // this sub-queue is exhausted: steal from another one
+          if (steal_q < 0 || probes >= STEAL_PROBES) { more = false; break; }
+          ++probes;
+          sq = steal_q;
+          draw(sq);
+          publish();
+          continue;
+        }
+        if (i >= n_gu) break;             // (the draw stays published for the loop below)
+        draw(sq);                         // the next draw, in flight during the item
+        const int u = i / slices_c, f0 = (i - u * slices_c) * rows;
+        pre = run_item(u, f0, F - f0 < rows ? F - f0 : rows, A, pre, true);
+      }
+    }
+    while (more) {
       const int k = ctl.item, steal_q = ctl.steal;
       __syncthreads();    // every thread has read the draw
       const int i = sq + nq * k;
@@ -1630,12 +1684,13 @@ __device__ __forceinline__ bool op_gateup(int task) {
         continue;
       }
       draw(sq);                         // the next draw, in flight during the item
-      if (i < n_gu) {
-        const int u = i / slices_c, j = i - u * slices_c, f0 = j * rows;
-        run_item(u, f0, F - f0 < rows ? F - f0 : rows);
+      if (i < n_gu) {                   // (a stolen gate/up item after the sub-queue's others)
+        const int u = i / slices_c, f0 = (i - u * slices_c) * rows;
+        WBuf<KWH, NP, S::WF> A;
+        run_item(u, f0, F - f0 < rows ? F - f0 : rows, A, false, false);
       } else if (i >= n_gu + n_oi) {
         const int i2 = i - n_gu - n_oi, u = i2 / qd;
-        if (!run_down(u, i2 - u * qd, slices_c)) return false;
+        if (!run_down(u, i2 - u * qd)) return false;
       } else {
         // (compiled for bf16 and MXFP4 matrices: in the FP8 instances the extra GEMV path costs 15
         // more spilled registers, and the schedule gives them no such items)

@@ -199,7 +199,8 @@ def _drain_queue(tickets, nq, n_items, rng):
 
 
 @pytest.mark.parametrize("name,lens,workers", [("full", [8193] * 8, 512), ("full", [8193, 8193], 512), ("tiny", [65, 17, 200], 16),
-                                               ("full", [1025, 30000, 4096, 77, 16, 17, 32768, 9000], 512)])
+                                               ("full", [1025, 30000, 4096, 77, 16, 17, 32768, 9000], 512),
+                                               ("full_fp8", [8193] * 8, 512), ("full_mxfp4", [8193] * 8, 512)])
 def test_expert_queue_runs_every_item_once(name, lens, workers):
     """Queue-mode expert tasks (batches above 1): one queue counter per layer that nothing waits on, every sub-queue
     owned by some task, and under random interleavings every (slot, slice) item of the step's union
@@ -218,8 +219,10 @@ def test_expert_queue_runs_every_item_once(name, lens, workers):
     rng = np.random.default_rng(0)
     slots = min(wl.n_experts, wl.top_k * len(lens))
     for nu in sorted({wl.top_k, (wl.top_k + slots) // 2, slots}):
-        # the kernel's item size: two adjacent slices per draw once there are 4 slices per worker
-        grain = 2 if nu * slices >= 4 * workers and 2 * nfs <= 32 else 1
+        # the kernel's item size: three adjacent slices per draw (two for MXFP4 rows) once there
+        # are 4 slices per worker
+        gmax = 2 if wl.weights == "mxfp4" else 3
+        grain = gmax if nu * slices >= 4 * workers and gmax * nfs <= 48 else 1
         slices_c = -(-slices // grain)
         runs = _drain_queue(list(gu[:, 2]), nq, nu * slices_c, rng)
         assert np.all(runs == 1)
