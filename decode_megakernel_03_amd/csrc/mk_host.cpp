@@ -195,8 +195,8 @@ mk_status build_plan(const mk_model_desc& desc, int B, const int32_t* seq_lens, 
   const int64_t gu_target = std::max<int64_t>(slots, W - splits_for(split));
   int nf = (int)ceil_div(m.F, std::max<int64_t>(1, gu_target / slots));
   nf = std::max(4, std::min(32, nf));   // at most 256 KB of gate + up per task (balance at large batches)
-  // with several sequences the slices are queue items: 16 rows, which the kernel takes two at a time
-  // when the step's union is large (see the expert queue in the kernel)
+  // with several sequences the slices are queue items: 16 rows, which the kernel takes three at a
+  // time (two for MXFP4 rows) when the step's union is large (see the expert queue in the kernel)
   if (B > 1 && !(flags & MK_FLAG_STATIC_EXPERTS)) nf = 16;
   if (align > 1) nf = std::max(align, (nf + align / 2) / align * align);
   const int slices = (int)ceil_div(m.F, nf);
