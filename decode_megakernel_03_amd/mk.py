@@ -409,10 +409,11 @@ class Engine:
             mk_destroy(self.h)
             self.h = None
 
-    def __del__(self):
+    def __del__(self, _finalizing=_finalizing):
         # at interpreter shutdown the HIP runtime (and a profiler attached to it) may already be torn
-        # down: leave the engine to process exit then, and never call into the library
-        if _finalizing():
+        # down: leave the engine to process exit then, and never call into the library. (The check is
+        # bound as a default argument: module globals may already be cleared when this runs.)
+        if not getattr(self, "h", None) or _finalizing():
             return
         try:
             self.close()

@@ -77,3 +77,20 @@ def test_plan_build_rejects_bad_arguments():
     assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, one, 64, 0, 0, 0, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG   # rows_per_seq 0
     assert mk.LIB.mk_plan_build(ctypes.byref(d), 1, one, 64, 0, 0, 2, ctypes.byref(h)) == mk.MK_ERR_INVALID_ARG   # > batch
     assert not h.value
+
+
+def test_engine_finalizer_makes_no_library_call_when_closed_or_at_shutdown(monkeypatch):
+    """Engine.__del__ must not call into the library for a closed engine or while the interpreter
+    shuts down (the runtime may be gone), and must work after the module's globals were cleared."""
+    calls = []
+    monkeypatch.setattr(mk.Engine, "close", lambda self: calls.append(self.h))
+    e = mk.Engine.__new__(mk.Engine)
+    e.h = None
+    monkeypatch.setattr(mk, "_finalizing", None)      # module teardown clears globals
+    e.__del__()
+    e.h = 7
+    e.__del__(_finalizing=lambda: True)
+    assert calls == []
+    e.__del__(_finalizing=lambda: False)
+    assert calls == [7]
+    e.h = None
