@@ -565,9 +565,9 @@ __device__ __forceinline__ void compute_block(const WBuf<KD, NP, WF>& b, int blk
 // so a batch of TB tokens reads LDS NP times less. Per row, the products are summed in the same
 // order as compute_block.
 //
-// TG = 2 (every token of the batch multiplies every row: QKV, router): tokens are taken in pairs, so
-// that each weight is unpacked from bf16 once per pair (the GEMV is bound by vector-ALU issue at 8
-// tokens). A pair is computed whole once its first token is in range (act_of must return readable
+// TG = 2 (tokens that share every row: the batch in the QKV and router GEMVs of the vector-ALU form,
+// the tokens of a union slot in bf16 expert items): tokens are taken in pairs, so that each weight
+// is unpacked from bf16 once per pair (such GEMVs are bound by vector-ALU issue at several tokens). A pair is computed whole once its first token is in range (act_of must return readable
 // LDS for every t < TB); the second token's result is emitted only if it is in range. Same per-row
 // order of products.
 //
@@ -1389,6 +1389,11 @@ __device__ __forceinline__ bool op_gateup(int task) {
   float* sm = smem;
   const TaskHdr T = read_task(p, task);
   constexpr int H = S::H, F = S::F, K = S::K, KWH = S::kw(H), NP = (Geo<KWH>::CPL >= 4) ? 2 : 4;
+  // bf16 rows of an item take the slot's tokens in pairs (each weight unpacked once per pair; the
+  // same products in the same order). Measured on MI355X: batch 8 1179 -> 1195 tok/s, the ragged
+  // Zipf-routed batch (hot experts with up to 8 tokens) 1353 -> 1442. FP8 and MXFP4 rows keep one
+  // token at a time: pairs spill 74 and 346 registers in those instances.
+  constexpr int TGE = (TB > 1 && S::WF == 0) ? 2 : 1;
   const int l = T.layer;
   const auto& Lp = cst(p.layers)[l];
   // Queue mode (a3 >= 0, P3 "Scheduling and Performance Benchmarks": dynamic work stealing): the
@@ -1506,7 +1511,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
 #pragma unroll
     for (int t = 0; t < TB; ++t) brow[t] = t < ntok ? ctl.toks[t] : 0;
     float* gu = sm + (size_t)TB * H;                 // [TB][2 nf]
-    gemv_stream<KWH, NP, TB, 1, S::WF>(A, true, 2 * nf, ntok, rowptr,
+    gemv_stream<KWH, NP, TB, TGE, S::WF>(A, true, 2 * nf, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)brow[t] * H; },
         [&](int r, int t, float v) { gu[t * 2 * nf + r] = v; });
     bool next = false;
@@ -1582,7 +1587,7 @@ __device__ __forceinline__ bool op_gateup(int task) {
     __syncthreads();
     MARK(5);
     const __amdgpu_buffer_rsrc_t Y = rsrc(p.y + (size_t)l * MAXB * K * H);
-    gemv_stream<S::kw(F), NPD, TB, 1, S::WF>(A, true, nr, ntok, rowptr,
+    gemv_stream<S::kw(F), NPD, TB, TGE, S::WF>(A, true, nr, ntok, rowptr,
         [&](int r, int t) { return sm + (size_t)t * F; },
         [&](int r, int t, float v) {
           int yo = 0;
